@@ -1,0 +1,51 @@
+"""Bit-level number conversions used by the oracle (its own; nothing here is shared with the GPU path).
+
+* bf16 values arrive as uint16 bit patterns; widening to float32 is exact (append 16 zero bits).
+* fp16 rounding uses numpy's float32 -> float16 cast, which rounds to nearest, ties to even
+  (checked by a pin on exact halfway cases).
+* ``f32_key`` maps non-negative float32 values to uint32 in an order-preserving way (the IEEE bit
+  pattern itself), the domain in which the bisection of the top-p threshold takes midpoints.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest even (used only to build test fixtures)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return (u >> np.uint64(16)).astype(np.uint16)
+
+
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    """float32 -> float16, round to nearest even."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+def f16_bits(x16: np.ndarray) -> np.ndarray:
+    return np.asarray(x16, dtype=np.float16).view(np.uint16)
+
+
+def f16_from_bits(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16)
+
+
+def f32_key(x: np.ndarray) -> np.ndarray:
+    """Order-preserving uint32 image of non-negative float32 values (their bit pattern)."""
+    x = np.asarray(x, dtype=np.float32)
+    if np.any(x < 0) or np.any(np.isnan(x)):
+        raise ValueError("f32_key expects non-negative, non-NaN values")
+    return (x + F32(0.0)).view(np.uint32)  # +0.0 turns -0.0 into +0.0
+
+
+def f32_from_key(k) -> np.float32:
+    return np.array([k], dtype=np.uint32).view(np.float32)[0]

@@ -1,0 +1,106 @@
+"""The whole select-then-prune decode step, composed from O1-O11 (Paper-Notes "整体框架";
+paperlayer §4.1, Fig. 5): base selector with a conservative budget -> INT4 weight estimate ->
+per-head top-p -> group union -> sparse attention over the survivors.
+
+``decode_unit`` runs one (sequence b, kv-head h) unit; ``decode`` runs them all.  Inputs are plain
+arrays (bf16 as uint16 bits) in the logical per-sequence order:
+
+  q        uint16 [G][128]      the group's query heads
+  kseq     uint16 [n][128]      this kv-head's keys, token order
+  vseq     uint16 [n][128]
+  keep_frac  selector budget as a fraction of pages (>= 1: every page is a candidate)
+  ranges   optional (begin, length) candidate ranges (the cluster path) instead of pages
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import attention, doublep, estimate, quantize, select, topp
+
+
+def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, keep_frac: float,
+                sm: float, ranges=None, with_f64_logits: bool = False) -> dict:
+    n = kseq.shape[0]
+    G = q.shape[0]
+    out: dict = {}
+    # ---- base selector -------------------------------------------------------------------------
+    if ranges is not None:
+        cand = select.candidates_from_ranges(ranges)
+        out["pages"] = None
+    elif keep_frac >= 1.0:
+        npg = -(-n // 16)
+        out["pages"] = np.arange(npg, dtype=np.int32)
+        cand = select.candidates_from_pages(out["pages"], n)
+    else:
+        kmin, kmax = quantize.page_bounds(kseq[:, None, :])
+        kmin, kmax = kmin[:, 0, :], kmax[:, 0, :]
+        gs = select.group_scores(q, kmin, kmax)
+        out["group_scores"] = gs
+        out["pages"] = select.top_pages(gs, select.keep_count(kmin.shape[0], keep_frac))
+        cand = select.candidates_from_pages(out["pages"], n)
+    out["candidates"] = cand
+    # ---- INT4 estimate, softmax, top-p per query head ------------------------------------------
+    qz = quantize.quantize_rows(kseq[cand]) if cand.size else None
+    heads = []
+    for h in range(G):
+        if cand.size:
+            lg = estimate.logits_spec(q[h], qz["codes"], qz["scale"], qz["zero"], sm)
+            W = estimate.softmax_f64(lg)
+        else:
+            lg = np.zeros(0, np.float32)
+            W = np.zeros(0)
+        res = topp.topp_sort(W, p)
+        hd = {"logits": lg, "W": W, "topp": res, "tokens": cand[res["sel"]]}
+        if with_f64_logits and cand.size:
+            hd["logits_f64"] = estimate.logits_f64(q[h], qz["codes"], qz["scale"], qz["zero"], sm)
+        heads.append(hd)
+    out["heads"] = heads
+    # ---- union and attention -------------------------------------------------------------------
+    U = attention.union([hd["tokens"] for hd in heads])
+    out["union"] = U
+    o = np.zeros((G, 128))
+    lse = np.zeros(G)
+    for h in range(G):
+        o[h], lse[h] = attention.sparse_attention(q[h], kseq, vseq, U, sm)
+    out["out"], out["lse"] = o, lse
+    return out
+
+
+def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=False) -> dict:
+    """Run the oracle on a workload-like object (fields of ``gen.Workload``).
+
+    ``units`` optionally restricts the work to a list of (b, kv-head) pairs; the cluster path is
+    taken when the workload carries clusters (``w.csize`` is not None).
+    Returns ``{(b, h): decode_unit result}``.
+    """
+    p = w.p if p is None else p
+    keep_frac = w.keep_frac if keep_frac is None else keep_frac
+    sm = float(np.float32(1.0 / math.sqrt(128))) if sm is None else sm
+    G = w.num_q_heads // w.num_kv_heads
+    if units is None:
+        units = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    res = {}
+    logical_k = {}
+    logical_v = {}
+    for b, h in units:
+        if b not in logical_k:
+            logical_k[b] = w.logical("k", b)
+            logical_v[b] = w.logical("v", b)
+        q = w.q[b, h * G:(h + 1) * G]
+        kseq, vseq = logical_k[b][:, h, :], logical_v[b][:, h, :]
+        ranges = None
+        if getattr(w, "csize", None) is not None:
+            cs = doublep.select_clusters(q, w.centroids[b, h], w.csize[b, h], w.p1, sm)
+            ranges = doublep.ranges_of(cs["kept"], w.coff[b, h])
+            r = decode_unit(q, kseq, vseq, p=p, keep_frac=1.0, sm=sm, ranges=ranges,
+                            with_f64_logits=with_f64_logits)
+            r["clusters"] = cs
+            r["ranges"] = ranges
+        else:
+            r = decode_unit(q, kseq, vseq, p=p, keep_frac=keep_frac, sm=sm,
+                            with_f64_logits=with_f64_logits)
+        res[(b, h)] = r
+    return res

@@ -1,0 +1,137 @@
+"""O1 INT4 K quantisation and O2 page key bounds.
+
+O1 follows the 4-bit K cache of the pages (Paper-Notes "关键设计 / 4-bit K缓存量化"; paperlayer
+§4.2 and §B.1: dynamic quantisation with FP16 scales and zero points, two 4-bit values per byte).
+The pages leave the granularity, the rounding and the nibble order open; the readings taken are:
+
+* asymmetric min/max quantisation in groups of 32 consecutive channels of one (token, kv-head) row,
+  one fp16 scale and one fp16 zero point per group (128 channels -> 4 groups);
+* scale  s = fp16_rne( fp32(max - min) / 15 ),  zero  z = fp16_rne(min);
+* code_c = 0 when s == 0, else clamp(rint_even( fp32(x_c - z) / s ), 0, 15), with the fp16 s and z
+  widened to fp32 and every operation a correctly rounded fp32 operation;
+* byte j of a row holds code_{2j} in its low nibble and code_{2j+1} in its high nibble;
+* dequantised value  x^_c = code_c * s + z  in fp32 (the product is exact, so fused or not agrees).
+
+This is an encoding, so its float32 operation sequence is the specification; numpy float32
+arithmetic performs each operation with IEEE rounding, one at a time.
+
+O2 is the per-page, per-channel key minimum and maximum over the page's valid slots, used by the
+Quest-style page bound (the base selector that the Twilight pages name but do not define).  Min and
+max of bf16 values are bf16 values, so the bounds are exact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import F32, bf16_to_f32, f16_bits
+
+GROUP = 32
+NGROUPS = 128 // GROUP
+PAGE = 16
+
+
+def quantize_rows(kbits: np.ndarray) -> dict:
+    """Quantise bf16 key rows ``uint16 [..., 128]``.
+
+    Returns ``codes`` uint8 [..., 128], ``packed`` uint8 [..., 64], ``scale`` and ``zero`` float16
+    [..., 4].
+    """
+    x = bf16_to_f32(kbits)
+    shp = x.shape[:-1]
+    xg = x.reshape(shp + (NGROUPS, GROUP))
+    mn = xg.min(axis=-1)
+    mx = xg.max(axis=-1)
+    if not (np.all(np.isfinite(x)) and np.all(np.abs(x) <= 65504.0)):
+        raise ValueError("quantisation input must be finite and within the fp16 range")
+    rng = (mx - mn).astype(F32)                      # fp32 subtraction
+    s16 = (rng / F32(15.0)).astype(np.float16)      # fp32 division, then fp16 round-to-nearest-even
+    z16 = mn.astype(np.float16)
+    s = s16.astype(F32)
+    z = z16.astype(F32)
+    diff = (xg - z[..., None]).astype(F32)           # fp32 subtraction
+    safe = np.where(s == 0, F32(1.0), s).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = (diff / safe[..., None]).astype(F32)     # fp32 division
+    code = np.clip(np.rint(t), 0, 15)                # rint = round half to even
+    code = np.where((s == 0)[..., None], 0, code).astype(np.uint8).reshape(shp + (128,))
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return {"codes": code, "packed": packed, "scale": s16, "zero": z16}
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """uint8 [..., 64] -> codes uint8 [..., 128] (element 2j = low nibble of byte j)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (128,), np.uint8)
+    out[..., 0::2] = packed & 0x0F
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def dequantize(codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray) -> np.ndarray:
+    """x^ = code * s + z in fp32; codes [..., 128], scale/zero [..., 4]."""
+    c = np.asarray(codes, dtype=F32).reshape(codes.shape[:-1] + (NGROUPS, GROUP))
+    s = np.asarray(scale16, dtype=np.float16).astype(F32)[..., None]
+    z = np.asarray(zero16, dtype=np.float16).astype(F32)[..., None]
+    return ((c * s).astype(F32) + z).astype(F32).reshape(codes.shape)
+
+
+def page_bounds(kbits_seq: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """O2: per-page channel-wise key min and max of one sequence.
+
+    ``kbits_seq`` uint16 [n][Hkv][128] in logical order.  Returns float32 ``kmin``, ``kmax`` of
+    shape [ceil(n/16)][Hkv][128]; a partial last page uses only its valid slots.
+    """
+    x = bf16_to_f32(kbits_seq)
+    n = x.shape[0]
+    npg = -(-n // PAGE)
+    kmin = np.empty((npg,) + x.shape[1:], F32)
+    kmax = np.empty((npg,) + x.shape[1:], F32)
+    for j in range(npg):
+        blk = x[j * PAGE:min(n, (j + 1) * PAGE)]
+        kmin[j] = blk.min(axis=0)
+        kmax[j] = blk.max(axis=0)
+    return kmin, kmax
+
+
+# --------------------------------------------------------------------------------------------------
+# Expected device arrays in the paged layout (for element-by-element comparison)
+# --------------------------------------------------------------------------------------------------
+def expected_paged(k_pages: np.ndarray, page_table: np.ndarray, seq_lens: np.ndarray,
+                   tok_begin=None, tok_end=None) -> dict:
+    """Expected ``k4`` [P][Hkv][16][64] u8, ``k4_meta`` [P][Hkv][16][4][2] fp16 bits and ``kbound``
+    [P][Hkv][2][128] bf16 bits for the tokens in [tok_begin[b], tok_end[b]) of each sequence
+    (default: the whole sequence).  Entries that the range does not define are returned as masks
+    ``tok_mask`` [P][Hkv?][16] and ``page_mask`` [P] so a comparison can skip them.
+    """
+    P, Hkv = k_pages.shape[0], k_pages.shape[1]
+    B = len(seq_lens)
+    tb = np.zeros(B, np.int64) if tok_begin is None else np.asarray(tok_begin, np.int64)
+    te = np.asarray(seq_lens, np.int64) if tok_end is None else np.asarray(tok_end, np.int64)
+    k4 = np.zeros((P, Hkv, PAGE, 64), np.uint8)
+    meta = np.zeros((P, Hkv, PAGE, NGROUPS, 2), np.uint16)
+    kb = np.zeros((P, Hkv, 2, 128), np.uint16)
+    tok_mask = np.zeros((P, PAGE), bool)
+    page_mask = np.zeros(P, bool)
+    for b in range(B):
+        if te[b] <= tb[b]:
+            continue
+        first_pg, last_pg = tb[b] // PAGE, (te[b] - 1) // PAGE
+        for j in range(int(first_pg), int(last_pg) + 1):
+            phys = int(page_table[b, j])
+            rows = k_pages[phys]                      # [Hkv][16][128]
+            q = quantize_rows(rows)
+            lo = max(int(tb[b]) - j * PAGE, 0)
+            hi = min(int(te[b]) - j * PAGE, PAGE)
+            sl = slice(lo, hi)
+            k4[phys, :, sl] = q["packed"][:, sl]
+            meta[phys, :, sl, :, 0] = f16_bits(q["scale"][:, sl])
+            meta[phys, :, sl, :, 1] = f16_bits(q["zero"][:, sl])
+            tok_mask[phys, sl] = True
+            # bounds over the page's slots that hold tokens < tok_end
+            valid = min(int(te[b]) - j * PAGE, PAGE)
+            x = bf16_to_f32(rows[:, :valid, :])         # [Hkv][valid][128]
+            kb[phys, :, 0, :] = (x.min(axis=1).view(np.uint32) >> 16).astype(np.uint16)
+            kb[phys, :, 1, :] = (x.max(axis=1).view(np.uint32) >> 16).astype(np.uint16)
+            page_mask[phys] = True
+    return {"k4": k4, "k4_meta": meta, "kbound": kb, "tok_mask": tok_mask, "page_mask": page_mask}

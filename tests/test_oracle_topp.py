@@ -1,0 +1,132 @@
+"""Pins for O7 (minimal top-p set) and the model of its bisection search.
+
+* Brute force over every subset for n <= 14: the oracle's set has the minimal size among all sets
+  that reach p, and the largest mass among the minimal sets.
+* Closed forms from tests/golden/topp_closed_form.json (geometric and uniform weights, explicit
+  small vectors), one-hot weights, p = 1.
+* Invariants: monotone in p, permutation invariant.
+* The bisection on the uint32 image of float32 weights returns exactly the sort-based set (up to
+  ties) once converged, and a superset that still reaches p when stopped early.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import topp
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _brute(W, p):
+    n = len(W)
+    best_k, best_mass, best = None, -1.0, None
+    for k in range(0, n + 1):
+        for sub in itertools.combinations(range(n), k):
+            m = math.fsum(W[list(sub)])
+            if m >= p and (best_k is None or k < best_k or (k == best_k and m > best_mass)):
+                best_k, best_mass, best = k, m, sub
+        if best_k is not None:
+            break
+    return best_k, best_mass, best
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_brute_force_minimal_and_max_mass(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 15))
+    W = rng.dirichlet(np.full(n, rng.choice([0.2, 1.0, 5.0])))
+    p = float(rng.uniform(0.3, 0.99))
+    r = topp.topp_sort(W, p)
+    k, mass, _ = _brute(W, p)
+    assert r["k"] == k
+    assert math.isclose(r["mass"], mass, rel_tol=0, abs_tol=1e-15)
+    assert math.fsum(W[r["sel"]]) >= p
+
+
+def test_golden_closed_forms():
+    g = json.load(open(os.path.join(GOLD, "topp_closed_form.json")))
+    for c in g["geometric"]["cases"]:
+        n = c["n"]
+        W = 2.0 ** -np.arange(1, n + 1)
+        W = W / W.sum()
+        r = topp.topp_sort(W, c["p"])
+        assert r["k"] == c["k"], c
+        assert r["sel"].tolist() == list(range(c["k"]))
+    for c in g["uniform"]["cases"]:
+        W = np.full(c["n"], 1.0 / c["n"])
+        assert topp.topp_sort(W, c["p"])["k"] == c["k"], c
+    for c in g["explicit"]["cases"]:
+        assert topp.topp_sort(np.array(c["W"]), c["p"])["sel"].tolist() == c["sel"], c
+
+
+def test_one_hot_and_p_one():
+    W = np.zeros(50)
+    W[17] = 1.0
+    assert topp.topp_sort(W, 0.9)["sel"].tolist() == [17]
+    W = np.random.default_rng(0).dirichlet(np.ones(40))
+    assert topp.topp_sort(W, 1.0)["sel"].tolist() == list(range(40))
+    assert topp.topp_sort(np.zeros(0), 0.9)["k"] == 0
+
+
+def test_monotone_in_p_and_permutation_invariant():
+    rng = np.random.default_rng(4)
+    W = rng.dirichlet(np.full(300, 0.3))
+    prev = set()
+    for p in np.linspace(0.05, 0.99, 25):
+        cur = set(topp.topp_sort(W, p)["sel"].tolist())
+        assert prev <= cur
+        prev = cur
+    perm = rng.permutation(300)
+    a = topp.topp_sort(W, 0.85)["sel"]
+    b = topp.topp_sort(W[perm], 0.85)["sel"]
+    assert sorted(perm[b].tolist()) == a.tolist()
+
+
+def test_ambiguity_sets_cover_ties_and_cut():
+    W = np.array([0.4, 0.2, 0.2, 0.2])
+    r = topp.topp_sort(W, 0.55)          # 0.4 then one of three equal 0.2
+    assert r["sel"].tolist() == [0, 1]
+    assert set(r["amb_i"].tolist()) == {1, 2, 3}
+    ok, _ = topp.set_matches(np.array([0, 3]), r, W, 0.55)
+    assert ok
+    ok, _ = topp.set_matches(np.array([0]), r, W, 0.55)
+    assert not ok
+    W = np.array([0.5, 0.35, 0.15])
+    r = topp.topp_sort(W, 0.85)          # prefix mass 0.85 sits exactly at p: clause (ii)
+    assert 2 in r["amb_ii"].tolist()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_bisection_equals_sort_based_set(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 5000))
+    logits = rng.standard_normal(n) * rng.choice([0.05, 1.0, 3.0, 12.0])
+    w = np.exp(logits - logits.max()).astype(np.float32)        # float32 weights, max exactly 1
+    if seed % 3 == 0:
+        w[rng.integers(0, n, size=n // 4)] = w[0]                # many exact ties
+    p = float(rng.uniform(0.5, 0.99))
+    b = topp.topp_bisect(w, p, iters=32)
+    assert b["converged"]
+    W = w.astype(np.float64) / math.fsum(w.astype(np.float64))
+    r = topp.topp_sort(W, p)
+    # the search returns every token at or above the exact threshold weight w_(k*)
+    thr = np.float32(w[r["order"][r["k"] - 1]])
+    assert b["threshold"] == thr
+    ok, msg = topp.set_matches(b["sel"], r, W, p)
+    assert ok, msg
+
+
+def test_bisection_stopped_early_is_a_superset_reaching_p():
+    rng = np.random.default_rng(9)
+    w = np.exp(rng.standard_normal(4000) * 2).astype(np.float32)
+    full = topp.topp_bisect(w, 0.9, iters=64)
+    for it in (1, 4, 10, 20):
+        b = topp.topp_bisect(w, 0.9, iters=it)
+        assert set(full["sel"].tolist()) <= set(b["sel"].tolist())
+        assert math.fsum(w[b["sel"]].astype(np.float64)) >= 0.9 * math.fsum(w.astype(np.float64))
+    assert full["steps"] <= 31
