@@ -73,6 +73,8 @@ def set_matches(gpu_sel: np.ndarray, res: dict, W: np.ndarray, p: float) -> tupl
     """Parity rule: the symmetric difference lies inside the ambiguity sets and the GPU set's mass
     (under ``W``) reaches p - TAU_P."""
     g = np.unique(np.asarray(gpu_sel, np.int64))
+    if np.asarray(W).size == 0:  # no candidates: the empty set is the only subset
+        return (g.size == 0), "empty candidate list"
     o = res["sel"]
     diff = np.setxor1d(g, o)
     allowed = np.union1d(res["amb_i"], res["amb_ii"])

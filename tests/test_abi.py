@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every symbol the header
+declares, and rejects invalid arguments with the documented status before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def twl():
+    import top_sparse_attention_int4_amd as t
+    if not os.path.exists(t.LIB_PATH):
+        from top_sparse_attention_int4_amd import build
+        build.build()
+    t.lib()
+    return t
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "twl.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:twl_status|size_t|const char\*)\s+(twl_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["twl_quantize_k", "twl_select_pages", "twl_estimate_topp", "twl_sparse_attn", "twl_decode",
+              "twl_decode_profiled", "twl_select_clusters_topp", "twl_workspace_bytes", "twl_status_str"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(twl):
+    L = twl.lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def _fake_cache(twl, **kw):
+    fake = ctypes.c_void_p(0x10000)
+    c = twl.CacheC(1, 32, 8, 128, 16, 32, 2048, 2048, 32768, fake, fake, fake, fake, fake, fake, fake)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_status_strings(twl):
+    for s in range(5):
+        assert twl.status_str(s).startswith("TWL_")
+    assert "gfx950" in twl.version()
+
+
+def test_workspace_bytes(twl):
+    L = twl.lib()
+    c = _fake_cache(twl)
+    a = L.twl_workspace_bytes(ctypes.byref(c), 8192)
+    b = L.twl_workspace_bytes(ctypes.byref(c), 32768)
+    assert 0 < a < b
+    assert a % 256 == 0
+    assert L.twl_workspace_bytes(None, 8192) == 0
+    bad = _fake_cache(twl, head_dim=64)
+    assert L.twl_workspace_bytes(ctypes.byref(bad), 8192) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, 2), ("page_size", 32, 2), ("quant_group", 64, 2), ("num_kv_heads", 5, 1),
+    ("num_kv_heads", 2, 2), ("batch", 0, 1), ("max_seq_len", 2048 * 16 + 1, 1), ("page_table", None, 1),
+])
+def test_decode_rejects_bad_cache(twl, field, value, status):
+    L = twl.lib()
+    c = _fake_cache(twl, **{field: value})
+    prm = twl.ParamsC(0.85, 0.25, 0.088, 32)
+    fake = ctypes.c_void_p(0x10000)
+    st = L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, None, None, 0, fake, 1 << 40, None)
+    assert st == status
+
+
+@pytest.mark.parametrize("p,kf,iters,status", [
+    (0.0, 0.25, 32, 1), (1.5, 0.25, 32, 1), (float("nan"), 0.25, 32, 1), (0.85, 0.0, 32, 1),
+    (0.85, float("inf"), 32, 1), (0.85, 0.25, 0, 1), (0.85, 0.25, 65, 1),
+])
+def test_decode_rejects_bad_params(twl, p, kf, iters, status):
+    L = twl.lib()
+    c = _fake_cache(twl)
+    prm = twl.ParamsC(p, kf, 0.088, iters)
+    fake = ctypes.c_void_p(0x10000)
+    st = L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, None, None, 0, fake, 1 << 40, None)
+    assert st == status
+
+
+def test_workspace_and_capacity_checks(twl):
+    L = twl.lib()
+    c = _fake_cache(twl)
+    prm = twl.ParamsC(0.85, 0.25, 0.088, 32)
+    fake = ctypes.c_void_p(0x10000)
+    need = L.twl_workspace_bytes(ctypes.byref(c), 16 * 512)
+    # too small, NULL, misaligned workspace
+    assert L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, None, None, 0, fake, need - 1, None) == 3
+    assert L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, None, None, 0, None, need, None) == 3
+    assert L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, None, None, 0,
+                        ctypes.c_void_p(0x10010), need, None) == 3
+    # CSR outputs need both pointers and enough capacity
+    assert L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, fake, None, 0, fake, need, None) == 1
+    assert L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, fake, fake, 8 * 8192 - 1, fake,
+                        need, None) == 1
+
+
+def test_split_entry_points_validate(twl):
+    L = twl.lib()
+    c = _fake_cache(twl)
+    fake = ctypes.c_void_p(0x10000)
+    assert L.twl_quantize_k(ctypes.byref(c), None, fake, 16, None) == 1
+    assert L.twl_quantize_k(ctypes.byref(c), fake, fake, -1, None) == 1
+    assert L.twl_select_pages(ctypes.byref(c), fake, 0.25, 511, fake, fake, fake, 1 << 40, None) == 1  # needs 512
+    cand = twl.CandC(fake, fake, fake, 4)  # both pages and ranges
+    assert L.twl_estimate_topp(ctypes.byref(c), fake, 0.088, 0.9, 32, ctypes.byref(cand), fake, None, None, 0,
+                               fake, fake, 1 << 30, fake, 1 << 40, None) == 1
+    cand = twl.CandC(fake, None, None, 4)  # count missing
+    assert L.twl_estimate_topp(ctypes.byref(c), fake, 0.088, 0.9, 32, ctypes.byref(cand), fake, None, None, 0,
+                               fake, fake, 1 << 30, fake, 1 << 40, None) == 1
+    assert L.twl_sparse_attn(ctypes.byref(c), fake, 0.088, fake, fake, -1, fake, None, fake, 1 << 40, None) == 1
+    assert L.twl_select_clusters_topp(ctypes.byref(c), fake, 0.088, 0.0, 32, fake, fake, fake, 64, fake, fake,
+                                      fake, 1 << 40, None) == 1

@@ -130,3 +130,9 @@ def test_bisection_stopped_early_is_a_superset_reaching_p():
         assert set(full["sel"].tolist()) <= set(b["sel"].tolist())
         assert math.fsum(w[b["sel"]].astype(np.float64)) >= 0.9 * math.fsum(w.astype(np.float64))
     assert full["steps"] <= 31
+
+
+def test_set_rule_on_empty_candidates():
+    r = topp.topp_sort(np.zeros(0), 0.9)
+    assert topp.set_matches(np.zeros(0, np.int64), r, np.zeros(0), 0.9)[0]
+    assert not topp.set_matches(np.array([0]), r, np.zeros(0), 0.9)[0]

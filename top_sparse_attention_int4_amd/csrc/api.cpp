@@ -1,0 +1,405 @@
+// C ABI of libtwl: host-side validation, workspace carving and kernel orchestration.
+//
+// Every entry point validates its arguments before its first HIP call, then checks that the
+// current device is gfx950, carves the caller's workspace and enqueues the kernels on the caller's
+// stream.  Nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "twl.h"
+#include "twl_internal.h"
+
+namespace {
+
+using namespace twl;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// ---- argument validation (host only, no HIP calls) -------------------------------------------------
+twl_status check_cache(const twl_cache* c, bool need_kv, bool need_quant) {
+  if (!c) return TWL_EINVAL;
+  if (c->batch < 1 || c->num_q_heads < 1 || c->num_kv_heads < 1) return TWL_EINVAL;
+  if (c->num_q_heads % c->num_kv_heads) return TWL_EINVAL;
+  const int G = c->num_q_heads / c->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return TWL_EUNSUPPORTED;
+  if (c->head_dim != 128 || c->page_size != 16 || c->quant_group != 32) return TWL_EUNSUPPORTED;
+  if (c->max_pages_per_seq < 1 || c->num_phys_pages < 1) return TWL_EINVAL;
+  if (c->max_seq_len < 0 || (int64_t)c->max_seq_len > 16 * (int64_t)c->max_pages_per_seq) return TWL_EINVAL;
+  if ((int64_t)c->num_phys_pages * c->num_kv_heads * 16 >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
+  if ((int64_t)c->batch * c->max_pages_per_seq >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
+  if ((int64_t)c->batch * c->num_kv_heads > 65535) return TWL_EUNSUPPORTED;
+  if (!c->page_table || !c->seq_lens) return TWL_EINVAL;
+  if (need_kv && (!c->k || !c->v)) return TWL_EINVAL;
+  if (need_quant && (!c->k4 || !c->k4_meta || !c->kbound)) return TWL_EINVAL;
+  return TWL_OK;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+// Kept-page count bound for the longest sequence (matches the device computation).
+int keep_count(int P, float keep_frac) {
+  if (P <= 0) return 0;
+  float kf = std::ceil(std::fmin(keep_frac * (float)P, (float)P));
+  int k = (int)kf;
+  return k < 1 ? 1 : (k > P ? P : k);
+}
+
+// ---- device check (first HIP call of an entry point) ------------------------------------------------
+twl_status check_device() {
+  static std::atomic<int> state[64];  // 0 unknown, 1 gfx950, 2 other
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TWL_EHIP;
+  if (dev >= 0 && dev < 64) {
+    const int s = state[dev].load(std::memory_order_relaxed);
+    if (s == 1) return TWL_OK;
+    if (s == 2) return TWL_EUNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TWL_EHIP;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? TWL_OK : TWL_EUNSUPPORTED;
+}
+
+CacheView make_view(const twl_cache* c) {
+  CacheView v;
+  v.B = c->batch;
+  v.Hq = c->num_q_heads;
+  v.Hkv = c->num_kv_heads;
+  v.G = c->num_q_heads / c->num_kv_heads;
+  v.maxP = c->max_pages_per_seq;
+  v.nphys = c->num_phys_pages;
+  v.maxTok = c->max_pages_per_seq * 16;
+  v.page_table = c->page_table;
+  v.seq_lens = c->seq_lens;
+  v.k = static_cast<const uint16_t*>(c->k);
+  v.v = static_cast<const uint16_t*>(c->v);
+  v.k4 = static_cast<uint8_t*>(c->k4);
+  v.k4_meta = static_cast<uint32_t*>(c->k4_meta);
+  v.kbound = static_cast<uint16_t*>(c->kbound);
+  return v;
+}
+
+// ---- workspace layout ----------------------------------------------------------------------------------
+struct Layout {
+  int64_t ncap = 0;       // candidate capacity per unit (multiple of 1024)
+  int chunk_tokens = 64;  // attention chunk
+  int64_t max_chunks = 0;
+  size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, logits = 0, masks = 0, utok = 0, ucnt = 0, counters = 0,
+         parts = 0, thr = 0, total = 0;
+};
+
+// ncap_of(maxcand): the top-p block holds 1024*E candidates, E a power of two up to 64.
+int64_t ncap_of(int64_t maxcand) {
+  const int E = topp_elems_per_thread(maxcand < 1 ? 1 : maxcand);
+  return E ? (int64_t)E * kToppThreads : 0;
+}
+
+bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
+  const int64_t U = (int64_t)c->batch * c->num_kv_heads;
+  const int64_t BH = (int64_t)c->batch * c->num_q_heads;
+  const int G = c->num_q_heads / c->num_kv_heads;
+  L->ncap = ncap;
+  L->chunk_tokens = attn_chunk_tokens(U * ncap);
+  L->max_chunks = U * ((ncap + L->chunk_tokens - 1) / L->chunk_tokens);
+  if (L->max_chunks < 1) L->max_chunks = 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L->scores = take((size_t)U * c->max_pages_per_seq * 4);
+  L->pages = take((size_t)U * c->max_pages_per_seq * 4);
+  L->pcnt = take((size_t)U * 4);
+  L->rpre = take((size_t)U * (ncap + 1) * 4);
+  L->logits = take((size_t)BH * ncap * 4);
+  L->masks = take((size_t)BH * (ncap / 32) * 4);
+  L->utok = take((size_t)U * ncap * 4);
+  L->ucnt = take((size_t)U * 4);
+  L->counters = take((size_t)U * 4);
+  L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
+  L->thr = take((size_t)BH * 4);
+  L->total = off;
+  return true;
+}
+
+twl_status check_ws(const void* ws, size_t ws_bytes, const Layout& L) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1))) return TWL_EWORKSPACE;
+  if (ws_bytes < L.total) return TWL_EWORKSPACE;
+  return TWL_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+twl_status hip_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_EHIP; }
+
+#define TWL_TRY(expr)                          \
+  do {                                         \
+    const hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return TWL_EHIP;     \
+  } while (0)
+
+// Event hook for profiled runs.
+struct Events {
+  void* const* ev = nullptr;
+  hipStream_t s = nullptr;
+  hipError_t rec(int i) const {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  }
+};
+
+twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_params* prm, float* out,
+                       float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
+                       void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  twl_status st = check_cache(cache, true, true);
+  if (st != TWL_OK) return st;
+  if (!q || !prm || !out) return TWL_EINVAL;
+  if (!finite(prm->p) || !(prm->p > 0.f) || prm->p > 1.f) return TWL_EINVAL;
+  if (!finite(prm->keep_frac) || !(prm->keep_frac > 0.f)) return TWL_EINVAL;
+  if (!finite(prm->sm_scale)) return TWL_EINVAL;
+  if (prm->iters < 1 || prm->iters > 64) return TWL_EINVAL;
+  if ((sel_indptr == nullptr) != (sel_tokens == nullptr)) return TWL_EINVAL;
+  const bool selector = prm->keep_frac < 1.0f;
+  const int64_t U = (int64_t)cache->batch * cache->num_kv_heads;
+  const int max_keep = keep_count(cache->max_pages_per_seq, prm->keep_frac);
+  const int64_t maxcand = selector ? 16 * (int64_t)max_keep : (int64_t)cache->max_seq_len;
+  if (sel_tokens && capacity < U * maxcand) return TWL_EINVAL;
+  const int64_t ncap = ncap_of(maxcand);
+  if (ncap == 0) return TWL_EUNSUPPORTED;
+  Layout L;
+  make_layout(cache, ncap, &L);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != TWL_OK) return st;
+  if (events) {
+    for (int i = 0; i < 2 * TWL_NUM_STAGES; ++i)
+      if (!events[i]) return TWL_EINVAL;
+  }
+  // ---- enqueue ----
+  st = check_device();
+  if (st != TWL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Events E{events, s};
+  const CacheView c = make_view(cache);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+
+  CandView cand{};
+  if (selector) {
+    TWL_TRY(E.rec(0));
+    TWL_TRY(launch_page_score(c, qb, at<float>(ws, L.scores), s));
+    TWL_TRY(E.rec(1));
+    TWL_TRY(E.rec(2));
+    TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), prm->keep_frac, cache->max_pages_per_seq,
+                               at<int32_t>(ws, L.pages), at<int32_t>(ws, L.pcnt), s));
+    TWL_TRY(E.rec(3));
+    cand.mode = kCandPages;
+    cand.items = at<int32_t>(ws, L.pages);
+    cand.count = at<int32_t>(ws, L.pcnt);
+    cand.max_items = cache->max_pages_per_seq;
+  } else {
+    for (int i = 0; i < 4; ++i) TWL_TRY(E.rec(i));
+    cand.mode = kCandAll;
+  }
+  float* thr = threshold ? threshold : at<float>(ws, L.thr);
+  TWL_TRY(E.rec(4));
+  TWL_TRY(launch_estimate(c, qb, prm->sm_scale, cand, (int)ncap, at<float>(ws, L.logits),
+                          at<int32_t>(ws, L.counters), s));
+  TWL_TRY(E.rec(5));
+  TWL_TRY(E.rec(6));
+  TWL_TRY(launch_topp(c, cand, at<float>(ws, L.logits), (int)ncap, prm->p, prm->iters, thr, nullptr,
+                      at<uint32_t>(ws, L.masks), nullptr, 0, at<int32_t>(ws, L.counters),
+                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), s));
+  TWL_TRY(E.rec(7));
+  ListView lv{at<int32_t>(ws, L.utok), nullptr, at<int32_t>(ws, L.ucnt), ncap};
+  TWL_TRY(E.rec(8));
+  TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
+                      sel_tokens, capacity, s));
+  TWL_TRY(E.rec(9));
+  TWL_TRY(E.rec(10));
+  TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));
+  TWL_TRY(E.rec(11));
+  return TWL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t twl_workspace_bytes(const twl_cache* cache, int64_t max_candidates_per_group) {
+  if (check_cache(cache, false, false) != TWL_OK || max_candidates_per_group < 0) return 0;
+  int64_t ncap = ncap_of(max_candidates_per_group);
+  if (ncap == 0) ncap = ((max_candidates_per_group + 1023) / 1024) * 1024;
+  Layout L;
+  make_layout(cache, ncap, &L);
+  return L.total;
+}
+
+twl_status twl_quantize_k(const twl_cache* cache, const int32_t* tok_begin, const int32_t* tok_end,
+                          int32_t max_span, void* stream) {
+  twl_status st = check_cache(cache, true, true);
+  if (st != TWL_OK) return st;
+  if (!tok_begin || !tok_end) return TWL_EINVAL;
+  if (max_span < 0 || (int64_t)max_span > 16 * (int64_t)cache->max_pages_per_seq) return TWL_EINVAL;
+  st = check_device();
+  if (st != TWL_OK) return st;
+  int span_pages = max_span == 0 ? 0 : (max_span + 15) / 16 + 1;
+  if (span_pages > cache->max_pages_per_seq) span_pages = cache->max_pages_per_seq;
+  return hip_status(launch_quantize(make_view(cache), tok_begin, tok_end, span_pages, static_cast<hipStream_t>(stream)));
+}
+
+twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_frac, int32_t max_keep,
+                            int32_t* page_ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  twl_status st = check_cache(cache, false, true);
+  if (st != TWL_OK) return st;
+  if (!q || !page_ids || !count) return TWL_EINVAL;
+  if (!finite(keep_frac) || !(keep_frac > 0.f)) return TWL_EINVAL;
+  if (max_keep < keep_count(cache->max_pages_per_seq, keep_frac)) return TWL_EINVAL;
+  Layout L;
+  make_layout(cache, kToppThreads, &L);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != TWL_OK) return st;
+  st = check_device();
+  if (st != TWL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const CacheView c = make_view(cache);
+  TWL_TRY(launch_page_score(c, static_cast<const uint16_t*>(q), at<float>(ws, L.scores), s));
+  TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), keep_frac, max_keep, page_ids, count, s));
+  return TWL_OK;
+}
+
+twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_scale, float p, int32_t iters,
+                             const twl_candidates* cand, float* threshold, float* mass, uint32_t* head_mask,
+                             int32_t mask_words, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
+                             void* ws, size_t ws_bytes, void* stream) {
+  twl_status st = check_cache(cache, false, true);
+  if (st != TWL_OK) return st;
+  if (!q || !cand || !threshold || !sel_indptr || !sel_tokens) return TWL_EINVAL;
+  if (!finite(p) || !(p > 0.f) || p > 1.f) return TWL_EINVAL;
+  if (!finite(sm_scale)) return TWL_EINVAL;
+  if (iters < 1 || iters > 64) return TWL_EINVAL;
+  if (cand->page_ids && cand->ranges) return TWL_EINVAL;
+  const int64_t U = (int64_t)cache->batch * cache->num_kv_heads;
+  CandView cv{};
+  int64_t maxcand;
+  if (cand->page_ids || cand->ranges) {
+    if (!cand->count || cand->max_items < 1) return TWL_EINVAL;
+  }
+  if (cand->page_ids) {
+    if (cand->max_items > cache->max_pages_per_seq) return TWL_EINVAL;
+    cv.mode = kCandPages;
+    cv.items = cand->page_ids;
+    maxcand = 16 * (int64_t)cand->max_items;
+  } else if (cand->ranges) {
+    cv.mode = kCandRanges;
+    cv.items = cand->ranges;
+    maxcand = cache->max_seq_len;
+  } else {
+    cv.mode = kCandAll;
+    maxcand = cache->max_seq_len;
+  }
+  cv.count = cand->count;
+  cv.max_items = cand->max_items;
+  if (capacity < U * maxcand) return TWL_EINVAL;
+  if (head_mask && (int64_t)mask_words * 32 < maxcand) return TWL_EINVAL;
+  const int64_t ncap = ncap_of(maxcand);
+  if (ncap == 0) return TWL_EUNSUPPORTED;
+  if (cv.mode == kCandRanges && cand->max_items > ncap) return TWL_EINVAL;
+  Layout L;
+  make_layout(cache, ncap, &L);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != TWL_OK) return st;
+  st = check_device();
+  if (st != TWL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const CacheView c = make_view(cache);
+  if (cv.mode == kCandRanges) {
+    cv.range_prefix = at<int32_t>(ws, L.rpre);
+    TWL_TRY(launch_range_prefix(c, cv, at<int32_t>(ws, L.rpre), s));
+  }
+  TWL_TRY(launch_estimate(c, static_cast<const uint16_t*>(q), sm_scale, cv, (int)ncap, at<float>(ws, L.logits),
+                          at<int32_t>(ws, L.counters), s));
+  TWL_TRY(launch_topp(c, cv, at<float>(ws, L.logits), (int)ncap, p, iters, threshold, mass,
+                      at<uint32_t>(ws, L.masks), head_mask, mask_words, at<int32_t>(ws, L.counters),
+                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), s));
+  TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
+                          capacity, s));
+  return TWL_OK;
+}
+
+twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale, const int32_t* sel_indptr,
+                           const int32_t* sel_tokens, int32_t max_selected_per_group, float* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream) {
+  twl_status st = check_cache(cache, true, false);
+  if (st != TWL_OK) return st;
+  if (!q || !sel_indptr || !sel_tokens || !out) return TWL_EINVAL;
+  if (!finite(sm_scale)) return TWL_EINVAL;
+  if (max_selected_per_group < 0) return TWL_EINVAL;
+  int64_t ncap = ncap_of(max_selected_per_group);
+  if (ncap == 0) ncap = (((int64_t)max_selected_per_group + 1023) / 1024) * 1024;
+  Layout L;
+  make_layout(cache, ncap, &L);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != TWL_OK) return st;
+  st = check_device();
+  if (st != TWL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const CacheView c = make_view(cache);
+  ListView lv{sel_tokens, sel_indptr, nullptr, 0};
+  TWL_TRY(launch_attn(c, static_cast<const uint16_t*>(q), sm_scale, lv, L.chunk_tokens, L.max_chunks,
+                      at<float>(ws, L.parts), nullptr, nullptr, 0, s));
+  TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));
+  return TWL_OK;
+}
+
+twl_status twl_decode(const twl_cache* cache, const void* q, const twl_decode_params* params, float* out,
+                      float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
+                      void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(cache, q, params, out, lse, threshold, sel_indptr, sel_tokens, capacity, ws, ws_bytes,
+                     stream, nullptr);
+}
+
+twl_status twl_decode_profiled(const twl_cache* cache, const void* q, const twl_decode_params* params,
+                               float* out, float* lse, float* threshold, int32_t* sel_indptr,
+                               int32_t* sel_tokens, int64_t capacity, void* ws, size_t ws_bytes,
+                               void* stream, void* const* events) {
+  if (!events) return TWL_EINVAL;
+  return decode_impl(cache, q, params, out, lse, threshold, sel_indptr, sel_tokens, capacity, ws, ws_bytes,
+                     stream, events);
+}
+
+twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float sm_scale, float p1,
+                                    int32_t iters, const void* centroids, const int32_t* csize,
+                                    const int32_t* coff, int32_t num_clusters, int32_t* ranges,
+                                    int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  twl_status st = check_cache(cache, false, false);
+  if (st != TWL_OK) return st;
+  if (!q || !centroids || !csize || !coff || !ranges || !count) return TWL_EINVAL;
+  if (!finite(p1) || !(p1 > 0.f) || p1 > 1.f || !finite(sm_scale)) return TWL_EINVAL;
+  if (iters < 1 || iters > 64 || num_clusters < 1) return TWL_EINVAL;
+  (void)ws;
+  (void)ws_bytes;
+  (void)stream;
+  return TWL_EUNSUPPORTED;
+}
+
+const char* twl_status_str(twl_status status) {
+  switch (status) {
+    case TWL_OK: return "TWL_OK: success";
+    case TWL_EINVAL: return "TWL_EINVAL: invalid argument";
+    case TWL_EUNSUPPORTED: return "TWL_EUNSUPPORTED: unsupported shape or device (needs gfx950, head_dim 128, page 16, group 32, G in {1,2,4,8})";
+    case TWL_EWORKSPACE: return "TWL_EWORKSPACE: workspace missing, misaligned or too small";
+    case TWL_EHIP: return "TWL_EHIP: HIP launch failed";
+  }
+  return "unknown twl_status";
+}
+
+const char* twl_version(void) { return "twl 0.1.0 (gfx950)"; }
+
+}  // extern "C"

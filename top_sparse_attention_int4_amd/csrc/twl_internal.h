@@ -1,0 +1,70 @@
+// Internal declarations shared by the HIP translation units of libtwl (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace twl {
+
+constexpr int kD = 128;     // head dim
+constexpr int kPage = 16;   // tokens per page
+constexpr int kGroups = 4;  // 32-channel quantisation groups per key row
+
+// Device-side view of the paged cache (plain values, passed by value to kernels).
+struct CacheView {
+  int B, Hq, Hkv, G, maxP, nphys, maxTok;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint8_t* k4;
+  uint32_t* k4_meta;  // per (row, group): scale bits | zero bits << 16
+  uint16_t* kbound;
+};
+
+// Candidate enumeration of a unit (b, kv-head).
+enum CandMode : int { kCandAll = 0, kCandPages = 1, kCandRanges = 2 };
+struct CandView {
+  int mode;
+  const int32_t* items;         // page ids [U][max_items] or ranges [U][max_items][2]
+  const int32_t* count;         // [U]
+  const int32_t* range_prefix;  // [U][max_items+1] (ranges only; written by launch_range_prefix)
+  int max_items;
+};
+
+// Token list of each unit for the attention stage: either padded rows (stride) with counts, or CSR.
+struct ListView {
+  const int32_t* tokens;
+  const int32_t* indptr;  // [U+1] when CSR, else nullptr
+  const int32_t* counts;  // [U] when padded, else nullptr
+  int64_t stride;         // row stride when padded
+};
+
+// ---- launchers (each returns the launch status) --------------------------------------------------
+hipError_t launch_quantize(const CacheView& c, const int32_t* tok_begin, const int32_t* tok_end,
+                           int span_pages, hipStream_t s);
+hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* scores, hipStream_t s);
+hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep,
+                              int32_t* page_ids, int32_t* count, hipStream_t s);
+hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, hipStream_t s);
+hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
+                           float* logits, int32_t* counters, hipStream_t s);
+hipError_t launch_topp(const CacheView& c, const CandView& cand, const float* logits, int ncap, float p,
+                       int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
+                       int mask_words, int32_t* counters, int32_t* union_tok, int32_t* union_cnt,
+                       hipStream_t s);
+hipError_t launch_csr_emit(const CacheView& c, const int32_t* union_tok, const int32_t* union_cnt, int ncap,
+                           int32_t* indptr, int32_t* tokens, int64_t capacity, hipStream_t s);
+// tokens per attention chunk for an upper bound of the total selected tokens
+int attn_chunk_tokens(int64_t total_upper);
+hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
+                       int64_t max_chunks, float* partials, int32_t* csr_indptr, int32_t* csr_tokens,
+                       int64_t capacity, hipStream_t s);
+hipError_t launch_merge(const CacheView& c, const ListView& list, int chunk_tokens, int64_t max_chunks,
+                        const float* partials, float* out, float* lse, hipStream_t s);
+constexpr int kPartFloats = 2 + kD;  // per (chunk, head): max, sum, output row
+// elements per thread of the top-p block for a candidate capacity (0 = unsupported)
+int topp_elems_per_thread(int64_t ncap);
+constexpr int kToppThreads = 1024;
+
+}  // namespace twl
