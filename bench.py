@@ -1,0 +1,222 @@
+"""Benchmark: one decode layer-step of top-p sparse attention with an INT4 K estimate, on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload C2] [--layers L] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch: Quest-style page selection -> INT4 weight
+estimate -> per-head top-p (bisection) -> GQA union -> split-K sparse attention -> merge.  Steps
+rotate over L independently drawn layer caches of identical shape whose footprint exceeds 1 GiB, so
+every step reads cold HBM rather than the 256 MB Infinity Cache.  Inputs are resident in HBM before
+timing starts.
+
+Prints ONE JSON line.  ``value`` is microseconds per layer-step (lower is better).  ``roofline``
+describes the split-K attention kernel (the stage that moves most bytes): its algorithmic bytes per
+launch (512 B of K/V rows + 4 B index per kept token, plus the group's q) over its average launch
+duration, measured with HIP events around that kernel in a second timed pass.  ``cpu_baseline`` times
+the numpy oracle on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode attention µs/layer-step + HBM GB/s fraction, 32K–256K ctx"
+HBM_PEAK = 8.0e12  # MI355X HBM3E, bytes/s
+DESCR = {
+    "C1": "single MHA head, n=4096, no selector, p=0.9",
+    "C2": "Llama-3-8B-shaped decode layer: B=1, 32/8 GQA heads, n=32768, 4 K outlier channels, keep 1/4 pages, p=0.85",
+    "C3": "head heterogeneity: B=16, 32/8 heads, n=32768, per-head temperature, keep 1/4, p=0.85",
+    "C4": "long context: B=4, 32/8 heads, n=131072, 64 planted keys per head, keep 1/4, p=0.9",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C2", choices=sorted(DESCR))
+    ap.add_argument("--layers", type=int, default=0, help="distinct layer caches (0: enough for >= 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: auto)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "top_sparse_attention_int4_amd", "csrc")
+    for f in sorted(os.listdir(cdir)):
+        with open(os.path.join(cdir, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the path shards over (batch, kv-head) units "
+              "with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import top_sparse_attention_int4_amd as twl
+    from gen import make_config
+    from gen.device import upload
+
+    if not os.path.exists(twl.LIB_PATH):
+        from top_sparse_attention_int4_amd import build as b
+        b.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- layers ----------------------------------------------------------------------------------
+    w0 = make_config(args.workload, layer=0)
+    per_layer = 2.35 * w0.k_pages.nbytes  # K + V + INT4 codes + scale/zero + page bounds
+    L = args.layers or max(1, math.ceil((1 << 30) / per_layer))
+    print(f"[bench] {args.workload}: {L} layer(s), {per_layer / 1e6:.0f} MB each", file=sys.stderr, flush=True)
+    layers = []
+    for li in range(L):
+        w = w0 if li == 0 else make_config(args.workload, layer=li)
+        t = upload(w, dev)
+        cache = twl.PagedCache(t["k_pages"], t["v_pages"], t["page_table"], t["seq_lens"], w.num_q_heads,
+                               max_seq_len=w.max_seq_len)
+        twl.quantize_k(cache, torch.zeros(w.batch, dtype=torch.int32, device=dev), t["seq_lens"], w.max_seq_len)
+        layers.append((w, cache, t))
+    torch.cuda.synchronize()
+    w = w0
+    B, Hq, Hkv, G = w.batch, w.num_q_heads, w.num_kv_heads, w.group
+    U = B * Hkv
+    kf, p = w.keep_frac, w.p
+    selector = kf < 1.0
+    maxcand = 16 * twl.keep_count(w.max_pages, kf) if selector else w.max_seq_len
+    ws = torch.empty(twl.workspace_bytes(layers[0][1], maxcand), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), device=dev)
+    lse = torch.empty((B, Hq), device=dev)
+    thr = torch.empty((B, Hq), device=dev)
+    indptrs = [torch.zeros(U + 1, dtype=torch.int32, device=dev) for _ in range(L)]
+    toks = torch.empty(U * maxcand, dtype=torch.int32, device=dev)
+
+    def step(i):
+        _, cache, t = layers[i % L]
+        twl.decode(cache, t["q"], p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
+                   sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # ---- timed region: K plain steps -------------------------------------------------------------
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- second timed pass: HIP events around every stage kernel ---------------------------------
+    nev = 2 * twl.NUM_STAGES
+    stage_ms = np.zeros(twl.NUM_STAGES)
+    kept = []
+    K2 = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(K2)]
+    torch.cuda.synchronize()
+    for i in range(K2):
+        _, cache, t = layers[i % L]
+        twl.decode_profiled(cache, t["q"], evs[i], p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
+                            sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
+    torch.cuda.synchronize()
+    for i in range(K2):
+        for s in range(twl.NUM_STAGES):
+            stage_ms[s] += evs[i][2 * s].elapsed_time(evs[i][2 * s + 1])
+    stage_ms /= K2
+    for li in range(L):
+        kept.append(indptrs[li].cpu().numpy())
+
+    # ---- algorithmic bytes (per layer-step, averaged over the layers) ----------------------------
+    seq = w.seq_lens.astype(np.int64)
+    pages = -(-seq // 16)
+    cand = np.array([min(16 * twl.keep_count(int(P), kf), int(n)) if selector else int(n)
+                     for P, n in zip(pages, seq)])  # valid candidates per sequence (upper bound)
+    sel_tokens_total = float(np.mean([ip[-1] for ip in kept]))
+    q_bytes = 2 * Hq * 128
+    bytes_sel = (512 * pages.sum() * Hkv) if selector else 0
+    bytes_est = 80 * cand.sum() * Hkv
+    bytes_attn = 516 * sel_tokens_total + q_bytes
+    bytes_step = bytes_sel + bytes_est + bytes_attn + 4 * Hq * 128 + q_bytes
+    attn_ms = stage_ms[4]
+    achieved = bytes_attn / (attn_ms * 1e-3)
+
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", f"traffic_attn_splitk_{args.workload}.json")
+    if os.path.exists(prof):
+        with open(prof) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {DESCR[args.workload]}", "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "context": int(seq.max()), "p": p, "keep_frac": kf,
+                   "layers_rotated": L, "parallelism": "single GPU"},
+        "hbm": {"algorithmic_bytes_per_step": int(bytes_step), "gbps": round(bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+                "frac_of_8TBps": round(bytes_step / (ms_per_step * 1e-3) / HBM_PEAK, 4),
+                "kept_tokens_per_step": sel_tokens_total},
+        "stages_us": {n: round(float(x) * 1e3, 3) for n, x in zip(twl.STAGE_NAMES, stage_ms)},
+        "roofline": {"kernel": "k_attn (split-K sparse attention)", "bound": "hbm",
+                     "achieved": round(achieved / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(bytes_attn), "avg_launch_us": round(attn_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, units: int):
+    """The numpy oracle (as it stands) on a bounded sample of the workload's (sequence, kv-head)
+    units; scaled to microseconds per whole layer-step."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pipeline
+    U = w.batch * w.num_kv_heads
+    sample = [(u // w.num_kv_heads, u % w.num_kv_heads) for u in range(U)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        pipeline.decode(w, units=sample[:1])
+        one = time.perf_counter() - t0
+        n = units or max(1, min(U, int(20.0 / max(one, 1e-3))))
+        t0 = time.perf_counter()
+        pipeline.decode(w, units=sample[:n])
+        dt = time.perf_counter() - t0
+    per_step = dt / n * U
+    return {"value": round(per_step * 1e6, 1), "unit": "us/layer-step", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {U} (sequence, kv-head) units of one layer-step, numpy float64 oracle, "
+                      f"{dt:.1f} s, scaled by {U}/{n}"}
+
+
+if __name__ == "__main__":
+    main()

@@ -89,8 +89,8 @@ struct Layout {
   int64_t ncap = 0;       // candidate capacity per unit (multiple of 1024)
   int chunk_tokens = 64;  // attention chunk
   int64_t max_chunks = 0;
-  size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, logits = 0, masks = 0, utok = 0, ucnt = 0, counters = 0,
-         parts = 0, thr = 0, total = 0;
+  size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, logits = 0, masks = 0, utok = 0, urow = 0, ucnt = 0,
+         counters = 0, parts = 0, thr = 0, total = 0;
 };
 
 // ncap_of(maxcand): the top-p block holds 1024*E candidates, E a power of two up to 64.
@@ -120,6 +120,7 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->logits = take((size_t)BH * ncap * 4);
   L->masks = take((size_t)BH * (ncap / 32) * 4);
   L->utok = take((size_t)U * ncap * 4);
+  L->urow = take((size_t)U * ncap * 4);
   L->ucnt = take((size_t)U * 4);
   L->counters = take((size_t)U * 4);
   L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
@@ -214,10 +215,10 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
   TWL_TRY(E.rec(5));
   TWL_TRY(E.rec(6));
   TWL_TRY(launch_topp(c, cand, at<float>(ws, L.logits), (int)ncap, prm->p, prm->iters, thr, nullptr,
-                      at<uint32_t>(ws, L.masks), nullptr, 0, at<int32_t>(ws, L.counters),
-                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), s));
+                      at<uint32_t>(ws, L.masks), nullptr, 0,
+                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s));
   TWL_TRY(E.rec(7));
-  ListView lv{at<int32_t>(ws, L.utok), nullptr, at<int32_t>(ws, L.ucnt), ncap};
+  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap};
   TWL_TRY(E.rec(8));
   TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
                       sel_tokens, capacity, s));
@@ -326,8 +327,8 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
   TWL_TRY(launch_estimate(c, static_cast<const uint16_t*>(q), sm_scale, cv, (int)ncap, at<float>(ws, L.logits),
                           at<int32_t>(ws, L.counters), s));
   TWL_TRY(launch_topp(c, cv, at<float>(ws, L.logits), (int)ncap, p, iters, threshold, mass,
-                      at<uint32_t>(ws, L.masks), head_mask, mask_words, at<int32_t>(ws, L.counters),
-                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), s));
+                      at<uint32_t>(ws, L.masks), head_mask, mask_words,
+                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s));
   TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
                           capacity, s));
   return TWL_OK;
@@ -351,7 +352,7 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
   if (st != TWL_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheView c = make_view(cache);
-  ListView lv{sel_tokens, sel_indptr, nullptr, 0};
+  ListView lv{sel_tokens, nullptr, sel_indptr, nullptr, 0};
   TWL_TRY(launch_attn(c, static_cast<const uint16_t*>(q), sm_scale, lv, L.chunk_tokens, L.max_chunks,
                       at<float>(ws, L.parts), nullptr, nullptr, 0, s));
   TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));

@@ -31,6 +31,9 @@ __device__ __forceinline__ int list_count(const ListView& L, int u) {
 __device__ __forceinline__ const int32_t* list_ptr(const ListView& L, int u) {
   return L.indptr ? (L.tokens + L.indptr[u]) : (L.tokens + (size_t)u * L.stride);
 }
+__device__ __forceinline__ const int32_t* list_rows(const ListView& L, int u) {
+  return L.indptr ? (L.rows + L.indptr[u]) : (L.rows + (size_t)u * L.stride);
+}
 
 // Find the unit owning flattened chunk `cid`: returns u, and its first chunk id and token offset.
 // Executed by a whole wave; every lane gets the same answer.  Returns -1 when cid >= total.
@@ -109,13 +112,18 @@ __global__ __launch_bounds__(64) void k_attn(CacheView c, const uint16_t* __rest
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[hh][i] = 0.f;
 
+    const int32_t* rws = L.rows ? list_rows(L, u) : nullptr;
     for (int sb = t_begin; sb < t_end; sb += 64) {
       const int idx = sb + lane;
-      const int tok = (idx < t_end) ? toks[idx] : -1;
       int row = -1;  // K/V row index; rows < 2^31 is checked on the host
-      if (tok >= 0 && tok < n) {
-        const int phys = c.page_table[(size_t)b * c.maxP + (tok >> 4)];
-        row = (phys * c.Hkv + h) * kPage + (tok & 15);
+      if (rws) {
+        if (idx < t_end) row = rws[idx];
+      } else {
+        const int tok = (idx < t_end) ? toks[idx] : -1;
+        if (tok >= 0 && tok < n) {
+          const int phys = c.page_table[(size_t)b * c.maxP + (tok >> 4)];
+          row = (phys * c.Hkv + h) * kPage + (tok & 15);
+        }
       }
       const unsigned long long vmask = __ballot(row >= 0);
 
@@ -235,19 +243,24 @@ __global__ __launch_bounds__(64) void k_attn(CacheView c, const uint16_t* __rest
   }
 }
 
-// One block per unit: combine the unit's chunk partials in chunk order.
+// One block per (unit, head), one thread per output dim: combine the unit's chunk partials in chunk
+// order.  The per-chunk rescale factors are staged in LDS 128 chunks at a time so the output loads
+// of many chunks are in flight together.
 template <int G>
-__global__ __launch_bounds__(256) void k_merge(CacheView c, ListView L, int CH, int max_chunks,
+__global__ __launch_bounds__(128) void k_merge(CacheView c, ListView L, int CH, int max_chunks,
                                                const float* __restrict__ partials, float* out, float* lse) {
-  const int U = c.B * c.Hkv;
-  const int u = blockIdx.x;
+  const int u = blockIdx.x / G, hh = blockIdx.x - (blockIdx.x / G) * G;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int tid = threadIdx.x;
   __shared__ int s_c0, s_nch;
-  if (threadIdx.x < 64) {
+  __shared__ float sc[128];
+  __shared__ float red[2 * 2 * 4];
+  BlockReduce<2> br{red};
+  if (tid < 64) {
     int acc = 0;
-    for (int i = (int)threadIdx.x; i < u; i += 64) acc += (max(0, list_count(L, i)) + CH - 1) / CH;
+    for (int i = tid; i < u; i += 64) acc += (max(0, list_count(L, i)) + CH - 1) / CH;
     acc = wave_sum_int(acc);
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       s_c0 = acc;
       s_nch = (max(0, list_count(L, u)) + CH - 1) / CH;
     }
@@ -255,24 +268,33 @@ __global__ __launch_bounds__(256) void k_merge(CacheView c, ListView L, int CH, 
   __syncthreads();
   const int c0 = s_c0;
   const int nch = max(0, min(s_nch, max_chunks - c0));
-  (void)U;
-  for (int o = threadIdx.x; o < G * kD; o += 256) {
-    const int hh = o / kD, d = o - hh * kD;
-    float M = -__builtin_inff();
-    for (int k = 0; k < nch; ++k) M = fmaxf(M, partials[((size_t)(c0 + k) * G + hh) * kPartStride]);
-    float Ls = 0.f, Os = 0.f;
-    if (M != -__builtin_inff()) {
-      for (int k = 0; k < nch; ++k) {
-        const float* pp = partials + ((size_t)(c0 + k) * G + hh) * kPartStride;
-        const float sc = exp2f(pp[0] - M);
-        Ls += pp[1] * sc;
-        Os += pp[2 + d] * sc;
+  const float* base = partials + ((size_t)c0 * G + hh) * kPartStride;
+  constexpr size_t kStep = (size_t)G * kPartStride;
+  float mloc = -__builtin_inff();
+  for (int k = tid; k < nch; k += 128) mloc = fmaxf(mloc, base[k * kStep]);
+  const float M = br.max(mloc);
+  float lpart = 0.f, Os = 0.f;
+  if (M != -__builtin_inff()) {
+    for (int k0 = 0; k0 < nch; k0 += 128) {
+      const int k = k0 + tid;
+      float s = 0.f;
+      if (k < nch) {
+        s = exp2f(base[k * kStep] - M);
+        lpart += base[k * kStep + 1] * s;
       }
+      sc[tid] = s;
+      __syncthreads();
+      const int kn = min(128, nch - k0);
+      const float* po = base + (size_t)k0 * kStep + 2 + tid;
+#pragma unroll 8
+      for (int i = 0; i < kn; ++i) Os += po[i * kStep] * sc[i];
+      __syncthreads();
     }
-    const size_t oh = (size_t)b * c.Hq + (size_t)h * G + hh;
-    out[oh * kD + d] = (Ls > 0.f) ? Os / Ls : 0.f;
-    if (lse && d == 0) lse[oh] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994530942f : -__builtin_inff();
   }
+  const float Ls = br.sum(lpart);
+  const size_t oh = (size_t)b * c.Hq + (size_t)h * G + hh;
+  out[oh * kD + tid] = (Ls > 0.f) ? Os / Ls : 0.f;
+  if (lse && tid == 0) lse[oh] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994530942f : -__builtin_inff();
 }
 
 int attn_chunk_tokens(int64_t total_upper) {
@@ -302,12 +324,12 @@ hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const Li
 
 hipError_t launch_merge(const CacheView& c, const ListView& list, int chunk_tokens, int64_t max_chunks,
                         const float* partials, float* out, float* lse, hipStream_t s) {
-  dim3 grid((unsigned)(c.B * c.Hkv));
+  dim3 grid((unsigned)(c.B * c.Hkv * c.G));
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_merge<1>, grid, dim3(256), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 2: hipLaunchKernelGGL(k_merge<2>, grid, dim3(256), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 4: hipLaunchKernelGGL(k_merge<4>, grid, dim3(256), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 8: hipLaunchKernelGGL(k_merge<8>, grid, dim3(256), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 1: hipLaunchKernelGGL(k_merge<1>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 2: hipLaunchKernelGGL(k_merge<2>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 4: hipLaunchKernelGGL(k_merge<4>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 8: hipLaunchKernelGGL(k_merge<8>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -1,6 +1,6 @@
 // INT4 weight estimate: the mixed-precision SpGEMV of the query against the dequantised 4-bit keys
-// (paperlayer §4.2; §B.1, Fig. 12).  One lane per candidate token, the GQA group's G query heads
-// in the same lane so each 64-byte code row and 16-byte scale/zero row is read once.
+// (paperlayer §4.2; §B.1, Fig. 12).  One lane per candidate token and quantisation group, the GQA
+// group's G query heads in the same lane so each code byte and scale/zero pair is read once.
 //
 // Per head and 32-channel group g the logit is factorised exactly as
 //   sum_{c in g} q_c (code_c s_g + z_g) = s_g * a_g + z_g * b_g,  a_g = sum q_c code_c,  b_g = sum q_c
@@ -60,6 +60,9 @@ __global__ __launch_bounds__(256) void k_range_prefix(CacheView c, CandView cand
   if (threadIdx.x == 0) pre[cnt] = carry;
 }
 
+// One block = 64 candidates x 4 waves; wave g handles quantisation group g (32 channels) of every
+// candidate for all G heads, so each wave reads only its 16-byte slice of the code row and its
+// scale/zero pair.  The per-group terms meet in LDS and are combined in the committed order.
 template <int G>
 __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
                                                   CandView cand, int ncap, int chunks_per_unit,
@@ -71,6 +74,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
 
   __shared__ float qs[G][kD];
   __shared__ float bs[G][kGroups];
+  __shared__ float T[kGroups][G][64];
   const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
   for (int i = threadIdx.x; i < G * kD; i += 256) qs[i / kD][i % kD] = __uint_as_float((uint32_t)qg[i] << 16);
   __syncthreads();
@@ -82,68 +86,57 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   }
   __syncthreads();
 
+  const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int k = ck * 256 + (int)threadIdx.x;
+  const int k = ck * 64 + lane;
   const int tok = cand_token(cand, u, k, n);
-  float lg[G];
   if (tok >= 0) {
     const int phys = c.page_table[(size_t)b * c.maxP + (tok >> 4)];
     const size_t row = ((size_t)phys * c.Hkv + h) * kPage + (tok & 15);
-    const uint4* cp = reinterpret_cast<const uint4*>(c.k4 + row * 64);
-    const uint4 meta = *reinterpret_cast<const uint4*>(c.k4_meta + row * kGroups);
-    uint4 cw[4];
+    const uint4 cw = reinterpret_cast<const uint4*>(c.k4 + row * 64)[g];
+    const uint32_t mw = c.k4_meta[row * kGroups + g];
+    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+    float a[G];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) cw[g] = cp[g];
-    const uint32_t mw[4] = {meta.x, meta.y, meta.z, meta.w};
-    float t[G][kGroups];
+    for (int hh = 0; hh < G; ++hh) a[hh] = 0.f;
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      const uint32_t words[4] = {cw[g].x, cw[g].y, cw[g].z, cw[g].w};
-      float a[G];
+    for (int wi = 0; wi < 4; ++wi) {
+      const uint32_t lo = words[wi] & 0x0F0F0F0Fu;
+      const uint32_t hi = (words[wi] >> 4) & 0x0F0F0F0Fu;
+      float code[8];
+      code[0] = (float)(lo & 0xFFu);
+      code[1] = (float)(hi & 0xFFu);
+      code[2] = (float)((lo >> 8) & 0xFFu);
+      code[3] = (float)((hi >> 8) & 0xFFu);
+      code[4] = (float)((lo >> 16) & 0xFFu);
+      code[5] = (float)((hi >> 16) & 0xFFu);
+      code[6] = (float)(lo >> 24);
+      code[7] = (float)(hi >> 24);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) a[hh] = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        const int ch = g * 32 + wi * 8 + e;
 #pragma unroll
-      for (int wi = 0; wi < 4; ++wi) {
-        const uint32_t lo = words[wi] & 0x0F0F0F0Fu;
-        const uint32_t hi = (words[wi] >> 4) & 0x0F0F0F0Fu;
-        float code[8];
-        code[0] = (float)(lo & 0xFFu);
-        code[1] = (float)(hi & 0xFFu);
-        code[2] = (float)((lo >> 8) & 0xFFu);
-        code[3] = (float)((hi >> 8) & 0xFFu);
-        code[4] = (float)((lo >> 16) & 0xFFu);
-        code[5] = (float)((hi >> 16) & 0xFFu);
-        code[6] = (float)(lo >> 24);
-        code[7] = (float)(hi >> 24);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = g * 32 + wi * 8 + e;
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) a[hh] = fmaf(qs[hh][ch], code[e], a[hh]);
-        }
-      }
-      const float s = half_bits_to_float(mw[g] & 0xffffu);
-      const float z = half_bits_to_float(mw[g] >> 16);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float sa = s * a[hh];
-        const float zb = z * bs[hh][g];
-        t[hh][g] = sa + zb;
+        for (int hh = 0; hh < G; ++hh) a[hh] = fmaf(qs[hh][ch], code[e], a[hh]);
       }
     }
+    const float s = half_bits_to_float(mw & 0xffffu);
+    const float z = half_bits_to_float(mw >> 16);
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const float r01 = t[hh][0] + t[hh][1];
-      const float r23 = t[hh][2] + t[hh][3];
-      lg[hh] = sm * (r01 + r23);
+      const float sa = s * a[hh];
+      const float zb = z * bs[hh][g];
+      T[g][hh][lane] = sa + zb;
     }
-  } else {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) lg[hh] = -__builtin_inff();
   }
-  if (k < ncap) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg[hh];
+  __syncthreads();
+  for (int hh = g; hh < G; hh += kGroups) {
+    float lg = -__builtin_inff();
+    if (tok >= 0) {
+      const float r01 = T[0][hh][lane] + T[1][hh][lane];
+      const float r23 = T[2][hh][lane] + T[3][hh][lane];
+      lg = sm * (r01 + r23);
+    }
+    if (k < ncap) logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
   }
 }
 
@@ -154,7 +147,7 @@ hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t
 
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
                            float* logits, int32_t* counters, hipStream_t s) {
-  const int cpu = (ncap + 255) / 256;
+  const int cpu = (ncap + 63) / 64;
   dim3 grid((unsigned)(c.B * c.Hkv * cpu));
   switch (c.G) {
     case 1: hipLaunchKernelGGL(k_estimate<1>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, counters); break;

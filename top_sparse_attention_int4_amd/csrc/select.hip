@@ -3,69 +3,72 @@
 // The Twilight pages run a base sparse-attention selector with a conservative budget before the
 // top-p pruner (Paper-Notes "整体框架"; paperlayer §4.1, Fig. 5) and name Quest among those
 // selectors.  The page score of query head h is sum_c max(q_c*kmin_c, q_c*kmax_c); it is evaluated
-// as a float32 left-to-right fold over the 128 channels, one lane per page, so the result is the
-// same on every run and equal to the documented operation sequence.  Because q_c*bound is exact in
-// float32 (bf16 x bf16), max(q*kmin, q*kmax) = q+ * kmax + q- * kmin with q+ = max(q,0),
-// q- = min(q,0): the second product is then an exact zero and adding it changes nothing, so two
-// fused multiply-adds per channel and head reproduce the fold bit for bit without a compare.
+// as a float32 left-to-right fold over the 128 channels, one lane per page, so the result equals the
+// documented operation sequence on every run.  Because q_c*bound is exact in float32 (bf16 x bf16),
+// max(q*kmin, q*kmax) = q+ * kmax + q- * kmin with q+ = max(q,0), q- = min(q,0): the second product
+// is then an exact zero and adding it changes nothing, so two fused multiply-adds per channel and
+// head reproduce the fold bit for bit without a compare.  Each wave of a block folds one query head
+// for the block's 64 pages; the group score then folds the heads in order.
 #include "twl_device.h"
 #include "twl_internal.h"
 
 namespace twl {
 
 template <int G>
-__global__ __launch_bounds__(64) void k_page_score(CacheView c, const uint16_t* __restrict__ q,
-                                                   float* __restrict__ scores, int blocks_per_unit) {
+__global__ __launch_bounds__(64 * G) void k_page_score(CacheView c, const uint16_t* __restrict__ q,
+                                                       float* __restrict__ scores, int blocks_per_unit) {
   const int u = blockIdx.x / blocks_per_unit;
   const int blk = blockIdx.x - u * blocks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
   if (blk * 64 >= P) return;
+  const int hh = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
   __shared__ float qpos[G][kD];
   __shared__ float qneg[G][kD];
+  __shared__ float sig[G][64];
   const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
-  for (int i = threadIdx.x; i < G * kD; i += 64) {
+  for (int i = threadIdx.x; i < G * kD; i += 64 * G) {
     const float x = __uint_as_float((uint32_t)qg[i] << 16);
     qpos[i / kD][i % kD] = x > 0.f ? x : 0.f;
     qneg[i / kD][i % kD] = x < 0.f ? x : 0.f;
   }
   __syncthreads();
 
-  const int j = blk * 64 + threadIdx.x;
-  if (j >= P) return;
-  const int phys = c.page_table[(size_t)b * c.maxP + j];
-  const uint4* bnd = reinterpret_cast<const uint4*>(c.kbound + ((size_t)phys * c.Hkv + h) * 2 * kD);
-  uint4 mnv[16], mxv[16];
+  const int j = blk * 64 + lane;
+  if (j < P) {
+    const int phys = c.page_table[(size_t)b * c.maxP + j];
+    const uint4* bnd = reinterpret_cast<const uint4*>(c.kbound + ((size_t)phys * c.Hkv + h) * 2 * kD);
+    uint4 mnv[16], mxv[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    mnv[i] = bnd[i];
-    mxv[i] = bnd[16 + i];
-  }
-  float acc[G];
+    for (int i = 0; i < 16; ++i) {
+      mnv[i] = bnd[i];
+      mxv[i] = bnd[16 + i];
+    }
+    float acc = 0.f;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) acc[hh] = 0.f;
+    for (int c8 = 0; c8 < 16; ++c8) {
+      const uint32_t wm[4] = {mnv[c8].x, mnv[c8].y, mnv[c8].z, mnv[c8].w};
+      const uint32_t wx[4] = {mxv[c8].x, mxv[c8].y, mxv[c8].z, mxv[c8].w};
 #pragma unroll
-  for (int c8 = 0; c8 < 16; ++c8) {
-    const uint32_t wm[4] = {mnv[c8].x, mnv[c8].y, mnv[c8].z, mnv[c8].w};
-    const uint32_t wx[4] = {mxv[c8].x, mxv[c8].y, mxv[c8].z, mxv[c8].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int ch = c8 * 8 + e;
-      const float mn = (e & 1) ? bf16_hi(wm[e >> 1]) : bf16_lo(wm[e >> 1]);
-      const float mx = (e & 1) ? bf16_hi(wx[e >> 1]) : bf16_lo(wx[e >> 1]);
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        acc[hh] = fmaf(qpos[hh][ch], mx, acc[hh]);
-        acc[hh] = fmaf(qneg[hh][ch], mn, acc[hh]);
+      for (int e = 0; e < 8; ++e) {
+        const int ch = c8 * 8 + e;
+        const float mn = (e & 1) ? bf16_hi(wm[e >> 1]) : bf16_lo(wm[e >> 1]);
+        const float mx = (e & 1) ? bf16_hi(wx[e >> 1]) : bf16_lo(wx[e >> 1]);
+        acc = fmaf(qpos[hh][ch], mx, acc);
+        acc = fmaf(qneg[hh][ch], mn, acc);
       }
     }
+    sig[hh][lane] = acc;
   }
-  float gs = 0.f;
+  __syncthreads();
+  if (hh == 0 && j < P) {
+    float gs = 0.f;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) gs = gs + acc[hh];
-  scores[(size_t)u * c.maxP + j] = gs;
+    for (int k = 0; k < G; ++k) gs = gs + sig[k][lane];
+    scores[(size_t)u * c.maxP + j] = gs;
+  }
 }
 
 // Ascending key <=> descending score (float order mapped onto uint32).
@@ -74,6 +77,8 @@ __device__ __forceinline__ uint32_t desc_key(float f) {
   const uint32_t o = (x & 0x80000000u) ? ~x : (x | 0x80000000u);
   return ~o;
 }
+
+constexpr int kSelLdsKeys = 8192;
 
 // Exact top-K of one unit's page scores: radix select of the K-th smallest key (4 passes of 8 bits,
 // integer histograms), ties at the threshold key resolved towards lower page ids, then an
@@ -100,52 +105,56 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
   }
   const float* sc = scores + (size_t)u * c.maxP;
 
-  __shared__ int hist[256];
+  __shared__ uint32_t keys[kSelLdsKeys];
+  __shared__ int hist[2][256];
   __shared__ uint32_t s_prefix, s_mask;
   __shared__ int s_rem;
   __shared__ int scan_sm[NW + 1];
+  const bool in_lds = P <= kSelLdsKeys;
+  if (in_lds)
+    for (int i = threadIdx.x; i < P; i += NT) keys[i] = desc_key(sc[i]);
+  for (int i = threadIdx.x; i < 512; i += NT) (&hist[0][0])[i] = 0;
   if (threadIdx.x == 0) {
     s_prefix = 0u;
     s_mask = 0u;
     s_rem = K;
   }
+  __syncthreads();
+  auto key = [&](int i) -> uint32_t { return in_lds ? keys[i] : desc_key(sc[i]); };
+
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
+    int* hs = hist[pass & 1];
     const uint32_t prefix = s_prefix, mask = s_mask;
     for (int i = threadIdx.x; i < P; i += NT) {
-      const uint32_t k = desc_key(sc[i]);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+      const uint32_t k = key(i);
+      if ((k & mask) == prefix) atomicAdd(&hs[(k >> shift) & 255u], 1);
     }
     __syncthreads();
     if (threadIdx.x < 64) {
-      // lane l owns bins 4l..4l+3
+      // lane l owns bins 4l..4l+3; find the bin where the cumulative count first reaches rem
       const int lane = threadIdx.x;
-      const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+      const int h0 = hs[4 * lane], h1 = hs[4 * lane + 1], h2 = hs[4 * lane + 2], h3 = hs[4 * lane + 3];
       const int sum4 = h0 + h1 + h2 + h3;
       const int incl = wave_incl_scan(sum4);
       const int excl = incl - sum4;
       const int rem = s_rem;
-      // the bin where the cumulative count first reaches rem
-      int found = -1, before = 0;
       if (excl < rem && rem <= incl) {
         int acc = excl;
-        const int hs[4] = {h0, h1, h2, h3};
+        const int hv[4] = {h0, h1, h2, h3};
         for (int t = 0; t < 4; ++t) {
-          if (acc + hs[t] >= rem) {
-            found = 4 * lane + t;
-            before = acc;
+          if (acc + hv[t] >= rem) {
+            s_prefix = prefix | ((uint32_t)(4 * lane + t) << shift);
+            s_mask = mask | (255u << shift);
+            s_rem = rem - acc;
             break;
           }
-          acc += hs[t];
+          acc += hv[t];
         }
       }
-      if (found >= 0) {
-        s_prefix = prefix | ((uint32_t)found << shift);
-        s_mask = mask | (255u << shift);
-        s_rem = rem - before;
-      }
+    } else {
+      int* other = hist[(pass + 1) & 1];
+      for (int i = (int)threadIdx.x - 64; i < 256; i += NT - 64) other[i] = 0;
     }
     __syncthreads();
   }
@@ -156,27 +165,25 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
   const int E = (P + NT - 1) / NT;
   const int i0 = min(P, (int)threadIdx.x * E), i1 = min(P, i0 + E);
   int eq_local = 0;
-  for (int i = i0; i < i1; ++i) eq_local += (desc_key(sc[i]) == T);
+  for (int i = i0; i < i1; ++i) eq_local += (key(i) == T);
   int total;
-  int eq_rank = block_excl_scan<NW>(eq_local, scan_sm, &total);
+  const int eq_rank = block_excl_scan<NW>(eq_local, scan_sm, &total);
   int keep_local = 0;
   {
     int r = eq_rank;
     for (int i = i0; i < i1; ++i) {
-      const uint32_t k = desc_key(sc[i]);
-      const bool keep = k < T || (k == T && r < take_eq);
+      const uint32_t k = key(i);
+      keep_local += (k < T || (k == T && r < take_eq));
       r += (k == T);
-      keep_local += keep;
     }
   }
   int pos = block_excl_scan<NW>(keep_local, scan_sm, &total);
   {
     int r = eq_rank;
     for (int i = i0; i < i1; ++i) {
-      const uint32_t k = desc_key(sc[i]);
-      const bool keep = k < T || (k == T && r < take_eq);
+      const uint32_t k = key(i);
+      if (k < T || (k == T && r < take_eq)) out[pos++] = i;
       r += (k == T);
-      if (keep) out[pos++] = i;
     }
   }
 }
@@ -186,9 +193,9 @@ hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* score
   dim3 grid((unsigned)(c.B * c.Hkv * bpu));
   switch (c.G) {
     case 1: hipLaunchKernelGGL(k_page_score<1>, grid, dim3(64), 0, s, c, q, scores, bpu); break;
-    case 2: hipLaunchKernelGGL(k_page_score<2>, grid, dim3(64), 0, s, c, q, scores, bpu); break;
-    case 4: hipLaunchKernelGGL(k_page_score<4>, grid, dim3(64), 0, s, c, q, scores, bpu); break;
-    case 8: hipLaunchKernelGGL(k_page_score<8>, grid, dim3(64), 0, s, c, q, scores, bpu); break;
+    case 2: hipLaunchKernelGGL(k_page_score<2>, grid, dim3(128), 0, s, c, q, scores, bpu); break;
+    case 4: hipLaunchKernelGGL(k_page_score<4>, grid, dim3(256), 0, s, c, q, scores, bpu); break;
+    case 8: hipLaunchKernelGGL(k_page_score<8>, grid, dim3(512), 0, s, c, q, scores, bpu); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -2,17 +2,24 @@
 //
 // Paper-Notes "关键设计 / 高效Top-p": instead of sorting, search the threshold m with
 // sum_{W_i >= m} W_i >= p; each round is one parallel pass over the weights.  One 1024-thread block
-// handles one (sequence, query head): the head's weights stay in registers (E per thread), the
-// softmax maximum and normaliser are computed from the logits in the same block, and each bisection
-// step is one fixed-order block reduction.  Midpoints are taken on the uint32 image of the
-// non-negative float32 weights, keeping f(lo) >= p*Z > f(hi); the kept set is {e_i >= lo}.
+// handles one (sequence, query head); the head's weights stay in registers (E per thread).
 //
-// The weights are kept unnormalised, e_i = exp(l_i - M) in (0, 1] (the maximum is exactly 1), and
-// the target is p*Z with Z = sum e_i, which selects the same set as comparing W_i = e_i/Z with p.
-// Candidates that do not exist carry e = -1 so no threshold >= 0 ever selects them.
+// Weights are kept unnormalised, e_i = exp(l_i - M) in (0, 1] (the maximum is exactly 1), with the
+// target p*Z, Z = sum e_i, which keeps the same set as comparing W_i = e_i/Z with p.  Midpoints are
+// taken on the uint32 image of the non-negative float32 weights and the bracket keeps
+// f(lo) >= p*Z > f(hi); the kept set is {e_i >= lo}.  The bracket starts at [min e, 1] (all of the
+// mass lies at or above the smallest weight).  Candidates that do not exist carry e = -1.
 //
-// The last of the G blocks of a kv-head (paperlayer §B.2: the union over a GQA group's query heads)
-// ORs the G head masks and writes the unit's kept token ids, ascending, with their count.
+// Two phases share that bisection.  While many weights remain inside the bracket, every step is a
+// block-wide pass with one fixed-order reduction of f(mid) and #{e >= mid}; the counts at the two
+// ends of the bracket give the number of weights inside it.  Once at most kCap weights are inside,
+// they are compacted into LDS together with the mass above the bracket, and a single wave finishes
+// the search with DPP reductions and no barriers, compacting the shrinking bracket as it goes
+// (weights leaving through the top add their mass to that constant).  Rounding order differs
+// between the phases but is fixed, so results are reproducible.
+//
+// The GQA union (paperlayer §B.2: the union over a group's query heads, read once) is a separate
+// small kernel over the head masks.
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -42,53 +49,58 @@ __device__ int cand_token_topp(const CandView& cand, int u, int k, int n) {
   return (t >= 0 && t < n) ? t : -1;
 }
 
-// Union of the G head masks of unit u, compacted to ascending token ids.  Called by a whole block.
-template <int NW>
-__device__ void group_union(const CacheView& c, const CandView& cand, int u, int b, const uint32_t* mask_ws,
-                            int mw, int32_t* union_tok, int32_t* union_cnt, int ncap, int* scan_sm) {
-  constexpr int NT = NW * 64;
-  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int h = u - b * c.Hkv;
-  const uint32_t* m0 = mask_ws + ((size_t)b * c.Hq + (size_t)h * c.G) * mw;
-  const int wpt = (mw + NT - 1) / NT;  // contiguous words per thread keep the token order
-  const int w0 = min(mw, (int)threadIdx.x * wpt), w1 = min(mw, w0 + wpt);
-  int local = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = 0u;
-    for (int hh = 0; hh < c.G; ++hh) bits |= m0[(size_t)hh * mw + w];
-    local += __popc(bits);
+constexpr int kCap = 1024;  // weights handed to the single-wave phase
+
+// One bisection step of the single-wave phase over `n` compacted weights in `buf`; compacts the kept
+// bracket into `dst`, updates lo/hi and the mass above hi, and returns the new count.
+__device__ __forceinline__ int wave_step(const float* buf, float* dst, int n, uint32_t& lo, uint32_t& hi,
+                                         float& c_hi, float target) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t mid = lo + ((hi - lo) >> 1);
+  const float m = __uint_as_float(mid);
+  float f = 0.f;
+  for (int i = lane; i < n; i += 64) {
+    const float x = buf[i];
+    f += (x >= m) ? x : 0.f;
   }
-  int total;
-  int pos = block_excl_scan<NW>(local, scan_sm, &total);
-  int32_t* out = union_tok + (size_t)u * ncap;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = 0u;
-    for (int hh = 0; hh < c.G; ++hh) bits |= m0[(size_t)hh * mw + w];
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      out[pos++] = cand_token_topp(cand, u, w * 32 + bit, n);
-    }
+  f = c_hi + wave_sum_dpp(f);
+  const bool up = f >= target;
+  const float klo = __uint_as_float(up ? mid : lo);
+  const float khi = __uint_as_float(up ? hi : mid);
+  float above = 0.f;
+  int base = 0;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const float x = (i < n) ? buf[i] : -1.f;
+    const bool keep = (i < n) && x >= klo && x < khi;
+    if (i < n && x >= khi) above += x;
+    const unsigned long long bal = __ballot(keep);
+    const int pos =
+        base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (keep) dst[pos] = x;
+    base += __popcll(bal);
   }
-  if (threadIdx.x == 0) union_cnt[u] = total;
+  __builtin_amdgcn_wave_barrier();  // the next step reads what other lanes wrote
+  c_hi += wave_sum_dpp(above);
+  if (up) lo = mid; else hi = mid;
+  return base;
 }
 
 template <int E>
-__global__ __launch_bounds__(1024) void k_topp(CacheView c, CandView cand, const float* __restrict__ logits,
-                                               int ncap, float p, int iters, float* threshold, float* mass,
-                                               uint32_t* mask_ws, uint32_t* head_mask, int mask_words,
-                                               int32_t* counters, int32_t* union_tok, int32_t* union_cnt) {
+__global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restrict__ logits, int ncap, float p,
+                                               int iters, float* threshold, float* mass, uint32_t* mask_ws,
+                                               uint32_t* head_mask, int mask_words) {
   constexpr int NT = kToppThreads, NW = NT / 64;
-  __shared__ float red[2 * NW];
+  __shared__ float red[2 * NW * 4];
   __shared__ int scan_sm[NW + 1];
-  __shared__ int s_last;
+  __shared__ float buf[2][kCap];
+  __shared__ uint32_t s_lo;
   BlockReduce<NW> br{red};
 
   const int bh = blockIdx.x;
-  const int b = bh / c.Hq, hq = bh - b * c.Hq;
-  const int h = hq / c.G, u = b * c.Hkv + h;
   const float* lg = logits + (size_t)bh * ncap;
   const int tid = threadIdx.x;
+  const int wv = tid >> 6;
 
   float e[E];
   float mloc = -__builtin_inff();
@@ -99,31 +111,80 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, CandView cand, const
     mloc = fmaxf(mloc, e[j]);
   }
   const float M = br.max(mloc);
-  float zloc = 0.f;
-  if (M == -__builtin_inff()) {
-#pragma unroll
-    for (int j = 0; j < E; ++j) e[j] = -1.f;
-  } else {
+  float Z = 0.f, emin = __builtin_inff(), nval = 0.f;
+  if (M != -__builtin_inff()) {
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       e[j] = (e[j] == -__builtin_inff()) ? -1.f : exp_diff(e[j], M);
-      zloc += fmaxf(e[j], 0.f);
+      if (e[j] >= 0.f) {
+        Z += e[j];
+        emin = fminf(emin, e[j]);
+        nval += 1.f;
+      }
     }
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) e[j] = -1.f;
   }
-  const float Z = br.sum(zloc);
+  br.sum_min(Z, emin);
+  nval = br.sum(nval);
 
   uint32_t lo = 0u;
   if (Z > 0.f && p < 1.0f) {
     const float target = p * Z;
+    lo = __float_as_uint(emin);                // f(min e) = Z >= target
     uint32_t hi = __float_as_uint(1.0f) + 1u;  // e <= 1 = exp(0)
-    for (int it = 0; it < iters && hi - lo > 1u; ++it) {
+    float n_lo = nval, n_hi = 0.f;             // #{e >= lo}, #{e >= hi}
+    int it = 0;
+    // ---- block phase -------------------------------------------------------------------------
+    while (it < iters && hi - lo > 1u && n_lo - n_hi > (float)kCap) {
       const uint32_t mid = lo + ((hi - lo) >> 1);
       const float m = __uint_as_float(mid);
-      float f = 0.f;
+      float f = 0.f, cm = 0.f;
 #pragma unroll
-      for (int j = 0; j < E; ++j) f += (e[j] >= m) ? e[j] : 0.f;
-      f = br.sum(f);
-      if (f >= target) lo = mid; else hi = mid;
+      for (int j = 0; j < E; ++j) {
+        const bool ge = e[j] >= m;
+        f += ge ? e[j] : 0.f;
+        cm += ge ? 1.f : 0.f;
+      }
+      br.sum2(f, cm);
+      if (f >= target) {
+        lo = mid;
+        n_lo = cm;
+      } else {
+        hi = mid;
+        n_hi = cm;
+      }
+      ++it;
+    }
+    // ---- single-wave phase --------------------------------------------------------------------
+    if (it < iters && hi - lo > 1u) {
+      const float mlo = __uint_as_float(lo), mhi = __uint_as_float(hi);
+      int local = 0;
+      float above = 0.f;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        local += (e[j] >= mlo && e[j] < mhi) ? 1 : 0;
+        above += (e[j] >= mhi) ? e[j] : 0.f;
+      }
+      int total;
+      int pos = block_excl_scan<NW>(local, scan_sm, &total);
+      float c_hi = br.sum(above);
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (e[j] >= mlo && e[j] < mhi) buf[0][pos++] = e[j];
+      __syncthreads();
+      if (wv == 0) {
+        int n = min(total, kCap), cur = 0;
+        while (it < iters && hi - lo > 1u && n > 0) {
+          n = wave_step(buf[cur], buf[cur ^ 1], n, lo, hi, c_hi, target);
+          cur ^= 1;
+          ++it;
+        }
+        if (tid == 0) s_lo = lo;
+      }
+      __syncthreads();
+      lo = s_lo;
     }
   }
   const float m = __uint_as_float(lo);
@@ -138,7 +199,7 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, CandView cand, const
 
   // head mask: bit k of the head's bitmap <=> candidate k kept
   const int mw = ncap / 32;
-  const int lane = tid & 63, wv = tid >> 6;
+  const int lane = tid & 63;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const unsigned long long bal = __ballot(e[j] >= m);
@@ -152,15 +213,72 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, CandView cand, const
       }
     }
   }
+}
 
-  // the last block of the group forms the union
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&counters[u], 1) == c.G - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  group_union<NW>(c, cand, u, b, mask_ws, mw, union_tok, union_cnt, ncap, scan_sm);
+// One block per unit: OR the unit's G head masks, write the kept token ids in ascending order, their
+// K/V row indices, and the count.  A mask word covers 32 candidates, i.e. two pages when candidates
+// are whole pages, so the page-id and page-table lookups are made once per word, not per token.
+__global__ __launch_bounds__(1024) void k_union(CacheView c, CandView cand, const uint32_t* __restrict__ mask_ws,
+                                                int ncap, int32_t* union_tok, int32_t* union_row,
+                                                int32_t* union_cnt) {
+  constexpr int NT = 1024, NW = NT / 64;
+  __shared__ int scan_sm[NW + 1];
+  const int u = blockIdx.x;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+  const int mw = ncap / 32;
+  const uint32_t* m0 = mask_ws + ((size_t)b * c.Hq + (size_t)h * c.G) * mw;
+  const int wpt = (mw + NT - 1) / NT;  // contiguous words per thread keep the token order
+  const int w0 = min(mw, (int)threadIdx.x * wpt), w1 = min(mw, w0 + wpt);
+  int local = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = 0u;
+    for (int hh = 0; hh < c.G; ++hh) bits |= m0[(size_t)hh * mw + w];
+    local += __popc(bits);
+  }
+  int total;
+  int pos = block_excl_scan<NW>(local, scan_sm, &total);
+  int32_t* out = union_tok + (size_t)u * ncap;
+  int32_t* rows = union_row + (size_t)u * ncap;
+  const int32_t* pt = c.page_table + (size_t)b * c.maxP;
+  const int cnt = clampi(cand.mode == kCandAll ? 0 : cand.count[u], 0, cand.max_items);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = 0u;
+    for (int hh = 0; hh < c.G; ++hh) bits |= m0[(size_t)hh * mw + w];
+    if (!bits) continue;
+    if (cand.mode == kCandRanges) {
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        const int t = cand_token_topp(cand, u, w * 32 + bit, n);
+        out[pos] = t;
+        rows[pos] = (pt[t >> 4] * c.Hkv + h) * kPage + (t & 15);
+        ++pos;
+      }
+      continue;
+    }
+    // the two pages of this word (kept bits are valid candidates, so their pages exist)
+    int page0, page1;
+    if (cand.mode == kCandPages) {
+      const int32_t* items = cand.items + (size_t)u * cand.max_items;
+      page0 = (2 * w < cnt) ? items[2 * w] : 0;
+      page1 = (2 * w + 1 < cnt) ? items[2 * w + 1] : 0;
+    } else {
+      page0 = 2 * w;
+      page1 = 2 * w + 1;
+    }
+    const int phys0 = (bits & 0xffffu) ? pt[page0] : 0;
+    const int phys1 = (bits >> 16) ? pt[page1] : 0;
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int hi = bit >> 4, slot = bit & 15;
+      out[pos] = (hi ? page1 : page0) * kPage + slot;
+      rows[pos] = ((hi ? phys1 : phys0) * c.Hkv + h) * kPage + slot;
+      ++pos;
+    }
+  }
+  if (threadIdx.x == 0) union_cnt[u] = total;
 }
 
 __global__ __launch_bounds__(256) void k_csr_emit(CacheView c, const int32_t* __restrict__ union_tok,
@@ -194,14 +312,14 @@ int topp_elems_per_thread(int64_t ncap) {
 
 hipError_t launch_topp(const CacheView& c, const CandView& cand, const float* logits, int ncap, float p,
                        int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
-                       int mask_words, int32_t* counters, int32_t* union_tok, int32_t* union_cnt,
+                       int mask_words, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt,
                        hipStream_t s) {
   const int E = ncap / kToppThreads;
   dim3 grid((unsigned)(c.B * c.Hq)), block(kToppThreads);
-#define TWL_TOPP_CASE(EE)                                                                               \
-  case EE:                                                                                              \
-    hipLaunchKernelGGL(k_topp<EE>, grid, block, 0, s, c, cand, logits, ncap, p, iters, threshold, mass, \
-                       mask_ws, head_mask, mask_words, counters, union_tok, union_cnt);                 \
+#define TWL_TOPP_CASE(EE)                                                                                 \
+  case EE:                                                                                                \
+    hipLaunchKernelGGL(k_topp<EE>, grid, block, 0, s, c, logits, ncap, p, iters, threshold, mass, mask_ws, \
+                       head_mask, mask_words);                                                           \
     break;
   switch (E) {
     TWL_TOPP_CASE(1)
@@ -214,6 +332,10 @@ hipError_t launch_topp(const CacheView& c, const CandView& cand, const float* lo
     default: return hipErrorInvalidValue;
   }
 #undef TWL_TOPP_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_union, dim3((unsigned)(c.B * c.Hkv)), dim3(1024), 0, s, c, cand, mask_ws, ncap, union_tok,
+                     union_row, union_cnt);
   return hipGetLastError();
 }
 

@@ -20,6 +20,59 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
+// ---- DPP reductions: within each 16-lane row (xor 1, xor 2, rotate 4, rotate 8), then the four
+// row results are read from lanes 0/16/32/48 and combined as (r0 + r1) + (r2 + r3).  The order is
+// fixed by lane position, so the result is the same on every run; it is uniform across the wave.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;  // row_ror:4
+constexpr int kDppRor8 = 0x128;  // row_ror:8
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppRor4>(x);
+  x += dpp_f<kDppRor8>(x);
+  const float r0 = readlane_f(x, 0), r1 = readlane_f(x, 16), r2 = readlane_f(x, 32), r3 = readlane_f(x, 48);
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppRor4>(x));
+  x = fmaxf(x, dpp_f<kDppRor8>(x));
+  const float r0 = readlane_f(x, 0), r1 = readlane_f(x, 16), r2 = readlane_f(x, 32), r3 = readlane_f(x, 48);
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_min_dpp(float x) {
+  x = fminf(x, dpp_f<kDppXor1>(x));
+  x = fminf(x, dpp_f<kDppXor2>(x));
+  x = fminf(x, dpp_f<kDppRor4>(x));
+  x = fminf(x, dpp_f<kDppRor8>(x));
+  const float r0 = readlane_f(x, 0), r1 = readlane_f(x, 16), r2 = readlane_f(x, 32), r3 = readlane_f(x, 48);
+  return fminf(fminf(r0, r1), fminf(r2, r3));
+}
+__device__ __forceinline__ int wave_sum_int_dpp(int x) {
+  x += dpp_i<kDppXor1>(x);
+  x += dpp_i<kDppXor2>(x);
+  x += dpp_i<kDppRor4>(x);
+  x += dpp_i<kDppRor8>(x);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+
 // Butterfly all-reduce over the 64 lanes; every lane ends with the same bits (fp add/max commute).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -47,35 +100,100 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Block-wide reductions for blocks of NW waves.  `red` must hold 2*NW floats of LDS; calls
-// alternate between its two halves, so consecutive calls need only one barrier each.
+// Block-wide reductions for blocks of NW waves, built on the DPP wave reductions.  `red` must hold
+// 2*NW*4 floats of LDS; calls alternate between its two halves, so consecutive calls need only one
+// barrier each.  The wave results are combined in wave order, so the result is reproducible and
+// identical in every thread.
 template <int NW>
 struct BlockReduce {
   float* red;
   int slot = 0;
-  __device__ float sum(float x) {
-    x = wave_sum(x);
-    const int w = threadIdx.x >> 6;
-    float* r = red + slot * NW;
+  __device__ float* next() {
+    float* r = red + slot * NW * 4;
     slot ^= 1;
-    if ((threadIdx.x & 63) == 0) r[w] = x;
+    return r;
+  }
+  __device__ float sum(float x) {
+    x = wave_sum_dpp(x);
+    float* r = next();
+    if ((threadIdx.x & 63) == 0) r[threadIdx.x >> 6] = x;
     __syncthreads();
-    float t = 0.f;
+    float t = r[0];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) t += r[i];
+    for (int i = 1; i < NW; ++i) t += r[i];
     return t;
   }
   __device__ float max(float x) {
-    x = wave_max(x);
-    const int w = threadIdx.x >> 6;
-    float* r = red + slot * NW;
-    slot ^= 1;
-    if ((threadIdx.x & 63) == 0) r[w] = x;
+    x = wave_max_dpp(x);
+    float* r = next();
+    if ((threadIdx.x & 63) == 0) r[threadIdx.x >> 6] = x;
     __syncthreads();
     float t = r[0];
 #pragma unroll
     for (int i = 1; i < NW; ++i) t = fmaxf(t, r[i]);
     return t;
+  }
+  // sum of a, min of b
+  __device__ void sum_min(float& a, float& b) {
+    a = wave_sum_dpp(a);
+    b = wave_min_dpp(b);
+    float* r = next();
+    if ((threadIdx.x & 63) == 0) {
+      r[threadIdx.x >> 6] = a;
+      r[NW + (threadIdx.x >> 6)] = b;
+    }
+    __syncthreads();
+    float ta = r[0], tb = r[NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      ta += r[i];
+      tb = fminf(tb, r[NW + i]);
+    }
+    a = ta;
+    b = tb;
+  }
+  // two sums at once (counts below 2^24 are exact in float)
+  __device__ void sum2(float& a, float& b) {
+    a = wave_sum_dpp(a);
+    b = wave_sum_dpp(b);
+    float* r = next();
+    if ((threadIdx.x & 63) == 0) {
+      r[threadIdx.x >> 6] = a;
+      r[NW + (threadIdx.x >> 6)] = b;
+    }
+    __syncthreads();
+    float ta = r[0], tb = r[NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      ta += r[i];
+      tb += r[NW + i];
+    }
+    a = ta;
+    b = tb;
+  }
+  // three sums at once (counts below 2^24 are exact in float)
+  __device__ void sum3(float& a, float& b, float& c) {
+    a = wave_sum_dpp(a);
+    b = wave_sum_dpp(b);
+    c = wave_sum_dpp(c);
+    float* r = next();
+    if ((threadIdx.x & 63) == 0) {
+      const int w = threadIdx.x >> 6;
+      r[w] = a;
+      r[NW + w] = b;
+      r[2 * NW + w] = c;
+    }
+    __syncthreads();
+    float ta = r[0], tb = r[NW], tc = r[2 * NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      ta += r[i];
+      tb += r[NW + i];
+      tc += r[2 * NW + i];
+    }
+    a = ta;
+    b = tb;
+    c = tc;
   }
 };
 

@@ -35,6 +35,7 @@ struct CandView {
 // Token list of each unit for the attention stage: either padded rows (stride) with counts, or CSR.
 struct ListView {
   const int32_t* tokens;
+  const int32_t* rows;    // K/V row index per listed token (same indexing as tokens), or nullptr
   const int32_t* indptr;  // [U+1] when CSR, else nullptr
   const int32_t* counts;  // [U] when padded, else nullptr
   int64_t stride;         // row stride when padded
@@ -51,8 +52,8 @@ hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, cons
                            float* logits, int32_t* counters, hipStream_t s);
 hipError_t launch_topp(const CacheView& c, const CandView& cand, const float* logits, int ncap, float p,
                        int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
-                       int mask_words, int32_t* counters, int32_t* union_tok, int32_t* union_cnt,
-                       hipStream_t s);
+                       int mask_words, int32_t* union_tok, int32_t* union_row,
+                       int32_t* union_cnt, hipStream_t s);
 hipError_t launch_csr_emit(const CacheView& c, const int32_t* union_tok, const int32_t* union_cnt, int ncap,
                            int32_t* indptr, int32_t* tokens, int64_t capacity, hipStream_t s);
 // tokens per attention chunk for an upper bound of the total selected tokens
