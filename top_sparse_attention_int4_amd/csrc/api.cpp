@@ -90,7 +90,7 @@ struct Layout {
   int chunk_tokens = 64;  // attention chunk
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, logits = 0, masks = 0, utok = 0, urow = 0, ucnt = 0,
-         counters = 0, parts = 0, thr = 0, total = 0;
+         ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, total = 0;
 };
 
 // ncap_of(maxcand): the top-p block holds 1024*E candidates, E a power of two up to 64.
@@ -116,13 +116,15 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->scores = take((size_t)U * c->max_pages_per_seq * 4);
   L->pages = take((size_t)U * c->max_pages_per_seq * 4);
   L->pcnt = take((size_t)U * 4);
+  L->pphys = take((size_t)U * c->max_pages_per_seq * 4);
   L->rpre = take((size_t)U * (ncap + 1) * 4);
   L->logits = take((size_t)BH * ncap * 4);
   L->masks = take((size_t)BH * (ncap / 32) * 4);
   L->utok = take((size_t)U * ncap * 4);
   L->urow = take((size_t)U * ncap * 4);
   L->ucnt = take((size_t)U * 4);
-  L->counters = take((size_t)U * 4);
+  L->ctok = take((size_t)U * ncap * 4);
+  L->crow = take((size_t)U * ncap * 4);
   L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
   L->thr = take((size_t)BH * 4);
   L->total = off;
@@ -198,23 +200,26 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
     TWL_TRY(E.rec(1));
     TWL_TRY(E.rec(2));
     TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), prm->keep_frac, cache->max_pages_per_seq,
+                               at<int32_t>(ws, L.pphys),
                                at<int32_t>(ws, L.pages), at<int32_t>(ws, L.pcnt), s));
     TWL_TRY(E.rec(3));
     cand.mode = kCandPages;
     cand.items = at<int32_t>(ws, L.pages);
     cand.count = at<int32_t>(ws, L.pcnt);
     cand.max_items = cache->max_pages_per_seq;
+    cand.phys = at<int32_t>(ws, L.pphys);
   } else {
     for (int i = 0; i < 4; ++i) TWL_TRY(E.rec(i));
     cand.mode = kCandAll;
   }
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   TWL_TRY(E.rec(4));
-  TWL_TRY(launch_estimate(c, qb, prm->sm_scale, cand, (int)ncap, at<float>(ws, L.logits),
-                          at<int32_t>(ws, L.counters), s));
+  TWL_TRY(launch_estimate(c, qb, prm->sm_scale, cand, (int)ncap, at<float>(ws, L.logits), at<int32_t>(ws, L.ctok),
+                          at<int32_t>(ws, L.crow), s));
   TWL_TRY(E.rec(5));
   TWL_TRY(E.rec(6));
-  TWL_TRY(launch_topp(c, cand, at<float>(ws, L.logits), (int)ncap, prm->p, prm->iters, thr, nullptr,
+  TWL_TRY(launch_topp(c, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), (int)ncap,
+                      prm->p, prm->iters, thr, nullptr,
                       at<uint32_t>(ws, L.masks), nullptr, 0,
                       at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s));
   TWL_TRY(E.rec(7));
@@ -271,7 +276,7 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheView c = make_view(cache);
   TWL_TRY(launch_page_score(c, static_cast<const uint16_t*>(q), at<float>(ws, L.scores), s));
-  TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), keep_frac, max_keep, page_ids, count, s));
+  TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), keep_frac, max_keep, nullptr, page_ids, count, s));
   return TWL_OK;
 }
 
@@ -325,8 +330,9 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
     TWL_TRY(launch_range_prefix(c, cv, at<int32_t>(ws, L.rpre), s));
   }
   TWL_TRY(launch_estimate(c, static_cast<const uint16_t*>(q), sm_scale, cv, (int)ncap, at<float>(ws, L.logits),
-                          at<int32_t>(ws, L.counters), s));
-  TWL_TRY(launch_topp(c, cv, at<float>(ws, L.logits), (int)ncap, p, iters, threshold, mass,
+                          at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), s));
+  TWL_TRY(launch_topp(c, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), (int)ncap, p,
+                      iters, threshold, mass,
                       at<uint32_t>(ws, L.masks), head_mask, mask_words,
                       at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s));
   TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(128) void k_merge(CacheView c, ListView L, int CH, 
       __syncthreads();
       const int kn = min(128, nch - k0);
       const float* po = base + (size_t)k0 * kStep + 2 + tid;
-#pragma unroll 8
+#pragma unroll 16
       for (int i = 0; i < kn; ++i) Os += po[i * kStep] * sc[i];
       __syncthreads();
     }

@@ -9,6 +9,12 @@
 //   a_g = fold_{c in g}(a + q_c*code_c),  t_g = fl(s_g*a_g) + fl(z_g*b_g),
 //   logit = fl(sm * ((t_0 + t_1) + (t_2 + t_3))).
 // The file is compiled without floating-point contraction so that t_g rounds each product.
+//
+// A block holds 4 batches of 64 candidates x 4 waves; wave g handles group g of every candidate, reading only its
+// 16-byte slice of the code row and its scale/zero pair.  The query values of a wave's group are
+// wave-uniform and live in scalar registers.  The per-group terms meet in LDS and are combined in the
+// committed order.  The block also records, per candidate, its token id and K/V row index, which the
+// union of the kept sets then gathers without further lookups.
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -60,83 +66,131 @@ __global__ __launch_bounds__(256) void k_range_prefix(CacheView c, CandView cand
   if (threadIdx.x == 0) pre[cnt] = carry;
 }
 
-// One block = 64 candidates x 4 waves; wave g handles quantisation group g (32 channels) of every
-// candidate for all G heads, so each wave reads only its 16-byte slice of the code row and its
-// scale/zero pair.  The per-group terms meet in LDS and are combined in the committed order.
+constexpr int kEstBatches = 4;  // 64-candidate batches per block
+
+// Token id and K/V row of candidate k (row -1 when k is not a candidate).  `cnt` is the unit's item
+// count for the page and range forms.
+__device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView& cand, int u, int b, int h, int k,
+                                             int n, int cnt, int& tok, int& row) {
+  tok = -1;
+  row = -1;
+  if (cand.mode == kCandPages && cand.phys) {
+    const int pi = k >> 4;
+    if (pi < cnt) {
+      const size_t idx = (size_t)u * cand.max_items + pi;
+      const int page = cand.items[idx];
+      const int phys = cand.phys[idx];
+      const int t = page * kPage + (k & 15);
+      if (page >= 0 && t < n) {
+        tok = t;
+        row = (phys * c.Hkv + h) * kPage + (k & 15);
+      }
+    }
+    return;
+  }
+  tok = cand_token(cand, u, k, n);
+  if (tok >= 0) row = (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15);
+}
+
 template <int G>
 __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
                                                   CandView cand, int ncap, int chunks_per_unit,
-                                                  float* __restrict__ logits, int32_t* counters) {
+                                                  float* __restrict__ logits, int32_t* __restrict__ cand_tok,
+                                                  int32_t* __restrict__ cand_row) {
+  constexpr int NB = kEstBatches;
   const int u = blockIdx.x / chunks_per_unit;
   const int ck = blockIdx.x - u * chunks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  if (ck == 0 && threadIdx.x == 0) counters[u] = 0;  // arrival counter of the group's top-p blocks
+  const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  __shared__ float T[2][kGroups][G][64];
 
-  __shared__ float qs[G][kD];
-  __shared__ float bs[G][kGroups];
-  __shared__ float T[kGroups][G][64];
-  const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
-  for (int i = threadIdx.x; i < G * kD; i += 256) qs[i / kD][i % kD] = __uint_as_float((uint32_t)qg[i] << 16);
-  __syncthreads();
-  if (threadIdx.x < G * kGroups) {
-    const int hh = threadIdx.x / kGroups, g = threadIdx.x % kGroups;
-    float acc = 0.f;
-    for (int ch = g * 32; ch < g * 32 + 32; ++ch) acc = acc + qs[hh][ch];
-    bs[hh][g] = acc;
-  }
-  __syncthreads();
-
-  const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // resolve every batch's candidates, then issue all code and scale/zero loads at once
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int k = ck * 64 + lane;
-  const int tok = cand_token(cand, u, k, n);
-  if (tok >= 0) {
-    const int phys = c.page_table[(size_t)b * c.maxP + (tok >> 4)];
-    const size_t row = ((size_t)phys * c.Hkv + h) * kPage + (tok & 15);
-    const uint4 cw = reinterpret_cast<const uint4*>(c.k4 + row * 64)[g];
-    const uint32_t mw = c.k4_meta[row * kGroups + g];
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
-    float a[G];
+  const int cnt = (cand.mode == kCandAll) ? 0 : clampi(cand.count[u], 0, cand.max_items);
+  const int kbase = ck * (64 * NB) + lane;
+  int tokv[NB], rowv[NB];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) a[hh] = 0.f;
+  for (int bt = 0; bt < NB; ++bt) cand_resolve(c, cand, u, b, h, kbase + 64 * bt, n, cnt, tokv[bt], rowv[bt]);
+  uint4 cwv[NB];
+  uint32_t mwv[NB];
 #pragma unroll
-    for (int wi = 0; wi < 4; ++wi) {
-      const uint32_t lo = words[wi] & 0x0F0F0F0Fu;
-      const uint32_t hi = (words[wi] >> 4) & 0x0F0F0F0Fu;
-      float code[8];
-      code[0] = (float)(lo & 0xFFu);
-      code[1] = (float)(hi & 0xFFu);
-      code[2] = (float)((lo >> 8) & 0xFFu);
-      code[3] = (float)((hi >> 8) & 0xFFu);
-      code[4] = (float)((lo >> 16) & 0xFFu);
-      code[5] = (float)((hi >> 16) & 0xFFu);
-      code[6] = (float)(lo >> 24);
-      code[7] = (float)(hi >> 24);
+  for (int bt = 0; bt < NB; ++bt) {
+    if (rowv[bt] >= 0) {
+      cwv[bt] = reinterpret_cast<const uint4*>(c.k4 + (size_t)rowv[bt] * 64)[g];
+      mwv[bt] = c.k4_meta[(size_t)rowv[bt] * kGroups + g];
+    } else {
+      cwv[bt] = make_uint4(0u, 0u, 0u, 0u);
+      mwv[bt] = 0u;
+    }
+  }
+
+  // this wave's 32 query channels per head, as bf16 pairs (wave-uniform: scalar loads)
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * c.Hq + (size_t)h * G) * kD) + g * 16;
+  float bsum[G];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ch = g * 32 + wi * 8 + e;
+  for (int hh = 0; hh < G; ++hh) {
+    float acc = 0.f;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) a[hh] = fmaf(qs[hh][ch], code[e], a[hh]);
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w = qw[hh * 64 + i];
+      acc = acc + bf16_lo(w);
+      acc = acc + bf16_hi(w);
+    }
+    bsum[hh] = acc;
+  }
+
+#pragma unroll
+  for (int bt = 0; bt < NB; ++bt) {
+    const int k = kbase + 64 * bt;
+    if (rowv[bt] >= 0) {
+      // the group's 32 codes as floats (element 2j of byte j is its low nibble)
+      const uint32_t words[4] = {cwv[bt].x, cwv[bt].y, cwv[bt].z, cwv[bt].w};
+      float code[32];
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi) {
+        const uint32_t lo = words[wi] & 0x0F0F0F0Fu;
+        const uint32_t hi = (words[wi] >> 4) & 0x0F0F0F0Fu;
+        code[8 * wi + 0] = (float)(lo & 0xFFu);
+        code[8 * wi + 1] = (float)(hi & 0xFFu);
+        code[8 * wi + 2] = (float)((lo >> 8) & 0xFFu);
+        code[8 * wi + 3] = (float)((hi >> 8) & 0xFFu);
+        code[8 * wi + 4] = (float)((lo >> 16) & 0xFFu);
+        code[8 * wi + 5] = (float)((hi >> 16) & 0xFFu);
+        code[8 * wi + 6] = (float)(lo >> 24);
+        code[8 * wi + 7] = (float)(hi >> 24);
+      }
+      const float s = half_bits_to_float(mwv[bt] & 0xffffu);
+      const float z = half_bits_to_float(mwv[bt] >> 16);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        // head-outer order keeps only one head's 32 query values in scalar registers at a time
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t w = qw[hh * 64 + i];  // channels 32g + 2i, 2i + 1
+          a = fmaf(bf16_lo(w), code[2 * i], a);
+          a = fmaf(bf16_hi(w), code[2 * i + 1], a);
+        }
+        const float sa = s * a;
+        const float zb = z * bsum[hh];
+        T[bt & 1][g][hh][lane] = sa + zb;
       }
     }
-    const float s = half_bits_to_float(mw & 0xffffu);
-    const float z = half_bits_to_float(mw >> 16);
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float sa = s * a[hh];
-      const float zb = z * bs[hh][g];
-      T[g][hh][lane] = sa + zb;
+    if (g == 0 && k < ncap) {
+      cand_tok[(size_t)u * ncap + k] = tokv[bt];
+      cand_row[(size_t)u * ncap + k] = rowv[bt];
     }
-  }
-  __syncthreads();
-  for (int hh = g; hh < G; hh += kGroups) {
-    float lg = -__builtin_inff();
-    if (tok >= 0) {
-      const float r01 = T[0][hh][lane] + T[1][hh][lane];
-      const float r23 = T[2][hh][lane] + T[3][hh][lane];
-      lg = sm * (r01 + r23);
+    __syncthreads();  // T[bt & 1] complete; T[(bt + 1) & 1] was last read before this barrier
+    for (int hh = g; hh < G; hh += kGroups) {
+      float lg = -__builtin_inff();
+      if (rowv[bt] >= 0) {
+        const float r01 = T[bt & 1][0][hh][lane] + T[bt & 1][1][hh][lane];
+        const float r23 = T[bt & 1][2][hh][lane] + T[bt & 1][3][hh][lane];
+        lg = sm * (r01 + r23);
+      }
+      if (k < ncap) logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
     }
-    if (k < ncap) logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
   }
 }
 
@@ -146,16 +200,22 @@ hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t
 }
 
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
-                           float* logits, int32_t* counters, hipStream_t s) {
-  const int cpu = (ncap + 63) / 64;
+                           float* logits, int32_t* cand_tok, int32_t* cand_row, hipStream_t s) {
+  const int cpu = (ncap + 64 * kEstBatches - 1) / (64 * kEstBatches);
   dim3 grid((unsigned)(c.B * c.Hkv * cpu));
+#define TWL_EST_CASE(GG)                                                                                   \
+  case GG:                                                                                                 \
+    hipLaunchKernelGGL(k_estimate<GG>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, cand_tok, \
+                       cand_row);                                                                          \
+    break;
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_estimate<1>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, counters); break;
-    case 2: hipLaunchKernelGGL(k_estimate<2>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, counters); break;
-    case 4: hipLaunchKernelGGL(k_estimate<4>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, counters); break;
-    case 8: hipLaunchKernelGGL(k_estimate<8>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, counters); break;
+    TWL_EST_CASE(1)
+    TWL_EST_CASE(2)
+    TWL_EST_CASE(4)
+    TWL_EST_CASE(8)
     default: return hipErrorInvalidValue;
   }
+#undef TWL_EST_CASE
   return hipGetLastError();
 }
 

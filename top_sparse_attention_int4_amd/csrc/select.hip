@@ -8,15 +8,18 @@
 // max(q*kmin, q*kmax) = q+ * kmax + q- * kmin with q+ = max(q,0), q- = min(q,0): the second product
 // is then an exact zero and adding it changes nothing, so two fused multiply-adds per channel and
 // head reproduce the fold bit for bit without a compare.  Each wave of a block folds one query head
-// for the block's 64 pages; the group score then folds the heads in order.
+// for the block's 64 pages (read from an LDS copy of the bounds that the whole block loads with
+// coalesced accesses); the group score then folds the heads in order.
 #include "twl_device.h"
 #include "twl_internal.h"
 
 namespace twl {
 
 template <int G>
-__global__ __launch_bounds__(64 * G) void k_page_score(CacheView c, const uint16_t* __restrict__ q,
-                                                       float* __restrict__ scores, int blocks_per_unit) {
+__global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score(CacheView c, const uint16_t* __restrict__ q,
+                                                                     float* __restrict__ scores,
+                                                                     int blocks_per_unit) {
+  constexpr int NT = 64 * (G > 4 ? G : 4);
   const int u = blockIdx.x / blocks_per_unit;
   const int blk = blockIdx.x - u * blocks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
@@ -25,11 +28,22 @@ __global__ __launch_bounds__(64 * G) void k_page_score(CacheView c, const uint16
   if (blk * 64 >= P) return;
   const int hh = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
+  // the block's 64 pages of bounds, staged with coalesced loads (row = 32 x 16 B, padded by 16 B)
+  __shared__ uint4 tile[64][33];
   __shared__ float qpos[G][kD];
   __shared__ float qneg[G][kD];
   __shared__ float sig[G][64];
+  const int32_t* pt = c.page_table + (size_t)b * c.maxP;
+  for (int i = threadIdx.x; i < 64 * 32; i += NT) {
+    const int pg = i >> 5, part = i & 31;
+    const int j = blk * 64 + pg;
+    if (j < P) {
+      const uint4* bnd = reinterpret_cast<const uint4*>(c.kbound + ((size_t)pt[j] * c.Hkv + h) * 2 * kD);
+      tile[pg][part] = bnd[part];
+    }
+  }
   const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
-  for (int i = threadIdx.x; i < G * kD; i += 64 * G) {
+  for (int i = threadIdx.x; i < G * kD; i += NT) {
     const float x = __uint_as_float((uint32_t)qg[i] << 16);
     qpos[i / kD][i % kD] = x > 0.f ? x : 0.f;
     qneg[i / kD][i % kD] = x < 0.f ? x : 0.f;
@@ -37,20 +51,13 @@ __global__ __launch_bounds__(64 * G) void k_page_score(CacheView c, const uint16
   __syncthreads();
 
   const int j = blk * 64 + lane;
-  if (j < P) {
-    const int phys = c.page_table[(size_t)b * c.maxP + j];
-    const uint4* bnd = reinterpret_cast<const uint4*>(c.kbound + ((size_t)phys * c.Hkv + h) * 2 * kD);
-    uint4 mnv[16], mxv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      mnv[i] = bnd[i];
-      mxv[i] = bnd[16 + i];
-    }
+  if (hh < G && j < P) {
     float acc = 0.f;
 #pragma unroll
     for (int c8 = 0; c8 < 16; ++c8) {
-      const uint32_t wm[4] = {mnv[c8].x, mnv[c8].y, mnv[c8].z, mnv[c8].w};
-      const uint32_t wx[4] = {mxv[c8].x, mxv[c8].y, mxv[c8].z, mxv[c8].w};
+      const uint4 mnv = tile[lane][c8], mxv = tile[lane][16 + c8];
+      const uint32_t wm[4] = {mnv.x, mnv.y, mnv.z, mnv.w};
+      const uint32_t wx[4] = {mxv.x, mxv.y, mxv.z, mxv.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int ch = c8 * 8 + e;
@@ -84,11 +91,13 @@ constexpr int kSelLdsKeys = 8192;
 // integer histograms), ties at the threshold key resolved towards lower page ids, then an
 // order-preserving compaction writes the kept page ids in ascending order.
 __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* __restrict__ scores,
-                                                      float keep_frac, int max_keep, int32_t* page_ids,
-                                                      int32_t* count) {
+                                                      float keep_frac, int max_keep, int32_t* page_phys,
+                                                      int32_t* page_ids, int32_t* count) {
   constexpr int NT = 1024, NW = NT / 64;
   const int u = blockIdx.x;
   const int b = u / c.Hkv;
+  const int32_t* pt = c.page_table + (size_t)b * c.maxP;
+  int32_t* phys_out = page_phys ? page_phys + (size_t)u * max_keep : nullptr;
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
   int K = 0;
@@ -100,7 +109,10 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
   if (K == 0) return;
   int32_t* out = page_ids + (size_t)u * max_keep;
   if (K == P) {
-    for (int i = threadIdx.x; i < P; i += NT) out[i] = i;
+    for (int i = threadIdx.x; i < P; i += NT) {
+      out[i] = i;
+      if (phys_out) phys_out[i] = pt[i];
+    }
     return;
   }
   const float* sc = scores + (size_t)u * c.maxP;
@@ -182,7 +194,10 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
     int r = eq_rank;
     for (int i = i0; i < i1; ++i) {
       const uint32_t k = key(i);
-      if (k < T || (k == T && r < take_eq)) out[pos++] = i;
+      if (k < T || (k == T && r < take_eq)) {
+        if (phys_out) phys_out[pos] = pt[i];
+        out[pos++] = i;
+      }
       r += (k == T);
     }
   }
@@ -192,8 +207,8 @@ hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* score
   const int bpu = (c.maxP + 63) / 64;
   dim3 grid((unsigned)(c.B * c.Hkv * bpu));
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_page_score<1>, grid, dim3(64), 0, s, c, q, scores, bpu); break;
-    case 2: hipLaunchKernelGGL(k_page_score<2>, grid, dim3(128), 0, s, c, q, scores, bpu); break;
+    case 1: hipLaunchKernelGGL(k_page_score<1>, grid, dim3(256), 0, s, c, q, scores, bpu); break;
+    case 2: hipLaunchKernelGGL(k_page_score<2>, grid, dim3(256), 0, s, c, q, scores, bpu); break;
     case 4: hipLaunchKernelGGL(k_page_score<4>, grid, dim3(256), 0, s, c, q, scores, bpu); break;
     case 8: hipLaunchKernelGGL(k_page_score<8>, grid, dim3(512), 0, s, c, q, scores, bpu); break;
     default: return hipErrorInvalidValue;
@@ -201,10 +216,10 @@ hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* score
   return hipGetLastError();
 }
 
-hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep,
+hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep, int32_t* page_phys,
                               int32_t* page_ids, int32_t* count, hipStream_t s) {
   hipLaunchKernelGGL(k_page_select, dim3((unsigned)(c.B * c.Hkv)), dim3(1024), 0, s, c, scores, keep_frac,
-                     max_keep, page_ids, count);
+                     max_keep, page_phys, page_ids, count);
   return hipGetLastError();
 }
 

@@ -25,66 +25,7 @@
 
 namespace twl {
 
-__device__ int cand_token_topp(const CandView& cand, int u, int k, int n) {
-  const int P = (n + kPage - 1) / kPage;
-  if (cand.mode == kCandAll) return k < n ? k : -1;
-  if (cand.mode == kCandPages) {
-    const int cnt = clampi(cand.count[u], 0, cand.max_items);
-    const int pi = k >> 4;
-    if (pi >= cnt) return -1;
-    const int page = cand.items[(size_t)u * cand.max_items + pi];
-    if (page < 0 || page >= P) return -1;
-    const int t = page * kPage + (k & 15);
-    return t < n ? t : -1;
-  }
-  const int cnt = clampi(cand.count[u], 0, cand.max_items);
-  const int32_t* pre = cand.range_prefix + (size_t)u * (cand.max_items + 1);
-  if (k >= pre[cnt]) return -1;
-  int lo = 0, hi = cnt;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= k) lo = mid; else hi = mid;
-  }
-  const int t = cand.items[((size_t)u * cand.max_items + lo) * 2] + (k - pre[lo]);
-  return (t >= 0 && t < n) ? t : -1;
-}
-
-constexpr int kCap = 1024;  // weights handed to the single-wave phase
-
-// One bisection step of the single-wave phase over `n` compacted weights in `buf`; compacts the kept
-// bracket into `dst`, updates lo/hi and the mass above hi, and returns the new count.
-__device__ __forceinline__ int wave_step(const float* buf, float* dst, int n, uint32_t& lo, uint32_t& hi,
-                                         float& c_hi, float target) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t mid = lo + ((hi - lo) >> 1);
-  const float m = __uint_as_float(mid);
-  float f = 0.f;
-  for (int i = lane; i < n; i += 64) {
-    const float x = buf[i];
-    f += (x >= m) ? x : 0.f;
-  }
-  f = c_hi + wave_sum_dpp(f);
-  const bool up = f >= target;
-  const float klo = __uint_as_float(up ? mid : lo);
-  const float khi = __uint_as_float(up ? hi : mid);
-  float above = 0.f;
-  int base = 0;
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const int i = i0 + lane;
-    const float x = (i < n) ? buf[i] : -1.f;
-    const bool keep = (i < n) && x >= klo && x < khi;
-    if (i < n && x >= khi) above += x;
-    const unsigned long long bal = __ballot(keep);
-    const int pos =
-        base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (keep) dst[pos] = x;
-    base += __popcll(bal);
-  }
-  __builtin_amdgcn_wave_barrier();  // the next step reads what other lanes wrote
-  c_hi += wave_sum_dpp(above);
-  if (up) lo = mid; else hi = mid;
-  return base;
-}
+constexpr int kCap = 1024;  // weights handed to the single-wave phase (16 per lane)
 
 template <int E>
 __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restrict__ logits, int ncap, float p,
@@ -92,15 +33,16 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
                                                uint32_t* head_mask, int mask_words) {
   constexpr int NT = kToppThreads, NW = NT / 64;
   __shared__ float red[2 * NW * 4];
+  __shared__ int cnt_sm[2][NW];
   __shared__ int scan_sm[NW + 1];
-  __shared__ float buf[2][kCap];
+  __shared__ float buf[kCap];
   __shared__ uint32_t s_lo;
   BlockReduce<NW> br{red};
 
   const int bh = blockIdx.x;
   const float* lg = logits + (size_t)bh * ncap;
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  const int lane = tid & 63, wv = tid >> 6;
 
   float e[E];
   float mloc = -__builtin_inff();
@@ -111,43 +53,73 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     mloc = fmaxf(mloc, e[j]);
   }
   const float M = br.max(mloc);
-  float Z = 0.f, emin = __builtin_inff(), nval = 0.f;
+  float Z = 0.f, emin = __builtin_inff();
+  int nval_w = 0;  // wave-uniform count of existing candidates
   if (M != -__builtin_inff()) {
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       e[j] = (e[j] == -__builtin_inff()) ? -1.f : exp_diff(e[j], M);
-      if (e[j] >= 0.f) {
+      const bool ok = e[j] >= 0.f;
+      if (ok) {
         Z += e[j];
         emin = fminf(emin, e[j]);
-        nval += 1.f;
       }
+      nval_w += __popcll(__ballot(ok));
     }
   } else {
 #pragma unroll
     for (int j = 0; j < E; ++j) e[j] = -1.f;
   }
   br.sum_min(Z, emin);
-  nval = br.sum(nval);
+
+  // block-wide sum of f and of a wave-uniform count, with one barrier
+  int slot = 0;
+  auto block_f_count = [&](float& f, int& cnt) {
+    f = wave_sum_dpp(f);
+    float* r = red + slot * NW * 4;
+    int* cs = cnt_sm[slot];
+    slot ^= 1;
+    if (lane == 0) {
+      r[wv] = f;
+      cs[wv] = cnt;
+    }
+    __syncthreads();
+    float t = r[0];
+    int ct = cs[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) {
+      t += r[i];
+      ct += cs[i];
+    }
+    f = t;
+    cnt = ct;
+  };
+  {
+    float dummy = 0.f;
+    block_f_count(dummy, nval_w);
+  }
+  const int nval = nval_w;
 
   uint32_t lo = 0u;
   if (Z > 0.f && p < 1.0f) {
     const float target = p * Z;
     lo = __float_as_uint(emin);                // f(min e) = Z >= target
     uint32_t hi = __float_as_uint(1.0f) + 1u;  // e <= 1 = exp(0)
-    float n_lo = nval, n_hi = 0.f;             // #{e >= lo}, #{e >= hi}
+    int n_lo = nval, n_hi = 0;                 // #{e >= lo}, #{e >= hi}
     int it = 0;
-    // ---- block phase -------------------------------------------------------------------------
-    while (it < iters && hi - lo > 1u && n_lo - n_hi > (float)kCap) {
+    // ---- block phase: one fixed-order reduction of f(mid) and #{e >= mid} per step ------------
+    while (it < iters && hi - lo > 1u && n_lo - n_hi > kCap) {
       const uint32_t mid = lo + ((hi - lo) >> 1);
       const float m = __uint_as_float(mid);
-      float f = 0.f, cm = 0.f;
+      float f = 0.f;
+      int cm = 0;
 #pragma unroll
       for (int j = 0; j < E; ++j) {
         const bool ge = e[j] >= m;
         f += ge ? e[j] : 0.f;
-        cm += ge ? 1.f : 0.f;
+        cm += __popcll(__ballot(ge));
       }
-      br.sum2(f, cm);
+      block_f_count(f, cm);
       if (f >= target) {
         lo = mid;
         n_lo = cm;
@@ -169,19 +141,74 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
       }
       int total;
       int pos = block_excl_scan<NW>(local, scan_sm, &total);
-      float c_hi = br.sum(above);
+      const float c_hi = br.sum(above);  // mass at or above the bracket
 #pragma unroll
       for (int j = 0; j < E; ++j)
-        if (e[j] >= mlo && e[j] < mhi) buf[0][pos++] = e[j];
+        if (e[j] >= mlo && e[j] < mhi) buf[pos++] = e[j];
       __syncthreads();
       if (wv == 0) {
-        int n = min(total, kCap), cur = 0;
-        while (it < iters && hi - lo > 1u && n > 0) {
-          n = wave_step(buf[cur], buf[cur ^ 1], n, lo, hi, c_hi, target);
-          cur ^= 1;
+        // the bracket's weights, 16 per lane (-1 marks an empty slot)
+        float xs[kCap / 64];
+        const int nb0 = min(total, kCap);
+#pragma unroll
+        for (int i = 0; i < kCap / 64; ++i) xs[i] = (lane + 64 * i < nb0) ? buf[lane + 64 * i] : -1.f;
+        int c_lo = nb0, c_hi_n = 0;  // #{x >= lo}, #{x >= hi} among the register weights
+        bool exact = false;
+        while (it < iters && hi - lo > 1u) {
+          const uint32_t need = 32u - (uint32_t)__clz((int)(hi - lo - 1u));  // steps left to converge
+          if (c_lo - c_hi_n <= 64 && (uint32_t)(iters - it) >= need) {
+            exact = true;
+            break;
+          }
+          const uint32_t mid = lo + ((hi - lo) >> 1);
+          const float m = __uint_as_float(mid);
+          float f = 0.f;
+          int cm = 0;
+#pragma unroll
+          for (int i = 0; i < kCap / 64; ++i) {
+            const bool ge = xs[i] >= m;
+            f += ge ? xs[i] : 0.f;
+            cm += __popcll(__ballot(ge));
+          }
+          f = c_hi + wave_sum_dpp(f);
+          if (f >= target) {
+            lo = mid;
+            c_lo = cm;
+          } else {
+            hi = mid;
+            c_hi_n = cm;
+          }
           ++it;
         }
-        if (tid == 0) s_lo = lo;
+        if (exact) {
+          // Finish in one step: the converged threshold is the largest weight x in the bracket with
+          // f(x) >= target, and every lane evaluates f at one of the (at most 64) bracket weights.
+          const float mlo2 = __uint_as_float(lo), mhi2 = __uint_as_float(hi);
+          float mabove = 0.f;
+          int base = 0;
+          float y = -1.f;
+#pragma unroll
+          for (int i = 0; i < kCap / 64; ++i) {
+            const bool inb = xs[i] >= mlo2 && xs[i] < mhi2;
+            mabove += (xs[i] >= mhi2) ? xs[i] : 0.f;
+            const unsigned long long bal = __ballot(inb);
+            const int r = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (inb) buf[r] = xs[i];
+            base += __popcll(bal);
+          }
+          __builtin_amdgcn_wave_barrier();
+          const int nb = base;
+          y = (lane < nb) ? buf[lane] : -1.f;
+          float fy = c_hi + wave_sum_dpp(mabove);
+          for (int i = 0; i < nb; ++i) {
+            const float yi = readlane_f(y, i);
+            fy += (yi >= y) ? yi : 0.f;
+          }
+          const float best = wave_max_dpp((lane < nb && fy >= target) ? y : -1.f);
+          if (best >= 0.f) lo = __float_as_uint(best);
+        }
+        if (lane == 0) s_lo = lo;
       }
       __syncthreads();
       lo = s_lo;
@@ -199,7 +226,6 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
 
   // head mask: bit k of the head's bitmap <=> candidate k kept
   const int mw = ncap / 32;
-  const int lane = tid & 63;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const unsigned long long bal = __ballot(e[j] >= m);
@@ -215,70 +241,67 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   }
 }
 
-// One block per unit: OR the unit's G head masks, write the kept token ids in ascending order, their
-// K/V row indices, and the count.  A mask word covers 32 candidates, i.e. two pages when candidates
-// are whole pages, so the page-id and page-table lookups are made once per word, not per token.
-__global__ __launch_bounds__(1024) void k_union(CacheView c, CandView cand, const uint32_t* __restrict__ mask_ws,
-                                                int ncap, int32_t* union_tok, int32_t* union_row,
-                                                int32_t* union_cnt) {
+// One block per unit: OR the unit's G head masks and write the kept token ids (ascending), their K/V
+// row indices and the count.  First every thread forms the union of its mask words (all loads in
+// flight together) and the block scans their popcounts into per-word output offsets in LDS; then
+// thread t of pass j handles candidate j*1024 + t, so the gathers of the ids and rows the estimate
+// recorded, and the writes of the kept ones, are coalesced.
+template <int E, int G>
+__global__ __launch_bounds__(1024) void k_union(CacheView c, const uint32_t* __restrict__ mask_ws,
+                                                const int32_t* __restrict__ cand_tok,
+                                                const int32_t* __restrict__ cand_row, int ncap, int32_t* union_tok,
+                                                int32_t* union_row, int32_t* union_cnt) {
   constexpr int NT = 1024, NW = NT / 64;
+  constexpr int MW = E * 32;                 // mask words per head (ncap / 32)
+  constexpr int WPT = (MW + NT - 1) / NT;    // words per thread
+  __shared__ uint32_t uw[MW];
+  __shared__ int woff[MW];
   __shared__ int scan_sm[NW + 1];
   const int u = blockIdx.x;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int mw = ncap / 32;
-  const uint32_t* m0 = mask_ws + ((size_t)b * c.Hq + (size_t)h * c.G) * mw;
-  const int wpt = (mw + NT - 1) / NT;  // contiguous words per thread keep the token order
-  const int w0 = min(mw, (int)threadIdx.x * wpt), w1 = min(mw, w0 + wpt);
+  const int tid = threadIdx.x;
+  const uint32_t* m0 = mask_ws + ((size_t)b * c.Hq + (size_t)h * G) * MW;
+  uint32_t words[WPT];
   int local = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = 0u;
-    for (int hh = 0; hh < c.G; ++hh) bits |= m0[(size_t)hh * mw + w];
-    local += __popc(bits);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    uint32_t x = 0u;
+    if (w < MW) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) x |= m0[(size_t)hh * MW + w];
+    }
+    words[i] = x;
+    local += __popc(x);
   }
   int total;
-  int pos = block_excl_scan<NW>(local, scan_sm, &total);
-  int32_t* out = union_tok + (size_t)u * ncap;
-  int32_t* rows = union_row + (size_t)u * ncap;
-  const int32_t* pt = c.page_table + (size_t)b * c.maxP;
-  const int cnt = clampi(cand.mode == kCandAll ? 0 : cand.count[u], 0, cand.max_items);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = 0u;
-    for (int hh = 0; hh < c.G; ++hh) bits |= m0[(size_t)hh * mw + w];
-    if (!bits) continue;
-    if (cand.mode == kCandRanges) {
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1u;
-        const int t = cand_token_topp(cand, u, w * 32 + bit, n);
-        out[pos] = t;
-        rows[pos] = (pt[t >> 4] * c.Hkv + h) * kPage + (t & 15);
-        ++pos;
-      }
-      continue;
-    }
-    // the two pages of this word (kept bits are valid candidates, so their pages exist)
-    int page0, page1;
-    if (cand.mode == kCandPages) {
-      const int32_t* items = cand.items + (size_t)u * cand.max_items;
-      page0 = (2 * w < cnt) ? items[2 * w] : 0;
-      page1 = (2 * w + 1 < cnt) ? items[2 * w + 1] : 0;
-    } else {
-      page0 = 2 * w;
-      page1 = 2 * w + 1;
-    }
-    const int phys0 = (bits & 0xffffu) ? pt[page0] : 0;
-    const int phys1 = (bits >> 16) ? pt[page1] : 0;
-    while (bits) {
-      const int bit = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      const int hi = bit >> 4, slot = bit & 15;
-      out[pos] = (hi ? page1 : page0) * kPage + slot;
-      rows[pos] = ((hi ? phys1 : phys0) * c.Hkv + h) * kPage + slot;
-      ++pos;
+  int off = block_excl_scan<NW>(local, scan_sm, &total);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    if (w < MW) {
+      uw[w] = words[i];
+      woff[w] = off;
+      off += __popc(words[i]);
     }
   }
-  if (threadIdx.x == 0) union_cnt[u] = total;
+  __syncthreads();
+  const int32_t* ct = cand_tok + (size_t)u * ncap;
+  const int32_t* cr = cand_row + (size_t)u * ncap;
+  int32_t* out = union_tok + (size_t)u * ncap;
+  int32_t* rows = union_row + (size_t)u * ncap;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const int k = j * NT + tid;
+    const uint32_t x = uw[k >> 5];
+    const int bit = k & 31;
+    if ((x >> bit) & 1u) {
+      const int pos = woff[k >> 5] + __popc(x & ((1u << bit) - 1u));
+      out[pos] = ct[k];
+      rows[pos] = cr[k];
+    }
+  }
+  if (tid == 0) union_cnt[u] = total;
 }
 
 __global__ __launch_bounds__(256) void k_csr_emit(CacheView c, const int32_t* __restrict__ union_tok,
@@ -310,7 +333,8 @@ int topp_elems_per_thread(int64_t ncap) {
   return 0;
 }
 
-hipError_t launch_topp(const CacheView& c, const CandView& cand, const float* logits, int ncap, float p,
+hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_t* cand_row, const float* logits,
+                       int ncap, float p,
                        int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
                        int mask_words, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt,
                        hipStream_t s) {
@@ -334,8 +358,34 @@ hipError_t launch_topp(const CacheView& c, const CandView& cand, const float* lo
 #undef TWL_TOPP_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_union, dim3((unsigned)(c.B * c.Hkv)), dim3(1024), 0, s, c, cand, mask_ws, ncap, union_tok,
-                     union_row, union_cnt);
+  dim3 ugrid((unsigned)(c.B * c.Hkv));
+#define TWL_UNION_G(EE, GG)                                                                                \
+  case GG:                                                                                                 \
+    hipLaunchKernelGGL((k_union<EE, GG>), ugrid, block, 0, s, c, mask_ws, cand_tok, cand_row, ncap,      \
+                       union_tok, union_row, union_cnt);                                                 \
+    break;
+#define TWL_UNION_CASE(EE)        \
+  case EE:                        \
+    switch (c.G) {                \
+      TWL_UNION_G(EE, 1)          \
+      TWL_UNION_G(EE, 2)          \
+      TWL_UNION_G(EE, 4)          \
+      TWL_UNION_G(EE, 8)          \
+      default: return hipErrorInvalidValue; \
+    }                             \
+    break;
+  switch (E) {
+    TWL_UNION_CASE(1)
+    TWL_UNION_CASE(2)
+    TWL_UNION_CASE(4)
+    TWL_UNION_CASE(8)
+    TWL_UNION_CASE(16)
+    TWL_UNION_CASE(32)
+    TWL_UNION_CASE(64)
+    default: return hipErrorInvalidValue;
+  }
+#undef TWL_UNION_G
+#undef TWL_UNION_CASE
   return hipGetLastError();
 }
 

@@ -30,6 +30,7 @@ struct CandView {
   const int32_t* count;         // [U]
   const int32_t* range_prefix;  // [U][max_items+1] (ranges only; written by launch_range_prefix)
   int max_items;
+  const int32_t* phys;          // pages only, optional: physical page of each listed page id
 };
 
 // Token list of each unit for the attention stage: either padded rows (stride) with counts, or CSR.
@@ -45,12 +46,13 @@ struct ListView {
 hipError_t launch_quantize(const CacheView& c, const int32_t* tok_begin, const int32_t* tok_end,
                            int span_pages, hipStream_t s);
 hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* scores, hipStream_t s);
-hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep,
+hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep, int32_t* page_phys,
                               int32_t* page_ids, int32_t* count, hipStream_t s);
 hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, hipStream_t s);
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
-                           float* logits, int32_t* counters, hipStream_t s);
-hipError_t launch_topp(const CacheView& c, const CandView& cand, const float* logits, int ncap, float p,
+                           float* logits, int32_t* cand_tok, int32_t* cand_row, hipStream_t s);
+hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_t* cand_row, const float* logits,
+                       int ncap, float p,
                        int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
                        int mask_words, int32_t* union_tok, int32_t* union_row,
                        int32_t* union_cnt, hipStream_t s);
