@@ -113,18 +113,17 @@ __global__ __launch_bounds__(64) void k_attn(CacheView c, const uint16_t* __rest
       for (int i = 0; i < 8; ++i) acc[hh][i] = 0.f;
 
     const int32_t* rws = L.rows ? list_rows(L, u) : nullptr;
+    // K/V row of list entry idx (-1 past the chunk or for a token outside the sequence)
+    auto row_of = [&](int idx) -> int {
+      if (idx >= t_end) return -1;
+      if (rws) return rws[idx];
+      const int tok = toks[idx];
+      if (tok < 0 || tok >= n) return -1;
+      return (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15);
+    };
+    int row_next = row_of(t_begin + lane);
     for (int sb = t_begin; sb < t_end; sb += 64) {
-      const int idx = sb + lane;
-      int row = -1;  // K/V row index; rows < 2^31 is checked on the host
-      if (rws) {
-        if (idx < t_end) row = rws[idx];
-      } else {
-        const int tok = (idx < t_end) ? toks[idx] : -1;
-        if (tok >= 0 && tok < n) {
-          const int phys = c.page_table[(size_t)b * c.maxP + (tok >> 4)];
-          row = (phys * c.Hkv + h) * kPage + (tok & 15);
-        }
-      }
+      const int row = row_next;  // K/V row index; rows < 2^31 is checked on the host
       const unsigned long long vmask = __ballot(row >= 0);
 
       bf16x8_t kv[4][4];
@@ -142,6 +141,7 @@ __global__ __launch_bounds__(64) void k_attn(CacheView c, const uint16_t* __rest
         const int r = __shfl(row, grp + 4 * s);
         vv[s] = (r >= 0) ? *reinterpret_cast<const uint4*>(c.v + (size_t)r * kD + nn * 8) : make_uint4(0u, 0u, 0u, 0u);
       }
+      row_next = row_of(sb + 64 + lane);  // next sub-block's rows load while this one computes
 
       floatx4_t sacc[4];
 #pragma unroll

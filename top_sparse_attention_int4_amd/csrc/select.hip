@@ -34,13 +34,24 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score(CacheView c
   __shared__ float qneg[G][kD];
   __shared__ float sig[G][64];
   const int32_t* pt = c.page_table + (size_t)b * c.maxP;
-  for (int i = threadIdx.x; i < 64 * 32; i += NT) {
-    const int pg = i >> 5, part = i & 31;
-    const int j = blk * 64 + pg;
-    if (j < P) {
-      const uint4* bnd = reinterpret_cast<const uint4*>(c.kbound + ((size_t)pt[j] * c.Hkv + h) * 2 * kD);
-      tile[pg][part] = bnd[part];
+  {
+    // all page-table reads first, then all bound reads, so every load of the tile is in flight at once
+    constexpr int R = 64 * 32 / NT;
+    const int part = threadIdx.x & 31;
+    int phys[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int j = blk * 64 + ((int)threadIdx.x >> 5) + r * (NT / 32);
+      phys[r] = (j < P) ? pt[j] : -1;
     }
+    uint4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint4* src = reinterpret_cast<const uint4*>(c.kbound + ((size_t)max(phys[r], 0) * c.Hkv + h) * 2 * kD);
+      v[r] = (phys[r] >= 0) ? src[part] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile[((int)threadIdx.x >> 5) + r * (NT / 32)][part] = v[r];
   }
   const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
   for (int i = threadIdx.x; i < G * kD; i += NT) {
@@ -123,8 +134,20 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
   __shared__ int s_rem;
   __shared__ int scan_sm[NW + 1];
   const bool in_lds = P <= kSelLdsKeys;
-  if (in_lds)
-    for (int i = threadIdx.x; i < P; i += NT) keys[i] = desc_key(sc[i]);
+  if (in_lds) {
+    constexpr int R = kSelLdsKeys / NT;  // all score loads in flight together
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = (int)threadIdx.x + r * NT;
+      v[r] = (i < P) ? sc[i] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = (int)threadIdx.x + r * NT;
+      if (i < P) keys[i] = desc_key(v[r]);
+    }
+  }
   for (int i = threadIdx.x; i < 512; i += NT) (&hist[0][0])[i] = 0;
   if (threadIdx.x == 0) {
     s_prefix = 0u;
