@@ -145,6 +145,9 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
  *   non-negative float32 weights keeping f(lo) >= p > f(hi); the kept set is {W_i >= lo}.  p = 1
  *   keeps every candidate.  With iters >= 31 the set equals the minimal top-p set up to ties and
  *   float32 rounding of the prefix masses; fewer steps return a superset whose mass still reaches p.
+ *   Above 65536 candidates per unit (up to 2^22) the same search decides 11 key bits per pass over
+ *   the weights from a mass histogram, with masses summed in 64-bit fixed point (2^-40 units of the
+ *   largest weight); `iters` < 31 then keeps the threshold's top `iters` key bits.
  * - Union (paperlayer §B.2): the kept tokens of a unit are the union over its G query heads.
  * Outputs:
  *   threshold  f32 [B][Hq]   the weight threshold m (required)
@@ -197,11 +200,25 @@ twl_status twl_decode_profiled(const twl_cache* cache, const void* q, const twl_
  * the `ranges` candidate form of twl_estimate_topp.
  *   centroids  bf16 [B][Hkv][num_clusters][128]; csize int32 [B][Hkv][num_clusters];
  *   coff       int32 [B][Hkv][num_clusters+1] token offsets (cluster c = tokens coff[c]..coff[c+1]-1)
- *   ranges     int32 [B][Hkv][num_clusters][2] (out);  count int32 [B][Hkv] (out) */
+ *   ranges     int32 [B][Hkv][num_clusters][2] (out);  count int32 [B][Hkv] (out)
+ *   num_clusters  1..65536; the workspace is sized by twl_workspace_bytes(cache, m), m >= num_clusters */
 twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float sm_scale, float p1,
                                     int32_t iters, const void* centroids, const int32_t* csize,
                                     const int32_t* coff, int32_t num_clusters, int32_t* ranges,
                                     int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole Double-P decode step ("Double-P", 方法详解 and 关键设计): twl_select_clusters_topp with
+ * p1, then twl_estimate_topp over the kept ranges with params->p (keep_frac is ignored), then the
+ * sparse attention over the union -- the same kernels as the split calls.  Unkept clusters are
+ * dropped.  Requires 2*num_clusters <= max_seq_len rounded up to the top-p capacity; the workspace
+ * is twl_workspace_bytes(cache, max_seq_len).  `events` is NULL or holds 2*TWL_NUM_STAGES events as
+ * for twl_decode_profiled, the stages being 0 cluster scores + cluster top-p + cluster union,
+ * 1 range prefix sums, 2 INT4 estimate, 3 token top-p + union, 4 attention, 5 merge. */
+twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_decode_params* params, float p1,
+                               const void* centroids, const int32_t* csize, const int32_t* coff,
+                               int32_t num_clusters, float* out, float* lse, float* threshold, int32_t* sel_indptr,
+                               int32_t* sel_tokens, int64_t capacity, void* ws, size_t ws_bytes, void* stream,
+                               void* const* events);
 
 /* Static description of a status code. */
 const char* twl_status_str(twl_status status);

@@ -28,7 +28,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ["twl_quantize_k", "twl_select_pages", "twl_estimate_topp", "twl_sparse_attn", "twl_decode",
-              "twl_decode_profiled", "twl_select_clusters_topp", "twl_workspace_bytes", "twl_status_str"]:
+              "twl_decode_profiled", "twl_select_clusters_topp", "twl_decode_clusters", "twl_workspace_bytes",
+              "twl_status_str"]:
         assert n in names
 
 
@@ -123,3 +124,33 @@ def test_split_entry_points_validate(twl):
     assert L.twl_sparse_attn(ctypes.byref(c), fake, 0.088, fake, fake, -1, fake, None, fake, 1 << 40, None) == 1
     assert L.twl_select_clusters_topp(ctypes.byref(c), fake, 0.088, 0.0, 32, fake, fake, fake, 64, fake, fake,
                                       fake, 1 << 40, None) == 1
+    assert L.twl_select_clusters_topp(ctypes.byref(c), fake, 0.088, 0.95, 32, fake, fake, fake, 65537, fake, fake,
+                                      fake, 1 << 40, None) == 2
+
+
+def test_workspace_grows_into_the_wide_top_p():
+    """Candidate capacities above 65536 per unit use the multi-pass top-p and its extra state."""
+    import top_sparse_attention_int4_amd as t
+    L = t.lib()
+    c = _fake_cache(t, max_pages_per_seq=1 << 15, num_phys_pages=1 << 15, max_seq_len=1 << 19)
+    a = L.twl_workspace_bytes(ctypes.byref(c), 65536)
+    b = L.twl_workspace_bytes(ctypes.byref(c), 65537)
+    assert b > a * 65537 / 65536  # the wide state comes on top of the per-candidate buffers
+
+
+def test_decode_clusters_validates():
+    import top_sparse_attention_int4_amd as t
+    L = t.lib()
+    c = _fake_cache(t)
+    fake = ctypes.c_void_p(0x10000)
+    prm = t.ParamsC(0.9, 1.0, 0.088, 32)
+    args = lambda p1, ncl, ws_bytes: (ctypes.byref(c), fake, ctypes.byref(prm), p1, fake, fake, fake, ncl, fake, None,
+                                      None, None, None, 0, fake, ws_bytes, None, None)
+    assert L.twl_decode_clusters(*args(0.0, 4096, 1 << 40)) == 1      # p1 out of range
+    assert L.twl_decode_clusters(*args(0.95, 0, 1 << 40)) == 1        # no clusters
+    assert L.twl_decode_clusters(*args(0.95, 16385, 1 << 40)) == 2    # more than half the capacity
+    need = L.twl_workspace_bytes(ctypes.byref(c), 32768)
+    assert L.twl_decode_clusters(*args(0.95, 4096, need - 256)) == 3  # workspace too small
+    nulls = (ctypes.byref(c), fake, ctypes.byref(prm), 0.95, None, fake, fake, 4096, fake, None, None, None, None, 0,
+             fake, 1 << 40, None, None)
+    assert L.twl_decode_clusters(*nulls) == 1                         # centroids missing

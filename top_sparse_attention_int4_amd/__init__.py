@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, _p, ctypes.POINTER(_p)]),
         "twl_select_clusters_topp": (_i32, [C, _p, _f32, _f32, _i32, _p, _p, _p, _i32, _p, _p, _p,
                                             ctypes.c_size_t, _p]),
+        "twl_decode_clusters": (_i32, [C, _p, ctypes.POINTER(ParamsC), _f32, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
+                                       _i64, _p, ctypes.c_size_t, _p, ctypes.POINTER(_p)]),
         "twl_status_str": (ctypes.c_char_p, [_i32]),
         "twl_version": (ctypes.c_char_p, []),
     }
@@ -259,3 +261,25 @@ def select_clusters_topp(cache: PagedCache, q: torch.Tensor, sm_scale: float, p1
                                           int(iters), _ptr(centroids), _ptr(csize), _ptr(coff), int(num_clusters),
                                           _ptr(ranges), _ptr(count), _ptr(ws), ws.numel() * ws.element_size(),
                                           _stream(stream)))
+
+
+def decode_clusters(cache: PagedCache, q: torch.Tensor, *, p: float, p1: float, centroids: torch.Tensor,
+                    csize: torch.Tensor, coff: torch.Tensor, sm_scale: float = DEFAULT_SM_SCALE, iters: int = 32,
+                    out: torch.Tensor, lse: Optional[torch.Tensor] = None, threshold: Optional[torch.Tensor] = None,
+                    sel_indptr: Optional[torch.Tensor] = None, sel_tokens: Optional[torch.Tensor] = None,
+                    ws: torch.Tensor, events=None, stream=None):
+    """Double-P decode step; ``events`` optionally holds 2*NUM_STAGES timing events."""
+    arr = None
+    if events is not None:
+        if len(events) != 2 * NUM_STAGES:
+            raise ValueError("need 2*NUM_STAGES events")
+        for e in events:
+            if e.cuda_event == 0:
+                e.record()
+        arr = (_p * (2 * NUM_STAGES))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    prm = _params(p, 1.0, sm_scale, iters)
+    cap = 0 if sel_tokens is None else int(sel_tokens.numel())
+    _check(lib().twl_decode_clusters(ctypes.byref(cache.struct()), _ptr(q), ctypes.byref(prm), float(p1),
+                                     _ptr(centroids), _ptr(csize), _ptr(coff), int(csize.shape[-1]), _ptr(out),
+                                     _ptr(lse), _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream), arr))

@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libtwl.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "select.hip", "estimate.hip", "topp.hip", "attention.hip", "cluster.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "select.hip", "estimate.hip", "topp.hip", "topp_wide.hip", "attention.hip",
+           "cluster.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -39,7 +40,7 @@ def hipcc() -> str:
 
 
 def sources() -> list[str]:
-    return [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    return [os.path.join(CSRC, s) for s in SOURCES]
 
 
 def build(verbose: bool = False) -> str:

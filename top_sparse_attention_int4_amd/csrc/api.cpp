@@ -32,6 +32,8 @@ twl_status check_cache(const twl_cache* c, bool need_kv, bool need_quant) {
   if ((int64_t)c->num_phys_pages * c->num_kv_heads * 16 >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
   if ((int64_t)c->batch * c->max_pages_per_seq >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
   if ((int64_t)c->batch * c->num_kv_heads > 65535) return TWL_EUNSUPPORTED;
+  // int32 CSR offsets and candidate indices over all units (with headroom for padded capacities)
+  if ((int64_t)c->batch * c->num_q_heads * c->max_seq_len > ((int64_t)1 << 31) / 4) return TWL_EUNSUPPORTED;
   if (!c->page_table || !c->seq_lens) return TWL_EINVAL;
   if (need_kv && (!c->k || !c->v)) return TWL_EINVAL;
   if (need_quant && (!c->k4 || !c->k4_meta || !c->kbound)) return TWL_EINVAL;
@@ -89,15 +91,21 @@ struct Layout {
   int64_t ncap = 0;       // candidate capacity per unit (multiple of 1024)
   int chunk_tokens = 64;  // attention chunk
   int64_t max_chunks = 0;
-  size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, logits = 0, masks = 0, utok = 0, urow = 0, ucnt = 0,
-         ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, total = 0;
+  size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
+         ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
+         total = 0;
 };
 
-// ncap_of(maxcand): the top-p block holds 1024*E candidates, E a power of two up to 64.
+// ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
+// to 64; beyond, the wide top-p takes multiples of its 4096-candidate chunk, up to 2^22.  0 = too many.
 int64_t ncap_of(int64_t maxcand) {
-  const int E = topp_elems_per_thread(maxcand < 1 ? 1 : maxcand);
-  return E ? (int64_t)E * kToppThreads : 0;
+  if (maxcand < 1) maxcand = 1;
+  if (maxcand <= kNarrowMaxCands) return (int64_t)topp_elems_per_thread(maxcand) * kToppThreads;
+  if (maxcand > kWideMaxCands) return 0;
+  return (maxcand + kWideChunk - 1) / kWideChunk * kWideChunk;
 }
+
+bool is_wide(int64_t ncap) { return ncap > kNarrowMaxCands; }
 
 bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   const int64_t U = (int64_t)c->batch * c->num_kv_heads;
@@ -118,6 +126,7 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->pcnt = take((size_t)U * 4);
   L->pphys = take((size_t)U * c->max_pages_per_seq * 4);
   L->rpre = take((size_t)U * (ncap + 1) * 4);
+  L->cfirst = take((size_t)U * (ncap / kEstCands) * 4);
   L->logits = take((size_t)BH * ncap * 4);
   L->masks = take((size_t)BH * (ncap / 32) * 4);
   L->utok = take((size_t)U * ncap * 4);
@@ -127,6 +136,12 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->crow = take((size_t)U * ncap * 4);
   L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
   L->thr = take((size_t)BH * 4);
+  if (is_wide(ncap)) {
+    L->pmax = take((size_t)BH * (ncap / kEstCands) * 4);
+    L->wstate = take((size_t)BH * kWideStateWords * 8);
+    L->wcnt = take((size_t)U * (ncap / kWideChunk) * 4);
+    L->uwords = take((size_t)U * (ncap / 32) * 4);
+  }
   L->total = off;
   return true;
 }
@@ -142,14 +157,6 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-twl_status hip_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_EHIP; }
-
-#define TWL_TRY(expr)                          \
-  do {                                         \
-    const hipError_t e_ = (expr);              \
-    if (e_ != hipSuccess) return TWL_EHIP;     \
-  } while (0)
-
 // Event hook for profiled runs.
 struct Events {
   void* const* ev = nullptr;
@@ -158,6 +165,44 @@ struct Events {
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   }
 };
+
+twl_status hip_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_EHIP; }
+
+WideWs wide_of(void* ws, const Layout& L) {
+  return WideWs{at<float>(ws, L.pmax), at<uint64_t>(ws, L.wstate), at<int32_t>(ws, L.wcnt), at<uint32_t>(ws, L.uwords)};
+}
+
+// Estimate, top-p and union of every unit (the narrow or the wide top-p by candidate capacity).
+hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, void* ws,
+                         const Layout& L, float p, int iters, float* thr, float* mass, uint32_t* head_mask,
+                         int mask_words, const Events& E, hipStream_t s) {
+  const int ncap = (int)L.ncap;
+  const WideWs wd = wide_of(ws, L);
+  const bool wide = is_wide(L.ncap);
+  hipError_t e;
+  if ((e = E.rec(4)) != hipSuccess) return e;
+  e = launch_estimate(c, q, sm, cand, ncap, at<float>(ws, L.logits), at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow),
+                      wide ? &wd : nullptr, s);
+  if (e != hipSuccess) return e;
+  if ((e = E.rec(5)) != hipSuccess) return e;
+  if ((e = E.rec(6)) != hipSuccess) return e;
+  if (wide)
+    e = launch_topp_wide(c, wd, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), ncap, p,
+                         iters, thr, mass, head_mask, mask_words, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow),
+                         at<int32_t>(ws, L.ucnt), s);
+  else
+    e = launch_topp(c, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), ncap, p, iters, thr,
+                    mass, at<uint32_t>(ws, L.masks), head_mask, mask_words, at<int32_t>(ws, L.utok),
+                    at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s);
+  if (e != hipSuccess) return e;
+  return E.rec(7);
+}
+
+#define TWL_TRY(expr)                          \
+  do {                                         \
+    const hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return TWL_EHIP;     \
+  } while (0)
 
 twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_params* prm, float* out,
                        float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
@@ -213,16 +258,74 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
     cand.mode = kCandAll;
   }
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
-  TWL_TRY(E.rec(4));
-  TWL_TRY(launch_estimate(c, qb, prm->sm_scale, cand, (int)ncap, at<float>(ws, L.logits), at<int32_t>(ws, L.ctok),
-                          at<int32_t>(ws, L.crow), s));
-  TWL_TRY(E.rec(5));
-  TWL_TRY(E.rec(6));
-  TWL_TRY(launch_topp(c, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), (int)ncap,
-                      prm->p, prm->iters, thr, nullptr,
-                      at<uint32_t>(ws, L.masks), nullptr, 0,
-                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s));
-  TWL_TRY(E.rec(7));
+  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, E, s));
+  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap};
+  TWL_TRY(E.rec(8));
+  TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
+                      sel_tokens, capacity, s));
+  TWL_TRY(E.rec(9));
+  TWL_TRY(E.rec(10));
+  TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));
+  TWL_TRY(E.rec(11));
+  return TWL_OK;
+}
+
+// Double-P decode: cluster top-p -> ranges -> estimate / token top-p / union -> attention -> merge.
+// The kept ranges live in the union-row region (read only before the union overwrites it) and their
+// count in the page-count region.
+twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl_decode_params* prm, float p1,
+                                const void* centroids, const int32_t* csize, const int32_t* coff,
+                                int32_t num_clusters, float* out, float* lse, float* threshold,
+                                int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity, void* ws,
+                                size_t ws_bytes, void* stream, void* const* events) {
+  twl_status st = check_cache(cache, true, true);
+  if (st != TWL_OK) return st;
+  if (!q || !prm || !out || !centroids || !csize || !coff) return TWL_EINVAL;
+  if (!finite(prm->p) || !(prm->p > 0.f) || prm->p > 1.f) return TWL_EINVAL;
+  if (!finite(p1) || !(p1 > 0.f) || p1 > 1.f) return TWL_EINVAL;
+  if (!finite(prm->sm_scale)) return TWL_EINVAL;
+  if (prm->iters < 1 || prm->iters > 64 || num_clusters < 1) return TWL_EINVAL;
+  if ((sel_indptr == nullptr) != (sel_tokens == nullptr)) return TWL_EINVAL;
+  const int64_t U = (int64_t)cache->batch * cache->num_kv_heads;
+  const int64_t maxcand = cache->max_seq_len;
+  if (sel_tokens && capacity < U * maxcand) return TWL_EINVAL;
+  const int64_t ncap = ncap_of(maxcand);
+  if (ncap == 0 || num_clusters > kNarrowMaxCands || 2 * (int64_t)num_clusters > ncap) return TWL_EUNSUPPORTED;
+  const int64_t cpad = ncap_of(num_clusters);
+  if (cpad > ncap) return TWL_EUNSUPPORTED;
+  Layout L;
+  make_layout(cache, ncap, &L);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != TWL_OK) return st;
+  if (events) {
+    for (int i = 0; i < 2 * TWL_NUM_STAGES; ++i)
+      if (!events[i]) return TWL_EINVAL;
+  }
+  st = check_device();
+  if (st != TWL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const Events E{events, s};
+  const CacheView c = make_view(cache);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  int32_t* ranges = at<int32_t>(ws, L.urow);
+  int32_t* rcount = at<int32_t>(ws, L.pcnt);
+  TWL_TRY(E.rec(0));
+  TWL_TRY(launch_cluster_select(c, qb, prm->sm_scale, p1, prm->iters, static_cast<const uint16_t*>(centroids), csize,
+                                coff, num_clusters, (int)cpad, at<float>(ws, L.logits), at<float>(ws, L.thr),
+                                at<uint32_t>(ws, L.masks), ranges, rcount, s));
+  TWL_TRY(E.rec(1));
+  CandView cand{};
+  cand.mode = kCandRanges;
+  cand.items = ranges;
+  cand.count = rcount;
+  cand.max_items = num_clusters;
+  cand.range_prefix = at<int32_t>(ws, L.rpre);
+  cand.chunk_first = at<int32_t>(ws, L.cfirst);
+  TWL_TRY(E.rec(2));
+  TWL_TRY(launch_range_prefix(c, cand, at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
+  TWL_TRY(E.rec(3));
+  float* thr = threshold ? threshold : at<float>(ws, L.thr);
+  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, E, s));
   ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap};
   TWL_TRY(E.rec(8));
   TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
@@ -327,14 +430,11 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
   const CacheView c = make_view(cache);
   if (cv.mode == kCandRanges) {
     cv.range_prefix = at<int32_t>(ws, L.rpre);
-    TWL_TRY(launch_range_prefix(c, cv, at<int32_t>(ws, L.rpre), s));
+    cv.chunk_first = at<int32_t>(ws, L.cfirst);
+    TWL_TRY(launch_range_prefix(c, cv, at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
   }
-  TWL_TRY(launch_estimate(c, static_cast<const uint16_t*>(q), sm_scale, cv, (int)ncap, at<float>(ws, L.logits),
-                          at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), s));
-  TWL_TRY(launch_topp(c, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), (int)ncap, p,
-                      iters, threshold, mass,
-                      at<uint32_t>(ws, L.masks), head_mask, mask_words,
-                      at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s));
+  TWL_TRY(estimate_topp(c, static_cast<const uint16_t*>(q), sm_scale, cv, ws, L, p, iters, threshold, mass, head_mask,
+                        mask_words, Events{}, s));
   TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
                           capacity, s));
   return TWL_OK;
@@ -390,10 +490,28 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
   if (!q || !centroids || !csize || !coff || !ranges || !count) return TWL_EINVAL;
   if (!finite(p1) || !(p1 > 0.f) || p1 > 1.f || !finite(sm_scale)) return TWL_EINVAL;
   if (iters < 1 || iters > 64 || num_clusters < 1) return TWL_EINVAL;
-  (void)ws;
-  (void)ws_bytes;
-  (void)stream;
-  return TWL_EUNSUPPORTED;
+  if (num_clusters > kNarrowMaxCands) return TWL_EUNSUPPORTED;
+  const int64_t cpad = ncap_of(num_clusters);
+  Layout L;
+  make_layout(cache, cpad, &L);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != TWL_OK) return st;
+  st = check_device();
+  if (st != TWL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(launch_cluster_select(make_view(cache), static_cast<const uint16_t*>(q), sm_scale, p1, iters,
+                                          static_cast<const uint16_t*>(centroids), csize, coff, num_clusters,
+                                          (int)cpad, at<float>(ws, L.logits), at<float>(ws, L.thr),
+                                          at<uint32_t>(ws, L.masks), ranges, count, s));
+}
+
+twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_decode_params* params, float p1,
+                               const void* centroids, const int32_t* csize, const int32_t* coff,
+                               int32_t num_clusters, float* out, float* lse, float* threshold, int32_t* sel_indptr,
+                               int32_t* sel_tokens, int64_t capacity, void* ws, size_t ws_bytes, void* stream,
+                               void* const* events) {
+  return decode_clusters_impl(cache, q, params, p1, centroids, csize, coff, num_clusters, out, lse, threshold,
+                              sel_indptr, sel_tokens, capacity, ws, ws_bytes, stream, events);
 }
 
 const char* twl_status_str(twl_status status) {

@@ -1,0 +1,157 @@
+// Double-P first stage: cluster-level top-p on size-weighted centroids, and the union of the kept
+// clusters as token ranges ("Double-P: Hierarchical Top-P Sparse Attention for Long-Context LLMs",
+// sections 方法详解 and 关键设计: a coarse top-p over clusters precedes a token-level top-p inside
+// the kept clusters).
+//
+// Clusters of a (sequence, kv-head) unit are contiguous token ranges with a given bf16 centroid mu_c
+// and size n_c.  Per query head the cluster logit is l_c = fl(sm * fold_{c'}(acc + q_c' mu_c,c')), a
+// float32 left-to-right fold from +0 (bf16 x bf16 products are exact, so each fused multiply-add
+// is the rounded addition of the fold); its weight is n_c exp(l_c - M) with M the largest logit of
+// a non-empty cluster.  Empty clusters, and the padding up to the top-p block size, carry a logit of
+// -inf and are never candidates.  The top-p itself is the weighted mode of the token-level
+// bisection kernel.
+#include "twl_device.h"
+#include "twl_internal.h"
+
+namespace twl {
+
+// One block per (unit, 64 clusters); wave hh folds query head hh for the block's 64 clusters from an
+// LDS copy of their centroids (read with coalesced 16-byte loads).
+template <int G>
+__global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_cluster_score(CacheView c, const uint16_t* __restrict__ q,
+                                                                        const uint16_t* __restrict__ cent,
+                                                                        const int32_t* __restrict__ csize, int C,
+                                                                        int cpad, float sm, float* __restrict__ lam,
+                                                                        int blocks_per_unit) {
+  constexpr int NT = 64 * (G > 4 ? G : 4);
+  const int u = blockIdx.x / blocks_per_unit;
+  const int blk = blockIdx.x - u * blocks_per_unit;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int hh = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ uint4 tile[64][17];  // 64 centroid rows of 16 x 16 B, padded by 16 B
+  __shared__ float qs[G][kD];
+  {
+    constexpr int R = 64 * 16 / NT;
+    const int part = threadIdx.x & 15;
+    uint4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int j = blk * 64 + ((int)threadIdx.x >> 4) + r * (NT / 16);
+      v[r] = (j < C) ? reinterpret_cast<const uint4*>(cent + ((size_t)u * C + j) * kD)[part]
+                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) tile[((int)threadIdx.x >> 4) + r * (NT / 16)][part] = v[r];
+  }
+  const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
+  for (int i = threadIdx.x; i < G * kD; i += NT) qs[i / kD][i % kD] = __uint_as_float((uint32_t)qg[i] << 16);
+  __syncthreads();
+
+  const int j = blk * 64 + lane;
+  if (hh < G && j < cpad) {
+    float out = -__builtin_inff();
+    if (j < C && csize[(size_t)u * C + j] > 0) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < 16; ++c8) {
+        const uint4 w4 = tile[lane][c8];
+        const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float mu = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+          acc = fmaf(qs[hh][c8 * 8 + e], mu, acc);
+        }
+      }
+      out = sm * acc;
+    }
+    lam[((size_t)b * c.Hq + (size_t)h * G + hh) * cpad + j] = out;
+  }
+}
+
+// One block per unit: OR of the G head masks over the clusters, then the kept clusters written in
+// ascending order as (first token, length) ranges, and their count.
+template <int G>
+__global__ __launch_bounds__(1024) void k_cluster_union(CacheView c, const uint32_t* __restrict__ mask_ws, int cpad,
+                                                        const int32_t* __restrict__ csize,
+                                                        const int32_t* __restrict__ coff, int C,
+                                                        int32_t* __restrict__ ranges, int32_t* __restrict__ count) {
+  constexpr int NT = 1024, NW = NT / 64;
+  constexpr int kMaxWords = 65536 / 32;
+  constexpr int WPT = kMaxWords / NT;
+  __shared__ uint32_t uw[kMaxWords];
+  __shared__ int woff[kMaxWords];
+  __shared__ int scan_sm[NW + 1];
+  const int u = blockIdx.x;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int tid = threadIdx.x;
+  const int MW = cpad / 32;
+  const uint32_t* m0 = mask_ws + ((size_t)b * c.Hq + (size_t)h * G) * MW;
+  uint32_t words[WPT];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    uint32_t x = 0u;
+    if (w < MW) {
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) x |= m0[(size_t)hh * MW + w];
+    }
+    words[i] = x;
+    local += __popc(x);
+  }
+  int total;
+  int off = block_excl_scan<NW>(local, scan_sm, &total);
+#pragma unroll
+  for (int i = 0; i < WPT; ++i) {
+    const int w = tid * WPT + i;
+    if (w < MW) {
+      uw[w] = words[i];
+      woff[w] = off;
+      off += __popc(words[i]);
+    }
+  }
+  __syncthreads();
+  const int32_t* cs = csize + (size_t)u * C;
+  const int32_t* co = coff + (size_t)u * (C + 1);
+  int32_t* rg = ranges + (size_t)u * C * 2;
+  for (int k = tid; k < C; k += NT) {
+    const uint32_t x = uw[k >> 5];
+    const int bit = k & 31;
+    if ((x >> bit) & 1u) {
+      const int pos = woff[k >> 5] + __popc(x & ((1u << bit) - 1u));
+      rg[2 * pos] = co[k];
+      rg[2 * pos + 1] = cs[k];
+    }
+  }
+  if (tid == 0) count[u] = total;
+}
+
+hipError_t launch_cluster_select(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
+                                 const uint16_t* centroids, const int32_t* csize, const int32_t* coff, int C,
+                                 int cpad, float* lam, float* thr, uint32_t* mask_ws, int32_t* ranges,
+                                 int32_t* count, hipStream_t s) {
+  const int bpu = cpad / 64;
+  dim3 grid((unsigned)(c.B * c.Hkv * bpu));
+  switch (c.G) {
+    case 1: hipLaunchKernelGGL(k_cluster_score<1>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
+    case 2: hipLaunchKernelGGL(k_cluster_score<2>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
+    case 4: hipLaunchKernelGGL(k_cluster_score<4>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
+    case 8: hipLaunchKernelGGL(k_cluster_score<8>, grid, dim3(512), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_topp_weighted(c, lam, cpad, p1, iters, thr, mask_ws, csize, C, s);
+  if (e != hipSuccess) return e;
+  dim3 ugrid((unsigned)(c.B * c.Hkv));
+  switch (c.G) {
+    case 1: hipLaunchKernelGGL(k_cluster_union<1>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
+    case 2: hipLaunchKernelGGL(k_cluster_union<2>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
+    case 4: hipLaunchKernelGGL(k_cluster_union<4>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
+    case 8: hipLaunchKernelGGL(k_cluster_union<8>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace twl

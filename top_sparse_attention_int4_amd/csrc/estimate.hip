@@ -20,39 +20,30 @@
 
 namespace twl {
 
-// Map candidate index k of unit u to a logical token id; returns -1 when k is not a candidate.
+// Map candidate index k of unit u to a logical token id for the "all" and "pages" forms; returns -1
+// when k is not a candidate.  (The ranges form is resolved block-wide inside the estimate.)
 __device__ __forceinline__ int cand_token(const CandView& cand, int u, int k, int n) {
-  const int P = (n + kPage - 1) / kPage;
   if (cand.mode == kCandAll) return k < n ? k : -1;
-  if (cand.mode == kCandPages) {
-    const int cnt = clampi(cand.count[u], 0, cand.max_items);
-    const int pi = k >> 4;
-    if (pi >= cnt) return -1;
-    const int page = cand.items[(size_t)u * cand.max_items + pi];
-    if (page < 0 || page >= P) return -1;
-    const int t = page * kPage + (k & 15);
-    return t < n ? t : -1;
-  }
-  // ranges: binary search the item whose prefix interval holds k
+  const int P = (n + kPage - 1) / kPage;
   const int cnt = clampi(cand.count[u], 0, cand.max_items);
-  const int32_t* pre = cand.range_prefix + (size_t)u * (cand.max_items + 1);
-  if (k >= pre[cnt]) return -1;
-  int lo = 0, hi = cnt;  // pre[lo] <= k < pre[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= k) lo = mid; else hi = mid;
-  }
-  const int t = cand.items[((size_t)u * cand.max_items + lo) * 2] + (k - pre[lo]);
-  return (t >= 0 && t < n) ? t : -1;
+  const int pi = k >> 4;
+  if (pi >= cnt) return -1;
+  const int page = cand.items[(size_t)u * cand.max_items + pi];
+  if (page < 0 || page >= P) return -1;
+  const int t = page * kPage + (k & 15);
+  return t < n ? t : -1;
 }
 
-// Prefix sums of range lengths per unit (lengths < 0 count as 0).
-__global__ __launch_bounds__(256) void k_range_prefix(CacheView c, CandView cand, int32_t* prefix) {
+// Prefix sums of range lengths per unit (lengths < 0 count as 0), and for every block of kEstCands
+// candidates the index of the range holding its first candidate (count when past the last one).
+__global__ __launch_bounds__(256) void k_range_prefix(CacheView c, CandView cand, int32_t* prefix,
+                                                      int32_t* chunk_first, int nchunk) {
   constexpr int NW = 4;
   __shared__ int scan_sm[NW + 1];
   const int u = blockIdx.x;
   const int cnt = clampi(cand.count[u], 0, cand.max_items);
   int32_t* pre = prefix + (size_t)u * (cand.max_items + 1);
+  int32_t* cf = chunk_first + (size_t)u * nchunk;
   int carry = 0;
   for (int base = 0; base < cnt; base += 256) {
     const int i = base + (int)threadIdx.x;
@@ -60,13 +51,22 @@ __global__ __launch_bounds__(256) void k_range_prefix(CacheView c, CandView cand
     if (i < cnt) len = max(0, cand.items[((size_t)u * cand.max_items + i) * 2 + 1]);
     int total;
     const int ex = block_excl_scan<NW>(len, scan_sm, &total);
-    if (i < cnt) pre[i] = carry + ex;
+    if (i < cnt) {
+      const int s0 = carry + ex;
+      pre[i] = s0;
+      if (len > 0) {
+        const int64_t e0 = (int64_t)s0 + len;
+        for (int j = (s0 + kEstCands - 1) / kEstCands; j < nchunk && (int64_t)j * kEstCands < e0; ++j) cf[j] = i;
+      }
+    }
     carry += total;
   }
   if (threadIdx.x == 0) pre[cnt] = carry;
+  for (int j = threadIdx.x; j < nchunk; j += 256)
+    if ((int64_t)j * kEstCands >= carry) cf[j] = cnt;
 }
 
-constexpr int kEstBatches = 4;  // 64-candidate batches per block
+constexpr int kEstBatches = kEstCands / 64;  // 64-candidate batches per block
 
 // Token id and K/V row of candidate k (row -1 when k is not a candidate).  `cnt` is the unit's item
 // count for the page and range forms.
@@ -96,7 +96,8 @@ template <int G>
 __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
                                                   CandView cand, int ncap, int chunks_per_unit,
                                                   float* __restrict__ logits, int32_t* __restrict__ cand_tok,
-                                                  int32_t* __restrict__ cand_row) {
+                                                  int32_t* __restrict__ cand_row, float* __restrict__ pmax,
+                                                  uint64_t* __restrict__ wstate, size_t wstate_words) {
   constexpr int NB = kEstBatches;
   const int u = blockIdx.x / chunks_per_unit;
   const int ck = blockIdx.x - u * chunks_per_unit;
@@ -110,8 +111,64 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   const int cnt = (cand.mode == kCandAll) ? 0 : clampi(cand.count[u], 0, cand.max_items);
   const int kbase = ck * (64 * NB) + lane;
   int tokv[NB], rowv[NB];
+  if (wstate) {
+    // clear the wide top-p state for the passes that follow this kernel
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < wstate_words; i += (size_t)gridDim.x * 256)
+      wstate[i] = 0ull;
+  }
+  if (cand.mode == kCandRanges) {
+    // The block's candidates lie in the ranges r0..rmax; their prefix sums and first tokens are
+    // staged in LDS when they fit, and every lane searches there.
+    __shared__ int s_pre[kEstCands];
+    __shared__ int s_beg[kEstCands];
+    const int32_t* pre = cand.range_prefix + (size_t)u * (cand.max_items + 1);
+    const int nchunk = ncap / kEstCands;
+    const int r0 = clampi(cand.chunk_first[(size_t)u * nchunk + ck], 0, cnt);
+    const int r1 = (ck + 1 < nchunk) ? clampi(cand.chunk_first[(size_t)u * nchunk + ck + 1], 0, cnt) : cnt;
+    const int rmax = min(r1, cnt - 1);
+    const int nr = rmax - r0 + 1;
+    const int tot = pre[cnt];
+    const bool staged = nr >= 1 && nr <= kEstCands;
+    if (staged && (int)threadIdx.x < nr) {
+      s_pre[threadIdx.x] = pre[r0 + threadIdx.x];
+      s_beg[threadIdx.x] = cand.items[((size_t)u * cand.max_items + r0 + threadIdx.x) * 2];
+    }
+    __syncthreads();
 #pragma unroll
-  for (int bt = 0; bt < NB; ++bt) cand_resolve(c, cand, u, b, h, kbase + 64 * bt, n, cnt, tokv[bt], rowv[bt]);
+    for (int bt = 0; bt < NB; ++bt) {
+      const int k = kbase + 64 * bt;
+      int t = -1;
+      if (nr >= 1 && k < tot) {
+        int lo, beg, p0;
+        if (staged) {
+          lo = 0;
+          int hi = nr;  // largest lo with s_pre[lo] <= k
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_pre[mid] <= k) lo = mid; else hi = mid;
+          }
+          p0 = s_pre[lo];
+          beg = s_beg[lo];
+        } else {
+          lo = r0;
+          int hi = rmax + 1;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (pre[mid] <= k) lo = mid; else hi = mid;
+          }
+          p0 = pre[lo];
+          beg = cand.items[((size_t)u * cand.max_items + lo) * 2];
+        }
+        if (p0 <= k) t = beg + (k - p0);
+      }
+      tokv[bt] = (t >= 0 && t < n) ? t : -1;
+      rowv[bt] = tokv[bt] >= 0 ? (c.page_table[(size_t)b * c.maxP + (tokv[bt] >> 4)] * c.Hkv + h) * kPage + (tokv[bt] & 15)
+                               : -1;
+    }
+  } else {
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) cand_resolve(c, cand, u, b, h, kbase + 64 * bt, n, cnt, tokv[bt], rowv[bt]);
+  }
   uint4 cwv[NB];
   uint32_t mwv[NB];
 #pragma unroll
@@ -140,6 +197,9 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
     bsum[hh] = acc;
   }
 
+  float mx[(G + kGroups - 1) / kGroups];  // running maxima of this wave's heads (pmax)
+#pragma unroll
+  for (int i = 0; i < (G + kGroups - 1) / kGroups; ++i) mx[i] = -__builtin_inff();
 #pragma unroll
   for (int bt = 0; bt < NB; ++bt) {
     const int k = kbase + 64 * bt;
@@ -182,31 +242,52 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       cand_row[(size_t)u * ncap + k] = rowv[bt];
     }
     __syncthreads();  // T[bt & 1] complete; T[(bt + 1) & 1] was last read before this barrier
-    for (int hh = g; hh < G; hh += kGroups) {
-      float lg = -__builtin_inff();
-      if (rowv[bt] >= 0) {
-        const float r01 = T[bt & 1][0][hh][lane] + T[bt & 1][1][hh][lane];
-        const float r23 = T[bt & 1][2][hh][lane] + T[bt & 1][3][hh][lane];
-        lg = sm * (r01 + r23);
+#pragma unroll
+    for (int i = 0; i < (G + kGroups - 1) / kGroups; ++i) {
+      const int hh = g + kGroups * i;
+      if (hh < G) {
+        float lg = -__builtin_inff();
+        if (rowv[bt] >= 0) {
+          const float r01 = T[bt & 1][0][hh][lane] + T[bt & 1][1][hh][lane];
+          const float r23 = T[bt & 1][2][hh][lane] + T[bt & 1][3][hh][lane];
+          lg = sm * (r01 + r23);
+        }
+        mx[i] = fmaxf(mx[i], lg);
+        if (k < ncap) logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
       }
-      if (k < ncap) logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
+    }
+  }
+  if (pmax) {
+#pragma unroll
+    for (int i = 0; i < (G + kGroups - 1) / kGroups; ++i) {
+      const int hh = g + kGroups * i;
+      if (hh < G) {
+        const float m = wave_max_dpp(mx[i]);
+        if (lane == 0) pmax[((size_t)b * c.Hq + (size_t)h * G + hh) * chunks_per_unit + ck] = m;
+      }
     }
   }
 }
 
-hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, hipStream_t s) {
-  hipLaunchKernelGGL(k_range_prefix, dim3((unsigned)(c.B * c.Hkv)), dim3(256), 0, s, c, cand, prefix);
+hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, int32_t* chunk_first,
+                               int nchunk, hipStream_t s) {
+  hipLaunchKernelGGL(k_range_prefix, dim3((unsigned)(c.B * c.Hkv)), dim3(256), 0, s, c, cand, prefix, chunk_first,
+                     nchunk);
   return hipGetLastError();
 }
 
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
-                           float* logits, int32_t* cand_tok, int32_t* cand_row, hipStream_t s) {
-  const int cpu = (ncap + 64 * kEstBatches - 1) / (64 * kEstBatches);
+                           float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s) {
+  if (ncap % kEstCands) return hipErrorInvalidValue;
+  const int cpu = ncap / kEstCands;
   dim3 grid((unsigned)(c.B * c.Hkv * cpu));
+  float* pmax = wide ? wide->pmax : nullptr;
+  uint64_t* wst = wide ? wide->state : nullptr;
+  const size_t wwords = wide ? (size_t)c.B * c.Hq * kWideStateWords : 0;
 #define TWL_EST_CASE(GG)                                                                                   \
   case GG:                                                                                                 \
     hipLaunchKernelGGL(k_estimate<GG>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, cand_tok, \
-                       cand_row);                                                                          \
+                       cand_row, pmax, wst, wwords);                                                       \
     break;
   switch (c.G) {
     TWL_EST_CASE(1)

@@ -27,10 +27,13 @@ namespace twl {
 
 constexpr int kCap = 1024;  // weights handed to the single-wave phase (16 per lane)
 
-template <int E>
+// W: weighted mode -- candidate k of unit u carries the integer multiplicity mult[u * mult_stride + k]
+// (k < mult_stride), its weight being mult * exp(l - M); the largest weight is then not 1.
+template <int E, bool W>
 __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restrict__ logits, int ncap, float p,
                                                int iters, float* threshold, float* mass, uint32_t* mask_ws,
-                                               uint32_t* head_mask, int mask_words) {
+                                               uint32_t* head_mask, int mask_words,
+                                               const int32_t* __restrict__ mult, int mult_stride) {
   constexpr int NT = kToppThreads, NW = NT / 64;
   __shared__ float red[2 * NW * 4];
   __shared__ int cnt_sm[2][NW];
@@ -56,9 +59,14 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   float Z = 0.f, emin = __builtin_inff();
   int nval_w = 0;  // wave-uniform count of existing candidates
   if (M != -__builtin_inff()) {
+    const int32_t* mu = W ? mult + (size_t)(bh / c.G) * mult_stride : nullptr;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       e[j] = (e[j] == -__builtin_inff()) ? -1.f : exp_diff(e[j], M);
+      if (W) {
+        const int k = j * NT + tid;
+        if (e[j] >= 0.f) e[j] = (k < mult_stride) ? (float)mu[k] * e[j] : -1.f;
+      }
       const bool ok = e[j] >= 0.f;
       if (ok) {
         Z += e[j];
@@ -71,6 +79,13 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     for (int j = 0; j < E; ++j) e[j] = -1.f;
   }
   br.sum_min(Z, emin);
+  float emax = 1.0f;  // exp(0): the largest unweighted weight
+  if (W) {
+    float x = -1.f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) x = fmaxf(x, e[j]);
+    emax = br.max(x);
+  }
 
   // block-wide sum of f and of a wave-uniform count, with one barrier
   int slot = 0;
@@ -104,7 +119,7 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   if (Z > 0.f && p < 1.0f) {
     const float target = p * Z;
     lo = __float_as_uint(emin);                // f(min e) = Z >= target
-    uint32_t hi = __float_as_uint(1.0f) + 1u;  // e <= 1 = exp(0)
+    uint32_t hi = __float_as_uint(emax) + 1u;  // every weight is <= emax
     int n_lo = nval, n_hi = 0;                 // #{e >= lo}, #{e >= hi}
     int it = 0;
     // ---- block phase: one fixed-order reduction of f(mid) and #{e >= mid} per step ------------
@@ -340,10 +355,10 @@ hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_
                        hipStream_t s) {
   const int E = ncap / kToppThreads;
   dim3 grid((unsigned)(c.B * c.Hq)), block(kToppThreads);
-#define TWL_TOPP_CASE(EE)                                                                                 \
-  case EE:                                                                                                \
-    hipLaunchKernelGGL(k_topp<EE>, grid, block, 0, s, c, logits, ncap, p, iters, threshold, mass, mask_ws, \
-                       head_mask, mask_words);                                                           \
+#define TWL_TOPP_CASE(EE)                                                                                   \
+  case EE:                                                                                                  \
+    hipLaunchKernelGGL((k_topp<EE, false>), grid, block, 0, s, c, logits, ncap, p, iters, threshold, mass,   \
+                       mask_ws, head_mask, mask_words, nullptr, 0);                                        \
     break;
   switch (E) {
     TWL_TOPP_CASE(1)
@@ -386,6 +401,28 @@ hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_
   }
 #undef TWL_UNION_G
 #undef TWL_UNION_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_topp_weighted(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
+                                uint32_t* mask_ws, const int32_t* mult, int mult_stride, hipStream_t s) {
+  dim3 grid((unsigned)(c.B * c.Hq)), block(kToppThreads);
+#define TWL_TOPPW_CASE(EE)                                                                                \
+  case EE:                                                                                                \
+    hipLaunchKernelGGL((k_topp<EE, true>), grid, block, 0, s, c, logits, ncap, p, iters, threshold, nullptr, \
+                       mask_ws, nullptr, 0, mult, mult_stride);                                          \
+    break;
+  switch (ncap / kToppThreads) {
+    TWL_TOPPW_CASE(1)
+    TWL_TOPPW_CASE(2)
+    TWL_TOPPW_CASE(4)
+    TWL_TOPPW_CASE(8)
+    TWL_TOPPW_CASE(16)
+    TWL_TOPPW_CASE(32)
+    TWL_TOPPW_CASE(64)
+    default: return hipErrorInvalidValue;
+  }
+#undef TWL_TOPPW_CASE
   return hipGetLastError();
 }
 

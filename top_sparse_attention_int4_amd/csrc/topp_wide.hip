@@ -1,0 +1,387 @@
+// Top-p for heads with more candidates than one block holds in registers (more than 65536).
+//
+// Same threshold search as the block kernel (Paper-Notes "关键设计 / 高效Top-p": find the threshold m
+// with sum_{W_i >= m} W_i >= p by repeated parallel passes, no sort), over the same weights
+// e_i = exp(l_i - M) and the same key, the uint32 image of the non-negative float32 weight.  A
+// bisection of that key over [0, 2^31) decides one key bit per step, top bit first; here each pass
+// over the data decides 11 bits at once from a histogram of the mass per value of those bits (2048
+// bins), which is the outcome of 11 consecutive bisection steps.  Three passes (bits 30..20, 19..9,
+// 8..0) give the exact largest threshold T with mass{e >= T} >= p * Z, so the kept set {e >= T} is
+// the converged bisection's.  With fewer steps requested the threshold keeps only its top `iters`
+// bits, the point a shorter bisection stops at: a superset that still reaches p.
+//
+// Masses are 64-bit fixed point, floor(e * 2^40) (e <= 1, at most 2^22 candidates per head), so the
+// histograms can be summed across blocks with integer atomics in any order and still give the same
+// result on every run.  Truncation costs at most 2^-40 per weight, below 2.4e-7 of Z for 2^18
+// candidates.
+//
+// Kernels, one pass each over the head's candidates (4096 per block):
+//   k_wide_hist1  M from the estimate's per-block maxima; e written over the logits; histogram of bits 30..20
+//   k_wide_hist2  resolve bits 30..20, histogram bits 19..9 inside the chosen bin
+//   k_wide_hist3  resolve bits 19..9, histogram bits 8..0
+//   k_wide_mask   per (unit, chunk): resolve bits 8..0 for the G heads, head masks, kept mass, union
+//                 words and their count
+//   k_wide_emit   per (unit, chunk): compaction of the union (ascending ids and K/V rows), outputs
+#include "twl_device.h"
+#include "twl_internal.h"
+
+namespace twl {
+
+namespace {
+
+constexpr int NT = kWideThreads;
+constexpr int NW = NT / 64;
+constexpr int EPT = kWideChunk / NT;  // candidates per thread
+constexpr float kFixScale = 1099511627776.0f;  // 2^40
+
+__device__ __forceinline__ uint64_t to_fix(float e) { return (uint64_t)(e * kFixScale); }
+
+__device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t y = __shfl_down(x, d);
+    if (lane + d < 64) x += y;
+  }
+  return x;
+}
+
+// Largest bin of one histogram level whose suffix mass reaches `target` (>= 1), from its coarse
+// sums (one per 32 bins) and then the 32 bins of the chosen coarse block; `rem` is the mass still
+// needed inside the bin (target minus everything above it).  Called by a whole wave.
+__device__ __forceinline__ void wide_find(const uint64_t* fine, const uint64_t* coarse, int ncoarse,
+                                          uint64_t target, int& bin, uint64_t& rem) {
+  const int lane = threadIdx.x & 63;
+  uint64_t x = (lane < ncoarse) ? coarse[lane] : 0ull;
+  x = wave_suffix_u64(x);
+  unsigned long long bal = __ballot(lane < ncoarse && x >= target);
+  const int cb = bal ? 63 - __clzll(bal) : 0;
+  const uint64_t above = (cb < 63) ? __shfl(x, cb + 1) : 0ull;
+  const uint64_t r1 = target - above;
+  uint64_t y = (lane < 32) ? fine[32 * cb + lane] : 0ull;
+  y = wave_suffix_u64(y);
+  bal = __ballot(lane < 32 && y >= r1);
+  const int fb = bal ? 63 - __clzll(bal) : 0;
+  const uint64_t above2 = __shfl(y, fb + 1);  // lanes >= 32 hold 0
+  bin = 32 * cb + fb;
+  rem = r1 - above2;
+}
+
+__device__ __forceinline__ void flush_hist(const uint64_t* h, int nbins, uint64_t* g_fine, uint64_t* g_coarse) {
+  for (int i = threadIdx.x; i < nbins; i += NT)
+    if (h[i]) atomicAdd((unsigned long long*)&g_fine[i], (unsigned long long)h[i]);
+  for (int cb = threadIdx.x; cb < nbins / 32; cb += NT) {
+    uint64_t s = 0;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) s += h[32 * cb + i];
+    if (s) atomicAdd((unsigned long long*)&g_coarse[cb], (unsigned long long)s);
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kWideThreads) void k_wide_hist1(float* __restrict__ logits, int ncap,
+                                                             const float* __restrict__ pmax, int npm,
+                                                             uint64_t* __restrict__ state) {
+  __shared__ uint64_t h[2048];
+  __shared__ float red[2 * NW * 4];
+  BlockReduce<NW> br{red};
+  const int nch = ncap / kWideChunk;
+  const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
+  for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
+  float m = -__builtin_inff();
+  for (int i = threadIdx.x; i < npm; i += NT) m = fmaxf(m, pmax[(size_t)bh * npm + i]);
+  const float M = br.max(m);  // (its barrier also orders the clearing of h)
+  float* lg = logits + (size_t)bh * ncap + (size_t)ch * kWideChunk;
+  float v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) v[j] = lg[j * NT + threadIdx.x];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const float e = (v[j] == -__builtin_inff() || M == -__builtin_inff()) ? -1.f : exp_diff(v[j], M);
+    lg[j * NT + threadIdx.x] = e;
+    if (e >= 0.f) {
+      const uint64_t f = to_fix(e);
+      if (f) atomicAdd((unsigned long long*)&h[__float_as_uint(e) >> 20], (unsigned long long)f);
+    }
+  }
+  __syncthreads();
+  uint64_t* st = state + (size_t)bh * kWideStateWords;
+  flush_hist(h, 2048, st + kWideH1, st + kWideC1);
+}
+
+// Level-1 resolution of one head (whole wave): Z, the trivial cases, target, bin and remainder.
+__device__ __forceinline__ void wide_level1(const uint64_t* st, float p, int& mode, uint64_t& Z, int& b1,
+                                            uint64_t& rem1) {
+  const int lane = threadIdx.x & 63;
+  uint64_t z = st[kWideC1 + lane];
+  z = wave_suffix_u64(z);
+  Z = __shfl(z, 0);
+  b1 = 0;
+  rem1 = 0;
+  if (Z == 0ull || !(p < 1.0f)) {
+    mode = 1;  // keep every candidate (threshold 0)
+    return;
+  }
+  mode = 0;
+  double t = ceil((double)p * (double)Z);
+  uint64_t target = (uint64_t)t;
+  if (target < 1ull) target = 1ull;
+  if (target > Z) target = Z;
+  wide_find(st + kWideH1, st + kWideC1, 64, target, b1, rem1);
+}
+
+__global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __restrict__ w, int ncap, float p,
+                                                             uint64_t* __restrict__ state) {
+  __shared__ uint64_t h[2048];
+  __shared__ int s_mode, s_b1;
+  const int nch = ncap / kWideChunk;
+  const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
+  uint64_t* st = state + (size_t)bh * kWideStateWords;
+  for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
+  if (threadIdx.x < 64) {
+    int mode, b1;
+    uint64_t Z, rem1;
+    wide_level1(st, p, mode, Z, b1, rem1);
+    if (threadIdx.x == 0) {
+      s_mode = mode;
+      s_b1 = b1;
+      if (ch == 0) {
+        st[kWideSZ] = Z;
+        st[kWideSMode] = (uint64_t)mode;
+        st[kWideSB1] = (uint64_t)b1;
+        st[kWideSR1] = rem1;
+      }
+    }
+  }
+  __syncthreads();
+  if (s_mode != 0) return;
+  const uint32_t b1 = (uint32_t)s_b1;
+  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
+  float v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const uint32_t key = __float_as_uint(v[j]);
+    if (v[j] >= 0.f && (key >> 20) == b1) {
+      const uint64_t f = to_fix(v[j]);
+      if (f) atomicAdd((unsigned long long*)&h[(key >> 9) & 2047u], (unsigned long long)f);
+    }
+  }
+  __syncthreads();
+  flush_hist(h, 2048, st + kWideH2, st + kWideC2);
+}
+
+__global__ __launch_bounds__(kWideThreads) void k_wide_hist3(const float* __restrict__ w, int ncap,
+                                                             uint64_t* __restrict__ state) {
+  __shared__ uint64_t h[512];
+  __shared__ int s_b2;
+  const int nch = ncap / kWideChunk;
+  const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
+  uint64_t* st = state + (size_t)bh * kWideStateWords;
+  if (st[kWideSMode] != 0ull) return;  // uniform over the head's blocks
+  for (int i = threadIdx.x; i < 512; i += NT) h[i] = 0ull;
+  const uint32_t b1 = (uint32_t)st[kWideSB1];
+  if (threadIdx.x < 64) {
+    int b2;
+    uint64_t rem2;
+    wide_find(st + kWideH2, st + kWideC2, 64, st[kWideSR1], b2, rem2);
+    if (threadIdx.x == 0) {
+      s_b2 = b2;
+      if (ch == 0) {
+        st[kWideSB2] = (uint64_t)b2;
+        st[kWideSR2] = rem2;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t pre = (b1 << 11) | (uint32_t)s_b2;
+  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
+  float v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const uint32_t key = __float_as_uint(v[j]);
+    if (v[j] >= 0.f && (key >> 9) == pre) {
+      const uint64_t f = to_fix(v[j]);
+      if (f) atomicAdd((unsigned long long*)&h[key & 511u], (unsigned long long)f);
+    }
+  }
+  __syncthreads();
+  flush_hist(h, 512, st + kWideH3, st + kWideC3);
+}
+
+// Per (unit, chunk): the G thresholds, head masks, the kept mass per head, union words and count.
+template <int G>
+__global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const float* __restrict__ w, int ncap,
+                                                            int iters, uint64_t* __restrict__ state,
+                                                            uint32_t* __restrict__ head_mask, int mask_words,
+                                                            uint32_t* __restrict__ uwords,
+                                                            int32_t* __restrict__ chunk_cnt) {
+  __shared__ float s_thr[G];
+  __shared__ int s_cnt[NW];
+  const int nch = ncap / kWideChunk;
+  const int u = blockIdx.x / nch, ch = blockIdx.x - u * nch;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const size_t bh0 = (size_t)b * c.Hq + (size_t)h * G;
+  for (int hh = wv; hh < G; hh += NW) {
+    uint64_t* st = state + (bh0 + hh) * kWideStateWords;
+    uint32_t T = 0u;
+    if (st[kWideSMode] == 0ull) {
+      int b3;
+      uint64_t rem3;
+      wide_find(st + kWideH3, st + kWideC3, 16, st[kWideSR2], b3, rem3);
+      T = ((uint32_t)st[kWideSB1] << 20) | ((uint32_t)st[kWideSB2] << 9) | (uint32_t)b3;
+      if (iters < 31) T &= ~((1u << (31 - iters)) - 1u);
+    }
+    if (lane == 0) {
+      s_thr[hh] = __uint_as_float(T);
+      if (ch == 0) st[kWideST] = (uint64_t)T;
+    }
+  }
+  __syncthreads();
+  float thr[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) thr[hh] = s_thr[hh];
+  uint64_t kept[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) kept[hh] = 0ull;
+  int cnt = 0;
+  const int MW = ncap / 32;
+  for (int j = 0; j < EPT; ++j) {
+    const int k = ch * kWideChunk + j * NT + (int)threadIdx.x;
+    const int wd = (ch * kWideChunk + j * NT + wv * 64) >> 5;  // first of the wave's two words
+    float x[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) x[hh] = w[(bh0 + hh) * ncap + k];
+    bool any = false;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const bool keep = x[hh] >= 0.f && x[hh] >= thr[hh];
+      any |= keep;
+      if (keep) kept[hh] += to_fix(x[hh]);
+      if (head_mask) {
+        const unsigned long long bal = __ballot(keep);
+        if (lane == 0) {
+          if (wd < mask_words) head_mask[(bh0 + hh) * mask_words + wd] = (uint32_t)bal;
+          if (wd + 1 < mask_words) head_mask[(bh0 + hh) * mask_words + wd + 1] = (uint32_t)(bal >> 32);
+        }
+      }
+    }
+    const unsigned long long ub = __ballot(any);
+    cnt += __popcll(ub);
+    if (lane == 0) {
+      uwords[(size_t)u * MW + wd] = (uint32_t)ub;
+      uwords[(size_t)u * MW + wd + 1] = (uint32_t)(ub >> 32);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    uint64_t s = wave_suffix_u64(kept[hh]);
+    if (lane == 0 && s) atomicAdd((unsigned long long*)&state[(bh0 + hh) * kWideStateWords + kWideMass],
+                                  (unsigned long long)s);
+  }
+  if (lane == 0) s_cnt[wv] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) t += s_cnt[i];
+    chunk_cnt[(size_t)u * nch + ch] = t;
+  }
+}
+
+// Per (unit, chunk): kept candidates of the union in ascending order, with the token ids and K/V
+// rows the estimate recorded; chunk 0 also writes each head's threshold and kept mass.
+template <int G>
+__global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int ncap, const uint64_t* __restrict__ state,
+                                                            const uint32_t* __restrict__ uwords,
+                                                            const int32_t* __restrict__ chunk_cnt,
+                                                            const int32_t* __restrict__ cand_tok,
+                                                            const int32_t* __restrict__ cand_row,
+                                                            int32_t* __restrict__ union_tok,
+                                                            int32_t* __restrict__ union_row,
+                                                            int32_t* __restrict__ union_cnt, float* threshold,
+                                                            float* mass) {
+  constexpr int WPB = kWideChunk / 32;  // union words per chunk
+  __shared__ uint32_t uw[WPB];
+  __shared__ int woff[WPB];
+  __shared__ int scan_sm[NW + 1];
+  __shared__ int s_off;
+  const int nch = ncap / kWideChunk;
+  const int u = blockIdx.x / nch, ch = blockIdx.x - u * nch;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int tid = threadIdx.x;
+  const size_t bh0 = (size_t)b * c.Hq + (size_t)h * G;
+  if (ch == 0 && tid < G) {
+    const uint64_t* st = state + (bh0 + tid) * kWideStateWords;
+    const uint64_t Z = st[kWideSZ];
+    const float zf = (float)((double)Z / 1099511627776.0);
+    const float T = __uint_as_float((uint32_t)st[kWideST]);
+    threshold[bh0 + tid] = Z ? T / zf : 0.f;
+    if (mass) mass[bh0 + tid] = Z ? (float)((double)st[kWideMass] / (double)Z) : 0.f;
+  }
+  if (tid < 64) {
+    int acc = 0;
+    for (int i = tid; i < ch; i += 64) acc += chunk_cnt[(size_t)u * nch + i];
+    acc = wave_sum_int(acc);
+    if (tid == 0) s_off = acc;
+  }
+  const uint32_t x = (tid < WPB) ? uwords[(size_t)u * (ncap / 32) + (size_t)ch * WPB + tid] : 0u;
+  int total;
+  const int off = block_excl_scan<NW>(__popc(x), scan_sm, &total);
+  if (tid < WPB) {
+    uw[tid] = x;
+    woff[tid] = off;
+  }
+  __syncthreads();
+  const int base = s_off;
+  if (ch == nch - 1 && tid == 0) union_cnt[u] = base + total;
+  const size_t ub = (size_t)u * ncap;
+#pragma unroll 4
+  for (int j = 0; j < EPT; ++j) {
+    const int kl = j * NT + tid;
+    const uint32_t wd = uw[kl >> 5];
+    const int bit = kl & 31;
+    if ((wd >> bit) & 1u) {
+      const int pos = base + woff[kl >> 5] + __popc(wd & ((1u << bit) - 1u));
+      const size_t k = (size_t)ch * kWideChunk + kl;
+      union_tok[ub + pos] = cand_tok[ub + k];
+      union_row[ub + pos] = cand_row[ub + k];
+    }
+  }
+}
+
+hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
+                            float* logits, int ncap, float p, int iters, float* threshold, float* mass,
+                            uint32_t* head_mask, int mask_words, int32_t* union_tok, int32_t* union_row,
+                            int32_t* union_cnt, hipStream_t s) {
+  if (ncap % kWideChunk) return hipErrorInvalidValue;
+  const int nch = ncap / kWideChunk;
+  const unsigned hgrid = (unsigned)(c.B * c.Hq * nch), ugrid = (unsigned)(c.B * c.Hkv * nch);
+  const dim3 blk(kWideThreads);
+  hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, ncap / kEstCands, wd.state);
+  hipLaunchKernelGGL(k_wide_hist2, dim3(hgrid), blk, 0, s, logits, ncap, p, wd.state);
+  hipLaunchKernelGGL(k_wide_hist3, dim3(hgrid), blk, 0, s, logits, ncap, wd.state);
+#define TWL_WIDE_G(GG)                                                                                      \
+  case GG:                                                                                                  \
+    hipLaunchKernelGGL(k_wide_mask<GG>, dim3(ugrid), blk, 0, s, c, logits, ncap, iters, wd.state, head_mask, \
+                       mask_words, wd.uwords, wd.chunk_cnt);                                                \
+    hipLaunchKernelGGL(k_wide_emit<GG>, dim3(ugrid), blk, 0, s, c, ncap, wd.state, wd.uwords, wd.chunk_cnt,  \
+                       cand_tok, cand_row, union_tok, union_row, union_cnt, threshold, mass);              \
+    break;
+  switch (c.G) {
+    TWL_WIDE_G(1)
+    TWL_WIDE_G(2)
+    TWL_WIDE_G(4)
+    TWL_WIDE_G(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef TWL_WIDE_G
+  return hipGetLastError();
+}
+
+}  // namespace twl

@@ -29,9 +29,30 @@ struct CandView {
   const int32_t* items;         // page ids [U][max_items] or ranges [U][max_items][2]
   const int32_t* count;         // [U]
   const int32_t* range_prefix;  // [U][max_items+1] (ranges only; written by launch_range_prefix)
+  const int32_t* chunk_first;   // [U][ncap/kEstCands] (ranges only): range holding each block's first candidate
   int max_items;
   const int32_t* phys;          // pages only, optional: physical page of each listed page id
 };
+
+// Wide top-p (more than 65536 candidates per head): per-head state in 64-bit words -- the three
+// histogram levels (fine bins, then one coarse sum per 32 bins), the kept mass, and the resolved
+// search state.  Words [0, kWideZeroWords) must be zero before the first histogram pass.
+constexpr int kWideChunk = 4096;  // candidates per block of the wide kernels
+constexpr int kWideThreads = 256;
+constexpr int kWideH1 = 0, kWideC1 = 2048, kWideH2 = 2112, kWideC2 = 4160, kWideH3 = 4224, kWideC3 = 4736;
+constexpr int kWideMass = 4752, kWideZeroWords = 4753;
+constexpr int kWideSZ = 4753, kWideSMode = 4754, kWideSB1 = 4755, kWideSR1 = 4756, kWideSB2 = 4757,
+              kWideSR2 = 4758, kWideST = 4759;
+constexpr int kWideStateWords = 4760;
+constexpr int kNarrowMaxCands = 65536;      // largest candidate count of the register-resident top-p
+constexpr int kWideMaxCands = 1 << 22;      // fixed-point mass bound
+struct WideWs {
+  float* pmax;         // [B*Hq][ncap / kEstCands] per-estimate-block logit maxima
+  uint64_t* state;     // [B*Hq][kWideStateWords]
+  int32_t* chunk_cnt;  // [B*Hkv][ncap / kWideChunk]
+  uint32_t* uwords;    // [B*Hkv][ncap / 32] union bitmap
+};
+constexpr int kEstCands = 256;  // candidates per block of the estimate
 
 // Token list of each unit for the attention stage: either padded rows (stride) with counts, or CSR.
 struct ListView {
@@ -48,9 +69,21 @@ hipError_t launch_quantize(const CacheView& c, const int32_t* tok_begin, const i
 hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* scores, hipStream_t s);
 hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep, int32_t* page_phys,
                               int32_t* page_ids, int32_t* count, hipStream_t s);
-hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, hipStream_t s);
+hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, int32_t* chunk_first,
+                               int nchunk, hipStream_t s);
+// wide: when non-null, the estimate also writes the per-block logit maxima and clears the wide state
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
-                           float* logits, int32_t* cand_tok, int32_t* cand_row, hipStream_t s);
+                           float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s);
+hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
+                            float* logits, int ncap, float p, int iters, float* threshold, float* mass,
+                            uint32_t* head_mask, int mask_words, int32_t* union_tok, int32_t* union_row,
+                            int32_t* union_cnt, hipStream_t s);
+hipError_t launch_topp_weighted(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
+                                uint32_t* mask_ws, const int32_t* mult, int mult_stride, hipStream_t s);
+hipError_t launch_cluster_select(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
+                                 const uint16_t* centroids, const int32_t* csize, const int32_t* coff, int C,
+                                 int cpad, float* lam, float* thr, uint32_t* mask_ws, int32_t* ranges,
+                                 int32_t* count, hipStream_t s);
 hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_t* cand_row, const float* logits,
                        int ncap, float p,
                        int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
