@@ -37,7 +37,10 @@ DESCR = {
     "C2": "Llama-3-8B-shaped decode layer: B=1, 32/8 GQA heads, n=32768, 4 K outlier channels, keep 1/4 pages, p=0.85",
     "C3": "head heterogeneity: B=16, 32/8 heads, n=32768, per-head temperature, keep 1/4, p=0.85",
     "C4": "long context: B=4, 32/8 heads, n=131072, 64 planted keys per head, keep 1/4, p=0.9",
+    "C5": "Double-P hierarchical: B=1, 32/8 heads, n=262144, 4096 Zipf(1.1) clusters, cluster p1=0.95 "
+          "then token p=0.9",
 }
+STAGES_CLUSTER = ["cluster_select", "range_prefix", "estimate", "topp_union", "attention", "merge"]
 
 
 def parse():
@@ -107,7 +110,8 @@ def main():
     B, Hq, Hkv, G = w.batch, w.num_q_heads, w.num_kv_heads, w.group
     U = B * Hkv
     kf, p = w.keep_frac, w.p
-    selector = kf < 1.0
+    clusters = w.csize is not None
+    selector = kf < 1.0 and not clusters
     maxcand = 16 * twl.keep_count(w.max_pages, kf) if selector else w.max_seq_len
     ws = torch.empty(twl.workspace_bytes(layers[0][1], maxcand), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, 128), device=dev)
@@ -116,10 +120,18 @@ def main():
     indptrs = [torch.zeros(U + 1, dtype=torch.int32, device=dev) for _ in range(L)]
     toks = torch.empty(U * maxcand, dtype=torch.int32, device=dev)
 
-    def step(i):
+    def step(i, events=None):
         _, cache, t = layers[i % L]
-        twl.decode(cache, t["q"], p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
-                   sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
+        if clusters:
+            twl.decode_clusters(cache, t["q"], p=p, p1=w.p1, centroids=t["centroids"], csize=t["csize"],
+                                coff=t["coff"], out=out, lse=lse, threshold=thr, sel_indptr=indptrs[i % L],
+                                sel_tokens=toks, ws=ws, events=events)
+        elif events is not None:
+            twl.decode_profiled(cache, t["q"], events, p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
+                                sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
+        else:
+            twl.decode(cache, t["q"], p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
+                       sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -142,9 +154,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(K2)]
     torch.cuda.synchronize()
     for i in range(K2):
-        _, cache, t = layers[i % L]
-        twl.decode_profiled(cache, t["q"], evs[i], p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
-                            sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
+        step(i, evs[i])
     torch.cuda.synchronize()
     for i in range(K2):
         for s in range(twl.NUM_STAGES):
@@ -156,12 +166,27 @@ def main():
     # ---- algorithmic bytes (per layer-step, averaged over the layers) ----------------------------
     seq = w.seq_lens.astype(np.int64)
     pages = -(-seq // 16)
-    cand = np.array([min(16 * twl.keep_count(int(P), kf), int(n)) if selector else int(n)
-                     for P, n in zip(pages, seq)])  # valid candidates per sequence (upper bound)
     sel_tokens_total = float(np.mean([ip[-1] for ip in kept]))
     q_bytes = 2 * Hq * 128
-    bytes_sel = (512 * pages.sum() * Hkv) if selector else 0
-    bytes_est = 80 * cand.sum() * Hkv
+    if clusters:
+        # candidates = tokens of the kept clusters, read back from one extra cluster selection per layer
+        C = w.num_clusters
+        ncand = []
+        for _, cache, t in layers:
+            rg = torch.empty((U, C, 2), dtype=torch.int32, device=dev)
+            ct = torch.empty((U,), dtype=torch.int32, device=dev)
+            twl.select_clusters_topp(cache, t["q"], twl.DEFAULT_SM_SCALE, w.p1, 32, t["centroids"], t["csize"],
+                                     t["coff"], C, rg, ct, ws)
+            rg, ct = rg.cpu().numpy(), ct.cpu().numpy()
+            ncand.append(sum(int(rg[u, :ct[u], 1].sum()) for u in range(U)))
+        cand_units_total = float(np.mean(ncand))
+        bytes_sel = U * C * (256 + 8)  # centroid rows + size and offset
+    else:
+        cand = np.array([min(16 * twl.keep_count(int(P), kf), int(n)) if selector else int(n)
+                         for P, n in zip(pages, seq)])  # valid candidates per sequence (upper bound)
+        cand_units_total = float(cand.sum() * Hkv)
+        bytes_sel = (512 * pages.sum() * Hkv) if selector else 0
+    bytes_est = 80 * cand_units_total
     bytes_attn = 516 * sel_tokens_total + q_bytes
     bytes_step = bytes_sel + bytes_est + bytes_attn + 4 * Hq * 128 + q_bytes
     attn_ms = stage_ms[4]
@@ -190,11 +215,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {DESCR[args.workload]}", "batch": B, "q_heads": Hq,
                    "kv_heads": Hkv, "context": int(seq.max()), "p": p, "keep_frac": kf,
-                   "layers_rotated": L, "parallelism": "single GPU"},
+                   "layers_rotated": L, "parallelism": "single GPU",
+                   **({"p1": w.p1, "num_clusters": w.num_clusters} if clusters else {})},
         "hbm": {"algorithmic_bytes_per_step": int(bytes_step), "gbps": round(bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
                 "frac_of_8TBps": round(bytes_step / (ms_per_step * 1e-3) / HBM_PEAK, 4),
-                "kept_tokens_per_step": sel_tokens_total},
-        "stages_us": {n: round(float(x) * 1e3, 3) for n, x in zip(twl.STAGE_NAMES, stage_ms)},
+                "candidates_per_step": cand_units_total, "kept_tokens_per_step": sel_tokens_total},
+        "stages_us": {n: round(float(x) * 1e3, 3)
+                      for n, x in zip(STAGES_CLUSTER if clusters else twl.STAGE_NAMES, stage_ms)},
         "roofline": {"kernel": "k_attn (split-K sparse attention)", "bound": "hbm",
                      "achieved": round(achieved / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": traffic,

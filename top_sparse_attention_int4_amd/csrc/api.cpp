@@ -259,7 +259,7 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
   }
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, E, s));
-  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap};
+  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap, 0};
   TWL_TRY(E.rec(8));
   TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
                       sel_tokens, capacity, s));
@@ -326,7 +326,7 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   TWL_TRY(E.rec(3));
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, E, s));
-  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap};
+  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap, 0};
   TWL_TRY(E.rec(8));
   TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
                       sel_tokens, capacity, s));
@@ -458,7 +458,9 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
   if (st != TWL_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheView c = make_view(cache);
-  ListView lv{sel_tokens, nullptr, sel_indptr, nullptr, 0};
+  const int64_t U = (int64_t)cache->batch * cache->num_kv_heads;
+  TWL_TRY(launch_rows(c, sel_indptr, sel_tokens, at<int32_t>(ws, L.urow), U * ncap, s));
+  ListView lv{sel_tokens, at<int32_t>(ws, L.urow), sel_indptr, nullptr, 0, U * ncap};
   TWL_TRY(launch_attn(c, static_cast<const uint16_t*>(q), sm_scale, lv, L.chunk_tokens, L.max_chunks,
                       at<float>(ws, L.parts), nullptr, nullptr, 0, s));
   TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));

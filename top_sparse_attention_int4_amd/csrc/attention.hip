@@ -3,18 +3,23 @@
 // The pages compute attention only on the top-p survivors, group-wise for GQA over a flattened
 // paged cache, with FlashInfer's balancing across heads whose budgets differ widely (Paper-Notes
 // "关键设计 / 负载均衡": per-head budgets from ~2% to ~50%; paperlayer §4.2 and §B.2).  Here the
-// token lists of all (sequence, kv-head) units are cut into equal chunks of CH tokens and the
-// chunks are numbered across units (head-flattened); a persistent grid of one-wave workgroups walks
-// that numbering with a static stride, so a unit with a long list simply owns more chunks.
+// token lists of all (sequence, kv-head) units are cut into equal chunks of CH tokens, numbered
+// across units (head-flattened), and every chunk is one workgroup of four waves; the hardware
+// dispatcher hands chunks to compute units as they free up, so a unit with a long list simply owns
+// more chunks and no compute unit waits on a slow one.
 //
-// Per 64-token sub-block of a chunk (one wave):
-//   * each lane resolves one token id to its paged K/V row;
+// Each wave takes a contiguous quarter of its chunk in 16-token sub-blocks, software-pipelined: the
+// K/V rows of sub-block i+2 are read before the data of sub-block i+1 is requested, and that data is
+// in flight while sub-block i is computed.  Loads are unconditional (the row of a list entry past
+// the chunk is clamped to a real row and masked afterwards) so the compiler can count outstanding
+// loads exactly.  Per sub-block:
 //   * S = K q^T with bf16 MFMA (v_mfma_f32_16x16x32_bf16): A = 16 tokens x 32 dims of K loaded
 //     straight into registers, B = the G query heads (padded to 16 columns);
-//   * online softmax in the log2 domain per head, P and the rescale factor shared through LDS;
+//   * online softmax in the log2 domain per head, P and the rescale factor shared through LDS
+//     within the wave;
 //   * O += P V on the vector ALU in fp32: lane (g, n) owns dims 8n..8n+7 of tokens g, g+4, ...
-// The chunk's partial (max, sum, unnormalised output) per head goes to the workspace; the merge
-// combines a unit's chunks in chunk order.
+// The four waves' (max, sum, output) meet in LDS and the chunk's partial goes to the workspace; the
+// merge combines a unit's chunks in chunk order.
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -23,7 +28,7 @@ namespace twl {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPartStride = 2 + kD;  // (m, l, o[128]) per head
+constexpr int kPartStride = kPartFloats;  // (m, l, pad, pad, o[128]) per head
 
 __device__ __forceinline__ int list_count(const ListView& L, int u) {
   return L.indptr ? (L.indptr[u + 1] - L.indptr[u]) : L.counts[u];
@@ -61,17 +66,29 @@ __device__ int find_unit(const ListView& L, int U, int CH, int cid, int* chunk0,
   return -1;
 }
 
-template <int G>
-__global__ __launch_bounds__(64) void k_attn(CacheView c, const uint16_t* __restrict__ q, float sm_log2,
-                                             ListView L, int CH, int max_chunks, float* __restrict__ partials,
-                                             int32_t* csr_indptr, int32_t* csr_tokens, int64_t capacity) {
-  const int U = c.B * c.Hkv;
-  const int lane = threadIdx.x;
-  const int nn = lane & 15, grp = lane >> 4;
-  __shared__ float Pl[64 * G];
-  __shared__ float Al[G];
+constexpr int kAttnWaves = 4;
+constexpr int kAttnSB = 16;  // tokens per sub-block
 
-  if (csr_indptr && blockIdx.x == 0) {
+// NSB: sub-blocks per wave (chunk = 4 waves x NSB x 16 tokens); the sequence is fully unrolled so
+// the count of loads in flight is known at every wait.
+template <int G, int NSB>
+__global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uint16_t* __restrict__ q,
+                                                          float sm_log2, ListView L, int max_chunks,
+                                                          float* __restrict__ partials, int32_t* csr_indptr,
+                                                          int32_t* csr_tokens, int64_t capacity) {
+  constexpr int NWV = kAttnWaves, SB = kAttnSB, VS = SB / 4, CH = NWV * NSB * SB;
+  const int U = c.B * c.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nn = lane & 15, grp = lane >> 4;
+  __shared__ float Pl[NWV][SB * G];
+  __shared__ float Al[NWV][G];
+  __shared__ float sm_m[NWV][G], sm_l[NWV][G];
+  __shared__ float4 so[NWV][G][32];
+  __shared__ int s_u, s_c0, s_t0;
+
+  const int cid = blockIdx.x;
+  if (csr_indptr && cid == 0 && wv == 0) {
     int tbase = 0;
     for (int base = 0; base < U; base += 64) {
       const int u = base + lane;
@@ -82,180 +99,244 @@ __global__ __launch_bounds__(64) void k_attn(CacheView c, const uint16_t* __rest
     }
     if (lane == 0) csr_indptr[U] = tbase;
   }
-
-  for (int cid = blockIdx.x;; cid += gridDim.x) {
+  if (wv == 0) {
     int chunk0 = 0, tok0 = 0;
-    if (cid >= max_chunks) break;  // more chunks than the workspace holds: lists exceed their bound
     const int u = find_unit(L, U, CH, cid, &chunk0, &tok0);
-    if (u < 0) break;
-    const int b = u / c.Hkv, h = u - b * c.Hkv;
-    const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-    const int cnt = max(0, list_count(L, u));
-    const int32_t* toks = list_ptr(L, u);
-    const int t_begin = (cid - chunk0) * CH;
-    const int t_end = min(cnt, t_begin + CH);
-
-    // B operand: q of head nn (zero for padding columns), dims 32kb + 8grp .. +7
-    bf16x8_t qv[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (nn < G) {
-        qv[kb] = *reinterpret_cast<const bf16x8_t*>(q + ((size_t)b * c.Hq + (size_t)h * G + nn) * kD + kb * 32 + grp * 8);
-      } else {
-        qv[kb] = bf16x8_t{};
-      }
+    if (lane == 0) {
+      s_u = u;
+      s_c0 = chunk0;
+      s_t0 = tok0;
     }
-    float m_run = -__builtin_inff(), l_run = 0.f;
-    float acc[G][8];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[hh][i] = 0.f;
+  }
+  __syncthreads();
+  const int u = __builtin_amdgcn_readfirstlane(s_u);
+  if (u < 0) return;  // past the last chunk of the last unit
+  const int chunk0 = __builtin_amdgcn_readfirstlane(s_c0), tok0 = __builtin_amdgcn_readfirstlane(s_t0);
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  int cnt = __builtin_amdgcn_readfirstlane(max(0, list_count(L, u)));
+  if (L.indptr) {  // a CSR list that breaks its declared bound is cut at the arrays' end
+    const int64_t a = __builtin_amdgcn_readfirstlane(L.indptr[u]);
+    cnt = (a < 0 || a >= L.cap) ? 0 : (int)min((int64_t)cnt, L.cap - a);
+  }
+  const int32_t* toks = list_ptr(L, u);
+  const int32_t* rws = list_rows(L, u);
+  const int t_begin = (cid - chunk0) * CH;
+  const int t_end = max(t_begin, min(cnt, t_begin + CH));
+  const int t_last = max(t_end - 1, t_begin);
+  const int qlen = CH / NWV;
+  const int w_begin = t_begin + wv * qlen, w_end = min(t_end, w_begin + qlen);
 
-    const int32_t* rws = L.rows ? list_rows(L, u) : nullptr;
-    // K/V row of list entry idx (-1 past the chunk or for a token outside the sequence)
-    auto row_of = [&](int idx) -> int {
-      if (idx >= t_end) return -1;
-      if (rws) return rws[idx];
-      const int tok = toks[idx];
-      if (tok < 0 || tok >= n) return -1;
-      return (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15);
-    };
-    int row_next = row_of(t_begin + lane);
-    for (int sb = t_begin; sb < t_end; sb += 64) {
-      const int row = row_next;  // K/V row index; rows < 2^31 is checked on the host
-      const unsigned long long vmask = __ballot(row >= 0);
+  // B operand: q of head nn (zero for padding columns), dims 32kb + 8grp .. +7
+  bf16x8_t qv[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    if (nn < G) {
+      qv[kb] = *reinterpret_cast<const bf16x8_t*>(q + ((size_t)b * c.Hq + (size_t)h * G + nn) * kD + kb * 32 + grp * 8);
+    } else {
+      qv[kb] = bf16x8_t{};
+    }
+  }
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  float acc[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[hh][i] = 0.f;
 
-      bf16x8_t kv[4][4];
+  // a real row of the chunk for every index (validity is decided from the index at use)
+  auto row_ld = [&](int idx) -> int { return rws[min(idx, t_last)]; };
+  auto issue = [&](int row, bf16x8_t (&kv)[4], uint4 (&vv)[VS]) {
+    const int rs = max(row, 0);
+    const int r = __shfl(rs, nn);
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        const int r = __shfl(row, tau * 16 + nn);
+    for (int kb = 0; kb < 4; ++kb)
+      kv[kb] = *reinterpret_cast<const bf16x8_t*>(c.k + (size_t)r * kD + kb * 32 + grp * 8);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          kv[tau][kb] = (r >= 0) ? *reinterpret_cast<const bf16x8_t*>(c.k + (size_t)r * kD + kb * 32 + grp * 8)
-                                 : bf16x8_t{};
+    for (int s2 = 0; s2 < VS; ++s2) {
+      const int rv = __shfl(rs, grp + 4 * s2);
+      vv[s2] = *reinterpret_cast<const uint4*>(c.v + (size_t)rv * kD + nn * 8);
+    }
+  };
+  auto consume = [&](int sb, int row, const bf16x8_t (&kv)[4], const uint4 (&vv)[VS]) {
+    const unsigned long long vmask = __ballot(lane < SB && sb + lane < w_end && row >= 0);
+    floatx4_t sacc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[kb], qv[kb], sacc, 0, 0, 0);
+    // lane holds S[token 4*grp + e][head nn]
+    float sv[4];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * grp + e;
+      const float x = ((vmask >> t) & 1ull) ? sacc[e] * sm_log2 : -__builtin_inff();
+      sv[e] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2f(m_run - m_new);
+    float ps = 0.f;
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pv[e] = (sv[e] == -__builtin_inff()) ? 0.f : exp2f(sv[e] - m_new);
+      ps += pv[e];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (nn < G) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Pl[wv][(4 * grp + e) * G + nn] = pv[e];
+      if (grp == 0) Al[wv][nn] = alpha;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float a = Al[wv][hh];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[hh][i] *= a;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < VS; ++s2) {
+      const int t = grp + 4 * s2;
+      const bool ok = (vmask >> t) & 1ull;  // rows past the list or outside the sequence contribute 0
+      const uint32_t w[4] = {ok ? vv[s2].x : 0u, ok ? vv[s2].y : 0u, ok ? vv[s2].z : 0u, ok ? vv[s2].w : 0u};
+      float vf[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vf[2 * i] = bf16_lo(w[i]);
+        vf[2 * i + 1] = bf16_hi(w[i]);
       }
-      uint4 vv[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int r = __shfl(row, grp + 4 * s);
-        vv[s] = (r >= 0) ? *reinterpret_cast<const uint4*>(c.v + (size_t)r * kD + nn * 8) : make_uint4(0u, 0u, 0u, 0u);
-      }
-      row_next = row_of(sb + 64 + lane);  // next sub-block's rows load while this one computes
-
-      floatx4_t sacc[4];
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        sacc[tau] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv[tau][kb], qv[kb], sacc[tau], 0, 0, 0);
-      }
-
-      // lane holds S[token tau*16 + 4*grp + e][head nn]
-      float sv[16];
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = tau * 16 + 4 * grp + e;
-          const float x = ((vmask >> t) & 1ull) ? sacc[tau][e] * sm_log2 : -__builtin_inff();
-          sv[tau * 4 + e] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2f(m_run - m_new);
-      float ps = 0.f;
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        pv[i] = (sv[i] == -__builtin_inff()) ? 0.f : exp2f(sv[i] - m_new);
-        ps += pv[i];
-      }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      if (nn < G) {
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Pl[(tau * 16 + 4 * grp + e) * G + nn] = pv[tau * 4 + e];
-        if (grp == 0) Al[nn] = alpha;
-      }
-      __syncthreads();
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float a = Al[hh];
+        const float pp = Pl[wv][t * G + hh];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[hh][i] *= a;
+        for (int i = 0; i < 8; ++i) acc[hh][i] = fmaf(pp, vf[i], acc[hh][i]);
       }
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const int t = grp + 4 * s;
-        const uint32_t w[4] = {vv[s].x, vv[s].y, vv[s].z, vv[s].w};
-        float vf[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          vf[2 * i] = bf16_lo(w[i]);
-          vf[2 * i + 1] = bf16_hi(w[i]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          const float pp = Pl[t * G + hh];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[hh][i] = fmaf(pp, vf[i], acc[hh][i]);
-        }
-      }
-      __syncthreads();
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
-    // sum the four token groups
+  if (t_end > t_begin) {
+    // every row of the wave's quarter first, then the data of sub-block i + 1 in flight while
+    // sub-block i is computed; sub-blocks past the list read real rows and are masked
+    int rows[NSB];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh)
+    for (int i = 0; i < NSB; ++i) rows[i] = row_ld(w_begin + i * SB + lane);
+    bf16x8_t kv[2][4];
+    uint4 vv[2][VS];
+    issue(rows[0], kv[0], vv[0]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float x = acc[hh][i];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        acc[hh][i] = x;
-      }
-    float* part = partials + (size_t)cid * G * kPartStride;
-    if (grp == 0) {
+    for (int i = 0; i < NSB; ++i) {
+      if (i + 1 < NSB) issue(rows[i + 1], kv[(i + 1) & 1], vv[(i + 1) & 1]);
+      consume(w_begin + i * SB, rows[i], kv[i & 1], vv[i & 1]);
+    }
+  }
+
+  // sum the four token groups of the wave, then combine the block's waves in wave order
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float4* o4 = reinterpret_cast<float4*>(part + hh * kPartStride + 2 + nn * 8);
-        o4[0] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
-        o4[1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
-      }
-      if (nn < G) {
-        part[nn * kPartStride] = m_run;
-        part[nn * kPartStride + 1] = l_run;
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = acc[hh][i];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      acc[hh][i] = x;
+    }
+  if (grp == 0) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      so[wv][hh][2 * nn] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+      so[wv][hh][2 * nn + 1] = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
+    }
+    if (nn < G) {
+      sm_m[wv][nn] = m_run;
+      sm_l[wv][nn] = l_run;
+    }
+  }
+  __syncthreads();
+  float* part = partials + (size_t)cid * G * kPartStride;
+  for (int t = tid; t < G * 32; t += 64 * NWV) {
+    const int hh = t >> 5, d4 = t & 31;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, sm_m[w][hh]);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        if (sm_m[w][hh] != -__builtin_inff()) {
+          const float sc = exp2f(sm_m[w][hh] - M);
+          const float4 x = so[w][hh][d4];
+          o.x += x.x * sc;
+          o.y += x.y * sc;
+          o.z += x.z * sc;
+          o.w += x.w * sc;
+          l += sm_l[w][hh] * sc;
+        }
       }
     }
-    if (csr_tokens) {
-      for (int i = t_begin + lane; i < t_end; i += 64)
-        if (tok0 + i < capacity) csr_tokens[tok0 + i] = toks[i];
+    reinterpret_cast<float4*>(part + hh * kPartStride + 4)[d4] = o;
+    if (d4 == 0) {
+      part[hh * kPartStride] = M;
+      part[hh * kPartStride + 1] = l;
+    }
+  }
+  if (csr_tokens) {
+    // all loads of the chunk's token ids in flight before their stores (CH <= 512)
+    int tk[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = t_begin + 256 * r + tid;
+      tk[r] = (i < t_end) ? toks[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = t_begin + 256 * r + tid;
+      if (i < t_end && tok0 + i < capacity) csr_tokens[tok0 + i] = tk[r];
     }
   }
 }
 
-// One block per (unit, head), one thread per output dim: combine the unit's chunk partials in chunk
-// order.  The per-chunk rescale factors are staged in LDS 128 chunks at a time so the output loads
-// of many chunks are in flight together.
+// K/V row of every entry of a CSR token list (-1 for ids outside the sequence), so the attention's
+// loads never wait on a page-table lookup.
+__global__ __launch_bounds__(256) void k_rows(CacheView c, const int32_t* __restrict__ indptr,
+                                              const int32_t* __restrict__ tokens, int32_t* __restrict__ rows,
+                                              int64_t capacity) {
+  const int u = blockIdx.y;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int a = indptr[u], e = indptr[u + 1];
+  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+  for (int i = a + (int)(blockIdx.x * 256 + threadIdx.x); i < e; i += (int)(gridDim.x * 256)) {
+    if (i < 0 || i >= capacity) continue;
+    const int tok = tokens[i];
+    int r = -1;
+    if (tok >= 0 && tok < n) r = (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15);
+    rows[i] = r;
+  }
+}
+
+// One block per (unit, head): the unit's chunk partials are merged by 32 rows of 32 threads, row r
+// taking chunks r, r + 32, ... in order with a running maximum and thread j owning dims 4j..4j+3
+// (four chunks' loads in flight per thread); the 32 row results are then combined in row order.
 template <int G>
-__global__ __launch_bounds__(128) void k_merge(CacheView c, ListView L, int CH, int max_chunks,
-                                               const float* __restrict__ partials, float* out, float* lse) {
+__global__ __launch_bounds__(1024) void k_merge(CacheView c, ListView L, int CH, int max_chunks,
+                                                const float* __restrict__ partials, float* out, float* lse) {
+  constexpr int NR = 32, UNR = 4;
   const int u = blockIdx.x / G, hh = blockIdx.x - (blockIdx.x / G) * G;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, r = tid >> 5, j = tid & 31;
   __shared__ int s_c0, s_nch;
-  __shared__ float sc[128];
-  __shared__ float red[2 * 2 * 4];
-  BlockReduce<2> br{red};
+  __shared__ float sM[NR], sL[NR];
+  __shared__ float4 sO[NR][32];
   if (tid < 64) {
     int acc = 0;
     for (int i = tid; i < u; i += 64) acc += (max(0, list_count(L, i)) + CH - 1) / CH;
@@ -270,34 +351,64 @@ __global__ __launch_bounds__(128) void k_merge(CacheView c, ListView L, int CH, 
   const int nch = max(0, min(s_nch, max_chunks - c0));
   const float* base = partials + ((size_t)c0 * G + hh) * kPartStride;
   constexpr size_t kStep = (size_t)G * kPartStride;
-  float mloc = -__builtin_inff();
-  for (int k = tid; k < nch; k += 128) mloc = fmaxf(mloc, base[k * kStep]);
-  const float M = br.max(mloc);
-  float lpart = 0.f, Os = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int k0 = 0; k0 < nch; k0 += 128) {
-      const int k = k0 + tid;
-      float s = 0.f;
-      if (k < nch) {
-        s = exp2f(base[k * kStep] - M);
-        lpart += base[k * kStep + 1] * s;
+  float M = -__builtin_inff(), Ls = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = r; k0 < nch; k0 += NR * UNR) {
+    float mk[UNR], lk[UNR];
+    float4 ok[UNR];
+#pragma unroll
+    for (int i = 0; i < UNR; ++i) {
+      const int k = k0 + NR * i;
+      const bool v = k < nch;
+      const float* pk = base + (size_t)(v ? k : 0) * kStep;
+      mk[i] = v ? pk[0] : -__builtin_inff();
+      lk[i] = v ? pk[1] : 0.f;
+      ok[i] = v ? reinterpret_cast<const float4*>(pk + 4)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < UNR; ++i) {
+      if (mk[i] != -__builtin_inff()) {
+        const float Mn = fmaxf(M, mk[i]);
+        const float sa = exp2f(M - Mn), sb = exp2f(mk[i] - Mn);
+        Ls = Ls * sa + lk[i] * sb;
+        o.x = o.x * sa + ok[i].x * sb;
+        o.y = o.y * sa + ok[i].y * sb;
+        o.z = o.z * sa + ok[i].z * sb;
+        o.w = o.w * sa + ok[i].w * sb;
+        M = Mn;
       }
-      sc[tid] = s;
-      __syncthreads();
-      const int kn = min(128, nch - k0);
-      const float* po = base + (size_t)k0 * kStep + 2 + tid;
-#pragma unroll 16
-      for (int i = 0; i < kn; ++i) Os += po[i * kStep] * sc[i];
-      __syncthreads();
     }
   }
-  const float Ls = br.sum(lpart);
-  const size_t oh = (size_t)b * c.Hq + (size_t)h * G + hh;
-  out[oh * kD + tid] = (Ls > 0.f) ? Os / Ls : 0.f;
-  if (lse && tid == 0) lse[oh] = (Ls > 0.f) ? (M + log2f(Ls)) * 0.69314718055994530942f : -__builtin_inff();
+  if (j == 0) {
+    sM[r] = M;
+    sL[r] = Ls;
+  }
+  sO[r][j] = o;
+  __syncthreads();
+  if (tid < kD) {
+    float Mt = -__builtin_inff();
+#pragma unroll 8
+    for (int i = 0; i < NR; ++i) Mt = fmaxf(Mt, sM[i]);
+    float num = 0.f, den = 0.f;
+    if (Mt != -__builtin_inff()) {
+      const float* so = reinterpret_cast<const float*>(&sO[0][0]);
+#pragma unroll 8
+      for (int i = 0; i < NR; ++i) {
+        if (sM[i] != -__builtin_inff()) {
+          const float s = exp2f(sM[i] - Mt);
+          num += so[i * kD + tid] * s;
+          den += sL[i] * s;
+        }
+      }
+    }
+    const size_t oh = (size_t)b * c.Hq + (size_t)h * G + hh;
+    out[oh * kD + tid] = (den > 0.f) ? num / den : 0.f;
+    if (lse && tid == 0) lse[oh] = (den > 0.f) ? (Mt + log2f(den)) * 0.69314718055994530942f : -__builtin_inff();
+  }
 }
 
 int attn_chunk_tokens(int64_t total_upper) {
+  // 64 tokens (one sub-block per wave) up to 512, aiming at about 4096 chunks
   int64_t sb = total_upper / (64 * 4096);
   int s = 1;
   while (s * 2 <= sb && s < 8) s *= 2;
@@ -307,18 +418,40 @@ int attn_chunk_tokens(int64_t total_upper) {
 hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
                        int64_t max_chunks, float* partials, int32_t* csr_indptr, int32_t* csr_tokens,
                        int64_t capacity, hipStream_t s) {
+  if (!list.rows) return hipErrorInvalidValue;
   const float sm_log2 = sm * 1.44269504088896340736f;
-  int64_t grid = max_chunks;
-  const int64_t persistent = 256 * 8;
-  if (grid > persistent) grid = persistent;
-  if (grid < 1) grid = 1;
-  switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_attn<1>, dim3((unsigned)grid), dim3(64), 0, s, c, q, sm_log2, list, chunk_tokens, (int)max_chunks, partials, csr_indptr, csr_tokens, capacity); break;
-    case 2: hipLaunchKernelGGL(k_attn<2>, dim3((unsigned)grid), dim3(64), 0, s, c, q, sm_log2, list, chunk_tokens, (int)max_chunks, partials, csr_indptr, csr_tokens, capacity); break;
-    case 4: hipLaunchKernelGGL(k_attn<4>, dim3((unsigned)grid), dim3(64), 0, s, c, q, sm_log2, list, chunk_tokens, (int)max_chunks, partials, csr_indptr, csr_tokens, capacity); break;
-    case 8: hipLaunchKernelGGL(k_attn<8>, dim3((unsigned)grid), dim3(64), 0, s, c, q, sm_log2, list, chunk_tokens, (int)max_chunks, partials, csr_indptr, csr_tokens, capacity); break;
+  const int64_t grid = max_chunks < 1 ? 1 : max_chunks;
+  const dim3 blk(64 * kAttnWaves);
+#define TWL_ATTN_G(GG, NS)                                                                                    \
+  case GG:                                                                                                    \
+    hipLaunchKernelGGL((k_attn<GG, NS>), dim3((unsigned)grid), blk, 0, s, c, q, sm_log2, list, (int)max_chunks, \
+                       partials, csr_indptr, csr_tokens, capacity);                                          \
+    break;
+#define TWL_ATTN_NSB(NS)                   \
+  case NS * kAttnWaves * kAttnSB:          \
+    switch (c.G) {                         \
+      TWL_ATTN_G(1, NS)                    \
+      TWL_ATTN_G(2, NS)                    \
+      TWL_ATTN_G(4, NS)                    \
+      TWL_ATTN_G(8, NS)                    \
+      default: return hipErrorInvalidValue; \
+    }                                      \
+    break;
+  switch (chunk_tokens) {
+    TWL_ATTN_NSB(1)
+    TWL_ATTN_NSB(2)
+    TWL_ATTN_NSB(4)
+    TWL_ATTN_NSB(8)
     default: return hipErrorInvalidValue;
   }
+#undef TWL_ATTN_G
+#undef TWL_ATTN_NSB
+  return hipGetLastError();
+}
+
+hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,
+                       int64_t capacity, hipStream_t s) {
+  hipLaunchKernelGGL(k_rows, dim3(16, (unsigned)(c.B * c.Hkv)), dim3(256), 0, s, c, indptr, tokens, rows, capacity);
   return hipGetLastError();
 }
 
@@ -326,10 +459,10 @@ hipError_t launch_merge(const CacheView& c, const ListView& list, int chunk_toke
                         const float* partials, float* out, float* lse, hipStream_t s) {
   dim3 grid((unsigned)(c.B * c.Hkv * c.G));
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_merge<1>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 2: hipLaunchKernelGGL(k_merge<2>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 4: hipLaunchKernelGGL(k_merge<4>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 8: hipLaunchKernelGGL(k_merge<8>, grid, dim3(128), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 1: hipLaunchKernelGGL(k_merge<1>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 2: hipLaunchKernelGGL(k_merge<2>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 4: hipLaunchKernelGGL(k_merge<4>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    case 8: hipLaunchKernelGGL(k_merge<8>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -36,33 +36,43 @@ __device__ __forceinline__ int cand_token(const CandView& cand, int u, int k, in
 
 // Prefix sums of range lengths per unit (lengths < 0 count as 0), and for every block of kEstCands
 // candidates the index of the range holding its first candidate (count when past the last one).
-__global__ __launch_bounds__(256) void k_range_prefix(CacheView c, CandView cand, int32_t* prefix,
-                                                      int32_t* chunk_first, int nchunk) {
-  constexpr int NW = 4;
+// Each thread takes 4 consecutive ranges per pass (loads in flight together), 4096 ranges a pass.
+__global__ __launch_bounds__(1024) void k_range_prefix(CacheView c, CandView cand, int32_t* prefix,
+                                                       int32_t* chunk_first, int nchunk) {
+  constexpr int NT = 1024, NW = NT / 64, IPT = 4;
   __shared__ int scan_sm[NW + 1];
   const int u = blockIdx.x;
   const int cnt = clampi(cand.count[u], 0, cand.max_items);
   int32_t* pre = prefix + (size_t)u * (cand.max_items + 1);
   int32_t* cf = chunk_first + (size_t)u * nchunk;
+  const int32_t* it = cand.items + (size_t)u * cand.max_items * 2;
   int carry = 0;
-  for (int base = 0; base < cnt; base += 256) {
-    const int i = base + (int)threadIdx.x;
-    int len = 0;
-    if (i < cnt) len = max(0, cand.items[((size_t)u * cand.max_items + i) * 2 + 1]);
+  for (int base = 0; base < cnt; base += NT * IPT) {
+    const int i0 = base + (int)threadIdx.x * IPT;
+    int len[IPT];
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      len[i] = (i0 + i < cnt) ? max(0, it[(size_t)(i0 + i) * 2 + 1]) : 0;
+      local += len[i];
+    }
     int total;
-    const int ex = block_excl_scan<NW>(len, scan_sm, &total);
-    if (i < cnt) {
-      const int s0 = carry + ex;
-      pre[i] = s0;
-      if (len > 0) {
-        const int64_t e0 = (int64_t)s0 + len;
-        for (int j = (s0 + kEstCands - 1) / kEstCands; j < nchunk && (int64_t)j * kEstCands < e0; ++j) cf[j] = i;
+    int s0 = carry + block_excl_scan<NW>(local, scan_sm, &total);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      if (i0 + i < cnt) {
+        pre[i0 + i] = s0;
+        if (len[i] > 0) {
+          const int64_t e0 = (int64_t)s0 + len[i];
+          for (int j = (s0 + kEstCands - 1) / kEstCands; j < nchunk && (int64_t)j * kEstCands < e0; ++j) cf[j] = i0 + i;
+        }
+        s0 += len[i];
       }
     }
     carry += total;
   }
   if (threadIdx.x == 0) pre[cnt] = carry;
-  for (int j = threadIdx.x; j < nchunk; j += 256)
+  for (int j = threadIdx.x; j < nchunk; j += NT)
     if ((int64_t)j * kEstCands >= carry) cf[j] = cnt;
 }
 
@@ -75,16 +85,16 @@ __device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView&
   tok = -1;
   row = -1;
   if (cand.mode == kCandPages && cand.phys) {
+    // the id loads do not wait for the count: the index is clamped into the unit's row and the
+    // entry is discarded afterwards when it lies past the count
     const int pi = k >> 4;
-    if (pi < cnt) {
-      const size_t idx = (size_t)u * cand.max_items + pi;
-      const int page = cand.items[idx];
-      const int phys = cand.phys[idx];
-      const int t = page * kPage + (k & 15);
-      if (page >= 0 && t < n) {
-        tok = t;
-        row = (phys * c.Hkv + h) * kPage + (k & 15);
-      }
+    const size_t idx = (size_t)u * cand.max_items + min(pi, cand.max_items - 1);
+    const int page = cand.items[idx];
+    const int phys = cand.phys[idx];
+    const int t = page * kPage + (k & 15);
+    if (pi < cnt && page >= 0 && t < n) {
+      tok = t;
+      row = (phys * c.Hkv + h) * kPage + (k & 15);
     }
     return;
   }
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
 
 hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, int32_t* chunk_first,
                                int nchunk, hipStream_t s) {
-  hipLaunchKernelGGL(k_range_prefix, dim3((unsigned)(c.B * c.Hkv)), dim3(256), 0, s, c, cand, prefix, chunk_first,
+  hipLaunchKernelGGL(k_range_prefix, dim3((unsigned)(c.B * c.Hkv)), dim3(1024), 0, s, c, cand, prefix, chunk_first,
                      nchunk);
   return hipGetLastError();
 }

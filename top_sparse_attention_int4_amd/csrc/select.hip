@@ -23,9 +23,7 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score(CacheView c
   const int u = blockIdx.x / blocks_per_unit;
   const int blk = blockIdx.x - u * blocks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int P = (n + kPage - 1) / kPage;
-  if (blk * 64 >= P) return;
+  if (blk * 64 >= c.maxP) return;
   const int hh = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
   // the block's 64 pages of bounds, staged with coalesced loads (row = 32 x 16 B, padded by 16 B)
@@ -34,15 +32,23 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score(CacheView c
   __shared__ float qneg[G][kD];
   __shared__ float sig[G][64];
   const int32_t* pt = c.page_table + (size_t)b * c.maxP;
+  constexpr int R = 64 * 32 / NT;
+  int phys[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {  // page-table reads in flight with the sequence length
+    const int j = blk * 64 + ((int)threadIdx.x >> 5) + r * (NT / 32);
+    phys[r] = pt[min(j, c.maxP - 1)];
+  }
+  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+  const int P = (n + kPage - 1) / kPage;
+  if (blk * 64 >= P) return;
   {
-    // all page-table reads first, then all bound reads, so every load of the tile is in flight at once
-    constexpr int R = 64 * 32 / NT;
+    // then all bound reads, so every load of the tile is in flight at once
     const int part = threadIdx.x & 31;
-    int phys[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int j = blk * 64 + ((int)threadIdx.x >> 5) + r * (NT / 32);
-      phys[r] = (j < P) ? pt[j] : -1;
+      if (j >= P) phys[r] = -1;
     }
     uint4 v[R];
 #pragma unroll
@@ -98,17 +104,29 @@ __device__ __forceinline__ uint32_t desc_key(float f) {
 
 constexpr int kSelLdsKeys = 8192;
 
-// Exact top-K of one unit's page scores: radix select of the K-th smallest key (4 passes of 8 bits,
-// integer histograms), ties at the threshold key resolved towards lower page ids, then an
-// order-preserving compaction writes the kept page ids in ascending order.
+// Exact top-K of one unit's page scores: radix select of the K-th smallest key with integer
+// histograms of 8-bit digits, starting below the leading bits that all keys share (a block AND/OR
+// reduction finds them, so no pass histograms a digit every key has in common); ties at the
+// threshold key are resolved towards lower page ids, and an order-preserving compaction writes the
+// kept page ids in ascending order (one scan when every tied key is kept, else a second scan ranks
+// the ties).
 __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* __restrict__ scores,
                                                       float keep_frac, int max_keep, int32_t* page_phys,
                                                       int32_t* page_ids, int32_t* count) {
   constexpr int NT = 1024, NW = NT / 64;
   const int u = blockIdx.x;
   const int b = u / c.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t* pt = c.page_table + (size_t)b * c.maxP;
   int32_t* phys_out = page_phys ? page_phys + (size_t)u * max_keep : nullptr;
+  const float* sc = scores + (size_t)u * c.maxP;
+  constexpr int R = kSelLdsKeys / NT;
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {  // score reads in flight with the sequence length
+    const int i = tid + r * NT;
+    v[r] = (i < c.maxP) ? sc[i] : 0.f;
+  }
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
   int K = 0;
@@ -116,59 +134,81 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
     const float kf = ceilf(fminf(keep_frac * (float)P, (float)P));
     K = clampi((int)kf, 1, P);
   }
-  if (threadIdx.x == 0) count[u] = K;
+  if (tid == 0) count[u] = K;
   if (K == 0) return;
   int32_t* out = page_ids + (size_t)u * max_keep;
   if (K == P) {
-    for (int i = threadIdx.x; i < P; i += NT) {
+    for (int i = tid; i < P; i += NT) {
       out[i] = i;
       if (phys_out) phys_out[i] = pt[i];
     }
     return;
   }
-  const float* sc = scores + (size_t)u * c.maxP;
 
   __shared__ uint32_t keys[kSelLdsKeys];
   __shared__ int hist[2][256];
-  __shared__ uint32_t s_prefix, s_mask;
-  __shared__ int s_rem;
+  __shared__ uint32_t s_prefix, s_mask, s_and[NW], s_or[NW];
+  __shared__ int s_rem, s_cnt;
   __shared__ int scan_sm[NW + 1];
   const bool in_lds = P <= kSelLdsKeys;
+  uint32_t kand = 0xffffffffu, kor = 0u;
   if (in_lds) {
-    constexpr int R = kSelLdsKeys / NT;  // all score loads in flight together
-    float v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int i = (int)threadIdx.x + r * NT;
-      v[r] = (i < P) ? sc[i] : 0.f;
+      const int i = tid + r * NT;
+      if (i < P) {
+        const uint32_t k = desc_key(v[r]);
+        keys[i] = k;
+        kand &= k;
+        kor |= k;
+      }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int i = (int)threadIdx.x + r * NT;
-      if (i < P) keys[i] = desc_key(v[r]);
+  } else {
+    for (int i = tid; i < P; i += NT) {
+      const uint32_t k = desc_key(sc[i]);
+      kand &= k;
+      kor |= k;
     }
   }
-  for (int i = threadIdx.x; i < 512; i += NT) (&hist[0][0])[i] = 0;
-  if (threadIdx.x == 0) {
-    s_prefix = 0u;
-    s_mask = 0u;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    kand &= (uint32_t)__shfl_xor((int)kand, d);
+    kor |= (uint32_t)__shfl_xor((int)kor, d);
+  }
+  if (lane == 0) {
+    s_and[wv] = kand;
+    s_or[wv] = kor;
+  }
+  for (int i = tid; i < 512; i += NT) (&hist[0][0])[i] = 0;
+  if (tid == 0) {
     s_rem = K;
+    s_cnt = P;
   }
   __syncthreads();
+  kand = s_and[0];
+  kor = s_or[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) {
+    kand &= s_and[i];
+    kor |= s_or[i];
+  }
   auto key = [&](int i) -> uint32_t { return in_lds ? keys[i] : desc_key(sc[i]); };
 
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  // bits at and above hb are common to every key
+  int hb = 32 - __clz((int)(kand ^ kor));
+  uint32_t mask = (hb >= 32) ? 0u : ~((1u << hb) - 1u);
+  uint32_t prefix = kand & mask;
+  for (int pass = 0; hb > 0; ++pass) {
+    const int shift = hb > 8 ? hb - 8 : 0;
+    const uint32_t dmask = (1u << (hb - shift)) - 1u;
     int* hs = hist[pass & 1];
-    const uint32_t prefix = s_prefix, mask = s_mask;
-    for (int i = threadIdx.x; i < P; i += NT) {
+    for (int i = tid; i < P; i += NT) {
       const uint32_t k = key(i);
-      if ((k & mask) == prefix) atomicAdd(&hs[(k >> shift) & 255u], 1);
+      if ((k & mask) == prefix) atomicAdd(&hs[(k >> shift) & dmask], 1);
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
+    if (tid < 64) {
       // lane l owns bins 4l..4l+3; find the bin where the cumulative count first reaches rem
-      const int lane = threadIdx.x;
       const int h0 = hs[4 * lane], h1 = hs[4 * lane + 1], h2 = hs[4 * lane + 2], h3 = hs[4 * lane + 3];
       const int sum4 = h0 + h1 + h2 + h3;
       const int incl = wave_incl_scan(sum4);
@@ -180,8 +220,9 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
         for (int t = 0; t < 4; ++t) {
           if (acc + hv[t] >= rem) {
             s_prefix = prefix | ((uint32_t)(4 * lane + t) << shift);
-            s_mask = mask | (255u << shift);
+            s_mask = mask | (dmask << shift);
             s_rem = rem - acc;
+            s_cnt = hv[t];
             break;
           }
           acc += hv[t];
@@ -189,19 +230,35 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
       }
     } else {
       int* other = hist[(pass + 1) & 1];
-      for (int i = (int)threadIdx.x - 64; i < 256; i += NT - 64) other[i] = 0;
+      for (int i = tid - 64; i < 256; i += NT - 64) other[i] = 0;
     }
     __syncthreads();
+    prefix = s_prefix;
+    mask = s_mask;
+    hb = shift;
   }
-  const uint32_t T = s_prefix;
+  const uint32_t T = prefix;
   const int take_eq = s_rem;  // pages with key == T to keep, lowest ids first
+  const int cnt_eq = s_cnt;   // pages with key == T
 
   // contiguous ranges per thread keep page order = thread order then element order
   const int E = (P + NT - 1) / NT;
-  const int i0 = min(P, (int)threadIdx.x * E), i1 = min(P, i0 + E);
+  const int i0 = min(P, tid * E), i1 = min(P, i0 + E);
+  int total;
+  if (cnt_eq == take_eq) {
+    int keep_local = 0;
+    for (int i = i0; i < i1; ++i) keep_local += (key(i) <= T);
+    int pos = block_excl_scan<NW>(keep_local, scan_sm, &total);
+    for (int i = i0; i < i1; ++i) {
+      if (key(i) <= T) {
+        if (phys_out) phys_out[pos] = pt[i];
+        out[pos++] = i;
+      }
+    }
+    return;
+  }
   int eq_local = 0;
   for (int i = i0; i < i1; ++i) eq_local += (key(i) == T);
-  int total;
   const int eq_rank = block_excl_scan<NW>(eq_local, scan_sm, &total);
   int keep_local = 0;
   {

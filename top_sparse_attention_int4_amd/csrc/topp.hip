@@ -1,22 +1,23 @@
-// Top-p pruning by binary search of the weight threshold, and the GQA union of the kept tokens.
+// Top-p pruning by a search of the weight threshold, and the GQA union of the kept tokens.
 //
 // Paper-Notes "关键设计 / 高效Top-p": instead of sorting, search the threshold m with
 // sum_{W_i >= m} W_i >= p; each round is one parallel pass over the weights.  One 1024-thread block
 // handles one (sequence, query head); the head's weights stay in registers (E per thread).
 //
 // Weights are kept unnormalised, e_i = exp(l_i - M) in (0, 1] (the maximum is exactly 1), with the
-// target p*Z, Z = sum e_i, which keeps the same set as comparing W_i = e_i/Z with p.  Midpoints are
-// taken on the uint32 image of the non-negative float32 weights and the bracket keeps
-// f(lo) >= p*Z > f(hi); the kept set is {e_i >= lo}.  The bracket starts at [min e, 1] (all of the
-// mass lies at or above the smallest weight).  Candidates that do not exist carry e = -1.
+// target p*Z, Z = sum e_i, which keeps the same set as comparing W_i = e_i/Z with p.  The search runs
+// on the key of a weight, the uint32 image of the non-negative float32 value (order-preserving).  A
+// bisection of the key over [0, 2^31) decides one key bit per step, top bit first, keeping the
+// largest threshold whose mass{e >= T} still reaches p*Z.  Here each round decides 11 bits at once
+// from an LDS histogram of the mass per value of those bits (the outcome of 11 consecutive bisection
+// steps); rounds on bits 30..20, 19..9 and 8..0 give the exact threshold T, and the kept set
+// {e >= T} is the converged bisection's.  With fewer steps requested T keeps only its top `iters`
+// bits, where a shorter bisection stops: a superset that still reaches p.  p = 1 keeps everything.
 //
-// Two phases share that bisection.  While many weights remain inside the bracket, every step is a
-// block-wide pass with one fixed-order reduction of f(mid) and #{e >= mid}; the counts at the two
-// ends of the bracket give the number of weights inside it.  Once at most kCap weights are inside,
-// they are compacted into LDS together with the mass above the bracket, and a single wave finishes
-// the search with DPP reductions and no barriers, compacting the shrinking bracket as it goes
-// (weights leaving through the top add their mass to that constant).  Rounding order differs
-// between the phases but is fixed, so results are reproducible.
+// Masses are 64-bit fixed point, floor(e * 2^40), added with integer LDS atomics, so the decision does
+// not depend on the order of the additions; the cost is at most 2^-40 per weight (below 1e-7 of Z
+// for 65536 candidates).  Candidates that do not exist carry e = -1.  The reported threshold and kept
+// mass are float32 sums in a fixed order.
 //
 // The GQA union (paperlayer §B.2: the union over a group's query heads, read once) is a separate
 // small kernel over the head masks.
@@ -24,8 +25,6 @@
 #include "twl_internal.h"
 
 namespace twl {
-
-constexpr int kCap = 1024;  // weights handed to the single-wave phase (16 per lane)
 
 // W: weighted mode -- candidate k of unit u carries the integer multiplicity mult[u * mult_stride + k]
 // (k < mult_stride), its weight being mult * exp(l - M); the largest weight is then not 1.
@@ -36,10 +35,9 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
                                                const int32_t* __restrict__ mult, int mult_stride) {
   constexpr int NT = kToppThreads, NW = NT / 64;
   __shared__ float red[2 * NW * 4];
-  __shared__ int cnt_sm[2][NW];
-  __shared__ int scan_sm[NW + 1];
-  __shared__ float buf[kCap];
-  __shared__ uint32_t s_lo;
+  __shared__ uint64_t h1[2048], h2[2048], h3[512], cs[64];
+  __shared__ uint64_t s_rem;
+  __shared__ int s_bin, s_mode;
   BlockReduce<NW> br{red};
 
   const int bh = blockIdx.x;
@@ -55,9 +53,13 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     e[j] = (k < ncap) ? lg[k] : -__builtin_inff();
     mloc = fmaxf(mloc, e[j]);
   }
-  const float M = br.max(mloc);
-  float Z = 0.f, emin = __builtin_inff();
-  int nval_w = 0;  // wave-uniform count of existing candidates
+  for (int i = tid; i < 2048; i += NT) {
+    h1[i] = 0ull;
+    h2[i] = 0ull;
+  }
+  if (tid < 512) h3[tid] = 0ull;
+  const float M = br.max(mloc);  // its barrier also orders the clearing above
+  float Z = 0.f;
   if (M != -__builtin_inff()) {
     const int32_t* mu = W ? mult + (size_t)(bh / c.G) * mult_stride : nullptr;
 #pragma unroll
@@ -67,169 +69,99 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
         const int k = j * NT + tid;
         if (e[j] >= 0.f) e[j] = (k < mult_stride) ? (float)mu[k] * e[j] : -1.f;
       }
-      const bool ok = e[j] >= 0.f;
-      if (ok) {
-        Z += e[j];
-        emin = fminf(emin, e[j]);
-      }
-      nval_w += __popcll(__ballot(ok));
+      if (e[j] >= 0.f) Z += e[j];
     }
   } else {
 #pragma unroll
     for (int j = 0; j < E; ++j) e[j] = -1.f;
   }
-  br.sum_min(Z, emin);
-  float emax = 1.0f;  // exp(0): the largest unweighted weight
-  if (W) {
-    float x = -1.f;
-#pragma unroll
-    for (int j = 0; j < E; ++j) x = fmaxf(x, e[j]);
-    emax = br.max(x);
-  }
+  Z = br.sum(Z);
 
-  // block-wide sum of f and of a wave-uniform count, with one barrier
-  int slot = 0;
-  auto block_f_count = [&](float& f, int& cnt) {
-    f = wave_sum_dpp(f);
-    float* r = red + slot * NW * 4;
-    int* cs = cnt_sm[slot];
-    slot ^= 1;
-    if (lane == 0) {
-      r[wv] = f;
-      cs[wv] = cnt;
+  // ---- round 1: bits 30..20 ------------------------------------------------------------------------
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (e[j] >= 0.f) {
+      const uint64_t f = to_fix(e[j]);
+      if (f) atomicAdd((unsigned long long*)&h1[__float_as_uint(e[j]) >> 20], (unsigned long long)f);
+    }
+  }
+  __syncthreads();
+  auto coarse = [&](const uint64_t* h, int ncoarse) {
+    if (tid < ncoarse) {
+      uint64_t x = 0;
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) x += h[32 * tid + i];
+      cs[tid] = x;
     }
     __syncthreads();
-    float t = r[0];
-    int ct = cs[0];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) {
-      t += r[i];
-      ct += cs[i];
-    }
-    f = t;
-    cnt = ct;
   };
-  {
-    float dummy = 0.f;
-    block_f_count(dummy, nval_w);
-  }
-  const int nval = nval_w;
-
-  uint32_t lo = 0u;
-  if (Z > 0.f && p < 1.0f) {
-    const float target = p * Z;
-    lo = __float_as_uint(emin);                // f(min e) = Z >= target
-    uint32_t hi = __float_as_uint(emax) + 1u;  // every weight is <= emax
-    int n_lo = nval, n_hi = 0;                 // #{e >= lo}, #{e >= hi}
-    int it = 0;
-    // ---- block phase: one fixed-order reduction of f(mid) and #{e >= mid} per step ------------
-    while (it < iters && hi - lo > 1u && n_lo - n_hi > kCap) {
-      const uint32_t mid = lo + ((hi - lo) >> 1);
-      const float m = __uint_as_float(mid);
-      float f = 0.f;
-      int cm = 0;
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        const bool ge = e[j] >= m;
-        f += ge ? e[j] : 0.f;
-        cm += __popcll(__ballot(ge));
-      }
-      block_f_count(f, cm);
-      if (f >= target) {
-        lo = mid;
-        n_lo = cm;
-      } else {
-        hi = mid;
-        n_hi = cm;
-      }
-      ++it;
+  coarse(h1, 64);
+  if (wv == 0) {
+    const uint64_t zf = __shfl(wave_suffix_u64(cs[lane]), 0);
+    int mode = 1, bin = 0;
+    uint64_t rem = 0;
+    if (zf != 0ull && p < 1.0f) {
+      uint64_t target = (uint64_t)ceil((double)p * (double)zf);
+      target = target < 1ull ? 1ull : (target > zf ? zf : target);
+      wide_find(h1, cs, 64, target, bin, rem);
+      mode = 0;
     }
-    // ---- single-wave phase --------------------------------------------------------------------
-    if (it < iters && hi - lo > 1u) {
-      const float mlo = __uint_as_float(lo), mhi = __uint_as_float(hi);
-      int local = 0;
-      float above = 0.f;
-#pragma unroll
-      for (int j = 0; j < E; ++j) {
-        local += (e[j] >= mlo && e[j] < mhi) ? 1 : 0;
-        above += (e[j] >= mhi) ? e[j] : 0.f;
-      }
-      int total;
-      int pos = block_excl_scan<NW>(local, scan_sm, &total);
-      const float c_hi = br.sum(above);  // mass at or above the bracket
-#pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (e[j] >= mlo && e[j] < mhi) buf[pos++] = e[j];
-      __syncthreads();
-      if (wv == 0) {
-        // the bracket's weights, 16 per lane (-1 marks an empty slot)
-        float xs[kCap / 64];
-        const int nb0 = min(total, kCap);
-#pragma unroll
-        for (int i = 0; i < kCap / 64; ++i) xs[i] = (lane + 64 * i < nb0) ? buf[lane + 64 * i] : -1.f;
-        int c_lo = nb0, c_hi_n = 0;  // #{x >= lo}, #{x >= hi} among the register weights
-        bool exact = false;
-        while (it < iters && hi - lo > 1u) {
-          const uint32_t need = 32u - (uint32_t)__clz((int)(hi - lo - 1u));  // steps left to converge
-          if (c_lo - c_hi_n <= 64 && (uint32_t)(iters - it) >= need) {
-            exact = true;
-            break;
-          }
-          const uint32_t mid = lo + ((hi - lo) >> 1);
-          const float m = __uint_as_float(mid);
-          float f = 0.f;
-          int cm = 0;
-#pragma unroll
-          for (int i = 0; i < kCap / 64; ++i) {
-            const bool ge = xs[i] >= m;
-            f += ge ? xs[i] : 0.f;
-            cm += __popcll(__ballot(ge));
-          }
-          f = c_hi + wave_sum_dpp(f);
-          if (f >= target) {
-            lo = mid;
-            c_lo = cm;
-          } else {
-            hi = mid;
-            c_hi_n = cm;
-          }
-          ++it;
-        }
-        if (exact) {
-          // Finish in one step: the converged threshold is the largest weight x in the bracket with
-          // f(x) >= target, and every lane evaluates f at one of the (at most 64) bracket weights.
-          const float mlo2 = __uint_as_float(lo), mhi2 = __uint_as_float(hi);
-          float mabove = 0.f;
-          int base = 0;
-          float y = -1.f;
-#pragma unroll
-          for (int i = 0; i < kCap / 64; ++i) {
-            const bool inb = xs[i] >= mlo2 && xs[i] < mhi2;
-            mabove += (xs[i] >= mhi2) ? xs[i] : 0.f;
-            const unsigned long long bal = __ballot(inb);
-            const int r = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (inb) buf[r] = xs[i];
-            base += __popcll(bal);
-          }
-          __builtin_amdgcn_wave_barrier();
-          const int nb = base;
-          y = (lane < nb) ? buf[lane] : -1.f;
-          float fy = c_hi + wave_sum_dpp(mabove);
-          for (int i = 0; i < nb; ++i) {
-            const float yi = readlane_f(y, i);
-            fy += (yi >= y) ? yi : 0.f;
-          }
-          const float best = wave_max_dpp((lane < nb && fy >= target) ? y : -1.f);
-          if (best >= 0.f) lo = __float_as_uint(best);
-        }
-        if (lane == 0) s_lo = lo;
-      }
-      __syncthreads();
-      lo = s_lo;
+    if (lane == 0) {
+      s_mode = mode;
+      s_bin = bin;
+      s_rem = rem;
     }
   }
-  const float m = __uint_as_float(lo);
+  __syncthreads();
+  uint32_t T = 0u;
+  if (s_mode == 0) {
+    const uint32_t b1 = (uint32_t)s_bin;
+    const uint64_t rem1 = s_rem;
+    // ---- round 2: bits 19..9 inside bin b1 -------------------------------------------------------
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint32_t key = __float_as_uint(e[j]);
+      if (e[j] >= 0.f && (key >> 20) == b1) {
+        const uint64_t f = to_fix(e[j]);
+        if (f) atomicAdd((unsigned long long*)&h2[(key >> 9) & 2047u], (unsigned long long)f);
+      }
+    }
+    __syncthreads();
+    coarse(h2, 64);
+    if (wv == 0) {
+      int bin;
+      uint64_t rem;
+      wide_find(h2, cs, 64, rem1, bin, rem);
+      if (lane == 0) {
+        s_bin = bin;
+        s_rem = rem;
+      }
+    }
+    __syncthreads();
+    const uint32_t pre = (b1 << 11) | (uint32_t)s_bin;
+    const uint64_t rem2 = s_rem;
+    // ---- round 3: bits 8..0 ------------------------------------------------------------------------
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint32_t key = __float_as_uint(e[j]);
+      if (e[j] >= 0.f && (key >> 9) == pre) {
+        const uint64_t f = to_fix(e[j]);
+        if (f) atomicAdd((unsigned long long*)&h3[key & 511u], (unsigned long long)f);
+      }
+    }
+    __syncthreads();
+    coarse(h3, 16);
+    if (wv == 0) {
+      int bin;
+      uint64_t rem;
+      wide_find(h3, cs, 16, rem2, bin, rem);
+      if (lane == 0) s_bin = bin;
+    }
+    __syncthreads();
+    T = (pre << 9) | (uint32_t)s_bin;
+    if (iters < 31) T &= ~((1u << (31 - iters)) - 1u);
+  }
+  const float m = __uint_as_float(T);
   float f = 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) f += (e[j] >= m) ? e[j] : 0.f;

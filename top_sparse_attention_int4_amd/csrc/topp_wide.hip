@@ -32,41 +32,6 @@ namespace {
 constexpr int NT = kWideThreads;
 constexpr int NW = NT / 64;
 constexpr int EPT = kWideChunk / NT;  // candidates per thread
-constexpr float kFixScale = 1099511627776.0f;  // 2^40
-
-__device__ __forceinline__ uint64_t to_fix(float e) { return (uint64_t)(e * kFixScale); }
-
-__device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t y = __shfl_down(x, d);
-    if (lane + d < 64) x += y;
-  }
-  return x;
-}
-
-// Largest bin of one histogram level whose suffix mass reaches `target` (>= 1), from its coarse
-// sums (one per 32 bins) and then the 32 bins of the chosen coarse block; `rem` is the mass still
-// needed inside the bin (target minus everything above it).  Called by a whole wave.
-__device__ __forceinline__ void wide_find(const uint64_t* fine, const uint64_t* coarse, int ncoarse,
-                                          uint64_t target, int& bin, uint64_t& rem) {
-  const int lane = threadIdx.x & 63;
-  uint64_t x = (lane < ncoarse) ? coarse[lane] : 0ull;
-  x = wave_suffix_u64(x);
-  unsigned long long bal = __ballot(lane < ncoarse && x >= target);
-  const int cb = bal ? 63 - __clzll(bal) : 0;
-  const uint64_t above = (cb < 63) ? __shfl(x, cb + 1) : 0ull;
-  const uint64_t r1 = target - above;
-  uint64_t y = (lane < 32) ? fine[32 * cb + lane] : 0ull;
-  y = wave_suffix_u64(y);
-  bal = __ballot(lane < 32 && y >= r1);
-  const int fb = bal ? 63 - __clzll(bal) : 0;
-  const uint64_t above2 = __shfl(y, fb + 1);  // lanes >= 32 hold 0
-  bin = 32 * cb + fb;
-  rem = r1 - above2;
-}
-
 __device__ __forceinline__ void flush_hist(const uint64_t* h, int nbins, uint64_t* g_fine, uint64_t* g_coarse) {
   for (int i = threadIdx.x; i < nbins; i += NT)
     if (h[i]) atomicAdd((unsigned long long*)&g_fine[i], (unsigned long long)h[i]);
@@ -88,14 +53,14 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist1(float* __restrict__
   BlockReduce<NW> br{red};
   const int nch = ncap / kWideChunk;
   const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
+  float* lg = logits + (size_t)bh * ncap + (size_t)ch * kWideChunk;
+  float v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) v[j] = lg[j * NT + threadIdx.x];  // in flight while M is formed
   for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
   float m = -__builtin_inff();
   for (int i = threadIdx.x; i < npm; i += NT) m = fmaxf(m, pmax[(size_t)bh * npm + i]);
   const float M = br.max(m);  // (its barrier also orders the clearing of h)
-  float* lg = logits + (size_t)bh * ncap + (size_t)ch * kWideChunk;
-  float v[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) v[j] = lg[j * NT + threadIdx.x];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const float e = (v[j] == -__builtin_inff() || M == -__builtin_inff()) ? -1.f : exp_diff(v[j], M);
@@ -138,6 +103,10 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __rest
   const int nch = ncap / kWideChunk;
   const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
   uint64_t* st = state + (size_t)bh * kWideStateWords;
+  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
+  float v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];  // in flight during the resolution
   for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
   if (threadIdx.x < 64) {
     int mode, b1;
@@ -157,10 +126,6 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __rest
   __syncthreads();
   if (s_mode != 0) return;
   const uint32_t b1 = (uint32_t)s_b1;
-  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
-  float v[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const uint32_t key = __float_as_uint(v[j]);
@@ -180,6 +145,10 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist3(const float* __rest
   const int nch = ncap / kWideChunk;
   const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
   uint64_t* st = state + (size_t)bh * kWideStateWords;
+  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
+  float v[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];  // in flight during the resolution
   if (st[kWideSMode] != 0ull) return;  // uniform over the head's blocks
   for (int i = threadIdx.x; i < 512; i += NT) h[i] = 0ull;
   const uint32_t b1 = (uint32_t)st[kWideSB1];
@@ -197,10 +166,6 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist3(const float* __rest
   }
   __syncthreads();
   const uint32_t pre = (b1 << 11) | (uint32_t)s_b2;
-  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
-  float v[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const uint32_t key = __float_as_uint(v[j]);

@@ -234,4 +234,41 @@ __device__ __forceinline__ float exp_diff(float a, float b) {
 // Clamp helpers
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// ---- radix form of the top-p threshold search (shared by the block and the multi-block kernels) ----
+// Masses are 64-bit fixed point, floor(w * 2^40): exact integer sums in any order.
+constexpr float kFixScale = 1099511627776.0f;  // 2^40
+
+__device__ __forceinline__ uint64_t to_fix(float e) { return (uint64_t)(e * kFixScale); }
+
+__device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t y = __shfl_down(x, d);
+    if (lane + d < 64) x += y;
+  }
+  return x;
+}
+
+// Largest bin of one histogram level whose suffix mass reaches `target` (>= 1), from its coarse
+// sums (one per 32 bins) and then the 32 bins of the chosen coarse block; `rem` is the mass still
+// needed inside the bin (target minus everything above it).  Called by a whole wave.
+__device__ __forceinline__ void wide_find(const uint64_t* fine, const uint64_t* coarse, int ncoarse,
+                                          uint64_t target, int& bin, uint64_t& rem) {
+  const int lane = threadIdx.x & 63;
+  uint64_t x = (lane < ncoarse) ? coarse[lane] : 0ull;
+  x = wave_suffix_u64(x);
+  unsigned long long bal = __ballot(lane < ncoarse && x >= target);
+  const int cb = bal ? 63 - __clzll(bal) : 0;
+  const uint64_t above = (cb < 63) ? __shfl(x, cb + 1) : 0ull;
+  const uint64_t r1 = target - above;
+  uint64_t y = (lane < 32) ? fine[32 * cb + lane] : 0ull;
+  y = wave_suffix_u64(y);
+  bal = __ballot(lane < 32 && y >= r1);
+  const int fb = bal ? 63 - __clzll(bal) : 0;
+  const uint64_t above2 = __shfl(y, fb + 1);  // lanes >= 32 hold 0
+  bin = 32 * cb + fb;
+  rem = r1 - above2;
+}
+
 }  // namespace twl

@@ -61,6 +61,7 @@ struct ListView {
   const int32_t* indptr;  // [U+1] when CSR, else nullptr
   const int32_t* counts;  // [U] when padded, else nullptr
   int64_t stride;         // row stride when padded
+  int64_t cap;            // CSR: entries the tokens/rows arrays hold (0 when padded)
 };
 
 // ---- launchers (each returns the launch status) --------------------------------------------------
@@ -96,9 +97,12 @@ int attn_chunk_tokens(int64_t total_upper);
 hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
                        int64_t max_chunks, float* partials, int32_t* csr_indptr, int32_t* csr_tokens,
                        int64_t capacity, hipStream_t s);
+// K/V rows of a CSR token list (into `rows`, same indexing), entries at or past `capacity` skipped
+hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,
+                       int64_t capacity, hipStream_t s);
 hipError_t launch_merge(const CacheView& c, const ListView& list, int chunk_tokens, int64_t max_chunks,
                         const float* partials, float* out, float* lse, hipStream_t s);
-constexpr int kPartFloats = 2 + kD;  // per (chunk, head): max, sum, output row
+constexpr int kPartFloats = 4 + kD;  // per (chunk, head): max, sum, 2 pad, output row (16-byte aligned)
 // elements per thread of the top-p block for a candidate capacity (0 = unsupported)
 int topp_elems_per_thread(int64_t ncap);
 constexpr int kToppThreads = 1024;
