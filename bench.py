@@ -120,18 +120,21 @@ def main():
     indptrs = [torch.zeros(U + 1, dtype=torch.int32, device=dev) for _ in range(L)]
     toks = torch.empty(U * maxcand, dtype=torch.int32, device=dev)
 
-    def step(i, events=None):
+    def step(i, events=None, lists=False):
+        # the timed step returns out, lse and the thresholds; the compacted kept-token list is an
+        # optional output, requested once per layer outside the timed region for the byte count
         _, cache, t = layers[i % L]
+        ip, tk = (indptrs[i % L], toks) if lists else (None, None)
         if clusters:
             twl.decode_clusters(cache, t["q"], p=p, p1=w.p1, centroids=t["centroids"], csize=t["csize"],
-                                coff=t["coff"], out=out, lse=lse, threshold=thr, sel_indptr=indptrs[i % L],
-                                sel_tokens=toks, ws=ws, events=events)
+                                coff=t["coff"], out=out, lse=lse, threshold=thr, sel_indptr=ip, sel_tokens=tk,
+                                ws=ws, events=events)
         elif events is not None:
             twl.decode_profiled(cache, t["q"], events, p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
-                                sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
+                                sel_indptr=ip, sel_tokens=tk, ws=ws)
         else:
-            twl.decode(cache, t["q"], p=p, keep_frac=kf, out=out, lse=lse, threshold=thr,
-                       sel_indptr=indptrs[i % L], sel_tokens=toks, ws=ws)
+            twl.decode(cache, t["q"], p=p, keep_frac=kf, out=out, lse=lse, threshold=thr, sel_indptr=ip,
+                       sel_tokens=tk, ws=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -155,6 +158,9 @@ def main():
     torch.cuda.synchronize()
     for i in range(K2):
         step(i, evs[i])
+    torch.cuda.synchronize()
+    for li in range(L):
+        step(li, lists=True)
     torch.cuda.synchronize()
     for i in range(K2):
         for s in range(twl.NUM_STAGES):

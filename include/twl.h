@@ -25,8 +25,9 @@
  *   {1, 2, 4, 8}, or a current device that is not gfx950.  TWL_EHIP: a kernel launch failed (the
  *   HIP error is left for hipGetLastError()).  Device faults surface at the caller's next
  *   synchronisation.
- * - Results are deterministic: the same inputs give bitwise identical outputs on every run, and the
- *   fused entry point gives bitwise the same outputs as the split entry points.
+ * - Results are deterministic: the same inputs give bitwise identical outputs on every run.  The
+ *   fused entry points select bitwise the same pages, top-p sets and thresholds as the split entry
+ *   points; their attention outputs agree to float32 rounding (the work is partitioned differently).
  *
  * Data layout of the paged cache (B = batch, Hq/Hkv = query/KV heads, G = Hq/Hkv)
  * ------------------------------------------------------------------------------
@@ -176,9 +177,12 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
                            void* ws, size_t ws_bytes, void* stream);
 
 /* The whole decode step for one layer: twl_select_pages (skipped when keep_frac >= 1), then
- * twl_estimate_topp over the kept pages, then twl_sparse_attn over the union -- the same kernels,
- * so the outputs are bitwise those of the split calls.  threshold, lse, sel_indptr and sel_tokens
- * may be NULL (sel_indptr and sel_tokens together); capacity is ignored when they are NULL. */
+ * twl_estimate_topp over the kept pages, then the sparse attention over the union.  Pages, top-p
+ * sets and thresholds are bitwise those of the split calls; the attention reads the top-p bitmaps
+ * directly (chunks of the candidate index space), so its outputs agree with twl_sparse_attn on the
+ * same kept list to float32 rounding.  threshold, lse, sel_indptr and sel_tokens may be NULL
+ * (sel_indptr and sel_tokens together; the kept list is then not compacted at all); capacity is
+ * ignored when they are NULL. */
 twl_status twl_decode(const twl_cache* cache, const void* q, const twl_decode_params* params, float* out,
                       float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
                       void* ws, size_t ws_bytes, void* stream);

@@ -174,8 +174,9 @@ def test_decode_clusters_fused_equals_split():
     n = int(a["indptr"][-1])
     assert np.array_equal(toks.cpu().numpy()[:n], a["tokens"][:n])
     assert np.array_equal(thr.cpu().numpy(), a["thr"])
-    assert np.array_equal(out.cpu().numpy(), a["out"])
-    assert np.array_equal(lse.cpu().numpy(), a["lse"])
+    # same kept sets, attention partitioned differently: float32 sums agree to rounding
+    assert np.allclose(out.cpu().numpy(), a["out"], rtol=1e-5, atol=1e-5)
+    assert np.allclose(lse.cpu().numpy(), a["lse"], rtol=1e-5, atol=1e-5)
 
 
 # ---- top-p above 65536 candidates per head ------------------------------------------------------------

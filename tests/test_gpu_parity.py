@@ -362,9 +362,14 @@ def test_fused_equals_split_and_is_deterministic():
     twl.sparse_attn(cache, t["q"], SM, torch.from_numpy(e["indptr"]).cuda(),
                     torch.from_numpy(e["tokens"][:max(n, 1)]).cuda(), maxcand, out, lse, ws)
     torch.cuda.synchronize()
-    assert np.array_equal(out.cpu().numpy(), a["out"])
-    assert np.array_equal(lse.cpu().numpy(), a["lse"])
+    # same kept sets; the attention partitions the work differently (candidate-space chunks in the
+    # fused call, list chunks in the split one), so the float32 sums agree to rounding
+    assert np.allclose(out.cpu().numpy(), a["out"], rtol=1e-5, atol=1e-5)
+    assert np.allclose(lse.cpu().numpy(), a["lse"], rtol=1e-5, atol=1e-5)
     _ = maxsel
+    # the fused call without the optional kept-list output computes the same attention
+    g = run_decode(w, cache, t, with_lists=False)
+    assert np.array_equal(g["out"], a["out"]) and np.array_equal(g["lse"], a["lse"]) and np.array_equal(g["thr"], a["thr"])
 
 
 @pytest.mark.parametrize("G", [1, 2, 8])

@@ -90,6 +90,7 @@ CacheView make_view(const twl_cache* c) {
 struct Layout {
   int64_t ncap = 0;       // candidate capacity per unit (multiple of 1024)
   int chunk_tokens = 64;  // attention chunk
+  int slots = 1;          // attention chunk slots per unit (ceil(ncap / chunk_tokens))
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
          ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
@@ -113,8 +114,9 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   const int G = c->num_q_heads / c->num_kv_heads;
   L->ncap = ncap;
   L->chunk_tokens = attn_chunk_tokens(U * ncap);
-  L->max_chunks = U * ((ncap + L->chunk_tokens - 1) / L->chunk_tokens);
-  if (L->max_chunks < 1) L->max_chunks = 1;
+  L->slots = (int)((ncap + L->chunk_tokens - 1) / L->chunk_tokens);
+  if (L->slots < 1) L->slots = 1;
+  L->max_chunks = U * L->slots;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -168,14 +170,21 @@ struct Events {
 
 twl_status hip_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_EHIP; }
 
+#define TWL_TRY(expr)                          \
+  do {                                         \
+    const hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return TWL_EHIP;     \
+  } while (0)
+
 WideWs wide_of(void* ws, const Layout& L) {
   return WideWs{at<float>(ws, L.pmax), at<uint64_t>(ws, L.wstate), at<int32_t>(ws, L.wcnt), at<uint32_t>(ws, L.uwords)};
 }
 
-// Estimate, top-p and union of every unit (the narrow or the wide top-p by candidate capacity).
+// Estimate, top-p and (when `with_union`) the compacted GQA union of every unit, the narrow or the
+// wide top-p by candidate capacity.  Events 4/5 bracket the estimate, 6/7 the rest.
 hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, void* ws,
                          const Layout& L, float p, int iters, float* thr, float* mass, uint32_t* head_mask,
-                         int mask_words, const Events& E, hipStream_t s) {
+                         int mask_words, bool with_union, const Events& E, hipStream_t s) {
   const int ncap = (int)L.ncap;
   const WideWs wd = wide_of(ws, L);
   const bool wide = is_wide(L.ncap);
@@ -186,23 +195,42 @@ hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const 
   if (e != hipSuccess) return e;
   if ((e = E.rec(5)) != hipSuccess) return e;
   if ((e = E.rec(6)) != hipSuccess) return e;
-  if (wide)
-    e = launch_topp_wide(c, wd, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), ncap, p,
-                         iters, thr, mass, head_mask, mask_words, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow),
-                         at<int32_t>(ws, L.ucnt), s);
-  else
-    e = launch_topp(c, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), at<float>(ws, L.logits), ncap, p, iters, thr,
-                    mass, at<uint32_t>(ws, L.masks), head_mask, mask_words, at<int32_t>(ws, L.utok),
-                    at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s);
+  if (wide) {
+    e = launch_topp_wide(c, wd, at<float>(ws, L.logits), ncap, p, iters, thr, head_mask, mask_words, s);
+    if (e == hipSuccess && (with_union || mass))
+      e = launch_wide_emit(c, wd, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), ncap, at<int32_t>(ws, L.utok),
+                           at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), mass, s);
+  } else {
+    e = launch_topp(c, at<float>(ws, L.logits), ncap, p, iters, thr, mass, at<uint32_t>(ws, L.masks), head_mask,
+                    mask_words, s);
+    if (e == hipSuccess && with_union)
+      e = launch_union(c, at<uint32_t>(ws, L.masks), at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), ncap,
+                       at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s);
+  }
   if (e != hipSuccess) return e;
   return E.rec(7);
 }
 
-#define TWL_TRY(expr)                          \
-  do {                                         \
-    const hipError_t e_ = (expr);              \
-    if (e_ != hipSuccess) return TWL_EHIP;     \
-  } while (0)
+// Attention over the top-p bitmaps (no compacted list needed) and the merge; events 8..11.
+hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, void* ws, const Layout& L, float* out,
+                         float* lse, const Events& E, hipStream_t s) {
+  const bool wide = is_wide(L.ncap);
+  MaskView mv{};
+  if (wide) {
+    mv.union_words = at<uint32_t>(ws, L.uwords);
+  } else {
+    mv.head_masks = at<uint32_t>(ws, L.masks);
+  }
+  mv.cand_row = at<int32_t>(ws, L.crow);
+  mv.ncap = L.ncap;
+  hipError_t e;
+  if ((e = E.rec(8)) != hipSuccess) return e;
+  if ((e = launch_attn_masked(c, q, sm, mv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), s)) != hipSuccess) return e;
+  if ((e = E.rec(9)) != hipSuccess) return e;
+  if ((e = E.rec(10)) != hipSuccess) return e;
+  if ((e = launch_merge(c, nullptr, L.chunk_tokens, L.slots, at<float>(ws, L.parts), out, lse, s)) != hipSuccess) return e;
+  return E.rec(11);
+}
 
 twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_params* prm, float* out,
                        float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
@@ -258,15 +286,12 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
     cand.mode = kCandAll;
   }
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
-  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, E, s));
-  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap, 0};
-  TWL_TRY(E.rec(8));
-  TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
-                      sel_tokens, capacity, s));
-  TWL_TRY(E.rec(9));
-  TWL_TRY(E.rec(10));
-  TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));
-  TWL_TRY(E.rec(11));
+  const bool csr = sel_tokens != nullptr;
+  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s));
+  if (csr)
+    TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
+                            capacity, s));
+  TWL_TRY(attend_masked(c, qb, prm->sm_scale, ws, L, out, lse, E, s));
   return TWL_OK;
 }
 
@@ -325,15 +350,12 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   TWL_TRY(launch_range_prefix(c, cand, at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
   TWL_TRY(E.rec(3));
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
-  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, E, s));
-  ListView lv{at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), nullptr, at<int32_t>(ws, L.ucnt), ncap, 0};
-  TWL_TRY(E.rec(8));
-  TWL_TRY(launch_attn(c, qb, prm->sm_scale, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), sel_indptr,
-                      sel_tokens, capacity, s));
-  TWL_TRY(E.rec(9));
-  TWL_TRY(E.rec(10));
-  TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));
-  TWL_TRY(E.rec(11));
+  const bool csr = sel_tokens != nullptr;
+  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s));
+  if (csr)
+    TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
+                            capacity, s));
+  TWL_TRY(attend_masked(c, qb, prm->sm_scale, ws, L, out, lse, E, s));
   return TWL_OK;
 }
 
@@ -434,7 +456,7 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
     TWL_TRY(launch_range_prefix(c, cv, at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
   }
   TWL_TRY(estimate_topp(c, static_cast<const uint16_t*>(q), sm_scale, cv, ws, L, p, iters, threshold, mass, head_mask,
-                        mask_words, Events{}, s));
+                        mask_words, true, Events{}, s));
   TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
                           capacity, s));
   return TWL_OK;
@@ -461,9 +483,9 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
   const int64_t U = (int64_t)cache->batch * cache->num_kv_heads;
   TWL_TRY(launch_rows(c, sel_indptr, sel_tokens, at<int32_t>(ws, L.urow), U * ncap, s));
   ListView lv{sel_tokens, at<int32_t>(ws, L.urow), sel_indptr, nullptr, 0, U * ncap};
-  TWL_TRY(launch_attn(c, static_cast<const uint16_t*>(q), sm_scale, lv, L.chunk_tokens, L.max_chunks,
-                      at<float>(ws, L.parts), nullptr, nullptr, 0, s));
-  TWL_TRY(launch_merge(c, lv, L.chunk_tokens, L.max_chunks, at<float>(ws, L.parts), out, lse, s));
+  TWL_TRY(launch_attn(c, static_cast<const uint16_t*>(q), sm_scale, lv, L.chunk_tokens, L.slots,
+                      at<float>(ws, L.parts), s));
+  TWL_TRY(launch_merge(c, &lv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), out, lse, s));
   return TWL_OK;
 }
 

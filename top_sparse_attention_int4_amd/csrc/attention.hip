@@ -40,44 +40,18 @@ __device__ __forceinline__ const int32_t* list_rows(const ListView& L, int u) {
   return L.indptr ? (L.rows + L.indptr[u]) : (L.rows + (size_t)u * L.stride);
 }
 
-// Find the unit owning flattened chunk `cid`: returns u, and its first chunk id and token offset.
-// Executed by a whole wave; every lane gets the same answer.  Returns -1 when cid >= total.
-__device__ int find_unit(const ListView& L, int U, int CH, int cid, int* chunk0, int* tok0) {
-  const int lane = threadIdx.x & 63;
-  int cbase = 0, tbase = 0;
-  for (int base = 0; base < U; base += 64) {
-    const int u = base + lane;
-    const int cnt = (u < U) ? max(0, list_count(L, u)) : 0;
-    const int nch = (cnt + CH - 1) / CH;
-    const int cinc = wave_incl_scan(nch);
-    const int tinc = wave_incl_scan(cnt);
-    const int cex = cbase + cinc - nch;
-    const bool mine = (u < U) && nch > 0 && cid >= cex && cid < cex + nch;
-    const unsigned long long bal = __ballot(mine);
-    if (bal) {
-      const int src = __ffsll((long long)bal) - 1;
-      *chunk0 = __shfl(cex, src);
-      *tok0 = __shfl(tbase + tinc - cnt, src);
-      return base + src;
-    }
-    cbase += __shfl(cinc, 63);
-    tbase += __shfl(tinc, 63);
-  }
-  return -1;
-}
-
 constexpr int kAttnWaves = 4;
 constexpr int kAttnSB = 16;  // tokens per sub-block
 
 // NSB: sub-blocks per wave (chunk = 4 waves x NSB x 16 tokens); the sequence is fully unrolled so
 // the count of loads in flight is known at every wait.
-template <int G, int NSB>
+// MK: the chunk is a range of the candidate index space whose kept entries come from bitmaps (each
+// wave compacts its kept candidates' rows in LDS first); otherwise it is a range of a token list.
+template <int G, int NSB, bool MK>
 __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uint16_t* __restrict__ q,
-                                                          float sm_log2, ListView L, int max_chunks,
-                                                          float* __restrict__ partials, int32_t* csr_indptr,
-                                                          int32_t* csr_tokens, int64_t capacity) {
-  constexpr int NWV = kAttnWaves, SB = kAttnSB, VS = SB / 4, CH = NWV * NSB * SB;
-  const int U = c.B * c.Hkv;
+                                                          float sm_log2, ListView L, MaskView MV, int slots,
+                                                          float* __restrict__ partials) {
+  constexpr int NWV = kAttnWaves, SB = kAttnSB, VS = SB / 4, CH = NWV * NSB * SB, QL = CH / NWV;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nn = lane & 15, grp = lane >> 4;
@@ -85,47 +59,75 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
   __shared__ float Al[NWV][G];
   __shared__ float sm_m[NWV][G], sm_l[NWV][G];
   __shared__ float4 so[NWV][G][32];
-  __shared__ int s_u, s_c0, s_t0;
+  __shared__ int cr[MK ? NWV : 1][MK ? QL : 1];
 
-  const int cid = blockIdx.x;
-  if (csr_indptr && cid == 0 && wv == 0) {
-    int tbase = 0;
-    for (int base = 0; base < U; base += 64) {
-      const int u = base + lane;
-      const int cnt = (u < U) ? max(0, list_count(L, u)) : 0;
-      const int tinc = wave_incl_scan(cnt);
-      if (u < U) csr_indptr[u] = tbase + tinc - cnt;
-      tbase += __shfl(tinc, 63);
-    }
-    if (lane == 0) csr_indptr[U] = tbase;
-  }
-  if (wv == 0) {
-    int chunk0 = 0, tok0 = 0;
-    const int u = find_unit(L, U, CH, cid, &chunk0, &tok0);
-    if (lane == 0) {
-      s_u = u;
-      s_c0 = chunk0;
-      s_t0 = tok0;
-    }
-  }
-  __syncthreads();
-  const int u = __builtin_amdgcn_readfirstlane(s_u);
-  if (u < 0) return;  // past the last chunk of the last unit
-  const int chunk0 = __builtin_amdgcn_readfirstlane(s_c0), tok0 = __builtin_amdgcn_readfirstlane(s_t0);
+  // chunk slot k of unit u (the unit's chunks are its first ceil(count / CH) slots)
+  const int u = blockIdx.x / slots, k = blockIdx.x - u * slots;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  int cnt = __builtin_amdgcn_readfirstlane(max(0, list_count(L, u)));
-  if (L.indptr) {  // a CSR list that breaks its declared bound is cut at the arrays' end
-    const int64_t a = __builtin_amdgcn_readfirstlane(L.indptr[u]);
-    cnt = (a < 0 || a >= L.cap) ? 0 : (int)min((int64_t)cnt, L.cap - a);
+  const int t_begin = k * CH;
+  const int w_begin = t_begin + wv * QL;
+  int rows[NSB];
+  int w_end;
+  if constexpr (MK) {
+    // the quarter's candidate rows and kept bits (one round trip with q), then the kept rows compacted
+    const int64_t ub = (int64_t)u * MV.ncap;
+    const int mw = (int)(MV.ncap >> 5);
+    int crw[NSB];
+    uint32_t wd[NSB];
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) {
+      const int cidx = w_begin + i * SB + (lane & 15);
+      crw[i] = MV.cand_row[ub + cidx];
+      const int wi = cidx >> 5;
+      if (MV.union_words) {
+        wd[i] = MV.union_words[(int64_t)u * mw + wi];
+      } else {
+        uint32_t x = 0u;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) x |= MV.head_masks[((int64_t)b * c.Hq + h * G + hh) * mw + wi];
+        wd[i] = x;
+      }
+    }
+    int kept = 0;
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) {
+      const int cidx = w_begin + i * SB + (lane & 15);
+      const bool f = lane < SB && ((wd[i] >> (cidx & 31)) & 1u);
+      const unsigned long long bal = __ballot(f);
+      const int pos = kept + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (f) cr[wv][pos] = crw[i];
+      kept += __popcll(bal);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int kl = kept > 0 ? kept - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) rows[i] = cr[wv][min(i * SB + (lane & 15), kl)];
+    w_end = kept;
+  } else {
+    // The rows of this wave's quarter are read together with the count and q (one round trip).
+    // Entries past the count may hold anything: a row is used as an address only after a range
+    // check, and whether it counts is decided from its index.
+    const int32_t* rws;
+    int lim;
+    if (L.indptr) {
+      const int64_t a = __builtin_amdgcn_readfirstlane(L.indptr[u]);
+      const bool ok = a >= 0 && a < L.cap;
+      rws = L.rows + (ok ? a : 0);
+      lim = ok ? (int)min(L.cap - a, (int64_t)1 << 30) - 1 : -1;
+    } else {
+      rws = L.rows + (size_t)u * L.stride;
+      lim = (int)L.stride - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) rows[i] = (lim >= 0) ? rws[min(w_begin + i * SB + lane, lim)] : -1;
+    int cnt = __builtin_amdgcn_readfirstlane(max(0, list_count(L, u)));
+    cnt = min(cnt, lim + 1);  // a CSR list that breaks its declared bound is cut at the arrays' end
+    if (t_begin >= cnt) return;  // an unused slot
+    const int t_end = min(cnt, t_begin + CH);
+    w_end = min(t_end, w_begin + QL);
   }
-  const int32_t* toks = list_ptr(L, u);
-  const int32_t* rws = list_rows(L, u);
-  const int t_begin = (cid - chunk0) * CH;
-  const int t_end = max(t_begin, min(cnt, t_begin + CH));
-  const int t_last = max(t_end - 1, t_begin);
-  const int qlen = CH / NWV;
-  const int w_begin = t_begin + wv * qlen, w_end = min(t_end, w_begin + qlen);
-
   // B operand: q of head nn (zero for padding columns), dims 32kb + 8grp .. +7
   bf16x8_t qv[4];
 #pragma unroll
@@ -136,6 +138,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
       qv[kb] = bf16x8_t{};
     }
   }
+  const int w_first = MK ? 0 : w_begin;  // list index of the first entry of sub-block 0
+  const int nrows = c.nphys * c.Hkv * kPage;
   float m_run = -__builtin_inff(), l_run = 0.f;
   float acc[G][8];
 #pragma unroll
@@ -143,10 +147,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[hh][i] = 0.f;
 
-  // a real row of the chunk for every index (validity is decided from the index at use)
-  auto row_ld = [&](int idx) -> int { return rws[min(idx, t_last)]; };
   auto issue = [&](int row, bf16x8_t (&kv)[4], uint4 (&vv)[VS]) {
-    const int rs = max(row, 0);
+    const int rs = ((unsigned)row < (unsigned)nrows) ? row : 0;
     const int r = __shfl(rs, nn);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -224,19 +226,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  if (t_end > t_begin) {
-    // every row of the wave's quarter first, then the data of sub-block i + 1 in flight while
-    // sub-block i is computed; sub-blocks past the list read real rows and are masked
-    int rows[NSB];
-#pragma unroll
-    for (int i = 0; i < NSB; ++i) rows[i] = row_ld(w_begin + i * SB + lane);
+  if (w_end > w_first) {
+    // the data of sub-block i + 1 in flight while sub-block i is computed; sub-blocks past the list
+    // read in-range rows and are masked
     bf16x8_t kv[2][4];
     uint4 vv[2][VS];
     issue(rows[0], kv[0], vv[0]);
 #pragma unroll
     for (int i = 0; i < NSB; ++i) {
       if (i + 1 < NSB) issue(rows[i + 1], kv[(i + 1) & 1], vv[(i + 1) & 1]);
-      consume(w_begin + i * SB, rows[i], kv[i & 1], vv[i & 1]);
+      consume(w_first + i * SB, rows[i], kv[i & 1], vv[i & 1]);
     }
   }
 
@@ -262,7 +261,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     }
   }
   __syncthreads();
-  float* part = partials + (size_t)cid * G * kPartStride;
+  float* part = partials + (size_t)blockIdx.x * G * kPartStride;
   for (int t = tid; t < G * 32; t += 64 * NWV) {
     const int hh = t >> 5, d4 = t & 31;
     float M = -__builtin_inff();
@@ -290,20 +289,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
       part[hh * kPartStride + 1] = l;
     }
   }
-  if (csr_tokens) {
-    // all loads of the chunk's token ids in flight before their stores (CH <= 512)
-    int tk[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = t_begin + 256 * r + tid;
-      tk[r] = (i < t_end) ? toks[i] : 0;
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = t_begin + 256 * r + tid;
-      if (i < t_end && tok0 + i < capacity) csr_tokens[tok0 + i] = tk[r];
-    }
-  }
 }
 
 // K/V row of every entry of a CSR token list (-1 for ids outside the sequence), so the attention's
@@ -327,28 +312,18 @@ __global__ __launch_bounds__(256) void k_rows(CacheView c, const int32_t* __rest
 // One block per (unit, head): the unit's chunk partials are merged by 32 rows of 32 threads, row r
 // taking chunks r, r + 32, ... in order with a running maximum and thread j owning dims 4j..4j+3
 // (four chunks' loads in flight per thread); the 32 row results are then combined in row order.
+// With a token list the unit has ceil(count / CH) chunks; without one every slot holds a partial.
 template <int G>
-__global__ __launch_bounds__(1024) void k_merge(CacheView c, ListView L, int CH, int max_chunks,
+__global__ __launch_bounds__(1024) void k_merge(CacheView c, ListView L, bool use_list, int CH, int slots,
                                                 const float* __restrict__ partials, float* out, float* lse) {
   constexpr int NR = 32, UNR = 4;
   const int u = blockIdx.x / G, hh = blockIdx.x - (blockIdx.x / G) * G;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int tid = threadIdx.x, r = tid >> 5, j = tid & 31;
-  __shared__ int s_c0, s_nch;
   __shared__ float sM[NR], sL[NR];
   __shared__ float4 sO[NR][32];
-  if (tid < 64) {
-    int acc = 0;
-    for (int i = tid; i < u; i += 64) acc += (max(0, list_count(L, i)) + CH - 1) / CH;
-    acc = wave_sum_int(acc);
-    if (tid == 0) {
-      s_c0 = acc;
-      s_nch = (max(0, list_count(L, u)) + CH - 1) / CH;
-    }
-  }
-  __syncthreads();
-  const int c0 = s_c0;
-  const int nch = max(0, min(s_nch, max_chunks - c0));
+  const int nch = use_list ? min((max(0, list_count(L, u)) + CH - 1) / CH, slots) : slots;
+  const int c0 = u * slots;
   const float* base = partials + ((size_t)c0 * G + hh) * kPartStride;
   constexpr size_t kStep = (size_t)G * kPartStride;
   float M = -__builtin_inff(), Ls = 0.f;
@@ -415,17 +390,15 @@ int attn_chunk_tokens(int64_t total_upper) {
   return 64 * s;
 }
 
-hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
-                       int64_t max_chunks, float* partials, int32_t* csr_indptr, int32_t* csr_tokens,
-                       int64_t capacity, hipStream_t s) {
-  if (!list.rows) return hipErrorInvalidValue;
+template <bool MK>
+static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float sm, const ListView& list,
+                                   const MaskView& mv, int chunk_tokens, int slots, float* partials, hipStream_t s) {
+  if (slots < 1) return hipErrorInvalidValue;
   const float sm_log2 = sm * 1.44269504088896340736f;
-  const int64_t grid = max_chunks < 1 ? 1 : max_chunks;
-  const dim3 blk(64 * kAttnWaves);
-#define TWL_ATTN_G(GG, NS)                                                                                    \
-  case GG:                                                                                                    \
-    hipLaunchKernelGGL((k_attn<GG, NS>), dim3((unsigned)grid), blk, 0, s, c, q, sm_log2, list, (int)max_chunks, \
-                       partials, csr_indptr, csr_tokens, capacity);                                          \
+  const dim3 grid((unsigned)((int64_t)c.B * c.Hkv * slots)), blk(64 * kAttnWaves);
+#define TWL_ATTN_G(GG, NS)                                                                                  \
+  case GG:                                                                                                  \
+    hipLaunchKernelGGL((k_attn<GG, NS, MK>), grid, blk, 0, s, c, q, sm_log2, list, mv, slots, partials);   \
     break;
 #define TWL_ATTN_NSB(NS)                   \
   case NS * kAttnWaves * kAttnSB:          \
@@ -449,22 +422,42 @@ hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const Li
   return hipGetLastError();
 }
 
+hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
+                       int slots, float* partials, hipStream_t s) {
+  if (!list.rows) return hipErrorInvalidValue;
+  return launch_attn_impl<false>(c, q, sm, list, MaskView{}, chunk_tokens, slots, partials, s);
+}
+
+hipError_t launch_attn_masked(const CacheView& c, const uint16_t* q, float sm, const MaskView& mv, int chunk_tokens,
+                              int slots, float* partials, hipStream_t s) {
+  if (!mv.cand_row || (!mv.head_masks && !mv.union_words) || mv.ncap % chunk_tokens) return hipErrorInvalidValue;
+  return launch_attn_impl<true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, s);
+}
+
 hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,
                        int64_t capacity, hipStream_t s) {
   hipLaunchKernelGGL(k_rows, dim3(16, (unsigned)(c.B * c.Hkv)), dim3(256), 0, s, c, indptr, tokens, rows, capacity);
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const CacheView& c, const ListView& list, int chunk_tokens, int64_t max_chunks,
-                        const float* partials, float* out, float* lse, hipStream_t s) {
+hipError_t launch_merge(const CacheView& c, const ListView* list, int chunk_tokens, int slots, const float* partials,
+                        float* out, float* lse, hipStream_t s) {
   dim3 grid((unsigned)(c.B * c.Hkv * c.G));
+  const ListView lv = list ? *list : ListView{};
+  const bool use_list = list != nullptr;
+#define TWL_MERGE_CASE(GG)                                                                                   \
+  case GG:                                                                                                   \
+    hipLaunchKernelGGL(k_merge<GG>, grid, dim3(1024), 0, s, c, lv, use_list, chunk_tokens, slots, partials,  \
+                       out, lse);                                                                           \
+    break;
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_merge<1>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 2: hipLaunchKernelGGL(k_merge<2>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 4: hipLaunchKernelGGL(k_merge<4>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
-    case 8: hipLaunchKernelGGL(k_merge<8>, grid, dim3(1024), 0, s, c, list, chunk_tokens, (int)max_chunks, partials, out, lse); break;
+    TWL_MERGE_CASE(1)
+    TWL_MERGE_CASE(2)
+    TWL_MERGE_CASE(4)
+    TWL_MERGE_CASE(8)
     default: return hipErrorInvalidValue;
   }
+#undef TWL_MERGE_CASE
   return hipGetLastError();
 }
 

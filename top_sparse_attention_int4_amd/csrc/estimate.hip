@@ -36,43 +36,87 @@ __device__ __forceinline__ int cand_token(const CandView& cand, int u, int k, in
 
 // Prefix sums of range lengths per unit (lengths < 0 count as 0), and for every block of kEstCands
 // candidates the index of the range holding its first candidate (count when past the last one).
-// Each thread takes 4 consecutive ranges per pass (loads in flight together), 4096 ranges a pass.
+// Up to 4096 ranges (4 per thread, loads issued together with the count) the prefix sums stay in
+// LDS and each block start is found there by binary search; longer lists take passes of 4096 and
+// each range marks the block starts it holds.
 __global__ __launch_bounds__(1024) void k_range_prefix(CacheView c, CandView cand, int32_t* prefix,
                                                        int32_t* chunk_first, int nchunk) {
-  constexpr int NT = 1024, NW = NT / 64, IPT = 4;
+  constexpr int NT = 1024, NW = NT / 64, IPT = 4, MAXL = NT * IPT;
   __shared__ int scan_sm[NW + 1];
+  __shared__ int spre[MAXL + 1];
   const int u = blockIdx.x;
-  const int cnt = clampi(cand.count[u], 0, cand.max_items);
+  const int tid = threadIdx.x;
   int32_t* pre = prefix + (size_t)u * (cand.max_items + 1);
   int32_t* cf = chunk_first + (size_t)u * nchunk;
   const int32_t* it = cand.items + (size_t)u * cand.max_items * 2;
-  int carry = 0;
-  for (int base = 0; base < cnt; base += NT * IPT) {
-    const int i0 = base + (int)threadIdx.x * IPT;
-    int len[IPT];
+  const int i0 = tid * IPT;
+  int len[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) len[i] = it[(size_t)min(i0 + i, cand.max_items - 1) * 2 + 1];
+  const int cnt = clampi(cand.count[u], 0, cand.max_items);
+  if (cnt <= MAXL) {
     int local = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      len[i] = (i0 + i < cnt) ? max(0, it[(size_t)(i0 + i) * 2 + 1]) : 0;
+      len[i] = (i0 + i < cnt) ? max(0, len[i]) : 0;
+      local += len[i];
+    }
+    int total;
+    int s0 = block_excl_scan<NW>(local, scan_sm, &total);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      if (i0 + i < cnt) {
+        pre[i0 + i] = s0;
+        spre[i0 + i] = s0;
+      }
+      s0 += len[i];
+    }
+    if (tid == 0) {
+      pre[cnt] = total;
+      spre[cnt] = total;
+    }
+    __syncthreads();
+    for (int j = tid; j < nchunk; j += NT) {
+      const int x = j * kEstCands;
+      int r = cnt;
+      if (x < total) {
+        int lo = 0, hi = cnt;  // largest lo with spre[lo] <= x (a non-empty range: x < total)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (spre[mid] <= x) lo = mid; else hi = mid;
+        }
+        r = lo;
+      }
+      cf[j] = r;
+    }
+    return;
+  }
+  int carry = 0;
+  for (int base = 0; base < cnt; base += MAXL) {
+    const int ib = base + i0;
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      len[i] = (ib + i < cnt) ? max(0, it[(size_t)(ib + i) * 2 + 1]) : 0;
       local += len[i];
     }
     int total;
     int s0 = carry + block_excl_scan<NW>(local, scan_sm, &total);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      if (i0 + i < cnt) {
-        pre[i0 + i] = s0;
+      if (ib + i < cnt) {
+        pre[ib + i] = s0;
         if (len[i] > 0) {
           const int64_t e0 = (int64_t)s0 + len[i];
-          for (int j = (s0 + kEstCands - 1) / kEstCands; j < nchunk && (int64_t)j * kEstCands < e0; ++j) cf[j] = i0 + i;
+          for (int j = (s0 + kEstCands - 1) / kEstCands; j < nchunk && (int64_t)j * kEstCands < e0; ++j) cf[j] = ib + i;
         }
         s0 += len[i];
       }
     }
     carry += total;
   }
-  if (threadIdx.x == 0) pre[cnt] = carry;
-  for (int j = threadIdx.x; j < nchunk; j += NT)
+  if (tid == 0) pre[cnt] = carry;
+  for (int j = tid; j < nchunk; j += NT)
     if ((int64_t)j * kEstCands >= carry) cf[j] = cnt;
 }
 

@@ -280,11 +280,8 @@ int topp_elems_per_thread(int64_t ncap) {
   return 0;
 }
 
-hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_t* cand_row, const float* logits,
-                       int ncap, float p,
-                       int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
-                       int mask_words, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt,
-                       hipStream_t s) {
+hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
+                       float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, hipStream_t s) {
   const int E = ncap / kToppThreads;
   dim3 grid((unsigned)(c.B * c.Hq)), block(kToppThreads);
 #define TWL_TOPP_CASE(EE)                                                                                   \
@@ -303,9 +300,13 @@ hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_
     default: return hipErrorInvalidValue;
   }
 #undef TWL_TOPP_CASE
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 ugrid((unsigned)(c.B * c.Hkv));
+  return hipGetLastError();
+}
+
+hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, const int32_t* cand_row,
+                        int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, hipStream_t s) {
+  const int E = ncap / kToppThreads;
+  dim3 ugrid((unsigned)(c.B * c.Hkv)), block(kToppThreads);
 #define TWL_UNION_G(EE, GG)                                                                                \
   case GG:                                                                                                 \
     hipLaunchKernelGGL((k_union<EE, GG>), ugrid, block, 0, s, c, mask_ws, cand_tok, cand_row, ncap,      \

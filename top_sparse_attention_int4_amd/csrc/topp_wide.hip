@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
                                                             int iters, uint64_t* __restrict__ state,
                                                             uint32_t* __restrict__ head_mask, int mask_words,
                                                             uint32_t* __restrict__ uwords,
-                                                            int32_t* __restrict__ chunk_cnt) {
+                                                            int32_t* __restrict__ chunk_cnt, float* threshold) {
   __shared__ float s_thr[G];
   __shared__ int s_cnt[NW];
   const int nch = ncap / kWideChunk;
@@ -204,7 +204,11 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
     }
     if (lane == 0) {
       s_thr[hh] = __uint_as_float(T);
-      if (ch == 0) st[kWideST] = (uint64_t)T;
+      if (ch == 0) {
+        st[kWideST] = (uint64_t)T;
+        const uint64_t Z = st[kWideSZ];
+        if (threshold) threshold[bh0 + hh] = Z ? __uint_as_float(T) / (float)((double)Z / 1099511627776.0) : 0.f;
+      }
     }
   }
   __syncthreads();
@@ -269,8 +273,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int nca
                                                             const int32_t* __restrict__ cand_row,
                                                             int32_t* __restrict__ union_tok,
                                                             int32_t* __restrict__ union_row,
-                                                            int32_t* __restrict__ union_cnt, float* threshold,
-                                                            float* mass) {
+                                                            int32_t* __restrict__ union_cnt, float* mass) {
   constexpr int WPB = kWideChunk / 32;  // union words per chunk
   __shared__ uint32_t uw[WPB];
   __shared__ int woff[WPB];
@@ -281,13 +284,10 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int nca
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int tid = threadIdx.x;
   const size_t bh0 = (size_t)b * c.Hq + (size_t)h * G;
-  if (ch == 0 && tid < G) {
+  if (ch == 0 && tid < G && mass) {
     const uint64_t* st = state + (bh0 + tid) * kWideStateWords;
     const uint64_t Z = st[kWideSZ];
-    const float zf = (float)((double)Z / 1099511627776.0);
-    const float T = __uint_as_float((uint32_t)st[kWideST]);
-    threshold[bh0 + tid] = Z ? T / zf : 0.f;
-    if (mass) mass[bh0 + tid] = Z ? (float)((double)st[kWideMass] / (double)Z) : 0.f;
+    mass[bh0 + tid] = Z ? (float)((double)st[kWideMass] / (double)Z) : 0.f;
   }
   if (tid < 64) {
     int acc = 0;
@@ -320,10 +320,8 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int nca
   }
 }
 
-hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
-                            float* logits, int ncap, float p, int iters, float* threshold, float* mass,
-                            uint32_t* head_mask, int mask_words, int32_t* union_tok, int32_t* union_row,
-                            int32_t* union_cnt, hipStream_t s) {
+hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits, int ncap, float p, int iters,
+                            float* threshold, uint32_t* head_mask, int mask_words, hipStream_t s) {
   if (ncap % kWideChunk) return hipErrorInvalidValue;
   const int nch = ncap / kWideChunk;
   const unsigned hgrid = (unsigned)(c.B * c.Hq * nch), ugrid = (unsigned)(c.B * c.Hkv * nch);
@@ -334,9 +332,7 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const int32_t*
 #define TWL_WIDE_G(GG)                                                                                      \
   case GG:                                                                                                  \
     hipLaunchKernelGGL(k_wide_mask<GG>, dim3(ugrid), blk, 0, s, c, logits, ncap, iters, wd.state, head_mask, \
-                       mask_words, wd.uwords, wd.chunk_cnt);                                                \
-    hipLaunchKernelGGL(k_wide_emit<GG>, dim3(ugrid), blk, 0, s, c, ncap, wd.state, wd.uwords, wd.chunk_cnt,  \
-                       cand_tok, cand_row, union_tok, union_row, union_cnt, threshold, mass);              \
+                       mask_words, wd.uwords, wd.chunk_cnt, threshold);                                     \
     break;
   switch (c.G) {
     TWL_WIDE_G(1)
@@ -346,6 +342,29 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const int32_t*
     default: return hipErrorInvalidValue;
   }
 #undef TWL_WIDE_G
+  return hipGetLastError();
+}
+
+hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
+                            int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, float* mass,
+                            hipStream_t s) {
+  if (ncap % kWideChunk) return hipErrorInvalidValue;
+  const int nch = ncap / kWideChunk;
+  const unsigned ugrid = (unsigned)(c.B * c.Hkv * nch);
+  const dim3 blk(kWideThreads);
+#define TWL_WIDE_E(GG)                                                                                      \
+  case GG:                                                                                                  \
+    hipLaunchKernelGGL(k_wide_emit<GG>, dim3(ugrid), blk, 0, s, c, ncap, wd.state, wd.uwords, wd.chunk_cnt,  \
+                       cand_tok, cand_row, union_tok, union_row, union_cnt, mass);                         \
+    break;
+  switch (c.G) {
+    TWL_WIDE_E(1)
+    TWL_WIDE_E(2)
+    TWL_WIDE_E(4)
+    TWL_WIDE_E(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef TWL_WIDE_E
   return hipGetLastError();
 }
 

@@ -75,33 +75,47 @@ hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t
 // wide: when non-null, the estimate also writes the per-block logit maxima and clears the wide state
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
                            float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s);
-hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
-                            float* logits, int ncap, float p, int iters, float* threshold, float* mass,
-                            uint32_t* head_mask, int mask_words, int32_t* union_tok, int32_t* union_row,
-                            int32_t* union_cnt, hipStream_t s);
+// wide top-p: histogram passes and masks (union bitmap in wd.uwords); the emit kernel writes the
+// compacted union lists and the threshold/mass outputs
+hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits, int ncap, float p, int iters,
+                            float* threshold, uint32_t* head_mask, int mask_words, hipStream_t s);
+hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
+                            int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, float* mass,
+                            hipStream_t s);
 hipError_t launch_topp_weighted(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
                                 uint32_t* mask_ws, const int32_t* mult, int mult_stride, hipStream_t s);
 hipError_t launch_cluster_select(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
                                  const uint16_t* centroids, const int32_t* csize, const int32_t* coff, int C,
                                  int cpad, float* lam, float* thr, uint32_t* mask_ws, int32_t* ranges,
                                  int32_t* count, hipStream_t s);
-hipError_t launch_topp(const CacheView& c, const int32_t* cand_tok, const int32_t* cand_row, const float* logits,
-                       int ncap, float p,
-                       int iters, float* threshold, float* mass, uint32_t* mask_ws, uint32_t* head_mask,
-                       int mask_words, int32_t* union_tok, int32_t* union_row,
-                       int32_t* union_cnt, hipStream_t s);
+hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
+                       float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, hipStream_t s);
+hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, const int32_t* cand_row,
+                        int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, hipStream_t s);
 hipError_t launch_csr_emit(const CacheView& c, const int32_t* union_tok, const int32_t* union_cnt, int ncap,
                            int32_t* indptr, int32_t* tokens, int64_t capacity, hipStream_t s);
 // tokens per attention chunk for an upper bound of the total selected tokens
 int attn_chunk_tokens(int64_t total_upper);
+// Kept candidates given as bitmaps over the candidate index space (the top-p output), with the K/V
+// row of every candidate: the attention then reads no compacted list.
+struct MaskView {
+  const uint32_t* head_masks;   // [B*Hq][ncap/32] per-head bitmaps (OR-ed over the group), or
+  const uint32_t* union_words;  // [B*Hkv][ncap/32] union bitmaps (used when non-null)
+  const int32_t* cand_row;      // [B*Hkv][ncap] K/V row of each candidate
+  int64_t ncap;
+};
+// one workgroup per chunk slot: slot k of unit u covers list entries [k*chunk_tokens, (k+1)*chunk_tokens)
 hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
-                       int64_t max_chunks, float* partials, int32_t* csr_indptr, int32_t* csr_tokens,
-                       int64_t capacity, hipStream_t s);
+                       int slots, float* partials, hipStream_t s);
+// one workgroup per chunk slot of the candidate space (every slot writes a partial)
+hipError_t launch_attn_masked(const CacheView& c, const uint16_t* q, float sm, const MaskView& mv, int chunk_tokens,
+                              int slots, float* partials, hipStream_t s);
 // K/V rows of a CSR token list (into `rows`, same indexing), entries at or past `capacity` skipped
 hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,
                        int64_t capacity, hipStream_t s);
-hipError_t launch_merge(const CacheView& c, const ListView& list, int chunk_tokens, int64_t max_chunks,
-                        const float* partials, float* out, float* lse, hipStream_t s);
+// list: chunks per unit from the list counts; list == nullptr: every slot holds a partial
+hipError_t launch_merge(const CacheView& c, const ListView* list, int chunk_tokens, int slots, const float* partials,
+                        float* out, float* lse, hipStream_t s);
 constexpr int kPartFloats = 4 + kD;  // per (chunk, head): max, sum, 2 pad, output row (16-byte aligned)
 // elements per thread of the top-p block for a candidate capacity (0 = unsupported)
 int topp_elems_per_thread(int64_t ncap);
