@@ -120,8 +120,6 @@ __global__ __launch_bounds__(1024) void k_range_prefix(CacheView c, CandView can
     if ((int64_t)j * kEstCands >= carry) cf[j] = cnt;
 }
 
-constexpr int kEstBatches = kEstCands / 64;  // 64-candidate batches per block
-
 // Token id and K/V row of candidate k (row -1 when k is not a candidate).  `cnt` is the unit's item
 // count for the page and range forms.
 __device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView& cand, int u, int b, int h, int k,
@@ -146,51 +144,62 @@ __device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView&
   if (tok >= 0) row = (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15);
 }
 
-template <int G>
+// Byte n of x as a float (one conversion instruction each).
+__device__ __forceinline__ float ub0(uint32_t x) { float r; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ub1(uint32_t x) { float r; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ub2(uint32_t x) { float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ub3(uint32_t x) { float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); return r; }
+
+// NB batches of 64 candidates per block (64 * NB candidates, NB a multiple of kGroups / 2 .. 8).
+template <int G, int NB>
 __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
                                                   CandView cand, int ncap, int chunks_per_unit,
                                                   float* __restrict__ logits, int32_t* __restrict__ cand_tok,
                                                   int32_t* __restrict__ cand_row, float* __restrict__ pmax,
                                                   uint64_t* __restrict__ wstate, size_t wstate_words) {
-  constexpr int NB = kEstBatches;
+  constexpr int NC = 64 * NB;
+  constexpr int NH = (G + kGroups - 1) / kGroups;  // heads combined per wave
   const int u = blockIdx.x / chunks_per_unit;
   const int ck = blockIdx.x - u * chunks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   __shared__ float T[2][kGroups][G][64];
-
-  // resolve every batch's candidates, then issue all code and scale/zero loads at once
-  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int cnt = (cand.mode == kCandAll) ? 0 : clampi(cand.count[u], 0, cand.max_items);
-  const int kbase = ck * (64 * NB) + lane;
-  int tokv[NB], rowv[NB];
+  __shared__ int s_row[NB][64];
   if (wstate) {
     // clear the wide top-p state for the passes that follow this kernel
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < wstate_words; i += (size_t)gridDim.x * 256)
       wstate[i] = 0ull;
   }
+  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+  const int cnt = (cand.mode == kCandAll) ? 0 : clampi(cand.count[u], 0, cand.max_items);
+  const int k0 = ck * NC;
+
+  // ---- candidate resolution: wave w resolves batches w, w + 4, ... (token id and K/V row); the
+  // rows meet in LDS so each is resolved once
   if (cand.mode == kCandRanges) {
     // The block's candidates lie in the ranges r0..rmax; their prefix sums and first tokens are
     // staged in LDS when they fit, and every lane searches there.
-    __shared__ int s_pre[kEstCands];
-    __shared__ int s_beg[kEstCands];
+    __shared__ int s_pre[NC + 1];
+    __shared__ int s_beg[NC + 1];
     const int32_t* pre = cand.range_prefix + (size_t)u * (cand.max_items + 1);
     const int nchunk = ncap / kEstCands;
-    const int r0 = clampi(cand.chunk_first[(size_t)u * nchunk + ck], 0, cnt);
-    const int r1 = (ck + 1 < nchunk) ? clampi(cand.chunk_first[(size_t)u * nchunk + ck + 1], 0, cnt) : cnt;
+    const int j0 = k0 / kEstCands, j1 = (k0 + NC - 1) / kEstCands;
+    const int r0 = clampi(cand.chunk_first[(size_t)u * nchunk + j0], 0, cnt);
+    const int r1 = (j1 + 1 < nchunk) ? clampi(cand.chunk_first[(size_t)u * nchunk + j1 + 1], 0, cnt) : cnt;
     const int rmax = min(r1, cnt - 1);
     const int nr = rmax - r0 + 1;
     const int tot = pre[cnt];
-    const bool staged = nr >= 1 && nr <= kEstCands;
-    if (staged && (int)threadIdx.x < nr) {
-      s_pre[threadIdx.x] = pre[r0 + threadIdx.x];
-      s_beg[threadIdx.x] = cand.items[((size_t)u * cand.max_items + r0 + threadIdx.x) * 2];
+    const bool staged = nr >= 1 && nr <= NC + 1;
+    if (staged) {
+      for (int i = threadIdx.x; i < nr; i += 256) {
+        s_pre[i] = pre[r0 + i];
+        s_beg[i] = cand.items[((size_t)u * cand.max_items + r0 + i) * 2];
+      }
     }
     __syncthreads();
-#pragma unroll
-    for (int bt = 0; bt < NB; ++bt) {
-      const int k = kbase + 64 * bt;
+    for (int bt = g; bt < NB; bt += kGroups) {
+      const int k = k0 + 64 * bt + lane;
       int t = -1;
       if (nr >= 1 && k < tot) {
         int lo, beg, p0;
@@ -215,16 +224,30 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
         }
         if (p0 <= k) t = beg + (k - p0);
       }
-      tokv[bt] = (t >= 0 && t < n) ? t : -1;
-      rowv[bt] = tokv[bt] >= 0 ? (c.page_table[(size_t)b * c.maxP + (tokv[bt] >> 4)] * c.Hkv + h) * kPage + (tokv[bt] & 15)
-                               : -1;
+      const int tok = (t >= 0 && t < n) ? t : -1;
+      const int row = tok >= 0 ? (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15) : -1;
+      s_row[bt][lane] = row;
+      cand_tok[(size_t)u * ncap + k] = tok;
+      cand_row[(size_t)u * ncap + k] = row;
     }
   } else {
-#pragma unroll
-    for (int bt = 0; bt < NB; ++bt) cand_resolve(c, cand, u, b, h, kbase + 64 * bt, n, cnt, tokv[bt], rowv[bt]);
+    for (int bt = g; bt < NB; bt += kGroups) {
+      const int k = k0 + 64 * bt + lane;
+      int tok, row;
+      cand_resolve(c, cand, u, b, h, k, n, cnt, tok, row);
+      s_row[bt][lane] = row;
+      cand_tok[(size_t)u * ncap + k] = tok;
+      cand_row[(size_t)u * ncap + k] = row;
+    }
   }
+  __syncthreads();
+
+  // ---- this wave's group of every candidate: code and scale/zero loads all in flight together
+  int rowv[NB];
   uint4 cwv[NB];
   uint32_t mwv[NB];
+#pragma unroll
+  for (int bt = 0; bt < NB; ++bt) rowv[bt] = s_row[bt][lane];
 #pragma unroll
   for (int bt = 0; bt < NB; ++bt) {
     if (rowv[bt] >= 0) {
@@ -251,12 +274,12 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
     bsum[hh] = acc;
   }
 
-  float mx[(G + kGroups - 1) / kGroups];  // running maxima of this wave's heads (pmax)
+  float mx[NH];  // running maxima of this wave's heads (pmax)
 #pragma unroll
-  for (int i = 0; i < (G + kGroups - 1) / kGroups; ++i) mx[i] = -__builtin_inff();
+  for (int i = 0; i < NH; ++i) mx[i] = -__builtin_inff();
 #pragma unroll
   for (int bt = 0; bt < NB; ++bt) {
-    const int k = kbase + 64 * bt;
+    const int k = k0 + 64 * bt + lane;
     if (rowv[bt] >= 0) {
       // the group's 32 codes as floats (element 2j of byte j is its low nibble)
       const uint32_t words[4] = {cwv[bt].x, cwv[bt].y, cwv[bt].z, cwv[bt].w};
@@ -265,14 +288,14 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       for (int wi = 0; wi < 4; ++wi) {
         const uint32_t lo = words[wi] & 0x0F0F0F0Fu;
         const uint32_t hi = (words[wi] >> 4) & 0x0F0F0F0Fu;
-        code[8 * wi + 0] = (float)(lo & 0xFFu);
-        code[8 * wi + 1] = (float)(hi & 0xFFu);
-        code[8 * wi + 2] = (float)((lo >> 8) & 0xFFu);
-        code[8 * wi + 3] = (float)((hi >> 8) & 0xFFu);
-        code[8 * wi + 4] = (float)((lo >> 16) & 0xFFu);
-        code[8 * wi + 5] = (float)((hi >> 16) & 0xFFu);
-        code[8 * wi + 6] = (float)(lo >> 24);
-        code[8 * wi + 7] = (float)(hi >> 24);
+        code[8 * wi + 0] = ub0(lo);
+        code[8 * wi + 1] = ub0(hi);
+        code[8 * wi + 2] = ub1(lo);
+        code[8 * wi + 3] = ub1(hi);
+        code[8 * wi + 4] = ub2(lo);
+        code[8 * wi + 5] = ub2(hi);
+        code[8 * wi + 6] = ub3(lo);
+        code[8 * wi + 7] = ub3(hi);
       }
       const float s = half_bits_to_float(mwv[bt] & 0xffffu);
       const float z = half_bits_to_float(mwv[bt] >> 16);
@@ -291,13 +314,9 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
         T[bt & 1][g][hh][lane] = sa + zb;
       }
     }
-    if (g == 0 && k < ncap) {
-      cand_tok[(size_t)u * ncap + k] = tokv[bt];
-      cand_row[(size_t)u * ncap + k] = rowv[bt];
-    }
     __syncthreads();  // T[bt & 1] complete; T[(bt + 1) & 1] was last read before this barrier
 #pragma unroll
-    for (int i = 0; i < (G + kGroups - 1) / kGroups; ++i) {
+    for (int i = 0; i < NH; ++i) {
       const int hh = g + kGroups * i;
       if (hh < G) {
         float lg = -__builtin_inff();
@@ -307,13 +326,13 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
           lg = sm * (r01 + r23);
         }
         mx[i] = fmaxf(mx[i], lg);
-        if (k < ncap) logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
+        logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
       }
     }
   }
   if (pmax) {
 #pragma unroll
-    for (int i = 0; i < (G + kGroups - 1) / kGroups; ++i) {
+    for (int i = 0; i < NH; ++i) {
       const int hh = g + kGroups * i;
       if (hh < G) {
         const float m = wave_max_dpp(mx[i]);
@@ -330,27 +349,43 @@ hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t
   return hipGetLastError();
 }
 
+// 8 batches for large steps (and always for the wide top-p, whose per-block maxima region holds
+// ncap / 256 entries per head), 2 for small ones (more blocks in flight)
+int est_batches(int64_t ncap, int64_t units) {
+  return (ncap > kNarrowMaxCands || ncap * units >= ((int64_t)1 << 19)) ? 8 : 2;
+}
+
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
                            float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s) {
-  if (ncap % kEstCands) return hipErrorInvalidValue;
-  const int cpu = ncap / kEstCands;
+  const int nb = est_batches(ncap, (int64_t)c.B * c.Hkv);
+  if (ncap % (64 * nb) || ncap % kEstCands) return hipErrorInvalidValue;
+  const int cpu = ncap / (64 * nb);
   dim3 grid((unsigned)(c.B * c.Hkv * cpu));
   float* pmax = wide ? wide->pmax : nullptr;
   uint64_t* wst = wide ? wide->state : nullptr;
   const size_t wwords = wide ? (size_t)c.B * c.Hq * kWideStateWords : 0;
-#define TWL_EST_CASE(GG)                                                                                   \
-  case GG:                                                                                                 \
-    hipLaunchKernelGGL(k_estimate<GG>, grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits, cand_tok, \
-                       cand_row, pmax, wst, wwords);                                                       \
+#define TWL_EST_G(GG, NB)                                                                                     \
+  case GG:                                                                                                    \
+    hipLaunchKernelGGL((k_estimate<GG, NB>), grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits,        \
+                       cand_tok, cand_row, pmax, wst, wwords);                                               \
     break;
-  switch (c.G) {
-    TWL_EST_CASE(1)
-    TWL_EST_CASE(2)
-    TWL_EST_CASE(4)
-    TWL_EST_CASE(8)
+#define TWL_EST_NB(NB)                      \
+  case NB:                                  \
+    switch (c.G) {                          \
+      TWL_EST_G(1, NB)                      \
+      TWL_EST_G(2, NB)                      \
+      TWL_EST_G(4, NB)                      \
+      TWL_EST_G(8, NB)                      \
+      default: return hipErrorInvalidValue; \
+    }                                       \
+    break;
+  switch (nb) {
+    TWL_EST_NB(2)
+    TWL_EST_NB(8)
     default: return hipErrorInvalidValue;
   }
-#undef TWL_EST_CASE
+#undef TWL_EST_G
+#undef TWL_EST_NB
   return hipGetLastError();
 }
 

@@ -21,6 +21,8 @@
 //
 // The GQA union (paperlayer §B.2: the union over a group's query heads, read once) is a separate
 // small kernel over the head masks.
+#include <algorithm>
+
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -251,14 +253,15 @@ __global__ __launch_bounds__(1024) void k_union(CacheView c, const uint32_t* __r
   if (tid == 0) union_cnt[u] = total;
 }
 
+// CSR of the units' kept lists: block (x, u) copies part x of unit u's list (eight loads in flight per
+// thread), its offset being the sum of the counts of the units before it.
 __global__ __launch_bounds__(256) void k_csr_emit(CacheView c, const int32_t* __restrict__ union_tok,
                                                   const int32_t* __restrict__ union_cnt, int ncap,
                                                   int32_t* indptr, int32_t* tokens, int64_t capacity) {
   const int U = c.B * c.Hkv;
-  const int u = blockIdx.x;
+  const int u = blockIdx.y;
   __shared__ int s_off;
   if (threadIdx.x < 64) {
-    // offset of unit u = sum of the counts of units before it
     int acc = 0;
     for (int i = (int)threadIdx.x; i < u; i += 64) acc += union_cnt[i];
     acc = wave_sum_int(acc);
@@ -266,12 +269,24 @@ __global__ __launch_bounds__(256) void k_csr_emit(CacheView c, const int32_t* __
   }
   __syncthreads();
   const int off = s_off, cnt = union_cnt[u];
-  if (threadIdx.x == 0) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     indptr[u] = off;
     if (u == U - 1) indptr[U] = off + cnt;
   }
-  for (int i = threadIdx.x; i < cnt; i += 256)
-    if (off + i < capacity) tokens[off + i] = union_tok[(size_t)u * ncap + i];
+  const int32_t* src = union_tok + (size_t)u * ncap;
+  for (int base = (int)blockIdx.x * 2048; base < cnt; base += (int)gridDim.x * 2048) {
+    int v[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = base + r * 256 + (int)threadIdx.x;
+      v[r] = (i < cnt) ? src[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int i = base + r * 256 + (int)threadIdx.x;
+      if (i < cnt && off + (int64_t)i < capacity) tokens[off + i] = v[r];
+    }
+  }
 }
 
 int topp_elems_per_thread(int64_t ncap) {
@@ -361,7 +376,8 @@ hipError_t launch_topp_weighted(const CacheView& c, const float* logits, int nca
 
 hipError_t launch_csr_emit(const CacheView& c, const int32_t* union_tok, const int32_t* union_cnt, int ncap,
                            int32_t* indptr, int32_t* tokens, int64_t capacity, hipStream_t s) {
-  hipLaunchKernelGGL(k_csr_emit, dim3((unsigned)(c.B * c.Hkv)), dim3(256), 0, s, c, union_tok, union_cnt, ncap,
+  const unsigned parts = (unsigned)std::min<int64_t>(64, ((int64_t)ncap + 2047) / 2048);
+  hipLaunchKernelGGL(k_csr_emit, dim3(parts, (unsigned)(c.B * c.Hkv)), dim3(256), 0, s, c, union_tok, union_cnt, ncap,
                      indptr, tokens, capacity);
   return hipGetLastError();
 }

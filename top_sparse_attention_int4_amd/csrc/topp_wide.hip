@@ -326,7 +326,8 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits,
   const int nch = ncap / kWideChunk;
   const unsigned hgrid = (unsigned)(c.B * c.Hq * nch), ugrid = (unsigned)(c.B * c.Hkv * nch);
   const dim3 blk(kWideThreads);
-  hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, ncap / kEstCands, wd.state);
+  const int npm = ncap / (64 * est_batches(ncap, (int64_t)c.B * c.Hkv));
+  hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, npm, wd.state);
   hipLaunchKernelGGL(k_wide_hist2, dim3(hgrid), blk, 0, s, logits, ncap, p, wd.state);
   hipLaunchKernelGGL(k_wide_hist3, dim3(hgrid), blk, 0, s, logits, ncap, wd.state);
 #define TWL_WIDE_G(GG)                                                                                      \

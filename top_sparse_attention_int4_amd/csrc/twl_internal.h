@@ -47,12 +47,14 @@ constexpr int kWideStateWords = 4760;
 constexpr int kNarrowMaxCands = 65536;      // largest candidate count of the register-resident top-p
 constexpr int kWideMaxCands = 1 << 22;      // fixed-point mass bound
 struct WideWs {
-  float* pmax;         // [B*Hq][ncap / kEstCands] per-estimate-block logit maxima
+  float* pmax;         // [B*Hq][ncap / (64 * est_batches)] per-estimate-block logit maxima
   uint64_t* state;     // [B*Hq][kWideStateWords]
   int32_t* chunk_cnt;  // [B*Hkv][ncap / kWideChunk]
   uint32_t* uwords;    // [B*Hkv][ncap / 32] union bitmap
 };
-constexpr int kEstCands = 256;  // candidates per block of the estimate
+constexpr int kEstCands = 256;  // candidate block of the range starts (chunk_first); divides the estimate's blocks
+// 64-candidate batches per estimate block for a candidate capacity and unit count (2 or 8)
+int est_batches(int64_t ncap, int64_t units);
 
 // Token list of each unit for the attention stage: either padded rows (stride) with counts, or CSR.
 struct ListView {
