@@ -88,18 +88,17 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     }
   }
   __syncthreads();
+  // coarse sums (32 bins each): thread t adds bins 2t and 2t+1, a row of 16 lanes scans its 32
   auto coarse = [&](const uint64_t* h, int ncoarse) {
-    if (tid < ncoarse) {
-      uint64_t x = 0;
-#pragma unroll 8
-      for (int i = 0; i < 32; ++i) x += h[32 * tid + i];
-      cs[tid] = x;
+    if (tid < ncoarse * 16) {
+      const uint64_t x = row16_incl_scan_u64(h[2 * tid] + h[2 * tid + 1]);
+      if ((lane & 15) == 15) cs[tid >> 4] = x;
     }
     __syncthreads();
   };
   coarse(h1, 64);
   if (wv == 0) {
-    const uint64_t zf = __shfl(wave_suffix_u64(cs[lane]), 0);
+    const uint64_t zf = readlane_u64(wave_incl_scan_u64(cs[lane]), 63);
     int mode = 1, bin = 0;
     uint64_t rem = 0;
     if (zf != 0ull && p < 1.0f) {

@@ -89,15 +89,55 @@ __device__ __forceinline__ int wave_sum_int(int x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-// Inclusive prefix sum over the lanes of a wave.
+// DPP lane moves for scans: row_shr:n shifts within each row of 16 lanes (lanes with no source read
+// 0); row_bcast:15 / row_bcast:31 copy lane 15 / 31 into the rows selected by the row mask.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_scan_move(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, true);
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Inclusive prefix sum over the lanes of a wave (DPP: four in-row steps, two row broadcasts).
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  x += dpp_scan_move<kDppShr1, 0xf>(x);
+  x += dpp_scan_move<kDppShr2, 0xf>(x);
+  x += dpp_scan_move<kDppShr4, 0xf>(x);
+  x += dpp_scan_move<kDppShr8, 0xf>(x);
+  x += dpp_scan_move<kDppBcast15, 0xa>(x);
+  x += dpp_scan_move<kDppBcast31, 0xc>(x);
   return x;
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_scan_move_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)dpp_scan_move<CTRL, ROW_MASK>((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)dpp_scan_move<CTRL, ROW_MASK>((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+// Inclusive prefix sum of 64-bit integers over the lanes of a wave.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x) {
+  x += dpp_scan_move_u64<kDppShr1, 0xf>(x);
+  x += dpp_scan_move_u64<kDppShr2, 0xf>(x);
+  x += dpp_scan_move_u64<kDppShr4, 0xf>(x);
+  x += dpp_scan_move_u64<kDppShr8, 0xf>(x);
+  x += dpp_scan_move_u64<kDppBcast15, 0xa>(x);
+  x += dpp_scan_move_u64<kDppBcast31, 0xc>(x);
+  return x;
+}
+// Inclusive prefix sum of 64-bit integers within each row of 16 lanes (lane 15 of a row holds the
+// row's total).
+__device__ __forceinline__ uint64_t row16_incl_scan_u64(uint64_t x) {
+  x += dpp_scan_move_u64<kDppShr1, 0xf>(x);
+  x += dpp_scan_move_u64<kDppShr2, 0xf>(x);
+  x += dpp_scan_move_u64<kDppShr4, 0xf>(x);
+  x += dpp_scan_move_u64<kDppShr8, 0xf>(x);
+  return x;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Block-wide reductions for blocks of NW waves, built on the DPP wave reductions.  `red` must hold
@@ -241,13 +281,9 @@ constexpr float kFixScale = 1099511627776.0f;  // 2^40
 __device__ __forceinline__ uint64_t to_fix(float e) { return (uint64_t)(e * kFixScale); }
 
 __device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t y = __shfl_down(x, d);
-    if (lane + d < 64) x += y;
-  }
-  return x;
+  // sum over lanes >= l: total minus the exclusive prefix
+  const uint64_t p = wave_incl_scan_u64(x);
+  return readlane_u64(p, 63) - p + x;
 }
 
 // Largest bin of one histogram level whose suffix mass reaches `target` (>= 1), from its coarse
@@ -256,17 +292,19 @@ __device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t x) {
 __device__ __forceinline__ void wide_find(const uint64_t* fine, const uint64_t* coarse, int ncoarse,
                                           uint64_t target, int& bin, uint64_t& rem) {
   const int lane = threadIdx.x & 63;
-  uint64_t x = (lane < ncoarse) ? coarse[lane] : 0ull;
-  x = wave_suffix_u64(x);
-  unsigned long long bal = __ballot(lane < ncoarse && x >= target);
+  const uint64_t x = (lane < ncoarse) ? coarse[lane] : 0ull;
+  const uint64_t px = wave_incl_scan_u64(x);
+  const uint64_t tx = readlane_u64(px, 63);
+  unsigned long long bal = __ballot(lane < ncoarse && tx - px + x >= target);
   const int cb = bal ? 63 - __clzll(bal) : 0;
-  const uint64_t above = (cb < 63) ? __shfl(x, cb + 1) : 0ull;
+  const uint64_t above = tx - readlane_u64(px, cb);  // mass of the coarse blocks above cb
   const uint64_t r1 = target - above;
-  uint64_t y = (lane < 32) ? fine[32 * cb + lane] : 0ull;
-  y = wave_suffix_u64(y);
-  bal = __ballot(lane < 32 && y >= r1);
+  const uint64_t y = (lane < 32) ? fine[32 * cb + lane] : 0ull;
+  const uint64_t py = wave_incl_scan_u64(y);
+  const uint64_t ty = readlane_u64(py, 63);
+  bal = __ballot(lane < 32 && ty - py + y >= r1);
   const int fb = bal ? 63 - __clzll(bal) : 0;
-  const uint64_t above2 = __shfl(y, fb + 1);  // lanes >= 32 hold 0
+  const uint64_t above2 = ty - readlane_u64(py, fb);
   bin = 32 * cb + fb;
   rem = r1 - above2;
 }
