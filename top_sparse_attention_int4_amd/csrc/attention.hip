@@ -66,6 +66,16 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int t_begin = k * CH;
   const int w_begin = t_begin + wv * QL;
+  // B operand: q of head nn (zero for padding columns), dims 32kb + 8grp .. +7
+  bf16x8_t qv[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    if (nn < G) {
+      qv[kb] = *reinterpret_cast<const bf16x8_t*>(q + ((size_t)b * c.Hq + (size_t)h * G + nn) * kD + kb * 32 + grp * 8);
+    } else {
+      qv[kb] = bf16x8_t{};
+    }
+  }
   int rows[NSB];
   int w_end;
   if constexpr (MK) {
@@ -127,16 +137,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     if (t_begin >= cnt) return;  // an unused slot
     const int t_end = min(cnt, t_begin + CH);
     w_end = min(t_end, w_begin + QL);
-  }
-  // B operand: q of head nn (zero for padding columns), dims 32kb + 8grp .. +7
-  bf16x8_t qv[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    if (nn < G) {
-      qv[kb] = *reinterpret_cast<const bf16x8_t*>(q + ((size_t)b * c.Hq + (size_t)h * G + nn) * kD + kb * 32 + grp * 8);
-    } else {
-      qv[kb] = bf16x8_t{};
-    }
   }
   const int w_first = MK ? 0 : w_begin;  // list index of the first entry of sub-block 0
   const int nrows = c.nphys * c.Hkv * kPage;
@@ -383,9 +383,9 @@ __global__ __launch_bounds__(1024) void k_merge(CacheView c, ListView L, bool us
 }
 
 int attn_chunk_tokens(int64_t total_upper) {
-  // 64 tokens (one sub-block per wave) up to 512, aiming at about 4096 chunks
+  // 128 tokens (two pipelined sub-blocks per wave) up to 512, aiming at about 4096 chunks
   int64_t sb = total_upper / (64 * 4096);
-  int s = 1;
+  int s = 2;
   while (s * 2 <= sb && s < 8) s *= 2;
   return 64 * s;
 }
