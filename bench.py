@@ -4,9 +4,10 @@
 
 A step is one pass of the whole hot path over one batch: Quest-style page selection -> INT4 weight
 estimate -> per-head top-p (bisection) -> GQA union -> split-K sparse attention -> merge.  Steps
-rotate over L independently drawn layer caches of identical shape whose footprint exceeds 1 GiB, so
-every step reads cold HBM rather than the 256 MB Infinity Cache.  Inputs are resident in HBM before
-timing starts.
+rotate over L layer caches of identical shape, enough that the rotation exceeds 4 GiB and its INT4
+codes and page bounds alone exceed 1 GiB, so every step reads cold HBM rather than the 256 MB Infinity
+Cache, as a many-layer model does (up to 1 GiB of layers are drawn independently, the rest are device
+copies of them at their own addresses).  Inputs are resident in HBM before timing starts.
 
 Prints ONE JSON line.  ``value`` is microseconds per layer-step (lower is better).  ``roofline``
 describes the split-K attention kernel (the stage that moves most bytes): its algorithmic bytes per
@@ -49,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="C2", choices=sorted(DESCR))
-    ap.add_argument("--layers", type=int, default=0, help="distinct layer caches (0: enough for >= 1 GiB)")
+    ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0: see above)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: auto)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -94,13 +95,25 @@ def main():
 
     # ---- layers ----------------------------------------------------------------------------------
     w0 = make_config(args.workload, layer=0)
-    per_layer = 2.35 * w0.k_pages.nbytes  # K + V + INT4 codes + scale/zero + page bounds
-    L = args.layers or max(1, math.ceil((1 << 30) / per_layer))
-    print(f"[bench] {args.workload}: {L} layer(s), {per_layer / 1e6:.0f} MB each", file=sys.stderr, flush=True)
+    # per (page, kv-head): K and V 4 KiB each; INT4 codes 1 KiB, scale/zero 256 B, page bounds 512 B
+    small = 0.4375 * w0.k_pages.nbytes
+    per_layer = 2 * w0.k_pages.nbytes + small
+    # enough layers that the whole rotation exceeds 4 GiB and its codes and bounds alone exceed 1 GiB
+    # (four times the 256 MB Infinity Cache), as in a many-layer model
+    L = args.layers or max(math.ceil((4 << 30) / per_layer), math.ceil((1 << 30) / small))
+    n_drawn = min(L, max(1, math.ceil((1 << 30) / per_layer)))
+    print(f"[bench] {args.workload}: {L} layer(s) ({n_drawn} drawn, the rest device copies), "
+          f"{per_layer / 1e6:.0f} MB each", file=sys.stderr, flush=True)
     layers = []
     for li in range(L):
-        w = w0 if li == 0 else make_config(args.workload, layer=li)
-        t = upload(w, dev)
+        if li < n_drawn:
+            w = w0 if li == 0 else make_config(args.workload, layer=li)
+            t = upload(w, dev)
+        else:
+            # a copy at its own addresses: the same values (so the same work), cold in every cache
+            w, t0 = layers[li % n_drawn][0], layers[li % n_drawn][2]
+            t = dict(t0)
+            t["k_pages"], t["v_pages"] = t0["k_pages"].clone(), t0["v_pages"].clone()
         cache = twl.PagedCache(t["k_pages"], t["v_pages"], t["page_table"], t["seq_lens"], w.num_q_heads,
                                max_seq_len=w.max_seq_len)
         twl.quantize_k(cache, torch.zeros(w.batch, dtype=torch.int32, device=dev), t["seq_lens"], w.max_seq_len)

@@ -113,7 +113,7 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   const int64_t BH = (int64_t)c->batch * c->num_q_heads;
   const int G = c->num_q_heads / c->num_kv_heads;
   L->ncap = ncap;
-  L->chunk_tokens = attn_chunk_tokens(U * ncap);
+  L->chunk_tokens = attn_chunk_tokens(U * ncap, G);
   L->slots = (int)((ncap + L->chunk_tokens - 1) / L->chunk_tokens);
   if (L->slots < 1) L->slots = 1;
   L->max_chunks = U * L->slots;

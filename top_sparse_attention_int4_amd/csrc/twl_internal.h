@@ -97,7 +97,7 @@ hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32
 hipError_t launch_csr_emit(const CacheView& c, const int32_t* union_tok, const int32_t* union_cnt, int ncap,
                            int32_t* indptr, int32_t* tokens, int64_t capacity, hipStream_t s);
 // tokens per attention chunk for an upper bound of the total selected tokens
-int attn_chunk_tokens(int64_t total_upper);
+int attn_chunk_tokens(int64_t total_upper, int group);
 // Kept candidates given as bitmaps over the candidate index space (the top-p output), with the K/V
 // row of every candidate: the attention then reads no compacted list.
 struct MaskView {
