@@ -98,12 +98,13 @@ struct Layout {
 };
 
 // ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
-// to 64; beyond, the wide top-p takes multiples of its 4096-candidate chunk, up to 2^22.  0 = too many.
+// to 64; beyond, the wide top-p takes multiples of 16384 (four of its 4096-candidate chunks per
+// histogram block), up to 2^22.  0 = too many.
 int64_t ncap_of(int64_t maxcand) {
   if (maxcand < 1) maxcand = 1;
   if (maxcand <= kNarrowMaxCands) return (int64_t)topp_elems_per_thread(maxcand) * kToppThreads;
   if (maxcand > kWideMaxCands) return 0;
-  return (maxcand + kWideChunk - 1) / kWideChunk * kWideChunk;
+  return (maxcand + kWideAlign - 1) / kWideAlign * kWideAlign;
 }
 
 bool is_wide(int64_t ncap) { return ncap > kNarrowMaxCands; }

@@ -10,8 +10,8 @@
 //   logit = fl(sm * ((t_0 + t_1) + (t_2 + t_3))).
 // The file is compiled without floating-point contraction so that t_g rounds each product.
 //
-// A block holds 4 batches of 64 candidates x 4 waves; wave g handles group g of every candidate, reading only its
-// 16-byte slice of the code row and its scale/zero pair.  The query values of a wave's group are
+// A block holds 2 or 4 batches of 64 candidates x 4 waves; wave g handles group g of every
+// candidate, reading only its 16-byte slice of the code row and its scale/zero pair.  The query values of a wave's group are
 // wave-uniform and live in scalar registers.  The per-group terms meet in LDS and are combined in the
 // committed order.  The block also records, per candidate, its token id and K/V row index, which the
 // union of the kept sets then gathers without further lookups.
@@ -150,7 +150,7 @@ __device__ __forceinline__ float ub1(uint32_t x) { float r; asm("v_cvt_f32_ubyte
 __device__ __forceinline__ float ub2(uint32_t x) { float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); return r; }
 __device__ __forceinline__ float ub3(uint32_t x) { float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); return r; }
 
-// NB batches of 64 candidates per block (64 * NB candidates, NB a multiple of kGroups / 2 .. 8).
+// NB batches of 64 candidates per block (64 * NB candidates, NB = 2 or 4).
 template <int G, int NB>
 __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
                                                   CandView cand, int ncap, int chunks_per_unit,
@@ -349,10 +349,10 @@ hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t
   return hipGetLastError();
 }
 
-// 8 batches for large steps (and always for the wide top-p, whose per-block maxima region holds
+// 4 batches for large steps (and always for the wide top-p, whose per-block maxima region holds
 // ncap / 256 entries per head), 2 for small ones (more blocks in flight)
 int est_batches(int64_t ncap, int64_t units) {
-  return (ncap > kNarrowMaxCands || ncap * units >= ((int64_t)1 << 19)) ? 8 : 2;
+  return (ncap > kNarrowMaxCands || ncap * units >= ((int64_t)1 << 19)) ? 4 : 2;
 }
 
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
@@ -381,7 +381,7 @@ hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, cons
     break;
   switch (nb) {
     TWL_EST_NB(2)
-    TWL_EST_NB(8)
+    TWL_EST_NB(4)
     default: return hipErrorInvalidValue;
   }
 #undef TWL_EST_G

@@ -15,7 +15,8 @@
 // result on every run.  Truncation costs at most 2^-40 per weight, below 2.4e-7 of Z for 2^18
 // candidates.
 //
-// Kernels, one pass each over the head's candidates (4096 per block):
+// Kernels, one pass each over the head's candidates (the histogram passes take four 4096-candidate
+// chunks per block, the next chunk's loads in flight while one is processed, and flush once):
 //   k_wide_hist1  M from the estimate's per-block maxima; e written over the logits; histogram of bits 30..20
 //   k_wide_hist2  resolve bits 30..20, histogram bits 19..9 inside the chosen bin
 //   k_wide_hist3  resolve bits 19..9, histogram bits 8..0
@@ -32,6 +33,19 @@ namespace {
 constexpr int NT = kWideThreads;
 constexpr int NW = NT / 64;
 constexpr int EPT = kWideChunk / NT;  // candidates per thread
+constexpr int QPT = EPT / 4;            // of them as float4 (the histogram passes read 16 B per lane)
+
+// the thread's candidates of a chunk as float4: candidates 4 (j NT + t) .. + 3
+__device__ __forceinline__ void load_chunk4(const float* x, float (&v)[EPT]) {
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const float4 q = reinterpret_cast<const float4*>(x)[j * NT + threadIdx.x];
+    v[4 * j] = q.x;
+    v[4 * j + 1] = q.y;
+    v[4 * j + 2] = q.z;
+    v[4 * j + 3] = q.w;
+  }
+}
 __device__ __forceinline__ void flush_hist(const uint64_t* h, int nbins, uint64_t* g_fine, uint64_t* g_coarse) {
   for (int i = threadIdx.x; i < nbins; i += NT)
     if (h[i]) atomicAdd((unsigned long long*)&g_fine[i], (unsigned long long)h[i]);
@@ -43,6 +57,16 @@ __device__ __forceinline__ void flush_hist(const uint64_t* h, int nbins, uint64_
   }
 }
 
+// Lane l of each group of 8 lanes holds the keep bits of candidates 4l .. 4l + 3 of a 32-candidate
+// word (bit e for candidate 4l + e); every lane of the group gets the word (bit k <=> candidate k).
+__device__ __forceinline__ uint32_t nibbles_to_word(uint32_t nib) {
+  uint32_t x = nib << (4 * (threadIdx.x & 7));
+  x |= (uint32_t)__shfl_xor((int)x, 1);
+  x |= (uint32_t)__shfl_xor((int)x, 2);
+  x |= (uint32_t)__shfl_xor((int)x, 4);
+  return x;
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kWideThreads) void k_wide_hist1(float* __restrict__ logits, int ncap,
@@ -51,23 +75,33 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist1(float* __restrict__
   __shared__ uint64_t h[2048];
   __shared__ float red[2 * NW * 4];
   BlockReduce<NW> br{red};
-  const int nch = ncap / kWideChunk;
-  const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
-  float* lg = logits + (size_t)bh * ncap + (size_t)ch * kWideChunk;
-  float v[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) v[j] = lg[j * NT + threadIdx.x];  // in flight while M is formed
+  const int nbk = ncap / kWideAlign;
+  const int bh = blockIdx.x / nbk, bk = blockIdx.x - bh * nbk;
+  float* lg = logits + (size_t)bh * ncap + (size_t)bk * kWideAlign;
+  float v[2][EPT];
+  load_chunk4(lg, v[0]);  // in flight while M is formed
   for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
   float m = -__builtin_inff();
   for (int i = threadIdx.x; i < npm; i += NT) m = fmaxf(m, pmax[(size_t)bh * npm + i]);
   const float M = br.max(m);  // (its barrier also orders the clearing of h)
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const float e = (v[j] == -__builtin_inff() || M == -__builtin_inff()) ? -1.f : exp_diff(v[j], M);
-    lg[j * NT + threadIdx.x] = e;
-    if (e >= 0.f) {
-      const uint64_t f = to_fix(e);
-      if (f) atomicAdd((unsigned long long*)&h[__float_as_uint(e) >> 20], (unsigned long long)f);
+  for (int c = 0; c < kWideBlockChunks; ++c) {
+    // the next chunk's logits in flight while this one is weighted
+    if (c + 1 < kWideBlockChunks) load_chunk4(lg + (size_t)(c + 1) * kWideChunk, v[(c + 1) & 1]);
+    float (&x)[EPT] = v[c & 1];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      x[j] = (x[j] == -__builtin_inff() || M == -__builtin_inff()) ? -1.f : exp_diff(x[j], M);
+    float4* out = reinterpret_cast<float4*>(lg + (size_t)c * kWideChunk);
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) out[j * NT + threadIdx.x] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const float e = x[j];
+      if (e >= 0.f) {
+        const uint64_t f = to_fix(e);
+        if (f) atomicAdd((unsigned long long*)&h[__float_as_uint(e) >> 20], (unsigned long long)f);
+      }
     }
   }
   __syncthreads();
@@ -100,13 +134,12 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __rest
                                                              uint64_t* __restrict__ state) {
   __shared__ uint64_t h[2048];
   __shared__ int s_mode, s_b1;
-  const int nch = ncap / kWideChunk;
-  const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
+  const int nbk = ncap / kWideAlign;
+  const int bh = blockIdx.x / nbk, bk = blockIdx.x - bh * nbk;
   uint64_t* st = state + (size_t)bh * kWideStateWords;
-  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
-  float v[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];  // in flight during the resolution
+  const float* x0 = w + (size_t)bh * ncap + (size_t)bk * kWideAlign;
+  float v[2][EPT];
+  load_chunk4(x0, v[0]);  // in flight during the resolution
   for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
   if (threadIdx.x < 64) {
     int mode, b1;
@@ -115,7 +148,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __rest
     if (threadIdx.x == 0) {
       s_mode = mode;
       s_b1 = b1;
-      if (ch == 0) {
+      if (bk == 0) {
         st[kWideSZ] = Z;
         st[kWideSMode] = (uint64_t)mode;
         st[kWideSB1] = (uint64_t)b1;
@@ -127,11 +160,16 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __rest
   if (s_mode != 0) return;
   const uint32_t b1 = (uint32_t)s_b1;
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const uint32_t key = __float_as_uint(v[j]);
-    if (v[j] >= 0.f && (key >> 20) == b1) {
-      const uint64_t f = to_fix(v[j]);
-      if (f) atomicAdd((unsigned long long*)&h[(key >> 9) & 2047u], (unsigned long long)f);
+  for (int c = 0; c < kWideBlockChunks; ++c) {
+    if (c + 1 < kWideBlockChunks) load_chunk4(x0 + (size_t)(c + 1) * kWideChunk, v[(c + 1) & 1]);
+    const float (&x)[EPT] = v[c & 1];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const uint32_t key = __float_as_uint(x[j]);
+      if (x[j] >= 0.f && (key >> 20) == b1) {
+        const uint64_t f = to_fix(x[j]);
+        if (f) atomicAdd((unsigned long long*)&h[(key >> 9) & 2047u], (unsigned long long)f);
+      }
     }
   }
   __syncthreads();
@@ -142,13 +180,12 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist3(const float* __rest
                                                              uint64_t* __restrict__ state) {
   __shared__ uint64_t h[512];
   __shared__ int s_b2;
-  const int nch = ncap / kWideChunk;
-  const int bh = blockIdx.x / nch, ch = blockIdx.x - bh * nch;
+  const int nbk = ncap / kWideAlign;
+  const int bh = blockIdx.x / nbk, bk = blockIdx.x - bh * nbk;
   uint64_t* st = state + (size_t)bh * kWideStateWords;
-  const float* x = w + (size_t)bh * ncap + (size_t)ch * kWideChunk;
-  float v[EPT];
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) v[j] = x[j * NT + threadIdx.x];  // in flight during the resolution
+  const float* x0 = w + (size_t)bh * ncap + (size_t)bk * kWideAlign;
+  float v[2][EPT];
+  load_chunk4(x0, v[0]);  // in flight during the resolution
   if (st[kWideSMode] != 0ull) return;  // uniform over the head's blocks
   for (int i = threadIdx.x; i < 512; i += NT) h[i] = 0ull;
   const uint32_t b1 = (uint32_t)st[kWideSB1];
@@ -158,7 +195,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist3(const float* __rest
     wide_find(st + kWideH2, st + kWideC2, 64, st[kWideSR1], b2, rem2);
     if (threadIdx.x == 0) {
       s_b2 = b2;
-      if (ch == 0) {
+      if (bk == 0) {
         st[kWideSB2] = (uint64_t)b2;
         st[kWideSR2] = rem2;
       }
@@ -167,11 +204,16 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist3(const float* __rest
   __syncthreads();
   const uint32_t pre = (b1 << 11) | (uint32_t)s_b2;
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const uint32_t key = __float_as_uint(v[j]);
-    if (v[j] >= 0.f && (key >> 9) == pre) {
-      const uint64_t f = to_fix(v[j]);
-      if (f) atomicAdd((unsigned long long*)&h[key & 511u], (unsigned long long)f);
+  for (int c = 0; c < kWideBlockChunks; ++c) {
+    if (c + 1 < kWideBlockChunks) load_chunk4(x0 + (size_t)(c + 1) * kWideChunk, v[(c + 1) & 1]);
+    const float (&x)[EPT] = v[c & 1];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const uint32_t key = __float_as_uint(x[j]);
+      if (x[j] >= 0.f && (key >> 9) == pre) {
+        const uint64_t f = to_fix(x[j]);
+        if (f) atomicAdd((unsigned long long*)&h[key & 511u], (unsigned long long)f);
+      }
     }
   }
   __syncthreads();
@@ -192,14 +234,24 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const size_t bh0 = (size_t)b * c.Hq + (size_t)h * G;
+  // every weight of the chunk in flight before the thresholds are resolved (thread t holds
+  // candidates 4 (j NT + t) .. + 3 of round j)
+  float4 x[QPT][G];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+      x[j][hh] = reinterpret_cast<const float4*>(w + (bh0 + hh) * ncap + (size_t)ch * kWideChunk)[j * NT + threadIdx.x];
   for (int hh = wv; hh < G; hh += NW) {
     uint64_t* st = state + (bh0 + hh) * kWideStateWords;
+    // the resolved state of the passes before, read together
+    const uint64_t mode = st[kWideSMode], sb1 = st[kWideSB1], sb2 = st[kWideSB2], sr2 = st[kWideSR2];
     uint32_t T = 0u;
-    if (st[kWideSMode] == 0ull) {
+    if (mode == 0ull) {
       int b3;
       uint64_t rem3;
-      wide_find(st + kWideH3, st + kWideC3, 16, st[kWideSR2], b3, rem3);
-      T = ((uint32_t)st[kWideSB1] << 20) | ((uint32_t)st[kWideSB2] << 9) | (uint32_t)b3;
+      wide_find(st + kWideH3, st + kWideC3, 16, sr2, b3, rem3);
+      T = ((uint32_t)sb1 << 20) | ((uint32_t)sb2 << 9) | (uint32_t)b3;
       if (iters < 31) T &= ~((1u << (31 - iters)) - 1u);
     }
     if (lane == 0) {
@@ -220,32 +272,30 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
   for (int hh = 0; hh < G; ++hh) kept[hh] = 0ull;
   int cnt = 0;
   const int MW = ncap / 32;
-  for (int j = 0; j < EPT; ++j) {
-    const int k = ch * kWideChunk + j * NT + (int)threadIdx.x;
-    const int wd = (ch * kWideChunk + j * NT + wv * 64) >> 5;  // first of the wave's two words
-    float x[G];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) x[hh] = w[(bh0 + hh) * ncap + k];
-    bool any = false;
+  for (int j = 0; j < QPT; ++j) {
+    const int wbase = (ch * kWideChunk + 4 * (j * NT + wv * 64)) >> 5;  // first of the wave's 8 words
+    const int wd = wbase + (lane >> 3);
+    uint32_t unib = 0u;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      const bool keep = x[hh] >= 0.f && x[hh] >= thr[hh];
-      any |= keep;
-      if (keep) kept[hh] += to_fix(x[hh]);
+      const float xs[4] = {x[j][hh].x, x[j][hh].y, x[j][hh].z, x[j][hh].w};
+      uint32_t nib = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool keep = xs[e] >= 0.f && xs[e] >= thr[hh];
+        if (keep) kept[hh] += to_fix(xs[e]);
+        nib |= (keep ? 1u : 0u) << e;
+      }
+      unib |= nib;
       if (head_mask) {
-        const unsigned long long bal = __ballot(keep);
-        if (lane == 0) {
-          if (wd < mask_words) head_mask[(bh0 + hh) * mask_words + wd] = (uint32_t)bal;
-          if (wd + 1 < mask_words) head_mask[(bh0 + hh) * mask_words + wd + 1] = (uint32_t)(bal >> 32);
-        }
+        const uint32_t word = nibbles_to_word(nib);
+        if ((lane & 7) == 0 && wd < mask_words) head_mask[(bh0 + hh) * mask_words + wd] = word;
       }
     }
-    const unsigned long long ub = __ballot(any);
-    cnt += __popcll(ub);
-    if (lane == 0) {
-      uwords[(size_t)u * MW + wd] = (uint32_t)ub;
-      uwords[(size_t)u * MW + wd + 1] = (uint32_t)(ub >> 32);
-    }
+    cnt += __popc(unib);
+    const uint32_t uword = nibbles_to_word(unib);
+    if ((lane & 7) == 0) uwords[(size_t)u * MW + wd] = uword;
   }
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
@@ -253,6 +303,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
     if (lane == 0 && s) atomicAdd((unsigned long long*)&state[(bh0 + hh) * kWideStateWords + kWideMass],
                                   (unsigned long long)s);
   }
+  cnt = wave_sum_int(cnt);
   if (lane == 0) s_cnt[wv] = cnt;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -324,7 +375,8 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits,
                             float* threshold, uint32_t* head_mask, int mask_words, hipStream_t s) {
   if (ncap % kWideChunk) return hipErrorInvalidValue;
   const int nch = ncap / kWideChunk;
-  const unsigned hgrid = (unsigned)(c.B * c.Hq * nch), ugrid = (unsigned)(c.B * c.Hkv * nch);
+  if (ncap % kWideAlign) return hipErrorInvalidValue;
+  const unsigned hgrid = (unsigned)(c.B * c.Hq * (ncap / kWideAlign)), ugrid = (unsigned)(c.B * c.Hkv * nch);
   const dim3 blk(kWideThreads);
   const int npm = ncap / (64 * est_batches(ncap, (int64_t)c.B * c.Hkv));
   hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, npm, wd.state);

@@ -37,8 +37,10 @@ struct CandView {
 // Wide top-p (more than 65536 candidates per head): per-head state in 64-bit words -- the three
 // histogram levels (fine bins, then one coarse sum per 32 bins), the kept mass, and the resolved
 // search state.  Words [0, kWideZeroWords) must be zero before the first histogram pass.
-constexpr int kWideChunk = 4096;  // candidates per block of the wide kernels
+constexpr int kWideChunk = 4096;  // candidates per chunk of the wide kernels
 constexpr int kWideThreads = 256;
+constexpr int kWideBlockChunks = 4;  // chunks per block of the histogram passes (software-pipelined)
+constexpr int kWideAlign = kWideChunk * kWideBlockChunks;  // wide candidate capacities are multiples
 constexpr int kWideH1 = 0, kWideC1 = 2048, kWideH2 = 2112, kWideC2 = 4160, kWideH3 = 4224, kWideC3 = 4736;
 constexpr int kWideMass = 4752, kWideZeroWords = 4753;
 constexpr int kWideSZ = 4753, kWideSMode = 4754, kWideSB1 = 4755, kWideSR1 = 4756, kWideSB2 = 4757,
