@@ -8,24 +8,32 @@ Two versions of O5 are given:
 
 * ``logits_f64`` -- the plain definition: l_i = sm * sum_c q_c * x^_ic in float64, with x^ the fp32
   dequantised key (see ``quantize.dequantize``).
-* ``logits_spec`` -- the float32 evaluation order the GPU kernel commits to.  A top-p *set* is decided
-  from these logits, so both sides must hold the same values; the pages leave the arithmetic open
-  (their kernel dequantises to FP16), so the reading taken is fp32 with this fixed order:
+* ``logits_spec`` -- the arithmetic the GPU kernel commits to.  A top-p *set* is decided from these
+  logits, so both sides must hold the same values.  The pages fix only the estimator's precision
+  (fp16 queries against INT4 keys) and leave the arithmetic open; the reading taken holds the query
+  per head and 32-channel group g in fixed point at least as fine as fp16 for the group's large
+  channels, so that every group sum is exact:
 
-      per group g (32 channels) and head h:
-          a_g = fold_{c in g, ascending} (a + q_c * code_c)     starting at +0; products are exact
-          b_g = fold_{c in g, ascending} (b + q_c)              starting at +0
-          t_g = fl(s_g * a_g) + fl(z_g * b_g)                   three rounded fp32 operations
+      E_g = floor(log2 max_{c in g} |q_c|)  (clamped to >= -100; 0 for an all-zero group)
+      Q_c = rne(q_c * 2^(13 - E_g))           integers, |Q_c| <= 16320; exact for every channel
+                                              within 2^6 of the group's largest (bf16 has 8 bits)
+      a_g = 2^(E_g - 13) * sum_{c in g} Q_c * code_c     exact (|sum| < 2^23, a float32 integer)
+      b_g = 2^(E_g - 13) * sum_{c in g} Q_c              exact
+      t_g = fl(s_g * a_g) + fl(z_g * b_g)                three rounded fp32 operations
       r = (t_0 + t_1) + (t_2 + t_3);   l = fl(sm * r)
 
-  which equals the plain definition exactly in real arithmetic (x^ = code*s + z factorises per
-  group) and is pinned to ``logits_f64`` within a derived float32 error bound.
+  which is sm * q~ . x^ for the fixed-point query q~ (|q - q~| <= 2^(E_g - 14) per channel, below
+  half an fp16 ulp of the group's largest channel) and is pinned to ``logits_f64`` within the bound
+  that this rounding and the float32 operation count imply.  The exact integer sums are what an
+  int8 matrix-core contraction computes, in any order.
 
 O6 normalises over the candidates only (the selector's output is the domain of the top-p pruning,
 Paper-Notes "整体框架"), in float64 from the given logits with the maximum subtracted.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -35,37 +43,43 @@ from .quantize import dequantize
 GROUP = 32
 
 
-def group_qsums(q: np.ndarray) -> np.ndarray:
-    """b_g = float32 fold of q over each 32-channel group."""
-    out = np.zeros(4, F32)
+QFIX_BITS = 13  # Q_c = rne(q_c * 2^(QFIX_BITS - E_g))
+E_MIN = -100
+
+
+def q_fixed(q: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Fixed-point query per 32-channel group: (Q int64 [128], E int64 [4]) as defined above."""
+    q = np.asarray(q, np.float64)
+    Q = np.zeros(128, np.int64)
+    E = np.zeros(4, np.int64)
     for g in range(4):
-        acc = F32(0.0)
-        for c in range(g * GROUP, (g + 1) * GROUP):
-            acc = F32(acc + q[c])
-        out[g] = acc
-    return out
+        seg = q[g * GROUP:(g + 1) * GROUP]
+        m = float(np.abs(seg).max())
+        if m == 0.0:
+            continue
+        E[g] = max(math.frexp(m)[1] - 1, E_MIN)  # m = f * 2^e with f in [0.5, 1): floor(log2 m) = e - 1
+        Q[g * GROUP:(g + 1) * GROUP] = np.rint(np.ldexp(seg, QFIX_BITS - int(E[g]))).astype(np.int64)
+    return Q, E
 
 
 def logits_spec(qbits_h: np.ndarray, codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray,
                 sm: float) -> np.ndarray:
-    """float32 logits in the committed evaluation order (see module docstring).
+    """float32 logits in the committed arithmetic (see module docstring).
 
     ``qbits_h`` uint16 [128]; ``codes`` uint8 [N][128]; ``scale16``/``zero16`` float16 [N][4];
     ``sm`` the float32 softmax scale.
     """
-    q = bf16_to_f32(qbits_h)
-    c = np.asarray(codes).astype(F32)
+    Q, E = q_fixed(bf16_to_f32(qbits_h))
+    c = np.asarray(codes).astype(np.int64)
     s = np.asarray(scale16, np.float16).astype(F32)
     z = np.asarray(zero16, np.float16).astype(F32)
-    bsum = group_qsums(q)
-    N = c.shape[0]
     t = []
     for g in range(4):
-        a = np.zeros(N, F32)
-        for ch in range(g * GROUP, (g + 1) * GROUP):
-            a = (a + (q[ch] * c[:, ch]).astype(F32)).astype(F32)
+        sl = slice(g * GROUP, (g + 1) * GROUP)
+        a = np.ldexp((c[:, sl] @ Q[sl]).astype(np.float64), int(E[g]) - QFIX_BITS).astype(F32)  # exact
+        b = F32(np.ldexp(float(Q[sl].sum()), int(E[g]) - QFIX_BITS))                                # exact
         sa = (s[:, g] * a).astype(F32)
-        zb = (z[:, g] * bsum[g]).astype(F32)
+        zb = (z[:, g] * b).astype(F32)
         t.append((sa + zb).astype(F32))
     r = ((t[0] + t[1]).astype(F32) + (t[2] + t[3]).astype(F32)).astype(F32)
     return (F32(sm) * r).astype(F32)

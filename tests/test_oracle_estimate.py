@@ -1,10 +1,13 @@
 """Pins for O5 (INT4 logit estimate) and O6 (softmax weights).
 
-* The committed float32 order (``logits_spec``) agrees with the float64 definition (``logits_f64``)
-  within the error bound that the float32 operation count implies (derived below); a dropped or
-  mis-signed term in the factorised form misses that bound by orders of magnitude.
-* Special case: keys already on the INT4 grid dequantise to themselves, so the estimate equals the
-  exact bf16 attention logits (float64 dot product) within the same bound.
+* The fixed-point query meets its definition's guarantees: |Q| <= 16320, channels within 2^6 of their
+  group's largest magnitude are held exactly, every channel within half a grid step, and the group
+  exponent brackets the largest magnitude (computed here with log2, independently of the oracle).
+* The committed arithmetic (``logits_spec``) agrees with the float64 definition (``logits_f64``)
+  within the error bound that the query rounding and the float32 operation count imply (derived
+  below); a dropped or mis-signed term, or a group scale off by a power of two, misses that bound.
+* Special case: a query on the fixed-point grid and keys already on the INT4 grid make the estimate
+  the exact bf16 attention logit up to the final float32 roundings alone.
 * Softmax: non-negative, sums to one, invariant under a common shift of the logits, and equal to
   scipy's softmax.
 """
@@ -21,29 +24,74 @@ U = 2.0**-24
 SM = float(np.float32(1 / math.sqrt(128)))
 
 
-def _bound(qbits, codes, s16, z16, xhat, logits):
-    """|spec - f64| <= sm * (34u * sum_g (|s_g| sum|q c| + |z_g| sum|q|) + u sum|q||x^|) + 2u|l|.
+def _group_exponents(q):
+    """floor(log2 max |q|) per 32-channel group, clamped to >= -100 (0 for an all-zero group)."""
+    m = np.abs(np.asarray(q, np.float64)).reshape(4, 32).max(-1)
+    return np.array([max(int(np.floor(np.log2(x))), -100) if x > 0 else 0 for x in m])
 
-    Derivation: each group sum a_g, b_g is a 32-term float32 fold (error <= 31u * sum of |terms|);
-    t_g adds two rounded products and a rounded sum (<= 2u relative each); r adds two levels of
-    rounded sums; l rounds once more; the float64 reference itself uses x^ rounded to fp32 once per
-    element (<= u |x^|).  34u covers 31u + the three further roundings of each group's terms.
+
+def _bound(qbits, codes, s16, z16, xhat, logits):
+    """|spec - f64| <= sm * (sum_c 2^(E_g - 14) |x^_c| (1 + u) + 5u sum_g (|s_g a_g| + |z_g b_g|)
+                             + u sum_c |q_c| |x^_c|) + 2u |l|.
+
+    Derivation: spec in exact arithmetic is sm * sum_c q~_c x_c with |q_c - q~_c| <= 2^(E_g - 14)
+    (half a grid step) and x_c = code_c s_g + z_g, whose float32 rounding x^_c is what the float64
+    reference uses (<= u |x^_c|).  a_g and b_g are exact; t_g rounds two products and their sum
+    (<= 2u (|s_g a_g| + |z_g b_g|)); r adds two levels of rounded sums (<= 2u of the same terms);
+    l rounds once more (<= u |l|, doubled for the reference's own rounding).  5u covers 4u plus the
+    second-order terms.
     """
-    q = np.abs(numerics.bf16_to_f32(qbits).astype(np.float64)).reshape(1, 4, 32)
+    q = numerics.bf16_to_f32(qbits).astype(np.float64)
+    E = _group_exponents(q)
+    step = np.repeat(2.0 ** (E - 14), 32)  # half a grid step per channel
+    qa = np.abs(q).reshape(1, 4, 32)
     c = codes.astype(np.float64).reshape(-1, 4, 32)
     s = np.abs(s16.astype(np.float64))
     z = np.abs(z16.astype(np.float64))
-    terms = (s * (q * c).sum(-1) + z * q.sum(-1)).sum(-1)
-    xq = (np.abs(xhat.astype(np.float64)) * q.reshape(1, 128)).sum(-1)
-    return SM * (34 * U * terms + U * xq) + 2 * U * np.abs(logits)
+    terms = (s * (qa * c).sum(-1) + z * qa.sum(-1)).sum(-1) * (1 + 2.0**-13)
+    xa = np.abs(xhat.astype(np.float64))
+    quant = (xa * step.reshape(1, 128)).sum(-1) * (1 + U)
+    xq = (xa * np.abs(q).reshape(1, 128)).sum(-1)
+    return SM * (quant + 5 * U * terms + U * xq) + 2 * U * np.abs(logits)
 
 
-@pytest.mark.parametrize("seed,kscale,qscale", [(0, 1, 1), (1, 8, 1), (2, 1, 3.5), (3, 0.02, 0.05)])
-def test_spec_order_matches_float64_definition(seed, kscale, qscale):
+def _qvec(rng, scales):
+    """A bf16 query whose four groups have the given magnitudes (0 gives an all-zero group)."""
+    q = np.concatenate([rng.standard_normal(32) * sc for sc in scales]).astype(np.float32)
+    return numerics.f32_to_bf16_bits(q)
+
+
+QCASES = [(0, 1, (1, 1, 1, 1)), (1, 8, (1, 1, 1, 1)), (2, 1, (3.5, 3.5, 3.5, 3.5)), (3, 0.02, (0.05,) * 4),
+          (4, 1, (1e-3, 1, 100, 0)), (5, 3, (2.0**-90, 1e-30, 7, 0.25)), (6, 1, (2.0**-110, 1, 0.5, 2))]
+
+
+@pytest.mark.parametrize("seed,kscale,qscales", QCASES)
+def test_fixed_point_query_guarantees(seed, kscale, qscales):
+    rng = np.random.default_rng(seed)
+    q = numerics.bf16_to_f32(_qvec(rng, qscales)).astype(np.float64)
+    Q, E = estimate.q_fixed(q)
+    assert E.tolist() == _group_exponents(q).tolist()
+    assert np.abs(Q).max() <= 16320
+    for g in range(4):
+        seg, Qg = q[32 * g:32 * g + 32], Q[32 * g:32 * g + 32]
+        m = np.abs(seg).max()
+        if m == 0:
+            assert not Qg.any()
+            continue
+        if E[g] > -100:
+            assert 2.0 ** E[g] <= m < 2.0 ** (E[g] + 1)
+        back = np.ldexp(Qg.astype(np.float64), int(E[g]) - 13)
+        assert np.all(np.abs(back - seg) <= 2.0 ** (int(E[g]) - 14))
+        big = np.abs(seg) >= 2.0 ** (int(E[g]) - 6)
+        assert np.array_equal(back[big], seg[big])
+
+
+@pytest.mark.parametrize("seed,kscale,qscales", QCASES)
+def test_spec_matches_float64_definition(seed, kscale, qscales):
     rng = np.random.default_rng(seed)
     n = 3000
     kbits = numerics.f32_to_bf16_bits((rng.standard_normal((n, 128)) * kscale).astype(np.float32))
-    qbits = numerics.f32_to_bf16_bits((rng.standard_normal(128) * qscale).astype(np.float32))
+    qbits = _qvec(rng, qscales)
     qz = quantize.quantize_rows(kbits)
     spec = estimate.logits_spec(qbits, qz["codes"], qz["scale"], qz["zero"], SM).astype(np.float64)
     ref = estimate.logits_f64(qbits, qz["codes"], qz["scale"], qz["zero"], SM)
@@ -53,11 +101,27 @@ def test_spec_order_matches_float64_definition(seed, kscale, qscale):
     # the bound is tight enough to catch a dropped zero-point term
     q = numerics.bf16_to_f32(qbits).astype(np.float64)
     z = qz["zero"].astype(np.float64)
-    dropped = ref - SM * (z * q.reshape(4, 32).sum(-1)).sum(-1)
-    assert np.mean(np.abs(dropped - ref) > bound) > 0.9
+    zterm = SM * (z * q.reshape(4, 32).sum(-1)).sum(-1)
+    live = np.abs(zterm) > 4 * bound
+    assert live.mean() > 0.5 and np.all(np.abs((ref - zterm) - ref)[live] > bound[live])
 
 
-def test_keys_on_grid_give_exact_bf16_logits():
+def test_scale_exponent_error_would_be_caught():
+    # the same logits with one group's contribution off by a factor 2 miss the bound
+    rng = np.random.default_rng(11)
+    n = 1000
+    kbits = numerics.f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32))
+    qbits = _qvec(rng, (1, 1, 1, 1))
+    qz = quantize.quantize_rows(kbits)
+    ref = estimate.logits_f64(qbits, qz["codes"], qz["scale"], qz["zero"], SM)
+    xhat = quantize.dequantize(qz["codes"], qz["scale"], qz["zero"]).astype(np.float64)
+    q = numerics.bf16_to_f32(qbits).astype(np.float64)
+    g1 = SM * (xhat[:, 32:64] @ q[32:64])
+    bound = _bound(qbits, qz["codes"], qz["scale"], qz["zero"], xhat, ref)
+    assert np.mean(np.abs(g1) > bound) > 0.9
+
+
+def test_grid_query_and_grid_keys_give_exact_bf16_logits():
     rng = np.random.default_rng(7)
     n = 2048
     codes = rng.integers(0, 16, size=(n, 4, 32))
@@ -66,17 +130,21 @@ def test_keys_on_grid_give_exact_bf16_logits():
     z16 = (rng.integers(-32, 32, size=(n, 4)) * s16.astype(np.float64)).astype(np.float16)
     x = codes * s16.astype(np.float64)[..., None] + z16.astype(np.float64)[..., None]
     kbits = numerics.f32_to_bf16_bits(x.reshape(n, 128).astype(np.float32))
-    qbits = numerics.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32))
+    # every channel within 2^6 of its group's largest magnitude: held exactly in fixed point
+    scale = (2.0 ** np.array([-2, 0, 1, 2])).repeat(32)
+    q = rng.choice([-1, 1], 128) * rng.uniform(0.02, 0.99, 128) * scale
+    q[::32] = 0.999 * scale[::32]  # each group's largest magnitude, pinning its exponent
+    qbits = numerics.f32_to_bf16_bits(q.astype(np.float32))
     qz = quantize.quantize_rows(kbits)
     spec = estimate.logits_spec(qbits, qz["codes"], qz["scale"], qz["zero"], SM).astype(np.float64)
     exact = SM * (numerics.bf16_to_f32(kbits).astype(np.float64) @ numerics.bf16_to_f32(qbits).astype(np.float64))
-    bound = _bound(qbits, qz["codes"], qz["scale"], qz["zero"], x.reshape(n, 128), exact)
-    assert np.all(np.abs(spec - exact) <= bound)
-
-
-def test_group_sums_are_the_channel_sums():
-    q = np.arange(128, dtype=np.float32) * np.float32(0.5)
-    assert estimate.group_qsums(q).tolist() == [0.5 * sum(range(g * 32, g * 32 + 32)) for g in range(4)]
+    qq = numerics.bf16_to_f32(qbits).astype(np.float64)
+    Q, E = estimate.q_fixed(qq)
+    assert np.array_equal(np.ldexp(Q.astype(np.float64), np.repeat(E - 13, 32)), qq)
+    xa = np.abs(x.reshape(n, 128))
+    terms = (xa * np.abs(qq)).sum(-1)
+    # only t_g, r and l round: <= sm * 5u * sum|q x| + 2u |l|
+    assert np.all(np.abs(spec - exact) <= SM * 5 * U * terms + 2 * U * np.abs(exact))
 
 
 def test_softmax_properties():
