@@ -1,20 +1,21 @@
 // INT4 weight estimate: the mixed-precision SpGEMV of the query against the dequantised 4-bit keys
-// (paperlayer §4.2; §B.1, Fig. 12).  One lane per candidate token and quantisation group, the GQA
-// group's G query heads in the same lane so each code byte and scale/zero pair is read once.
+// (paperlayer §4.2; §B.1, Fig. 12) as an int8 matrix-core contraction.
 //
-// Per head and 32-channel group g the logit is factorised exactly as
-//   sum_{c in g} q_c (code_c s_g + z_g) = s_g * a_g + z_g * b_g,  a_g = sum q_c code_c,  b_g = sum q_c
-// and evaluated in this fixed float32 order (the products q_c*code_c are exact, so the fused
-// multiply-adds are plain rounded additions):
-//   a_g = fold_{c in g}(a + q_c*code_c),  t_g = fl(s_g*a_g) + fl(z_g*b_g),
-//   logit = fl(sm * ((t_0 + t_1) + (t_2 + t_3))).
+// Per head and 32-channel group g the query is held in fixed point, Q_c = rne(q_c 2^(13 - E_g)) with
+// E_g = floor(log2 max |q_c|) (|Q_c| <= 16320; exact for channels within 2^6 of the largest), so
+//   sum_{c in g} q~_c (code_c s_g + z_g) = s_g a_g + z_g b_g,  a_g = 2^(E_g-13) sum Q_c code_c,
+//   b_g = 2^(E_g-13) sum Q_c
+// has exact group sums (|sum| < 2^23) in any order; then
+//   t_g = fl(s_g a_g) + fl(z_g b_g),  logit = fl(sm * ((t_0 + t_1) + (t_2 + t_3))).
 // The file is compiled without floating-point contraction so that t_g rounds each product.
 //
-// A block holds 2 or 4 batches of 64 candidates x 4 waves; wave g handles group g of every
-// candidate, reading only its 16-byte slice of the code row and its scale/zero pair.  The query values of a wave's group are
-// wave-uniform and live in scalar registers.  The per-group terms meet in LDS and are combined in the
-// committed order.  The block also records, per candidate, its token id and K/V row index, which the
-// union of the kept sets then gathers without further lookups.
+// The sums are v_mfma_i32_16x16x32_i8 products: A = 16 candidates x 32 code nibbles (lane (r, kb)
+// reads the 16 code bytes of group kb of candidate r with one load and feeds 8 of them to each of
+// four MFMAs), B = the query digits (Q = 128 hi + lo, both int8), one column per (group, head) and
+// zero outside the lane's group, so each output column accumulates one group of one head.  A wave
+// takes 16-candidate tiles; the four groups of a (candidate, head) then meet by two lane exchanges
+// in the committed order.  The block also records, per candidate, its token id and K/V row index,
+// which the union of the kept sets then gathers without further lookups.
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -144,13 +145,9 @@ __device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView&
   if (tok >= 0) row = (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15);
 }
 
-// Byte n of x as a float (one conversion instruction each).
-__device__ __forceinline__ float ub0(uint32_t x) { float r; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ub1(uint32_t x) { float r; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ub2(uint32_t x) { float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ub3(uint32_t x) { float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); return r; }
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-// NB batches of 64 candidates per block (64 * NB candidates, NB = 2 or 4).
+// NB batches of 64 candidates per block (64 * NB candidates, NB = 2 or 4): 4 NB tiles of 16, NB per wave.
 template <int G, int NB>
 __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
                                                   CandView cand, int ncap, int chunks_per_unit,
@@ -158,14 +155,20 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
                                                   int32_t* __restrict__ cand_row, float* __restrict__ pmax,
                                                   uint64_t* __restrict__ wstate, size_t wstate_words) {
   constexpr int NC = 64 * NB;
-  constexpr int NH = (G + kGroups - 1) / kGroups;  // heads combined per wave
+  constexpr int GT = G < 4 ? G : 4;  // heads per 16-column MFMA tile (4 groups x GT heads)
+  constexpr int NTL = G / GT;        // column tiles
   const int u = blockIdx.x / chunks_per_unit;
   const int ck = blockIdx.x - u * chunks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  const int g = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  __shared__ float T[2][kGroups][G][64];
   __shared__ int s_row[NB][64];
+  // query digits (Q = 128 [0] + [1]), channel 8j + w of a group at byte 8j + perm(w), the order in
+  // which the nibbles of 4 code bytes are unpacked (low nibbles of bytes 0..3, then high nibbles)
+  __shared__ __align__(8) int8_t s_qd[2][G][kD];
+  __shared__ int s_qe[G][kGroups];   // group exponents E_g
+  __shared__ float s_qb[G][kGroups]; // b_g
+  __shared__ float s_max[4][G];
   if (wstate) {
     // clear the wide top-p state for the passes that follow this kernel
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < wstate_words; i += (size_t)gridDim.x * 256)
@@ -174,6 +177,15 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int cnt = (cand.mode == kCandAll) ? 0 : clampi(cand.count[u], 0, cand.max_items);
   const int k0 = ck * NC;
+  // the query channels this lane turns into fixed point (half a wave per (head, group)), read first
+  constexpr int QP = (kGroups * G + 7) / 8;  // (head, group) pairs per half-wave
+  float qx[QP];
+#pragma unroll
+  for (int i = 0; i < QP; ++i) {
+    const int pr = 2 * wv + (lane >> 5) + 8 * i;
+    const int hh = min(pr >> 2, G - 1), g = pr & 3;
+    qx[i] = __uint_as_float((uint32_t)q[((size_t)b * c.Hq + (size_t)h * G + hh) * kD + g * 32 + (lane & 31)] << 16);
+  }
 
   // ---- candidate resolution: wave w resolves batches w, w + 4, ... (token id and K/V row); the
   // rows meet in LDS so each is resolved once
@@ -198,7 +210,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       }
     }
     __syncthreads();
-    for (int bt = g; bt < NB; bt += kGroups) {
+    for (int bt = wv; bt < NB; bt += kGroups) {
       const int k = k0 + 64 * bt + lane;
       int t = -1;
       if (nr >= 1 && k < tot) {
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       cand_row[(size_t)u * ncap + k] = row;
     }
   } else {
-    for (int bt = g; bt < NB; bt += kGroups) {
+    for (int bt = wv; bt < NB; bt += kGroups) {
       const int k = k0 + 64 * bt + lane;
       int tok, row;
       cand_resolve(c, cand, u, b, h, k, n, cnt, tok, row);
@@ -242,102 +254,128 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   }
   __syncthreads();
 
-  // ---- this wave's group of every candidate: code and scale/zero loads all in flight together
-  int rowv[NB];
-  uint4 cwv[NB];
-  uint32_t mwv[NB];
+  // ---- this wave's tiles (wv, wv + 4, ...): code and scale/zero loads all in flight together
+  const int kb = lane >> 4, nn = lane & 15, rg = lane >> 4;
+  const int gc = nn / GT, hl = nn - gc * GT;
+  const bool colok = nn < kGroups * GT;
+  uint4 cw[NB];
+  uint32_t mw[NB][4];
+  int rw[NB][4];
 #pragma unroll
-  for (int bt = 0; bt < NB; ++bt) rowv[bt] = s_row[bt][lane];
+  for (int i = 0; i < NB; ++i) {
+    const int ti = wv + 4 * i;
+    const int ra = (&s_row[0][0])[16 * ti + nn];
+    cw[i] = reinterpret_cast<const uint4*>(c.k4 + (size_t)max(ra, 0) * 64)[kb];
 #pragma unroll
-  for (int bt = 0; bt < NB; ++bt) {
-    if (rowv[bt] >= 0) {
-      cwv[bt] = reinterpret_cast<const uint4*>(c.k4 + (size_t)rowv[bt] * 64)[g];
-      mwv[bt] = c.k4_meta[(size_t)rowv[bt] * kGroups + g];
-    } else {
-      cwv[bt] = make_uint4(0u, 0u, 0u, 0u);
-      mwv[bt] = 0u;
+    for (int e = 0; e < 4; ++e) {
+      rw[i][e] = (&s_row[0][0])[16 * ti + 4 * rg + e];
+      mw[i][e] = c.k4_meta[(size_t)max(rw[i][e], 0) * kGroups + (gc & 3)];
     }
   }
 
-  // this wave's 32 query channels per head, as bf16 pairs (wave-uniform: scalar loads)
-  const uint32_t* qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * c.Hq + (size_t)h * G) * kD) + g * 16;
-  float bsum[G];
+  // ---- the fixed-point query, while those loads are in flight
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    float acc = 0.f;
+  for (int i = 0; i < QP; ++i) {
+    const int pr = 2 * wv + (lane >> 5) + 8 * i;
+    if (pr < kGroups * G) {  // uniform over each half-wave; the shuffles stay inside it
+      const int hh = pr >> 2, g = pr & 3, cl = lane & 31;
+      const float x = qx[i];
+      float m = fabsf(x);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t w = qw[hh * 64 + i];
-      acc = acc + bf16_lo(w);
-      acc = acc + bf16_hi(w);
+      for (int s = 1; s < 32; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 32));
+      int E = 0;
+      if (m > 0.f) E = max((int)(__float_as_uint(m) >> 23) - 127, -100);
+      const int Qv = (int)rintf(ldexpf(x, 13 - E));
+      const int w = cl & 7, pos = g * 32 + (cl & ~7) + ((w & 1) ? 4 + (w >> 1) : (w >> 1));
+      s_qd[0][hh][pos] = (int8_t)(Qv >> 7);   // floor(Q / 128), in [-128, 127]
+      s_qd[1][hh][pos] = (int8_t)(Qv & 127);  // Q - 128 floor(Q / 128)
+      int qs = Qv;
+#pragma unroll
+      for (int s = 1; s < 32; s <<= 1) qs += __shfl_xor(qs, s, 32);
+      if (cl == 0) {
+        s_qe[hh][g] = E;
+        s_qb[hh][g] = ldexpf((float)qs, E - 13);  // exact: |sum Q| < 2^19
+      }
     }
-    bsum[hh] = acc;
   }
+  __syncthreads();
 
-  float mx[NH];  // running maxima of this wave's heads (pmax)
+  // ---- B operands, the same in every wave: lane (kb, nn) holds column nn = (group gc, head ct GT + hl)
+  long Bop[NTL][2][4];
+  int ecol[NTL];
+  float bcol[NTL];
 #pragma unroll
-  for (int i = 0; i < NH; ++i) mx[i] = -__builtin_inff();
+  for (int ct = 0; ct < NTL; ++ct) {
+    const int hh = ct * GT + hl;
 #pragma unroll
-  for (int bt = 0; bt < NB; ++bt) {
-    const int k = k0 + 64 * bt + lane;
-    if (rowv[bt] >= 0) {
-      // the group's 32 codes as floats (element 2j of byte j is its low nibble)
-      const uint32_t words[4] = {cwv[bt].x, cwv[bt].y, cwv[bt].z, cwv[bt].w};
-      float code[32];
+    for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int wi = 0; wi < 4; ++wi) {
-        const uint32_t lo = words[wi] & 0x0F0F0F0Fu;
-        const uint32_t hi = (words[wi] >> 4) & 0x0F0F0F0Fu;
-        code[8 * wi + 0] = ub0(lo);
-        code[8 * wi + 1] = ub0(hi);
-        code[8 * wi + 2] = ub1(lo);
-        code[8 * wi + 3] = ub1(hi);
-        code[8 * wi + 4] = ub2(lo);
-        code[8 * wi + 5] = ub2(hi);
-        code[8 * wi + 6] = ub3(lo);
-        code[8 * wi + 7] = ub3(hi);
-      }
-      const float s = half_bits_to_float(mwv[bt] & 0xffffu);
-      const float z = half_bits_to_float(mwv[bt] >> 16);
+      for (int j = 0; j < 4; ++j)
+        Bop[ct][d][j] = (colok && kb == gc) ? *reinterpret_cast<const long*>(&s_qd[d][hh][32 * kb + 8 * j]) : 0l;
+    ecol[ct] = colok ? s_qe[hh][gc] : 0;
+    bcol[ct] = colok ? s_qb[hh][gc] : 0.f;
+  }
+  float mx[NTL];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        // head-outer order keeps only one head's 32 query values in scalar registers at a time
-        float a = 0.f;
+  for (int ct = 0; ct < NTL; ++ct) mx[ct] = -__builtin_inff();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t w = qw[hh * 64 + i];  // channels 32g + 2i, 2i + 1
-          a = fmaf(bf16_lo(w), code[2 * i], a);
-          a = fmaf(bf16_hi(w), code[2 * i + 1], a);
-        }
-        const float sa = s * a;
-        const float zb = z * bsum[hh];
-        T[bt & 1][g][hh][lane] = sa + zb;
-      }
+  for (int i = 0; i < NB; ++i) {
+    const int ti = wv + 4 * i;
+    i32x4_t acc[NTL][2];
+#pragma unroll
+    for (int ct = 0; ct < NTL; ++ct) acc[ct][0] = acc[ct][1] = i32x4_t{0, 0, 0, 0};
+    const uint32_t D[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = D[j] & 0x0F0F0F0Fu, hi = (D[j] >> 4) & 0x0F0F0F0Fu;
+      const long a = (long)((uint64_t)lo | ((uint64_t)hi << 32));
+#pragma unroll
+      for (int ct = 0; ct < NTL; ++ct)
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+          acc[ct][d] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, Bop[ct][d][j], acc[ct][d], 0, 0, 0);
     }
-    __syncthreads();  // T[bt & 1] complete; T[(bt + 1) & 1] was last read before this barrier
+    // lane (rg, nn) holds the group sums of candidates 16 ti + 4 rg + e for column nn
 #pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const int hh = g + kGroups * i;
-      if (hh < G) {
-        float lg = -__builtin_inff();
-        if (rowv[bt] >= 0) {
-          const float r01 = T[bt & 1][0][hh][lane] + T[bt & 1][1][hh][lane];
-          const float r23 = T[bt & 1][2][hh][lane] + T[bt & 1][3][hh][lane];
-          lg = sm * (r01 + r23);
-        }
-        mx[i] = fmaxf(mx[i], lg);
-        logits[((size_t)b * c.Hq + (size_t)h * G + hh) * ncap + k] = lg;
+    for (int ct = 0; ct < NTL; ++ct) {
+      float lg4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int S = acc[ct][0][e] * 128 + acc[ct][1][e];
+        const float av = ldexpf((float)S, ecol[ct] - 13);  // exact
+        const float s = half_bits_to_float(mw[i][e] & 0xffffu);
+        const float z = half_bits_to_float(mw[i][e] >> 16);
+        const float sa = s * av;
+        const float zb = z * bcol[ct];
+        const float t = sa + zb;
+        const float t01 = t + __shfl_xor(t, GT);      // groups (0, 1) and (2, 3)
+        const float r = t01 + __shfl_xor(t01, 2 * GT);  // (t0 + t1) + (t2 + t3)
+        lg4[e] = (rw[i][e] >= 0) ? sm * r : -__builtin_inff();
+        mx[ct] = fmaxf(mx[ct], lg4[e]);
+      }
+      if (colok && gc == 0) {
+        const int k = k0 + 16 * ti + 4 * rg;
+        *reinterpret_cast<float4*>(logits + ((size_t)b * c.Hq + (size_t)h * G + ct * GT + hl) * ncap + k) =
+            make_float4(lg4[0], lg4[1], lg4[2], lg4[3]);
       }
     }
   }
   if (pmax) {
+    // the block's largest logit per head: over the wave's lanes of the head, then over the waves
 #pragma unroll
-    for (int i = 0; i < NH; ++i) {
-      const int hh = g + kGroups * i;
-      if (hh < G) {
-        const float m = wave_max_dpp(mx[i]);
-        if (lane == 0) pmax[((size_t)b * c.Hq + (size_t)h * G + hh) * chunks_per_unit + ck] = m;
-      }
+    for (int ct = 0; ct < NTL; ++ct) {
+      float v = (colok && gc == 0) ? mx[ct] : -__builtin_inff();
+      v = fmaxf(v, __shfl_xor(v, 16));
+      v = fmaxf(v, __shfl_xor(v, 32));
+#pragma unroll
+      for (int s = GT; s < 16; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
+      if (lane < GT) s_max[wv][ct * GT + lane] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < G) {
+      const float m = fmaxf(fmaxf(s_max[0][threadIdx.x], s_max[1][threadIdx.x]),
+                            fmaxf(s_max[2][threadIdx.x], s_max[3][threadIdx.x]));
+      pmax[((size_t)b * c.Hq + (size_t)h * G + threadIdx.x) * chunks_per_unit + ck] = m;
     }
   }
 }
