@@ -136,10 +136,13 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
 
 /* Weight estimate + top-p pruning + GQA union (Twilight pruner).
  * - Estimate (paperlayer §4.2, §B.1: mixed-precision SpGEMV of the query against dequantised INT4
- *   keys): for each candidate and each query head, with codes c, fp16 scale s_g and zero z_g:
- *     a_g = fold_{c in group g}(a + q_c*code_c), b_g = fold_{c in g}(b + q_c)  (fp32 from +0)
+ *   keys): the query is held per head and 32-channel group g in fixed point,
+ *     E_g = floor(log2 max_{c in g} |q_c|) (>= -100),  Q_c = rne(q_c * 2^(13 - E_g)),
+ *   exact for channels within 2^6 of the group's largest; then for each candidate and query head,
+ *   with codes code_c, fp16 scale s_g and zero z_g,
+ *     a_g = 2^(E_g-13) sum_{c in g} Q_c*code_c,  b_g = 2^(E_g-13) sum_{c in g} Q_c   (exact)
  *     logit = fl(sm_scale * ((t_0 + t_1) + (t_2 + t_3))),  t_g = fl(s_g*a_g) + fl(z_g*b_g)
- *   i.e. sm * q . dequant(k) evaluated in this fixed float32 order.
+ *   i.e. sm * q~ . dequant(k) for the fixed-point query q~, every group sum exact.
  * - Weights: softmax of the logits over the unit's candidates only.
  * - Top-p (Paper-Notes "关键设计 / 高效Top-p": binary search of the threshold m with
  *   sum_{W_i >= m} W_i >= p, no sort): `iters` bisection steps on the uint32 image of the

@@ -4,8 +4,9 @@
     python -m top_sparse_attention_int4_amd.build --asm DIR  # also write gfx950 assembly per source
 
 The library is a single shared object holding every kernel (single-source HIP, no runtime code
-loading).  Floating-point contraction is off (the estimate's committed float32 order relies on it;
-fused multiply-adds are written explicitly where wanted) and packed fp32 instructions are disabled.
+loading).  Floating-point contraction is off (the committed float32 roundings of the page scores and
+the estimate rely on it; fused multiply-adds are written explicitly where wanted) and packed fp32
+instructions are disabled.
 """
 
 from __future__ import annotations
