@@ -7,16 +7,21 @@
 // documented operation sequence on every run.  Because q_c*bound is exact in float32 (bf16 x bf16),
 // max(q*kmin, q*kmax) = q+ * kmax + q- * kmin with q+ = max(q,0), q- = min(q,0): the second product
 // is then an exact zero and adding it changes nothing, so two fused multiply-adds per channel and
-// head reproduce the fold bit for bit without a compare.  Each wave of a block folds one query head
-// for the block's 64 pages (read from an LDS copy of the bounds that the whole block loads with
-// coalesced accesses); the group score then folds the heads in order.
+// head reproduce the fold bit for bit without a compare.  Two layouts compute the same folds: for
+// small steps each wave of a 4-wave block folds one query head for 64 pages (latency bound: every
+// head in parallel); for large ones a block is one wave and 64 pages, one lane per page folding all G
+// query heads, so each bound is converted once (the bounds staged in LDS in two halves of 64
+// channels with coalesced loads, 17 KB of LDS so that several blocks share a compute unit and cover
+// each other's loads; q+ and q- broadcast from LDS).  The group score then folds the heads in order.
 #include "twl_device.h"
 #include "twl_internal.h"
 
 namespace twl {
 
+// Small steps (few blocks, latency bound): each wave of a block folds one query head for the block's
+// 64 pages, read from an LDS copy of the bounds that the whole block loads at once.
 template <int G>
-__global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score(CacheView c, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(CacheView c, const uint16_t* __restrict__ q,
                                                                      float* __restrict__ scores,
                                                                      int blocks_per_unit) {
   constexpr int NT = 64 * (G > 4 ? G : 4);
@@ -91,6 +96,110 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score(CacheView c
     float gs = 0.f;
 #pragma unroll
     for (int k = 0; k < G; ++k) gs = gs + sig[k][lane];
+    scores[(size_t)u * c.maxP + j] = gs;
+  }
+}
+
+// Fold 64 channels (ch0 .. ch0 + 63) of one page into the G heads' scores: row = the page's staged
+// half (8 x 16 B of kmin, then 8 x 16 B of kmax), q+ / q- broadcast from LDS.
+template <int G>
+__device__ __forceinline__ void page_fold(const uint4* row, const float4 (*qp)[kD / 4], const float4 (*qn)[kD / 4],
+                                          int ch0, float (&acc)[G]) {
+#pragma unroll 1
+  for (int c8 = 0; c8 < 8; ++c8) {
+    const uint4 mnv = row[c8], mxv = row[8 + c8];
+    const uint32_t wm[4] = {mnv.x, mnv.y, mnv.z, mnv.w};
+    const uint32_t wx[4] = {mxv.x, mxv.y, mxv.z, mxv.w};
+    float mn[8], mx[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mn[2 * e] = bf16_lo(wm[e]);
+      mn[2 * e + 1] = bf16_hi(wm[e]);
+      mx[2 * e] = bf16_lo(wx[e]);
+      mx[2 * e + 1] = bf16_hi(wx[e]);
+    }
+    const int ch4 = (ch0 + 8 * c8) / 4;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float4 p0 = qp[i][ch4], p1 = qp[i][ch4 + 1], n0 = qn[i][ch4], n1 = qn[i][ch4 + 1];
+      const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      const float nv[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+      float a = acc[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a = fmaf(pv[e], mx[e], a);
+        a = fmaf(nv[e], mn[e], a);
+      }
+      acc[i] = a;
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
+                                                         float* __restrict__ scores, int blocks_per_unit) {
+  constexpr int RS = 17;  // LDS row of a page: 16 x 16 B of one half (mn 64 ch, mx 64 ch) + 16 B pad
+  const int u = blockIdx.x / blocks_per_unit;
+  const int blk = blockIdx.x - u * blocks_per_unit;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int lane = threadIdx.x;
+  __shared__ uint4 tile[64 * RS];
+  __shared__ float4 qp[G][kD / 4], qn[G][kD / 4];
+  // the page-table entry of this lane's page, in flight with the sequence length and q
+  const int j = blk * 64 + lane;
+  int phys = c.page_table[(size_t)b * c.maxP + min(j, c.maxP - 1)];
+  const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
+  uint32_t qw[G * kD / 128];  // two bf16 channels per word, G * 64 words over 64 lanes
+#pragma unroll
+  for (int i = 0; i < G; ++i) qw[i] = reinterpret_cast<const uint32_t*>(qg)[i * 64 + lane];
+  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+  const int P = (n + kPage - 1) / kPage;
+  if (blk * 64 >= P) return;  // uniform
+  if (j >= P) phys = -1;
+  // q+ and q- of every (head, channel) into LDS: lane l holds channels 2l, 2l + 1 of head i
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float x0 = bf16_lo(qw[i]), x1 = bf16_hi(qw[i]);
+    float* pp = reinterpret_cast<float*>(&qp[i][0]);
+    float* pn = reinterpret_cast<float*>(&qn[i][0]);
+    pp[2 * lane] = x0 > 0.f ? x0 : 0.f;
+    pp[2 * lane + 1] = x1 > 0.f ? x1 : 0.f;
+    pn[2 * lane] = x0 < 0.f ? x0 : 0.f;
+    pn[2 * lane + 1] = x1 < 0.f ? x1 : 0.f;
+  }
+  // half hf of page p: mn channels 64 hf .. + 63 (128 B) and mx channels 64 hf .. + 63 (128 B);
+  // load r covers pages 4r .. 4r + 3, lane l taking 16 B (segment l & 15) of page 4r + (l >> 4)
+  const int seg = lane & 15;
+  const uint4* rowp[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int pg = __shfl(phys, 4 * r + (lane >> 4));
+    rowp[r] = reinterpret_cast<const uint4*>(c.kbound + ((size_t)max(pg, 0) * c.Hkv + h) * 2 * kD) +
+              (seg < 8 ? 0 : 16) + (seg & 7);
+  }
+  float acc[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) acc[i] = 0.f;
+#pragma unroll 1
+  for (int hf = 0; hf < 2; ++hf) {
+    uint4 v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = rowp[r][8 * hf];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) tile[(4 * r + (lane >> 4)) * RS + seg] = v[r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    page_fold<G>(tile + lane * RS, qp, qn, 64 * hf, acc);
+    // this half's reads are done before the next one overwrites the tile
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (j < P) {
+    float gs = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) gs = gs + acc[i];
     scores[(size_t)u * c.maxP + j] = gs;
   }
 }
@@ -286,13 +395,22 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
 hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* scores, hipStream_t s) {
   const int bpu = (c.maxP + 63) / 64;
   dim3 grid((unsigned)(c.B * c.Hkv * bpu));
+  // up to two blocks per compute unit the step is latency bound: one wave per head; beyond, one lane
+  // per page folds every head so that each bound is converted once
+  const bool pages = grid.x > 512u;
+#define TWL_PS_G(GG)                                                                                        \
+  case GG:                                                                                                  \
+    if (pages) hipLaunchKernelGGL(k_page_score_pages<GG>, grid, dim3(64), 0, s, c, q, scores, bpu);         \
+    else hipLaunchKernelGGL(k_page_score_heads<GG>, grid, dim3(64 * (GG > 4 ? GG : 4)), 0, s, c, q, scores, bpu); \
+    break;
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_page_score<1>, grid, dim3(256), 0, s, c, q, scores, bpu); break;
-    case 2: hipLaunchKernelGGL(k_page_score<2>, grid, dim3(256), 0, s, c, q, scores, bpu); break;
-    case 4: hipLaunchKernelGGL(k_page_score<4>, grid, dim3(256), 0, s, c, q, scores, bpu); break;
-    case 8: hipLaunchKernelGGL(k_page_score<8>, grid, dim3(512), 0, s, c, q, scores, bpu); break;
+    TWL_PS_G(1)
+    TWL_PS_G(2)
+    TWL_PS_G(4)
+    TWL_PS_G(8)
     default: return hipErrorInvalidValue;
   }
+#undef TWL_PS_G
   return hipGetLastError();
 }
 
