@@ -182,6 +182,40 @@ def main():
     for li in range(L):
         kept.append(indptrs[li].cpu().numpy())
 
+    # ---- per-step spread: a third pass with one event pair around each step -----------------------
+    pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        pe[i][0].record()
+        step(i)
+        pe[i][1].record()
+    torch.cuda.synchronize()
+    st_us = np.array([a.elapsed_time(b) for a, b in pe]) * 1e3
+    step_spread = {k: round(float(np.percentile(st_us, q)), 3) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+    # ---- reference rates on this GPU: a plain device copy, and the INT4 append (a0) --------------
+    def timed(fn, reps=5):
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3  # seconds per call
+    csrc = torch.empty(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
+    cdst = torch.empty_like(csrc)
+    copy_gbps = 2 * csrc.numel() * 4 / timed(lambda: cdst.copy_(csrc)) / 1e9
+    del csrc, cdst
+    _, cache0, t0 = layers[0]
+    zeros_b = torch.zeros(B, dtype=torch.int32, device=dev)
+    ntok = int(w.seq_lens.astype(np.int64).sum())
+    # per (token, kv-head): 256 B of K read, 64 B of codes and 16 B of scale/zero written;
+    # per (page, kv-head): 512 B of bounds written
+    append_bytes = Hkv * (ntok * (256 + 80) + int((-(-w.seq_lens.astype(np.int64) // 16)).sum()) * 512)
+    append_gbps = append_bytes / timed(lambda: twl.quantize_k(cache0, zeros_b, t0["seq_lens"], w.max_seq_len)) / 1e9
+
     # ---- algorithmic bytes (per layer-step, averaged over the layers) ----------------------------
     seq = w.seq_lens.astype(np.int64)
     pages = -(-seq // 16)
@@ -218,6 +252,15 @@ def main():
             tr = json.load(fh)
         if tr.get("kernel_source_hash") == kernel_source_hash():
             traffic = tr.get("hbm_bytes_per_launch")
+    # bytes the whole step touches (counter passes over every kernel of the step, committed under
+    # profiles/), while the kernel sources still hash to the recorded value
+    touched = None
+    prof = os.path.join(ROOT, "profiles", f"traffic_step_{args.workload}.json")
+    if os.path.exists(prof):
+        with open(prof) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            touched = tr.get("hbm_bytes_per_step")
 
     rec = {
         "metric": METRIC,
@@ -238,13 +281,20 @@ def main():
                    **({"p1": w.p1, "num_clusters": w.num_clusters} if clusters else {})},
         "hbm": {"algorithmic_bytes_per_step": int(bytes_step), "gbps": round(bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
                 "frac_of_8TBps": round(bytes_step / (ms_per_step * 1e-3) / HBM_PEAK, 4),
+                "touched_bytes_per_step": touched,
+                "touched_frac_of_8TBps": (round(touched / (ms_per_step * 1e-3) / HBM_PEAK, 4) if touched else None),
+                "copy_gbps": round(copy_gbps, 1),
+                "frac_of_copy": round(bytes_step / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4),
+                "append_gbps": round(append_gbps, 1),
                 "candidates_per_step": cand_units_total, "kept_tokens_per_step": sel_tokens_total},
+        "step_us_with_events": step_spread,
         "stages_us": {n: round(float(x) * 1e3, 3)
                       for n, x in zip(STAGES_CLUSTER if clusters else twl.STAGE_NAMES, stage_ms)},
         "roofline": {"kernel": "k_attn (split-K sparse attention)", "bound": "hbm",
                      "achieved": round(achieved / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": int(bytes_attn), "avg_launch_us": round(attn_ms * 1e3, 3)},
+                     "algorithmic_bytes_per_launch": int(bytes_attn), "avg_launch_us": round(attn_ms * 1e3, 3),
+                     "frac_of_copy": round(achieved / 1e9 / copy_gbps, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -274,6 +324,7 @@ def cpu_baseline(w, units: int):
             reps += 1
     per_step = dt / (reps * n) * U
     return {"value": round(per_step * 1e6, 1), "unit": "us/layer-step", "cores": 1, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "blas_threads": 1,
             "sample": f"{n} of {U} (sequence, kv-head) units of one layer-step x {reps} repetitions, numpy "
                       f"float64 oracle on 1 thread, {dt:.1f} s in total, scaled to {U} units"}
 
