@@ -149,9 +149,10 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
  *   non-negative float32 weights keeping f(lo) >= p > f(hi); the kept set is {W_i >= lo}.  p = 1
  *   keeps every candidate.  With iters >= 31 the set equals the minimal top-p set up to ties and
  *   float32 rounding of the prefix masses; fewer steps return a superset whose mass still reaches p.
- *   Above 65536 candidates per unit (up to 2^22) the same search decides 11 key bits per pass over
- *   the weights from a mass histogram, with masses summed in 64-bit fixed point (2^-40 units of the
- *   largest weight); `iters` < 31 then keeps the threshold's top `iters` key bits.
+ *   Above 65536 candidates per unit (up to 2^22) the same search decides the top 11 key bits from a
+ *   mass histogram over all the weights, then the remaining 20 from histograms over the keys inside
+ *   the chosen bin, with masses summed in 64-bit fixed point (2^-40 units of the largest weight);
+ *   `iters` < 31 then keeps the threshold's top `iters` key bits.
  * - Union (paperlayer §B.2): the kept tokens of a unit are the union over its G query heads.
  * Outputs:
  *   threshold  f32 [B][Hq]   the weight threshold m (required)

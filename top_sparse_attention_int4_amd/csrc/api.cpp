@@ -94,7 +94,7 @@ struct Layout {
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
          ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
-         total = 0;
+         wkeys = 0, total = 0;
 };
 
 // ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
@@ -144,6 +144,7 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
     L->wstate = take((size_t)BH * kWideStateWords * 8);
     L->wcnt = take((size_t)U * (ncap / kWideChunk) * 4);
     L->uwords = take((size_t)U * (ncap / 32) * 4);
+    L->wkeys = take((size_t)BH * ncap * 4);
   }
   L->total = off;
   return true;
@@ -178,7 +179,8 @@ twl_status hip_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_EHIP
   } while (0)
 
 WideWs wide_of(void* ws, const Layout& L) {
-  return WideWs{at<float>(ws, L.pmax), at<uint64_t>(ws, L.wstate), at<int32_t>(ws, L.wcnt), at<uint32_t>(ws, L.uwords)};
+  return WideWs{at<float>(ws, L.pmax), at<uint64_t>(ws, L.wstate), at<int32_t>(ws, L.wcnt), at<uint32_t>(ws, L.uwords),
+                at<uint32_t>(ws, L.wkeys)};
 }
 
 // Estimate, top-p and (when `with_union`) the compacted GQA union of every unit, the narrow or the

@@ -15,14 +15,16 @@
 // result on every run.  Truncation costs at most 2^-40 per weight, below 2.4e-7 of Z for 2^18
 // candidates.
 //
-// Kernels, one pass each over the head's candidates (the histogram passes take four 4096-candidate
-// chunks per block, the next chunk's loads in flight while one is processed, and flush once):
-//   k_wide_hist1  M from the estimate's per-block maxima; e written over the logits; histogram of bits 30..20
-//   k_wide_hist2  resolve bits 30..20, histogram bits 19..9 inside the chosen bin
-//   k_wide_hist3  resolve bits 19..9, histogram bits 8..0
-//   k_wide_mask   per (unit, chunk): resolve bits 8..0 for the G heads, head masks, kept mass, union
-//                 words and their count
-//   k_wide_emit   per (unit, chunk): compaction of the union (ascending ids and K/V rows), outputs
+// Kernels:
+//   k_wide_hist1    M from the estimate's per-block maxima; e written over the logits; histogram of
+//                   bits 30..20 (four 4096-candidate chunks per block, the next chunk's loads in flight
+//                   while one is processed, one flush of integer atomics to the global histogram)
+//   k_wide_collect  resolve bits 30..20; the keys of the candidates inside the chosen bin appended to a
+//                   per-head buffer (one atomic per block and chunk; their order does not matter)
+//   k_wide_finish   one block per head: bits 19..9 and 8..0 from LDS histograms over the collected keys
+//                   (the bisection steps left), the threshold
+//   k_wide_mask     per (unit, chunk): head masks, kept mass, union words and their count
+//   k_wide_emit     per (unit, chunk): compaction of the union (ascending ids and K/V rows), outputs
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -130,17 +132,19 @@ __device__ __forceinline__ void wide_level1(const uint64_t* st, float p, int& mo
   wide_find(st + kWideH1, st + kWideC1, 64, target, b1, rem1);
 }
 
-__global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __restrict__ w, int ncap, float p,
-                                                             uint64_t* __restrict__ state) {
-  __shared__ uint64_t h[2048];
+__global__ __launch_bounds__(kWideThreads) void k_wide_collect(const float* __restrict__ w, int ncap, float p,
+                                                               uint64_t* __restrict__ state,
+                                                               uint32_t* __restrict__ keys) {
   __shared__ int s_mode, s_b1;
+  __shared__ int scan_sm[NW + 1];
+  __shared__ int s_base;
   const int nbk = ncap / kWideAlign;
   const int bh = blockIdx.x / nbk, bk = blockIdx.x - bh * nbk;
   uint64_t* st = state + (size_t)bh * kWideStateWords;
   const float* x0 = w + (size_t)bh * ncap + (size_t)bk * kWideAlign;
+  uint32_t* kout = keys + (size_t)bh * ncap;
   float v[2][EPT];
   load_chunk4(x0, v[0]);  // in flight during the resolution
-  for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
   if (threadIdx.x < 64) {
     int mode, b1;
     uint64_t Z, rem1;
@@ -163,70 +167,120 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist2(const float* __rest
   for (int c = 0; c < kWideBlockChunks; ++c) {
     if (c + 1 < kWideBlockChunks) load_chunk4(x0 + (size_t)(c + 1) * kWideChunk, v[(c + 1) & 1]);
     const float (&x)[EPT] = v[c & 1];
+    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const uint32_t key = __float_as_uint(x[j]);
-      if (x[j] >= 0.f && (key >> 20) == b1) {
-        const uint64_t f = to_fix(x[j]);
-        if (f) atomicAdd((unsigned long long*)&h[(key >> 9) & 2047u], (unsigned long long)f);
-      }
-    }
+    for (int j = 0; j < EPT; ++j) cnt += (x[j] >= 0.f && (__float_as_uint(x[j]) >> 20) == b1) ? 1 : 0;
+    int total;
+    const int off = block_excl_scan<NW>(cnt, scan_sm, &total);
+    if (total == 0) continue;  // uniform
+    if (threadIdx.x == 0)
+      s_base = (int)atomicAdd((unsigned long long*)&st[kWideNKeys], (unsigned long long)total);
+    __syncthreads();
+    int pos = s_base + off;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (x[j] >= 0.f && (__float_as_uint(x[j]) >> 20) == b1) kout[pos++] = __float_as_uint(x[j]);
   }
-  __syncthreads();
-  flush_hist(h, 2048, st + kWideH2, st + kWideC2);
 }
 
-__global__ __launch_bounds__(kWideThreads) void k_wide_hist3(const float* __restrict__ w, int ncap,
-                                                             uint64_t* __restrict__ state) {
-  __shared__ uint64_t h[512];
-  __shared__ int s_b2;
-  const int nbk = ncap / kWideAlign;
-  const int bh = blockIdx.x / nbk, bk = blockIdx.x - bh * nbk;
+// One block per head: the remaining 20 key bits from LDS histograms of the collected keys (all in the
+// first level's bin), then the threshold.
+__global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint64_t* __restrict__ state,
+                                                      const uint32_t* __restrict__ keys, float* threshold) {
+  constexpr int FT = 1024, FU = 8;
+  __shared__ uint64_t h2[2048], h3[512], cs[64];
+  __shared__ int s_bin;
+  __shared__ uint64_t s_rem;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint64_t* st = state + (size_t)bh * kWideStateWords;
-  const float* x0 = w + (size_t)bh * ncap + (size_t)bk * kWideAlign;
-  float v[2][EPT];
-  load_chunk4(x0, v[0]);  // in flight during the resolution
-  if (st[kWideSMode] != 0ull) return;  // uniform over the head's blocks
-  for (int i = threadIdx.x; i < 512; i += NT) h[i] = 0ull;
+  const uint32_t* kin = keys + (size_t)bh * ncap;
+  const uint64_t mode = st[kWideSMode], Z = st[kWideSZ];
   const uint32_t b1 = (uint32_t)st[kWideSB1];
-  if (threadIdx.x < 64) {
-    int b2;
-    uint64_t rem2;
-    wide_find(st + kWideH2, st + kWideC2, 64, st[kWideSR1], b2, rem2);
-    if (threadIdx.x == 0) {
-      s_b2 = b2;
-      if (bk == 0) {
-        st[kWideSB2] = (uint64_t)b2;
-        st[kWideSR2] = rem2;
+  const uint64_t rem1 = st[kWideSR1];
+  const int n = (int)min(st[kWideNKeys], (uint64_t)ncap);
+  uint32_t T = 0u;
+  if (mode == 0ull) {
+    for (int i = tid; i < 2048; i += FT) h2[i] = 0ull;
+    if (tid < 512) h3[tid] = 0ull;
+    __syncthreads();
+    auto coarse = [&](const uint64_t* h, int ncoarse) {
+      if (tid < ncoarse * 16) {
+        const uint64_t x = row16_incl_scan_u64(h[2 * tid] + h[2 * tid + 1]);
+        if ((lane & 15) == 15) cs[tid >> 4] = x;
+      }
+      __syncthreads();
+    };
+    // bits 19..9 of every collected key
+    for (int i0 = 0; i0 < n; i0 += FT * FU) {
+      uint32_t kk[FU];
+#pragma unroll
+      for (int e = 0; e < FU; ++e) {
+        const int i = i0 + e * FT + tid;
+        kk[e] = (i < n) ? kin[i] : 0xFFFFFFFFu;  // a weight key never has the sign bit set
+      }
+#pragma unroll
+      for (int e = 0; e < FU; ++e) {
+        if (kk[e] != 0xFFFFFFFFu) {
+          const uint64_t f = to_fix(__uint_as_float(kk[e]));
+          if (f) atomicAdd((unsigned long long*)&h2[(kk[e] >> 9) & 2047u], (unsigned long long)f);
+        }
       }
     }
-  }
-  __syncthreads();
-  const uint32_t pre = (b1 << 11) | (uint32_t)s_b2;
-#pragma unroll
-  for (int c = 0; c < kWideBlockChunks; ++c) {
-    if (c + 1 < kWideBlockChunks) load_chunk4(x0 + (size_t)(c + 1) * kWideChunk, v[(c + 1) & 1]);
-    const float (&x)[EPT] = v[c & 1];
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const uint32_t key = __float_as_uint(x[j]);
-      if (x[j] >= 0.f && (key >> 9) == pre) {
-        const uint64_t f = to_fix(x[j]);
-        if (f) atomicAdd((unsigned long long*)&h[key & 511u], (unsigned long long)f);
+    __syncthreads();
+    coarse(h2, 64);
+    if (wv == 0) {
+      int bin;
+      uint64_t rem;
+      wide_find(h2, cs, 64, rem1, bin, rem);
+      if (lane == 0) {
+        s_bin = bin;
+        s_rem = rem;
       }
     }
+    __syncthreads();
+    const uint32_t pre = (b1 << 11) | (uint32_t)s_bin;
+    const uint64_t rem2 = s_rem;
+    // bits 8..0 of the keys inside that bin
+    for (int i0 = 0; i0 < n; i0 += FT * FU) {
+      uint32_t kk[FU];
+#pragma unroll
+      for (int e = 0; e < FU; ++e) {
+        const int i = i0 + e * FT + tid;
+        kk[e] = (i < n) ? kin[i] : 0xFFFFFFFFu;
+      }
+#pragma unroll
+      for (int e = 0; e < FU; ++e) {
+        if (kk[e] != 0xFFFFFFFFu && (kk[e] >> 9) == pre) {
+          const uint64_t f = to_fix(__uint_as_float(kk[e]));
+          if (f) atomicAdd((unsigned long long*)&h3[kk[e] & 511u], (unsigned long long)f);
+        }
+      }
+    }
+    __syncthreads();
+    coarse(h3, 16);
+    if (wv == 0) {
+      int bin;
+      uint64_t rem;
+      wide_find(h3, cs, 16, rem2, bin, rem);
+      if (lane == 0) s_bin = bin;
+    }
+    __syncthreads();
+    T = (pre << 9) | (uint32_t)s_bin;
+    if (iters < 31) T &= ~((1u << (31 - iters)) - 1u);
   }
-  __syncthreads();
-  flush_hist(h, 512, st + kWideH3, st + kWideC3);
+  if (tid == 0) {
+    st[kWideST] = (uint64_t)T;
+    if (threshold) threshold[bh] = Z ? __uint_as_float(T) / (float)((double)Z / 1099511627776.0) : 0.f;
+  }
 }
 
-// Per (unit, chunk): the G thresholds, head masks, the kept mass per head, union words and count.
+// Per (unit, chunk): head masks under the finished thresholds, the kept mass per head, union words and count.
 template <int G>
 __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const float* __restrict__ w, int ncap,
-                                                            int iters, uint64_t* __restrict__ state,
+                                                            uint64_t* __restrict__ state,
                                                             uint32_t* __restrict__ head_mask, int mask_words,
                                                             uint32_t* __restrict__ uwords,
-                                                            int32_t* __restrict__ chunk_cnt, float* threshold) {
+                                                            int32_t* __restrict__ chunk_cnt) {
   __shared__ float s_thr[G];
   __shared__ int s_cnt[NW];
   const int nch = ncap / kWideChunk;
@@ -242,27 +296,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
       x[j][hh] = reinterpret_cast<const float4*>(w + (bh0 + hh) * ncap + (size_t)ch * kWideChunk)[j * NT + threadIdx.x];
-  for (int hh = wv; hh < G; hh += NW) {
-    uint64_t* st = state + (bh0 + hh) * kWideStateWords;
-    // the resolved state of the passes before, read together
-    const uint64_t mode = st[kWideSMode], sb1 = st[kWideSB1], sb2 = st[kWideSB2], sr2 = st[kWideSR2];
-    uint32_t T = 0u;
-    if (mode == 0ull) {
-      int b3;
-      uint64_t rem3;
-      wide_find(st + kWideH3, st + kWideC3, 16, sr2, b3, rem3);
-      T = ((uint32_t)sb1 << 20) | ((uint32_t)sb2 << 9) | (uint32_t)b3;
-      if (iters < 31) T &= ~((1u << (31 - iters)) - 1u);
-    }
-    if (lane == 0) {
-      s_thr[hh] = __uint_as_float(T);
-      if (ch == 0) {
-        st[kWideST] = (uint64_t)T;
-        const uint64_t Z = st[kWideSZ];
-        if (threshold) threshold[bh0 + hh] = Z ? __uint_as_float(T) / (float)((double)Z / 1099511627776.0) : 0.f;
-      }
-    }
-  }
+  if (threadIdx.x < G) s_thr[threadIdx.x] = __uint_as_float((uint32_t)state[(bh0 + threadIdx.x) * kWideStateWords + kWideST]);
   __syncthreads();
   float thr[G];
 #pragma unroll
@@ -380,12 +414,13 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits,
   const dim3 blk(kWideThreads);
   const int npm = ncap / (64 * est_batches(ncap, (int64_t)c.B * c.Hkv));
   hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, npm, wd.state);
-  hipLaunchKernelGGL(k_wide_hist2, dim3(hgrid), blk, 0, s, logits, ncap, p, wd.state);
-  hipLaunchKernelGGL(k_wide_hist3, dim3(hgrid), blk, 0, s, logits, ncap, wd.state);
+  hipLaunchKernelGGL(k_wide_collect, dim3(hgrid), blk, 0, s, logits, ncap, p, wd.state, wd.keys);
+  hipLaunchKernelGGL(k_wide_finish, dim3((unsigned)(c.B * c.Hq)), dim3(1024), 0, s, ncap, iters, wd.state, wd.keys,
+                     threshold);
 #define TWL_WIDE_G(GG)                                                                                      \
   case GG:                                                                                                  \
-    hipLaunchKernelGGL(k_wide_mask<GG>, dim3(ugrid), blk, 0, s, c, logits, ncap, iters, wd.state, head_mask, \
-                       mask_words, wd.uwords, wd.chunk_cnt, threshold);                                     \
+    hipLaunchKernelGGL(k_wide_mask<GG>, dim3(ugrid), blk, 0, s, c, logits, ncap, wd.state, head_mask,        \
+                       mask_words, wd.uwords, wd.chunk_cnt);                                                \
     break;
   switch (c.G) {
     TWL_WIDE_G(1)

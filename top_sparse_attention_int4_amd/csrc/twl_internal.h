@@ -34,18 +34,16 @@ struct CandView {
   const int32_t* phys;          // pages only, optional: physical page of each listed page id
 };
 
-// Wide top-p (more than 65536 candidates per head): per-head state in 64-bit words -- the three
-// histogram levels (fine bins, then one coarse sum per 32 bins), the kept mass, and the resolved
-// search state.  Words [0, kWideZeroWords) must be zero before the first histogram pass.
+// Wide top-p (more than 65536 candidates per head): per-head state in 64-bit words -- the first
+// histogram level (fine bins, then one coarse sum per 32 bins), the count of collected keys, the kept
+// mass, and the resolved search state.  Words [0, kWideZeroWords) must be zero before the first pass.
 constexpr int kWideChunk = 4096;  // candidates per chunk of the wide kernels
 constexpr int kWideThreads = 256;
-constexpr int kWideBlockChunks = 4;  // chunks per block of the histogram passes (software-pipelined)
+constexpr int kWideBlockChunks = 4;  // chunks per block of the first two passes (software-pipelined)
 constexpr int kWideAlign = kWideChunk * kWideBlockChunks;  // wide candidate capacities are multiples
-constexpr int kWideH1 = 0, kWideC1 = 2048, kWideH2 = 2112, kWideC2 = 4160, kWideH3 = 4224, kWideC3 = 4736;
-constexpr int kWideMass = 4752, kWideZeroWords = 4753;
-constexpr int kWideSZ = 4753, kWideSMode = 4754, kWideSB1 = 4755, kWideSR1 = 4756, kWideSB2 = 4757,
-              kWideSR2 = 4758, kWideST = 4759;
-constexpr int kWideStateWords = 4760;
+constexpr int kWideH1 = 0, kWideC1 = 2048, kWideNKeys = 2112, kWideMass = 2113, kWideZeroWords = 2114;
+constexpr int kWideSZ = 2114, kWideSMode = 2115, kWideSB1 = 2116, kWideSR1 = 2117, kWideST = 2118;
+constexpr int kWideStateWords = 2119;
 constexpr int kNarrowMaxCands = 65536;      // largest candidate count of the register-resident top-p
 constexpr int kWideMaxCands = 1 << 22;      // fixed-point mass bound
 struct WideWs {
@@ -53,6 +51,7 @@ struct WideWs {
   uint64_t* state;     // [B*Hq][kWideStateWords]
   int32_t* chunk_cnt;  // [B*Hkv][ncap / kWideChunk]
   uint32_t* uwords;    // [B*Hkv][ncap / 32] union bitmap
+  uint32_t* keys;      // [B*Hq][ncap] keys of the candidates in the first level's chosen bin
 };
 constexpr int kEstCands = 256;  // candidate block of the range starts (chunk_first); divides the estimate's blocks
 // 64-candidate batches per estimate block for a candidate capacity and unit count (2 or 8)
