@@ -41,7 +41,7 @@ DESCR = {
     "C5": "Double-P hierarchical: B=1, 32/8 heads, n=262144, 4096 Zipf(1.1) clusters, cluster p1=0.95 "
           "then token p=0.9",
 }
-STAGES_CLUSTER = ["cluster_select", "range_prefix", "estimate", "topp_union", "attention", "merge"]
+STAGES_CLUSTER = ["cluster_scores_topp", "cluster_union", "estimate", "topp_union", "attention", "merge"]
 
 
 def parse():

@@ -220,8 +220,8 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
  * sparse attention over the union -- the same kernels as the split calls.  Unkept clusters are
  * dropped.  Requires 2*num_clusters <= max_seq_len rounded up to the top-p capacity; the workspace
  * is twl_workspace_bytes(cache, max_seq_len).  `events` is NULL or holds 2*TWL_NUM_STAGES events as
- * for twl_decode_profiled, the stages being 0 cluster scores + cluster top-p + cluster union,
- * 1 range prefix sums, 2 INT4 estimate, 3 token top-p + union, 4 attention, 5 merge. */
+ * for twl_decode_profiled, the stages being 0 cluster scores + cluster top-p, 1 cluster union (with
+ * the kept ranges' prefix sums), 2 INT4 estimate, 3 token top-p + union, 4 attention, 5 merge. */
 twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_decode_params* params, float p1,
                                const void* centroids, const int32_t* csize, const int32_t* coff,
                                int32_t num_clusters, float* out, float* lse, float* threshold, int32_t* sel_indptr,

@@ -41,8 +41,12 @@ CLUSTER = [
          num_clusters=64),
     dict(batch=1, num_q_heads=4, num_kv_heads=2, seq_lens=[2500], kind="cluster", seed=14, p=0.9, p1=1.0,
          num_clusters=200),
+    # more than 4096 kept clusters (4614 non-empty of 6000, all kept at p1 = 1): the range prefix sums
+    # no longer fit the union kernel's LDS and the block starts are searched in global memory
+    dict(batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=[60000], kind="cluster", seed=15, p=0.9, p1=1.0,
+         num_clusters=6000),
 ]
-CLUSTER_IDS = ["g4_two_seqs", "g8_1500_clusters", "g1_empty_seq", "p1_one"]
+CLUSTER_IDS = ["g4_two_seqs", "g8_1500_clusters", "g1_empty_seq", "p1_one", "over_4096_kept"]
 
 
 def _cluster_gpu(w, cache, t, p1, iters=32):

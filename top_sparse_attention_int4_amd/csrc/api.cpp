@@ -338,10 +338,15 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   int32_t* ranges = at<int32_t>(ws, L.urow);
   int32_t* rcount = at<int32_t>(ws, L.pcnt);
   TWL_TRY(E.rec(0));
-  TWL_TRY(launch_cluster_select(c, qb, prm->sm_scale, p1, prm->iters, static_cast<const uint16_t*>(centroids), csize,
-                                coff, num_clusters, (int)cpad, at<float>(ws, L.logits), at<float>(ws, L.thr),
-                                at<uint32_t>(ws, L.masks), ranges, rcount, s));
+  TWL_TRY(launch_cluster_scores_topp(c, qb, prm->sm_scale, p1, prm->iters, static_cast<const uint16_t*>(centroids),
+                                     csize, num_clusters, (int)cpad, at<float>(ws, L.logits), at<float>(ws, L.thr),
+                                     at<uint32_t>(ws, L.masks), s));
   TWL_TRY(E.rec(1));
+  TWL_TRY(E.rec(2));
+  // the kept clusters' token ranges, with the prefix sums and block starts the estimate resolves by
+  TWL_TRY(launch_cluster_union(c, at<uint32_t>(ws, L.masks), (int)cpad, csize, coff, num_clusters, ranges, rcount,
+                               at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
+  TWL_TRY(E.rec(3));
   CandView cand{};
   cand.mode = kCandRanges;
   cand.items = ranges;
@@ -349,9 +354,6 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   cand.max_items = num_clusters;
   cand.range_prefix = at<int32_t>(ws, L.rpre);
   cand.chunk_first = at<int32_t>(ws, L.cfirst);
-  TWL_TRY(E.rec(2));
-  TWL_TRY(launch_range_prefix(c, cand, at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
-  TWL_TRY(E.rec(3));
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   const bool csr = sel_tokens != nullptr;
   TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s));
@@ -526,10 +528,12 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
   st = check_device();
   if (st != TWL_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(launch_cluster_select(make_view(cache), static_cast<const uint16_t*>(q), sm_scale, p1, iters,
-                                          static_cast<const uint16_t*>(centroids), csize, coff, num_clusters,
-                                          (int)cpad, at<float>(ws, L.logits), at<float>(ws, L.thr),
-                                          at<uint32_t>(ws, L.masks), ranges, count, s));
+  const CacheView c = make_view(cache);
+  TWL_TRY(launch_cluster_scores_topp(c, static_cast<const uint16_t*>(q), sm_scale, p1, iters,
+                                     static_cast<const uint16_t*>(centroids), csize, num_clusters, (int)cpad,
+                                     at<float>(ws, L.logits), at<float>(ws, L.thr), at<uint32_t>(ws, L.masks), s));
+  return hip_status(launch_cluster_union(c, at<uint32_t>(ws, L.masks), (int)cpad, csize, coff, num_clusters, ranges,
+                                         count, nullptr, nullptr, 0, s));
 }
 
 twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_decode_params* params, float p1,

@@ -74,13 +74,16 @@ template <int G>
 __global__ __launch_bounds__(1024) void k_cluster_union(CacheView c, const uint32_t* __restrict__ mask_ws, int cpad,
                                                         const int32_t* __restrict__ csize,
                                                         const int32_t* __restrict__ coff, int C,
-                                                        int32_t* __restrict__ ranges, int32_t* __restrict__ count) {
+                                                        int32_t* __restrict__ ranges, int32_t* __restrict__ count,
+                                                        int32_t* __restrict__ prefix, int32_t* __restrict__ chunk_first,
+                                                        int nchunk) {
   constexpr int NT = 1024, NW = NT / 64;
   constexpr int kMaxWords = 65536 / 32;
   constexpr int WPT = kMaxWords / NT;
   __shared__ uint32_t uw[kMaxWords];
   __shared__ int woff[kMaxWords];
   __shared__ int scan_sm[NW + 1];
+  __shared__ int spre[4096 + 1];
   const int u = blockIdx.x;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int tid = threadIdx.x;
@@ -114,22 +117,121 @@ __global__ __launch_bounds__(1024) void k_cluster_union(CacheView c, const uint3
   const int32_t* cs = csize + (size_t)u * C;
   const int32_t* co = coff + (size_t)u * (C + 1);
   int32_t* rg = ranges + (size_t)u * C * 2;
-  for (int k = tid; k < C; k += NT) {
+  // each thread takes a contiguous run of clusters, so the kept ones' positions and token offsets
+  // follow from block scans; ranges hold (first token, length).  Up to CR clusters per thread their
+  // sizes and offsets are read together (one round trip); more take a loop.
+  constexpr int CR = 4;
+  const int cpt = (C + NT - 1) / NT;
+  const int k0 = tid * cpt, k1 = min(k0 + cpt, C);
+  const bool regs = cpt <= CR;  // uniform
+  int lenr[CR], offr[CR];
+#pragma unroll
+  for (int i = 0; i < CR; ++i) {
+    const int k = min(k0 + i, C - 1);
+    lenr[i] = regs ? cs[k] : 0;
+    offr[i] = regs ? co[k] : 0;
+  }
+  auto kept_at = [&](int k, int& pos) {
     const uint32_t x = uw[k >> 5];
     const int bit = k & 31;
-    if ((x >> bit) & 1u) {
-      const int pos = woff[k >> 5] + __popc(x & ((1u << bit) - 1u));
-      rg[2 * pos] = co[k];
-      rg[2 * pos + 1] = cs[k];
+    pos = woff[k >> 5] + __popc(x & ((1u << bit) - 1u));
+    return ((x >> bit) & 1u) != 0u;
+  };
+  int tok_local = 0;
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+      int pos;
+      if (k0 + i < k1 && kept_at(k0 + i, pos)) {
+        rg[2 * pos] = offr[i];
+        rg[2 * pos + 1] = lenr[i];
+        tok_local += max(lenr[i], 0);
+      }
+    }
+  } else {
+    for (int k = k0; k < k1; ++k) {
+      int pos;
+      if (kept_at(k, pos)) {
+        const int len = cs[k];
+        rg[2 * pos] = co[k];
+        rg[2 * pos + 1] = len;
+        tok_local += max(len, 0);
+      }
     }
   }
   if (tid == 0) count[u] = total;
+  if (!prefix) return;  // uniform
+  // prefix sums of the kept ranges' lengths (negative lengths count as 0), and for every block of
+  // kEstCands candidates the range holding its first candidate (the count when past the last one)
+  int tok_total;
+  int run = block_excl_scan<NW>(tok_local, scan_sm, &tok_total);
+  int32_t* pre = prefix + (size_t)u * (C + 1);
+  int32_t* cf = chunk_first + (size_t)u * nchunk;
+  constexpr int kLdsPre = 4096;
+  const bool in_lds = total <= kLdsPre;  // uniform
+  auto put = [&](int pos, int len) {
+    pre[pos] = run;
+    if (in_lds) spre[pos] = run;
+    run += len;
+  };
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < CR; ++i) {
+      int pos;
+      if (k0 + i < k1 && kept_at(k0 + i, pos)) put(pos, max(lenr[i], 0));
+    }
+  } else {
+    for (int k = k0; k < k1; ++k) {
+      int pos;
+      if (kept_at(k, pos)) put(pos, max(cs[k], 0));
+    }
+  }
+  if (tid == 0) {
+    pre[total] = tok_total;
+    if (in_lds) spre[total] = tok_total;
+  }
+  __syncthreads();  // (also orders this block's global writes of pre before the reads below)
+  // block j starts at candidate j * kEstCands: the last range whose prefix is <= that (empty ranges
+  // share their successor's prefix, so the last of equal ones is the non-empty one)
+  const int32_t* sp = in_lds ? spre : pre;
+  for (int j = tid; j < nchunk; j += NT) {
+    const int x = j * kEstCands;
+    int r = total;
+    if (x < tok_total) {
+      int lo = 0, hi = total;  // sp[lo] <= x < sp[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sp[mid] <= x) lo = mid; else hi = mid;
+      }
+      r = lo;
+    }
+    cf[j] = r;
+  }
 }
 
-hipError_t launch_cluster_select(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
-                                 const uint16_t* centroids, const int32_t* csize, const int32_t* coff, int C,
-                                 int cpad, float* lam, float* thr, uint32_t* mask_ws, int32_t* ranges,
-                                 int32_t* count, hipStream_t s) {
+hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
+                                const int32_t* coff, int C, int32_t* ranges, int32_t* count, int32_t* prefix,
+                                int32_t* chunk_first, int nchunk, hipStream_t s) {
+  dim3 ugrid((unsigned)(c.B * c.Hkv));
+#define TWL_CU_G(GG)                                                                                         \
+  case GG:                                                                                                   \
+    hipLaunchKernelGGL(k_cluster_union<GG>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, \
+                       count, prefix, chunk_first, nchunk);                                                  \
+    break;
+  switch (c.G) {
+    TWL_CU_G(1)
+    TWL_CU_G(2)
+    TWL_CU_G(4)
+    TWL_CU_G(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef TWL_CU_G
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
+                                      const uint16_t* centroids, const int32_t* csize, int C, int cpad, float* lam,
+                                      float* thr, uint32_t* mask_ws, hipStream_t s) {
   const int bpu = cpad / 64;
   dim3 grid((unsigned)(c.B * c.Hkv * bpu));
   switch (c.G) {
@@ -141,17 +243,7 @@ hipError_t launch_cluster_select(const CacheView& c, const uint16_t* q, float sm
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_topp_weighted(c, lam, cpad, p1, iters, thr, mask_ws, csize, C, s);
-  if (e != hipSuccess) return e;
-  dim3 ugrid((unsigned)(c.B * c.Hkv));
-  switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_cluster_union<1>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
-    case 2: hipLaunchKernelGGL(k_cluster_union<2>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
-    case 4: hipLaunchKernelGGL(k_cluster_union<4>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
-    case 8: hipLaunchKernelGGL(k_cluster_union<8>, ugrid, dim3(1024), 0, s, c, mask_ws, cpad, csize, coff, C, ranges, count); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_topp_weighted(c, lam, cpad, p1, iters, thr, mask_ws, csize, C, s);
 }
 
 }  // namespace twl

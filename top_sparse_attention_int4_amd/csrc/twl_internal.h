@@ -87,10 +87,15 @@ hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t*
                             hipStream_t s);
 hipError_t launch_topp_weighted(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
                                 uint32_t* mask_ws, const int32_t* mult, int mult_stride, hipStream_t s);
-hipError_t launch_cluster_select(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
-                                 const uint16_t* centroids, const int32_t* csize, const int32_t* coff, int C,
-                                 int cpad, float* lam, float* thr, uint32_t* mask_ws, int32_t* ranges,
-                                 int32_t* count, hipStream_t s);
+// cluster scores (size-weighted logits) and the per-head cluster top-p (head masks in mask_ws)
+hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
+                                      const uint16_t* centroids, const int32_t* csize, int C, int cpad, float* lam,
+                                      float* thr, uint32_t* mask_ws, hipStream_t s);
+// union of a unit's head masks -> kept ranges (first token, length) and count; with prefix non-NULL
+// also the ranges' prefix sums [U][C + 1] and the range of each 256-candidate block [U][nchunk]
+hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
+                                const int32_t* coff, int C, int32_t* ranges, int32_t* count, int32_t* prefix,
+                                int32_t* chunk_first, int nchunk, hipStream_t s);
 hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
                        float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, hipStream_t s);
 hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, const int32_t* cand_row,
