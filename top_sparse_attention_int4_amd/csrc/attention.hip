@@ -316,14 +316,15 @@ __global__ __launch_bounds__(256) void k_rows(CacheView c, const int32_t* __rest
   }
 }
 
-// One block per (unit, head): the unit's chunk partials are merged by 32 rows of 32 threads, row r
-// taking chunks r, r + 32, ... in order with a running maximum and thread j owning dims 4j..4j+3
-// (four chunks' loads in flight per thread); the 32 row results are then combined in row order.
-// With a token list the unit has ceil(count / CH) chunks; without one every slot holds a partial.
-template <int G>
-__global__ __launch_bounds__(1024) void k_merge(CacheView c, ListView L, bool use_list, int CH, int slots,
-                                                const float* __restrict__ partials, float* out, float* lse) {
-  constexpr int NR = 32, UNR = 4;
+// One block per (unit, head): the unit's chunk partials are merged by NR rows of 32 threads (8, 16 or
+// 32 rows as the slot count needs), row r taking chunks r, r + NR, ... in order with a running
+// maximum and thread j owning dims 4j..4j+3 (four chunks' loads in flight per thread); the NR row
+// results are then combined in row order.  With a token list the unit has ceil(count / CH) chunks;
+// without one every slot holds a partial.
+template <int G, int NR>
+__global__ __launch_bounds__(NR * 32) void k_merge(CacheView c, ListView L, bool use_list, int CH, int slots,
+                                                   const float* __restrict__ partials, float* out, float* lse) {
+  constexpr int UNR = 4;
   const int u = blockIdx.x / G, hh = blockIdx.x - (blockIdx.x / G) * G;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int tid = threadIdx.x, r = tid >> 5, j = tid & 31;
@@ -466,10 +467,21 @@ hipError_t launch_merge(const CacheView& c, const ListView* list, int chunk_toke
   dim3 grid((unsigned)(c.B * c.Hkv * c.G));
   const ListView lv = list ? *list : ListView{};
   const bool use_list = list != nullptr;
-#define TWL_MERGE_CASE(GG)                                                                                   \
-  case GG:                                                                                                   \
-    hipLaunchKernelGGL(k_merge<GG>, grid, dim3(1024), 0, s, c, lv, use_list, chunk_tokens, slots, partials,  \
-                       out, lse);                                                                           \
+  // rows of 32 threads: enough for about four chunks per row (one round of loads), at least 8 (the
+  // final combine uses 128 threads)
+  const int nr = slots <= 32 ? 8 : (slots <= 64 ? 16 : 32);
+#define TWL_MERGE_NR(GG, NR)                                                                                 \
+  case NR:                                                                                                   \
+    hipLaunchKernelGGL((k_merge<GG, NR>), grid, dim3(NR * 32), 0, s, c, lv, use_list, chunk_tokens, slots,   \
+                       partials, out, lse);                                                                 \
+    break;
+#define TWL_MERGE_CASE(GG)     \
+  case GG:                     \
+    switch (nr) {              \
+      TWL_MERGE_NR(GG, 8)      \
+      TWL_MERGE_NR(GG, 16)     \
+      TWL_MERGE_NR(GG, 32)     \
+    }                          \
     break;
   switch (c.G) {
     TWL_MERGE_CASE(1)
@@ -479,6 +491,7 @@ hipError_t launch_merge(const CacheView& c, const ListView* list, int chunk_toke
     default: return hipErrorInvalidValue;
   }
 #undef TWL_MERGE_CASE
+#undef TWL_MERGE_NR
   return hipGetLastError();
 }
 
