@@ -8,10 +8,12 @@
 // target p*Z, Z = sum e_i, which keeps the same set as comparing W_i = e_i/Z with p.  The search runs
 // on the key of a weight, the uint32 image of the non-negative float32 value (order-preserving).  A
 // bisection of the key over [0, 2^31) decides one key bit per step, top bit first, keeping the
-// largest threshold whose mass{e >= T} still reaches p*Z.  Here each round decides 11 bits at once
-// from an LDS histogram of the mass per value of those bits (the outcome of 11 consecutive bisection
-// steps); rounds on bits 30..20, 19..9 and 8..0 give the exact threshold T, and the kept set
-// {e >= T} is the converged bisection's.  With fewer steps requested T keeps only its top `iters`
+// largest threshold whose mass{e >= T} still reaches p*Z.  Here each round decides a digit of the key
+// at once from an LDS histogram of the mass per value of the digit (the outcome of as many
+// consecutive bisection steps).  Only weights >= 2^-40 carry mass, so the digits run over keys from
+// that floor up: 11 bits of (key - floor) >> 18 (exponent and five mantissa bits, which spreads the
+// crowded first round over four times as many bins as the key's top 11 bits), then bits 17..9 and
+// 8..0; they give the exact threshold T, and the kept set {e >= T} is the converged bisection's.  With fewer steps requested T keeps only its top `iters`
 // bits, where a shorter bisection stops: a superset that still reaches p.  p = 1 keeps everything.
 //
 // Masses are 64-bit fixed point, floor(e * 2^40), added with integer LDS atomics, so the decision does
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
                                                const int32_t* __restrict__ mult, int mult_stride) {
   constexpr int NT = kToppThreads, NW = NT / 64;
   __shared__ float red[2 * NW * 4];
-  __shared__ uint64_t h1[2048], h2[2048], h3[512], cs[64];
+  __shared__ uint64_t h1[2048], h2[512], h3[512], cs[64];
   __shared__ uint64_t s_rem;
   __shared__ int s_bin, s_mode;
   BlockReduce<NW> br{red};
@@ -55,11 +57,11 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     e[j] = (k < ncap) ? lg[k] : -__builtin_inff();
     mloc = fmaxf(mloc, e[j]);
   }
-  for (int i = tid; i < 2048; i += NT) {
-    h1[i] = 0ull;
-    h2[i] = 0ull;
+  for (int i = tid; i < 2048; i += NT) h1[i] = 0ull;
+  if (tid < 512) {
+    h2[tid] = 0ull;
+    h3[tid] = 0ull;
   }
-  if (tid < 512) h3[tid] = 0ull;
   const float M = br.max(mloc);  // its barrier also orders the clearing above
   float Z = 0.f;
   if (M != -__builtin_inff()) {
@@ -79,12 +81,12 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   }
   Z = br.sum(Z);
 
-  // ---- round 1: bits 30..20 ------------------------------------------------------------------------
+  // ---- round 1: first digit (weights carrying mass are >= 2^-40) ---------------------------------------
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     if (e[j] >= 0.f) {
       const uint64_t f = to_fix(e[j]);
-      if (f) atomicAdd((unsigned long long*)&h1[__float_as_uint(e[j]) >> 20], (unsigned long long)f);
+      if (f) atomicAdd((unsigned long long*)&h1[key_d1(__float_as_uint(e[j]))], (unsigned long long)f);
     }
   }
   __syncthreads();
@@ -118,28 +120,28 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   if (s_mode == 0) {
     const uint32_t b1 = (uint32_t)s_bin;
     const uint64_t rem1 = s_rem;
-    // ---- round 2: bits 19..9 inside bin b1 -------------------------------------------------------
+    // ---- round 2: bits 17..9 inside bin b1 (keys below the floor wrap past every bin) --------------
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const uint32_t key = __float_as_uint(e[j]);
-      if (e[j] >= 0.f && (key >> 20) == b1) {
+      if (e[j] >= 0.f && key_d1(key) == b1) {
         const uint64_t f = to_fix(e[j]);
-        if (f) atomicAdd((unsigned long long*)&h2[(key >> 9) & 2047u], (unsigned long long)f);
+        if (f) atomicAdd((unsigned long long*)&h2[key_d2(key)], (unsigned long long)f);
       }
     }
     __syncthreads();
-    coarse(h2, 64);
+    coarse(h2, 16);
     if (wv == 0) {
       int bin;
       uint64_t rem;
-      wide_find(h2, cs, 64, rem1, bin, rem);
+      wide_find(h2, cs, 16, rem1, bin, rem);
       if (lane == 0) {
         s_bin = bin;
         s_rem = rem;
       }
     }
     __syncthreads();
-    const uint32_t pre = (b1 << 11) | (uint32_t)s_bin;
+    const uint32_t pre = key_pre2(b1, (uint32_t)s_bin);
     const uint64_t rem2 = s_rem;
     // ---- round 3: bits 8..0 ------------------------------------------------------------------------
 #pragma unroll
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
       const uint32_t key = __float_as_uint(e[j]);
       if (e[j] >= 0.f && (key >> 9) == pre) {
         const uint64_t f = to_fix(e[j]);
-        if (f) atomicAdd((unsigned long long*)&h3[key & 511u], (unsigned long long)f);
+        if (f) atomicAdd((unsigned long long*)&h3[key_d3(key)], (unsigned long long)f);
       }
     }
     __syncthreads();

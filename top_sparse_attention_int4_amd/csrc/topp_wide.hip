@@ -3,11 +3,11 @@
 // Same threshold search as the block kernel (Paper-Notes "关键设计 / 高效Top-p": find the threshold m
 // with sum_{W_i >= m} W_i >= p by repeated parallel passes, no sort), over the same weights
 // e_i = exp(l_i - M) and the same key, the uint32 image of the non-negative float32 weight.  A
-// bisection of that key over [0, 2^31) decides one key bit per step, top bit first; here each pass
-// over the data decides 11 bits at once from a histogram of the mass per value of those bits (2048
-// bins), which is the outcome of 11 consecutive bisection steps.  Three passes (bits 30..20, 19..9,
-// 8..0) give the exact largest threshold T with mass{e >= T} >= p * Z, so the kept set {e >= T} is
-// the converged bisection's.  With fewer steps requested the threshold keeps only its top `iters`
+// bisection of that key over [0, 2^31) decides one key bit per step, top bit first; here a histogram
+// of the mass per value of a digit of the key decides several steps at once.  Only weights >= 2^-40
+// carry fixed-point mass, so the digits run over keys from that floor: 11 bits of (key - floor) >> 18,
+// then bits 17..9 and 8..0, which give the exact largest threshold T with mass{e >= T} >= p * Z, so
+// the kept set {e >= T} is the converged bisection's.  With fewer steps requested the threshold keeps only its top `iters`
 // bits, the point a shorter bisection stops at: a superset that still reaches p.
 //
 // Masses are 64-bit fixed point, floor(e * 2^40) (e <= 1, at most 2^22 candidates per head), so the
@@ -17,11 +17,11 @@
 //
 // Kernels:
 //   k_wide_hist1    M from the estimate's per-block maxima; e written over the logits; histogram of
-//                   bits 30..20 (four 4096-candidate chunks per block, the next chunk's loads in flight
+//                   the first digit (four 4096-candidate chunks per block, the next chunk's loads in flight
 //                   while one is processed, one flush of integer atomics to the global histogram)
-//   k_wide_collect  resolve bits 30..20; the keys of the candidates inside the chosen bin appended to a
+//   k_wide_collect  resolve the first digit; the keys of the candidates inside its bin appended to a
 //                   per-head buffer (one atomic per block and chunk; their order does not matter)
-//   k_wide_finish   one block per head: bits 19..9 and 8..0 from LDS histograms over the collected keys
+//   k_wide_finish   one block per head: bits 17..9 and 8..0 from LDS histograms over the collected keys
 //                   (the bisection steps left), the threshold
 //   k_wide_mask     per (unit, chunk): head masks, kept mass, union words and their count
 //   k_wide_emit     per (unit, chunk): compaction of the union (ascending ids and K/V rows), outputs
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist1(float* __restrict__
       const float e = x[j];
       if (e >= 0.f) {
         const uint64_t f = to_fix(e);
-        if (f) atomicAdd((unsigned long long*)&h[__float_as_uint(e) >> 20], (unsigned long long)f);
+        if (f) atomicAdd((unsigned long long*)&h[key_d1(__float_as_uint(e))], (unsigned long long)f);
       }
     }
   }
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_collect(const float* __re
     const float (&x)[EPT] = v[c & 1];
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) cnt += (x[j] >= 0.f && (__float_as_uint(x[j]) >> 20) == b1) ? 1 : 0;
+    for (int j = 0; j < EPT; ++j) cnt += (x[j] >= 0.f && key_d1(__float_as_uint(x[j])) == b1) ? 1 : 0;
     int total;
     const int off = block_excl_scan<NW>(cnt, scan_sm, &total);
     if (total == 0) continue;  // uniform
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_collect(const float* __re
     int pos = s_base + off;
 #pragma unroll
     for (int j = 0; j < EPT; ++j)
-      if (x[j] >= 0.f && (__float_as_uint(x[j]) >> 20) == b1) kout[pos++] = __float_as_uint(x[j]);
+      if (x[j] >= 0.f && key_d1(__float_as_uint(x[j])) == b1) kout[pos++] = __float_as_uint(x[j]);
   }
 }
 
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_collect(const float* __re
 __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint64_t* __restrict__ state,
                                                       const uint32_t* __restrict__ keys, float* threshold) {
   constexpr int FT = 1024, FU = 8;
-  __shared__ uint64_t h2[2048], h3[512], cs[64];
+  __shared__ uint64_t h2[512], h3[512], cs[64];
   __shared__ int s_bin;
   __shared__ uint64_t s_rem;
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -200,8 +200,10 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
   const int n = (int)min(st[kWideNKeys], (uint64_t)ncap);
   uint32_t T = 0u;
   if (mode == 0ull) {
-    for (int i = tid; i < 2048; i += FT) h2[i] = 0ull;
-    if (tid < 512) h3[tid] = 0ull;
+    if (tid < 512) {
+      h2[tid] = 0ull;
+      h3[tid] = 0ull;
+    }
     __syncthreads();
     auto coarse = [&](const uint64_t* h, int ncoarse) {
       if (tid < ncoarse * 16) {
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
       }
       __syncthreads();
     };
-    // bits 19..9 of every collected key
+    // bits 17..9 of every collected key
     for (int i0 = 0; i0 < n; i0 += FT * FU) {
       uint32_t kk[FU];
 #pragma unroll
@@ -222,23 +224,23 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
       for (int e = 0; e < FU; ++e) {
         if (kk[e] != 0xFFFFFFFFu) {
           const uint64_t f = to_fix(__uint_as_float(kk[e]));
-          if (f) atomicAdd((unsigned long long*)&h2[(kk[e] >> 9) & 2047u], (unsigned long long)f);
+          if (f) atomicAdd((unsigned long long*)&h2[key_d2(kk[e])], (unsigned long long)f);
         }
       }
     }
     __syncthreads();
-    coarse(h2, 64);
+    coarse(h2, 16);
     if (wv == 0) {
       int bin;
       uint64_t rem;
-      wide_find(h2, cs, 64, rem1, bin, rem);
+      wide_find(h2, cs, 16, rem1, bin, rem);
       if (lane == 0) {
         s_bin = bin;
         s_rem = rem;
       }
     }
     __syncthreads();
-    const uint32_t pre = (b1 << 11) | (uint32_t)s_bin;
+    const uint32_t pre = key_pre2(b1, (uint32_t)s_bin);
     const uint64_t rem2 = s_rem;
     // bits 8..0 of the keys inside that bin
     for (int i0 = 0; i0 < n; i0 += FT * FU) {
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
       for (int e = 0; e < FU; ++e) {
         if (kk[e] != 0xFFFFFFFFu && (kk[e] >> 9) == pre) {
           const uint64_t f = to_fix(__uint_as_float(kk[e]));
-          if (f) atomicAdd((unsigned long long*)&h3[kk[e] & 511u], (unsigned long long)f);
+          if (f) atomicAdd((unsigned long long*)&h3[key_d3(kk[e])], (unsigned long long)f);
         }
       }
     }

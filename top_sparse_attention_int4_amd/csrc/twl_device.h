@@ -289,6 +289,17 @@ constexpr float kFixScale = 1099511627776.0f;  // 2^40
 
 __device__ __forceinline__ uint64_t to_fix(float e) { return (uint64_t)(e * kFixScale); }
 
+// Digits of the threshold key.  Only weights >= 2^-40 carry mass (floor(e 2^40) >= 1), so the search
+// runs over keys from the image of 2^-40 up: 11 bits of (key - floor) >> 18 (the exponent and five
+// mantissa bits; below 2048 for weights under 2^24, as the fixed-point masses require), then bits
+// 17..9 and 8..0 (the floor has no bits below 23, so those are the key's own bits).
+constexpr uint32_t kKeyFloor = 87u << 23;  // uint32 image of 2^-40
+__device__ __forceinline__ uint32_t key_d1(uint32_t key) { return (key - kKeyFloor) >> 18; }
+__device__ __forceinline__ uint32_t key_d2(uint32_t key) { return (key >> 9) & 511u; }
+__device__ __forceinline__ uint32_t key_d3(uint32_t key) { return key & 511u; }
+// key >> 9 of the keys whose first two digits are d1, d2
+__device__ __forceinline__ uint32_t key_pre2(uint32_t d1, uint32_t d2) { return (kKeyFloor >> 9) + (d1 << 9) + d2; }
+
 __device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t x) {
   // sum over lanes >= l: total minus the exclusive prefix
   const uint64_t p = wave_incl_scan_u64(x);
