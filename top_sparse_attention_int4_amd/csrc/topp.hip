@@ -79,7 +79,7 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
 #pragma unroll
     for (int j = 0; j < E; ++j) e[j] = -1.f;
   }
-  Z = br.sum(Z);
+  // (Z is reduced at the end with the kept mass: the search itself runs on the fixed-point sums)
 
   // ---- round 1: first digit (weights carrying mass are >= 2^-40) ---------------------------------------
 #pragma unroll
@@ -168,25 +168,37 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   float f = 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) f += (e[j] >= m) ? e[j] : 0.f;
-  f = br.sum(f);
+  br.sum2(Z, f);
   if (tid == 0) {
     threshold[bh] = (Z > 0.f) ? m / Z : 0.f;
     if (mass) mass[bh] = (Z > 0.f) ? f / Z : 0.f;
   }
 
-  // head mask: bit k of the head's bitmap <=> candidate k kept
+  // head mask: bit k of the head's bitmap <=> candidate k kept.  Element j of the wave's lanes covers
+  // candidates j NT + 64 wv .. + 63, words 2j, 2j + 1 of the wave's 2E; lane l writes word l (and
+  // 64 + l), so each wave stores its words with one or two instructions
   const int mw = ncap / 32;
+  uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const unsigned long long bal = __ballot(e[j] >= m);
-    const int w = (j * NT + wv * 64) / 32;
-    if (lane == 0) {
-      mask_ws[(size_t)bh * mw + w] = (uint32_t)bal;
-      mask_ws[(size_t)bh * mw + w + 1] = (uint32_t)(bal >> 32);
-      if (head_mask) {
-        if (w < mask_words) head_mask[(size_t)bh * mask_words + w] = (uint32_t)bal;
-        if (w + 1 < mask_words) head_mask[(size_t)bh * mask_words + w + 1] = (uint32_t)(bal >> 32);
-      }
+    const uint32_t lo = (uint32_t)bal, hi = (uint32_t)(bal >> 32);
+    if (2 * j < 64) {
+      if (lane == 2 * j) w0 = lo;
+      if (lane == 2 * j + 1) w0 = hi;
+    } else {
+      if (lane == 2 * j - 64) w1 = lo;
+      if (lane == 2 * j - 63) w1 = hi;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int wn = 64 * r + lane;  // the wave's word number
+    if (wn < 2 * E) {
+      const int w = (wn >> 1) * (NT / 32) + 2 * wv + (wn & 1);
+      const uint32_t x = r ? w1 : w0;
+      mask_ws[(size_t)bh * mw + w] = x;
+      if (head_mask && w < mask_words) head_mask[(size_t)bh * mask_words + w] = x;
     }
   }
 }
