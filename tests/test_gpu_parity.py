@@ -136,6 +136,48 @@ def test_select_pages_full_size_llama_layer():
         assert cnt[h] == 512 and np.array_equal(ids[h, :512], want)
 
 
+def _check_select_against_oracle(w, ids, cnt):
+    G = w.group
+    for b in range(w.batch):
+        k = w.logical("k", b)
+        for h in range(w.num_kv_heads):
+            u = b * w.num_kv_heads + h
+            kmin, kmax = quantize.page_bounds(k[:, h:h + 1, :])
+            gs = select.group_scores(w.q[b, h * G:(h + 1) * G], kmin[:, 0], kmax[:, 0])
+            want = select.top_pages(gs, select.keep_count(kmin.shape[0], w.keep_frac))
+            assert cnt[u] == len(want), (b, h)
+            assert np.array_equal(ids[u, :cnt[u]], want), (b, h)
+
+
+def test_select_pages_tied_scores():
+    # every sequence repeats 5 page contents, so each score value is shared by many pages and the
+    # K-th key falls inside a run of ties, which go to the lowest page ids
+    w = make_custom(batch=2, num_q_heads=8, num_kv_heads=2, seq_lens=[16 * 700, 16 * 2048], kind="normal",
+                    seed=21, keep_frac=0.25, p=0.9, name="tied_pages")
+    _print_case(w.name)
+    for b in range(w.batch):
+        npg = int(w.seq_lens[b]) // 16
+        phys = w.page_table[b, :npg]
+        w.k_pages[phys] = w.k_pages[phys[np.arange(npg) % 5]]
+    cache, t = device_cache(w)
+    ids, cnt = _select_pages_gpu(w, cache, t, w.keep_frac)
+    k = w.logical("k", 0)
+    kmin, kmax = quantize.page_bounds(k[:, 0:1, :])
+    gs_b0 = select.group_scores(w.q[0, 0:4], kmin[:, 0], kmax[:, 0])
+    assert len(np.unique(gs_b0)) <= 5  # the case really has ties
+    _check_select_against_oracle(w, ids, cnt)
+
+
+def test_select_pages_beyond_register_keys():
+    # 8750 pages in one unit (more than the 8192 scores one block holds in registers)
+    w = make_custom(batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=[140000], kind="outlier", seed=22,
+                    keep_frac=0.25, p=0.9, name="long_unit_select")
+    _print_case(w.name)
+    cache, t = device_cache(w)
+    ids, cnt = _select_pages_gpu(w, cache, t, w.keep_frac)
+    _check_select_against_oracle(w, ids, cnt)
+
+
 # ---- a2-a5: estimate, top-p, union on oracle-given candidates ---------------------------------------
 def _estimate_on_pages(w, cache, t, pages_per_unit, p, iters=32):
     U, Hq = w.batch * w.num_kv_heads, w.num_q_heads

@@ -177,25 +177,32 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
     rowp[r] = reinterpret_cast<const uint4*>(c.kbound + ((size_t)max(pg, 0) * c.Hkv + h) * 2 * kD) +
               (seg < 8 ? 0 : 16) + (seg & 7);
   }
+  // both halves in flight at once (32 x 16 B per lane); the tile then stages one half at a time
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 va[16], vb[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) va[r] = reinterpret_cast<const u32x4*>(rowp[r])[0];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) vb[r] = reinterpret_cast<const u32x4*>(rowp[r])[8];
   float acc[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) acc[i] = 0.f;
-#pragma unroll 1
-  for (int hf = 0; hf < 2; ++hf) {
-    uint4 v[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = rowp[r][8 * hf];
+  for (int r = 0; r < 16; ++r) reinterpret_cast<u32x4*>(tile)[(4 * r + (lane >> 4)) * RS + seg] = va[r];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  page_fold<G>(tile + lane * RS, qp, qn, 0, acc);
+  // the first half's reads are done before the second overwrites the tile
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int r = 0; r < 16; ++r) tile[(4 * r + (lane >> 4)) * RS + seg] = v[r];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    page_fold<G>(tile + lane * RS, qp, qn, 64 * hf, acc);
-    // this half's reads are done before the next one overwrites the tile
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
+  for (int r = 0; r < 16; ++r) reinterpret_cast<u32x4*>(tile)[(4 * r + (lane >> 4)) * RS + seg] = vb[r];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  page_fold<G>(tile + lane * RS, qp, qn, 64, acc);
   if (j < P) {
     float gs = 0.f;
 #pragma unroll
@@ -211,14 +218,20 @@ __device__ __forceinline__ uint32_t desc_key(float f) {
   return ~o;
 }
 
-constexpr int kSelLdsKeys = 8192;
+constexpr int kSelRegKeys = 8192;  // pages per unit held in registers (8 per thread)
 
 // Exact top-K of one unit's page scores: radix select of the K-th smallest key with integer
 // histograms of 8-bit digits, starting below the leading bits that all keys share (a block AND/OR
 // reduction finds them, so no pass histograms a digit every key has in common); ties at the
 // threshold key are resolved towards lower page ids, and an order-preserving compaction writes the
-// kept page ids in ascending order (one scan when every tied key is kept, else a second scan ranks
-// the ties).
+// kept page ids in ascending order.
+//
+// Up to 8192 pages the keys stay in registers (page r * 1024 + tid in slot r of thread tid); the
+// search stops early once every key of the chosen bin is kept, and the compaction is one pass of
+// wave ballots: with `lt` / `eq` the pages whose key is below / equal to the threshold T and take_eq
+// the number of tied pages kept, a page is kept iff lt, or eq with fewer than take_eq tied pages
+// before it, at position (lt pages before it) + min(eq pages before it, take_eq).  Longer units
+// read their scores from global memory in every pass.
 __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* __restrict__ scores,
                                                       float keep_frac, int max_keep, int32_t* page_phys,
                                                       int32_t* page_ids, int32_t* count) {
@@ -229,12 +242,14 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
   const int32_t* pt = c.page_table + (size_t)b * c.maxP;
   int32_t* phys_out = page_phys ? page_phys + (size_t)u * max_keep : nullptr;
   const float* sc = scores + (size_t)u * c.maxP;
-  constexpr int R = kSelLdsKeys / NT;
+  constexpr int R = kSelRegKeys / NT;
   float v[R];
+  int ptv[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {  // score reads in flight with the sequence length
+  for (int r = 0; r < R; ++r) {  // score and page-table reads in flight with the sequence length
     const int i = tid + r * NT;
     v[r] = (i < c.maxP) ? sc[i] : 0.f;
+    ptv[r] = (phys_out && i < c.maxP) ? pt[i] : 0;
   }
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
@@ -254,22 +269,21 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
     return;
   }
 
-  __shared__ uint32_t keys[kSelLdsKeys];
   __shared__ int hist[2][256];
   __shared__ uint32_t s_prefix, s_mask, s_and[NW], s_or[NW];
   __shared__ int s_rem, s_cnt;
   __shared__ int scan_sm[NW + 1];
-  const bool in_lds = P <= kSelLdsKeys;
+  __shared__ int s_clt[R * NW], s_ceq[R * NW];
+  const bool in_regs = P <= kSelRegKeys;
+  uint32_t kk[R];
   uint32_t kand = 0xffffffffu, kor = 0u;
-  if (in_lds) {
+  if (in_regs) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int i = tid + r * NT;
-      if (i < P) {
-        const uint32_t k = desc_key(v[r]);
-        keys[i] = k;
-        kand &= k;
-        kor |= k;
+      kk[r] = desc_key(v[r]);
+      if (tid + r * NT < P) {
+        kand &= kk[r];
+        kor |= kk[r];
       }
     }
   } else {
@@ -301,19 +315,28 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
     kand &= s_and[i];
     kor |= s_or[i];
   }
-  auto key = [&](int i) -> uint32_t { return in_lds ? keys[i] : desc_key(sc[i]); };
+  auto key = [&](int i) -> uint32_t { return desc_key(sc[i]); };
 
   // bits at and above hb are common to every key
   int hb = 32 - __clz((int)(kand ^ kor));
   uint32_t mask = (hb >= 32) ? 0u : ~((1u << hb) - 1u);
   uint32_t prefix = kand & mask;
+  bool early = false;
   for (int pass = 0; hb > 0; ++pass) {
     const int shift = hb > 8 ? hb - 8 : 0;
     const uint32_t dmask = (1u << (hb - shift)) - 1u;
     int* hs = hist[pass & 1];
-    for (int i = tid; i < P; i += NT) {
-      const uint32_t k = key(i);
-      if ((k & mask) == prefix) atomicAdd(&hs[(k >> shift) & dmask], 1);
+    if (in_regs) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r * NT >= P) break;  // uniform: the slots past the unit's pages
+        if (tid + r * NT < P && (kk[r] & mask) == prefix) atomicAdd(&hs[(kk[r] >> shift) & dmask], 1);
+      }
+    } else {
+      for (int i = tid; i < P; i += NT) {
+        const uint32_t k = key(i);
+        if ((k & mask) == prefix) atomicAdd(&hs[(k >> shift) & dmask], 1);
+      }
     }
     __syncthreads();
     if (tid < 64) {
@@ -345,8 +368,52 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
     prefix = s_prefix;
     mask = s_mask;
     hb = shift;
+    if (in_regs && s_cnt == s_rem && hb > 0) {  // every key of the bin is kept: T = the bin's top
+      prefix |= ~mask;
+      early = true;
+      break;
+    }
   }
   const uint32_t T = prefix;
+  if (in_regs) {
+    const int take_eq = early ? P : s_rem;  // tied pages to keep, lowest ids first
+    unsigned long long blt[R], beq[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool ok = tid + r * NT < P;
+      blt[r] = (r * NT < P) ? __ballot(ok && kk[r] < T) : 0ull;
+      beq[r] = (r * NT < P) ? __ballot(ok && kk[r] == T) : 0ull;
+      if (lane == 0) {
+        s_clt[r * NW + wv] = __popcll(blt[r]);
+        s_ceq[r * NW + wv] = __popcll(beq[r]);
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {  // exclusive prefixes over (slot, wave) in page order, two entries per lane
+      const int a0 = s_clt[2 * lane], a1 = s_clt[2 * lane + 1];
+      const int e0 = s_ceq[2 * lane], e1 = s_ceq[2 * lane + 1];
+      const int ia = wave_incl_scan(a0 + a1), ie = wave_incl_scan(e0 + e1);
+      s_clt[2 * lane] = ia - a0 - a1;
+      s_clt[2 * lane + 1] = ia - a1;
+      s_ceq[2 * lane] = ie - e0 - e1;
+      s_ceq[2 * lane + 1] = ie - e1;
+    }
+    __syncthreads();
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r * NT >= P) break;
+      const int lt_before = s_clt[r * NW + wv] + __popcll(blt[r] & below);
+      const int eq_before = s_ceq[r * NW + wv] + __popcll(beq[r] & below);
+      const bool lt = (blt[r] >> lane) & 1ull, eq = (beq[r] >> lane) & 1ull;
+      if (lt || (eq && eq_before < take_eq)) {
+        const int pos = lt_before + min(eq_before, take_eq);
+        out[pos] = tid + r * NT;
+        if (phys_out) phys_out[pos] = ptv[r];
+      }
+    }
+    return;
+  }
   const int take_eq = s_rem;  // pages with key == T to keep, lowest ids first
   const int cnt_eq = s_cnt;   // pages with key == T
 
