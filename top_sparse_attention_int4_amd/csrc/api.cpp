@@ -193,8 +193,10 @@ hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const 
   const bool wide = is_wide(L.ncap);
   hipError_t e;
   if ((e = E.rec(4)) != hipSuccess) return e;
-  e = launch_estimate(c, q, sm, cand, ncap, at<float>(ws, L.logits), at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow),
-                      wide ? &wd : nullptr, s);
+  // token ids of the candidates are read only by the passes that emit the union lists
+  const bool need_tok = with_union || (wide && mass);
+  e = launch_estimate(c, q, sm, cand, ncap, at<float>(ws, L.logits), need_tok ? at<int32_t>(ws, L.ctok) : nullptr,
+                      at<int32_t>(ws, L.crow), wide ? &wd : nullptr, s);
   if (e != hipSuccess) return e;
   if ((e = E.rec(5)) != hipSuccess) return e;
   if ((e = E.rec(6)) != hipSuccess) return e;

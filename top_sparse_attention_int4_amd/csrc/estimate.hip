@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       const int tok = (t >= 0 && t < n) ? t : -1;
       const int row = tok >= 0 ? (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15) : -1;
       s_row[bt][lane] = row;
-      cand_tok[(size_t)u * ncap + k] = tok;
+      if (cand_tok) cand_tok[(size_t)u * ncap + k] = tok;
       cand_row[(size_t)u * ncap + k] = row;
     }
   } else {
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       int tok, row;
       cand_resolve(c, cand, u, b, h, k, n, cnt, tok, row);
       s_row[bt][lane] = row;
-      cand_tok[(size_t)u * ncap + k] = tok;
+      if (cand_tok) cand_tok[(size_t)u * ncap + k] = tok;
       cand_row[(size_t)u * ncap + k] = row;
     }
   }

@@ -75,7 +75,8 @@ hipError_t launch_page_select(const CacheView& c, const float* scores, float kee
                               int32_t* page_ids, int32_t* count, hipStream_t s);
 hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, int32_t* chunk_first,
                                int nchunk, hipStream_t s);
-// wide: when non-null, the estimate also writes the per-block logit maxima and clears the wide state
+// wide: when non-null, the estimate also writes the per-block logit maxima and clears the wide state;
+// cand_tok may be null when no union list is emitted afterwards
 hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
                            float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s);
 // wide top-p: histogram passes and masks (union bitmap in wd.uwords); the emit kernel writes the
