@@ -351,6 +351,26 @@ def test_decode_end_to_end(cfg):
     _check_decode(w, g, pipeline.decode(w))
 
 
+def test_decode_tied_weights():
+    # pages repeat 5 contents, so each weight value is shared by ~60 tokens: the threshold search
+    # meets bins of tied keys and keeps every tie at the threshold
+    w = make_custom(batch=1, num_q_heads=8, num_kv_heads=2, seq_lens=[16 * 300], kind="normal", seed=23,
+                    keep_frac=1.0, p=0.9, name="tied_weights")
+    _print_case(w.name)
+    npg = int(w.seq_lens[0]) // 16
+    phys = w.page_table[0, :npg]
+    w.k_pages[phys] = w.k_pages[phys[np.arange(npg) % 5]]
+    cache, t = device_cache(w)
+    g = run_decode(w, cache, t)
+    _check_decode(w, g, pipeline.decode(w))
+    # the kept set is closed under ties: a token is kept iff every token with the same key is
+    for h in range(w.num_kv_heads):
+        gt = set(unit_tokens(g, h).tolist())
+        for tok in gt:
+            twins = [tok % 16 + 16 * pg for pg in range(tok // 16 % 5, npg, 5)]
+            assert all(x in gt for x in twins), (h, tok)
+
+
 @pytest.mark.parametrize("name", ["C1", "C2"])
 def test_decode_named_configs(name):
     w = make_config(name)
