@@ -17,7 +17,8 @@ Two versions of O5 are given:
       E_g = floor(log2 max_{c in g} |q_c|)  (clamped to >= -100; 0 for an all-zero group)
       Q_c = rne(q_c * 2^(13 - E_g))           integers, |Q_c| <= 16320; exact for every channel
                                               within 2^6 of the group's largest (bf16 has 8 bits)
-      a_g = 2^(E_g - 13) * sum_{c in g} Q_c * code_c     exact (|sum| < 2^23, a float32 integer)
+      a_g = 2^(E_g - 13) * fl(sum_{c in g} Q_c * code_c)  exact for 2- and 4-bit codes (|sum| < 2^23);
+                                                          8-bit sums (< 2^28) round once to float32
       b_g = 2^(E_g - 13) * sum_{c in g} Q_c              exact
       t_g = fl(s_g * a_g) + fl(z_g * b_g)                three rounded fp32 operations
       r = (t_0 + t_1) + (t_2 + t_3);   l = fl(sm * r)
@@ -66,8 +67,8 @@ def logits_spec(qbits_h: np.ndarray, codes: np.ndarray, scale16: np.ndarray, zer
                 sm: float) -> np.ndarray:
     """float32 logits in the committed arithmetic (see module docstring).
 
-    ``qbits_h`` uint16 [128]; ``codes`` uint8 [N][128]; ``scale16``/``zero16`` float16 [N][4];
-    ``sm`` the float32 softmax scale.
+    ``qbits_h`` uint16 [128]; ``codes`` uint8 [N][128] (of any width up to 8 bits);
+    ``scale16``/``zero16`` float16 [N][4]; ``sm`` the float32 softmax scale.
     """
     Q, E = q_fixed(bf16_to_f32(qbits_h))
     c = np.asarray(codes).astype(np.int64)
@@ -76,7 +77,8 @@ def logits_spec(qbits_h: np.ndarray, codes: np.ndarray, scale16: np.ndarray, zer
     t = []
     for g in range(4):
         sl = slice(g * GROUP, (g + 1) * GROUP)
-        a = np.ldexp((c[:, sl] @ Q[sl]).astype(np.float64), int(E[g]) - QFIX_BITS).astype(F32)  # exact
+        # the integer sum is exact in int64 and in float64; one rounding to float32 (none below 2^24)
+        a = np.ldexp((c[:, sl] @ Q[sl]).astype(np.float64), int(E[g]) - QFIX_BITS).astype(F32)
         b = F32(np.ldexp(float(Q[sl].sum()), int(E[g]) - QFIX_BITS))                                # exact
         sa = (s[:, g] * a).astype(F32)
         zb = (z[:, g] * b).astype(F32)

@@ -22,7 +22,7 @@ from . import attention, doublep, estimate, quantize, select, topp
 
 
 def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, keep_frac: float,
-                sm: float, ranges=None, with_f64_logits: bool = False) -> dict:
+                sm: float, ranges=None, with_f64_logits: bool = False, bits: int = 4) -> dict:
     n = kseq.shape[0]
     G = q.shape[0]
     out: dict = {}
@@ -43,7 +43,7 @@ def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, 
         cand = select.candidates_from_pages(out["pages"], n)
     out["candidates"] = cand
     # ---- INT4 estimate, softmax, top-p per query head ------------------------------------------
-    qz = quantize.quantize_rows(kseq[cand]) if cand.size else None
+    qz = quantize.quantize_rows(kseq[cand], bits) if cand.size else None
     heads = []
     for h in range(G):
         if cand.size:
@@ -69,11 +69,12 @@ def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, 
     return out
 
 
-def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=False) -> dict:
+def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=False, bits=4) -> dict:
     """Run the oracle on a workload-like object (fields of ``gen.Workload``).
 
     ``units`` optionally restricts the work to a list of (b, kv-head) pairs; the cluster path is
-    taken when the workload carries clusters (``w.csize`` is not None).
+    taken when the workload carries clusters (``w.csize`` is not None); ``bits`` is the code width
+    of the estimator's key copy.
     Returns ``{(b, h): decode_unit result}``.
     """
     p = w.p if p is None else p
@@ -96,11 +97,11 @@ def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=Fa
             cs = doublep.select_clusters(q, w.centroids[b, h], w.csize[b, h], w.p1, sm)
             ranges = doublep.ranges_of(cs["kept"], w.coff[b, h])
             r = decode_unit(q, kseq, vseq, p=p, keep_frac=1.0, sm=sm, ranges=ranges,
-                            with_f64_logits=with_f64_logits)
+                            with_f64_logits=with_f64_logits, bits=bits)
             r["clusters"] = cs
             r["ranges"] = ranges
         else:
             r = decode_unit(q, kseq, vseq, p=p, keep_frac=keep_frac, sm=sm,
-                            with_f64_logits=with_f64_logits)
+                            with_f64_logits=with_f64_logits, bits=bits)
         res[(b, h)] = r
     return res

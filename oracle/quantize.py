@@ -15,6 +15,12 @@ The pages leave the granularity, the rounding and the nibble order open; the rea
 This is an encoding, so its float32 operation sequence is the specification; numpy float32
 arithmetic performs each operation with IEEE rounding, one at a time.
 
+Other code widths (the pages' precision ablation of the estimator, paperlayer §4.2 and Fig. 6, and the
+4-bit table in Paper-Notes "关键设计 / 4-bit K缓存量化", compare 2-, 4- and 8-bit K copies at p = 0.85
+without defining the other widths' encodings).  Reading: the same scheme with L = 2^bits - 1 levels in
+place of 15 (s = fp16_rne(fp32(max - min) / L), codes clamped to [0, L]), the same groups and fp16
+scale/zero, and 8/bits codes per byte, the lowest-numbered channel in the lowest bits.
+
 O2 is the per-page, per-channel key minimum and maximum over the page's valid slots, used by the
 Quest-style page bound (the base selector that the Twilight pages name but do not define).  Min and
 max of bf16 values are bf16 values, so the bounds are exact.
@@ -31,12 +37,29 @@ NGROUPS = 128 // GROUP
 PAGE = 16
 
 
-def quantize_rows(kbits: np.ndarray) -> dict:
-    """Quantise bf16 key rows ``uint16 [..., 128]``.
+BITS = (2, 4, 8)  # code widths
 
-    Returns ``codes`` uint8 [..., 128], ``packed`` uint8 [..., 64], ``scale`` and ``zero`` float16
-    [..., 4].
+
+def pack_codes(code: np.ndarray, bits: int = 4) -> np.ndarray:
+    """codes uint8 [..., 128] -> uint8 [..., 16 * bits]: byte j holds codes (8/bits) j .. +(8/bits - 1),
+    the first in the lowest bits."""
+    per = 8 // bits
+    c = np.asarray(code, np.uint16).reshape(code.shape[:-1] + (128 // per, per))
+    out = np.zeros(c.shape[:-1], np.uint16)
+    for i in range(per):
+        out |= c[..., i] << (bits * i)
+    return out.astype(np.uint8)
+
+
+def quantize_rows(kbits: np.ndarray, bits: int = 4) -> dict:
+    """Quantise bf16 key rows ``uint16 [..., 128]`` to ``bits``-bit codes.
+
+    Returns ``codes`` uint8 [..., 128], ``packed`` uint8 [..., 16 * bits], ``scale`` and ``zero``
+    float16 [..., 4].
     """
+    if bits not in BITS:
+        raise ValueError("bits must be 2, 4 or 8")
+    L = (1 << bits) - 1
     x = bf16_to_f32(kbits)
     shp = x.shape[:-1]
     xg = x.reshape(shp + (NGROUPS, GROUP))
@@ -45,7 +68,7 @@ def quantize_rows(kbits: np.ndarray) -> dict:
     if not (np.all(np.isfinite(x)) and np.all(np.abs(x) <= 65504.0)):
         raise ValueError("quantisation input must be finite and within the fp16 range")
     rng = (mx - mn).astype(F32)                      # fp32 subtraction
-    s16 = (rng / F32(15.0)).astype(np.float16)      # fp32 division, then fp16 round-to-nearest-even
+    s16 = (rng / F32(L)).astype(np.float16)         # fp32 division, then fp16 round-to-nearest-even
     z16 = mn.astype(np.float16)
     s = s16.astype(F32)
     z = z16.astype(F32)
@@ -53,19 +76,19 @@ def quantize_rows(kbits: np.ndarray) -> dict:
     safe = np.where(s == 0, F32(1.0), s).astype(F32)
     with np.errstate(divide="ignore", invalid="ignore"):
         t = (diff / safe[..., None]).astype(F32)     # fp32 division
-    code = np.clip(np.rint(t), 0, 15)                # rint = round half to even
+    code = np.clip(np.rint(t), 0, L)                 # rint = round half to even
     code = np.where((s == 0)[..., None], 0, code).astype(np.uint8).reshape(shp + (128,))
-    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
-    return {"codes": code, "packed": packed, "scale": s16, "zero": z16}
+    return {"codes": code, "packed": pack_codes(code, bits), "scale": s16, "zero": z16}
 
 
-def unpack_codes(packed: np.ndarray) -> np.ndarray:
-    """uint8 [..., 64] -> codes uint8 [..., 128] (element 2j = low nibble of byte j)."""
+def unpack_codes(packed: np.ndarray, bits: int = 4) -> np.ndarray:
+    """uint8 [..., 16 * bits] -> codes uint8 [..., 128] (for 4 bits: element 2j = low nibble of byte j)."""
     packed = np.asarray(packed, dtype=np.uint8)
-    out = np.empty(packed.shape[:-1] + (128,), np.uint8)
-    out[..., 0::2] = packed & 0x0F
-    out[..., 1::2] = packed >> 4
-    return out
+    per = 8 // bits
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1], per), np.uint8)
+    for i in range(per):
+        out[..., i] = (packed >> (bits * i)) & ((1 << bits) - 1)
+    return out.reshape(packed.shape[:-1] + (128,))
 
 
 def dequantize(codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray) -> np.ndarray:
@@ -98,8 +121,8 @@ def page_bounds(kbits_seq: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 # Expected device arrays in the paged layout (for element-by-element comparison)
 # --------------------------------------------------------------------------------------------------
 def expected_paged(k_pages: np.ndarray, page_table: np.ndarray, seq_lens: np.ndarray,
-                   tok_begin=None, tok_end=None) -> dict:
-    """Expected ``k4`` [P][Hkv][16][64] u8, ``k4_meta`` [P][Hkv][16][4][2] fp16 bits and ``kbound``
+                   tok_begin=None, tok_end=None, bits: int = 4) -> dict:
+    """Expected ``k4`` [P][Hkv][16][16 * bits] u8, ``k4_meta`` [P][Hkv][16][4][2] fp16 bits and ``kbound``
     [P][Hkv][2][128] bf16 bits for the tokens in [tok_begin[b], tok_end[b]) of each sequence
     (default: the whole sequence).  Entries that the range does not define are returned as masks
     ``tok_mask`` [P][Hkv?][16] and ``page_mask`` [P] so a comparison can skip them.
@@ -108,7 +131,7 @@ def expected_paged(k_pages: np.ndarray, page_table: np.ndarray, seq_lens: np.nda
     B = len(seq_lens)
     tb = np.zeros(B, np.int64) if tok_begin is None else np.asarray(tok_begin, np.int64)
     te = np.asarray(seq_lens, np.int64) if tok_end is None else np.asarray(tok_end, np.int64)
-    k4 = np.zeros((P, Hkv, PAGE, 64), np.uint8)
+    k4 = np.zeros((P, Hkv, PAGE, 16 * bits), np.uint8)
     meta = np.zeros((P, Hkv, PAGE, NGROUPS, 2), np.uint16)
     kb = np.zeros((P, Hkv, 2, 128), np.uint16)
     tok_mask = np.zeros((P, PAGE), bool)
@@ -120,7 +143,7 @@ def expected_paged(k_pages: np.ndarray, page_table: np.ndarray, seq_lens: np.nda
         for j in range(int(first_pg), int(last_pg) + 1):
             phys = int(page_table[b, j])
             rows = k_pages[phys]                      # [Hkv][16][128]
-            q = quantize_rows(rows)
+            q = quantize_rows(rows, bits)
             lo = max(int(tb[b]) - j * PAGE, 0)
             hi = min(int(te[b]) - j * PAGE, PAGE)
             sl = slice(lo, hi)

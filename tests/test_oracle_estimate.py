@@ -30,16 +30,16 @@ def _group_exponents(q):
     return np.array([max(int(np.floor(np.log2(x))), -100) if x > 0 else 0 for x in m])
 
 
-def _bound(qbits, codes, s16, z16, xhat, logits):
-    """|spec - f64| <= sm * (sum_c 2^(E_g - 14) |x^_c| (1 + u) + 5u sum_g (|s_g a_g| + |z_g b_g|)
-                             + u sum_c |q_c| |x^_c|) + 2u |l|.
+def _bound(qbits, codes, s16, z16, xhat, logits, bits=4):
+    """|spec - f64| <= sm * (sum_c 2^(E_g - 14) |x^_c| (1 + u) + k u sum_g (|s_g a_g| + |z_g b_g|)
+                             + u sum_c |q_c| |x^_c|) + 2u |l|,  k = 5 (6 for 8-bit codes).
 
     Derivation: spec in exact arithmetic is sm * sum_c q~_c x_c with |q_c - q~_c| <= 2^(E_g - 14)
     (half a grid step) and x_c = code_c s_g + z_g, whose float32 rounding x^_c is what the float64
     reference uses (<= u |x^_c|).  a_g and b_g are exact; t_g rounds two products and their sum
     (<= 2u (|s_g a_g| + |z_g b_g|)); r adds two levels of rounded sums (<= 2u of the same terms);
     l rounds once more (<= u |l|, doubled for the reference's own rounding).  5u covers 4u plus the
-    second-order terms.
+    second-order terms; 8-bit group sums also round once to float32 (<= u |a_g|), one u more.
     """
     q = numerics.bf16_to_f32(qbits).astype(np.float64)
     E = _group_exponents(q)
@@ -52,7 +52,8 @@ def _bound(qbits, codes, s16, z16, xhat, logits):
     xa = np.abs(xhat.astype(np.float64))
     quant = (xa * step.reshape(1, 128)).sum(-1) * (1 + U)
     xq = (xa * np.abs(q).reshape(1, 128)).sum(-1)
-    return SM * (quant + 5 * U * terms + U * xq) + 2 * U * np.abs(logits)
+    k = 6 if bits == 8 else 5
+    return SM * (quant + k * U * terms + U * xq) + 2 * U * np.abs(logits)
 
 
 def _qvec(rng, scales):
@@ -86,17 +87,18 @@ def test_fixed_point_query_guarantees(seed, kscale, qscales):
         assert np.array_equal(back[big], seg[big])
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("seed,kscale,qscales", QCASES)
-def test_spec_matches_float64_definition(seed, kscale, qscales):
+def test_spec_matches_float64_definition(seed, kscale, qscales, bits):
     rng = np.random.default_rng(seed)
     n = 3000
     kbits = numerics.f32_to_bf16_bits((rng.standard_normal((n, 128)) * kscale).astype(np.float32))
     qbits = _qvec(rng, qscales)
-    qz = quantize.quantize_rows(kbits)
+    qz = quantize.quantize_rows(kbits, bits)
     spec = estimate.logits_spec(qbits, qz["codes"], qz["scale"], qz["zero"], SM).astype(np.float64)
     ref = estimate.logits_f64(qbits, qz["codes"], qz["scale"], qz["zero"], SM)
     xhat = quantize.dequantize(qz["codes"], qz["scale"], qz["zero"])
-    bound = _bound(qbits, qz["codes"], qz["scale"], qz["zero"], xhat, ref)
+    bound = _bound(qbits, qz["codes"], qz["scale"], qz["zero"], xhat, ref, bits)
     assert np.all(np.abs(spec - ref) <= bound)
     # the bound is tight enough to catch a dropped zero-point term
     q = numerics.bf16_to_f32(qbits).astype(np.float64)
@@ -145,6 +147,26 @@ def test_grid_query_and_grid_keys_give_exact_bf16_logits():
     terms = (xa * np.abs(qq)).sum(-1)
     # only t_g, r and l round: <= sm * 5u * sum|q x| + 2u |l|
     assert np.all(np.abs(spec - exact) <= SM * 5 * U * terms + 2 * U * np.abs(exact))
+
+
+def test_eight_bit_group_sums_round_once():
+    # the largest 8-bit group sum (all codes 255 against Q = 16320) exceeds 2^24, so the spec rounds
+    # it once to float32: compare with the integer sum rounded by hand (nearest even multiple of 8)
+    codes = np.full((1, 128), 255, np.uint8)
+    q = np.full(128, 0.99, np.float32)
+    qbits = numerics.f32_to_bf16_bits(q)
+    Q, E = estimate.q_fixed(numerics.bf16_to_f32(qbits))
+    S = int(Q[:32].sum()) * 255
+    assert S > 2**24
+    step = 1 << (S.bit_length() - 24)
+    lo = S - S % step
+    rnd = lo + step if (S - lo > step // 2 or (S - lo == step // 2 and (lo // step) % 2 == 1)) else lo
+    s16 = np.ones((1, 4), np.float16)
+    z16 = np.zeros((1, 4), np.float16)
+    l = estimate.logits_spec(qbits, codes, s16, z16, 1.0)
+    a = np.float32(np.ldexp(float(rnd), int(E[0]) - 13))
+    t = a  # s = 1, z = 0: each t_g is a_g, the same in every group
+    assert l[0] == np.float32(np.float32(t + t) + np.float32(t + t))
 
 
 def test_softmax_properties():
