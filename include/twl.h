@@ -21,8 +21,8 @@
  *   nothing has been enqueued and no output has been written.  Device-resident values (seq_lens,
  *   page tables, candidate lists) cannot be validated on the host: out-of-range values there are
  *   skipped by the kernels where stated, otherwise the behaviour is undefined.
- * - TWL_EUNSUPPORTED: head_dim != 128, page_size != 16, quant_group != 32, a GQA group size not in
- *   {1, 2, 4, 8}, or a current device that is not gfx950.  TWL_EHIP: a kernel launch failed (the
+ * - TWL_EUNSUPPORTED: head_dim != 128, page_size != 16, quant_group != 32, key_bits not in
+ *   {0, 2, 4, 8}, a GQA group size not in {1, 2, 4, 8}, or a current device that is not gfx950.  TWL_EHIP: a kernel launch failed (the
  *   HIP error is left for hipGetLastError()).  Device faults surface at the caller's next
  *   synchronisation.
  * - Results are deterministic: the same inputs give bitwise identical outputs on every run.  The
@@ -33,7 +33,9 @@
  * ------------------------------------------------------------------------------
  *   k, v      bf16 [num_phys_pages][Hkv][16][128]     token t of sequence b: physical page
  *                                                     page_table[b][t/16], slot t%16
- *   k4        u8   [num_phys_pages][Hkv][16][64]      INT4 codes, byte j = code(2j) | code(2j+1)<<4
+ *   k4        u8   [num_phys_pages][Hkv][16][16*kb]   key codes of kb = key_bits bits, 8/kb per byte with the
+ *                                                     lowest channel in the lowest bits (kb = 4: byte j =
+ *                                                     code(2j) | code(2j+1)<<4)
  *   k4_meta   fp16 [num_phys_pages][Hkv][16][4][2]    per 32-channel group: (scale, zero)
  *   kbound    bf16 [num_phys_pages][Hkv][2][128]      per page: channel-wise key min row, max row
  *   q         bf16 [B][Hq][128]; query head hq belongs to kv-head hq / G
@@ -74,6 +76,8 @@ typedef struct twl_cache {
   void* k4;                   /* INT4 key codes (written by twl_quantize_k)                      */
   void* k4_meta;              /* fp16 scale/zero (written by twl_quantize_k)                     */
   void* kbound;               /* bf16 page key bounds (written by twl_quantize_k)                */
+  int32_t key_bits;           /* code width of k4: 4 (0 means 4), or 2 / 8 for the estimator's    */
+                              /* precision ablation (paperlayer §4.2, Fig. 6)                    */
 } twl_cache;
 
 /* Candidate tokens of each (sequence b, kv-head h) unit, i.e. the base selector's output.
@@ -110,8 +114,8 @@ size_t twl_workspace_bytes(const twl_cache* cache, int64_t max_candidates_per_gr
  * paperlayer §4.2 and §B.1 -- dynamic quantisation with fp16 scales and zero points, two 4-bit
  * values per byte).  For every sequence b and token t in [tok_begin[b], tok_end[b]) and every
  * kv-head: asymmetric min/max quantisation of each 32-channel group of the bf16 key row,
- *   scale = fp16_rne(fp32(max-min)/15), zero = fp16_rne(min),
- *   code  = 0 if scale == 0 else clamp(rint_even(fp32(x-zero)/scale), 0, 15),
+ *   scale = fp16_rne(fp32(max-min)/L), zero = fp16_rne(min), L = 2^key_bits - 1 (15 for 4 bits),
+ *   code  = 0 if scale == 0 else clamp(rint_even(fp32(x-zero)/scale), 0, L),
  * written to k4 / k4_meta; and for every page the range touches, kbound = channel-wise min and max
  * over the page's slots holding tokens < tok_end[b] (the Quest-style page bound).
  *   tok_begin, tok_end  device int32 [B]; 0 <= tok_begin <= tok_end <= 16*max_pages_per_seq

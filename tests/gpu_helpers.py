@@ -14,10 +14,10 @@ from gen.device import upload
 SM = twl.DEFAULT_SM_SCALE
 
 
-def device_cache(w, device="cuda"):
+def device_cache(w, device="cuda", key_bits=4):
     t = upload(w, device)
     cache = twl.PagedCache(t["k_pages"], t["v_pages"], t["page_table"], t["seq_lens"], w.num_q_heads,
-                           max_seq_len=max(w.max_seq_len, 0))
+                           max_seq_len=max(w.max_seq_len, 0), key_bits=key_bits)
     tb = torch.zeros(w.batch, dtype=torch.int32, device=device)
     twl.quantize_k(cache, tb, t["seq_lens"], max(w.max_seq_len, 0))
     return cache, t

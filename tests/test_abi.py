@@ -68,6 +68,7 @@ def test_workspace_bytes(twl):
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, 2), ("page_size", 32, 2), ("quant_group", 64, 2), ("num_kv_heads", 5, 1),
     ("num_kv_heads", 2, 2), ("batch", 0, 1), ("max_seq_len", 2048 * 16 + 1, 1), ("page_table", None, 1),
+    ("key_bits", 3, 2), ("key_bits", 16, 2), ("key_bits", -4, 2),
 ])
 def test_decode_rejects_bad_cache(twl, field, value, status):
     L = twl.lib()

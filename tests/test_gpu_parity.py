@@ -66,6 +66,22 @@ def test_quantize_bitexact(cfg):
     assert np.array_equal(numerics.bf16_to_f32(kb[pm]), numerics.bf16_to_f32(exp["kbound"][pm]))
 
 
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("cfg", [TINY[0], TINY[3]], ids=[TINY_IDS[0], TINY_IDS[3]])
+def test_quantize_bitexact_other_widths(cfg, bits):
+    w = make_custom(**cfg)
+    _print_case(f"{w.name} bits={bits}")
+    cache, t = device_cache(w, key_bits=bits)
+    torch.cuda.synchronize()
+    exp = quantize.expected_paged(w.k_pages, w.page_table, w.seq_lens, bits=bits)
+    k4 = cache.k4.cpu().numpy()
+    meta = cache.k4_meta.cpu().numpy().view(np.uint16)
+    assert k4.shape[-1] == 16 * bits
+    m3 = np.broadcast_to(exp["tok_mask"][:, None, :], k4.shape[:3])
+    assert np.array_equal(k4[m3], exp["k4"][m3])
+    assert np.array_equal(meta[m3], exp["k4_meta"][m3])
+
+
 def test_quantize_incremental_equals_bulk():
     w = make_custom(batch=2, num_q_heads=4, num_kv_heads=2, seq_lens=[70, 45], seed=12)
     _print_case(w.name)
@@ -234,6 +250,28 @@ def test_estimate_topp_parity(cfg):
         assert np.all(np.diff(unit_tokens(g, u)) > 0)
 
 
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("cfg", [TINY[0], TINY[2], TINY[3]], ids=[TINY_IDS[0], TINY_IDS[2], TINY_IDS[3]])
+def test_estimate_topp_parity_other_widths(cfg, bits):
+    w = make_custom(**cfg)
+    _print_case(f"{w.name} bits={bits}")
+    cache, t = device_cache(w, key_bits=bits)
+    res = pipeline.decode(w, bits=bits)
+    G = w.group
+    pages = [res[(b, h)]["pages"] for b in range(w.batch) for h in range(w.num_kv_heads)]
+    g = _estimate_on_pages(w, cache, t, pages, w.p)
+    from oracle.topp import set_matches
+    for (b, h), r in res.items():
+        ncand = len(r["candidates"])
+        for j, hd in enumerate(r["heads"]):
+            hq = h * G + j
+            sel = _mask_indices(g["mask"][b, hq], ncand)
+            ok, msg = set_matches(sel, hd["topp"], hd["W"], w.p)
+            assert ok, (b, hq, msg)
+            if ncand:
+                assert abs(g["mass"][b, hq] - math.fsum(hd["W"][sel])) < 1e-5
+
+
 def test_topp_p_one_and_few_iterations():
     w = make_custom(batch=1, num_q_heads=4, num_kv_heads=1, seq_lens=[900], seed=3, keep_frac=0.5)
     _print_case(w.name)
@@ -349,6 +387,15 @@ def test_decode_end_to_end(cfg):
     cache, t = device_cache(w)
     g = run_decode(w, cache, t)
     _check_decode(w, g, pipeline.decode(w))
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+def test_decode_end_to_end_other_widths(bits):
+    w = make_custom(**TINY[0])
+    _print_case(f"{w.name} bits={bits}")
+    cache, t = device_cache(w, key_bits=bits)
+    g = run_decode(w, cache, t)
+    _check_decode(w, g, pipeline.decode(w, bits=bits))
 
 
 def test_decode_tied_weights():

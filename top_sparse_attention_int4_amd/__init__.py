@@ -49,7 +49,7 @@ class CacheC(ctypes.Structure):
         ("page_size", _i32), ("quant_group", _i32), ("max_pages_per_seq", _i32),
         ("num_phys_pages", _i32), ("max_seq_len", _i32),
         ("page_table", _p), ("seq_lens", _p), ("k", _p), ("v", _p),
-        ("k4", _p), ("k4_meta", _p), ("kbound", _p),
+        ("k4", _p), ("k4_meta", _p), ("kbound", _p), ("key_bits", _i32),
     ]
 
 
@@ -141,12 +141,14 @@ class PagedCache:
     """Device tensors of one layer's paged KV cache and its INT4 shadow.
 
     ``k_pages``/``v_pages``: bf16 (or their uint16 bits viewed as int16) [P][Hkv][16][128];
-    ``page_table`` int32 [B][max_pages]; ``seq_lens`` int32 [B].  The INT4 codes, fp16 scale/zero
-    and page bounds are allocated here and filled by :func:`quantize_k`.
+    ``page_table`` int32 [B][max_pages]; ``seq_lens`` int32 [B].  The key codes (``key_bits`` wide:
+    4, or 2 / 8 for the estimator's precision ablation), fp16 scale/zero and page bounds are allocated
+    here and filled by :func:`quantize_k`.
     """
 
     def __init__(self, k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
-                 seq_lens: torch.Tensor, num_q_heads: int, max_seq_len: Optional[int] = None):
+                 seq_lens: torch.Tensor, num_q_heads: int, max_seq_len: Optional[int] = None,
+                 key_bits: int = 4):
         P, Hkv, S, D = k_pages.shape
         if (S, D) != (16, 128) or v_pages.shape != k_pages.shape:
             raise ValueError("k/v pages must be [P][Hkv][16][128]")
@@ -161,12 +163,15 @@ class PagedCache:
         self.num_kv_heads = int(Hkv)
         self.num_phys_pages = int(P)
         self.max_seq_len = int(max_seq_len if max_seq_len is not None else self.max_pages * 16)
-        self.k4 = torch.zeros((P, Hkv, 16, 64), dtype=torch.uint8, device=dev)
+        if key_bits not in (2, 4, 8):
+            raise ValueError("key_bits must be 2, 4 or 8")
+        self.key_bits = int(key_bits)
+        self.k4 = torch.zeros((P, Hkv, 16, 16 * key_bits), dtype=torch.uint8, device=dev)
         self.k4_meta = torch.zeros((P, Hkv, 16, 4, 2), dtype=torch.int16, device=dev)
         self.kbound = torch.zeros((P, Hkv, 2, 128), dtype=torch.int16, device=dev)
         self._c = CacheC(self.batch, self.num_q_heads, self.num_kv_heads, 128, 16, 32, self.max_pages,
                          self.num_phys_pages, self.max_seq_len, _ptr(page_table), _ptr(seq_lens), _ptr(k_pages),
-                         _ptr(v_pages), _ptr(self.k4), _ptr(self.k4_meta), _ptr(self.kbound))
+                         _ptr(v_pages), _ptr(self.k4), _ptr(self.k4_meta), _ptr(self.kbound), self.key_bits)
 
     @property
     def group(self) -> int:

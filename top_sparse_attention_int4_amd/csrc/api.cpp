@@ -27,6 +27,7 @@ twl_status check_cache(const twl_cache* c, bool need_kv, bool need_quant) {
   const int G = c->num_q_heads / c->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return TWL_EUNSUPPORTED;
   if (c->head_dim != 128 || c->page_size != 16 || c->quant_group != 32) return TWL_EUNSUPPORTED;
+  if (c->key_bits != 0 && c->key_bits != 2 && c->key_bits != 4 && c->key_bits != 8) return TWL_EUNSUPPORTED;
   if (c->max_pages_per_seq < 1 || c->num_phys_pages < 1) return TWL_EINVAL;
   if (c->max_seq_len < 0 || (int64_t)c->max_seq_len > 16 * (int64_t)c->max_pages_per_seq) return TWL_EINVAL;
   if ((int64_t)c->num_phys_pages * c->num_kv_heads * 16 >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
@@ -76,6 +77,7 @@ CacheView make_view(const twl_cache* c) {
   v.maxP = c->max_pages_per_seq;
   v.nphys = c->num_phys_pages;
   v.maxTok = c->max_pages_per_seq * 16;
+  v.kbits = c->key_bits == 0 ? 4 : c->key_bits;
   v.page_table = c->page_table;
   v.seq_lens = c->seq_lens;
   v.k = static_cast<const uint16_t*>(c->k);

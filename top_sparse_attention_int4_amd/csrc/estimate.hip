@@ -9,9 +9,11 @@
 //   t_g = fl(s_g a_g) + fl(z_g b_g),  logit = fl(sm * ((t_0 + t_1) + (t_2 + t_3))).
 // The file is compiled without floating-point contraction so that t_g rounds each product.
 //
-// The sums are v_mfma_i32_16x16x32_i8 products: A = 16 candidates x 32 code nibbles (lane (r, kb)
-// reads the 16 code bytes of group kb of candidate r with one load and feeds 8 of them to each of
-// four MFMAs), B = the query digits (Q = 128 hi + lo, both int8), one column per (group, head) and
+// The sums are v_mfma_i32_16x16x32_i8 products: A = 16 candidates x 32 codes (lane (r, kb) reads the
+// code run of group kb of candidate r with one load -- 16 bytes of 4-bit codes; 8 or 32 bytes for the
+// 2- and 8-bit widths of the precision ablation, paperlayer §4.2, Fig. 6 -- and feeds 8 codes as bytes
+// to each of four MFMAs; 8-bit codes go in as code - 128 with the columns started at 128 x the digit
+// sums, and their group sums, up to 2^28, round once to float32), B = the query digits (Q = 128 hi + lo, both int8), one column per (group, head) and
 // zero outside the lane's group, so each output column accumulates one group of one head.  A wave
 // takes 16-candidate tiles; the four groups of a (candidate, head) then meet by two lane exchanges
 // in the committed order.  The block also records, per candidate, its token id and K/V row index,
@@ -146,9 +148,53 @@ __device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView&
 }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// The BITS words of one (candidate, group) code run: 32 codes of BITS bits, lowest channel lowest.
+template <int BITS>
+__device__ __forceinline__ void load_codes(const uint8_t* row, int group, uint32_t (&w)[BITS]) {
+  const uint8_t* p = row + group * 4 * BITS;
+  if constexpr (BITS == 2) {
+    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < BITS / 4; ++h) {
+      const u32x4_t x = reinterpret_cast<const u32x4_t*>(p)[h];
+      w[4 * h] = x.x;
+      w[4 * h + 1] = x.y;
+      w[4 * h + 2] = x.z;
+      w[4 * h + 3] = x.w;
+    }
+  }
+}
+
+// Four 4-bit fields (nibbles 0..3 of t) to the four bytes of a word.
+__device__ __forceinline__ uint32_t nibbles_to_bytes(uint32_t t) {
+  return (t & 0xFu) | ((t & 0xF0u) << 4) | ((t & 0xF00u) << 8) | ((t & 0xF000u) << 12);
+}
+
+// The 8 int8 operands of MFMA j: channels 8j .. 8j + 7 of the group.  For 2 and 4 bits they come in
+// the order (0, 2, 4, 6, 1, 3, 5, 7) of the slice; for 8 bits in channel order, shifted to code - 128.
+template <int BITS>
+__device__ __forceinline__ long code_operand(const uint32_t (&w)[BITS], int j) {
+  if constexpr (BITS == 4) {
+    const uint32_t lo = w[j] & 0x0F0F0F0Fu, hi = (w[j] >> 4) & 0x0F0F0F0Fu;
+    return (long)((uint64_t)lo | ((uint64_t)hi << 32));
+  } else if constexpr (BITS == 2) {
+    const uint32_t x = (w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+    const uint32_t lo = nibbles_to_bytes(x & 0x3333u), hi = nibbles_to_bytes((x >> 2) & 0x3333u);
+    return (long)((uint64_t)lo | ((uint64_t)hi << 32));
+  } else {
+    return (long)(((uint64_t)w[2 * j] | ((uint64_t)w[2 * j + 1] << 32)) ^ 0x8080808080808080ull);
+  }
+}
 
 // NB batches of 64 candidates per block (64 * NB candidates, NB = 2 or 4): 4 NB tiles of 16, NB per wave.
-template <int G, int NB>
+// BITS: code width (2, 4 or 8; rows of 16 * BITS bytes).
+template <int G, int NB, int BITS>
 __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
                                                   CandView cand, int ncap, int chunks_per_unit,
                                                   float* __restrict__ logits, int32_t* __restrict__ cand_tok,
@@ -168,6 +214,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   __shared__ __align__(8) int8_t s_qd[2][G][kD];
   __shared__ int s_qe[G][kGroups];   // group exponents E_g
   __shared__ float s_qb[G][kGroups]; // b_g
+  __shared__ int s_qds[2][G][kGroups];  // per digit, its sum over the group (8-bit codes: the offset of 128)
   __shared__ float s_max[4][G];
   if (wstate) {
     // clear the wide top-p state for the passes that follow this kernel
@@ -258,14 +305,14 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   const int kb = lane >> 4, nn = lane & 15, rg = lane >> 4;
   const int gc = nn / GT, hl = nn - gc * GT;
   const bool colok = nn < kGroups * GT;
-  uint4 cw[NB];
+  uint32_t cw[NB][BITS];
   uint32_t mw[NB][4];
   int rw[NB][4];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int ti = wv + 4 * i;
     const int ra = (&s_row[0][0])[16 * ti + nn];
-    cw[i] = reinterpret_cast<const uint4*>(c.k4 + (size_t)max(ra, 0) * 64)[kb];
+    load_codes<BITS>(c.k4 + (size_t)max(ra, 0) * (16 * BITS), kb, cw[i]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       rw[i][e] = (&s_row[0][0])[16 * ti + 4 * rg + e];
@@ -286,7 +333,8 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       int E = 0;
       if (m > 0.f) E = max((int)(__float_as_uint(m) >> 23) - 127, -100);
       const int Qv = (int)rintf(ldexpf(x, 13 - E));
-      const int w = cl & 7, pos = g * 32 + (cl & ~7) + ((w & 1) ? 4 + (w >> 1) : (w >> 1));
+      const int w = cl & 7;
+      const int pos = g * 32 + (cl & ~7) + (BITS == 8 ? w : ((w & 1) ? 4 + (w >> 1) : (w >> 1)));
       s_qd[0][hh][pos] = (int8_t)(Qv >> 7);   // floor(Q / 128), in [-128, 127]
       s_qd[1][hh][pos] = (int8_t)(Qv & 127);  // Q - 128 floor(Q / 128)
       int qs = Qv;
@@ -295,6 +343,18 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       if (cl == 0) {
         s_qe[hh][g] = E;
         s_qb[hh][g] = ldexpf((float)qs, E - 13);  // exact: |sum Q| < 2^19
+      }
+      if constexpr (BITS == 8) {
+        int d0 = Qv >> 7, d1 = Qv & 127;
+#pragma unroll
+        for (int s = 1; s < 32; s <<= 1) {
+          d0 += __shfl_xor(d0, s, 32);
+          d1 += __shfl_xor(d1, s, 32);
+        }
+        if (cl == 0) {
+          s_qds[0][hh][g] = d0;
+          s_qds[1][hh][g] = d1;
+        }
       }
     }
   }
@@ -315,6 +375,14 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
     ecol[ct] = colok ? s_qe[hh][gc] : 0;
     bcol[ct] = colok ? s_qb[hh][gc] : 0.f;
   }
+  // 8-bit codes enter the contraction as code - 128: each column starts at 128 x its digit sum
+  int acc0[NTL][2];
+#pragma unroll
+  for (int ct = 0; ct < NTL; ++ct) {
+    const int hh = ct * GT + hl;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) acc0[ct][d] = (BITS == 8 && colok) ? 128 * s_qds[d][hh][gc] : 0;
+  }
   float mx[NTL];
 #pragma unroll
   for (int ct = 0; ct < NTL; ++ct) mx[ct] = -__builtin_inff();
@@ -323,12 +391,12 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
     const int ti = wv + 4 * i;
     i32x4_t acc[NTL][2];
 #pragma unroll
-    for (int ct = 0; ct < NTL; ++ct) acc[ct][0] = acc[ct][1] = i32x4_t{0, 0, 0, 0};
-    const uint32_t D[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+    for (int ct = 0; ct < NTL; ++ct)
+#pragma unroll
+      for (int d = 0; d < 2; ++d) acc[ct][d] = i32x4_t{acc0[ct][d], acc0[ct][d], acc0[ct][d], acc0[ct][d]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = D[j] & 0x0F0F0F0Fu, hi = (D[j] >> 4) & 0x0F0F0F0Fu;
-      const long a = (long)((uint64_t)lo | ((uint64_t)hi << 32));
+      const long a = code_operand<BITS>(cw[i], j);
 #pragma unroll
       for (int ct = 0; ct < NTL; ++ct)
 #pragma unroll
@@ -342,7 +410,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int S = acc[ct][0][e] * 128 + acc[ct][1][e];
-        const float av = ldexpf((float)S, ecol[ct] - 13);  // exact
+        const float av = ldexpf((float)S, ecol[ct] - 13);  // exact below 2^24 (2- and 4-bit codes)
         const float s = half_bits_to_float(mw[i][e] & 0xffffu);
         const float z = half_bits_to_float(mw[i][e] >> 16);
         const float sa = s * av;
@@ -402,28 +470,38 @@ hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, cons
   float* pmax = wide ? wide->pmax : nullptr;
   uint64_t* wst = wide ? wide->state : nullptr;
   const size_t wwords = wide ? (size_t)c.B * c.Hq * kWideStateWords : 0;
-#define TWL_EST_G(GG, NB)                                                                                     \
+#define TWL_EST_G(GG, NB, BB)                                                                                 \
   case GG:                                                                                                    \
-    hipLaunchKernelGGL((k_estimate<GG, NB>), grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits,        \
+    hipLaunchKernelGGL((k_estimate<GG, NB, BB>), grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits,    \
                        cand_tok, cand_row, pmax, wst, wwords);                                               \
     break;
-#define TWL_EST_NB(NB)                      \
+#define TWL_EST_NB(NB, BB)                  \
   case NB:                                  \
     switch (c.G) {                          \
-      TWL_EST_G(1, NB)                      \
-      TWL_EST_G(2, NB)                      \
-      TWL_EST_G(4, NB)                      \
-      TWL_EST_G(8, NB)                      \
+      TWL_EST_G(1, NB, BB)                  \
+      TWL_EST_G(2, NB, BB)                  \
+      TWL_EST_G(4, NB, BB)                  \
+      TWL_EST_G(8, NB, BB)                  \
       default: return hipErrorInvalidValue; \
     }                                       \
     break;
-  switch (nb) {
-    TWL_EST_NB(2)
-    TWL_EST_NB(4)
+#define TWL_EST_B(BB)                       \
+  case BB:                                  \
+    switch (nb) {                           \
+      TWL_EST_NB(2, BB)                     \
+      TWL_EST_NB(4, BB)                     \
+      default: return hipErrorInvalidValue; \
+    }                                       \
+    break;
+  switch (c.kbits) {
+    TWL_EST_B(2)
+    TWL_EST_B(4)
+    TWL_EST_B(8)
     default: return hipErrorInvalidValue;
   }
 #undef TWL_EST_G
 #undef TWL_EST_NB
+#undef TWL_EST_B
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// INT4 K cache append and page key bounds.
+// INT4 K cache append (2- and 8-bit codes for the estimator's precision ablation) and page key bounds.
 //
 // Twilight keeps a 4-bit copy of K for weight estimation (Paper-Notes "关键设计 / 4-bit K缓存量化";
 // paperlayer §4.2 and §B.1: dynamic quantisation with fp16 scales and zero points, two values per
@@ -11,6 +11,9 @@
 
 namespace twl {
 
+// BITS: code width (2, 4 or 8); a group's 32 codes fill BITS words, 32 / BITS codes per word with the
+// lowest channel in the lowest bits, and L = 2^BITS - 1 levels.
+template <int BITS>
 __global__ __launch_bounds__(64) void k_quantize(CacheView c, const int32_t* __restrict__ tok_begin,
                                                  const int32_t* __restrict__ tok_end, int span_pages) {
   const int b = blockIdx.x / span_pages;
@@ -50,26 +53,26 @@ __global__ __launch_bounds__(64) void k_quantize(CacheView c, const int32_t* __r
       mx = fmaxf(mx, x[i]);
     }
     const float range = mx - mn;
-    const uint32_t sbits = float_to_half_bits(range / 15.0f);  // IEEE fp32 division, then fp16 RNE
+    constexpr int L = (1 << BITS) - 1, PER = 32 / BITS;
+    const uint32_t sbits = float_to_half_bits(range / (float)L);  // IEEE fp32 division, then fp16 RNE
     const uint32_t zbits = float_to_half_bits(mn);
     const float s = half_bits_to_float(sbits);
     const float z = half_bits_to_float(zbits);
-    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    uint32_t packed[BITS];
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) packed[i] = 0u;
     if (s != 0.0f) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         float t = rintf((x[i] - z) / s);  // round half to even
-        t = fminf(fmaxf(t, 0.0f), 15.0f);
+        t = fminf(fmaxf(t, 0.0f), (float)L);
         const uint32_t code = (uint32_t)t;
-        packed[i >> 3] |= code << (4 * (i & 7));
+        packed[i / PER] |= code << (BITS * (i % PER));
       }
     }
-    uint4 out;
-    out.x = packed[0];
-    out.y = packed[1];
-    out.z = packed[2];
-    out.w = packed[3];
-    reinterpret_cast<uint4*>(c.k4 + (row0 + slot) * 64)[g] = out;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(c.k4 + (row0 + slot) * (16 * BITS)) + g * BITS;
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) dst[i] = packed[i];
     c.k4_meta[(row0 + slot) * kGroups + g] = sbits | (zbits << 16);
   }
 
@@ -94,7 +97,12 @@ hipError_t launch_quantize(const CacheView& c, const int32_t* tok_begin, const i
                            int span_pages, hipStream_t s) {
   if (span_pages <= 0) return hipSuccess;
   dim3 grid((unsigned)(c.B * span_pages), (unsigned)c.Hkv);
-  hipLaunchKernelGGL(k_quantize, grid, dim3(64), 0, s, c, tok_begin, tok_end, span_pages);
+  switch (c.kbits) {
+    case 2: hipLaunchKernelGGL(k_quantize<2>, grid, dim3(64), 0, s, c, tok_begin, tok_end, span_pages); break;
+    case 4: hipLaunchKernelGGL(k_quantize<4>, grid, dim3(64), 0, s, c, tok_begin, tok_end, span_pages); break;
+    case 8: hipLaunchKernelGGL(k_quantize<8>, grid, dim3(64), 0, s, c, tok_begin, tok_end, span_pages); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ constexpr int kGroups = 4;  // 32-channel quantisation groups per key row
 // Device-side view of the paged cache (plain values, passed by value to kernels).
 struct CacheView {
   int B, Hq, Hkv, G, maxP, nphys, maxTok;
+  int kbits;  // code width of k4 (2, 4 or 8): rows of 16 * kbits bytes
   const int32_t* page_table;
   const int32_t* seq_lens;
   const uint16_t* k;
