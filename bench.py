@@ -9,6 +9,10 @@ codes and page bounds alone exceed 1 GiB, so every step reads cold HBM rather th
 Cache, as a many-layer model does (up to 1 GiB of layers are drawn independently, the rest are device
 copies of them at their own addresses).  Inputs are resident in HBM before timing starts.
 
+With ``--estimator-bits`` it instead reports the estimator's precision ablation (2-, 4- and 8-bit K
+codes on the Llama-layer workload at its p = 0.85): the event-timed estimate kernel per layer-step and
+the true attention mass (exact bf16 q.k softmax) of every head's selected set, one JSON line.
+
 Prints ONE JSON line.  ``value`` is microseconds per layer-step (lower is better).  ``roofline``
 describes the split-K attention kernel (the stage that moves most bytes): its algorithmic bytes per
 launch (512 B of K/V rows + 4 B index per kept token, plus the group's q) over its average launch
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0: see above)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: auto)")
+    ap.add_argument("--estimator-bits", action="store_true",
+                    help="report the 2/4/8-bit estimator ablation instead of the step benchmark")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (reference for HBM byte counters)")
     return ap.parse_args()
@@ -84,6 +90,9 @@ def main():
         b.build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.estimator_bits:
+        estimator_bits_report(args, dev)
+        return
     if args.copy_calibration:
         # a plain device copy of known size: 512 MiB read + 512 MiB written per launch
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
@@ -300,6 +309,106 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
     print(json.dumps(rec), flush=True)
+
+
+def estimator_bits_report(args, dev):
+    """The pages' precision ablation (paperlayer §4.2, Fig. 6): top-p at p = 0.85 on weights estimated
+    from 2-, 4- and 8-bit K codes.  Per width: the estimate kernel's event-timed duration (decode
+    steps rotating over enough code copies that they come from HBM), and per query head the exact
+    attention mass of its selected set -- over the base selector's candidates (top-p's domain) and
+    over the whole context -- from a float32 softmax of the bf16 q.k logits."""
+    import torch
+    import top_sparse_attention_int4_amd as twl
+    from gen import make_config
+    from gen.device import upload
+
+    name = "C2" if args.workload == "C2" else args.workload
+    w = make_config(name)
+    if w.csize is not None or w.keep_frac >= 1.0:
+        raise SystemExit("--estimator-bits needs a page-selector workload (C2, C3 or C4)")
+    t = upload(w, dev)
+    B, Hq, Hkv, G = w.batch, w.num_q_heads, w.num_kv_heads, w.group
+    U = B * Hkv
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+    mk = twl.keep_count(w.max_pages, w.keep_frac)
+    maxcand = 16 * mk
+    mw = maxcand // 32
+    # exact logits of every (b, q-head) over its sequence, float32 from bf16
+    kf = t["k_pages"].view(torch.bfloat16).float() if t["k_pages"].dtype != torch.bfloat16 else t["k_pages"].float()
+    qf = t["q"].view(torch.bfloat16).float() if t["q"].dtype != torch.bfloat16 else t["q"].float()
+    exact = {}
+    for b in range(B):
+        n = int(w.seq_lens[b])
+        npg = -(-n // 16)
+        pt = t["page_table"][b, :npg].long()
+        kseq = kf[pt].permute(1, 0, 2, 3).reshape(Hkv, npg * 16, 128)[:, :n]      # [Hkv][n][128]
+        for h in range(Hkv):
+            lg = (kseq[h] @ qf[b, h * G:(h + 1) * G].T).T * sm                       # [G][n]
+            exact[(b, h)] = lg
+    rows = []
+    L = 32  # code copies rotated in the timing (4-bit codes of one copy: 17 MB)
+    for bits in (2, 4, 8):
+        caches = []
+        for li in range(L):
+            c = twl.PagedCache(t["k_pages"], t["v_pages"], t["page_table"], t["seq_lens"], Hq,
+                               max_seq_len=w.max_seq_len, key_bits=bits)
+            twl.quantize_k(c, torch.zeros(B, dtype=torch.int32, device=dev), t["seq_lens"], w.max_seq_len)
+            caches.append(c)
+        ws = torch.empty(twl.workspace_bytes(caches[0], maxcand), dtype=torch.uint8, device=dev)
+        out = torch.empty((B, Hq, 128), device=dev)
+        K = max(args.steps, 20)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * twl.NUM_STAGES)] for _ in range(K)]
+        for i in range(5):
+            twl.decode(caches[i % L], t["q"], p=w.p, keep_frac=w.keep_frac, out=out, ws=ws)
+        torch.cuda.synchronize()
+        for i in range(K):
+            twl.decode_profiled(caches[i % L], t["q"], evs[i], p=w.p, keep_frac=w.keep_frac, out=out, ws=ws)
+        torch.cuda.synchronize()
+        est_us = 1e3 * float(np.mean([evs[i][4].elapsed_time(evs[i][5]) for i in range(K)]))
+        # the selection of one step, split into its stages to read every head's kept set
+        ids = torch.full((U, mk), -1, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(U, dtype=torch.int32, device=dev)
+        twl.select_pages(caches[0], t["q"], w.keep_frac, mk, ids, cnt, ws)
+        thr = torch.empty((B, Hq), device=dev)
+        mass = torch.empty((B, Hq), device=dev)
+        hm = torch.zeros((B, Hq, mw), dtype=torch.int32, device=dev)
+        indptr = torch.empty(U + 1, dtype=torch.int32, device=dev)
+        toks = torch.empty(U * maxcand, dtype=torch.int32, device=dev)
+        twl.estimate_topp(caches[0], t["q"], sm, w.p, 32, page_ids=ids, count=cnt, max_items=mk, threshold=thr,
+                          mass=mass, head_mask=hm, mask_words=mw, sel_indptr=indptr, sel_tokens=toks, ws=ws)
+        torch.cuda.synchronize()
+        ids_h, cnt_h = ids.cpu().numpy(), cnt.cpu().numpy()
+        bits_m = np.unpackbits(hm.cpu().numpy().view(np.uint8), axis=-1, bitorder="little")
+        m_cand, m_full, frac = [], [], []
+        for b in range(B):
+            n = int(w.seq_lens[b])
+            for h in range(Hkv):
+                u = b * Hkv + h
+                pages = ids_h[u, :cnt_h[u]].astype(np.int64)
+                cand = (pages[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
+                ok = cand < n
+                lg = exact[(b, h)]
+                cidx = torch.from_numpy(cand[ok]).to(dev)
+                for j in range(G):
+                    sel = np.nonzero(bits_m[b, h * G + j, :cand.size][ok])[0]
+                    wc = torch.softmax(lg[j, cidx], 0)
+                    wf = torch.softmax(lg[j], 0)
+                    s_idx = torch.from_numpy(sel).to(dev)
+                    m_cand.append(float(wc[s_idx].sum()))
+                    m_full.append(float(wf[cidx[s_idx]].sum()))
+                    frac.append(sel.size / max(1, int(ok.sum())))
+        rows.append({"bits": bits, "estimate_us": round(est_us, 3),
+                     "true_mass_over_candidates": {"mean": round(float(np.mean(m_cand)), 5),
+                                                   "min": round(float(np.min(m_cand)), 5)},
+                     "true_mass_over_context": {"mean": round(float(np.mean(m_full)), 5),
+                                                "min": round(float(np.min(m_full)), 5)},
+                     "kept_fraction_of_candidates": round(float(np.mean(frac)), 5),
+                     "code_bytes_per_candidate_head": 16 * bits + 16})
+        del caches
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "estimator precision ablation (top-p at p, true selected mass vs code bits)",
+                      "workload": name, "p": w.p, "heads": B * Hq, "steps": K, "data": "synthetic",
+                      "rows": rows}))
 
 
 def cpu_baseline(w, units: int):
