@@ -13,6 +13,11 @@ With ``--estimator-bits`` it instead reports the estimator's precision ablation 
 codes on the Llama-layer workload at its p = 0.85): the event-timed estimate kernel per layer-step and
 the true attention mass (exact bf16 q.k softmax) of every head's selected set, one JSON line.
 
+With ``--offload`` it runs the offloading scenario of the pages (paperlayer §E): the bf16 K/V of the
+Llama-layer workload stay in pinned host memory and the kernels read the selected rows over PCIe,
+while the INT4 codes and page bounds sit in HBM; it times the decode step with top-p (p = 0.85) and
+with the base selector alone (p = 1: every selected page is loaded, Quest's budget), one JSON line.
+
 Prints ONE JSON line.  ``value`` is microseconds per layer-step (lower is better).  ``roofline``
 describes the split-K attention kernel (the stage that moves most bytes): its algorithmic bytes per
 launch (512 B of K/V rows + 4 B index per kept token, plus the group's q) over its average launch
@@ -59,6 +64,8 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: auto)")
     ap.add_argument("--estimator-bits", action="store_true",
                     help="report the 2/4/8-bit estimator ablation instead of the step benchmark")
+    ap.add_argument("--offload", action="store_true",
+                    help="time the decode with K/V in pinned host memory (top-p vs the base selector alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run 5 plain 512 MiB device copies (reference for HBM byte counters)")
     return ap.parse_args()
@@ -92,6 +99,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.estimator_bits:
         estimator_bits_report(args, dev)
+        return
+    if args.offload:
+        offload_report(args, dev)
         return
     if args.copy_calibration:
         # a plain device copy of known size: 512 MiB read + 512 MiB written per launch
@@ -409,6 +419,62 @@ def estimator_bits_report(args, dev):
     print(json.dumps({"metric": "estimator precision ablation (top-p at p, true selected mass vs code bits)",
                       "workload": name, "p": w.p, "heads": B * Hq, "steps": K, "data": "synthetic",
                       "rows": rows}))
+
+
+def offload_report(args, dev):
+    """K/V in pinned host memory (paperlayer §E): decode µs per layer-step with top-p at the workload's
+    p and with p = 1 (the base selector's pages all loaded, as Quest alone would), plus the K/V rows
+    each loads; the same decode with K/V in HBM for reference."""
+    import torch
+    import top_sparse_attention_int4_amd as twl
+    from gen import make_config
+    from gen.device import upload
+
+    name = args.workload
+    w = make_config(name)
+    if w.csize is not None:
+        raise SystemExit("--offload runs the page-selector workloads (C1-C4)")
+    t = upload(w, dev)
+    B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
+    U = B * Hkv
+    maxcand = 16 * twl.keep_count(w.max_pages, w.keep_frac) if w.keep_frac < 1.0 else w.max_seq_len
+    zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+    kh = t["k_pages"].cpu().pin_memory()
+    vh = t["v_pages"].cpu().pin_memory()
+    placements = {}
+    for where, (kk, vv) in (("host", (kh, vh)), ("device", (t["k_pages"], t["v_pages"]))):
+        c = twl.PagedCache(kk, vv, t["page_table"], t["seq_lens"], Hq, max_seq_len=w.max_seq_len)
+        twl.quantize_k(c, zeros, t["seq_lens"], w.max_seq_len)
+        placements[where] = c
+    torch.cuda.synchronize()
+    ws = torch.empty(twl.workspace_bytes(placements["host"], maxcand), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, 128), device=dev)
+    indptr = torch.zeros(U + 1, dtype=torch.int32, device=dev)
+    toks = torch.empty(U * maxcand, dtype=torch.int32, device=dev)
+    K = max(10, min(args.steps, 50))
+    rows = []
+    for where, c in placements.items():
+        for mode, p in (("top-p", w.p), ("base selector only (p = 1)" if w.keep_frac < 1.0 else "dense (p = 1)", 1.0)):
+            for _ in range(3):
+                twl.decode(c, t["q"], p=p, keep_frac=w.keep_frac, out=out, ws=ws)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(K):
+                twl.decode(c, t["q"], p=p, keep_frac=w.keep_frac, out=out, ws=ws)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / K * 1e3
+            twl.decode(c, t["q"], p=p, keep_frac=w.keep_frac, out=out, ws=ws, sel_indptr=indptr, sel_tokens=toks)
+            torch.cuda.synchronize()
+            loaded = int(indptr[-1].item())
+            rows.append({"kv": where, "mode": mode, "p": p, "us_per_layer_step": round(us, 1),
+                         "kv_rows_loaded": loaded, "kv_bytes_loaded": loaded * 512,
+                         "kv_gb_per_s": round(loaded * 512 / (us * 1e-6) / 1e9, 1)})
+    host = [r["us_per_layer_step"] for r in rows if r["kv"] == "host"]
+    print(json.dumps({"metric": "offloaded-KV decode µs/layer-step (top-p vs base selector alone)",
+                      "workload": name, "steps": K, "data": "synthetic", "rows": rows,
+                      "host_speedup_of_top_p": round(host[1] / host[0], 2)}))
 
 
 def cpu_baseline(w, units: int):

@@ -398,6 +398,26 @@ def test_decode_end_to_end_other_widths(bits):
     _check_decode(w, g, pipeline.decode(w, bits=bits))
 
 
+def test_decode_with_kv_in_pinned_host_memory():
+    # the offloading scenario: K/V stay in pinned host memory, read over PCIe by the same kernels;
+    # every output is bitwise the device-resident run's
+    w = make_custom(**TINY[3])
+    _print_case(w.name + " host K/V")
+    cache, t = device_cache(w)
+    g_dev = run_decode(w, cache, t)
+    kh = t["k_pages"].cpu().pin_memory()
+    vh = t["v_pages"].cpu().pin_memory()
+    cache_h = twl.PagedCache(kh, vh, t["page_table"], t["seq_lens"], w.num_q_heads, max_seq_len=w.max_seq_len)
+    twl.quantize_k(cache_h, torch.zeros(w.batch, dtype=torch.int32, device="cuda"), t["seq_lens"], w.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(cache_h.k4, cache.k4) and torch.equal(cache_h.kbound, cache.kbound)
+    g_host = run_decode(w, cache_h, t)
+    for k in ("out", "lse", "thr", "indptr"):
+        assert np.array_equal(np.asarray(g_host[k]), np.asarray(g_dev[k]), equal_nan=True), k
+    n = int(g_dev["indptr"][-1])
+    assert np.array_equal(g_host["tokens"][:n], g_dev["tokens"][:n])
+
+
 def test_decode_tied_weights():
     # pages repeat 5 contents, so each weight value is shared by ~60 tokens: the threshold search
     # meets bins of tied keys and keeps every tie at the threshold

@@ -112,9 +112,26 @@ def _check(status: int) -> None:
         raise TwlError(status, status_str(status))
 
 
-def _ptr(t: Optional[torch.Tensor]):
+def _host_mapped_ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    """Device address of a pinned host tensor (the HIP runtime's mapping of that host memory)."""
+    fn = lib().hipHostGetDevicePointer
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    out = ctypes.c_void_p()
+    if fn(ctypes.byref(out), ctypes.c_void_p(t.data_ptr()), 0) != 0 or not out.value:
+        raise ValueError("the pinned host tensor has no device mapping")
+    return out
+
+
+def _ptr(t: Optional[torch.Tensor], allow_host: bool = False):
     if t is None:
         return None
+    if allow_host and t.device.type == "cpu":
+        if not t.is_pinned():
+            raise ValueError("host-resident K/V must be pinned (pin_memory=True)")
+        if not t.is_contiguous():
+            raise ValueError("libtwl takes contiguous tensors")
+        return _host_mapped_ptr(t)
     if t.device.type != "cuda":
         raise ValueError("libtwl takes device tensors")
     if not t.is_contiguous():
@@ -143,7 +160,9 @@ class PagedCache:
     ``k_pages``/``v_pages``: bf16 (or their uint16 bits viewed as int16) [P][Hkv][16][128];
     ``page_table`` int32 [B][max_pages]; ``seq_lens`` int32 [B].  The key codes (``key_bits`` wide:
     4, or 2 / 8 for the estimator's precision ablation), fp16 scale/zero and page bounds are allocated
-    here and filled by :func:`quantize_k`.
+    here and filled by :func:`quantize_k`.  ``k_pages``/``v_pages`` may instead be pinned host tensors
+    (the offloading scenario): the kernels then read them over PCIe through the runtime's mapping of
+    that memory, while the codes, bounds and everything else stay in device memory.
     """
 
     def __init__(self, k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
@@ -152,7 +171,9 @@ class PagedCache:
         P, Hkv, S, D = k_pages.shape
         if (S, D) != (16, 128) or v_pages.shape != k_pages.shape:
             raise ValueError("k/v pages must be [P][Hkv][16][128]")
-        dev = k_pages.device
+        dev = page_table.device
+        if dev.type != "cuda":
+            raise ValueError("page_table must be a device tensor")
         self.k = k_pages
         self.v = v_pages
         self.page_table = page_table
@@ -170,8 +191,9 @@ class PagedCache:
         self.k4_meta = torch.zeros((P, Hkv, 16, 4, 2), dtype=torch.int16, device=dev)
         self.kbound = torch.zeros((P, Hkv, 2, 128), dtype=torch.int16, device=dev)
         self._c = CacheC(self.batch, self.num_q_heads, self.num_kv_heads, 128, 16, 32, self.max_pages,
-                         self.num_phys_pages, self.max_seq_len, _ptr(page_table), _ptr(seq_lens), _ptr(k_pages),
-                         _ptr(v_pages), _ptr(self.k4), _ptr(self.k4_meta), _ptr(self.kbound), self.key_bits)
+                         self.num_phys_pages, self.max_seq_len, _ptr(page_table), _ptr(seq_lens),
+                         _ptr(k_pages, allow_host=True), _ptr(v_pages, allow_host=True), _ptr(self.k4),
+                         _ptr(self.k4_meta), _ptr(self.kbound), self.key_bits)
 
     @property
     def group(self) -> int:
