@@ -22,7 +22,10 @@ from . import attention, doublep, estimate, quantize, select, topp
 
 
 def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, keep_frac: float,
-                sm: float, ranges=None, with_f64_logits: bool = False, bits: int = 4) -> dict:
+                sm: float, ranges=None, with_f64_logits: bool = False, bits: int = 4, topk: int = 0,
+                headwise: bool = False) -> dict:
+    """``topk`` > 0 replaces each head's top-p set by its top-k set (the fixed-budget baseline);
+    ``headwise`` makes each query head attend over its own set instead of the group's union."""
     n = kseq.shape[0]
     G = q.shape[0]
     out: dict = {}
@@ -52,7 +55,7 @@ def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, 
         else:
             lg = np.zeros(0, np.float32)
             W = np.zeros(0)
-        res = topp.topp_sort(W, p)
+        res = topp.topk_sort(W, topk) if topk > 0 else topp.topp_sort(W, p)
         hd = {"logits": lg, "W": W, "topp": res, "tokens": cand[res["sel"]]}
         if with_f64_logits and cand.size:
             hd["logits_f64"] = estimate.logits_f64(q[h], qz["codes"], qz["scale"], qz["zero"], sm)
@@ -64,12 +67,13 @@ def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, 
     o = np.zeros((G, 128))
     lse = np.zeros(G)
     for h in range(G):
-        o[h], lse[h] = attention.sparse_attention(q[h], kseq, vseq, U, sm)
+        o[h], lse[h] = attention.sparse_attention(q[h], kseq, vseq, heads[h]["tokens"] if headwise else U, sm)
     out["out"], out["lse"] = o, lse
     return out
 
 
-def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=False, bits=4) -> dict:
+def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=False, bits=4, topk=0,
+           headwise=False) -> dict:
     """Run the oracle on a workload-like object (fields of ``gen.Workload``).
 
     ``units`` optionally restricts the work to a list of (b, kv-head) pairs; the cluster path is
@@ -102,6 +106,6 @@ def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=Fa
             r["ranges"] = ranges
         else:
             r = decode_unit(q, kseq, vseq, p=p, keep_frac=keep_frac, sm=sm,
-                            with_f64_logits=with_f64_logits, bits=bits)
+                            with_f64_logits=with_f64_logits, bits=bits, topk=topk, headwise=headwise)
         res[(b, h)] = r
     return res

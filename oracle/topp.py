@@ -89,6 +89,43 @@ def set_matches(gpu_sel: np.ndarray, res: dict, W: np.ndarray, p: float) -> tupl
     return True, f"ok (|diff|={diff.size}, amb_i={res['amb_i'].size}, amb_ii={res['amb_ii'].size})"
 
 
+FLOOR = 2.0**-40  # weights below this fraction of the largest carry no mass in the search
+
+
+def topk_sort(W: np.ndarray, k: int) -> dict:
+    """Top-k baseline at a fixed budget (the comparison the pages draw against top-p: paperlayer §3,
+    Fig. 2-3, and Paper-Notes "研究背景"): the k largest weights, every weight tied with the k-th kept.
+
+    Reading for the tail: weights below FLOOR times the largest count as one tie at zero, so a budget
+    that reaches them keeps every candidate (the search in the kernels resolves keys from that floor
+    up).  Returns ``sel`` (sorted indices), ``w_star`` (the k-th largest weight, 0 when all are kept)
+    and ``amb_i`` (indices within TAU_W relative of w_star: their membership is decided by rounding).
+    """
+    W = np.asarray(W, dtype=np.float64)
+    N = W.size
+    e = np.zeros(0, np.int64)
+    if N == 0 or k <= 0:
+        return {"sel": e, "w_star": math.nan, "amb_i": e}
+    above = int(np.count_nonzero(W >= FLOOR * W.max()))
+    if k > above:
+        return {"sel": np.arange(N), "w_star": 0.0, "amb_i": e}
+    ws = np.sort(W)[::-1]
+    w_star = float(ws[k - 1])
+    sel = np.nonzero(W >= w_star)[0]
+    amb_i = np.nonzero(np.abs(W - w_star) <= TAU_W * w_star)[0]
+    return {"sel": sel, "w_star": w_star, "amb_i": amb_i}
+
+
+def topk_matches(gpu_sel: np.ndarray, res: dict) -> tuple[bool, str]:
+    """Parity rule for top-k: the symmetric difference lies inside the near-ties of the k-th weight."""
+    g = np.unique(np.asarray(gpu_sel, np.int64))
+    diff = np.setxor1d(g, res["sel"])
+    bad = np.setdiff1d(diff, res["amb_i"])
+    if bad.size:
+        return False, f"{bad.size} unambiguous tokens differ (e.g. {bad[:8].tolist()})"
+    return True, f"ok (|diff|={diff.size})"
+
+
 def topp_bisect(w: np.ndarray, p: float, iters: int = 32) -> dict:
     """Bisection on the uint32 image of float32 weights ``w`` (not necessarily normalised).
 

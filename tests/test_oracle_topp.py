@@ -136,3 +136,32 @@ def test_set_rule_on_empty_candidates():
     r = topp.topp_sort(np.zeros(0), 0.9)
     assert topp.set_matches(np.zeros(0, np.int64), r, np.zeros(0), 0.9)[0]
     assert not topp.set_matches(np.array([0]), r, np.zeros(0), 0.9)[0]
+
+
+# ---- top-k baseline ------------------------------------------------------------------------------
+def test_topk_by_hand_with_ties():
+    W = np.array([0.1, 0.4, 0.4, 0.05, 0.05])
+    assert topp.topk_sort(W, 2)["sel"].tolist() == [1, 2]
+    assert topp.topk_sort(W, 1)["sel"].tolist() == [1, 2]          # the tie at the cut is kept
+    assert topp.topk_sort(W, 3)["sel"].tolist() == [0, 1, 2]
+    assert topp.topk_sort(W, 4)["sel"].tolist() == [0, 1, 2, 3, 4]
+    assert topp.topk_sort(W, 0)["sel"].size == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_equals_rank_characterisation(seed):
+    # brute force: i is kept iff fewer than k weights are strictly larger than W_i
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 60))
+    W = rng.integers(1, 12, size=n).astype(np.float64)  # small integers: many ties
+    W /= W.sum()
+    for k in range(1, n + 1):
+        want = [i for i in range(n) if sum(1 for j in range(n) if W[j] > W[i]) < k]
+        assert topp.topk_sort(W, k)["sel"].tolist() == want, (seed, k)
+
+
+def test_topk_budget_reaching_the_floor_keeps_everything():
+    W = np.array([1.0, 0.5, 2.0**-45, 2.0**-50])
+    W = W / W.sum()
+    assert topp.topk_sort(W, 2)["sel"].tolist() == [0, 1]
+    assert topp.topk_sort(W, 3)["sel"].tolist() == [0, 1, 2, 3]  # only two weights above the floor
