@@ -99,6 +99,16 @@ typedef struct twl_decode_params {
   float keep_frac;  /* base selector budget as a fraction of pages, > 0 (>= 1: no selector)         */
   float sm_scale;   /* softmax scale, finite (usually 1/sqrt(128))                                 */
   int32_t iters;    /* bisection steps, 1..64 (32 always converges)                                 */
+  /* Baselines the pages compare top-p against (paperlayer §3, Fig. 2-3; §B.2 on GQA); 0 = off.
+   * topk > 0: each head keeps its topk largest estimated weights (ties at the topk-th kept; when
+   *   fewer than topk weights reach 2^-40 of the head's largest, every candidate) instead of its
+   *   top-p set; p is then unused.
+   * headwise = 1: each query head attends over its own kept set instead of the group's union (the
+   *   union's rows are still read once per group).
+   * Both need at most 65536 candidates per group (TWL_EUNSUPPORTED otherwise, and in
+   * twl_decode_clusters); negative topk or headwise outside {0, 1}: TWL_EINVAL. */
+  int32_t topk;
+  int32_t headwise;
 } twl_decode_params;
 
 /* Number of stages twl_decode_profiled() brackets with events (see there). */

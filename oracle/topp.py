@@ -105,15 +105,15 @@ def topk_sort(W: np.ndarray, k: int) -> dict:
     N = W.size
     e = np.zeros(0, np.int64)
     if N == 0 or k <= 0:
-        return {"sel": e, "w_star": math.nan, "amb_i": e}
+        return {"sel": e, "w_star": math.nan, "amb_i": e, "amb_ii": e}
     above = int(np.count_nonzero(W >= FLOOR * W.max()))
     if k > above:
-        return {"sel": np.arange(N), "w_star": 0.0, "amb_i": e}
+        return {"sel": np.arange(N), "w_star": 0.0, "amb_i": e, "amb_ii": e}
     ws = np.sort(W)[::-1]
     w_star = float(ws[k - 1])
     sel = np.nonzero(W >= w_star)[0]
     amb_i = np.nonzero(np.abs(W - w_star) <= TAU_W * w_star)[0]
-    return {"sel": sel, "w_star": w_star, "amb_i": amb_i}
+    return {"sel": sel, "w_star": w_star, "amb_i": amb_i, "amb_ii": e}  # (no prefix-mass clause)
 
 
 def topk_matches(gpu_sel: np.ndarray, res: dict) -> tuple[bool, str]:

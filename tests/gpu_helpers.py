@@ -32,7 +32,8 @@ def workspace(cache, maxcand, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def run_decode(w, cache, t, *, p=None, keep_frac=None, iters=32, device="cuda", with_lists=True):
+def run_decode(w, cache, t, *, p=None, keep_frac=None, iters=32, device="cuda", with_lists=True, topk=0,
+               headwise=False):
     p = w.p if p is None else p
     keep_frac = w.keep_frac if keep_frac is None else keep_frac
     B, Hq, U = w.batch, w.num_q_heads, w.batch * w.num_kv_heads
@@ -44,7 +45,8 @@ def run_decode(w, cache, t, *, p=None, keep_frac=None, iters=32, device="cuda", 
     indptr = torch.full((U + 1,), -7, dtype=torch.int32, device=device)
     toks = torch.full((max(U * maxcand, 1),), -7, dtype=torch.int32, device=device)
     twl.decode(cache, t["q"], p=p, keep_frac=keep_frac, iters=iters, out=out, lse=lse, threshold=thr,
-               sel_indptr=indptr if with_lists else None, sel_tokens=toks if with_lists else None, ws=ws)
+               sel_indptr=indptr if with_lists else None, sel_tokens=toks if with_lists else None, ws=ws,
+               topk=topk, headwise=headwise)
     torch.cuda.synchronize()
     return {"out": out.cpu().numpy(), "lse": lse.cpu().numpy(), "thr": thr.cpu().numpy(),
             "indptr": indptr.cpu().numpy(), "tokens": toks.cpu().numpy()}

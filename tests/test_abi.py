@@ -92,6 +92,16 @@ def test_decode_rejects_bad_params(twl, p, kf, iters, status):
     assert st == status
 
 
+@pytest.mark.parametrize("topk,headwise,status", [(-1, 0, 1), (0, 2, 1), (0, -1, 1)])
+def test_decode_rejects_bad_baseline_params(twl, topk, headwise, status):
+    L = twl.lib()
+    c = _fake_cache(twl)
+    prm = twl.ParamsC(0.85, 0.25, 0.088, 32, topk, headwise)
+    fake = ctypes.c_void_p(0x10000)
+    st = L.twl_decode(ctypes.byref(c), fake, ctypes.byref(prm), fake, None, None, None, None, 0, fake, 1 << 40, None)
+    assert st == status
+
+
 def test_workspace_and_capacity_checks(twl):
     L = twl.lib()
     c = _fake_cache(twl)

@@ -418,6 +418,43 @@ def test_decode_with_kv_in_pinned_host_memory():
     assert np.array_equal(g_host["tokens"][:n], g_dev["tokens"][:n])
 
 
+@pytest.mark.parametrize("cfg", [TINY[0], TINY[2], TINY[3]], ids=[TINY_IDS[0], TINY_IDS[2], TINY_IDS[3]])
+def test_decode_topk_baseline(cfg):
+    # the fixed-budget baseline: every head keeps its 40 largest estimated weights
+    w = make_custom(**cfg)
+    _print_case(w.name + " top-40")
+    cache, t = device_cache(w)
+    g = run_decode(w, cache, t, topk=40)
+    _check_decode(w, g, pipeline.decode(w, topk=40))
+
+
+@pytest.mark.parametrize("cfg", [TINY[0], TINY[2], TINY[3], TINY[5]],
+                         ids=[TINY_IDS[0], TINY_IDS[2], TINY_IDS[3], TINY_IDS[5]])
+def test_decode_headwise(cfg):
+    # each query head attends over its own top-p set instead of the group's union
+    w = make_custom(**cfg)
+    _print_case(w.name + " head-wise")
+    cache, t = device_cache(w)
+    g = run_decode(w, cache, t, headwise=True)
+    res = pipeline.decode(w, headwise=True)
+    _check_decode(w, g, res)
+    # it differs from the union output wherever a head's set is smaller than the union
+    gu = run_decode(w, cache, t)
+    some = [(b, h) for (b, h), r in res.items() if any(len(hd["tokens"]) < len(r["union"]) for hd in r["heads"])]
+    if some:
+        b, h = some[0]
+        G = w.group
+        assert not np.allclose(g["out"][b, h * G:(h + 1) * G], gu["out"][b, h * G:(h + 1) * G])
+
+
+def test_decode_topk_headwise_together():
+    w = make_custom(**TINY[2])
+    _print_case(w.name + " top-25 head-wise")
+    cache, t = device_cache(w)
+    g = run_decode(w, cache, t, topk=25, headwise=True)
+    _check_decode(w, g, pipeline.decode(w, topk=25, headwise=True))
+
+
 def test_decode_tied_weights():
     # pages repeat 5 contents, so each weight value is shared by ~60 tokens: the threshold search
     # meets bins of tied keys and keeps every tie at the threshold

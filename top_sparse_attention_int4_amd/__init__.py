@@ -58,7 +58,8 @@ class CandC(ctypes.Structure):
 
 
 class ParamsC(ctypes.Structure):
-    _fields_ = [("p", _f32), ("keep_frac", _f32), ("sm_scale", _f32), ("iters", _i32)]
+    _fields_ = [("p", _f32), ("keep_frac", _f32), ("sm_scale", _f32), ("iters", _i32), ("topk", _i32),
+                ("headwise", _i32)]
 
 
 _lib = None
@@ -247,15 +248,16 @@ def sparse_attn(cache: PagedCache, q: torch.Tensor, sm_scale: float, sel_indptr:
                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def _params(p, keep_frac, sm_scale, iters) -> ParamsC:
-    return ParamsC(float(p), float(keep_frac), float(sm_scale), int(iters))
+def _params(p, keep_frac, sm_scale, iters, topk=0, headwise=False) -> ParamsC:
+    return ParamsC(float(p), float(keep_frac), float(sm_scale), int(iters), int(topk), int(bool(headwise)))
 
 
 def decode(cache: PagedCache, q: torch.Tensor, *, p: float, keep_frac: float, sm_scale: float = DEFAULT_SM_SCALE,
            iters: int = 32, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
            threshold: Optional[torch.Tensor] = None, sel_indptr: Optional[torch.Tensor] = None,
-           sel_tokens: Optional[torch.Tensor] = None, ws: torch.Tensor, stream=None):
-    prm = _params(p, keep_frac, sm_scale, iters)
+           sel_tokens: Optional[torch.Tensor] = None, ws: torch.Tensor, stream=None, topk: int = 0,
+           headwise: bool = False):
+    prm = _params(p, keep_frac, sm_scale, iters, topk, headwise)
     cap = 0 if sel_tokens is None else int(sel_tokens.numel())
     _check(lib().twl_decode(ctypes.byref(cache.struct()), _ptr(q), ctypes.byref(prm), _ptr(out), _ptr(lse),
                             _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap, _ptr(ws),
@@ -266,7 +268,7 @@ def decode_profiled(cache: PagedCache, q: torch.Tensor, events, *, p: float, kee
                     sm_scale: float = DEFAULT_SM_SCALE, iters: int = 32, out: torch.Tensor,
                     lse: Optional[torch.Tensor] = None, threshold: Optional[torch.Tensor] = None,
                     sel_indptr: Optional[torch.Tensor] = None, sel_tokens: Optional[torch.Tensor] = None,
-                    ws: torch.Tensor, stream=None):
+                    ws: torch.Tensor, stream=None, topk: int = 0, headwise: bool = False):
     """``events``: 2*NUM_STAGES torch.cuda.Event(enable_timing=True) recorded around each stage."""
     if len(events) != 2 * NUM_STAGES:
         raise ValueError("need 2*NUM_STAGES events")
@@ -274,7 +276,7 @@ def decode_profiled(cache: PagedCache, q: torch.Tensor, events, *, p: float, kee
         if e.cuda_event == 0:
             e.record()
     arr = (_p * (2 * NUM_STAGES))(*[ctypes.c_void_p(e.cuda_event) for e in events])
-    prm = _params(p, keep_frac, sm_scale, iters)
+    prm = _params(p, keep_frac, sm_scale, iters, topk, headwise)
     cap = 0 if sel_tokens is None else int(sel_tokens.numel())
     _check(lib().twl_decode_profiled(ctypes.byref(cache.struct()), _ptr(q), ctypes.byref(prm), _ptr(out),
                                      _ptr(lse), _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap,

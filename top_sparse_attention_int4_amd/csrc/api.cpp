@@ -189,7 +189,7 @@ WideWs wide_of(void* ws, const Layout& L) {
 // wide top-p by candidate capacity.  Events 4/5 bracket the estimate, 6/7 the rest.
 hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, void* ws,
                          const Layout& L, float p, int iters, float* thr, float* mass, uint32_t* head_mask,
-                         int mask_words, bool with_union, const Events& E, hipStream_t s) {
+                         int mask_words, bool with_union, const Events& E, hipStream_t s, int topk = 0) {
   const int ncap = (int)L.ncap;
   const WideWs wd = wide_of(ws, L);
   const bool wide = is_wide(L.ncap);
@@ -209,7 +209,7 @@ hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const 
                            at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), mass, s);
   } else {
     e = launch_topp(c, at<float>(ws, L.logits), ncap, p, iters, thr, mass, at<uint32_t>(ws, L.masks), head_mask,
-                    mask_words, s);
+                    mask_words, topk, s);
     if (e == hipSuccess && with_union)
       e = launch_union(c, at<uint32_t>(ws, L.masks), at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), ncap,
                        at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s);
@@ -220,7 +220,7 @@ hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const 
 
 // Attention over the top-p bitmaps (no compacted list needed) and the merge; events 8..11.
 hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, void* ws, const Layout& L, float* out,
-                         float* lse, const Events& E, hipStream_t s) {
+                         float* lse, const Events& E, hipStream_t s, bool headwise = false) {
   const bool wide = is_wide(L.ncap);
   MaskView mv{};
   if (wide) {
@@ -232,7 +232,8 @@ hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, void* 
   mv.ncap = L.ncap;
   hipError_t e;
   if ((e = E.rec(8)) != hipSuccess) return e;
-  if ((e = launch_attn_masked(c, q, sm, mv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), s)) != hipSuccess) return e;
+  if ((e = launch_attn_masked(c, q, sm, mv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), headwise, s)) != hipSuccess)
+    return e;
   if ((e = E.rec(9)) != hipSuccess) return e;
   if ((e = E.rec(10)) != hipSuccess) return e;
   if ((e = launch_merge(c, nullptr, L.chunk_tokens, L.slots, at<float>(ws, L.parts), out, lse, s)) != hipSuccess) return e;
@@ -249,6 +250,7 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
   if (!finite(prm->keep_frac) || !(prm->keep_frac > 0.f)) return TWL_EINVAL;
   if (!finite(prm->sm_scale)) return TWL_EINVAL;
   if (prm->iters < 1 || prm->iters > 64) return TWL_EINVAL;
+  if (prm->topk < 0 || (prm->headwise != 0 && prm->headwise != 1)) return TWL_EINVAL;
   if ((sel_indptr == nullptr) != (sel_tokens == nullptr)) return TWL_EINVAL;
   const bool selector = prm->keep_frac < 1.0f;
   const int64_t U = (int64_t)cache->batch * cache->num_kv_heads;
@@ -257,6 +259,8 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
   if (sel_tokens && capacity < U * maxcand) return TWL_EINVAL;
   const int64_t ncap = ncap_of(maxcand);
   if (ncap == 0) return TWL_EUNSUPPORTED;
+  // the top-k baseline and head-wise attention run on the one-block-per-head search's bitmaps
+  if ((prm->topk > 0 || prm->headwise) && is_wide(ncap)) return TWL_EUNSUPPORTED;
   Layout L;
   make_layout(cache, ncap, &L);
   st = check_ws(ws, ws_bytes, L);
@@ -294,11 +298,12 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
   }
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   const bool csr = sel_tokens != nullptr;
-  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s));
+  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s,
+                        prm->topk));
   if (csr)
     TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
                             capacity, s));
-  TWL_TRY(attend_masked(c, qb, prm->sm_scale, ws, L, out, lse, E, s));
+  TWL_TRY(attend_masked(c, qb, prm->sm_scale, ws, L, out, lse, E, s, prm->headwise != 0));
   return TWL_OK;
 }
 
@@ -317,6 +322,7 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   if (!finite(p1) || !(p1 > 0.f) || p1 > 1.f) return TWL_EINVAL;
   if (!finite(prm->sm_scale)) return TWL_EINVAL;
   if (prm->iters < 1 || prm->iters > 64 || num_clusters < 1) return TWL_EINVAL;
+  if (prm->topk != 0 || prm->headwise != 0) return TWL_EUNSUPPORTED;
   if ((sel_indptr == nullptr) != (sel_tokens == nullptr)) return TWL_EINVAL;
   const int64_t U = (int64_t)cache->batch * cache->num_kv_heads;
   const int64_t maxcand = cache->max_seq_len;

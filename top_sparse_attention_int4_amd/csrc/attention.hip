@@ -54,7 +54,9 @@ constexpr int kAttnSB = 16;  // tokens per sub-block
 // the count of loads in flight is known at every wait.
 // MK: the chunk is a range of the candidate index space whose kept entries come from bitmaps (each
 // wave compacts its kept candidates' rows in LDS first); otherwise it is a range of a token list.
-template <int G, int NSB, bool MK>
+// HW (with MK): head-wise -- a row read for the group's union counts for head h only when h's own
+// bitmap keeps it (the row's head bits travel with it through the compaction).
+template <int G, int NSB, bool MK, bool HW = false>
 __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uint16_t* __restrict__ q,
                                                           float sm_log2, ListView L, MaskView MV, int slots,
                                                           float* __restrict__ partials) {
@@ -67,6 +69,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
   __shared__ float sm_m[NWV][G], sm_l[NWV][G];
   __shared__ float4 so[NWV][G][32];
   __shared__ int cr[MK ? NWV : 1][MK ? QL : 1];
+  __shared__ int crh[HW ? NWV : 1][HW ? QL : 1];
 
   // chunk slot k of unit u (the unit's chunks are its first ceil(count / CH) slots)
   const int u = blockIdx.x / slots, k = blockIdx.x - u * slots;
@@ -84,6 +87,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     }
   }
   int rows[NSB];
+  int hrow[NSB] = {};  // head bits of each row (head-wise only)
   int w_end;
   if constexpr (MK) {
     // the quarter's candidate rows and kept bits (one round trip with q), then the kept rows compacted
@@ -91,17 +95,23 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     const int mw = (int)(MV.ncap >> 5);
     int crw[NSB];
     uint32_t wd[NSB];
+    int hb[NSB];
 #pragma unroll
     for (int i = 0; i < NSB; ++i) {
       const int cidx = w_begin + i * SB + (lane & 15);
       crw[i] = MV.cand_row[ub + cidx];
       const int wi = cidx >> 5;
-      if (MV.union_words) {
+      hb[i] = 0;
+      if (!HW && MV.union_words) {
         wd[i] = MV.union_words[(int64_t)u * mw + wi];
       } else {
         uint32_t x = 0u;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) x |= MV.head_masks[((int64_t)b * c.Hq + h * G + hh) * mw + wi];
+        for (int hh = 0; hh < G; ++hh) {
+          const uint32_t y = MV.head_masks[((int64_t)b * c.Hq + h * G + hh) * mw + wi];
+          x |= y;
+          if (HW) hb[i] |= (int)((y >> (cidx & 31)) & 1u) << hh;
+        }
         wd[i] = x;
       }
     }
@@ -112,7 +122,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
       const bool f = lane < SB && ((wd[i] >> (cidx & 31)) & 1u);
       const unsigned long long bal = __ballot(f);
       const int pos = kept + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-      if (f) cr[wv][pos] = crw[i];
+      if (f) {
+        cr[wv][pos] = crw[i];
+        if (HW) crh[HW ? wv : 0][HW ? pos : 0] = hb[i];
+      }
       kept += __popcll(bal);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -120,7 +133,10 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int kl = kept > 0 ? kept - 1 : 0;
 #pragma unroll
-    for (int i = 0; i < NSB; ++i) rows[i] = cr[wv][min(i * SB + (lane & 15), kl)];
+    for (int i = 0; i < NSB; ++i) {
+      rows[i] = cr[wv][min(i * SB + (lane & 15), kl)];
+      hrow[i] = HW ? crh[HW ? wv : 0][HW ? min(i * SB + (lane & 15), kl) : 0] : 0;
+    }
     w_end = kept;
   } else {
     // The rows of this wave's quarter are read together with the count and q (one round trip).
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
       vv[s2] = __builtin_bit_cast(uint4, stream_load(c.v + (size_t)rv * kD + nn * 8));
     }
   };
-  auto consume = [&](int sb, int row, const bf16x8_t (&kv)[4], const uint4 (&vv)[VS]) {
+  auto consume = [&](int sb, int row, int hr, const bf16x8_t (&kv)[4], const uint4 (&vv)[VS]) {
     const unsigned long long vmask = __ballot(lane < SB && sb + lane < w_end && row >= 0);
     floatx4_t sacc = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -177,7 +193,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 4 * grp + e;
-      const float x = ((vmask >> t) & 1ull) ? sacc[e] * sm_log2 : -__builtin_inff();
+      bool keep = (vmask >> t) & 1ull;
+      if (HW) keep = keep && ((__shfl(hr, t) >> nn) & 1);  // head nn's own bitmap keeps token t
+      const float x = keep ? sacc[e] * sm_log2 : -__builtin_inff();
       sv[e] = x;
       mx = fmaxf(mx, x);
     }
@@ -242,7 +260,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
 #pragma unroll
     for (int i = 0; i < NSB; ++i) {
       if (i + 1 < NSB) issue(rows[i + 1], kv[(i + 1) & 1], vv[(i + 1) & 1]);
-      consume(w_first + i * SB, rows[i], kv[i & 1], vv[i & 1]);
+      consume(w_first + i * SB, rows[i], hrow[i], kv[i & 1], vv[i & 1]);
     }
   }
 
@@ -401,7 +419,7 @@ int attn_chunk_tokens(int64_t total_upper, int group) {
   return 64 * s;
 }
 
-template <bool MK>
+template <bool MK, bool HW = false>
 static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float sm, const ListView& list,
                                    const MaskView& mv, int chunk_tokens, int slots, float* partials, hipStream_t s) {
   if (slots < 1) return hipErrorInvalidValue;
@@ -409,7 +427,7 @@ static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float 
   const dim3 grid((unsigned)((int64_t)c.B * c.Hkv * slots)), blk(64 * kAttnWaves);
 #define TWL_ATTN_G(GG, NS)                                                                                  \
   case GG:                                                                                                  \
-    hipLaunchKernelGGL((k_attn<GG, NS, MK>), grid, blk, 0, s, c, q, sm_log2, list, mv, slots, partials);   \
+    hipLaunchKernelGGL((k_attn<GG, NS, MK, HW>), grid, blk, 0, s, c, q, sm_log2, list, mv, slots, partials); \
     break;
 #define TWL_ATTN_NSB(NS)                   \
   case NS * kAttnWaves * kAttnSB:          \
@@ -451,8 +469,12 @@ hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const Li
 }
 
 hipError_t launch_attn_masked(const CacheView& c, const uint16_t* q, float sm, const MaskView& mv, int chunk_tokens,
-                              int slots, float* partials, hipStream_t s) {
+                              int slots, float* partials, bool headwise, hipStream_t s) {
   if (!mv.cand_row || (!mv.head_masks && !mv.union_words) || mv.ncap % chunk_tokens) return hipErrorInvalidValue;
+  if (headwise) {
+    if (!mv.head_masks) return hipErrorInvalidValue;
+    return launch_attn_impl<true, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, s);
+  }
   return launch_attn_impl<true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, s);
 }
 

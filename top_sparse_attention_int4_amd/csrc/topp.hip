@@ -32,11 +32,13 @@ namespace twl {
 
 // W: weighted mode -- candidate k of unit u carries the integer multiplicity mult[u * mult_stride + k]
 // (k < mult_stride), its weight being mult * exp(l - M); the largest weight is then not 1.
+// topk > 0: the fixed-budget baseline -- every weight >= 2^-40 counts 1 instead of its mass and the
+// target is topk, so T is the topk-th largest weight (ties kept); above the count, all are kept.
 template <int E, bool W>
 __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restrict__ logits, int ncap, float p,
                                                int iters, float* threshold, float* mass, uint32_t* mask_ws,
                                                uint32_t* head_mask, int mask_words,
-                                               const int32_t* __restrict__ mult, int mult_stride) {
+                                               const int32_t* __restrict__ mult, int mult_stride, int topk) {
   constexpr int NT = kToppThreads, NW = NT / 64;
   __shared__ float red[2 * NW * 4];
   __shared__ uint64_t h1[2048], h2[512], h3[512], cs[64];
@@ -85,7 +87,8 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     if (e[j] >= 0.f) {
-      const uint64_t f = to_fix(e[j]);
+      uint64_t f = to_fix(e[j]);
+      if (topk > 0) f = f ? 1ull : 0ull;
       if (f) atomicAdd((unsigned long long*)&h1[key_d1(__float_as_uint(e[j]))], (unsigned long long)f);
     }
   }
@@ -103,8 +106,8 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     const uint64_t zf = readlane_u64(wave_incl_scan_u64(cs[lane]), 63);
     int mode = 1, bin = 0;
     uint64_t rem = 0;
-    if (zf != 0ull && p < 1.0f) {
-      uint64_t target = (uint64_t)ceil((double)p * (double)zf);
+    if (zf != 0ull && (topk > 0 ? (uint64_t)topk <= zf : p < 1.0f)) {
+      uint64_t target = topk > 0 ? (uint64_t)topk : (uint64_t)ceil((double)p * (double)zf);
       target = target < 1ull ? 1ull : (target > zf ? zf : target);
       wide_find(h1, cs, 64, target, bin, rem);
       mode = 0;
@@ -125,7 +128,8 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     for (int j = 0; j < E; ++j) {
       const uint32_t key = __float_as_uint(e[j]);
       if (e[j] >= 0.f && key_d1(key) == b1) {
-        const uint64_t f = to_fix(e[j]);
+        uint64_t f = to_fix(e[j]);
+        if (topk > 0) f = f ? 1ull : 0ull;
         if (f) atomicAdd((unsigned long long*)&h2[key_d2(key)], (unsigned long long)f);
       }
     }
@@ -148,7 +152,8 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     for (int j = 0; j < E; ++j) {
       const uint32_t key = __float_as_uint(e[j]);
       if (e[j] >= 0.f && (key >> 9) == pre) {
-        const uint64_t f = to_fix(e[j]);
+        uint64_t f = to_fix(e[j]);
+        if (topk > 0) f = f ? 1ull : 0ull;
         if (f) atomicAdd((unsigned long long*)&h3[key_d3(key)], (unsigned long long)f);
       }
     }
@@ -309,13 +314,13 @@ int topp_elems_per_thread(int64_t ncap) {
 }
 
 hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
-                       float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, hipStream_t s) {
+                       float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, int topk, hipStream_t s) {
   const int E = ncap / kToppThreads;
   dim3 grid((unsigned)(c.B * c.Hq)), block(kToppThreads);
 #define TWL_TOPP_CASE(EE)                                                                                   \
   case EE:                                                                                                  \
     hipLaunchKernelGGL((k_topp<EE, false>), grid, block, 0, s, c, logits, ncap, p, iters, threshold, mass,   \
-                       mask_ws, head_mask, mask_words, nullptr, 0);                                        \
+                       mask_ws, head_mask, mask_words, nullptr, 0, topk);                                  \
     break;
   switch (E) {
     TWL_TOPP_CASE(1)
@@ -371,7 +376,7 @@ hipError_t launch_topp_weighted(const CacheView& c, const float* logits, int nca
 #define TWL_TOPPW_CASE(EE)                                                                                \
   case EE:                                                                                                \
     hipLaunchKernelGGL((k_topp<EE, true>), grid, block, 0, s, c, logits, ncap, p, iters, threshold, nullptr, \
-                       mask_ws, nullptr, 0, mult, mult_stride);                                          \
+                       mask_ws, nullptr, 0, mult, mult_stride, 0);                                       \
     break;
   switch (ncap / kToppThreads) {
     TWL_TOPPW_CASE(1)

@@ -98,8 +98,9 @@ hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, flo
 hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
                                 const int32_t* coff, int C, int32_t* ranges, int32_t* count, int32_t* prefix,
                                 int32_t* chunk_first, int nchunk, hipStream_t s);
+// topk > 0: keep each head's topk largest weights (ties kept) instead of its top-p set
 hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
-                       float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, hipStream_t s);
+                       float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, int topk, hipStream_t s);
 hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, const int32_t* cand_row,
                         int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, hipStream_t s);
 hipError_t launch_csr_emit(const CacheView& c, const int32_t* union_tok, const int32_t* union_cnt, int ncap,
@@ -117,9 +118,10 @@ struct MaskView {
 // one workgroup per chunk slot: slot k of unit u covers list entries [k*chunk_tokens, (k+1)*chunk_tokens)
 hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
                        int slots, float* partials, hipStream_t s);
-// one workgroup per chunk slot of the candidate space (every slot writes a partial)
+// one workgroup per chunk slot of the candidate space (every slot writes a partial); headwise: each
+// query head attends over its own bitmap's tokens (needs head_masks) instead of the group's union
 hipError_t launch_attn_masked(const CacheView& c, const uint16_t* q, float sm, const MaskView& mv, int chunk_tokens,
-                              int slots, float* partials, hipStream_t s);
+                              int slots, float* partials, bool headwise, hipStream_t s);
 // K/V rows of a CSR token list (into `rows`, same indexing), entries at or past `capacity` skipped
 hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,
                        int64_t capacity, hipStream_t s);
