@@ -18,6 +18,12 @@ Llama-layer workload stay in pinned host memory and the kernels read the selecte
 while the INT4 codes and page bounds sit in HBM; it times the decode step with top-p (p = 0.85) and
 with the base selector alone (p = 1: every selected page is loaded, Quest's budget), one JSON line.
 
+With ``--baselines`` it compares, on one layer-step, top-p against the top-k baseline at the same mean
+budget (top-k on the estimated weights, and top-k on the exact weights as an oracle reference), each
+with group-union and head-wise attention: K/V rows read, per-head set sizes, output error against
+attention over all the base selector's candidates (what the pruning approximates) and against dense
+attention, and decode time, one JSON line.
+
 Prints ONE JSON line.  ``value`` is microseconds per layer-step (lower is better).  ``roofline``
 describes the split-K attention kernel (the stage that moves most bytes): its algorithmic bytes per
 launch (512 B of K/V rows + 4 B index per kept token, plus the group's q) over its average launch
@@ -64,6 +70,8 @@ def parse():
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: auto)")
     ap.add_argument("--estimator-bits", action="store_true",
                     help="report the 2/4/8-bit estimator ablation instead of the step benchmark")
+    ap.add_argument("--baselines", action="store_true",
+                    help="compare top-p with the equal-budget top-k baseline, union vs head-wise")
     ap.add_argument("--offload", action="store_true",
                     help="time the decode with K/V in pinned host memory (top-p vs the base selector alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -102,6 +110,9 @@ def main():
         return
     if args.offload:
         offload_report(args, dev)
+        return
+    if args.baselines:
+        baselines_report(args, dev)
         return
     if args.copy_calibration:
         # a plain device copy of known size: 512 MiB read + 512 MiB written per launch
@@ -418,6 +429,119 @@ def estimator_bits_report(args, dev):
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "estimator precision ablation (top-p at p, true selected mass vs code bits)",
                       "workload": name, "p": w.p, "heads": B * Hq, "steps": K, "data": "synthetic",
+                      "rows": rows}))
+
+
+def baselines_report(args, dev):
+    """Top-p against the fixed-budget top-k baseline (paperlayer §3, Fig. 2-3) and group-union against
+    head-wise attention for GQA (paperlayer §B.2; Paper-Notes "局限与展望").  k = the mean size of the
+    heads' top-p sets, so both spend the same total budget.  Errors are relative L2 distances of each
+    head's output from attention over every candidate of the base selector (the decode at p = 1) --
+    the quantity top-p bounds -- and from dense attention over the whole context (float32 torch)."""
+    import torch
+    import top_sparse_attention_int4_amd as twl
+    from gen import make_config
+    from gen.device import upload
+
+    name = args.workload
+    w = make_config(name)
+    if w.csize is not None or w.keep_frac >= 1.0:
+        raise SystemExit("--baselines runs the page-selector workloads (C2, C3, C4)")
+    t = upload(w, dev)
+    B, Hq, Hkv, G = w.batch, w.num_q_heads, w.num_kv_heads, w.group
+    U = B * Hkv
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+    mk = twl.keep_count(w.max_pages, w.keep_frac)
+    maxcand = 16 * mk
+    mw = maxcand // 32
+    cache = twl.PagedCache(t["k_pages"], t["v_pages"], t["page_table"], t["seq_lens"], Hq, max_seq_len=w.max_seq_len)
+    twl.quantize_k(cache, torch.zeros(B, dtype=torch.int32, device=dev), t["seq_lens"], w.max_seq_len)
+    ws = torch.empty(twl.workspace_bytes(cache, maxcand), dtype=torch.uint8, device=dev)
+    # dense references and the per-unit logical K/V, float32
+    kf, vf, qf = t["k_pages"].float(), t["v_pages"].float(), t["q"].float()
+    dense, kv = {}, {}
+    for b in range(B):
+        n = int(w.seq_lens[b])
+        npg = -(-n // 16)
+        pt = t["page_table"][b, :npg].long()
+        ks = kf[pt].permute(1, 0, 2, 3).reshape(Hkv, npg * 16, 128)[:, :n]
+        vs = vf[pt].permute(1, 0, 2, 3).reshape(Hkv, npg * 16, 128)[:, :n]
+        for h in range(Hkv):
+            lg = (ks[h] @ qf[b, h * G:(h + 1) * G].T).T * sm                  # [G][n]
+            dense[(b, h)] = (torch.softmax(lg, -1) @ vs[h], lg)
+            kv[(b, h)] = vs[h]
+    # the heads' top-p sets (split entry points: page ids, then head bitmaps over the candidates)
+    ids = torch.full((U, mk), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros(U, dtype=torch.int32, device=dev)
+    twl.select_pages(cache, t["q"], w.keep_frac, mk, ids, cnt, ws)
+    thr = torch.empty((B, Hq), device=dev)
+    hm = torch.zeros((B, Hq, mw), dtype=torch.int32, device=dev)
+    indptr = torch.empty(U + 1, dtype=torch.int32, device=dev)
+    toks = torch.empty(U * maxcand, dtype=torch.int32, device=dev)
+    twl.estimate_topp(cache, t["q"], sm, w.p, 32, page_ids=ids, count=cnt, max_items=mk, threshold=thr,
+                      head_mask=hm, mask_words=mw, sel_indptr=indptr, sel_tokens=toks, ws=ws)
+    torch.cuda.synchronize()
+    bits_m = np.unpackbits(hm.cpu().numpy().view(np.uint8), axis=-1, bitorder="little")
+    k_eq = max(1, int(round(float(np.mean(bits_m[..., :maxcand].sum(-1))))))
+    ids_h, cnt_h = ids.cpu().numpy(), cnt.cpu().numpy()
+    out = torch.empty((B, Hq, 128), device=dev)
+    K = max(10, min(args.steps, 50))
+
+    o_cand = torch.empty((B, Hq, 128), device=dev)
+    twl.decode(cache, t["q"], p=1.0, keep_frac=w.keep_frac, out=o_cand, ws=ws)
+    torch.cuda.synchronize()
+
+    def err_of(o, ref=None):
+        e = []
+        for (b, h), (od, _) in dense.items():
+            r = od if ref is None else ref[b, h * G:(h + 1) * G]
+            x = o[b, h * G:(h + 1) * G]
+            e.append((torch.linalg.norm(x - r, dim=-1) / torch.linalg.norm(r, dim=-1)).cpu().numpy())
+        e = np.concatenate(e)
+        return {"mean": round(float(e.mean()), 6), "max": round(float(e.max()), 6)}
+
+    rows = []
+    for label, topk in (("top-p", 0), (f"top-k (estimated weights, k={k_eq})", k_eq)):
+        for headwise in (False, True):
+            for _ in range(3):
+                twl.decode(cache, t["q"], p=w.p, keep_frac=w.keep_frac, out=out, ws=ws, topk=topk, headwise=headwise)
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(K):
+                twl.decode(cache, t["q"], p=w.p, keep_frac=w.keep_frac, out=out, ws=ws, topk=topk, headwise=headwise)
+            b_.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b_) / K * 1e3
+            twl.decode(cache, t["q"], p=w.p, keep_frac=w.keep_frac, out=out, ws=ws, topk=topk, headwise=headwise,
+                       sel_indptr=indptr, sel_tokens=toks)
+            torch.cuda.synchronize()
+            rows.append({"selection": label, "attention": "head-wise" if headwise else "group union",
+                         "kv_rows_read": int(indptr[-1].item()), "us_per_layer_step": round(us, 1),
+                         "error_vs_candidates": err_of(out, o_cand), "error_vs_dense": err_of(out)})
+    # oracle reference: top-k on the exact weights over the same candidates, head-wise
+    o_ref = torch.zeros((B, Hq, 128), device=dev)
+    rows_ref = 0
+    for (b, h), (od, lg) in dense.items():
+        u = b * Hkv + h
+        n = int(w.seq_lens[b])
+        pages = ids_h[u, :cnt_h[u]].astype(np.int64)
+        cand = (pages[:, None] * 16 + np.arange(16)[None, :]).reshape(-1)
+        cidx = torch.from_numpy(cand[cand < n]).to(dev)
+        union = set()
+        for j in range(G):
+            top = cidx[torch.topk(lg[j, cidx], min(k_eq, cidx.numel())).indices]
+            union |= set(top.tolist())
+            o_ref[b, h * G + j] = torch.softmax(lg[j, top], 0) @ kv[(b, h)][top]
+        rows_ref += len(union)
+    rows.append({"selection": f"top-k (exact weights, k={k_eq}; torch reference)", "attention": "head-wise",
+                 "kv_rows_read": rows_ref, "us_per_layer_step": None,
+                 "error_vs_candidates": err_of(o_ref, o_cand), "error_vs_dense": err_of(o_ref)})
+    print(json.dumps({"metric": "top-p vs equal-budget top-k; group union vs head-wise attention",
+                      "workload": name, "p": w.p, "heads": B * Hq, "steps": K, "data": "synthetic",
+                      "top_p_set_size": {"mean": round(float(np.mean(bits_m[..., :maxcand].sum(-1))), 1),
+                                         "min": int(bits_m[..., :maxcand].sum(-1).min()),
+                                         "max": int(bits_m[..., :maxcand].sum(-1).max())},
                       "rows": rows}))
 
 
