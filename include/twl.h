@@ -12,6 +12,7 @@
  * ---------------------------------------
  * - Every pointer argument is a DEVICE pointer owned by the caller, unless it is a pointer to one of
  *   the structs below or to twl_decode_params, which are read on the host during the call only.
+ *   The query q must be 16-byte aligned (TWL_EINVAL otherwise; any hipMalloc/torch allocation is).
  * - The library never allocates, frees or synchronises.  Calls enqueue kernels on `stream` (a
  *   hipStream_t; NULL = the default stream) and return once enqueued.  Scratch memory is the
  *   caller's workspace `ws` (>= 256-byte aligned, `ws_bytes` long, contents need not be initialised);

@@ -102,6 +102,16 @@ def test_decode_rejects_bad_baseline_params(twl, topk, headwise, status):
     assert st == status
 
 
+def test_decode_rejects_misaligned_query(twl):
+    L = twl.lib()
+    c = _fake_cache(twl)
+    prm = twl.ParamsC(0.85, 0.25, 0.088, 32)
+    fake = ctypes.c_void_p(0x10000)
+    st = L.twl_decode(ctypes.byref(c), ctypes.c_void_p(0x10004), ctypes.byref(prm), fake, None, None, None, None, 0,
+                      fake, 1 << 40, None)
+    assert st == 1
+
+
 def test_workspace_and_capacity_checks(twl):
     L = twl.lib()
     c = _fake_cache(twl)

@@ -43,6 +43,9 @@ twl_status check_cache(const twl_cache* c, bool need_kv, bool need_quant) {
 
 bool finite(float x) { return std::isfinite(x); }
 
+// q rows are read with 16-byte loads
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
 // Kept-page count bound for the longest sequence (matches the device computation).
 int keep_count(int P, float keep_frac) {
   if (P <= 0) return 0;
@@ -245,7 +248,7 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
                        void* ws, size_t ws_bytes, void* stream, void* const* events) {
   twl_status st = check_cache(cache, true, true);
   if (st != TWL_OK) return st;
-  if (!q || !prm || !out) return TWL_EINVAL;
+  if (!q || misaligned16(q) || !prm || !out) return TWL_EINVAL;
   if (!finite(prm->p) || !(prm->p > 0.f) || prm->p > 1.f) return TWL_EINVAL;
   if (!finite(prm->keep_frac) || !(prm->keep_frac > 0.f)) return TWL_EINVAL;
   if (!finite(prm->sm_scale)) return TWL_EINVAL;
@@ -317,7 +320,7 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
                                 size_t ws_bytes, void* stream, void* const* events) {
   twl_status st = check_cache(cache, true, true);
   if (st != TWL_OK) return st;
-  if (!q || !prm || !out || !centroids || !csize || !coff) return TWL_EINVAL;
+  if (!q || misaligned16(q) || !prm || !out || !centroids || !csize || !coff) return TWL_EINVAL;
   if (!finite(prm->p) || !(prm->p > 0.f) || prm->p > 1.f) return TWL_EINVAL;
   if (!finite(p1) || !(p1 > 0.f) || p1 > 1.f) return TWL_EINVAL;
   if (!finite(prm->sm_scale)) return TWL_EINVAL;
@@ -404,7 +407,7 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
                             int32_t* page_ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
   twl_status st = check_cache(cache, false, true);
   if (st != TWL_OK) return st;
-  if (!q || !page_ids || !count) return TWL_EINVAL;
+  if (!q || misaligned16(q) || !page_ids || !count) return TWL_EINVAL;
   if (!finite(keep_frac) || !(keep_frac > 0.f)) return TWL_EINVAL;
   if (max_keep < keep_count(cache->max_pages_per_seq, keep_frac)) return TWL_EINVAL;
   Layout L;
@@ -426,7 +429,7 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
                              void* ws, size_t ws_bytes, void* stream) {
   twl_status st = check_cache(cache, false, true);
   if (st != TWL_OK) return st;
-  if (!q || !cand || !threshold || !sel_indptr || !sel_tokens) return TWL_EINVAL;
+  if (!q || misaligned16(q) || !cand || !threshold || !sel_indptr || !sel_tokens) return TWL_EINVAL;
   if (!finite(p) || !(p > 0.f) || p > 1.f) return TWL_EINVAL;
   if (!finite(sm_scale)) return TWL_EINVAL;
   if (iters < 1 || iters > 64) return TWL_EINVAL;
@@ -482,7 +485,7 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
                            void* ws, size_t ws_bytes, void* stream) {
   twl_status st = check_cache(cache, true, false);
   if (st != TWL_OK) return st;
-  if (!q || !sel_indptr || !sel_tokens || !out) return TWL_EINVAL;
+  if (!q || misaligned16(q) || !sel_indptr || !sel_tokens || !out) return TWL_EINVAL;
   if (!finite(sm_scale)) return TWL_EINVAL;
   if (max_selected_per_group < 0) return TWL_EINVAL;
   int64_t ncap = ncap_of(max_selected_per_group);
@@ -526,7 +529,7 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
                                     int32_t* count, void* ws, size_t ws_bytes, void* stream) {
   twl_status st = check_cache(cache, false, false);
   if (st != TWL_OK) return st;
-  if (!q || !centroids || !csize || !coff || !ranges || !count) return TWL_EINVAL;
+  if (!q || misaligned16(q) || !centroids || !csize || !coff || !ranges || !count) return TWL_EINVAL;
   if (!finite(p1) || !(p1 > 0.f) || p1 > 1.f || !finite(sm_scale)) return TWL_EINVAL;
   if (iters < 1 || iters > 64 || num_clusters < 1) return TWL_EINVAL;
   if (num_clusters > kNarrowMaxCands) return TWL_EUNSUPPORTED;

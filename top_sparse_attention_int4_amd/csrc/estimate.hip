@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   __shared__ int s_row[NB][64];
   // query digits (Q = 128 [0] + [1]), channel 8j + w of a group at byte 8j + perm(w), the order in
   // which the nibbles of 4 code bytes are unpacked (low nibbles of bytes 0..3, then high nibbles)
-  __shared__ __align__(8) int8_t s_qd[2][G][kD];
+  __shared__ __align__(16) int8_t s_qd[2][G][kD];
   __shared__ int s_qe[G][kGroups];   // group exponents E_g
   __shared__ float s_qb[G][kGroups]; // b_g
   __shared__ int s_qds[2][G][kGroups];  // per digit, its sum over the group (8-bit codes: the offset of 128)
@@ -224,14 +224,15 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int cnt = (cand.mode == kCandAll) ? 0 : clampi(cand.count[u], 0, cand.max_items);
   const int k0 = ck * NC;
-  // the query channels this lane turns into fixed point (half a wave per (head, group)), read first
-  constexpr int QP = (kGroups * G + 7) / 8;  // (head, group) pairs per half-wave
-  float qx[QP];
+  // the query: lane pr < 4 G of wave 0 turns the 32 channels of (head pr / 4, group pr % 4) into fixed
+  // point on its own (no cross-lane reductions); its 64 bytes are read first
+  const bool qlane = wv == 0 && lane < kGroups * G;
+  const int qh = qlane ? lane >> 2 : 0, qg = lane & 3;
+  u32x4_t qraw[4];
+  if (qlane) {
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(q + ((size_t)b * c.Hq + (size_t)h * G + qh) * kD + qg * 32);
 #pragma unroll
-  for (int i = 0; i < QP; ++i) {
-    const int pr = 2 * wv + (lane >> 5) + 8 * i;
-    const int hh = min(pr >> 2, G - 1), g = pr & 3;
-    qx[i] = __uint_as_float((uint32_t)q[((size_t)b * c.Hq + (size_t)h * G + hh) * kD + g * 32 + (lane & 31)] << 16);
+    for (int i = 0; i < 4; ++i) qraw[i] = qp[i];
   }
 
   // ---- candidate resolution: wave w resolves batches w, w + 4, ... (token id and K/V row); the
@@ -299,7 +300,53 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       cand_row[(size_t)u * ncap + k] = row;
     }
   }
-  __syncthreads();
+  // ---- the fixed-point query (wave 0), ordered before the code loads by the barrier below
+  if (qlane) {
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wq[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[8 * i + 2 * k] = bf16_lo(wq[k]);
+        x[8 * i + 2 * k + 1] = bf16_hi(wq[k]);
+      }
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 32; ++cc) m = fmaxf(m, fabsf(x[cc]));
+    int E = 0;
+    if (m > 0.f) E = max((int)(__float_as_uint(m) >> 23) - 127, -100);
+    int qs = 0, d0s = 0, d1s = 0;
+    uint32_t dw[2][8];  // the two digits' bytes, 4 per word, in the unpack order of the codes
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dw[0][k] = dw[1][k] = 0u;
+#pragma unroll
+    for (int cc = 0; cc < 32; ++cc) {
+      const int Qv = (int)rintf(ldexpf(x[cc], 13 - E));
+      const int hi = Qv >> 7, lo = Qv & 127;  // floor(Q / 128) in [-128, 127], and Q - 128 hi
+      qs += Qv;
+      d0s += hi;
+      d1s += lo;
+      const int w = cc & 7;
+      const int pos = (cc & ~7) + (BITS == 8 ? w : ((w & 1) ? 4 + (w >> 1) : (w >> 1)));
+      dw[0][pos >> 2] |= (uint32_t)(hi & 0xff) << (8 * (pos & 3));
+      dw[1][pos >> 2] |= (uint32_t)lo << (8 * (pos & 3));
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_qd[d][qh][qg * 32]);
+      dst[0] = u32x4_t{dw[d][0], dw[d][1], dw[d][2], dw[d][3]};
+      dst[1] = u32x4_t{dw[d][4], dw[d][5], dw[d][6], dw[d][7]};
+    }
+    s_qe[qh][qg] = E;
+    s_qb[qh][qg] = ldexpf((float)qs, E - 13);  // exact: |sum Q| < 2^19
+    if constexpr (BITS == 8) {
+      s_qds[0][qh][qg] = d0s;
+      s_qds[1][qh][qg] = d1s;
+    }
+  }
+  __syncthreads();  // rows and query digits in LDS
 
   // ---- this wave's tiles (wv, wv + 4, ...): code and scale/zero loads all in flight together
   const int kb = lane >> 4, nn = lane & 15, rg = lane >> 4;
@@ -319,46 +366,6 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       mw[i][e] = c.k4_meta[(size_t)max(rw[i][e], 0) * kGroups + (gc & 3)];
     }
   }
-
-  // ---- the fixed-point query, while those loads are in flight
-#pragma unroll
-  for (int i = 0; i < QP; ++i) {
-    const int pr = 2 * wv + (lane >> 5) + 8 * i;
-    if (pr < kGroups * G) {  // uniform over each half-wave; the shuffles stay inside it
-      const int hh = pr >> 2, g = pr & 3, cl = lane & 31;
-      const float x = qx[i];
-      float m = fabsf(x);
-#pragma unroll
-      for (int s = 1; s < 32; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 32));
-      int E = 0;
-      if (m > 0.f) E = max((int)(__float_as_uint(m) >> 23) - 127, -100);
-      const int Qv = (int)rintf(ldexpf(x, 13 - E));
-      const int w = cl & 7;
-      const int pos = g * 32 + (cl & ~7) + (BITS == 8 ? w : ((w & 1) ? 4 + (w >> 1) : (w >> 1)));
-      s_qd[0][hh][pos] = (int8_t)(Qv >> 7);   // floor(Q / 128), in [-128, 127]
-      s_qd[1][hh][pos] = (int8_t)(Qv & 127);  // Q - 128 floor(Q / 128)
-      int qs = Qv;
-#pragma unroll
-      for (int s = 1; s < 32; s <<= 1) qs += __shfl_xor(qs, s, 32);
-      if (cl == 0) {
-        s_qe[hh][g] = E;
-        s_qb[hh][g] = ldexpf((float)qs, E - 13);  // exact: |sum Q| < 2^19
-      }
-      if constexpr (BITS == 8) {
-        int d0 = Qv >> 7, d1 = Qv & 127;
-#pragma unroll
-        for (int s = 1; s < 32; s <<= 1) {
-          d0 += __shfl_xor(d0, s, 32);
-          d1 += __shfl_xor(d1, s, 32);
-        }
-        if (cl == 0) {
-          s_qds[0][hh][g] = d0;
-          s_qds[1][hh][g] = d1;
-        }
-      }
-    }
-  }
-  __syncthreads();
 
   // ---- B operands, the same in every wave: lane (kb, nn) holds column nn = (group gc, head ct GT + hl)
   long Bop[NTL][2][4];
