@@ -100,7 +100,7 @@ def test_cluster_select_parity(cfg):
             _check_clusters(w, ranges, count, w.p1, b, h)
 
 
-def _decode_clusters(w, cache, t, p=None, iters=32, events=None):
+def _decode_clusters(w, cache, t, p=None, iters=32, events=None, lists=True):
     B, Hq, U = w.batch, w.num_q_heads, w.batch * w.num_kv_heads
     ws = workspace(cache, w.max_seq_len)
     out = torch.full((B, Hq, 128), float("nan"), device="cuda")
@@ -110,7 +110,8 @@ def _decode_clusters(w, cache, t, p=None, iters=32, events=None):
     toks = torch.full((max(U * w.max_seq_len, 1),), -7, dtype=torch.int32, device="cuda")
     twl.decode_clusters(cache, t["q"], p=w.p if p is None else p, p1=w.p1, centroids=t["centroids"],
                         csize=t["csize"], coff=t["coff"], iters=iters, out=out, lse=lse, threshold=thr,
-                        sel_indptr=indptr, sel_tokens=toks, ws=ws, events=events)
+                        sel_indptr=indptr if lists else None, sel_tokens=toks if lists else None, ws=ws,
+                        events=events)
     torch.cuda.synchronize()
     return {"out": out.cpu().numpy(), "lse": lse.cpu().numpy(), "thr": thr.cpu().numpy(),
             "indptr": indptr.cpu().numpy(), "tokens": toks.cpu().numpy()}
@@ -276,6 +277,17 @@ def test_wide_decode_end_to_end(wide_case):
             assert err <= tol, (b, h * G + j, err, tol)
 
 
+def test_wide_decode_without_lists_is_bitwise_the_same(wide_case):
+    # the timed form of the decode (no token list requested) gives bitwise the listed run's outputs
+    w, cache, t, res = wide_case
+    _print_case(w.name + " wide decode, no lists")
+    from tests.gpu_helpers import run_decode
+    a = run_decode(w, cache, t)
+    b = run_decode(w, cache, t, with_lists=False)
+    for k in ("out", "lse", "thr"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
 # ---- full-size hierarchical layer (262144 tokens, 4096 clusters) ----------------------------------------
 def test_c5_full_size_sampled_units():
     w = make_config("C5")
@@ -289,3 +301,7 @@ def test_c5_full_size_sampled_units():
     res = pipeline.decode(w, units=[(0, 2), (0, 5)])
     _check_token_stage(w, g, res, ranges, count)
     assert np.all(np.isfinite(g["out"]))
+    # the timed form (no token list requested) is bitwise the same
+    g2 = _decode_clusters(w, cache, t, lists=False)
+    for k in ("out", "lse", "thr"):
+        assert np.array_equal(g[k], g2[k], equal_nan=True), k
