@@ -206,7 +206,8 @@ hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const 
   if ((e = E.rec(5)) != hipSuccess) return e;
   if ((e = E.rec(6)) != hipSuccess) return e;
   if (wide) {
-    e = launch_topp_wide(c, wd, at<float>(ws, L.logits), ncap, p, iters, thr, head_mask, mask_words, s);
+    e = launch_topp_wide(c, wd, at<float>(ws, L.logits), ncap, p, iters, thr, head_mask, mask_words,
+                         with_union || mass || head_mask, s);
     if (e == hipSuccess && (with_union || mass))
       e = launch_wide_emit(c, wd, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), ncap, at<int32_t>(ws, L.utok),
                            at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), mass, s);

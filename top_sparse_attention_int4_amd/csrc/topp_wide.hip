@@ -277,7 +277,8 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
 }
 
 // Per (unit, chunk): head masks under the finished thresholds, the kept mass per head, union words and count.
-template <int G>
+// FULL = false: the union words only (no head masks, kept mass or counts are asked for).
+template <int G, bool FULL>
 __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const float* __restrict__ w, int ncap,
                                                             uint64_t* __restrict__ state,
                                                             uint32_t* __restrict__ head_mask, int mask_words,
@@ -320,11 +321,11 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool keep = xs[e] >= 0.f && xs[e] >= thr[hh];
-        if (keep) kept[hh] += to_fix(xs[e]);
+        if (FULL && keep) kept[hh] += to_fix(xs[e]);
         nib |= (keep ? 1u : 0u) << e;
       }
       unib |= nib;
-      if (head_mask) {
+      if (FULL && head_mask) {
         const uint32_t word = nibbles_to_word(nib);
         if ((lane & 7) == 0 && wd < mask_words) head_mask[(bh0 + hh) * mask_words + wd] = word;
       }
@@ -333,6 +334,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
     const uint32_t uword = nibbles_to_word(unib);
     if ((lane & 7) == 0) uwords[(size_t)u * MW + wd] = uword;
   }
+  if (!FULL) return;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     uint64_t s = wave_suffix_u64(kept[hh]);
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int nca
 }
 
 hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits, int ncap, float p, int iters,
-                            float* threshold, uint32_t* head_mask, int mask_words, hipStream_t s) {
+                            float* threshold, uint32_t* head_mask, int mask_words, bool full, hipStream_t s) {
   if (ncap % kWideChunk) return hipErrorInvalidValue;
   const int nch = ncap / kWideChunk;
   if (ncap % kWideAlign) return hipErrorInvalidValue;
@@ -421,8 +423,12 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits,
                      threshold);
 #define TWL_WIDE_G(GG)                                                                                      \
   case GG:                                                                                                  \
-    hipLaunchKernelGGL(k_wide_mask<GG>, dim3(ugrid), blk, 0, s, c, logits, ncap, wd.state, head_mask,        \
-                       mask_words, wd.uwords, wd.chunk_cnt);                                                \
+    if (full)                                                                                               \
+      hipLaunchKernelGGL((k_wide_mask<GG, true>), dim3(ugrid), blk, 0, s, c, logits, ncap, wd.state,         \
+                         head_mask, mask_words, wd.uwords, wd.chunk_cnt);                                   \
+    else                                                                                                    \
+      hipLaunchKernelGGL((k_wide_mask<GG, false>), dim3(ugrid), blk, 0, s, c, logits, ncap, wd.state,        \
+                         nullptr, 0, wd.uwords, wd.chunk_cnt);                                              \
     break;
   switch (c.G) {
     TWL_WIDE_G(1)

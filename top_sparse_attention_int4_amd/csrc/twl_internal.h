@@ -82,8 +82,10 @@ hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, cons
                            float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s);
 // wide top-p: histogram passes and masks (union bitmap in wd.uwords); the emit kernel writes the
 // compacted union lists and the threshold/mass outputs
+// full: the mask pass also writes the head masks, the kept mass and the per-chunk union counts
+// (needed by head_mask, the mass output and the union lists); otherwise union words only
 hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits, int ncap, float p, int iters,
-                            float* threshold, uint32_t* head_mask, int mask_words, hipStream_t s);
+                            float* threshold, uint32_t* head_mask, int mask_words, bool full, hipStream_t s);
 hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
                             int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, float* mass,
                             hipStream_t s);
