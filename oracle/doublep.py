@@ -18,9 +18,17 @@ attention.  The page gives no formulas; readings taken:
 * token level: the INT4 estimate, one softmax and one top-p (p2) per query head over all tokens of
   the kept ranges (O5-O7), the group union (O8) and sparse attention (O9).  Unkept clusters are
   dropped.
+* optional cluster-level approximation of the unkept clusters (the abstract's refinement to token
+  level only where needed; the method summary has only selected tokens in the attention, so this is
+  an option, off by default): a cluster that no head of the group keeps enters the softmax as its
+  n_c members collapsed onto (mu_c, vbar_c), vbar_c the mean of its value rows -- n_c exp(lambda_c)
+  joins the normaliser and n_c exp(lambda_c) vbar_c the numerator, combined with the attention's
+  (out, lse) in log-sum-exp form.  Exact when every member's key is mu_c and value is vbar_c.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -67,3 +75,34 @@ def ranges_of(kept: np.ndarray, coff: np.ndarray) -> np.ndarray:
     kept = np.asarray(kept, np.int64)
     return np.stack([coff[kept], coff[kept + 1] - coff[kept]], axis=1).astype(np.int64) \
         if kept.size else np.zeros((0, 2), np.int64)
+
+
+def value_means(vbits_seq: np.ndarray, csize: np.ndarray, coff: np.ndarray) -> np.ndarray:
+    """Mean value row of each cluster (float64 [C][128]; zeros for an empty cluster).  ``vbits_seq``
+    uint16 [n][128] of one (sequence, kv-head) in token order."""
+    v = bf16_to_f32(vbits_seq).astype(np.float64)
+    C = len(csize)
+    out = np.zeros((C, 128))
+    for c in range(C):
+        n = int(csize[c])
+        if n > 0:
+            out[c] = v[int(coff[c]):int(coff[c]) + n].mean(axis=0)
+    return out
+
+
+def approx_unkept(out_h: np.ndarray, lse_h: float, lam: np.ndarray, csize: np.ndarray, kept: np.ndarray,
+                  vmean: np.ndarray) -> tuple[np.ndarray, float]:
+    """Combine one head's attention output (``out_h``, natural-log ``lse_h``) with the clusters not in
+    ``kept`` (the group's kept cluster ids): each non-empty one adds n_c exp(lambda_c) to the
+    normaliser and n_c exp(lambda_c) vbar_c to the numerator."""
+    C = len(csize)
+    unk = np.setdiff1d(np.nonzero(np.asarray(csize) > 0)[0], np.asarray(kept, np.int64))
+    if unk.size == 0:
+        return np.asarray(out_h, np.float64), float(lse_h)
+    s = np.asarray(lam, np.float64)[unk] + np.log(np.asarray(csize, np.float64)[unk])
+    M = max(float(s.max()), float(lse_h))
+    wa = math.exp(lse_h - M) if np.isfinite(lse_h) else 0.0
+    wc = np.exp(s - M)
+    den = wa + wc.sum()
+    num = wa * np.asarray(out_h, np.float64) + wc @ vmean[unk]
+    return num / den, M + math.log(den)

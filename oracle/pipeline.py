@@ -73,12 +73,13 @@ def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, 
 
 
 def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=False, bits=4, topk=0,
-           headwise=False) -> dict:
+           headwise=False, approx_unkept=False) -> dict:
     """Run the oracle on a workload-like object (fields of ``gen.Workload``).
 
     ``units`` optionally restricts the work to a list of (b, kv-head) pairs; the cluster path is
     taken when the workload carries clusters (``w.csize`` is not None); ``bits`` is the code width
-    of the estimator's key copy.
+    of the estimator's key copy; ``topk`` / ``headwise`` select the baselines; ``approx_unkept`` adds
+    the unkept clusters' centroid contributions on the cluster path.
     Returns ``{(b, h): decode_unit result}``.
     """
     p = w.p if p is None else p
@@ -104,6 +105,12 @@ def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=Fa
                             with_f64_logits=with_f64_logits, bits=bits)
             r["clusters"] = cs
             r["ranges"] = ranges
+            if approx_unkept:
+                vm = doublep.value_means(vseq, w.csize[b, h], w.coff[b, h])
+                for j in range(G):
+                    lam = cs["per_head"][j]["lam"]
+                    r["out"][j], r["lse"][j] = doublep.approx_unkept(r["out"][j], r["lse"][j], lam, w.csize[b, h],
+                                                                     cs["kept"], vm)
         else:
             r = decode_unit(q, kseq, vseq, p=p, keep_frac=keep_frac, sm=sm,
                             with_f64_logits=with_f64_logits, bits=bits, topk=topk, headwise=headwise)

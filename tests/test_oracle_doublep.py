@@ -71,3 +71,38 @@ def test_workload_clusters_and_ranges():
         # each kept range is exactly its cluster's member tokens
         for (b0, ln), c in zip(rg, cs["kept"]):
             assert b0 == w.coff[0, h, c] and ln == w.csize[0, h, c]
+
+
+# ---- optional approximation of the unkept clusters ---------------------------------------------------
+def test_value_means_by_hand():
+    v = numerics.f32_to_bf16_bits(np.array([[1.0] * 128, [3.0] * 128, [2.0] * 128, [-4.0] * 128], np.float32))
+    m = doublep.value_means(v, np.array([2, 0, 2]), np.array([0, 2, 2]))
+    assert np.array_equal(m[0], np.full(128, 2.0)) and not m[1].any() and np.array_equal(m[2], np.full(128, -1.0))
+
+
+def test_collapsed_clusters_make_the_approximation_exact():
+    # every member of a cluster has key mu_c and value v_c: attention over the kept clusters' tokens,
+    # combined with the unkept clusters' n_c exp(lambda_c) (v_c), is dense attention over every token
+    rng = np.random.default_rng(7)
+    C = 30
+    sizes = rng.integers(1, 20, size=C)
+    sizes[4] = 0
+    mu = numerics.f32_to_bf16_bits(rng.standard_normal((C, 128)).astype(np.float32))
+    vc = numerics.f32_to_bf16_bits(rng.standard_normal((C, 128)).astype(np.float32))
+    keys, vals = np.repeat(mu, sizes, axis=0), np.repeat(vc, sizes, axis=0)
+    coff = np.concatenate([[0], np.cumsum(sizes)])
+    q = numerics.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32))
+    kept = np.array([1, 2, 7, 11, 20])
+    idx = np.concatenate([np.arange(coff[c], coff[c + 1]) for c in kept])
+    o, lse = attention.sparse_attention(q, keys, vals, idx, SM)
+    lam = doublep.cluster_logits_spec(q, mu, SM)
+    vm = doublep.value_means(vals, sizes, coff[:-1])
+    oa, la = doublep.approx_unkept(o, lse, lam, sizes, kept, vm)
+    od, ld = attention.sparse_attention(q, keys, vals, np.arange(len(keys)), SM)
+    assert np.allclose(oa, od, rtol=0, atol=1e-5) and abs(la - ld) < 1e-5
+    # nothing kept: the clusters alone give the same; everything kept: the input is returned
+    oz, lz = doublep.approx_unkept(np.zeros(128), -math.inf, lam, sizes, np.zeros(0, np.int64), vm)
+    assert np.allclose(oz, od, rtol=0, atol=1e-5) and abs(lz - ld) < 1e-5
+    allc = np.nonzero(sizes)[0]
+    o2, l2 = doublep.approx_unkept(o, lse, lam, sizes, allc, vm)
+    assert np.array_equal(o2, o) and l2 == lse
