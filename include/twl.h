@@ -230,6 +230,27 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
                                     const int32_t* coff, int32_t num_clusters, int32_t* ranges,
                                     int32_t* count, void* ws, size_t ws_bytes, void* stream);
 
+/* Optional approximation of the clusters that no head of a group keeps (the Double-P abstract refines
+ * to token level only where the cluster level does not suffice; the pages give no formula, so this
+ * reading is an option and twl_decode_clusters does not apply it): a cluster c not kept enters the
+ * softmax as its n_c members collapsed onto (centroid mu_c, mean value vbar_c).
+ * twl_cluster_value_means: vbar_c of every cluster, the float32 mean of its value rows in token order
+ *   (tokens outside the sequence are skipped; an empty cluster gets zeros), at cache-append time.
+ *   csize, coff as in twl_select_clusters_topp; vmean float32 [B][Hkv][num_clusters][128] (out).
+ * twl_cluster_approx_unkept: after twl_decode_clusters with the same cache, q, sm_scale, p1, iters,
+ *   centroids and csize, merges into its out / lse (in place, natural-log lse) the unkept non-empty
+ *   clusters: with l_c the cluster logit and M = max(lse, max_c (l_c + ln n_c)),
+ *     den = exp(lse - M) + sum_c n_c exp(l_c - M),  out <- (exp(lse - M) out + sum_c n_c exp(l_c - M)
+ *     vbar_c) / den,  lse <- M + ln den.
+ *   It repeats the cluster stage in `ws` (sized by twl_workspace_bytes(cache, m), m >= num_clusters),
+ *   so it selects the decode's clusters; heads whose group keeps every cluster are left unchanged. */
+twl_status twl_cluster_value_means(const twl_cache* cache, const int32_t* csize, const int32_t* coff,
+                                   int32_t num_clusters, float* vmean, void* stream);
+twl_status twl_cluster_approx_unkept(const twl_cache* cache, const void* q, float sm_scale, float p1, int32_t iters,
+                                     const void* centroids, const int32_t* csize, int32_t num_clusters,
+                                     const float* vmean, float* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream);
+
 /* The whole Double-P decode step ("Double-P", 方法详解 and 关键设计): twl_select_clusters_topp with
  * p1, then twl_estimate_topp over the kept ranges with params->p (keep_frac is ignored), then the
  * sparse attention over the union -- the same kernels as the split calls.  Unkept clusters are

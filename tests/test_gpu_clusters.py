@@ -153,6 +153,63 @@ def test_decode_clusters_end_to_end(cfg):
     _check_token_stage(w, g, pipeline.decode(w), ranges, count)
 
 
+@pytest.mark.parametrize("cfg", CLUSTER[:3], ids=CLUSTER_IDS[:3])
+def test_cluster_value_means_parity(cfg):
+    w = make_custom(**cfg)
+    _print_case(w.name + " value means")
+    cache, t = device_cache(w)
+    C = w.csize.shape[-1]
+    vm = torch.full((w.batch, w.num_kv_heads, C, 128), float("nan"), device="cuda")
+    twl.cluster_value_means(cache, t["csize"], t["coff"], vm)
+    torch.cuda.synchronize()
+    vm = vm.cpu().numpy()
+    for b in range(w.batch):
+        v = w.logical("v", b)
+        for h in range(w.num_kv_heads):
+            want = doublep.value_means(v[:, h], w.csize[b, h], w.coff[b, h])
+            assert np.allclose(vm[b, h], want, rtol=0, atol=1e-5), (b, h)
+
+
+@pytest.mark.parametrize("cfg", CLUSTER[:4], ids=CLUSTER_IDS[:4])
+def test_decode_clusters_approx_unkept(cfg):
+    # the decode, then the unkept clusters merged in as (centroid, mean value) with their sizes
+    w = make_custom(**cfg)
+    _print_case(w.name + " approx unkept")
+    cache, t = device_cache(w)
+    g = _decode_clusters(w, cache, t)
+    B, Hq, C = w.batch, w.num_q_heads, w.csize.shape[-1]
+    out = torch.from_numpy(g["out"]).cuda()
+    lse = torch.from_numpy(g["lse"]).cuda()
+    vm = torch.empty((B, w.num_kv_heads, C, 128), device="cuda")
+    twl.cluster_value_means(cache, t["csize"], t["coff"], vm)
+    ws = workspace(cache, max(C, w.max_seq_len))
+    twl.cluster_approx_unkept(cache, t["q"], p1=w.p1, centroids=t["centroids"], csize=t["csize"], vmean=vm,
+                              out=out, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    res = pipeline.decode(w, approx_unkept=True)
+    ranges, count = _cluster_gpu(w, cache, t, w.p1)
+    G = w.group
+    checked = 0
+    for (b, h), r in res.items():
+        u = b * w.num_kv_heads + h
+        got, want = _check_clusters(w, ranges, count, w.p1, b, h)
+        if got != want:
+            continue
+        checked += 1
+        gt = unit_tokens(g, u)
+        k, v = w.logical("k", b)[:, h], w.logical("v", b)[:, h]
+        tol = attn_tolerance(w.q[b, h * G:(h + 1) * G], k, v, r["union"], gt) if len(r["union"]) else 2e-3
+        for j in range(G):
+            if int(w.seq_lens[b]) == 0:
+                continue
+            assert np.max(np.abs(go[b, h * G + j] - r["out"][j])) <= tol, (b, h * G + j)
+            assert abs(gl[b, h * G + j] - r["lse"][j]) <= 1e-3, (b, h * G + j)
+        if len(want) == int((w.csize[b, h] > 0).sum()):  # every cluster kept: the outputs are unchanged
+            assert np.array_equal(go[b, h * G:(h + 1) * G], g["out"][b, h * G:(h + 1) * G])
+    assert checked > 0
+
+
 def test_decode_clusters_fused_equals_split():
     w = make_custom(**CLUSTER[0])
     _print_case(w.name)

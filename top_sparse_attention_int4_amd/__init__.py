@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "LIB_PATH", "TwlError", "PagedCache", "lib", "workspace_bytes", "quantize_k", "select_pages",
     "estimate_topp", "sparse_attn", "decode", "decode_profiled", "select_clusters_topp", "status_str",
-    "version", "keep_count", "NUM_STAGES", "STAGE_NAMES", "DEFAULT_SM_SCALE",
+    "version", "keep_count", "NUM_STAGES", "STAGE_NAMES", "DEFAULT_SM_SCALE", "decode_clusters",
+    "cluster_value_means", "cluster_approx_unkept",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libtwl.so")
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
                                             ctypes.c_size_t, _p]),
         "twl_decode_clusters": (_i32, [C, _p, ctypes.POINTER(ParamsC), _f32, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
                                        _i64, _p, ctypes.c_size_t, _p, ctypes.POINTER(_p)]),
+        "twl_cluster_value_means": (_i32, [C, _p, _p, _i32, _p, _p]),
+        "twl_cluster_approx_unkept": (_i32, [C, _p, _f32, _f32, _i32, _p, _p, _i32, _p, _p, _p, _p, ctypes.c_size_t,
+                                             _p]),
         "twl_status_str": (ctypes.c_char_p, [_i32]),
         "twl_version": (ctypes.c_char_p, []),
     }
@@ -312,3 +316,20 @@ def decode_clusters(cache: PagedCache, q: torch.Tensor, *, p: float, p1: float, 
                                      _ptr(centroids), _ptr(csize), _ptr(coff), int(csize.shape[-1]), _ptr(out),
                                      _ptr(lse), _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap, _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream), arr))
+
+
+def cluster_value_means(cache: PagedCache, csize: torch.Tensor, coff: torch.Tensor, vmean: torch.Tensor,
+                        stream=None):
+    """Mean value row of every cluster into ``vmean`` (float32 [B][Hkv][C][128])."""
+    _check(lib().twl_cluster_value_means(ctypes.byref(cache.struct()), _ptr(csize), _ptr(coff),
+                                         int(csize.shape[-1]), _ptr(vmean), _stream(stream)))
+
+
+def cluster_approx_unkept(cache: PagedCache, q: torch.Tensor, *, p1: float, centroids: torch.Tensor,
+                          csize: torch.Tensor, vmean: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                          ws: torch.Tensor, sm_scale: float = DEFAULT_SM_SCALE, iters: int = 32, stream=None):
+    """Merge the clusters no head of a group kept into ``out`` / ``lse`` of a :func:`decode_clusters`."""
+    _check(lib().twl_cluster_approx_unkept(ctypes.byref(cache.struct()), _ptr(q), float(sm_scale), float(p1),
+                                           int(iters), _ptr(centroids), _ptr(csize), int(csize.shape[-1]),
+                                           _ptr(vmean), _ptr(out), _ptr(lse), _ptr(ws),
+                                           ws.numel() * ws.element_size(), _stream(stream)))

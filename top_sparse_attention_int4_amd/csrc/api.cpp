@@ -550,6 +550,44 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
                                          count, nullptr, nullptr, 0, s));
 }
 
+twl_status twl_cluster_value_means(const twl_cache* cache, const int32_t* csize, const int32_t* coff,
+                                   int32_t num_clusters, float* vmean, void* stream) {
+  twl_status st = check_cache(cache, true, false);
+  if (st != TWL_OK) return st;
+  if (!csize || !coff || !vmean || num_clusters < 1 || num_clusters > kNarrowMaxCands) return TWL_EINVAL;
+  st = check_device();
+  if (st != TWL_OK) return st;
+  return hip_status(launch_cluster_vmean(make_view(cache), csize, coff, num_clusters, vmean,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+twl_status twl_cluster_approx_unkept(const twl_cache* cache, const void* q, float sm_scale, float p1, int32_t iters,
+                                     const void* centroids, const int32_t* csize, int32_t num_clusters,
+                                     const float* vmean, float* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  twl_status st = check_cache(cache, false, false);
+  if (st != TWL_OK) return st;
+  if (!q || misaligned16(q) || !centroids || !csize || !vmean || !out || !lse) return TWL_EINVAL;
+  if (!finite(p1) || !(p1 > 0.f) || p1 > 1.f || !finite(sm_scale)) return TWL_EINVAL;
+  if (iters < 1 || iters > 64 || num_clusters < 1) return TWL_EINVAL;
+  if (num_clusters > kNarrowMaxCands) return TWL_EUNSUPPORTED;
+  const int64_t cpad = ncap_of(num_clusters);
+  Layout L;
+  make_layout(cache, cpad, &L);
+  st = check_ws(ws, ws_bytes, L);
+  if (st != TWL_OK) return st;
+  st = check_device();
+  if (st != TWL_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const CacheView c = make_view(cache);
+  // the cluster stage again (the same kernels and inputs select the same clusters as the decode did)
+  TWL_TRY(launch_cluster_scores_topp(c, static_cast<const uint16_t*>(q), sm_scale, p1, iters,
+                                     static_cast<const uint16_t*>(centroids), csize, num_clusters, (int)cpad,
+                                     at<float>(ws, L.logits), at<float>(ws, L.thr), at<uint32_t>(ws, L.masks), s));
+  return hip_status(launch_cluster_approx(c, at<float>(ws, L.logits), at<uint32_t>(ws, L.masks), (int)cpad, csize,
+                                          num_clusters, vmean, out, lse, s));
+}
+
 twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_decode_params* params, float p1,
                                const void* centroids, const int32_t* csize, const int32_t* coff,
                                int32_t num_clusters, float* out, float* lse, float* threshold, int32_t* sel_indptr,

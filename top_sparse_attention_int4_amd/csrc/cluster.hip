@@ -246,4 +246,116 @@ hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, flo
   return launch_topp_weighted(c, lam, cpad, p1, iters, thr, mask_ws, csize, C, s);
 }
 
+// ---- optional approximation of the clusters no head of the group keeps ------------------------------
+// (Double-P abstract: token-level attention only where the cluster level does not suffice.)  A cluster
+// that is not kept enters the softmax as its n members collapsed onto (centroid key, mean value):
+// n exp(l_c) joins the normaliser and n exp(l_c) vbar_c the numerator, merged with the attention's
+// (out, lse) in log-sum-exp form.
+
+// Mean value row of every cluster: one 128-thread block per (cluster, unit), thread d sums dim d over
+// the cluster's tokens in order (float32), then divides by the size; empty clusters get zeros.
+__global__ __launch_bounds__(128) void k_cluster_vmean(CacheView c, const int32_t* __restrict__ csize,
+                                                       const int32_t* __restrict__ coff, int C, float* vmean) {
+  const int cl = blockIdx.x, u = blockIdx.y;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int d = threadIdx.x;
+  const int n = csize[(size_t)u * C + cl];
+  const int t0 = coff[(size_t)u * (C + 1) + cl];
+  const int seq = clampi(c.seq_lens[b], 0, c.maxTok);
+  float acc = 0.f;
+  int cnt = 0;
+  for (int i = 0; i < n; ++i) {
+    const int t = t0 + i;
+    if (t < 0 || t >= seq) continue;  // tokens outside the sequence are not members
+    const int phys = c.page_table[(size_t)b * c.maxP + (t >> 4)];
+    const size_t row = ((size_t)phys * c.Hkv + h) * kPage + (t & 15);
+    acc += __uint_as_float((uint32_t)c.v[row * kD + d] << 16);
+    ++cnt;
+  }
+  vmean[((size_t)u * C + cl) * kD + d] = cnt > 0 ? acc / (float)cnt : 0.f;
+}
+
+// Per (sequence, query head): the unkept non-empty clusters' terms merged into out / lse.
+constexpr int kApproxChunk = 2048;
+template <int G>
+__global__ __launch_bounds__(256) void k_cluster_approx(CacheView c, const float* __restrict__ lam,
+                                                        const uint32_t* __restrict__ masks, int cpad,
+                                                        const int32_t* __restrict__ csize, int C,
+                                                        const float* __restrict__ vmean, float* out, float* lse) {
+  constexpr int NT = 256, NW = NT / 64;
+  __shared__ float s_w[kApproxChunk];
+  __shared__ float s_acc[2][kD];
+  __shared__ float red[2 * NW * 4];
+  BlockReduce<NW> br{red};
+  const int bh = blockIdx.x;
+  const int b = bh / c.Hq, hq = bh - b * c.Hq, h = hq / G;
+  const int u = b * c.Hkv + h;
+  const int tid = threadIdx.x, d = tid & (kD - 1), half = tid >> 7;
+  const int mw = cpad / 32;
+  const float* lm = lam + (size_t)bh * cpad;
+  const uint32_t* mk = masks + ((size_t)b * c.Hq + (size_t)h * G) * mw;
+  const int32_t* cs = csize + (size_t)u * C;
+  const float* vm = vmean + (size_t)u * C * kD;
+  auto weight_arg = [&](int cl) -> float {  // l_c + ln n_c of an unkept non-empty cluster, else -inf
+    const int n = cs[cl];
+    if (n <= 0) return -__builtin_inff();
+    uint32_t any = 0u;
+#pragma unroll
+    for (int g = 0; g < G; ++g) any |= mk[(size_t)g * mw + (cl >> 5)];
+    if ((any >> (cl & 31)) & 1u) return -__builtin_inff();
+    return lm[cl] + logf((float)n);
+  };
+  const float lse_a = lse[bh];
+  float m = -__builtin_inff();
+  for (int cl = tid; cl < C; cl += NT) m = fmaxf(m, weight_arg(cl));
+  m = br.max(m);
+  if (m == -__builtin_inff()) return;  // every non-empty cluster is kept: nothing to add
+  const float M = fmaxf(m, lse_a);
+  float acc = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < C; c0 += kApproxChunk) {
+    const int nc = min(kApproxChunk, C - c0);
+    for (int i = tid; i < nc; i += NT) {
+      const float a = weight_arg(c0 + i);
+      const float w = (a == -__builtin_inff()) ? 0.f : expf(a - M);
+      s_w[i] = w;
+      den += w;
+    }
+    __syncthreads();
+    for (int i = half; i < nc; i += 2) {
+      const float w = s_w[i];  // uniform over the half block
+      if (w != 0.f) acc = fmaf(w, vm[(size_t)(c0 + i) * kD + d], acc);
+    }
+    __syncthreads();
+  }
+  s_acc[half][d] = acc;
+  den = br.sum(den);  // (its barrier also orders s_acc)
+  if (tid < kD) {
+    const float wa = (lse_a == -__builtin_inff()) ? 0.f : expf(lse_a - M);
+    const float tot = wa + den;
+    float* o = out + (size_t)bh * kD;
+    o[d] = (wa * o[d] + s_acc[0][d] + s_acc[1][d]) / tot;
+    if (tid == 0) lse[bh] = M + logf(tot);
+  }
+}
+
+hipError_t launch_cluster_vmean(const CacheView& c, const int32_t* csize, const int32_t* coff, int C, float* vmean,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(k_cluster_vmean, dim3((unsigned)C, (unsigned)(c.B * c.Hkv)), dim3(128), 0, s, c, csize, coff, C,
+                     vmean);
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_approx(const CacheView& c, const float* lam, const uint32_t* masks, int cpad,
+                                 const int32_t* csize, int C, const float* vmean, float* out, float* lse, hipStream_t s) {
+  const dim3 grid((unsigned)(c.B * c.Hq)), blk(256);
+  switch (c.G) {
+    case 1: hipLaunchKernelGGL(k_cluster_approx<1>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
+    case 2: hipLaunchKernelGGL(k_cluster_approx<2>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
+    case 4: hipLaunchKernelGGL(k_cluster_approx<4>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
+    case 8: hipLaunchKernelGGL(k_cluster_approx<8>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace twl

@@ -97,6 +97,12 @@ hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, flo
                                       float* thr, uint32_t* mask_ws, hipStream_t s);
 // union of a unit's head masks -> kept ranges (first token, length) and count; with prefix non-NULL
 // also the ranges' prefix sums [U][C + 1] and the range of each 256-candidate block [U][nchunk]
+// optional approximation of unkept clusters: mean value rows [B*Hkv][C][128], then the merge into
+// out / lse of every (sequence, query head) from the cluster logits and head masks of the cluster stage
+hipError_t launch_cluster_vmean(const CacheView& c, const int32_t* csize, const int32_t* coff, int C, float* vmean,
+                                hipStream_t s);
+hipError_t launch_cluster_approx(const CacheView& c, const float* lam, const uint32_t* masks, int cpad,
+                                 const int32_t* csize, int C, const float* vmean, float* out, float* lse, hipStream_t s);
 hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
                                 const int32_t* coff, int C, int32_t* ranges, int32_t* count, int32_t* prefix,
                                 int32_t* chunk_first, int nchunk, hipStream_t s);
