@@ -24,6 +24,10 @@ with group-union and head-wise attention: K/V rows read, per-head set sizes, out
 attention over all the base selector's candidates (what the pruning approximates) and against dense
 attention, and decode time, one JSON line.
 
+With ``--cluster-approx`` (hierarchical workload) it measures the optional approximation of the
+clusters no head keeps: the time of that step and each head's output error against dense attention
+with and without it, one JSON line.
+
 Prints ONE JSON line.  ``value`` is microseconds per layer-step (lower is better).  ``roofline``
 describes the split-K attention kernel (the stage that moves most bytes): its algorithmic bytes per
 launch (512 B of K/V rows + 4 B index per kept token, plus the group's q) over its average launch
@@ -72,6 +76,8 @@ def parse():
                     help="report the 2/4/8-bit estimator ablation instead of the step benchmark")
     ap.add_argument("--baselines", action="store_true",
                     help="compare top-p with the equal-budget top-k baseline, union vs head-wise")
+    ap.add_argument("--cluster-approx", action="store_true",
+                    help="measure the optional approximation of the unkept clusters (C5)")
     ap.add_argument("--offload", action="store_true",
                     help="time the decode with K/V in pinned host memory (top-p vs the base selector alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -113,6 +119,9 @@ def main():
         return
     if args.baselines:
         baselines_report(args, dev)
+        return
+    if args.cluster_approx:
+        cluster_approx_report(args, dev)
         return
     if args.copy_calibration:
         # a plain device copy of known size: 512 MiB read + 512 MiB written per launch
@@ -543,6 +552,72 @@ def baselines_report(args, dev):
                                          "min": int(bits_m[..., :maxcand].sum(-1).min()),
                                          "max": int(bits_m[..., :maxcand].sum(-1).max())},
                       "rows": rows}))
+
+
+def cluster_approx_report(args, dev):
+    """The optional merge of the unkept clusters (as centroid key and mean value, times their size)
+    into the hierarchical decode's output: its event-timed duration, and every head's relative L2
+    error against dense attention over the whole context (float32 torch) with and without it."""
+    import torch
+    import top_sparse_attention_int4_amd as twl
+    from gen import make_config
+    from gen.device import upload
+
+    name = args.workload if args.workload == "C5" else "C5"
+    w = make_config(name)
+    t = upload(w, dev)
+    B, Hq, Hkv, G = w.batch, w.num_q_heads, w.num_kv_heads, w.group
+    C = w.csize.shape[-1]
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+    cache = twl.PagedCache(t["k_pages"], t["v_pages"], t["page_table"], t["seq_lens"], Hq, max_seq_len=w.max_seq_len)
+    twl.quantize_k(cache, torch.zeros(B, dtype=torch.int32, device=dev), t["seq_lens"], w.max_seq_len)
+    ws = torch.empty(twl.workspace_bytes(cache, max(C, w.max_seq_len)), dtype=torch.uint8, device=dev)
+    vm = torch.empty((B, Hkv, C, 128), device=dev)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    twl.cluster_value_means(cache, t["csize"], t["coff"], vm)
+    a1.record()
+    out = torch.empty((B, Hq, 128), device=dev)
+    lse = torch.empty((B, Hq), device=dev)
+    K = max(10, min(args.steps, 50))
+    dec_us, apx_us = [], []
+    for i in range(K + 3):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        twl.decode_clusters(cache, t["q"], p=w.p, p1=w.p1, centroids=t["centroids"], csize=t["csize"],
+                            coff=t["coff"], out=out, lse=lse, ws=ws)
+        e[1].record()
+        if i == K + 2:
+            base = out.clone()
+        twl.cluster_approx_unkept(cache, t["q"], p1=w.p1, centroids=t["centroids"], csize=t["csize"], vmean=vm,
+                                  out=out, lse=lse, ws=ws)
+        e[2].record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            dec_us.append(e[0].elapsed_time(e[1]) * 1e3)
+            apx_us.append(e[1].elapsed_time(e[2]) * 1e3)
+    approx = out.clone()
+    kf, vf, qf = t["k_pages"].float(), t["v_pages"].float(), t["q"].float()
+    errs = {"decode": [], "decode + unkept clusters": []}
+    for b in range(B):
+        n = int(w.seq_lens[b])
+        npg = -(-n // 16)
+        pt = t["page_table"][b, :npg].long()
+        ks = kf[pt].permute(1, 0, 2, 3).reshape(Hkv, npg * 16, 128)[:, :n]
+        vs = vf[pt].permute(1, 0, 2, 3).reshape(Hkv, npg * 16, 128)[:, :n]
+        for h in range(Hkv):
+            od = torch.softmax((ks[h] @ qf[b, h * G:(h + 1) * G].T).T * sm, -1) @ vs[h]
+            for key, o in (("decode", base), ("decode + unkept clusters", approx)):
+                x = o[b, h * G:(h + 1) * G]
+                errs[key].append((torch.linalg.norm(x - od, dim=-1) / torch.linalg.norm(od, dim=-1)).cpu().numpy())
+    rows = {k: {"mean": round(float(np.concatenate(v).mean()), 5), "max": round(float(np.concatenate(v).max()), 5)}
+            for k, v in errs.items()}
+    torch.cuda.synchronize()
+    print(json.dumps({"metric": "unkept-cluster approximation: time and error against dense attention",
+                      "workload": name, "clusters": C, "p1": w.p1, "p": w.p, "steps": K, "data": "synthetic",
+                      "decode_us": round(float(np.mean(dec_us)), 1), "approx_us": round(float(np.mean(apx_us)), 1),
+                      "value_means_us_once": round(a0.elapsed_time(a1) * 1e3, 1),
+                      "error_vs_dense": rows}))
 
 
 def offload_report(args, dev):

@@ -99,7 +99,7 @@ struct Layout {
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
          ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
-         wkeys = 0, total = 0;
+         wkeys = 0, apart = 0, total = 0;
 };
 
 // ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
@@ -144,6 +144,7 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->crow = take((size_t)U * ncap * 4);
   L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
   L->thr = take((size_t)BH * 4);
+  L->apart = take((size_t)BH * kApproxSlices * kApproxStride * 4);  // unkept-cluster approximation
   if (is_wide(ncap)) {
     L->pmax = take((size_t)BH * (ncap / kEstCands) * 4);
     L->wstate = take((size_t)BH * kWideStateWords * 8);
@@ -585,7 +586,7 @@ twl_status twl_cluster_approx_unkept(const twl_cache* cache, const void* q, floa
                                      static_cast<const uint16_t*>(centroids), csize, num_clusters, (int)cpad,
                                      at<float>(ws, L.logits), at<float>(ws, L.thr), at<uint32_t>(ws, L.masks), s));
   return hip_status(launch_cluster_approx(c, at<float>(ws, L.logits), at<uint32_t>(ws, L.masks), (int)cpad, csize,
-                                          num_clusters, vmean, out, lse, s));
+                                          num_clusters, vmean, out, lse, at<float>(ws, L.apart), s));
 }
 
 twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_decode_params* params, float p1,

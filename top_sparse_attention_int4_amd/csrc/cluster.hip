@@ -252,42 +252,71 @@ hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, flo
 // n exp(l_c) joins the normaliser and n exp(l_c) vbar_c the numerator, merged with the attention's
 // (out, lse) in log-sum-exp form.
 
-// Mean value row of every cluster: one 128-thread block per (cluster, unit), thread d sums dim d over
-// the cluster's tokens in order (float32), then divides by the size; empty clusters get zeros.
-__global__ __launch_bounds__(128) void k_cluster_vmean(CacheView c, const int32_t* __restrict__ csize,
-                                                       const int32_t* __restrict__ coff, int C, float* vmean) {
+// Mean value row of every cluster: one 1024-thread block per (cluster, unit); thread (j, d) sums dim d
+// over the cluster's tokens j, j + 8, ... (four rows in flight), the eight partial sums are added in
+// order of j and divided by the member count; empty clusters get zeros.
+__global__ __launch_bounds__(1024) void k_cluster_vmean(CacheView c, const int32_t* __restrict__ csize,
+                                                        const int32_t* __restrict__ coff, int C, float* vmean) {
+  constexpr int NJ = 8, UN = 4;
+  __shared__ float s_sum[NJ][kD];
+  __shared__ int s_cnt[NJ];
   const int cl = blockIdx.x, u = blockIdx.y;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x & (kD - 1), j = threadIdx.x >> 7;
   const int n = csize[(size_t)u * C + cl];
   const int t0 = coff[(size_t)u * (C + 1) + cl];
   const int seq = clampi(c.seq_lens[b], 0, c.maxTok);
   float acc = 0.f;
   int cnt = 0;
-  for (int i = 0; i < n; ++i) {
-    const int t = t0 + i;
-    if (t < 0 || t >= seq) continue;  // tokens outside the sequence are not members
-    const int phys = c.page_table[(size_t)b * c.maxP + (t >> 4)];
-    const size_t row = ((size_t)phys * c.Hkv + h) * kPage + (t & 15);
-    acc += __uint_as_float((uint32_t)c.v[row * kD + d] << 16);
-    ++cnt;
+  for (int i0 = j; i0 < n; i0 += NJ * UN) {
+    float x[UN];
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const int i = i0 + NJ * k, t = t0 + i;
+      x[k] = 0.f;
+      if (i < n && t >= 0 && t < seq) {  // tokens outside the sequence are not members
+        const int phys = c.page_table[(size_t)b * c.maxP + (t >> 4)];
+        const size_t row = ((size_t)phys * c.Hkv + h) * kPage + (t & 15);
+        x[k] = __uint_as_float((uint32_t)c.v[row * kD + d] << 16);
+        ++cnt;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < UN; ++k) acc += x[k];
   }
-  vmean[((size_t)u * C + cl) * kD + d] = cnt > 0 ? acc / (float)cnt : 0.f;
+  s_sum[j][d] = acc;
+  if (d == 0) s_cnt[j] = cnt;
+  __syncthreads();
+  if (j == 0) {
+    float tot = 0.f;
+    int m = 0;
+#pragma unroll
+    for (int k = 0; k < NJ; ++k) {
+      tot += s_sum[k][d];
+      m += s_cnt[k];
+    }
+    vmean[((size_t)u * C + cl) * kD + d] = m > 0 ? tot / (float)m : 0.f;
+  }
 }
 
-// Per (sequence, query head): the unkept non-empty clusters' terms merged into out / lse.
-constexpr int kApproxChunk = 2048;
+// Per (sequence, query head, slice of kApproxSlices): the unkept non-empty clusters of the slice summed
+// as (sum_c w_c vbar_c, sum_c w_c) with w_c = n_c exp(l_c - M), M the head's largest l_c + ln n_c over
+// all unkept clusters and its lse (each block finds M itself); then one block per head merges the
+// slices in order with the attention's (out, lse).
+constexpr int kApproxSliceMax = 1024;  // clusters per slice held in LDS at once
+
 template <int G>
 __global__ __launch_bounds__(256) void k_cluster_approx(CacheView c, const float* __restrict__ lam,
                                                         const uint32_t* __restrict__ masks, int cpad,
                                                         const int32_t* __restrict__ csize, int C,
-                                                        const float* __restrict__ vmean, float* out, float* lse) {
-  constexpr int NT = 256, NW = NT / 64;
-  __shared__ float s_w[kApproxChunk];
+                                                        const float* __restrict__ vmean, const float* __restrict__ lse,
+                                                        float* __restrict__ part) {
+  constexpr int NT = 256, NW = NT / 64, UN = 8;
+  __shared__ float s_w[kApproxSliceMax];
   __shared__ float s_acc[2][kD];
   __shared__ float red[2 * NW * 4];
   BlockReduce<NW> br{red};
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x, sl = blockIdx.y;
   const int b = bh / c.Hq, hq = bh - b * c.Hq, h = hq / G;
   const int u = b * c.Hkv + h;
   const int tid = threadIdx.x, d = tid & (kD - 1), half = tid >> 7;
@@ -305,56 +334,89 @@ __global__ __launch_bounds__(256) void k_cluster_approx(CacheView c, const float
     if ((any >> (cl & 31)) & 1u) return -__builtin_inff();
     return lm[cl] + logf((float)n);
   };
-  const float lse_a = lse[bh];
   float m = -__builtin_inff();
   for (int cl = tid; cl < C; cl += NT) m = fmaxf(m, weight_arg(cl));
   m = br.max(m);
-  if (m == -__builtin_inff()) return;  // every non-empty cluster is kept: nothing to add
-  const float M = fmaxf(m, lse_a);
+  const float M = fmaxf(m, lse[bh]);
+  const int per = (C + kApproxSlices - 1) / kApproxSlices;
+  const int c0 = sl * per, c1 = min(C, c0 + per);
   float acc = 0.f, den = 0.f;
-  for (int c0 = 0; c0 < C; c0 += kApproxChunk) {
-    const int nc = min(kApproxChunk, C - c0);
-    for (int i = tid; i < nc; i += NT) {
-      const float a = weight_arg(c0 + i);
-      const float w = (a == -__builtin_inff()) ? 0.f : expf(a - M);
-      s_w[i] = w;
-      den += w;
+  if (m != -__builtin_inff()) {
+    for (int cb = c0; cb < c1; cb += kApproxSliceMax) {
+      const int nc = min(kApproxSliceMax, c1 - cb);
+      for (int i = tid; i < nc; i += NT) {
+        const float a = weight_arg(cb + i);
+        const float w = (a == -__builtin_inff()) ? 0.f : expf(a - M);
+        s_w[i] = w;
+        den += w;
+      }
+      __syncthreads();
+      // UN clusters' value rows in flight per step (each half block takes every other cluster)
+      for (int i0 = half; i0 < nc; i0 += 2 * UN) {
+        float x[UN], wv[UN];
+#pragma unroll
+        for (int k = 0; k < UN; ++k) {
+          const int i = i0 + 2 * k;
+          wv[k] = i < nc ? s_w[i] : 0.f;
+          x[k] = (wv[k] != 0.f) ? vm[(size_t)(cb + i) * kD + d] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < UN; ++k) acc = fmaf(wv[k], x[k], acc);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int i = half; i < nc; i += 2) {
-      const float w = s_w[i];  // uniform over the half block
-      if (w != 0.f) acc = fmaf(w, vm[(size_t)(c0 + i) * kD + d], acc);
-    }
-    __syncthreads();
   }
   s_acc[half][d] = acc;
   den = br.sum(den);  // (its barrier also orders s_acc)
   if (tid < kD) {
-    const float wa = (lse_a == -__builtin_inff()) ? 0.f : expf(lse_a - M);
-    const float tot = wa + den;
-    float* o = out + (size_t)bh * kD;
-    o[d] = (wa * o[d] + s_acc[0][d] + s_acc[1][d]) / tot;
-    if (tid == 0) lse[bh] = M + logf(tot);
+    float* pp = part + ((size_t)bh * kApproxSlices + sl) * kApproxStride;
+    pp[d] = s_acc[0][d] + s_acc[1][d];
+    if (tid == 0) {
+      pp[kD] = den;
+      pp[kD + 1] = M;
+    }
   }
+}
+
+__global__ __launch_bounds__(128) void k_cluster_approx_merge(const float* __restrict__ part, float* out, float* lse) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* pp = part + (size_t)bh * kApproxSlices * kApproxStride;
+  const float M = pp[kD + 1];  // the same in every slice
+  float num = 0.f, den = 0.f;
+#pragma unroll 4
+  for (int sl = 0; sl < kApproxSlices; ++sl) {
+    num += pp[sl * kApproxStride + d];
+    den += pp[sl * kApproxStride + kD];
+  }
+  if (den == 0.f) return;  // every non-empty cluster kept: nothing to add
+  const float lse_a = lse[bh];
+  const float wa = (lse_a == -__builtin_inff()) ? 0.f : expf(lse_a - M);
+  const float tot = wa + den;
+  float* o = out + (size_t)bh * kD;
+  o[d] = (wa * o[d] + num) / tot;
+  __syncthreads();  // every thread has read lse before it is rewritten
+  if (d == 0) lse[bh] = M + logf(tot);
 }
 
 hipError_t launch_cluster_vmean(const CacheView& c, const int32_t* csize, const int32_t* coff, int C, float* vmean,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(k_cluster_vmean, dim3((unsigned)C, (unsigned)(c.B * c.Hkv)), dim3(128), 0, s, c, csize, coff, C,
-                     vmean);
+  hipLaunchKernelGGL(k_cluster_vmean, dim3((unsigned)C, (unsigned)(c.B * c.Hkv)), dim3(1024), 0, s, c, csize, coff,
+                     C, vmean);
   return hipGetLastError();
 }
 
 hipError_t launch_cluster_approx(const CacheView& c, const float* lam, const uint32_t* masks, int cpad,
-                                 const int32_t* csize, int C, const float* vmean, float* out, float* lse, hipStream_t s) {
-  const dim3 grid((unsigned)(c.B * c.Hq)), blk(256);
+                                 const int32_t* csize, int C, const float* vmean, float* out, float* lse, float* part,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)(c.B * c.Hq), kApproxSlices), blk(256);
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_cluster_approx<1>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
-    case 2: hipLaunchKernelGGL(k_cluster_approx<2>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
-    case 4: hipLaunchKernelGGL(k_cluster_approx<4>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
-    case 8: hipLaunchKernelGGL(k_cluster_approx<8>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, out, lse); break;
+    case 1: hipLaunchKernelGGL(k_cluster_approx<1>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, lse, part); break;
+    case 2: hipLaunchKernelGGL(k_cluster_approx<2>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, lse, part); break;
+    case 4: hipLaunchKernelGGL(k_cluster_approx<4>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, lse, part); break;
+    case 8: hipLaunchKernelGGL(k_cluster_approx<8>, grid, blk, 0, s, c, lam, masks, cpad, csize, C, vmean, lse, part); break;
     default: return hipErrorInvalidValue;
   }
+  hipLaunchKernelGGL(k_cluster_approx_merge, dim3((unsigned)(c.B * c.Hq)), dim3(128), 0, s, part, out, lse);
   return hipGetLastError();
 }
 

@@ -102,7 +102,10 @@ hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, flo
 hipError_t launch_cluster_vmean(const CacheView& c, const int32_t* csize, const int32_t* coff, int C, float* vmean,
                                 hipStream_t s);
 hipError_t launch_cluster_approx(const CacheView& c, const float* lam, const uint32_t* masks, int cpad,
-                                 const int32_t* csize, int C, const float* vmean, float* out, float* lse, hipStream_t s);
+                                 const int32_t* csize, int C, const float* vmean, float* out, float* lse, float* part,
+                                 hipStream_t s);
+constexpr int kApproxSlices = 16;       // cluster slices per head in the approximation's first pass
+constexpr int kApproxStride = 128 + 4;  // floats per slice partial: 128 sums, the weight sum, M
 hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
                                 const int32_t* coff, int C, int32_t* ranges, int32_t* count, int32_t* prefix,
                                 int32_t* chunk_first, int nchunk, hipStream_t s);
