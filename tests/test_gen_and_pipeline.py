@@ -1,6 +1,7 @@
 """Seeded generator checks and oracle pipeline invariants (CPU only)."""
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -65,3 +66,12 @@ def test_pipeline_empty_sequence():
     res = pipeline.decode(w)
     assert res[(0, 0)]["union"].size == 0 and np.all(res[(0, 0)]["out"] == 0)
     assert res[(1, 0)]["union"].size >= 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
