@@ -97,8 +97,8 @@ def kernel_source_hash() -> str:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the path shards over (batch, kv-head) units "
-              "with no exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py runs on one GPU only (the path would shard over (batch, kv-head) units with no "
+              "exchange). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,6 +1,6 @@
 """GPU parity: every stage of the HIP path against the CPU oracle on the same seeded inputs.
 
-Bars (stated by the benchmark spec and derived in the oracle):
+Bars (the parity rules that go with the oracle):
 * INT4 codes, fp16 scale/zero, page bounds and page selections: bit-exact;
 * top-p sets: equal except for tokens the oracle marks ambiguous (within 1e-6 relative of the
   threshold weight, or at a rank whose preceding prefix mass is within 1e-5 of p), and the kept
