@@ -74,7 +74,7 @@ typedef struct twl_cache {
   const int32_t* seq_lens;    /* [B] tokens per sequence, 0 <= seq_lens[b] <= max_seq_len         */
   const void* k;              /* bf16 keys                                                       */
   const void* v;              /* bf16 values                                                     */
-  void* k4;                   /* INT4 key codes (written by twl_quantize_k)                      */
+  void* k4;                   /* key codes, key_bits wide (written by twl_quantize_k)            */
   void* k4_meta;              /* fp16 scale/zero (written by twl_quantize_k)                     */
   void* kbound;               /* bf16 page key bounds (written by twl_quantize_k)                */
   int32_t key_bits;           /* code width of k4: 4 (0 means 4), or 2 / 8 for the estimator's    */
@@ -155,9 +155,10 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
  *     E_g = floor(log2 max_{c in g} |q_c|) (>= -100),  Q_c = rne(q_c * 2^(13 - E_g)),
  *   exact for channels within 2^6 of the group's largest; then for each candidate and query head,
  *   with codes code_c, fp16 scale s_g and zero z_g,
- *     a_g = 2^(E_g-13) sum_{c in g} Q_c*code_c,  b_g = 2^(E_g-13) sum_{c in g} Q_c   (exact)
+ *     a_g = 2^(E_g-13) fl(sum_{c in g} Q_c*code_c),  b_g = 2^(E_g-13) sum_{c in g} Q_c   (exact)
  *     logit = fl(sm_scale * ((t_0 + t_1) + (t_2 + t_3))),  t_g = fl(s_g*a_g) + fl(z_g*b_g)
- *   i.e. sm * q~ . dequant(k) for the fixed-point query q~, every group sum exact.
+ *   i.e. sm * q~ . dequant(k) for the fixed-point query q~, every group sum exact (with 8-bit codes,
+ *   key_bits = 8, the integer group sum exceeds 2^24 and rounds once to float32).
  * - Weights: softmax of the logits over the unit's candidates only.
  * - Top-p (Paper-Notes "关键设计 / 高效Top-p": binary search of the threshold m with
  *   sum_{W_i >= m} W_i >= p, no sort): `iters` bisection steps on the uint32 image of the
