@@ -175,3 +175,23 @@ def test_decode_clusters_validates():
     nulls = (ctypes.byref(c), fake, ctypes.byref(prm), 0.95, None, fake, fake, 4096, fake, None, None, None, None, 0,
              fake, 1 << 40, None, None)
     assert L.twl_decode_clusters(*nulls) == 1                         # centroids missing
+    prm.topk = 8                                                      # baselines are for the page path only
+    assert L.twl_decode_clusters(*args(0.95, 4096, 1 << 40)) == 2
+    prm.topk, prm.headwise = 0, 1
+    assert L.twl_decode_clusters(*args(0.95, 4096, 1 << 40)) == 2
+
+
+def test_cluster_approx_entry_points_validate():
+    import top_sparse_attention_int4_amd as t
+    L = t.lib()
+    c = _fake_cache(t)
+    fake = ctypes.c_void_p(0x10000)
+    assert L.twl_cluster_value_means(ctypes.byref(c), fake, fake, 0, fake, None) == 1       # no clusters
+    assert L.twl_cluster_value_means(ctypes.byref(c), None, fake, 64, fake, None) == 1      # csize missing
+    ok = (ctypes.byref(c), fake, 0.088, 0.95, 32, fake, fake, 64, fake, fake, fake, fake, 1 << 40, None)
+    bad_p1 = ok[:3] + (1.5,) + ok[4:]
+    assert L.twl_cluster_approx_unkept(*bad_p1) == 1
+    no_lse = ok[:10] + (None,) + ok[11:]
+    assert L.twl_cluster_approx_unkept(*no_lse) == 1
+    small_ws = ok[:12] + (256,) + ok[13:]
+    assert L.twl_cluster_approx_unkept(*small_ws) == 3
