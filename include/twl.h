@@ -101,9 +101,9 @@ typedef struct twl_decode_params {
   float sm_scale;   /* softmax scale, finite (usually 1/sqrt(128))                                 */
   int32_t iters;    /* bisection steps, 1..64 (32 always converges)                                 */
   /* Baselines the pages compare top-p against (paperlayer §3, Fig. 2-3; §B.2 on GQA); 0 = off.
-   * topk > 0: each head keeps its topk largest estimated weights (ties at the topk-th kept; when
-   *   fewer than topk weights reach 2^-40 of the head's largest, every candidate) instead of its
-   *   top-p set; p is then unused.
+   * topk > 0: each head keeps its topk largest estimated weights (ties at the topk-th kept) instead
+   *   of its top-p set; p is then unused.  The search counts only weights of at least 2^-40 of the
+   *   head's largest, so when fewer than topk weights reach that, every candidate is kept.
    * headwise = 1: each query head attends over its own kept set instead of the group's union (the
    *   union's rows are still read once per group).
    * Both need at most 65536 candidates per group (TWL_EUNSUPPORTED otherwise, and in
@@ -151,24 +151,27 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
 
 /* Weight estimate + top-p pruning + GQA union (Twilight pruner).
  * - Estimate (paperlayer §4.2, §B.1: mixed-precision SpGEMV of the query against dequantised INT4
- *   keys): the query is held per head and 32-channel group g in fixed point,
- *     E_g = floor(log2 max_{c in g} |q_c|) (>= -100),  Q_c = rne(q_c * 2^(13 - E_g)),
- *   exact for channels within 2^6 of the group's largest; then for each candidate and query head,
- *   with codes code_c, fp16 scale s_g and zero z_g,
- *     a_g = 2^(E_g-13) fl(sum_{c in g} Q_c*code_c),  b_g = 2^(E_g-13) sum_{c in g} Q_c   (exact)
- *     logit = fl(sm_scale * ((t_0 + t_1) + (t_2 + t_3))),  t_g = fl(s_g*a_g) + fl(z_g*b_g)
- *   i.e. sm * q~ . dequant(k) for the fixed-point query q~, every group sum exact (with 8-bit codes,
- *   key_bits = 8, the integer group sum exceeds 2^24 and rounds once to float32).
+ *   keys): logit_i = sm_scale * sum_c q_c * (code_ic * s_g + z_g), the query's bf16 values against the
+ *   exactly dequantised keys (fp16 scale s_g and zero z_g per 32-channel group g).  The query is held
+ *   per head and group in fixed point,
+ *     E_g = floor(log2 max_{c in g} |q_c|) (>= -100),  Q_c = rne(q_c * 2^(20 - E_g)),
+ *   which is exact for every channel within 2^12 of its group's largest magnitude (so for ordinary
+ *   bf16 queries q~ = q); the group sums sum_c Q_c*code_c are exact integers, the rest is float64 --
+ *     t_g = s_g*a_g + z_g*b_g,  a_g = 2^(E_g-20) sum Q_c*code_c,  b_g = 2^(E_g-20) sum Q_c,
+ *     logit = float32(sm_scale * ((t_0 + t_1) + (t_2 + t_3)))
+ *   -- so the logit is the exact estimate for the grid query, rounded once to float32.
  * - Weights: softmax of the logits over the unit's candidates only.
  * - Top-p (Paper-Notes "关键设计 / 高效Top-p": binary search of the threshold m with
- *   sum_{W_i >= m} W_i >= p, no sort): `iters` bisection steps on the uint32 image of the
- *   non-negative float32 weights keeping f(lo) >= p > f(hi); the kept set is {W_i >= lo}.  p = 1
- *   keeps every candidate.  With iters >= 31 the set equals the minimal top-p set up to ties and
- *   float32 rounding of the prefix masses; fewer steps return a superset whose mass still reaches p.
- *   Above 65536 candidates per unit (up to 2^22) the same search decides the top 11 key bits from a
- *   mass histogram over all the weights, then the remaining 20 from histograms over the keys inside
- *   the chosen bin, with masses summed in 64-bit fixed point (2^-40 units of the largest weight);
- *   `iters` < 31 then keeps the threshold's top `iters` key bits.
+ *   sum_{W_i >= m} W_i >= p, no sort): the weights are searched on the scale where the largest is 1
+ *   (e_i = exp(l_i - max l), target p * sum e); the threshold is a float32 value whose bit pattern is
+ *   bisected over [0, 2^31), one bit per step from the top, keeping the largest threshold whose kept
+ *   mass still reaches the target; the kept set is {e_i >= m}.  p = 1 keeps every candidate.  With
+ *   iters >= 31 the search has converged: the set is the minimal top-p set up to ties and the
+ *   precision of the weights; fewer steps keep the threshold's top `iters` bits, a superset whose
+ *   mass still reaches p.  Masses are summed in 64-bit fixed point (2^-40 units of the largest
+ *   weight; weights below 2^-40 of it carry no mass).  The search decides 11 bits per pass from mass
+ *   histograms; above 65536 candidates per unit (up to 2^22) the first pass runs over all the weights
+ *   in many blocks and the remaining 20 bits over the keys inside the chosen bin.
  * - Union (paperlayer §B.2): the kept tokens of a unit are the union over its G query heads.
  * Outputs:
  *   threshold  f32 [B][Hq]   the weight threshold m (required)
@@ -196,13 +199,24 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
                            const int32_t* sel_tokens, int32_t max_selected_per_group, float* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* The whole decode step for one layer: twl_select_pages (skipped when keep_frac >= 1), then
+/* The whole decode step for one layer, Twilight's select-then-prune path (Paper-Notes "整体框架";
+ * paperlayer §4.1, Fig. 5: a base selector with a conservative budget, then top-p pruning of its
+ * candidates, then sparse attention): twl_select_pages (skipped when keep_frac >= 1), then
  * twl_estimate_topp over the kept pages, then the sparse attention over the union.  Pages, top-p
  * sets and thresholds are bitwise those of the split calls; the attention reads the top-p bitmaps
  * directly (chunks of the candidate index space), so its outputs agree with twl_sparse_attn on the
- * same kept list to float32 rounding.  threshold, lse, sel_indptr and sel_tokens may be NULL
- * (sel_indptr and sel_tokens together; the kept list is then not compacted at all); capacity is
- * ignored when they are NULL. */
+ * same kept list to float32 rounding.
+ *   q          bf16 [B][Hq][128], 16-byte aligned
+ *   params     p, keep_frac, sm_scale, iters and the baseline switches (see twl_decode_params)
+ *   out        f32 [B][Hq][128] (required); lse f32 [B][Hq] (natural log) or NULL
+ *   threshold  f32 [B][Hq] the weight threshold (W scale) or NULL
+ *   sel_indptr int32 [B*Hkv+1] and sel_tokens int32 [capacity]: the kept tokens' CSR, or both NULL
+ *              (the kept list is then not compacted at all and capacity is ignored);
+ *              capacity >= B*Hkv*(max candidates per unit)
+ *   ws, ws_bytes  workspace of twl_workspace_bytes(cache, max candidates per unit)
+ * Errors: TWL_EINVAL for p outside (0, 1], keep_frac <= 0, a non-finite scale, iters outside 1..64,
+ * a misaligned q, or only one of sel_indptr / sel_tokens; TWL_EWORKSPACE for a small or misaligned
+ * workspace; nothing is enqueued then. */
 twl_status twl_decode(const twl_cache* cache, const void* q, const twl_decode_params* params, float* out,
                       float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
                       void* ws, size_t ws_bytes, void* stream);
@@ -268,8 +282,15 @@ twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_
 /* Static description of a status code. */
 const char* twl_status_str(twl_status status);
 
-/* Library version string. */
+/* Library version string: "twl <version> (gfx950) src <hash>", the hash identifying the kernel and
+ * ABI sources the library was built from. */
 const char* twl_version(void);
+
+/* The base selector's page budget for a sequence of num_pages pages (Paper-Notes "整体框架": a
+ * conservative budget such as 1/4 of the pages): clamp(ceil(fp32(keep_frac) * fp32(num_pages)), 1,
+ * num_pages), 0 when num_pages <= 0; -1 when keep_frac is not finite and > 0.  Host-only, no HIP
+ * call: callers size page lists (max_keep) and candidate capacities with it. */
+int32_t twl_keep_pages(int32_t num_pages, float keep_frac);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,12 @@ arrays (bf16 as uint16 bits) in the logical per-sequence order:
   vseq     uint16 [n][128]
   keep_frac  selector budget as a fraction of pages (>= 1: every page is a candidate)
   ranges   optional (begin, length) candidate ranges (the cluster path) instead of pages
+
+``band`` (optional) states the precision of an implementation the result will be compared with: a
+callable ``band(qbits_h, codes, scale16, zero16, logits) -> (err, tau_p_extra)`` giving, per
+candidate, a bound on that implementation's logit error (which bounds its relative weight error) and
+its mass-sum resolution.  It only widens the ambiguity sets of ``topp.topp_sort``; the sets
+themselves are always those of the float64 definition.
 """
 
 from __future__ import annotations
@@ -22,8 +28,8 @@ from . import attention, doublep, estimate, quantize, select, topp
 
 
 def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, keep_frac: float,
-                sm: float, ranges=None, with_f64_logits: bool = False, bits: int = 4, topk: int = 0,
-                headwise: bool = False) -> dict:
+                sm: float, ranges=None, bits: int = 4, topk: int = 0, headwise: bool = False,
+                band=None) -> dict:
     """``topk`` > 0 replaces each head's top-p set by its top-k set (the fixed-budget baseline);
     ``headwise`` makes each query head attend over its own set instead of the group's union."""
     n = kseq.shape[0]
@@ -49,16 +55,17 @@ def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, 
     qz = quantize.quantize_rows(kseq[cand], bits) if cand.size else None
     heads = []
     for h in range(G):
+        err, extra = None, 0.0
         if cand.size:
-            lg = estimate.logits_spec(q[h], qz["codes"], qz["scale"], qz["zero"], sm)
+            lg = estimate.logits_f64(q[h], qz["codes"], qz["scale"], qz["zero"], sm)
             W = estimate.softmax_f64(lg)
+            if band is not None:
+                err, extra = band(q[h], qz["codes"], qz["scale"], qz["zero"], lg)
         else:
-            lg = np.zeros(0, np.float32)
+            lg = np.zeros(0)
             W = np.zeros(0)
-        res = topp.topk_sort(W, topk) if topk > 0 else topp.topp_sort(W, p)
-        hd = {"logits": lg, "W": W, "topp": res, "tokens": cand[res["sel"]]}
-        if with_f64_logits and cand.size:
-            hd["logits_f64"] = estimate.logits_f64(q[h], qz["codes"], qz["scale"], qz["zero"], sm)
+        res = topp.topk_sort(W, topk, err) if topk > 0 else topp.topp_sort(W, p, err, extra)
+        hd = {"logits": lg, "W": W, "topp": res, "tokens": cand[res["sel"]], "err": err}
         heads.append(hd)
     out["heads"] = heads
     # ---- union and attention -------------------------------------------------------------------
@@ -72,14 +79,18 @@ def decode_unit(q: np.ndarray, kseq: np.ndarray, vseq: np.ndarray, *, p: float, 
     return out
 
 
-def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=False, bits=4, topk=0,
-           headwise=False, approx_unkept=False) -> dict:
+def decode(w, *, p=None, keep_frac=None, sm=None, units=None, bits=4, topk=0, headwise=False,
+           approx_unkept=False, band=None, ranges=None) -> dict:
     """Run the oracle on a workload-like object (fields of ``gen.Workload``).
 
     ``units`` optionally restricts the work to a list of (b, kv-head) pairs; the cluster path is
     taken when the workload carries clusters (``w.csize`` is not None); ``bits`` is the code width
     of the estimator's key copy; ``topk`` / ``headwise`` select the baselines; ``approx_unkept`` adds
-    the unkept clusters' centroid contributions on the cluster path.
+    the unkept clusters' centroid contributions on the cluster path; ``band`` is passed to
+    ``decode_unit``.  On the cluster path ``ranges`` may map (b, h) to given kept ranges (int
+    [m][2] of (first token, length)): the token stage then runs on those instead of the oracle's own
+    cluster selection (which is still computed and returned), so a second implementation's token
+    stage can be checked on its own cluster choice.
     Returns ``{(b, h): decode_unit result}``.
     """
     p = w.p if p is None else p
@@ -97,22 +108,25 @@ def decode(w, *, p=None, keep_frac=None, sm=None, units=None, with_f64_logits=Fa
             logical_v[b] = w.logical("v", b)
         q = w.q[b, h * G:(h + 1) * G]
         kseq, vseq = logical_k[b][:, h, :], logical_v[b][:, h, :]
-        ranges = None
         if getattr(w, "csize", None) is not None:
             cs = doublep.select_clusters(q, w.centroids[b, h], w.csize[b, h], w.p1, sm)
-            ranges = doublep.ranges_of(cs["kept"], w.coff[b, h])
-            r = decode_unit(q, kseq, vseq, p=p, keep_frac=1.0, sm=sm, ranges=ranges,
-                            with_f64_logits=with_f64_logits, bits=bits)
+            own = doublep.ranges_of(cs["kept"], w.coff[b, h])
+            rg = own if ranges is None or (b, h) not in ranges else np.asarray(ranges[(b, h)], np.int64)
+            r = decode_unit(q, kseq, vseq, p=p, keep_frac=1.0, sm=sm, ranges=rg, bits=bits, band=band)
             r["clusters"] = cs
-            r["ranges"] = ranges
+            r["ranges"] = rg
+            r["own_ranges"] = own
             if approx_unkept:
+                # the clusters the token stage ran on (the given ranges, when there are any)
+                first = {int(w.coff[b, h][c]): c for c in range(len(w.csize[b, h])) if w.csize[b, h][c] > 0}
+                kept = np.array(sorted(first[int(x)] for x in rg[:, 0]), np.int64) if len(rg) else np.zeros(0, np.int64)
                 vm = doublep.value_means(vseq, w.csize[b, h], w.coff[b, h])
                 for j in range(G):
                     lam = cs["per_head"][j]["lam"]
                     r["out"][j], r["lse"][j] = doublep.approx_unkept(r["out"][j], r["lse"][j], lam, w.csize[b, h],
-                                                                     cs["kept"], vm)
+                                                                     kept, vm)
         else:
-            r = decode_unit(q, kseq, vseq, p=p, keep_frac=keep_frac, sm=sm,
-                            with_f64_logits=with_f64_logits, bits=bits, topk=topk, headwise=headwise)
+            r = decode_unit(q, kseq, vseq, p=p, keep_frac=keep_frac, sm=sm, bits=bits, topk=topk,
+                            headwise=headwise, band=band)
         res[(b, h)] = r
     return res

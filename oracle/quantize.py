@@ -10,7 +10,9 @@ The pages leave the granularity, the rounding and the nibble order open; the rea
 * code_c = 0 when s == 0, else clamp(rint_even( fp32(x_c - z) / s ), 0, 15), with the fp16 s and z
   widened to fp32 and every operation a correctly rounded fp32 operation;
 * byte j of a row holds code_{2j} in its low nibble and code_{2j+1} in its high nibble;
-* dequantised value  x^_c = code_c * s + z  in fp32 (the product is exact, so fused or not agrees).
+* dequantised value  x^_c = code_c * s + z, exact (float64 holds it: an 8-bit code times an 11-bit
+  scale plus an 11-bit zero spans fewer than 53 bits over the whole fp16 range).  The pages dequantise
+  to FP16 on chip; the estimate's definition (``estimate.logits_f64``) takes the exact value.
 
 This is an encoding, so its float32 operation sequence is the specification; numpy float32
 arithmetic performs each operation with IEEE rounding, one at a time.
@@ -92,11 +94,11 @@ def unpack_codes(packed: np.ndarray, bits: int = 4) -> np.ndarray:
 
 
 def dequantize(codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray) -> np.ndarray:
-    """x^ = code * s + z in fp32; codes [..., 128], scale/zero [..., 4]."""
-    c = np.asarray(codes, dtype=F32).reshape(codes.shape[:-1] + (NGROUPS, GROUP))
-    s = np.asarray(scale16, dtype=np.float16).astype(F32)[..., None]
-    z = np.asarray(zero16, dtype=np.float16).astype(F32)[..., None]
-    return ((c * s).astype(F32) + z).astype(F32).reshape(codes.shape)
+    """x^ = code * s + z, exact in float64; codes [..., 128], scale/zero [..., 4]."""
+    c = np.asarray(codes, dtype=np.float64).reshape(codes.shape[:-1] + (NGROUPS, GROUP))
+    s = np.asarray(scale16, dtype=np.float16).astype(np.float64)[..., None]
+    z = np.asarray(zero16, dtype=np.float16).astype(np.float64)[..., None]
+    return (c * s + z).reshape(codes.shape)
 
 
 def page_bounds(kbits_seq: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

@@ -1,5 +1,10 @@
 """Helpers for the GPU parity tests: upload a workload, build the INT4 shadow with the library, and
-run the oracle on the same seeded inputs.  The oracle only ever receives generator outputs."""
+run the oracle on the same seeded inputs.  The oracle only ever receives generator outputs.
+
+The oracle's top-p sets are those of the float64 definition of the estimate; ``oracle_decode``
+passes it the estimate kernel's stated precision (``tests/kernel_model.py``), which only widens the
+ambiguity sets by that precision, per token.  ``SetStats`` counts, per test, how many tokens each
+clause of the parity rule excused."""
 
 from __future__ import annotations
 
@@ -10,8 +15,35 @@ import torch
 
 import top_sparse_attention_int4_amd as twl
 from gen.device import upload
+from oracle import pipeline, topp
+from tests import kernel_model
 
 SM = twl.DEFAULT_SM_SCALE
+
+
+def oracle_decode(w, **kw):
+    """The oracle's decode with the ambiguity band of the estimate kernel's stated precision."""
+    return pipeline.decode(w, band=kernel_model.band, **kw)
+
+
+class SetStats:
+    """Per-test tally of compared heads and of the tokens each parity clause excused."""
+
+    def __init__(self, name):
+        self.name = name
+        self.c = {"heads": 0, "diff": 0, "base": 0, "band": 0, "cut": 0}
+
+    def add(self, gpu_sel, res):
+        d = topp.diff_counts(gpu_sel, res)
+        self.c["heads"] += 1
+        for k in ("diff", "base", "band", "cut"):
+            self.c[k] += d[k]
+
+    def report(self):
+        c = self.c
+        print(f"[sets] {self.name}: {c['heads']} heads, {c['diff']} tokens differ -- excused by the 1e-6 band "
+              f"{c['base']}, by the kernel's stated logit error {c['band']}, by the prefix-mass clause {c['cut']}",
+              flush=True)
 
 
 def device_cache(w, device="cuda", key_bits=4):
@@ -57,14 +89,27 @@ def unit_tokens(res, u):
     return res["tokens"][a:b]
 
 
-def check_union(gpu_tokens, r, p):
-    """GPU union vs oracle union: differences only in tokens some head finds ambiguous, and each
-    head's kept set (restricted to its candidates) must still reach p - tau under oracle weights."""
+FLOOR = 2.0**-40  # the kernel's mass floor: weights below it (relative to the largest) carry no mass
+
+
+def floor_tokens(W):
+    """Candidates whose weight lies below the kernel's fixed-point floor (with a margin for the
+    kernel's rounding).  The top-k baseline kernel counts only weights at or above 2^-40 of the
+    largest and keeps every candidate when the budget exceeds their number -- a documented deviation
+    from the plain k-largest definition, so these tokens are undecided for top-k."""
+    W = np.asarray(W, np.float64)
+    return np.nonzero(W < FLOOR * W.max() * (1 + 1e-5))[0] if W.size else np.zeros(0, np.int64)
+
+
+def check_union(gpu_tokens, r, p, topk=False):
+    """GPU union vs oracle union: differences only in tokens some head finds ambiguous."""
     cand = r["candidates"]
     amb = set()
     for hd in r["heads"]:
         res = hd["topp"]
         amb |= set(cand[np.union1d(res["amb_i"], res["amb_ii"]).astype(np.int64)].tolist())
+        if topk:
+            amb |= set(cand[floor_tokens(hd["W"])].tolist())
     g = set(np.asarray(gpu_tokens).tolist())
     o = set(r["union"].tolist())
     bad = (g ^ o) - amb
@@ -88,3 +133,10 @@ def attn_tolerance(qg, kseq, vseq, oracle_union, gpu_tokens):
         a = dense_weights(qg[h], kseq[both], SM)
         extra = max(extra, 2 * float(a[pos].sum()) * vmax)
     return 2e-3 + extra
+
+
+def check_bisect(gpu_sel, hd, p, iters):
+    """A stopped-early GPU set against the oracle's bisection model at the same step count, with the
+    same precision band as the sorted-set comparison."""
+    b = topp.topp_bisect(hd["W"], p, iters, tau=hd["topp"]["tau_p"], err=hd["err"])
+    return topp.bisect_matches(gpu_sel, b, hd["W"])

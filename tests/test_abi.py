@@ -22,14 +22,14 @@ def twl():
 
 def _declared():
     src = open(os.path.join(ROOT, "include", "twl.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:twl_status|size_t|const char\*)\s+(twl_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:twl_status|size_t|const char\*|int32_t)\s+(twl_\w+)\s*\(", src, re.M)))
 
 
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ["twl_quantize_k", "twl_select_pages", "twl_estimate_topp", "twl_sparse_attn", "twl_decode",
               "twl_decode_profiled", "twl_select_clusters_topp", "twl_decode_clusters", "twl_workspace_bytes",
-              "twl_status_str"]:
+              "twl_status_str", "twl_version", "twl_keep_pages"]:
         assert n in names
 
 
@@ -51,6 +51,23 @@ def test_status_strings(twl):
     for s in range(5):
         assert twl.status_str(s).startswith("TWL_")
     assert "gfx950" in twl.version()
+
+
+def test_version_names_the_source_hash(twl):
+    # the loaded library was built from this tree's kernel and ABI sources (the binding refuses others)
+    from top_sparse_attention_int4_amd.build import source_hash
+    assert twl.version().endswith(" src " + source_hash())
+
+
+def test_keep_pages_rule(twl):
+    # clamp(ceil(fp32(keep) * fp32(P)), 1, P): the budget of the base selector, computed in the library
+    import numpy as np
+    for P, kf in [(2048, 0.25), (8192, 0.25), (7, 0.3), (1, 0.01), (5, 1.0), (5, 3.0), (3, 1e-9)]:
+        want = max(1, min(P, int(np.ceil(min(np.float32(kf) * np.float32(P), np.float32(P))))))
+        assert twl.keep_count(P, kf) == want, (P, kf)
+    assert twl.keep_count(0, 0.25) == 0
+    assert twl.lib().twl_keep_pages(10, float("nan")) == -1
+    assert twl.lib().twl_keep_pages(10, 0.0) == -1
 
 
 def test_workspace_bytes(twl):

@@ -3,7 +3,9 @@
 Bars as for the token path: the kept clusters of a unit must contain every cluster some head keeps
 unambiguously and only clusters some head keeps or finds ambiguous (oracle.topp rule on the size-
 weighted cluster weights); ranges are the kept clusters' exact (first token, length) in ascending
-order.  Token sets, union and attention as in test_gpu_parity.
+order.  The token stage (sets, union, attention) is then checked as in test_gpu_parity, with the
+oracle run on the GPU's own kept ranges, so a unit whose kept clusters differ in ambiguous ones is
+still compared.
 """
 
 import math
@@ -14,9 +16,10 @@ import torch
 
 import top_sparse_attention_int4_amd as twl
 from gen import make_config, make_custom
-from oracle import doublep, pipeline
+from oracle import doublep
 from oracle.topp import set_matches
-from tests.gpu_helpers import SM, attn_tolerance, check_union, device_cache, unit_tokens, workspace
+from tests.gpu_helpers import (SM, SetStats, attn_tolerance, check_bisect, check_union, device_cache, oracle_decode,
+                               unit_tokens, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,17 +120,25 @@ def _decode_clusters(w, cache, t, p=None, iters=32, events=None, lists=True):
             "indptr": indptr.cpu().numpy(), "tokens": toks.cpu().numpy()}
 
 
-def _check_token_stage(w, g, res, ranges, count):
-    """Token-level union and attention of every oracle unit whose kept clusters equal the GPU's."""
+def _gpu_ranges(ranges, count, u):
+    return np.asarray(ranges[u, :int(count[u])], np.int64).reshape(-1, 2)
+
+
+def _oracle_on_gpu_ranges(w, ranges, count, units, **kw):
+    """The oracle's decode of ``units`` with its token stage on the GPU's kept ranges (after checking
+    the GPU's kept clusters against the oracle's cluster top-p)."""
+    given = {}
+    for b, h in units:
+        _check_clusters(w, ranges, count, w.p1, b, h)
+        given[(b, h)] = _gpu_ranges(ranges, count, b * w.num_kv_heads + h)
+    return oracle_decode(w, units=units, ranges=given, **kw)
+
+
+def _check_token_stage(w, g, res):
+    """Token-level union and attention of every unit in ``res``."""
     G = w.group
-    checked = 0
     for (b, h), r in res.items():
         u = b * w.num_kv_heads + h
-        got, want = _check_clusters(w, ranges, count, w.p1, b, h)
-        if got != want:
-            print(f"[note] unit {(b, h)}: kept clusters differ in ambiguous ones; token stage not compared")
-            continue
-        checked += 1
         gt = unit_tokens(g, u)
         bad, diff = check_union(gt, r, w.p)
         assert not bad, (b, h, sorted(bad)[:8])
@@ -140,7 +151,10 @@ def _check_token_stage(w, g, res, ranges, count):
                 continue
             err = np.max(np.abs(g["out"][b, h * G + j] - r["out"][j]))
             assert err <= tol, (b, h * G + j, err, tol, len(diff))
-    assert checked > 0
+
+
+def _all_units(w):
+    return [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
 
 
 @pytest.mark.parametrize("cfg", CLUSTER, ids=CLUSTER_IDS)
@@ -150,7 +164,7 @@ def test_decode_clusters_end_to_end(cfg):
     cache, t = device_cache(w)
     g = _decode_clusters(w, cache, t)
     ranges, count = _cluster_gpu(w, cache, t, w.p1)
-    _check_token_stage(w, g, pipeline.decode(w), ranges, count)
+    _check_token_stage(w, g, _oracle_on_gpu_ranges(w, ranges, count, _all_units(w)))
 
 
 @pytest.mark.parametrize("cfg", CLUSTER[:3], ids=CLUSTER_IDS[:3])
@@ -187,16 +201,11 @@ def test_decode_clusters_approx_unkept(cfg):
                               out=out, lse=lse, ws=ws)
     torch.cuda.synchronize()
     go, gl = out.cpu().numpy(), lse.cpu().numpy()
-    res = pipeline.decode(w, approx_unkept=True)
     ranges, count = _cluster_gpu(w, cache, t, w.p1)
+    res = _oracle_on_gpu_ranges(w, ranges, count, _all_units(w), approx_unkept=True)
     G = w.group
-    checked = 0
     for (b, h), r in res.items():
         u = b * w.num_kv_heads + h
-        got, want = _check_clusters(w, ranges, count, w.p1, b, h)
-        if got != want:
-            continue
-        checked += 1
         gt = unit_tokens(g, u)
         k, v = w.logical("k", b)[:, h], w.logical("v", b)[:, h]
         tol = attn_tolerance(w.q[b, h * G:(h + 1) * G], k, v, r["union"], gt) if len(r["union"]) else 2e-3
@@ -205,9 +214,8 @@ def test_decode_clusters_approx_unkept(cfg):
                 continue
             assert np.max(np.abs(go[b, h * G + j] - r["out"][j])) <= tol, (b, h * G + j)
             assert abs(gl[b, h * G + j] - r["lse"][j]) <= 1e-3, (b, h * G + j)
-        if len(want) == int((w.csize[b, h] > 0).sum()):  # every cluster kept: the outputs are unchanged
+        if int(count[u]) == int((w.csize[b, h] > 0).sum()):  # every cluster kept: the outputs are unchanged
             assert np.array_equal(go[b, h * G:(h + 1) * G], g["out"][b, h * G:(h + 1) * G])
-    assert checked > 0
 
 
 def test_decode_clusters_fused_equals_split():
@@ -272,27 +280,37 @@ def _mask_indices(words, ncand):
 def wide_case():
     w = make_custom(**WIDE)
     cache, t = device_cache(w)
-    return w, cache, t, pipeline.decode(w)
+    return w, cache, t, oracle_decode(w)
+
+
+def _check_wide_sets(w, g, res, st, units=None):
+    G = w.group
+    for (b, h), r in res.items():
+        if units is not None and (b, h) not in units:
+            continue
+        u = b * w.num_kv_heads + h
+        ncand = len(r["candidates"])
+        for j, hd in enumerate(r["heads"]):
+            hq = h * G + j
+            sel = _mask_indices(g["mask"][b, hq], ncand)
+            ok, msg = set_matches(sel, hd["topp"], hd["W"], w.p)
+            assert ok, (b, hq, msg)
+            st.add(sel, hd["topp"])
+            assert abs(g["mass"][b, hq] - math.fsum(hd["W"][sel])) < 1e-5
+        bad, _ = check_union(unit_tokens(g, u), r, w.p)
+        assert not bad, (b, h, sorted(bad)[:8])
+        assert np.all(np.diff(unit_tokens(g, u)) > 0)
 
 
 def test_wide_topp_parity(wide_case):
     w, cache, t, res = wide_case
     _print_case(w.name + " wide top-p")
     g = _estimate_all(w, cache, t, w.p)
-    G = w.group
     for (b, h), r in res.items():
-        u = b * w.num_kv_heads + h
-        ncand = len(r["candidates"])
-        assert ncand > 65536 or b == 1
-        for j, hd in enumerate(r["heads"]):
-            hq = h * G + j
-            sel = _mask_indices(g["mask"][b, hq], ncand)
-            ok, msg = set_matches(sel, hd["topp"], hd["W"], w.p)
-            assert ok, (b, hq, msg)
-            assert abs(g["mass"][b, hq] - math.fsum(hd["W"][sel])) < 1e-5
-        bad, _ = check_union(unit_tokens(g, u), r, w.p)
-        assert not bad, (b, h, sorted(bad)[:8])
-        assert np.all(np.diff(unit_tokens(g, u)) > 0)
+        assert len(r["candidates"]) > 65536 or b == 1
+    st = SetStats(w.name + " wide")
+    _check_wide_sets(w, g, res, st)
+    st.report()
 
 
 def test_wide_topp_p_one_and_few_iterations(wide_case):
@@ -304,16 +322,19 @@ def test_wide_topp_p_one_and_few_iterations(wide_case):
         n = int(w.seq_lens[b])
         for hq in range(w.num_q_heads):
             assert len(_mask_indices(g1["mask"][b, hq], n)) == n
-    for it in (4, 11, 20):
+    for it in (4, 11, 20, 27):
         few = _estimate_all(w, cache, t, 0.9, iters=it)
         for (b, h), r in res.items():
             n = len(r["candidates"])
             for j in range(w.group):
                 hq = h * w.group + j
-                s_few = set(_mask_indices(few["mask"][b, hq], n).tolist())
-                s_full = set(_mask_indices(full["mask"][b, hq], n).tolist())
-                assert s_full <= s_few
-                assert math.fsum(r["heads"][j]["W"][sorted(s_few)]) >= 0.9 - 1e-5
+                s_few = _mask_indices(few["mask"][b, hq], n)
+                s_full = _mask_indices(full["mask"][b, hq], n)
+                assert set(s_full.tolist()) <= set(s_few.tolist())
+                hd = r["heads"][j]
+                ok, msg = check_bisect(s_few, hd, 0.9, it)
+                assert ok, (it, b, hq, msg)
+                assert math.fsum(hd["W"][s_few]) >= 0.9 - hd["topp"]["tau_p"]
 
 
 def test_wide_decode_end_to_end(wide_case):
@@ -355,8 +376,28 @@ def test_c5_full_size_sampled_units():
     for b in range(w.batch):
         for h in range(w.num_kv_heads):
             _check_clusters(w, ranges, count, w.p1, b, h)
-    res = pipeline.decode(w, units=[(0, 2), (0, 5)])
-    _check_token_stage(w, g, res, ranges, count)
+    units = [(0, 0), (0, 2), (0, 5), (0, 7)]
+    res = _oracle_on_gpu_ranges(w, ranges, count, units)
+    _check_token_stage(w, g, res)
+    # per-head token sets on the GPU's kept ranges (the multi-block top-p: ~250K candidates per head)
+    U, C = w.batch * w.num_kv_heads, w.num_clusters
+    maxcand = w.max_seq_len
+    mw = (maxcand + 31) // 32
+    thr = torch.empty((w.batch, w.num_q_heads), device="cuda")
+    mass = torch.empty((w.batch, w.num_q_heads), device="cuda")
+    hm = torch.zeros((w.batch, w.num_q_heads, mw), dtype=torch.int32, device="cuda")
+    indptr = torch.empty((U + 1,), dtype=torch.int32, device="cuda")
+    toks = torch.empty((U * maxcand,), dtype=torch.int32, device="cuda")
+    ws = workspace(cache, maxcand)
+    twl.estimate_topp(cache, t["q"], SM, w.p, 32, ranges=torch.from_numpy(ranges).cuda(),
+                      count=torch.from_numpy(count).cuda(), max_items=C, threshold=thr, mass=mass, head_mask=hm,
+                      mask_words=mw, sel_indptr=indptr, sel_tokens=toks, ws=ws)
+    torch.cuda.synchronize()
+    e = {"mask": hm.cpu().numpy().view(np.uint32), "mass": mass.cpu().numpy(), "indptr": indptr.cpu().numpy(),
+         "tokens": toks.cpu().numpy()}
+    st = SetStats(w.name)
+    _check_wide_sets(w, e, res, st)
+    st.report()
     assert np.all(np.isfinite(g["out"]))
     # the timed form (no token list requested) is bitwise the same
     g2 = _decode_clusters(w, cache, t, lists=False)

@@ -5,8 +5,12 @@
 * Closed forms from tests/golden/topp_closed_form.json (geometric and uniform weights, explicit
   small vectors), one-hot weights, p = 1.
 * Invariants: monotone in p, permutation invariant.
-* The bisection on the uint32 image of float32 weights returns exactly the sort-based set (up to
-  ties) once converged, and a superset that still reaches p when stopped early.
+* The bisection on the uint32 image of the float32 threshold returns exactly the sort-based set (up
+  to ties) once converged, a superset that still reaches p when stopped early, and after s steps the
+  converged bit pattern with its low 31 - s bits cleared.
+* Top-k is the k largest weights with ties at the k-th kept (rank characterisation by brute force).
+* The band of an implementation's stated precision widens clause (i) by the two tokens' errors and
+  the cut clause by twice their weighted mean.
 """
 
 import itertools
@@ -116,7 +120,7 @@ def test_bisection_equals_sort_based_set(seed):
     r = topp.topp_sort(W, p)
     # the search returns every token at or above the exact threshold weight w_(k*)
     thr = np.float32(w[r["order"][r["k"] - 1]])
-    assert b["threshold"] == thr
+    assert b["threshold"] == thr and b["key"] == int(np.float32(thr).view(np.uint32))
     ok, msg = topp.set_matches(b["sel"], r, W, p)
     assert ok, msg
 
@@ -160,8 +164,63 @@ def test_topk_equals_rank_characterisation(seed):
         assert topp.topk_sort(W, k)["sel"].tolist() == want, (seed, k)
 
 
-def test_topk_budget_reaching_the_floor_keeps_everything():
+def test_topk_is_the_k_largest_even_among_tiny_weights():
     W = np.array([1.0, 0.5, 2.0**-45, 2.0**-50])
     W = W / W.sum()
     assert topp.topk_sort(W, 2)["sel"].tolist() == [0, 1]
-    assert topp.topk_sort(W, 3)["sel"].tolist() == [0, 1, 2, 3]  # only two weights above the floor
+    assert topp.topk_sort(W, 3)["sel"].tolist() == [0, 1, 2]
+    assert topp.topk_sort(W, 4)["sel"].tolist() == [0, 1, 2, 3]
+    assert topp.topk_sort(W, 9)["sel"].tolist() == [0, 1, 2, 3]
+
+
+# ---- the band of an implementation's stated precision ---------------------------------------------
+def test_error_band_widens_only_clause_i_around_the_cut():
+    W = np.array([0.5, 0.2, 0.2 * (1 - 3e-6), 0.1 - 0.2 * (1 - 3e-6) + 0.2])
+    W = W / W.sum()
+    p = W[0] + 0.5 * W[1]                   # the canonical set is {0, 1}, far from any prefix cut
+    r0 = topp.topp_sort(W, p)
+    assert r0["sel"].tolist() == [0, 1] and 2 not in r0["amb_i"].tolist()
+    r1 = topp.topp_sort(W, p, err=np.full(4, 2e-6))   # 3e-6 apart < 1e-6 + 2e-6 + 2e-6
+    assert 2 in r1["amb_i"].tolist() and 2 not in r1["amb_i_base"].tolist()
+    ok, msg = topp.set_matches(np.array([0, 2]), r1, W, p)
+    assert ok, msg
+    c = topp.diff_counts(np.array([0, 2]), r1)
+    assert (c["base"], c["band"], c["bad"]) == (1, 1, 0)   # token 1 is the threshold token itself
+    assert not topp.set_matches(np.array([0, 2]), r0, W, p)[0]
+
+
+def test_cut_clause_tolerance_follows_the_weighted_error():
+    rng = np.random.default_rng(2)
+    W = rng.dirichlet(np.ones(200))
+    r = topp.topp_sort(W, 0.8, err=np.full(200, 1e-7), tau_p_extra=3e-9)
+    assert math.isclose(r["tau_p"], topp.TAU_P + 2e-7 + 3e-9, rel_tol=1e-9)
+    # an error carried only by tokens of no weight does not widen the cut
+    e = np.where(W < np.sort(W)[5], 1.0, 0.0)
+    r2 = topp.topp_sort(W, 0.8, err=e)
+    assert r2["tau_p"] <= topp.TAU_P + 2 * 6 * W.max()
+
+
+def test_bisection_stopped_early_keeps_the_top_bits_of_the_threshold():
+    # one key bit per step from the top: after s steps the bit pattern is the converged one with its
+    # low 31 - s bits cleared (no step decided within rounding here)
+    rng = np.random.default_rng(21)
+    for trial in range(6):
+        W = np.exp(rng.standard_normal(3000) * rng.choice([0.3, 2.0, 6.0]))
+        full = topp.topp_bisect(W, 0.9, iters=31)
+        assert full["converged"]
+        for s in (1, 3, 8, 13, 20, 30):
+            b = topp.topp_bisect(W, 0.9, iters=s, tau=1e-6)
+            if len(b["keys"]) == 1:
+                assert b["key"] == full["key"] & ~((1 << (31 - s)) - 1), (trial, s)
+
+
+def test_bisection_alternatives_when_a_step_is_within_tolerance():
+    # weights chosen so that the mass of the first probe above the largest key bit equals the target
+    W = np.array([1.0, 1.0, 1.0, 1.0])
+    b = topp.topp_bisect(W, 0.5, iters=31, tau=0.0)
+    assert b["sel"].tolist() == [0, 1, 2, 3]    # ties: all four weights equal the threshold
+    b = topp.topp_bisect(W, 1.0, iters=31)
+    assert b["sel"].tolist() == [0, 1, 2, 3]
+    W = np.array([0.6, 0.4])
+    b = topp.topp_bisect(W, 0.6, iters=31, tau=1e-3)
+    assert len(b["keys"]) >= 1 and b["keys"][0] == b["key"]

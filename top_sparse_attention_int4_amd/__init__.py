@@ -67,7 +67,8 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load libtwl.so (built in-tree by ``build.py``); raise if it is missing."""
+    """Load libtwl.so (built in-tree by ``build.py``); raise if it is missing or was built from other
+    sources than the ones in this tree (its version string carries their hash)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -75,6 +76,14 @@ def lib() -> ctypes.CDLL:
         raise ImportError(f"libtwl.so not found at {LIB_PATH}; build it with "
                           "`python -m top_sparse_attention_int4_amd.build` (no CPU fallback exists)")
     L = ctypes.CDLL(LIB_PATH)
+    from .build import source_hash
+    L.twl_version.restype = ctypes.c_char_p
+    L.twl_version.argtypes = []
+    ver = L.twl_version().decode()
+    want = source_hash()
+    if not ver.endswith(" src " + want):
+        raise ImportError(f"{LIB_PATH} ({ver}) was not built from the sources in this tree (src {want}); "
+                          "rebuild it with `python -m top_sparse_attention_int4_amd.build`")
     C = ctypes.POINTER(CacheC)
     sig = {
         "twl_workspace_bytes": (ctypes.c_size_t, [C, _i64]),
@@ -95,6 +104,7 @@ def lib() -> ctypes.CDLL:
                                              _p]),
         "twl_status_str": (ctypes.c_char_p, [_i32]),
         "twl_version": (ctypes.c_char_p, []),
+        "twl_keep_pages": (_i32, [_i32, _f32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -151,12 +161,11 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def keep_count(num_pages: int, keep_frac: float) -> int:
-    """Pages kept for a sequence of ``num_pages`` pages (the same float32 rule as the kernels)."""
-    if num_pages <= 0:
-        return 0
-    prod = float(torch.tensor(keep_frac, dtype=torch.float32) * torch.tensor(float(num_pages), dtype=torch.float32))
-    k = math.ceil(min(prod, float(num_pages)))
-    return max(1, min(num_pages, k))
+    """Pages the base selector keeps for a sequence of ``num_pages`` pages (``twl_keep_pages``)."""
+    k = int(lib().twl_keep_pages(int(num_pages), float(keep_frac)))
+    if k < 0:
+        raise TwlError(TWL_EINVAL, "keep_frac must be finite and > 0")
+    return k
 
 
 class PagedCache:

@@ -12,6 +12,7 @@ instructions are disabled.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import os
 import subprocess
 import sys
@@ -33,6 +34,18 @@ FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """sha256 (first 16 hex digits) of every file under csrc/ and of include/twl.h, the sources the
+    library is built from; embedded in the library's version string and checked when it is loaded."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))] + [os.path.join(INCLUDE, "twl.h")]
+    for f in files:
+        if os.path.isfile(f):
+            with open(f, "rb") as fh:
+                h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -45,19 +58,39 @@ def sources() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel, under _build/), then link libtwl.so."""
     os.makedirs(LIBDIR, exist_ok=True)
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    define = f'-DTWL_SOURCE_HASH="{source_hash()}"'
+    procs = []
+    objs = []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmd = [hipcc(), *FLAGS, define, "-c", "-I", INCLUDE, "-I", CSRC, src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    failed = False
+    for src, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out + err)
+            failed = True
+        elif verbose:
+            noise = [ln for ln in err.splitlines()
+                     if ln.strip() and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
+            if noise:
+                sys.stderr.write("\n".join(noise) + "\n")
+    if failed:
+        raise RuntimeError("hipcc failed building libtwl.so")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    res = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
+                         capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libtwl.so")
-    noise = [ln for ln in res.stderr.splitlines()
-             if ln.strip() and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
-    if verbose and noise:
-        sys.stderr.write("\n".join(noise) + "\n")
+        raise RuntimeError("hipcc failed linking libtwl.so")
     os.replace(tmp, LIB)
     return LIB
 

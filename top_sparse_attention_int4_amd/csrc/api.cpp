@@ -609,6 +609,14 @@ const char* twl_status_str(twl_status status) {
   return "unknown twl_status";
 }
 
-const char* twl_version(void) { return "twl 0.1.0 (gfx950)"; }
+#ifndef TWL_SOURCE_HASH
+#define TWL_SOURCE_HASH "unknown"
+#endif
+const char* twl_version(void) { return "twl 0.2.0 (gfx950) src " TWL_SOURCE_HASH; }
+
+int32_t twl_keep_pages(int32_t num_pages, float keep_frac) {
+  if (!finite(keep_frac) || !(keep_frac > 0.f)) return -1;
+  return keep_count(num_pages, keep_frac);
+}
 
 }  // extern "C"

@@ -1,23 +1,25 @@
 // INT4 weight estimate: the mixed-precision SpGEMV of the query against the dequantised 4-bit keys
 // (paperlayer §4.2; §B.1, Fig. 12) as an int8 matrix-core contraction.
 //
-// Per head and 32-channel group g the query is held in fixed point, Q_c = rne(q_c 2^(13 - E_g)) with
-// E_g = floor(log2 max |q_c|) (|Q_c| <= 16320; exact for channels within 2^6 of the largest), so
-//   sum_{c in g} q~_c (code_c s_g + z_g) = s_g a_g + z_g b_g,  a_g = 2^(E_g-13) sum Q_c code_c,
-//   b_g = 2^(E_g-13) sum Q_c
-// has exact group sums (|sum| < 2^23) in any order; then
-//   t_g = fl(s_g a_g) + fl(z_g b_g),  logit = fl(sm * ((t_0 + t_1) + (t_2 + t_3))).
-// The file is compiled without floating-point contraction so that t_g rounds each product.
+// Per head and 32-channel group g the query is held in fixed point, Q_c = rne(q_c 2^(20 - E_g)) with
+// E_g = floor(log2 max |q_c|) (|Q_c| <= 2088960; exact for channels within 2^12 of the largest, i.e.
+// for every channel of an ordinary bf16 query), as three int8 digits Q = 2^14 d2 + 2^7 d1 + d0, so
+//   sum_{c in g} q~_c (code_c s_g + z_g) = s_g a_g + z_g b_g,  a_g = 2^(E_g-20) sum Q_c code_c,
+//   b_g = 2^(E_g-20) sum Q_c
+// has exact integer group sums in any order; then, in float64,
+//   t_g = s_g a_g + z_g b_g (both products exact, one rounding),  r = (t_0 + t_1) + (t_2 + t_3),
+//   logit = float32(sm * r)
+// -- the float64 definition of the estimate for the grid query q~, rounded once to float32.
 //
 // The sums are v_mfma_i32_16x16x32_i8 products: A = 16 candidates x 32 codes (lane (r, kb) reads the
 // code run of group kb of candidate r with one load -- 16 bytes of 4-bit codes; 8 or 32 bytes for the
 // 2- and 8-bit widths of the precision ablation, paperlayer §4.2, Fig. 6 -- and feeds 8 codes as bytes
 // to each of four MFMAs; 8-bit codes go in as code - 128 with the columns started at 128 x the digit
-// sums, and their group sums, up to 2^28, round once to float32), B = the query digits (Q = 128 hi + lo, both int8), one column per (group, head) and
-// zero outside the lane's group, so each output column accumulates one group of one head.  A wave
-// takes 16-candidate tiles; the four groups of a (candidate, head) then meet by two lane exchanges
-// in the committed order.  The block also records, per candidate, its token id and K/V row index,
-// which the union of the kept sets then gathers without further lookups.
+// sums), B = the query digits, one column per (group, head) and zero outside the lane's group, so
+// each output column accumulates one group of one head.  A wave takes 16-candidate tiles; the four
+// groups of a (candidate, head) then meet by two lane exchanges in the committed order.  The block
+// also records, per candidate, its token id and K/V row index, which the union of the kept sets then
+// gathers without further lookups.
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -148,6 +150,9 @@ __device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView&
 }
 
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kQDigits = 3;     // int8 digits of the fixed-point query
+constexpr int kQFracBits = 20;  // Q = rne(q 2^(kQFracBits - E_g))
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -209,12 +214,12 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   __shared__ int s_row[NB][64];
-  // query digits (Q = 128 [0] + [1]), channel 8j + w of a group at byte 8j + perm(w), the order in
-  // which the nibbles of 4 code bytes are unpacked (low nibbles of bytes 0..3, then high nibbles)
-  __shared__ __align__(16) int8_t s_qd[2][G][kD];
+  // query digits (Q = 2^14 [0] + 2^7 [1] + [2]), channel 8j + w of a group at byte 8j + perm(w), the
+  // order in which the nibbles of 4 code bytes are unpacked (low nibbles of bytes 0..3, then high)
+  __shared__ __align__(16) int8_t s_qd[kQDigits][G][kD];
   __shared__ int s_qe[G][kGroups];   // group exponents E_g
-  __shared__ float s_qb[G][kGroups]; // b_g
-  __shared__ int s_qds[2][G][kGroups];  // per digit, its sum over the group (8-bit codes: the offset of 128)
+  __shared__ int s_qs[G][kGroups];   // sum_{c in g} Q_c (|.| < 2^26)
+  __shared__ int s_qds[kQDigits][G][kGroups];  // per digit, its sum over the group (8-bit codes: the offset of 128)
   __shared__ float s_max[4][G];
   if (wstate) {
     // clear the wide top-p state for the passes that follow this kernel
@@ -317,33 +322,39 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
     for (int cc = 0; cc < 32; ++cc) m = fmaxf(m, fabsf(x[cc]));
     int E = 0;
     if (m > 0.f) E = max((int)(__float_as_uint(m) >> 23) - 127, -100);
-    int qs = 0, d0s = 0, d1s = 0;
-    uint32_t dw[2][8];  // the two digits' bytes, 4 per word, in the unpack order of the codes
+    int qs = 0, ds[kQDigits] = {0, 0, 0};
+    uint32_t dw[kQDigits][8];  // the digits' bytes, 4 per word, in the unpack order of the codes
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dw[0][k] = dw[1][k] = 0u;
+    for (int d = 0; d < kQDigits; ++d)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) dw[d][k] = 0u;
 #pragma unroll
     for (int cc = 0; cc < 32; ++cc) {
-      const int Qv = (int)rintf(ldexpf(x[cc], 13 - E));
-      const int hi = Qv >> 7, lo = Qv & 127;  // floor(Q / 128) in [-128, 127], and Q - 128 hi
+      // |x| < 2^(E+1), so |Q| <= (2 - 2^-7) 2^20 (exact in float32 before and after the rounding)
+      const int Qv = (int)rintf(ldexpf(x[cc], kQFracBits - E));
+      const int d2 = Qv >> 14;            // floor(Q / 2^14) in [-128, 127]
+      const int rm = Qv - d2 * 16384;     // in [0, 2^14)
+      const int dg[kQDigits] = {d2, rm >> 7, rm & 127};
       qs += Qv;
-      d0s += hi;
-      d1s += lo;
       const int w = cc & 7;
       const int pos = (cc & ~7) + (BITS == 8 ? w : ((w & 1) ? 4 + (w >> 1) : (w >> 1)));
-      dw[0][pos >> 2] |= (uint32_t)(hi & 0xff) << (8 * (pos & 3));
-      dw[1][pos >> 2] |= (uint32_t)lo << (8 * (pos & 3));
+#pragma unroll
+      for (int d = 0; d < kQDigits; ++d) {
+        ds[d] += dg[d];
+        dw[d][pos >> 2] |= (uint32_t)(dg[d] & 0xff) << (8 * (pos & 3));
+      }
     }
 #pragma unroll
-    for (int d = 0; d < 2; ++d) {
+    for (int d = 0; d < kQDigits; ++d) {
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_qd[d][qh][qg * 32]);
       dst[0] = u32x4_t{dw[d][0], dw[d][1], dw[d][2], dw[d][3]};
       dst[1] = u32x4_t{dw[d][4], dw[d][5], dw[d][6], dw[d][7]};
     }
     s_qe[qh][qg] = E;
-    s_qb[qh][qg] = ldexpf((float)qs, E - 13);  // exact: |sum Q| < 2^19
+    s_qs[qh][qg] = qs;
     if constexpr (BITS == 8) {
-      s_qds[0][qh][qg] = d0s;
-      s_qds[1][qh][qg] = d1s;
+#pragma unroll
+      for (int d = 0; d < kQDigits; ++d) s_qds[d][qh][qg] = ds[d];
     }
   }
   __syncthreads();  // rows and query digits in LDS
@@ -368,46 +379,46 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
   }
 
   // ---- B operands, the same in every wave: lane (kb, nn) holds column nn = (group gc, head ct GT + hl)
-  long Bop[NTL][2][4];
-  int ecol[NTL];
-  float bcol[NTL];
+  long Bop[NTL][kQDigits][4];
+  double cscale[NTL], bcol[NTL];  // 2^(E_g - 20) and b_g of the lane's column
 #pragma unroll
   for (int ct = 0; ct < NTL; ++ct) {
     const int hh = ct * GT + hl;
 #pragma unroll
-    for (int d = 0; d < 2; ++d)
+    for (int d = 0; d < kQDigits; ++d)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         Bop[ct][d][j] = (colok && kb == gc) ? *reinterpret_cast<const long*>(&s_qd[d][hh][32 * kb + 8 * j]) : 0l;
-    ecol[ct] = colok ? s_qe[hh][gc] : 0;
-    bcol[ct] = colok ? s_qb[hh][gc] : 0.f;
+    cscale[ct] = colok ? ldexp(1.0, s_qe[hh][gc] - kQFracBits) : 0.0;
+    bcol[ct] = colok ? (double)s_qs[hh][gc] * cscale[ct] : 0.0;  // exact
   }
   // 8-bit codes enter the contraction as code - 128: each column starts at 128 x its digit sum
-  int acc0[NTL][2];
+  int acc0[NTL][kQDigits];
 #pragma unroll
   for (int ct = 0; ct < NTL; ++ct) {
     const int hh = ct * GT + hl;
 #pragma unroll
-    for (int d = 0; d < 2; ++d) acc0[ct][d] = (BITS == 8 && colok) ? 128 * s_qds[d][hh][gc] : 0;
+    for (int d = 0; d < kQDigits; ++d) acc0[ct][d] = (BITS == 8 && colok) ? 128 * s_qds[d][hh][gc] : 0;
   }
+  const double smd = (double)sm;
   float mx[NTL];
 #pragma unroll
   for (int ct = 0; ct < NTL; ++ct) mx[ct] = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int ti = wv + 4 * i;
-    i32x4_t acc[NTL][2];
+    i32x4_t acc[NTL][kQDigits];
 #pragma unroll
     for (int ct = 0; ct < NTL; ++ct)
 #pragma unroll
-      for (int d = 0; d < 2; ++d) acc[ct][d] = i32x4_t{acc0[ct][d], acc0[ct][d], acc0[ct][d], acc0[ct][d]};
+      for (int d = 0; d < kQDigits; ++d) acc[ct][d] = i32x4_t{acc0[ct][d], acc0[ct][d], acc0[ct][d], acc0[ct][d]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const long a = code_operand<BITS>(cw[i], j);
 #pragma unroll
       for (int ct = 0; ct < NTL; ++ct)
 #pragma unroll
-        for (int d = 0; d < 2; ++d)
+        for (int d = 0; d < kQDigits; ++d)
           acc[ct][d] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, Bop[ct][d][j], acc[ct][d], 0, 0, 0);
     }
     // lane (rg, nn) holds the group sums of candidates 16 ti + 4 rg + e for column nn
@@ -416,16 +427,21 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
       float lg4[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int S = acc[ct][0][e] * 128 + acc[ct][1][e];
-        const float av = ldexpf((float)S, ecol[ct] - 13);  // exact below 2^24 (2- and 4-bit codes)
-        const float s = half_bits_to_float(mw[i][e] & 0xffffu);
-        const float z = half_bits_to_float(mw[i][e] >> 16);
-        const float sa = s * av;
-        const float zb = z * bcol[ct];
-        const float t = sa + zb;
-        const float t01 = t + __shfl_xor(t, GT);      // groups (0, 1) and (2, 3)
-        const float r = t01 + __shfl_xor(t01, 2 * GT);  // (t0 + t1) + (t2 + t3)
-        lg4[e] = (rw[i][e] >= 0) ? sm * r : -__builtin_inff();
+        double S;
+        if constexpr (BITS == 8) {
+          // up to 2^34 in magnitude: combined in float64 (exact below 2^53)
+          S = (double)acc[ct][0][e] * 16384.0 + (double)acc[ct][1][e] * 128.0 + (double)acc[ct][2][e];
+        } else {
+          // |S| <= 2^14 * 128 * 15 * 32 + (2^14 - 1) * 15 * 32 < 2^31: exact in int32
+          S = (double)(acc[ct][0][e] * 16384 + acc[ct][1][e] * 128 + acc[ct][2][e]);
+        }
+        const double av = S * cscale[ct];  // exact (a power of two)
+        const double s = (double)half_bits_to_float(mw[i][e] & 0xffffu);
+        const double z = (double)half_bits_to_float(mw[i][e] >> 16);
+        const double t = fma(s, av, z * bcol[ct]);  // s a_g and z b_g are exact: one rounding
+        const double t01 = t + __shfl_xor(t, GT);      // groups (0, 1) and (2, 3)
+        const double r = t01 + __shfl_xor(t01, 2 * GT);  // (t0 + t1) + (t2 + t3)
+        lg4[e] = (rw[i][e] >= 0) ? (float)(smd * r) : -__builtin_inff();
         mx[ct] = fmaxf(mx[ct], lg4[e]);
       }
       if (colok && gc == 0) {
