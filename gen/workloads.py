@@ -40,10 +40,14 @@ FILL_VALUE = 5.0  # content of unused slots in a sequence's last page
 # bf16 bit helpers (input preparation only)
 # --------------------------------------------------------------------------------------------------
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest, ties to even); return the uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    """Round finite float32 values to bfloat16 (nearest, ties to even); return the uint16 bit patterns.
+    (For a finite value the rounding increment never carries out of 32 bits.)"""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
