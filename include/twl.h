@@ -221,6 +221,20 @@ twl_status twl_decode(const twl_cache* cache, const void* q, const twl_decode_pa
                       float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* twl_decode without a workspace argument, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The workspace is a static
+ * device array of TWL_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends; its device address is looked up once per device, on the first call there.  Calls
+ * whose twl_workspace_bytes() would exceed that size return TWL_EWORKSPACE before any HIP call (the
+ * Llama-shaped layer, B = 1, 32/8 heads, 32K context with a 1/4 page budget, needs 3.8 MiB; B = 16 at
+ * 32K, or B = 4 at 128K, about 46 MiB).  Everything else is as for twl_decode, with the same
+ * kernels and bitwise the same outputs.  This function allocates nothing; calls that overlap on one
+ * GPU share the array and race, so serialise them (one stream, or events). */
+#define TWL_NOALLOC_SCRATCH_BYTES (64u << 20)
+twl_status twl_decode_noalloc(const twl_cache* cache, const void* q, const twl_decode_params* params, float* out,
+                              float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens,
+                              int64_t capacity, void* stream);
+
 /* twl_decode with timing hooks: `events` holds 2*TWL_NUM_STAGES hipEvent_t created by the caller;
  * events[2i] / events[2i+1] are recorded on `stream` immediately before / after stage i's kernel:
  * 0 page scoring, 1 page top-K, 2 INT4 estimate, 3 top-p + union, 4 split-K attention, 5 merge.

@@ -29,7 +29,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ["twl_quantize_k", "twl_select_pages", "twl_estimate_topp", "twl_sparse_attn", "twl_decode",
               "twl_decode_profiled", "twl_select_clusters_topp", "twl_decode_clusters", "twl_workspace_bytes",
-              "twl_status_str", "twl_version", "twl_keep_pages"]:
+              "twl_status_str", "twl_version", "twl_keep_pages", "twl_decode_noalloc"]:
         assert n in names
 
 
@@ -212,3 +212,22 @@ def test_cluster_approx_entry_points_validate():
     assert L.twl_cluster_approx_unkept(*no_lse) == 1
     small_ws = ok[:12] + (256,) + ok[13:]
     assert L.twl_cluster_approx_unkept(*small_ws) == 3
+
+
+def test_noalloc_decode_rejects_steps_beyond_its_scratch(twl):
+    # validated on the host before any HIP call: a step whose workspace exceeds the static scratch,
+    # and the usual argument errors, are refused without touching a GPU
+    L = twl.lib()
+    fake = ctypes.c_void_p(0x10000)
+    prm = twl.ParamsC(0.9, 1.0, 0.088, 32, 0, 0)
+    big = twl.CacheC(4, 32, 8, 128, 16, 32, 16384, 65536, 262144, fake, fake, fake, fake, fake, fake, fake, 4)
+    need = L.twl_workspace_bytes(ctypes.byref(big), 262144)
+    assert need > twl.NOALLOC_SCRATCH_BYTES
+    r = L.twl_decode_noalloc(ctypes.byref(big), fake, ctypes.byref(prm), fake, None, None, None, None, 0, None)
+    assert r == twl.TWL_EWORKSPACE
+    small = _fake_cache(twl)
+    bad = twl.ParamsC(1.5, 0.25, 0.088, 32, 0, 0)
+    assert L.twl_decode_noalloc(ctypes.byref(small), fake, ctypes.byref(bad), fake, None, None, None, None, 0,
+                                None) == twl.TWL_EINVAL
+    assert L.twl_decode_noalloc(ctypes.byref(small), ctypes.c_void_p(0x10001), ctypes.byref(prm), fake, None, None,
+                                None, None, 0, None) == twl.TWL_EINVAL

@@ -22,7 +22,7 @@ __all__ = [
     "LIB_PATH", "TwlError", "PagedCache", "lib", "workspace_bytes", "quantize_k", "select_pages",
     "estimate_topp", "sparse_attn", "decode", "decode_profiled", "select_clusters_topp", "status_str",
     "version", "keep_count", "NUM_STAGES", "STAGE_NAMES", "DEFAULT_SM_SCALE", "decode_clusters",
-    "cluster_value_means", "cluster_approx_unkept",
+    "cluster_value_means", "cluster_approx_unkept", "decode_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libtwl.so")
@@ -31,6 +31,7 @@ STAGE_NAMES = ("page_score", "page_select", "estimate", "topp_union", "attn_spli
 DEFAULT_SM_SCALE = float(torch.tensor(1.0 / math.sqrt(128.0), dtype=torch.float32))
 
 TWL_OK, TWL_EINVAL, TWL_EUNSUPPORTED, TWL_EWORKSPACE, TWL_EHIP = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # TWL_NOALLOC_SCRATCH_BYTES
 
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -95,6 +96,7 @@ def lib() -> ctypes.CDLL:
         "twl_decode": (_i32, [C, _p, ctypes.POINTER(ParamsC), _p, _p, _p, _p, _p, _i64, _p, ctypes.c_size_t, _p]),
         "twl_decode_profiled": (_i32, [C, _p, ctypes.POINTER(ParamsC), _p, _p, _p, _p, _p, _i64, _p,
                                        ctypes.c_size_t, _p, ctypes.POINTER(_p)]),
+        "twl_decode_noalloc": (_i32, [C, _p, ctypes.POINTER(ParamsC), _p, _p, _p, _p, _p, _i64, _p]),
         "twl_select_clusters_topp": (_i32, [C, _p, _f32, _f32, _i32, _p, _p, _p, _i32, _p, _p, _p,
                                             ctypes.c_size_t, _p]),
         "twl_decode_clusters": (_i32, [C, _p, ctypes.POINTER(ParamsC), _f32, _p, _p, _p, _i32, _p, _p, _p, _p, _p,
@@ -275,6 +277,19 @@ def decode(cache: PagedCache, q: torch.Tensor, *, p: float, keep_frac: float, sm
     _check(lib().twl_decode(ctypes.byref(cache.struct()), _ptr(q), ctypes.byref(prm), _ptr(out), _ptr(lse),
                             _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap, _ptr(ws),
                             ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def decode_noalloc(cache: PagedCache, q: torch.Tensor, *, p: float, keep_frac: float,
+                   sm_scale: float = DEFAULT_SM_SCALE, iters: int = 32, out: torch.Tensor,
+                   lse: Optional[torch.Tensor] = None, threshold: Optional[torch.Tensor] = None,
+                   sel_indptr: Optional[torch.Tensor] = None, sel_tokens: Optional[torch.Tensor] = None,
+                   stream=None, topk: int = 0, headwise: bool = False):
+    """:func:`decode` on the library's static device workspace (no workspace argument, nothing
+    allocated); raises TwlError(TWL_EWORKSPACE) when the step needs more than NOALLOC_SCRATCH_BYTES."""
+    prm = _params(p, keep_frac, sm_scale, iters, topk, headwise)
+    cap = 0 if sel_tokens is None else int(sel_tokens.numel())
+    _check(lib().twl_decode_noalloc(ctypes.byref(cache.struct()), _ptr(q), ctypes.byref(prm), _ptr(out), _ptr(lse),
+                                    _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap, _stream(stream)))
 
 
 def decode_profiled(cache: PagedCache, q: torch.Tensor, events, *, p: float, keep_frac: float,

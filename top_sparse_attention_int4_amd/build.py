@@ -25,7 +25,7 @@ LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libtwl.so")
 
 SOURCES = ["api.cpp", "quantize.hip", "select.hip", "estimate.hip", "topp.hip", "topp_wide.hip", "attention.hip",
-           "cluster.hip"]
+           "cluster.hip", "noalloc.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -245,9 +245,10 @@ hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, void* 
   return E.rec(11);
 }
 
-twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_params* prm, float* out,
-                       float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
-                       void* ws, size_t ws_bytes, void* stream, void* const* events) {
+// Host-only validation of a decode call's arguments (everything but the workspace); on success the
+// workspace layout it needs is written to *L.
+twl_status decode_check(const twl_cache* cache, const void* q, const twl_decode_params* prm, const float* out,
+                        const int32_t* sel_indptr, const int32_t* sel_tokens, int64_t capacity, Layout* L) {
   twl_status st = check_cache(cache, true, true);
   if (st != TWL_OK) return st;
   if (!q || misaligned16(q) || !prm || !out) return TWL_EINVAL;
@@ -266,8 +267,18 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
   if (ncap == 0) return TWL_EUNSUPPORTED;
   // the top-k baseline and head-wise attention run on the one-block-per-head search's bitmaps
   if ((prm->topk > 0 || prm->headwise) && is_wide(ncap)) return TWL_EUNSUPPORTED;
+  make_layout(cache, ncap, L);
+  return TWL_OK;
+}
+
+twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_params* prm, float* out,
+                       float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
+                       void* ws, size_t ws_bytes, void* stream, void* const* events) {
   Layout L;
-  make_layout(cache, ncap, &L);
+  twl_status st = decode_check(cache, q, prm, out, sel_indptr, sel_tokens, capacity, &L);
+  if (st != TWL_OK) return st;
+  const int64_t ncap = L.ncap;
+  const bool selector = prm->keep_frac < 1.0f;
   st = check_ws(ws, ws_bytes, L);
   if (st != TWL_OK) return st;
   if (events) {
@@ -380,6 +391,26 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
 }
 
 }  // namespace
+
+namespace twl {
+
+twl_status decode_workspace_need(const twl_cache* cache, const void* q, const twl_decode_params* params,
+                                 const float* out, const int32_t* sel_indptr, const int32_t* sel_tokens,
+                                 int64_t capacity, size_t* need) {
+  Layout L;
+  const twl_status st = decode_check(cache, q, params, out, sel_indptr, sel_tokens, capacity, &L);
+  if (st == TWL_OK) *need = L.total;
+  return st;
+}
+
+twl_status decode_with_workspace(const twl_cache* cache, const void* q, const twl_decode_params* params, float* out,
+                                 float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens,
+                                 int64_t capacity, void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(cache, q, params, out, lse, threshold, sel_indptr, sel_tokens, capacity, ws, ws_bytes, stream,
+                     nullptr);
+}
+
+}  // namespace twl
 
 extern "C" {
 

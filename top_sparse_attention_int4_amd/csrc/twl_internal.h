@@ -2,7 +2,10 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "twl.h"
 
 namespace twl {
 
@@ -143,5 +146,16 @@ constexpr int kPartFloats = 4 + kD;  // per (chunk, head): max, sum, 2 pad, outp
 // elements per thread of the top-p block for a candidate capacity (0 = unsupported)
 int topp_elems_per_thread(int64_t ncap);
 constexpr int kToppThreads = 1024;
+
+// ---- the decode entry point's host side, shared with its allocation-free variant ------------------
+// Validates a decode call (everything but the workspace, no HIP call) and gives the workspace bytes it
+// needs.
+twl_status decode_workspace_need(const twl_cache* cache, const void* q, const twl_decode_params* params,
+                                 const float* out, const int32_t* sel_indptr, const int32_t* sel_tokens,
+                                 int64_t capacity, size_t* need);
+// twl_decode on the given workspace.
+twl_status decode_with_workspace(const twl_cache* cache, const void* q, const twl_decode_params* params, float* out,
+                                 float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens,
+                                 int64_t capacity, void* ws, size_t ws_bytes, void* stream);
 
 }  // namespace twl
