@@ -1,13 +1,27 @@
 """Benchmark: one decode layer-step of top-p sparse attention with an INT4 K estimate, on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload C2] [--layers L] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload all|C1..C5] [--layers L] [--no-cpu-baseline]
 
-A step is one pass of the whole hot path over one batch: Quest-style page selection -> INT4 weight
-estimate -> per-head top-p (bisection) -> GQA union -> split-K sparse attention -> merge.  Steps
-rotate over L layer caches of identical shape, enough that the rotation exceeds 4 GiB and its INT4
-codes and page bounds alone exceed 1 GiB, so every step reads cold HBM rather than the 256 MB Infinity
-Cache, as a many-layer model does (up to 1 GiB of layers are drawn independently, the rest are device
-copies of them at their own addresses).  Inputs are resident in HBM before timing starts.
+A step is one pass of the whole hot path over one batch: Quest-style page selection (or, for the
+hierarchical layer, cluster-level top-p) -> INT4 weight estimate -> per-head top-p (bisection) -> GQA
+union -> split-K sparse attention -> merge.  Steps rotate over L layer caches of identical shape, enough
+that the rotation exceeds 4 GiB and its INT4 codes and page bounds alone exceed 1 GiB, so every step
+reads cold HBM rather than the 256 MB Infinity Cache, as a many-layer model does (up to 1 GiB of
+layers are drawn independently, the rest are device copies of them at their own addresses).  Inputs
+are resident in HBM before timing starts.
+
+By default (``--workload all``) the line covers the metric's whole context range: the headline is the
+256K-token hierarchical layer (C5, the largest single-GPU configuration), and the 32K Llama-shaped
+layer (C2), the 16-sequence 32K layer (C3) and the 4-sequence 128K layer (C4) follow under
+``workloads`` in the same JSON line, each measured the same way.
+
+Per workload: K timed steps between synchronisations (``value`` = microseconds per layer-step, lower is
+better); then a pass with timing events around every stage kernel (events created without the
+system-scope fence, which would otherwise write back and invalidate caches at every event and
+distort the kernels it brackets); ``roofline`` describes the split-K attention kernel (the stage that
+moves most bytes): its algorithmic bytes per launch (512 B of K/V rows + 4 B index per kept token,
+plus the group's q) over its event-timed duration.  ``cpu_baseline`` times the numpy oracle on a
+bounded sample of the headline workload on the host cores.
 
 With ``--estimator-bits`` it instead reports the estimator's precision ablation (2-, 4- and 8-bit K
 codes on the Llama-layer workload at its p = 0.85): the event-timed estimate kernel per layer-step and
@@ -27,17 +41,12 @@ attention, and decode time, one JSON line.
 With ``--cluster-approx`` (hierarchical workload) it measures the optional approximation of the
 clusters no head keeps: the time of that step and each head's output error against dense attention
 with and without it, one JSON line.
-
-Prints ONE JSON line.  ``value`` is microseconds per layer-step (lower is better).  ``roofline``
-describes the split-K attention kernel (the stage that moves most bytes): its algorithmic bytes per
-launch (512 B of K/V rows + 4 B index per kept token, plus the group's q) over its average launch
-duration, measured with HIP events around that kernel in a second timed pass.  ``cpu_baseline`` times
-the numpy oracle on a bounded sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -60,15 +69,18 @@ DESCR = {
     "C5": "Double-P hierarchical: B=1, 32/8 heads, n=262144, 4096 Zipf(1.1) clusters, cluster p1=0.95 "
           "then token p=0.9",
 }
+HEADLINE = "C5"
+LINE = ["C2", "C3", "C4", "C5"]  # the metric's 32K-256K range, headline last
 STAGES_CLUSTER = ["cluster_scores_topp", "cluster_union", "estimate", "topp_union", "attention", "merge"]
+EVENT_NO_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C2", choices=sorted(DESCR))
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="all", choices=sorted(DESCR) + ["all"])
     ap.add_argument("--layers", type=int, default=0, help="layer caches rotated (0: see above)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-units", type=int, default=0, help="oracle sample size in units (0: auto)")
@@ -94,6 +106,47 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+class FenceFreeEvents:
+    """Raw HIP timing events created with hipEventDisableSystemFence (the runtime's own flag for
+    events used only to time work: no cache write-back and invalidation at each event)."""
+
+    def __init__(self, n: int):
+        import top_sparse_attention_int4_amd as twl
+        self.L = twl.lib()
+        self.L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.L.hipEventCreateWithFlags.restype = ctypes.c_int
+        self.L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventElapsedTime.restype = ctypes.c_int
+        self.L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.L.hipEventRecord.restype = ctypes.c_int
+        self.L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L.hipEventDestroy.restype = ctypes.c_int
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.L.hipEventCreateWithFlags(ctypes.byref(e), EVENT_NO_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e.value)
+
+    def handles(self, i0: int, n: int) -> list:
+        return self.ev[i0:i0 + n]
+
+    def record(self, i: int, stream) -> None:
+        if self.L.hipEventRecord(ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i: int, j: int) -> float:
+        out = ctypes.c_float()
+        if self.L.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(self.ev[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.L.hipEventDestroy(ctypes.c_void_p(e))
+        self.ev = []
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -103,12 +156,8 @@ def main():
 
     import torch
     import top_sparse_attention_int4_amd as twl
-    from gen import make_config
-    from gen.device import upload
 
-    if not os.path.exists(twl.LIB_PATH):
-        from top_sparse_attention_int4_amd import build as b
-        b.build()
+    twl.lib()  # raises if the library is missing or stale: build it before running
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.estimator_bits:
@@ -132,8 +181,72 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    names = LINE if args.workload == "all" else [args.workload]
+    head = HEADLINE if args.workload == "all" else args.workload
+    copy_gbps = plain_copy_gbps(dev)
+    recs, wl = {}, {}
+    for name in names:
+        recs[name], wl[name] = measure_workload(name, args, dev, copy_gbps)
+        torch.cuda.empty_cache()
+    r = recs[head]
+    line = {
+        "metric": METRIC,
+        "value": r["us_per_layer_step"],
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**r["config"], "parallelism": "single GPU",
+                   "also_in_line": [n for n in names if n != head]},
+        "hbm": r["hbm"],
+        "step_us_with_events": r["step_us_with_events"],
+        "stages_us": r["stages_us"],
+        "event_gap_us": r["event_gap_us"],
+        "roofline": r["roofline"],
+        "workloads": {n: {k: recs[n][k] for k in ("config", "us_per_layer_step", "hbm", "stages_us", "event_gap_us",
+                                                  "roofline")}
+                      for n in names if n != head},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl[head], args.cpu_units)
+    print(json.dumps(line), flush=True)
+
+
+def plain_copy_gbps(dev) -> float:
+    """A plain 512 MiB device copy on this GPU (read + written bytes over time)."""
+    import torch
+    src = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    s = a.elapsed_time(b) / 5 * 1e-3
+    del src, dst
+    return 2 * (128 << 20) * 4 / s / 1e9
+
+
+def measure_workload(name, args, dev, copy_gbps):
+    """One workload's record (and its layer-0 workload object, for the CPU baseline)."""
+    import torch
+    import top_sparse_attention_int4_amd as twl
+    from gen import make_config
+    from gen.device import upload
+
     # ---- layers ----------------------------------------------------------------------------------
-    w0 = make_config(args.workload, layer=0)
+    w0 = make_config(name, layer=0)
     # per (page, kv-head): K and V 4 KiB each; INT4 codes 1 KiB, scale/zero 256 B, page bounds 512 B
     small = 0.4375 * w0.k_pages.nbytes
     per_layer = 2 * w0.k_pages.nbytes + small
@@ -141,12 +254,12 @@ def main():
     # (four times the 256 MB Infinity Cache), as in a many-layer model
     L = args.layers or max(math.ceil((4 << 30) / per_layer), math.ceil((1 << 30) / small))
     n_drawn = min(L, max(1, math.ceil((1 << 30) / per_layer)))
-    print(f"[bench] {args.workload}: {L} layer(s) ({n_drawn} drawn, the rest device copies), "
+    print(f"[bench] {name}: {L} layer(s) ({n_drawn} drawn, the rest device copies), "
           f"{per_layer / 1e6:.0f} MB each", file=sys.stderr, flush=True)
     layers = []
     for li in range(L):
         if li < n_drawn:
-            w = w0 if li == 0 else make_config(args.workload, layer=li)
+            w = w0 if li == 0 else make_config(name, layer=li)
             t = upload(w, dev)
         else:
             # a copy at its own addresses: the same values (so the same work), cold in every cache
@@ -159,7 +272,7 @@ def main():
         layers.append((w, cache, t))
     torch.cuda.synchronize()
     w = w0
-    B, Hq, Hkv, G = w.batch, w.num_q_heads, w.num_kv_heads, w.group
+    B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
     U = B * Hkv
     kf, p = w.keep_frac, w.p
     clusters = w.csize is not None
@@ -201,59 +314,60 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # ---- second timed pass: HIP events around every stage kernel ---------------------------------
+    # ---- second timed pass: fence-free events around every stage kernel --------------------------
     nev = 2 * twl.NUM_STAGES
-    stage_ms = np.zeros(twl.NUM_STAGES)
-    kept = []
     K2 = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(K2)]
+    fe = FenceFreeEvents(nev * K2)
     torch.cuda.synchronize()
     for i in range(K2):
-        step(i, evs[i])
+        step(i, fe.handles(i * nev, nev))
     torch.cuda.synchronize()
+    stage_ms = np.zeros(twl.NUM_STAGES)
+    gap_ms = []
+    for i in range(K2):
+        b0 = i * nev
+        for s_ in range(twl.NUM_STAGES):
+            stage_ms[s_] += fe.ms(b0 + 2 * s_, b0 + 2 * s_ + 1)
+        # between one stage's closing event and the next stage's opening one nothing is enqueued:
+        # those gaps are the cost of an event record inside a busy stream
+        gap_ms += [fe.ms(b0 + 2 * s_ + 1, b0 + 2 * s_ + 2) for s_ in range(twl.NUM_STAGES - 1)]
+    stage_ms /= K2
+    fe.close()
+    gap_us = float(np.median(gap_ms)) * 1e3
     for li in range(L):
         step(li, lists=True)
     torch.cuda.synchronize()
-    for i in range(K2):
-        for s in range(twl.NUM_STAGES):
-            stage_ms[s] += evs[i][2 * s].elapsed_time(evs[i][2 * s + 1])
-    stage_ms /= K2
-    for li in range(L):
-        kept.append(indptrs[li].cpu().numpy())
+    kept = [indptrs[li].cpu().numpy() for li in range(L)]
 
     # ---- per-step spread: a third pass with one event pair around each step -----------------------
-    pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    fp = FenceFreeEvents(2 * args.steps)
+    stream = torch.cuda.current_stream()
     for i in range(args.steps):
-        pe[i][0].record()
+        fp.record(2 * i, stream)
         step(i)
-        pe[i][1].record()
+        fp.record(2 * i + 1, stream)
     torch.cuda.synchronize()
-    st_us = np.array([a.elapsed_time(b) for a, b in pe]) * 1e3
+    st_us = np.array([fp.ms(2 * i, 2 * i + 1) for i in range(args.steps)]) * 1e3
+    fp.close()
     step_spread = {k: round(float(np.percentile(st_us, q)), 3) for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
 
-    # ---- reference rates on this GPU: a plain device copy, and the INT4 append (a0) --------------
-    def timed(fn, reps=5):
-        for _ in range(2):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e-3  # seconds per call
-    csrc = torch.empty(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
-    cdst = torch.empty_like(csrc)
-    copy_gbps = 2 * csrc.numel() * 4 / timed(lambda: cdst.copy_(csrc)) / 1e9
-    del csrc, cdst
+    # ---- the INT4 append (a0), timed alone ---------------------------------------------------------
     _, cache0, t0 = layers[0]
     zeros_b = torch.zeros(B, dtype=torch.int32, device=dev)
     ntok = int(w.seq_lens.astype(np.int64).sum())
+    for _ in range(2):
+        twl.quantize_k(cache0, zeros_b, t0["seq_lens"], w.max_seq_len)
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a_.record()
+    for _ in range(5):
+        twl.quantize_k(cache0, zeros_b, t0["seq_lens"], w.max_seq_len)
+    b_.record()
+    torch.cuda.synchronize()
     # per (token, kv-head): 256 B of K read, 64 B of codes and 16 B of scale/zero written;
     # per (page, kv-head): 512 B of bounds written
     append_bytes = Hkv * (ntok * (256 + 80) + int((-(-w.seq_lens.astype(np.int64) // 16)).sum()) * 512)
-    append_gbps = append_bytes / timed(lambda: twl.quantize_k(cache0, zeros_b, t0["seq_lens"], w.max_seq_len)) / 1e9
+    append_gbps = append_bytes / (a_.elapsed_time(b_) / 5 * 1e-3) / 1e9
 
     # ---- algorithmic bytes (per layer-step, averaged over the layers) ----------------------------
     seq = w.seq_lens.astype(np.int64)
@@ -285,7 +399,7 @@ def main():
     achieved = bytes_attn / (attn_ms * 1e-3)
 
     traffic = None
-    prof = os.path.join(ROOT, "profiles", f"traffic_attn_splitk_{args.workload}.json")
+    prof = os.path.join(ROOT, "profiles", f"traffic_attn_splitk_{name}.json")
     if os.path.exists(prof):
         with open(prof) as fh:
             tr = json.load(fh)
@@ -294,51 +408,39 @@ def main():
     # bytes the whole step touches (counter passes over every kernel of the step, committed under
     # profiles/), while the kernel sources still hash to the recorded value
     touched = None
-    prof = os.path.join(ROOT, "profiles", f"traffic_step_{args.workload}.json")
+    prof = os.path.join(ROOT, "profiles", f"traffic_step_{name}.json")
     if os.path.exists(prof):
         with open(prof) as fh:
             tr = json.load(fh)
         if tr.get("kernel_source_hash") == kernel_source_hash():
             touched = tr.get("hbm_bytes_per_step")
-
+    step_s = ms_per_step * 1e-3
     rec = {
-        "metric": METRIC,
-        "value": round(ms_per_step * 1e3, 3),
-        "unit": "us/layer-step",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "us_per_layer_step": round(ms_per_step * 1e3, 3),
         "ms_per_step": round(ms_per_step, 6),
-        "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {DESCR[args.workload]}", "batch": B, "q_heads": Hq,
-                   "kv_heads": Hkv, "context": int(seq.max()), "p": p, "keep_frac": kf,
-                   "layers_rotated": L, "parallelism": "single GPU",
+        "config": {"workload": f"{name}: {DESCR[name]}", "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "context": int(seq.max()), "p": p, "keep_frac": kf, "layers_rotated": L,
                    **({"p1": w.p1, "num_clusters": w.num_clusters} if clusters else {})},
-        "hbm": {"algorithmic_bytes_per_step": int(bytes_step), "gbps": round(bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
-                "frac_of_8TBps": round(bytes_step / (ms_per_step * 1e-3) / HBM_PEAK, 4),
+        "hbm": {"algorithmic_bytes_per_step": int(bytes_step), "gbps": round(bytes_step / step_s / 1e9, 1),
+                "frac_of_8TBps": round(bytes_step / step_s / HBM_PEAK, 4),
                 "touched_bytes_per_step": touched,
-                "touched_frac_of_8TBps": (round(touched / (ms_per_step * 1e-3) / HBM_PEAK, 4) if touched else None),
+                "touched_frac_of_8TBps": (round(touched / step_s / HBM_PEAK, 4) if touched else None),
                 "copy_gbps": round(copy_gbps, 1),
-                "frac_of_copy": round(bytes_step / (ms_per_step * 1e-3) / 1e9 / copy_gbps, 4),
+                "frac_of_copy": round(bytes_step / step_s / 1e9 / copy_gbps, 4),
                 "append_gbps": round(append_gbps, 1),
                 "candidates_per_step": cand_units_total, "kept_tokens_per_step": sel_tokens_total},
         "step_us_with_events": step_spread,
         "stages_us": {n: round(float(x) * 1e3, 3)
                       for n, x in zip(STAGES_CLUSTER if clusters else twl.STAGE_NAMES, stage_ms)},
+        "event_gap_us": round(gap_us, 3),
         "roofline": {"kernel": "k_attn (split-K sparse attention)", "bound": "hbm",
                      "achieved": round(achieved / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(bytes_attn), "avg_launch_us": round(attn_ms * 1e3, 3),
                      "frac_of_copy": round(achieved / 1e9 / copy_gbps, 4)},
-        "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_units)
-    print(json.dumps(rec), flush=True)
+    del layers, ws, toks, indptrs
+    return rec, w0
 
 
 def estimator_bits_report(args, dev):

@@ -292,19 +292,31 @@ def decode_noalloc(cache: PagedCache, q: torch.Tensor, *, p: float, keep_frac: f
                                     _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap, _stream(stream)))
 
 
+def _event_array(events):
+    """2*NUM_STAGES timing events as a hipEvent_t array: torch.cuda.Event objects, or raw hipEvent_t
+    handles given as integers."""
+    if len(events) != 2 * NUM_STAGES:
+        raise ValueError("need 2*NUM_STAGES events")
+    ptrs = []
+    for e in events:
+        if isinstance(e, int):
+            ptrs.append(ctypes.c_void_p(e))
+            continue
+        if e.cuda_event == 0:  # make sure the underlying hipEvent_t exists
+            e.record()
+        ptrs.append(ctypes.c_void_p(e.cuda_event))
+    return (_p * (2 * NUM_STAGES))(*ptrs)
+
+
 def decode_profiled(cache: PagedCache, q: torch.Tensor, events, *, p: float, keep_frac: float,
                     sm_scale: float = DEFAULT_SM_SCALE, iters: int = 32, out: torch.Tensor,
                     lse: Optional[torch.Tensor] = None, threshold: Optional[torch.Tensor] = None,
                     sel_indptr: Optional[torch.Tensor] = None, sel_tokens: Optional[torch.Tensor] = None,
                     ws: torch.Tensor, stream=None, topk: int = 0, headwise: bool = False):
-    """``events``: 2*NUM_STAGES torch.cuda.Event(enable_timing=True) recorded around each stage."""
-    if len(events) != 2 * NUM_STAGES:
-        raise ValueError("need 2*NUM_STAGES events")
-    for e in events:  # make sure the underlying hipEvent_t exists
-        if e.cuda_event == 0:
-            e.record()
-    arr = (_p * (2 * NUM_STAGES))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    """``events``: 2*NUM_STAGES timing events (torch.cuda.Event(enable_timing=True), or hipEvent_t
+    handles as integers) recorded around each stage."""
     prm = _params(p, keep_frac, sm_scale, iters, topk, headwise)
+    arr = _event_array(events)
     cap = 0 if sel_tokens is None else int(sel_tokens.numel())
     _check(lib().twl_decode_profiled(ctypes.byref(cache.struct()), _ptr(q), ctypes.byref(prm), _ptr(out),
                                      _ptr(lse), _ptr(threshold), _ptr(sel_indptr), _ptr(sel_tokens), cap,
@@ -326,14 +338,7 @@ def decode_clusters(cache: PagedCache, q: torch.Tensor, *, p: float, p1: float, 
                     sel_indptr: Optional[torch.Tensor] = None, sel_tokens: Optional[torch.Tensor] = None,
                     ws: torch.Tensor, events=None, stream=None):
     """Double-P decode step; ``events`` optionally holds 2*NUM_STAGES timing events."""
-    arr = None
-    if events is not None:
-        if len(events) != 2 * NUM_STAGES:
-            raise ValueError("need 2*NUM_STAGES events")
-        for e in events:
-            if e.cuda_event == 0:
-                e.record()
-        arr = (_p * (2 * NUM_STAGES))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    arr = None if events is None else _event_array(events)
     prm = _params(p, 1.0, sm_scale, iters)
     cap = 0 if sel_tokens is None else int(sel_tokens.numel())
     _check(lib().twl_decode_clusters(ctypes.byref(cache.struct()), _ptr(q), ctypes.byref(prm), float(p1),
