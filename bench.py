@@ -184,6 +184,7 @@ def main():
     names = LINE if args.workload == "all" else [args.workload]
     head = HEADLINE if args.workload == "all" else args.workload
     copy_gbps = plain_copy_gbps(dev)
+    floor_us = launch_floor_us(dev)
     recs, wl = {}, {}
     for name in names:
         recs[name], wl[name] = measure_workload(name, args, dev, copy_gbps)
@@ -208,6 +209,7 @@ def main():
         "step_us_with_events": r["step_us_with_events"],
         "stages_us": r["stages_us"],
         "event_gap_us": r["event_gap_us"],
+        "six_empty_kernels_us": floor_us,
         "roofline": r["roofline"],
         "workloads": {n: {k: recs[n][k] for k in ("config", "us_per_layer_step", "hbm", "stages_us", "event_gap_us",
                                                   "roofline")}
@@ -217,6 +219,30 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl[head], args.cpu_units)
     print(json.dumps(line), flush=True)
+
+
+def launch_floor_us(dev) -> float:
+    """Six back-to-back one-element kernels queued behind a long copy (so they run as fast as the
+    GPU dispatches them), between fence-free events: the floor of a six-kernel dependent chain."""
+    import torch
+    src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    tiny = torch.empty(1, dtype=torch.float32, device=dev)
+    ev = FenceFreeEvents(2)
+    stream = torch.cuda.current_stream()
+    out = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        ev.record(0, stream)
+        for _ in range(6):
+            tiny.zero_()
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        out.append(ev.ms(0, 1) * 1e3)
+    ev.close()
+    del src, dst
+    return round(float(np.median(out)), 3)
 
 
 def plain_copy_gbps(dev) -> float:

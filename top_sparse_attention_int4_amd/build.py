@@ -5,8 +5,8 @@
 
 The library is a single shared object holding every kernel (single-source HIP, no runtime code
 loading).  Floating-point contraction is off (the committed float32 roundings of the page scores and
-the estimate rely on it; fused multiply-adds are written explicitly where wanted) and packed fp32
-instructions are disabled.
+the estimate rely on it; fused multiply-adds are written explicitly where wanted), packed fp32
+instructions are disabled, and matrix-core instructions write their results to ordinary VGPRs.
 """
 
 from __future__ import annotations
@@ -30,6 +30,8 @@ SOURCES = ["api.cpp", "quantize.hip", "select.hip", "estimate.hip", "topp.hip", 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results straight into VGPRs (no accumulator-register reads after every MFMA)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 

@@ -99,7 +99,7 @@ struct Layout {
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
          ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
-         wkeys = 0, apart = 0, total = 0;
+         wkeys = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
 };
 
 // ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
@@ -145,6 +145,8 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
   L->thr = take((size_t)BH * 4);
   L->apart = take((size_t)BH * kApproxSlices * kApproxStride * 4);  // unkept-cluster approximation
+  L->qdig = take((size_t)BH * kGroups * kQDigits * 32);             // the estimate's query digits
+  L->qmeta = take((size_t)BH * kGroups * kQMeta * 4);
   if (is_wide(ncap)) {
     L->pmax = take((size_t)BH * (ncap / kEstCands) * 4);
     L->wstate = take((size_t)BH * kWideStateWords * 8);
@@ -184,6 +186,8 @@ twl_status hip_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_EHIP
     if (e_ != hipSuccess) return TWL_EHIP;     \
   } while (0)
 
+QDigits qdigits_of(void* ws, const Layout& L) { return QDigits{at<uint8_t>(ws, L.qdig), at<int32_t>(ws, L.qmeta)}; }
+
 WideWs wide_of(void* ws, const Layout& L) {
   return WideWs{at<float>(ws, L.pmax), at<uint64_t>(ws, L.wstate), at<int32_t>(ws, L.wcnt), at<uint32_t>(ws, L.uwords),
                 at<uint32_t>(ws, L.wkeys)};
@@ -191,7 +195,8 @@ WideWs wide_of(void* ws, const Layout& L) {
 
 // Estimate, top-p and (when `with_union`) the compacted GQA union of every unit, the narrow or the
 // wide top-p by candidate capacity.  Events 4/5 bracket the estimate, 6/7 the rest.
-hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, void* ws,
+// The query digits must have been written (by the page scores or launch_qdigits) before this runs.
+hipError_t estimate_topp(const CacheView& c, float sm, const CandView& cand, void* ws,
                          const Layout& L, float p, int iters, float* thr, float* mass, uint32_t* head_mask,
                          int mask_words, bool with_union, const Events& E, hipStream_t s, int topk = 0) {
   const int ncap = (int)L.ncap;
@@ -201,8 +206,8 @@ hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const 
   if ((e = E.rec(4)) != hipSuccess) return e;
   // token ids of the candidates are read only by the passes that emit the union lists
   const bool need_tok = with_union || (wide && mass);
-  e = launch_estimate(c, q, sm, cand, ncap, at<float>(ws, L.logits), need_tok ? at<int32_t>(ws, L.ctok) : nullptr,
-                      at<int32_t>(ws, L.crow), wide ? &wd : nullptr, s);
+  e = launch_estimate(c, qdigits_of(ws, L), sm, cand, ncap, at<float>(ws, L.logits),
+                      need_tok ? at<int32_t>(ws, L.ctok) : nullptr, at<int32_t>(ws, L.crow), wide ? &wd : nullptr, s);
   if (e != hipSuccess) return e;
   if ((e = E.rec(5)) != hipSuccess) return e;
   if ((e = E.rec(6)) != hipSuccess) return e;
@@ -210,22 +215,25 @@ hipError_t estimate_topp(const CacheView& c, const uint16_t* q, float sm, const 
     e = launch_topp_wide(c, wd, at<float>(ws, L.logits), ncap, p, iters, thr, head_mask, mask_words,
                          with_union || mass || head_mask, s);
     if (e == hipSuccess && (with_union || mass))
-      e = launch_wide_emit(c, wd, at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), ncap, at<int32_t>(ws, L.utok),
-                           at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), mass, s);
+      e = launch_wide_emit(c, wd, at<int32_t>(ws, L.ctok), ncap, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt),
+                           mass, s);
   } else {
     e = launch_topp(c, at<float>(ws, L.logits), ncap, p, iters, thr, mass, at<uint32_t>(ws, L.masks), head_mask,
                     mask_words, topk, s);
     if (e == hipSuccess && with_union)
-      e = launch_union(c, at<uint32_t>(ws, L.masks), at<int32_t>(ws, L.ctok), at<int32_t>(ws, L.crow), ncap,
-                       at<int32_t>(ws, L.utok), at<int32_t>(ws, L.urow), at<int32_t>(ws, L.ucnt), s);
+      e = launch_union(c, at<uint32_t>(ws, L.masks), at<int32_t>(ws, L.ctok), ncap, at<int32_t>(ws, L.utok),
+                       at<int32_t>(ws, L.ucnt), s);
   }
   if (e != hipSuccess) return e;
   return E.rec(7);
 }
 
 // Attention over the top-p bitmaps (no compacted list needed) and the merge; events 8..11.
-hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, void* ws, const Layout& L, float* out,
-                         float* lse, const Events& E, hipStream_t s, bool headwise = false) {
+// `cand` names where the K/V row of each candidate comes from: the selector's physical page list,
+// the page table (every token a candidate), or the rows the estimate recorded (ranges).
+hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, void* ws,
+                         const Layout& L, float* out, float* lse, const Events& E, hipStream_t s,
+                         bool headwise = false) {
   const bool wide = is_wide(L.ncap);
   MaskView mv{};
   if (wide) {
@@ -233,7 +241,10 @@ hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, void* 
   } else {
     mv.head_masks = at<uint32_t>(ws, L.masks);
   }
+  mv.cand_mode = cand.mode;
   mv.cand_row = at<int32_t>(ws, L.crow);
+  mv.page_phys = cand.phys;
+  mv.page_stride = cand.max_items;
   mv.ncap = L.ncap;
   hipError_t e;
   if ((e = E.rec(8)) != hipSuccess) return e;
@@ -300,8 +311,8 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
     TWL_TRY(E.rec(1));
     TWL_TRY(E.rec(2));
     TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), prm->keep_frac, cache->max_pages_per_seq,
-                               at<int32_t>(ws, L.pphys),
-                               at<int32_t>(ws, L.pages), at<int32_t>(ws, L.pcnt), s));
+                               at<int32_t>(ws, L.pphys), at<int32_t>(ws, L.pages), at<int32_t>(ws, L.pcnt), qb,
+                               qdigits_of(ws, L), s));
     TWL_TRY(E.rec(3));
     cand.mode = kCandPages;
     cand.items = at<int32_t>(ws, L.pages);
@@ -309,17 +320,19 @@ twl_status decode_impl(const twl_cache* cache, const void* q, const twl_decode_p
     cand.max_items = cache->max_pages_per_seq;
     cand.phys = at<int32_t>(ws, L.pphys);
   } else {
-    for (int i = 0; i < 4; ++i) TWL_TRY(E.rec(i));
+    TWL_TRY(E.rec(0));
+    TWL_TRY(launch_qdigits(c, qb, qdigits_of(ws, L), s));
+    for (int i = 1; i < 4; ++i) TWL_TRY(E.rec(i));
     cand.mode = kCandAll;
   }
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   const bool csr = sel_tokens != nullptr;
-  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s,
+  TWL_TRY(estimate_topp(c, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s,
                         prm->topk));
   if (csr)
     TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
                             capacity, s));
-  TWL_TRY(attend_masked(c, qb, prm->sm_scale, ws, L, out, lse, E, s, prm->headwise != 0));
+  TWL_TRY(attend_masked(c, qb, prm->sm_scale, cand, ws, L, out, lse, E, s, prm->headwise != 0));
   return TWL_OK;
 }
 
@@ -366,7 +379,7 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   TWL_TRY(E.rec(0));
   TWL_TRY(launch_cluster_scores_topp(c, qb, prm->sm_scale, p1, prm->iters, static_cast<const uint16_t*>(centroids),
                                      csize, num_clusters, (int)cpad, at<float>(ws, L.logits), at<float>(ws, L.thr),
-                                     at<uint32_t>(ws, L.masks), s));
+                                     at<uint32_t>(ws, L.masks), qdigits_of(ws, L), s));
   TWL_TRY(E.rec(1));
   TWL_TRY(E.rec(2));
   // the kept clusters' token ranges, with the prefix sums and block starts the estimate resolves by
@@ -382,11 +395,11 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   cand.chunk_first = at<int32_t>(ws, L.cfirst);
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   const bool csr = sel_tokens != nullptr;
-  TWL_TRY(estimate_topp(c, qb, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s));
+  TWL_TRY(estimate_topp(c, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s));
   if (csr)
     TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
                             capacity, s));
-  TWL_TRY(attend_masked(c, qb, prm->sm_scale, ws, L, out, lse, E, s));
+  TWL_TRY(attend_masked(c, qb, prm->sm_scale, cand, ws, L, out, lse, E, s));
   return TWL_OK;
 }
 
@@ -452,7 +465,8 @@ twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_fr
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheView c = make_view(cache);
   TWL_TRY(launch_page_score(c, static_cast<const uint16_t*>(q), at<float>(ws, L.scores), s));
-  TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), keep_frac, max_keep, nullptr, page_ids, count, s));
+  TWL_TRY(launch_page_select(c, at<float>(ws, L.scores), keep_frac, max_keep, nullptr, page_ids, count, nullptr,
+                             QDigits{}, s));
   return TWL_OK;
 }
 
@@ -501,13 +515,13 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
   if (st != TWL_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const CacheView c = make_view(cache);
+  TWL_TRY(launch_qdigits(c, static_cast<const uint16_t*>(q), qdigits_of(ws, L), s));
   if (cv.mode == kCandRanges) {
     cv.range_prefix = at<int32_t>(ws, L.rpre);
     cv.chunk_first = at<int32_t>(ws, L.cfirst);
     TWL_TRY(launch_range_prefix(c, cv, at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
   }
-  TWL_TRY(estimate_topp(c, static_cast<const uint16_t*>(q), sm_scale, cv, ws, L, p, iters, threshold, mass, head_mask,
-                        mask_words, true, Events{}, s));
+  TWL_TRY(estimate_topp(c, sm_scale, cv, ws, L, p, iters, threshold, mass, head_mask, mask_words, true, Events{}, s));
   TWL_TRY(launch_csr_emit(c, at<int32_t>(ws, L.utok), at<int32_t>(ws, L.ucnt), (int)ncap, sel_indptr, sel_tokens,
                           capacity, s));
   return TWL_OK;
@@ -577,7 +591,8 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
   const CacheView c = make_view(cache);
   TWL_TRY(launch_cluster_scores_topp(c, static_cast<const uint16_t*>(q), sm_scale, p1, iters,
                                      static_cast<const uint16_t*>(centroids), csize, num_clusters, (int)cpad,
-                                     at<float>(ws, L.logits), at<float>(ws, L.thr), at<uint32_t>(ws, L.masks), s));
+                                     at<float>(ws, L.logits), at<float>(ws, L.thr), at<uint32_t>(ws, L.masks),
+                                     QDigits{}, s));
   return hip_status(launch_cluster_union(c, at<uint32_t>(ws, L.masks), (int)cpad, csize, coff, num_clusters, ranges,
                                          count, nullptr, nullptr, 0, s));
 }
@@ -615,7 +630,8 @@ twl_status twl_cluster_approx_unkept(const twl_cache* cache, const void* q, floa
   // the cluster stage again (the same kernels and inputs select the same clusters as the decode did)
   TWL_TRY(launch_cluster_scores_topp(c, static_cast<const uint16_t*>(q), sm_scale, p1, iters,
                                      static_cast<const uint16_t*>(centroids), csize, num_clusters, (int)cpad,
-                                     at<float>(ws, L.logits), at<float>(ws, L.thr), at<uint32_t>(ws, L.masks), s));
+                                     at<float>(ws, L.logits), at<float>(ws, L.thr), at<uint32_t>(ws, L.masks),
+                                     QDigits{}, s));
   return hip_status(launch_cluster_approx(c, at<float>(ws, L.logits), at<uint32_t>(ws, L.masks), (int)cpad, csize,
                                           num_clusters, vmean, out, lse, at<float>(ws, L.apart), s));
 }

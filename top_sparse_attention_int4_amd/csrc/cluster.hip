@@ -22,12 +22,14 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_cluster_score(CacheVie
                                                                         const uint16_t* __restrict__ cent,
                                                                         const int32_t* __restrict__ csize, int C,
                                                                         int cpad, float sm, float* __restrict__ lam,
-                                                                        int blocks_per_unit) {
+                                                                        int blocks_per_unit, QDigits qd) {
   constexpr int NT = 64 * (G > 4 ? G : 4);
   const int u = blockIdx.x / blocks_per_unit;
   const int blk = blockIdx.x - u * blocks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int hh = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the token-level estimate's query digits, shared out over the unit's blocks
+  if (qd.dig) unit_query_digits(q, c.Hq, c.kbits, b, h, G, NT, blk, blocks_per_unit, qd);
   __shared__ uint4 tile[64][17];  // 64 centroid rows of 16 x 16 B, padded by 16 B
   __shared__ float qs[G][kD];
   {
@@ -231,14 +233,14 @@ hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int
 
 hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
                                       const uint16_t* centroids, const int32_t* csize, int C, int cpad, float* lam,
-                                      float* thr, uint32_t* mask_ws, hipStream_t s) {
+                                      float* thr, uint32_t* mask_ws, const QDigits& qd, hipStream_t s) {
   const int bpu = cpad / 64;
   dim3 grid((unsigned)(c.B * c.Hkv * bpu));
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_cluster_score<1>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
-    case 2: hipLaunchKernelGGL(k_cluster_score<2>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
-    case 4: hipLaunchKernelGGL(k_cluster_score<4>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
-    case 8: hipLaunchKernelGGL(k_cluster_score<8>, grid, dim3(512), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu); break;
+    case 1: hipLaunchKernelGGL(k_cluster_score<1>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
+    case 2: hipLaunchKernelGGL(k_cluster_score<2>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
+    case 4: hipLaunchKernelGGL(k_cluster_score<4>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
+    case 8: hipLaunchKernelGGL(k_cluster_score<8>, grid, dim3(512), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -3,7 +3,8 @@
 //
 // Per head and 32-channel group g the query is held in fixed point, Q_c = rne(q_c 2^(20 - E_g)) with
 // E_g = floor(log2 max |q_c|) (|Q_c| <= 2088960; exact for channels within 2^12 of the largest, i.e.
-// for every channel of an ordinary bf16 query), as three int8 digits Q = 2^14 d2 + 2^7 d1 + d0, so
+// for every channel of an ordinary bf16 query), as three int8 digits Q = 2^14 d0 + 2^7 d1 + d2
+// (prepared once per step, see QDigits), so
 //   sum_{c in g} q~_c (code_c s_g + z_g) = s_g a_g + z_g b_g,  a_g = 2^(E_g-20) sum Q_c code_c,
 //   b_g = 2^(E_g-20) sum Q_c
 // has exact integer group sums in any order; then, in float64,
@@ -17,27 +18,17 @@
 // to each of four MFMAs; 8-bit codes go in as code - 128 with the columns started at 128 x the digit
 // sums), B = the query digits, one column per (group, head) and zero outside the lane's group, so
 // each output column accumulates one group of one head.  A wave takes 16-candidate tiles; the four
-// groups of a (candidate, head) then meet by two lane exchanges in the committed order.  The block
-// also records, per candidate, its token id and K/V row index, which the union of the kept sets then
-// gathers without further lookups.
+// groups of a (candidate, head) then meet by two DPP row rotations in the committed order.
+//
+// Candidates given as pages (the base selector's output) or as every token: a 16-candidate tile is
+// one page, so each wave finds its tiles' physical pages with scalar loads and works on its own (no
+// exchange, no barrier); the attention later derives the K/V rows from the same page lists.
+// Candidates given as token ranges (the cluster stage): the block resolves its candidates' rows
+// together (prefix sums of the range lengths, binary search) and records them for the attention.
 #include "twl_device.h"
 #include "twl_internal.h"
 
 namespace twl {
-
-// Map candidate index k of unit u to a logical token id for the "all" and "pages" forms; returns -1
-// when k is not a candidate.  (The ranges form is resolved block-wide inside the estimate.)
-__device__ __forceinline__ int cand_token(const CandView& cand, int u, int k, int n) {
-  if (cand.mode == kCandAll) return k < n ? k : -1;
-  const int P = (n + kPage - 1) / kPage;
-  const int cnt = clampi(cand.count[u], 0, cand.max_items);
-  const int pi = k >> 4;
-  if (pi >= cnt) return -1;
-  const int page = cand.items[(size_t)u * cand.max_items + pi];
-  if (page < 0 || page >= P) return -1;
-  const int t = page * kPage + (k & 15);
-  return t < n ? t : -1;
-}
 
 // Prefix sums of range lengths per unit (lengths < 0 count as 0), and for every block of kEstCands
 // candidates the index of the range holding its first candidate (count when past the last one).
@@ -125,34 +116,7 @@ __global__ __launch_bounds__(1024) void k_range_prefix(CacheView c, CandView can
     if ((int64_t)j * kEstCands >= carry) cf[j] = cnt;
 }
 
-// Token id and K/V row of candidate k (row -1 when k is not a candidate).  `cnt` is the unit's item
-// count for the page and range forms.
-__device__ __forceinline__ void cand_resolve(const CacheView& c, const CandView& cand, int u, int b, int h, int k,
-                                             int n, int cnt, int& tok, int& row) {
-  tok = -1;
-  row = -1;
-  if (cand.mode == kCandPages && cand.phys) {
-    // the id loads do not wait for the count: the index is clamped into the unit's row and the
-    // entry is discarded afterwards when it lies past the count
-    const int pi = k >> 4;
-    const size_t idx = (size_t)u * cand.max_items + min(pi, cand.max_items - 1);
-    const int page = cand.items[idx];
-    const int phys = cand.phys[idx];
-    const int t = page * kPage + (k & 15);
-    if (pi < cnt && page >= 0 && t < n) {
-      tok = t;
-      row = (phys * c.Hkv + h) * kPage + (k & 15);
-    }
-    return;
-  }
-  tok = cand_token(cand, u, k, n);
-  if (tok >= 0) row = (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15);
-}
-
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kQDigits = 3;     // int8 digits of the fixed-point query
-constexpr int kQFracBits = 20;  // Q = rne(q 2^(kQFracBits - E_g))
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -197,56 +161,242 @@ __device__ __forceinline__ long code_operand(const uint32_t (&w)[BITS], int j) {
   }
 }
 
-// NB batches of 64 candidates per block (64 * NB candidates, NB = 2 or 4): 4 NB tiles of 16, NB per wave.
-// BITS: code width (2, 4 or 8; rows of 16 * BITS bytes).
+// One wave's share of the contraction: its lane (kb, nn) holds the B operands of column nn = (group
+// gc, head ct GT + hl) of each column tile ct, and turns the MFMA results of a 16-candidate tile into
+// the logits of candidates 4 rg .. 4 rg + 3 for that column (rg = lane / 16).
+template <int G, int BITS>
+struct EstWave {
+  static constexpr int GT = G < 4 ? G : 4;  // heads per 16-column MFMA tile (4 groups x GT heads)
+  static constexpr int NTL = G / GT;        // column tiles
+  int lane, kb, nn, rg, gc, hl;
+  bool colok;
+  long Bop[NTL][kQDigits][4];
+  double cscale[NTL], bcol[NTL];  // 2^(E_g - 20) and b_g of the lane's column
+  int acc0[NTL][kQDigits];        // 8-bit codes: 128 x the digit sums (codes enter as code - 128)
+  double smd;
+
+  // the B operands and column constants of query rows bh0 .. bh0 + G - 1 (the unit's heads)
+  __device__ __forceinline__ void init(const QDigits& qd, size_t bh0, float sm) {
+    lane = threadIdx.x & 63;
+    kb = lane >> 4;
+    nn = lane & 15;
+    rg = lane >> 4;
+    gc = nn / GT;
+    hl = nn - gc * GT;
+    colok = nn < kGroups * GT;
+    smd = (double)sm;
+#pragma unroll
+    for (int ct = 0; ct < NTL; ++ct) {
+      const size_t gi = (bh0 + ct * GT + hl) * kGroups + (gc & 3);
+      const bool mine = colok && kb == gc;
+      const u32x4_t* dg = reinterpret_cast<const u32x4_t*>(qd.dig + gi * kQDigits * 32);
+#pragma unroll
+      for (int d = 0; d < kQDigits; ++d) {
+        const u32x4_t x0 = mine ? dg[2 * d] : u32x4_t{0u, 0u, 0u, 0u};
+        const u32x4_t x1 = mine ? dg[2 * d + 1] : u32x4_t{0u, 0u, 0u, 0u};
+        Bop[ct][d][0] = (long)((uint64_t)x0.x | ((uint64_t)x0.y << 32));
+        Bop[ct][d][1] = (long)((uint64_t)x0.z | ((uint64_t)x0.w << 32));
+        Bop[ct][d][2] = (long)((uint64_t)x1.x | ((uint64_t)x1.y << 32));
+        Bop[ct][d][3] = (long)((uint64_t)x1.z | ((uint64_t)x1.w << 32));
+      }
+      const int32_t* mt = qd.meta + gi * kQMeta;
+      const int E = colok ? mt[0] : 0;
+      cscale[ct] = colok ? ldexp(1.0, E - kQFracBits) : 0.0;
+      bcol[ct] = colok ? (double)mt[1] * cscale[ct] : 0.0;  // exact
+#pragma unroll
+      for (int d = 0; d < kQDigits; ++d) acc0[ct][d] = (BITS == 8 && colok) ? 128 * mt[2 + d] : 0;
+    }
+  }
+
+  // One tile: cw = this lane's code run (candidate nn, group kb), mw[e] = scale | zero << 16 of
+  // candidate 4 rg + e in group gc, ok[e] = whether that candidate exists.  Logits of the lane's four
+  // candidates for column tile ct land in lg[ct][e] (-inf for candidates that do not exist).
+  __device__ __forceinline__ void tile(const uint32_t (&cw)[BITS], const uint32_t (&mw)[4], const bool (&ok)[4],
+                                       float (&lg)[NTL][4]) const {
+    i32x4_t acc[NTL][kQDigits];
+#pragma unroll
+    for (int ct = 0; ct < NTL; ++ct)
+#pragma unroll
+      for (int d = 0; d < kQDigits; ++d) acc[ct][d] = i32x4_t{acc0[ct][d], acc0[ct][d], acc0[ct][d], acc0[ct][d]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long a = code_operand<BITS>(cw, j);
+#pragma unroll
+      for (int ct = 0; ct < NTL; ++ct)
+#pragma unroll
+        for (int d = 0; d < kQDigits; ++d)
+          acc[ct][d] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, Bop[ct][d][j], acc[ct][d], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NTL; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        double S;
+        if constexpr (BITS == 8) {
+          // up to 2^34 in magnitude: combined in float64 (exact below 2^53)
+          S = (double)acc[ct][0][e] * 16384.0 + (double)acc[ct][1][e] * 128.0 + (double)acc[ct][2][e];
+        } else {
+          // |S| <= 2^14 * 128 * 15 * 32 + (2^14 - 1) * 15 * 32 < 2^31: exact in int32
+          S = (double)(acc[ct][0][e] * 16384 + acc[ct][1][e] * 128 + acc[ct][2][e]);
+        }
+        const double s = (double)half_bits_to_float(mw[e] & 0xffffu);
+        const double z = (double)half_bits_to_float(mw[e] >> 16);
+        const double t = fma(s, S * cscale[ct], z * bcol[ct]);  // s a_g and z b_g are exact: one rounding
+        // groups meet along the row of 16 lanes (a rotation by 16 - N brings lane n + N to lane n):
+        // column gc GT + hl reads group gc + 1, then gc + 2
+        const double t01 = t + dpp_row_ror_f64<16 - GT>(t);          // (t0 + t1) in the lanes of group 0
+        const double r = t01 + dpp_row_ror_f64<16 - 2 * GT>(t01);    // (t0 + t1) + (t2 + t3)
+        lg[ct][e] = ok[e] ? (float)(smd * r) : -__builtin_inff();
+      }
+    }
+  }
+};
+
+// The block's largest logit per head over its waves' maxima (lanes of group 0 hold a head each).
+template <int G, int BITS>
+__device__ __forceinline__ void block_head_max(const EstWave<G, BITS>& ew, const float (&mx)[EstWave<G, BITS>::NTL],
+                                               float (*s_max)[G], int wv, float* pmax_row, int stride) {
+  constexpr int GT = EstWave<G, BITS>::GT, NTL = EstWave<G, BITS>::NTL;
+#pragma unroll
+  for (int ct = 0; ct < NTL; ++ct) {
+    float v = (ew.colok && ew.gc == 0) ? mx[ct] : -__builtin_inff();
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+#pragma unroll
+    for (int s = GT; s < 16; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
+    if (ew.lane < GT) s_max[wv][ct * GT + ew.lane] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const float m = fmaxf(fmaxf(s_max[0][threadIdx.x], s_max[1][threadIdx.x]),
+                          fmaxf(s_max[2][threadIdx.x], s_max[3][threadIdx.x]));
+    pmax_row[(size_t)threadIdx.x * stride] = m;
+  }
+}
+
+// Candidates as pages (MODE kCandPages, physical pages listed by the selector) or as every token
+// (kCandAll): NB 16-candidate tiles (pages) per wave, 4 waves per block, 64 NB candidates per block.
+template <int G, int NB, int BITS, int MODE>
+__global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd, float sm, CandView cand, int ncap,
+                                                        int chunks_per_unit, float* __restrict__ logits,
+                                                        int32_t* __restrict__ cand_tok, float* __restrict__ pmax,
+                                                        uint64_t* __restrict__ wstate, size_t wstate_words) {
+  using EW = EstWave<G, BITS>;
+  constexpr int GT = EW::GT, NTL = EW::NTL;
+  const int u = blockIdx.x / chunks_per_unit;
+  const int ck = blockIdx.x - u * chunks_per_unit;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (wstate) {
+    // clear the wide top-p state for the passes that follow this kernel
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < wstate_words; i += (size_t)gridDim.x * 256)
+      wstate[i] = 0ull;
+  }
+  // the wave's tiles: pages tp0 .. tp0 + NB - 1 of the unit's candidate list (wave-uniform values)
+  const int tp0 = ck * 4 * NB + wv * NB;
+  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+  int page[NB], phys[NB];
+  if constexpr (MODE == kCandPages) {
+    const int cnt = clampi(cand.count[u], 0, cand.max_items);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const size_t idx = (size_t)u * cand.max_items + min(tp0 + i, cand.max_items - 1);
+      page[i] = cand.items[idx];
+      if (tp0 + i >= cnt) page[i] = -1;
+      // the selector lists the physical pages too; a caller's page list is looked up in the table
+      phys[i] = cand.phys ? cand.phys[idx]
+                          : c.page_table[(size_t)b * c.maxP + clampi(page[i], 0, c.maxP - 1)];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      page[i] = tp0 + i;
+      phys[i] = c.page_table[(size_t)b * c.maxP + min(tp0 + i, c.maxP - 1)];
+    }
+  }
+  EW ew;
+  ew.init(qd, (size_t)b * c.Hq + (size_t)h * G, sm);
+  // a tile exists when its page does; its candidate k exists when page * 16 + k is a token
+  bool tok_ok[NB][4];
+  uint32_t cw[NB][BITS];
+  uint32_t mw[NB][4];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const bool pg_ok = page[i] >= 0 && page[i] * kPage < n && (unsigned)phys[i] < (unsigned)c.nphys;
+    const int row0 = pg_ok ? (phys[i] * c.Hkv + h) * kPage : 0;
+    load_codes<BITS>(c.k4 + (size_t)(row0 + ew.nn) * (16 * BITS), ew.kb, cw[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int slot = 4 * ew.rg + e;
+      mw[i][e] = c.k4_meta[(size_t)(row0 + slot) * kGroups + (ew.gc & 3)];
+      tok_ok[i][e] = pg_ok && page[i] * kPage + slot < n;
+    }
+  }
+  if (cand_tok && ew.kb == 0) {
+    // token ids of the candidates, for the union lists (lane nn of each tile)
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const bool pg_ok = page[i] >= 0 && page[i] * kPage < n && (unsigned)phys[i] < (unsigned)c.nphys;
+      const int t = page[i] * kPage + ew.nn;
+      cand_tok[(size_t)u * ncap + (size_t)(tp0 + i) * kPage + ew.nn] = (pg_ok && t < n) ? t : -1;
+    }
+  }
+  float mx[NTL];
+#pragma unroll
+  for (int ct = 0; ct < NTL; ++ct) mx[ct] = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    float lg[NTL][4];
+    ew.tile(cw[i], mw[i], tok_ok[i], lg);
+#pragma unroll
+    for (int ct = 0; ct < NTL; ++ct) {
+      mx[ct] = fmaxf(fmaxf(mx[ct], fmaxf(lg[ct][0], lg[ct][1])), fmaxf(lg[ct][2], lg[ct][3]));
+      if (ew.colok && ew.gc == 0) {
+        const int k = (tp0 + i) * kPage + 4 * ew.rg;
+        *reinterpret_cast<float4*>(logits + ((size_t)b * c.Hq + (size_t)h * G + ct * GT + ew.hl) * ncap + k) =
+            make_float4(lg[ct][0], lg[ct][1], lg[ct][2], lg[ct][3]);
+      }
+    }
+  }
+  if (pmax) {
+    __shared__ float s_max[4][G];
+    block_head_max<G, BITS>(ew, mx, s_max, wv, pmax + ((size_t)b * c.Hq + (size_t)h * G) * chunks_per_unit + ck,
+                            chunks_per_unit);
+  }
+}
+
+// Candidates as token ranges: NB batches of 64 candidates per block (64 NB candidates); the block
+// resolves every candidate's token and K/V row once (batch w by wave w), then each wave takes tiles
+// wv, wv + 4, ... of the block.
 template <int G, int NB, int BITS>
-__global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* __restrict__ q, float sm,
-                                                  CandView cand, int ncap, int chunks_per_unit,
-                                                  float* __restrict__ logits, int32_t* __restrict__ cand_tok,
-                                                  int32_t* __restrict__ cand_row, float* __restrict__ pmax,
-                                                  uint64_t* __restrict__ wstate, size_t wstate_words) {
+__global__ __launch_bounds__(256) void k_estimate_ranges(CacheView c, QDigits qd, float sm, CandView cand, int ncap,
+                                                         int chunks_per_unit, float* __restrict__ logits,
+                                                         int32_t* __restrict__ cand_tok,
+                                                         int32_t* __restrict__ cand_row, float* __restrict__ pmax,
+                                                         uint64_t* __restrict__ wstate, size_t wstate_words) {
+  using EW = EstWave<G, BITS>;
   constexpr int NC = 64 * NB;
-  constexpr int GT = G < 4 ? G : 4;  // heads per 16-column MFMA tile (4 groups x GT heads)
-  constexpr int NTL = G / GT;        // column tiles
+  constexpr int GT = EW::GT, NTL = EW::NTL;
   const int u = blockIdx.x / chunks_per_unit;
   const int ck = blockIdx.x - u * chunks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   __shared__ int s_row[NB][64];
-  // query digits (Q = 2^14 [0] + 2^7 [1] + [2]), channel 8j + w of a group at byte 8j + perm(w), the
-  // order in which the nibbles of 4 code bytes are unpacked (low nibbles of bytes 0..3, then high)
-  __shared__ __align__(16) int8_t s_qd[kQDigits][G][kD];
-  __shared__ int s_qe[G][kGroups];   // group exponents E_g
-  __shared__ int s_qs[G][kGroups];   // sum_{c in g} Q_c (|.| < 2^26)
-  __shared__ int s_qds[kQDigits][G][kGroups];  // per digit, its sum over the group (8-bit codes: the offset of 128)
-  __shared__ float s_max[4][G];
+  __shared__ int s_pre[NC + 1];
+  __shared__ int s_beg[NC + 1];
   if (wstate) {
-    // clear the wide top-p state for the passes that follow this kernel
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < wstate_words; i += (size_t)gridDim.x * 256)
       wstate[i] = 0ull;
   }
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int cnt = (cand.mode == kCandAll) ? 0 : clampi(cand.count[u], 0, cand.max_items);
+  const int cnt = clampi(cand.count[u], 0, cand.max_items);
   const int k0 = ck * NC;
-  // the query: lane pr < 4 G of wave 0 turns the 32 channels of (head pr / 4, group pr % 4) into fixed
-  // point on its own (no cross-lane reductions); its 64 bytes are read first
-  const bool qlane = wv == 0 && lane < kGroups * G;
-  const int qh = qlane ? lane >> 2 : 0, qg = lane & 3;
-  u32x4_t qraw[4];
-  if (qlane) {
-    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(q + ((size_t)b * c.Hq + (size_t)h * G + qh) * kD + qg * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qraw[i] = qp[i];
-  }
-
-  // ---- candidate resolution: wave w resolves batches w, w + 4, ... (token id and K/V row); the
-  // rows meet in LDS so each is resolved once
-  if (cand.mode == kCandRanges) {
-    // The block's candidates lie in the ranges r0..rmax; their prefix sums and first tokens are
-    // staged in LDS when they fit, and every lane searches there.
-    __shared__ int s_pre[NC + 1];
-    __shared__ int s_beg[NC + 1];
+  EW ew;
+  ew.init(qd, (size_t)b * c.Hq + (size_t)h * G, sm);
+  // ---- candidate resolution: the block's candidates lie in the ranges r0..rmax; their prefix sums
+  // and first tokens are staged in LDS when they fit, and every lane searches there
+  {
     const int32_t* pre = cand.range_prefix + (size_t)u * (cand.max_items + 1);
     const int nchunk = ncap / kEstCands;
     const int j0 = k0 / kEstCands, j1 = (k0 + NC - 1) / kEstCands;
@@ -290,185 +440,69 @@ __global__ __launch_bounds__(256) void k_estimate(CacheView c, const uint16_t* _
         if (p0 <= k) t = beg + (k - p0);
       }
       const int tok = (t >= 0 && t < n) ? t : -1;
-      const int row = tok >= 0 ? (c.page_table[(size_t)b * c.maxP + (tok >> 4)] * c.Hkv + h) * kPage + (tok & 15) : -1;
+      int row = -1;
+      if (tok >= 0) {
+        const int ph = c.page_table[(size_t)b * c.maxP + (tok >> 4)];
+        if ((unsigned)ph < (unsigned)c.nphys) row = (ph * c.Hkv + h) * kPage + (tok & 15);
+      }
       s_row[bt][lane] = row;
-      if (cand_tok) cand_tok[(size_t)u * ncap + k] = tok;
-      cand_row[(size_t)u * ncap + k] = row;
-    }
-  } else {
-    for (int bt = wv; bt < NB; bt += kGroups) {
-      const int k = k0 + 64 * bt + lane;
-      int tok, row;
-      cand_resolve(c, cand, u, b, h, k, n, cnt, tok, row);
-      s_row[bt][lane] = row;
-      if (cand_tok) cand_tok[(size_t)u * ncap + k] = tok;
+      if (cand_tok) cand_tok[(size_t)u * ncap + k] = row >= 0 ? tok : -1;
       cand_row[(size_t)u * ncap + k] = row;
     }
   }
-  // ---- the fixed-point query (wave 0), ordered before the code loads by the barrier below
-  if (qlane) {
-    float x[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t wq[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[8 * i + 2 * k] = bf16_lo(wq[k]);
-        x[8 * i + 2 * k + 1] = bf16_hi(wq[k]);
-      }
-    }
-    float m = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < 32; ++cc) m = fmaxf(m, fabsf(x[cc]));
-    int E = 0;
-    if (m > 0.f) E = max((int)(__float_as_uint(m) >> 23) - 127, -100);
-    int qs = 0, ds[kQDigits] = {0, 0, 0};
-    uint32_t dw[kQDigits][8];  // the digits' bytes, 4 per word, in the unpack order of the codes
-#pragma unroll
-    for (int d = 0; d < kQDigits; ++d)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) dw[d][k] = 0u;
-#pragma unroll
-    for (int cc = 0; cc < 32; ++cc) {
-      // |x| < 2^(E+1), so |Q| <= (2 - 2^-7) 2^20 (exact in float32 before and after the rounding)
-      const int Qv = (int)rintf(ldexpf(x[cc], kQFracBits - E));
-      const int d2 = Qv >> 14;            // floor(Q / 2^14) in [-128, 127]
-      const int rm = Qv - d2 * 16384;     // in [0, 2^14)
-      const int dg[kQDigits] = {d2, rm >> 7, rm & 127};
-      qs += Qv;
-      const int w = cc & 7;
-      const int pos = (cc & ~7) + (BITS == 8 ? w : ((w & 1) ? 4 + (w >> 1) : (w >> 1)));
-#pragma unroll
-      for (int d = 0; d < kQDigits; ++d) {
-        ds[d] += dg[d];
-        dw[d][pos >> 2] |= (uint32_t)(dg[d] & 0xff) << (8 * (pos & 3));
-      }
-    }
-#pragma unroll
-    for (int d = 0; d < kQDigits; ++d) {
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_qd[d][qh][qg * 32]);
-      dst[0] = u32x4_t{dw[d][0], dw[d][1], dw[d][2], dw[d][3]};
-      dst[1] = u32x4_t{dw[d][4], dw[d][5], dw[d][6], dw[d][7]};
-    }
-    s_qe[qh][qg] = E;
-    s_qs[qh][qg] = qs;
-    if constexpr (BITS == 8) {
-#pragma unroll
-      for (int d = 0; d < kQDigits; ++d) s_qds[d][qh][qg] = ds[d];
-    }
-  }
-  __syncthreads();  // rows and query digits in LDS
+  __syncthreads();  // rows in LDS
 
   // ---- this wave's tiles (wv, wv + 4, ...): code and scale/zero loads all in flight together
-  const int kb = lane >> 4, nn = lane & 15, rg = lane >> 4;
-  const int gc = nn / GT, hl = nn - gc * GT;
-  const bool colok = nn < kGroups * GT;
   uint32_t cw[NB][BITS];
   uint32_t mw[NB][4];
-  int rw[NB][4];
+  bool ok[NB][4];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int ti = wv + 4 * i;
-    const int ra = (&s_row[0][0])[16 * ti + nn];
-    load_codes<BITS>(c.k4 + (size_t)max(ra, 0) * (16 * BITS), kb, cw[i]);
+    const int ra = (&s_row[0][0])[16 * ti + ew.nn];
+    load_codes<BITS>(c.k4 + (size_t)max(ra, 0) * (16 * BITS), ew.kb, cw[i]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      rw[i][e] = (&s_row[0][0])[16 * ti + 4 * rg + e];
-      mw[i][e] = c.k4_meta[(size_t)max(rw[i][e], 0) * kGroups + (gc & 3)];
+      const int rwe = (&s_row[0][0])[16 * ti + 4 * ew.rg + e];
+      mw[i][e] = c.k4_meta[(size_t)max(rwe, 0) * kGroups + (ew.gc & 3)];
+      ok[i][e] = rwe >= 0;
     }
   }
-
-  // ---- B operands, the same in every wave: lane (kb, nn) holds column nn = (group gc, head ct GT + hl)
-  long Bop[NTL][kQDigits][4];
-  double cscale[NTL], bcol[NTL];  // 2^(E_g - 20) and b_g of the lane's column
-#pragma unroll
-  for (int ct = 0; ct < NTL; ++ct) {
-    const int hh = ct * GT + hl;
-#pragma unroll
-    for (int d = 0; d < kQDigits; ++d)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        Bop[ct][d][j] = (colok && kb == gc) ? *reinterpret_cast<const long*>(&s_qd[d][hh][32 * kb + 8 * j]) : 0l;
-    cscale[ct] = colok ? ldexp(1.0, s_qe[hh][gc] - kQFracBits) : 0.0;
-    bcol[ct] = colok ? (double)s_qs[hh][gc] * cscale[ct] : 0.0;  // exact
-  }
-  // 8-bit codes enter the contraction as code - 128: each column starts at 128 x its digit sum
-  int acc0[NTL][kQDigits];
-#pragma unroll
-  for (int ct = 0; ct < NTL; ++ct) {
-    const int hh = ct * GT + hl;
-#pragma unroll
-    for (int d = 0; d < kQDigits; ++d) acc0[ct][d] = (BITS == 8 && colok) ? 128 * s_qds[d][hh][gc] : 0;
-  }
-  const double smd = (double)sm;
   float mx[NTL];
 #pragma unroll
   for (int ct = 0; ct < NTL; ++ct) mx[ct] = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int ti = wv + 4 * i;
-    i32x4_t acc[NTL][kQDigits];
-#pragma unroll
-    for (int ct = 0; ct < NTL; ++ct)
-#pragma unroll
-      for (int d = 0; d < kQDigits; ++d) acc[ct][d] = i32x4_t{acc0[ct][d], acc0[ct][d], acc0[ct][d], acc0[ct][d]};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long a = code_operand<BITS>(cw[i], j);
-#pragma unroll
-      for (int ct = 0; ct < NTL; ++ct)
-#pragma unroll
-        for (int d = 0; d < kQDigits; ++d)
-          acc[ct][d] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, Bop[ct][d][j], acc[ct][d], 0, 0, 0);
-    }
-    // lane (rg, nn) holds the group sums of candidates 16 ti + 4 rg + e for column nn
+    float lg[NTL][4];
+    ew.tile(cw[i], mw[i], ok[i], lg);
 #pragma unroll
     for (int ct = 0; ct < NTL; ++ct) {
-      float lg4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        double S;
-        if constexpr (BITS == 8) {
-          // up to 2^34 in magnitude: combined in float64 (exact below 2^53)
-          S = (double)acc[ct][0][e] * 16384.0 + (double)acc[ct][1][e] * 128.0 + (double)acc[ct][2][e];
-        } else {
-          // |S| <= 2^14 * 128 * 15 * 32 + (2^14 - 1) * 15 * 32 < 2^31: exact in int32
-          S = (double)(acc[ct][0][e] * 16384 + acc[ct][1][e] * 128 + acc[ct][2][e]);
-        }
-        const double av = S * cscale[ct];  // exact (a power of two)
-        const double s = (double)half_bits_to_float(mw[i][e] & 0xffffu);
-        const double z = (double)half_bits_to_float(mw[i][e] >> 16);
-        const double t = fma(s, av, z * bcol[ct]);  // s a_g and z b_g are exact: one rounding
-        const double t01 = t + __shfl_xor(t, GT);      // groups (0, 1) and (2, 3)
-        const double r = t01 + __shfl_xor(t01, 2 * GT);  // (t0 + t1) + (t2 + t3)
-        lg4[e] = (rw[i][e] >= 0) ? (float)(smd * r) : -__builtin_inff();
-        mx[ct] = fmaxf(mx[ct], lg4[e]);
-      }
-      if (colok && gc == 0) {
-        const int k = k0 + 16 * ti + 4 * rg;
-        *reinterpret_cast<float4*>(logits + ((size_t)b * c.Hq + (size_t)h * G + ct * GT + hl) * ncap + k) =
-            make_float4(lg4[0], lg4[1], lg4[2], lg4[3]);
+      mx[ct] = fmaxf(fmaxf(mx[ct], fmaxf(lg[ct][0], lg[ct][1])), fmaxf(lg[ct][2], lg[ct][3]));
+      if (ew.colok && ew.gc == 0) {
+        const int k = k0 + 16 * ti + 4 * ew.rg;
+        *reinterpret_cast<float4*>(logits + ((size_t)b * c.Hq + (size_t)h * G + ct * GT + ew.hl) * ncap + k) =
+            make_float4(lg[ct][0], lg[ct][1], lg[ct][2], lg[ct][3]);
       }
     }
   }
   if (pmax) {
-    // the block's largest logit per head: over the wave's lanes of the head, then over the waves
-#pragma unroll
-    for (int ct = 0; ct < NTL; ++ct) {
-      float v = (colok && gc == 0) ? mx[ct] : -__builtin_inff();
-      v = fmaxf(v, __shfl_xor(v, 16));
-      v = fmaxf(v, __shfl_xor(v, 32));
-#pragma unroll
-      for (int s = GT; s < 16; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
-      if (lane < GT) s_max[wv][ct * GT + lane] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < G) {
-      const float m = fmaxf(fmaxf(s_max[0][threadIdx.x], s_max[1][threadIdx.x]),
-                            fmaxf(s_max[2][threadIdx.x], s_max[3][threadIdx.x]));
-      pmax[((size_t)b * c.Hq + (size_t)h * G + threadIdx.x) * chunks_per_unit + ck] = m;
-    }
+    __shared__ float s_max[4][G];
+    block_head_max<G, BITS>(ew, mx, s_max, wv, pmax + ((size_t)b * c.Hq + (size_t)h * G) * chunks_per_unit + ck,
+                            chunks_per_unit);
   }
+}
+
+// The query digits of every (sequence, query head) row: 8 (row, group) pairs per 256-thread block.
+__global__ __launch_bounds__(256) void k_qdigits(CacheView c, const uint16_t* __restrict__ q, QDigits qd) {
+  const int pr = blockIdx.x * 8 + ((int)threadIdx.x >> 5);
+  if (pr < c.B * c.Hq * kGroups) query_digits_half(q, pr >> 2, pr & 3, c.kbits, qd.dig, qd.meta);
+}
+
+hipError_t launch_qdigits(const CacheView& c, const uint16_t* q, const QDigits& qd, hipStream_t s) {
+  const int pairs = c.B * c.Hq * kGroups;
+  hipLaunchKernelGGL(k_qdigits, dim3((unsigned)((pairs + 7) / 8)), dim3(256), 0, s, c, q, qd);
+  return hipGetLastError();
 }
 
 hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, int32_t* chunk_first,
@@ -484,19 +518,27 @@ int est_batches(int64_t ncap, int64_t units) {
   return (ncap > kNarrowMaxCands || ncap * units >= ((int64_t)1 << 19)) ? 4 : 2;
 }
 
-hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
+hipError_t launch_estimate(const CacheView& c, const QDigits& qd, float sm, const CandView& cand, int ncap,
                            float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s) {
   const int nb = est_batches(ncap, (int64_t)c.B * c.Hkv);
   if (ncap % (64 * nb) || ncap % kEstCands) return hipErrorInvalidValue;
+  if (cand.mode == kCandRanges && !cand_row) return hipErrorInvalidValue;
   const int cpu = ncap / (64 * nb);
   dim3 grid((unsigned)(c.B * c.Hkv * cpu));
   float* pmax = wide ? wide->pmax : nullptr;
   uint64_t* wst = wide ? wide->state : nullptr;
   const size_t wwords = wide ? (size_t)c.B * c.Hq * kWideStateWords : 0;
-#define TWL_EST_G(GG, NB, BB)                                                                                 \
-  case GG:                                                                                                    \
-    hipLaunchKernelGGL((k_estimate<GG, NB, BB>), grid, dim3(256), 0, s, c, q, sm, cand, ncap, cpu, logits,    \
-                       cand_tok, cand_row, pmax, wst, wwords);                                               \
+#define TWL_EST_G(GG, NB, BB)                                                                                    \
+  case GG:                                                                                                       \
+    if (cand.mode == kCandRanges)                                                                                \
+      hipLaunchKernelGGL((k_estimate_ranges<GG, NB, BB>), grid, dim3(256), 0, s, c, qd, sm, cand, ncap, cpu,     \
+                         logits, cand_tok, cand_row, pmax, wst, wwords);                                        \
+    else if (cand.mode == kCandPages)                                                                            \
+      hipLaunchKernelGGL((k_estimate_pages<GG, NB, BB, kCandPages>), grid, dim3(256), 0, s, c, qd, sm, cand,     \
+                         ncap, cpu, logits, cand_tok, pmax, wst, wwords);                                        \
+    else                                                                                                         \
+      hipLaunchKernelGGL((k_estimate_pages<GG, NB, BB, kCandAll>), grid, dim3(256), 0, s, c, qd, sm, cand, ncap, \
+                         cpu, logits, cand_tok, pmax, wst, wwords);                                              \
     break;
 #define TWL_EST_NB(NB, BB)                  \
   case NB:                                  \

@@ -143,6 +143,7 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
   const int blk = blockIdx.x - u * blocks_per_unit;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int lane = threadIdx.x;
+
   __shared__ uint4 tile[64 * RS];
   __shared__ float4 qp[G][kD / 4], qn[G][kD / 4];
   // the page-table entry of this lane's page, in flight with the sequence length and q
@@ -234,7 +235,8 @@ constexpr int kSelRegKeys = 8192;  // pages per unit held in registers (8 per th
 // read their scores from global memory in every pass.
 __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* __restrict__ scores,
                                                       float keep_frac, int max_keep, int32_t* page_phys,
-                                                      int32_t* page_ids, int32_t* count) {
+                                                      int32_t* page_ids, int32_t* count,
+                                                      const uint16_t* __restrict__ q, QDigits qd) {
   constexpr int NT = 1024, NW = NT / 64;
   const int u = blockIdx.x;
   const int b = u / c.Hkv;
@@ -251,6 +253,8 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
     v[r] = (i < c.maxP) ? sc[i] : 0.f;
     ptv[r] = (phys_out && i < c.maxP) ? pt[i] : 0;
   }
+  // while the scores arrive: the unit's query digits for the estimate (one pair per half wave)
+  if (qd.dig) unit_query_digits(q, c.Hq, c.kbits, b, u - b * c.Hkv, c.G, NT, 0, 1, qd);
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
   int K = 0;
@@ -482,9 +486,9 @@ hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* score
 }
 
 hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep, int32_t* page_phys,
-                              int32_t* page_ids, int32_t* count, hipStream_t s) {
+                              int32_t* page_ids, int32_t* count, const uint16_t* q, const QDigits& qd, hipStream_t s) {
   hipLaunchKernelGGL(k_page_select, dim3((unsigned)(c.B * c.Hkv)), dim3(1024), 0, s, c, scores, keep_frac,
-                     max_keep, page_phys, page_ids, count);
+                     max_keep, page_phys, page_ids, count, q, qd);
   return hipGetLastError();
 }
 

@@ -208,16 +208,15 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   }
 }
 
-// One block per unit: OR the unit's G head masks and write the kept token ids (ascending), their K/V
-// row indices and the count.  First every thread forms the union of its mask words (all loads in
+// One block per unit: OR the unit's G head masks and write the kept token ids (ascending) and the
+// count.  First every thread forms the union of its mask words (all loads in
 // flight together) and the block scans their popcounts into per-word output offsets in LDS; then
-// thread t of pass j handles candidate j*1024 + t, so the gathers of the ids and rows the estimate
-// recorded, and the writes of the kept ones, are coalesced.
+// thread t of pass j handles candidate j*1024 + t, so the gathers of the ids the estimate recorded,
+// and the writes of the kept ones, are coalesced.
 template <int E, int G>
 __global__ __launch_bounds__(1024) void k_union(CacheView c, const uint32_t* __restrict__ mask_ws,
-                                                const int32_t* __restrict__ cand_tok,
-                                                const int32_t* __restrict__ cand_row, int ncap, int32_t* union_tok,
-                                                int32_t* union_row, int32_t* union_cnt) {
+                                                const int32_t* __restrict__ cand_tok, int ncap, int32_t* union_tok,
+                                                int32_t* union_cnt) {
   constexpr int NT = 1024, NW = NT / 64;
   constexpr int MW = E * 32;                 // mask words per head (ncap / 32)
   constexpr int WPT = (MW + NT - 1) / NT;    // words per thread
@@ -254,9 +253,7 @@ __global__ __launch_bounds__(1024) void k_union(CacheView c, const uint32_t* __r
   }
   __syncthreads();
   const int32_t* ct = cand_tok + (size_t)u * ncap;
-  const int32_t* cr = cand_row + (size_t)u * ncap;
   int32_t* out = union_tok + (size_t)u * ncap;
-  int32_t* rows = union_row + (size_t)u * ncap;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const int k = j * NT + tid;
@@ -265,7 +262,6 @@ __global__ __launch_bounds__(1024) void k_union(CacheView c, const uint32_t* __r
     if ((x >> bit) & 1u) {
       const int pos = woff[k >> 5] + __popc(x & ((1u << bit) - 1u));
       out[pos] = ct[k];
-      rows[pos] = cr[k];
     }
   }
   if (tid == 0) union_cnt[u] = total;
@@ -336,14 +332,14 @@ hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float 
   return hipGetLastError();
 }
 
-hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, const int32_t* cand_row,
-                        int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, hipStream_t s) {
+hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, int ncap,
+                        int32_t* union_tok, int32_t* union_cnt, hipStream_t s) {
   const int E = ncap / kToppThreads;
   dim3 ugrid((unsigned)(c.B * c.Hkv)), block(kToppThreads);
 #define TWL_UNION_G(EE, GG)                                                                                \
   case GG:                                                                                                 \
-    hipLaunchKernelGGL((k_union<EE, GG>), ugrid, block, 0, s, c, mask_ws, cand_tok, cand_row, ncap,      \
-                       union_tok, union_row, union_cnt);                                                 \
+    hipLaunchKernelGGL((k_union<EE, GG>), ugrid, block, 0, s, c, mask_ws, cand_tok, ncap, union_tok,     \
+                       union_cnt);                                                                       \
     break;
 #define TWL_UNION_CASE(EE)        \
   case EE:                        \

@@ -352,16 +352,14 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const f
   }
 }
 
-// Per (unit, chunk): kept candidates of the union in ascending order, with the token ids and K/V
-// rows the estimate recorded; chunk 0 also writes each head's threshold and kept mass.
+// Per (unit, chunk): kept candidates of the union in ascending order, with the token ids the estimate
+// recorded; chunk 0 also writes each head's threshold and kept mass.
 template <int G>
 __global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int ncap, const uint64_t* __restrict__ state,
                                                             const uint32_t* __restrict__ uwords,
                                                             const int32_t* __restrict__ chunk_cnt,
                                                             const int32_t* __restrict__ cand_tok,
-                                                            const int32_t* __restrict__ cand_row,
                                                             int32_t* __restrict__ union_tok,
-                                                            int32_t* __restrict__ union_row,
                                                             int32_t* __restrict__ union_cnt, float* mass) {
   constexpr int WPB = kWideChunk / 32;  // union words per chunk
   __shared__ uint32_t uw[WPB];
@@ -404,7 +402,6 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int nca
       const int pos = base + woff[kl >> 5] + __popc(wd & ((1u << bit) - 1u));
       const size_t k = (size_t)ch * kWideChunk + kl;
       union_tok[ub + pos] = cand_tok[ub + k];
-      union_row[ub + pos] = cand_row[ub + k];
     }
   }
 }
@@ -441,9 +438,8 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits,
   return hipGetLastError();
 }
 
-hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
-                            int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, float* mass,
-                            hipStream_t s) {
+hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, int ncap,
+                            int32_t* union_tok, int32_t* union_cnt, float* mass, hipStream_t s) {
   if (ncap % kWideChunk) return hipErrorInvalidValue;
   const int nch = ncap / kWideChunk;
   const unsigned ugrid = (unsigned)(c.B * c.Hkv * nch);
@@ -451,7 +447,7 @@ hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t*
 #define TWL_WIDE_E(GG)                                                                                      \
   case GG:                                                                                                  \
     hipLaunchKernelGGL(k_wide_emit<GG>, dim3(ugrid), blk, 0, s, c, ncap, wd.state, wd.uwords, wd.chunk_cnt,  \
-                       cand_tok, cand_row, union_tok, union_row, union_cnt, mass);                         \
+                       cand_tok, union_tok, union_cnt, mass);                                             \
     break;
   switch (c.G) {
     TWL_WIDE_E(1)

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "twl_internal.h"
+
 namespace twl {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -23,13 +25,14 @@ __device__ __forceinline__ uint32_t float_to_half_bits(float f) {
 // ---- DPP reductions: within each 16-lane row (xor 1, xor 2, rotate 4, rotate 8), then the four
 // row results are read from lanes 0/16/32/48 and combined as (r0 + r1) + (r2 + r3).  The order is
 // fixed by lane position, so the result is the same on every run; it is uniform across the wave.
+// (These patterns give every lane a source, so no old value is kept: plain DPP moves.)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xf, 0xf, false);
 }
 constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
@@ -282,6 +285,70 @@ __device__ __forceinline__ float exp_diff(float a, float b) {
 
 // Clamp helpers
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// DPP row rotation of a 64-bit value: within each row of 16 lanes, rotated right by N (lane n receives
+// lane (n - N) mod 16).
+// (Every lane has a source inside its row, so no lane keeps an old value: a plain DPP move.)
+template <int N>
+__device__ __forceinline__ double dpp_row_ror_f64(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, 0x120 + N, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), 0x120 + N, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// The estimate's fixed-point query for channel group g of query row bh, written by 32 lanes (one half
+// of a wave, lane l = channel 32 g + l):  E_g = floor(log2 max |q_c|) (>= -100; 0 for an all-zero
+// group), Q_c = rne(q_c 2^(20 - E_g)), |Q_c| <= (2 - 2^-7) 2^20, as the digits Q = 2^14 d0 + 2^7 d1 + d2
+// (d0 in [-128, 127], d1 and d2 in [0, 127]); byte pos of a digit row is channel 8 j + w of the group
+// with pos = 8 j + perm(w), perm the order in which the code unpack feeds the matrix cores (the low
+// nibbles or 2-bit fields of four code bytes first, then the high ones; identity for 8-bit codes).
+__device__ __forceinline__ void query_digits_half(const uint16_t* __restrict__ q, int bh, int g, int kbits,
+                                                  uint8_t* __restrict__ dig, int32_t* __restrict__ meta) {
+  const int l = threadIdx.x & 31;
+  const float x = __uint_as_float((uint32_t)q[(size_t)bh * kD + 32 * g + l] << 16);
+  float m = fabsf(x);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
+  int E = 0;
+  if (m > 0.f) E = max((int)(__float_as_uint(m) >> 23) - 127, -100);
+  const int Q = (int)rintf(ldexpf(x, kQFracBits - E));
+  const int d0 = Q >> 14;           // floor(Q / 2^14)
+  const int rm = Q - d0 * 16384;    // in [0, 2^14)
+  const int d1 = rm >> 7, d2 = rm & 127;
+  const int w = l & 7;
+  const int pos = (l & ~7) + (kbits == 8 ? w : ((w & 1) ? 4 + (w >> 1) : (w >> 1)));
+  uint8_t* row = dig + (size_t)(bh * 4 + g) * kQDigits * 32;
+  row[pos] = (uint8_t)(d0 & 0xff);
+  row[32 + pos] = (uint8_t)d1;
+  row[64 + pos] = (uint8_t)d2;
+  int sq = Q, s0 = d0, s1 = d1, s2 = d2;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    sq += __shfl_xor(sq, o, 32);
+    s0 += __shfl_xor(s0, o, 32);
+    s1 += __shfl_xor(s1, o, 32);
+    s2 += __shfl_xor(s2, o, 32);
+  }
+  if (l == 0) {
+    int32_t* mt = meta + (size_t)(bh * 4 + g) * kQMeta;
+    mt[0] = E;
+    mt[1] = sq;
+    mt[2] = s0;
+    mt[3] = s1;
+    mt[4] = s2;
+  }
+}
+
+// The query digit rows of the G heads of unit (b, h), shared out over the unit's blocks: block blk of
+// bpu (nthreads each, a multiple of 32) takes the (head, group) pairs blk * halves + i, i < halves,
+// then every bpu * halves-th pair after them.
+__device__ __forceinline__ void unit_query_digits(const uint16_t* __restrict__ q, int Hq, int kbits, int b, int h,
+                                                  int G, int nthreads, int blk, int bpu, const QDigits& qd) {
+  const int halves = nthreads >> 5;
+  for (int pr = blk * halves + ((int)threadIdx.x >> 5); pr < 4 * G; pr += bpu * halves)
+    query_digits_half(q, b * Hq + h * G + (pr >> 2), pr & 3, kbits, qd.dig, qd.meta);
+}
 
 // ---- radix form of the top-p threshold search (shared by the block and the multi-block kernels) ----
 // Masses are 64-bit fixed point, floor(w * 2^40): exact integer sums in any order.

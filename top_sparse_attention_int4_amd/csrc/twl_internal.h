@@ -58,6 +58,20 @@ struct WideWs {
   uint32_t* keys;      // [B*Hq][ncap] keys of the candidates in the first level's chosen bin
 };
 constexpr int kEstCands = 256;  // candidate block of the range starts (chunk_first); divides the estimate's blocks
+
+// The estimate's fixed-point query, prepared once per step (by the page selection or the cluster
+// scores of each unit, or by k_qdigits): per (sequence, query head) row bh and 32-channel group g,
+//   dig[((bh * 4 + g) * 3 + d) * 32 + pos]  digit d (0: the 2^14 digit, 1: 2^7, 2: units) of the
+//                                           channel at byte pos (the order in which the code unpack
+//                                           feeds the matrix cores: a permutation within each 8)
+//   meta[(bh * 4 + g) * 8 + {0, 1, 2, 3, 4}] E_g, sum_c Q_c, and the three digits' sums over the group
+constexpr int kQDigits = 3;     // int8 digits of Q = 2^14 d0 + 2^7 d1 + d2
+constexpr int kQFracBits = 20;  // Q_c = rne(q_c 2^(kQFracBits - E_g))
+constexpr int kQMeta = 8;       // ints of meta per (row, group)
+struct QDigits {
+  uint8_t* dig;   // [B*Hq][4][3][32]
+  int32_t* meta;  // [B*Hq][4][8]
+};
 // 64-candidate batches per estimate block for a candidate capacity and unit count (2 or 8)
 int est_batches(int64_t ncap, int64_t units);
 
@@ -75,13 +89,18 @@ struct ListView {
 hipError_t launch_quantize(const CacheView& c, const int32_t* tok_begin, const int32_t* tok_end,
                            int span_pages, hipStream_t s);
 hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* scores, hipStream_t s);
+// the query digits of every (sequence, query head) alone
+hipError_t launch_qdigits(const CacheView& c, const uint16_t* q, const QDigits& qd, hipStream_t s);
+// page top-K; with qd.dig non-null each unit's block also writes the unit's query digits
 hipError_t launch_page_select(const CacheView& c, const float* scores, float keep_frac, int max_keep, int32_t* page_phys,
-                              int32_t* page_ids, int32_t* count, hipStream_t s);
+                              int32_t* page_ids, int32_t* count, const uint16_t* q, const QDigits& qd, hipStream_t s);
 hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, int32_t* chunk_first,
                                int nchunk, hipStream_t s);
 // wide: when non-null, the estimate also writes the per-block logit maxima and clears the wide state;
-// cand_tok may be null when no union list is emitted afterwards
-hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, int ncap,
+// cand_tok may be null when no union list is emitted afterwards; cand_row (the K/V row of every
+// candidate) is written for the ranges form only -- for pages and all tokens the attention derives
+// rows from the page lists
+hipError_t launch_estimate(const CacheView& c, const QDigits& qd, float sm, const CandView& cand, int ncap,
                            float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s);
 // wide top-p: histogram passes and masks (union bitmap in wd.uwords); the emit kernel writes the
 // compacted union lists and the threshold/mass outputs
@@ -89,15 +108,15 @@ hipError_t launch_estimate(const CacheView& c, const uint16_t* q, float sm, cons
 // (needed by head_mask, the mass output and the union lists); otherwise union words only
 hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits, int ncap, float p, int iters,
                             float* threshold, uint32_t* head_mask, int mask_words, bool full, hipStream_t s);
-hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, const int32_t* cand_row,
-                            int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, float* mass,
-                            hipStream_t s);
+hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, int ncap,
+                            int32_t* union_tok, int32_t* union_cnt, float* mass, hipStream_t s);
 hipError_t launch_topp_weighted(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
                                 uint32_t* mask_ws, const int32_t* mult, int mult_stride, hipStream_t s);
-// cluster scores (size-weighted logits) and the per-head cluster top-p (head masks in mask_ws)
+// cluster scores (size-weighted logits) and the per-head cluster top-p (head masks in mask_ws); with
+// qd.dig non-null the score blocks also write the query digits of the token-level estimate
 hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
                                       const uint16_t* centroids, const int32_t* csize, int C, int cpad, float* lam,
-                                      float* thr, uint32_t* mask_ws, hipStream_t s);
+                                      float* thr, uint32_t* mask_ws, const QDigits& qd, hipStream_t s);
 // union of a unit's head masks -> kept ranges (first token, length) and count; with prefix non-NULL
 // also the ranges' prefix sums [U][C + 1] and the range of each 256-candidate block [U][nchunk]
 // optional approximation of unkept clusters: mean value rows [B*Hkv][C][128], then the merge into
@@ -115,8 +134,8 @@ hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int
 // topk > 0: keep each head's topk largest weights (ties kept) instead of its top-p set
 hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
                        float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, int topk, hipStream_t s);
-hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, const int32_t* cand_row,
-                        int ncap, int32_t* union_tok, int32_t* union_row, int32_t* union_cnt, hipStream_t s);
+hipError_t launch_union(const CacheView& c, const uint32_t* mask_ws, const int32_t* cand_tok, int ncap,
+                        int32_t* union_tok, int32_t* union_cnt, hipStream_t s);
 hipError_t launch_csr_emit(const CacheView& c, const int32_t* union_tok, const int32_t* union_cnt, int ncap,
                            int32_t* indptr, int32_t* tokens, int64_t capacity, hipStream_t s);
 // tokens per attention chunk for an upper bound of the total selected tokens
@@ -126,7 +145,10 @@ int attn_chunk_tokens(int64_t total_upper, int group);
 struct MaskView {
   const uint32_t* head_masks;   // [B*Hq][ncap/32] per-head bitmaps (OR-ed over the group), or
   const uint32_t* union_words;  // [B*Hkv][ncap/32] union bitmaps (used when non-null)
-  const int32_t* cand_row;      // [B*Hkv][ncap] K/V row of each candidate
+  int cand_mode;                // kCandPages / kCandAll: rows from the page lists; kCandRanges: cand_row
+  const int32_t* cand_row;      // [B*Hkv][ncap] K/V row of each candidate (ranges)
+  const int32_t* page_phys;     // [B*Hkv][page_stride] physical page of each kept page (pages)
+  int page_stride;
   int64_t ncap;
 };
 // one workgroup per chunk slot: slot k of unit u covers list entries [k*chunk_tokens, (k+1)*chunk_tokens)
