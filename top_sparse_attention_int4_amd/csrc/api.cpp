@@ -99,7 +99,7 @@ struct Layout {
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
          ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
-         wkeys = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
+         wkeys = 0, wrcnt = 0, wmass = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
 };
 
 // ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
@@ -152,7 +152,9 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
     L->wstate = take((size_t)BH * kWideStateWords * 8);
     L->wcnt = take((size_t)U * (ncap / kWideChunk) * 4);
     L->uwords = take((size_t)U * (ncap / 32) * 4);
-    L->wkeys = take((size_t)BH * ncap * 4);
+    L->wkeys = take((size_t)BH * ncap * 8);
+    L->wrcnt = take((size_t)BH * (ncap / kWideChunk) * 4);
+    L->wmass = take((size_t)BH * (ncap / kWideChunk) * 8);
   }
   L->total = off;
   return true;
@@ -190,7 +192,7 @@ QDigits qdigits_of(void* ws, const Layout& L) { return QDigits{at<uint8_t>(ws, L
 
 WideWs wide_of(void* ws, const Layout& L) {
   return WideWs{at<float>(ws, L.pmax), at<uint64_t>(ws, L.wstate), at<int32_t>(ws, L.wcnt), at<uint32_t>(ws, L.uwords),
-                at<uint32_t>(ws, L.wkeys)};
+                at<uint64_t>(ws, L.wkeys), at<int32_t>(ws, L.wrcnt), at<uint64_t>(ws, L.wmass)};
 }
 
 // Estimate, top-p and (when `with_union`) the compacted GQA union of every unit, the narrow or the

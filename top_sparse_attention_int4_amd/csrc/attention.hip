@@ -379,18 +379,22 @@ __global__ __launch_bounds__(NR * 32) void k_merge(CacheView c, ListView L, bool
   constexpr size_t kStep = (size_t)G * kPartStride;
   float M = -__builtin_inff(), Ls = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = r; k0 < nch; k0 += NR * UNR) {
+  for (int k0 = r; k0 < slots; k0 += NR * UNR) {
     float mk[UNR], lk[UNR];
     float4 ok[UNR];
+    // every load unconditional (a chunk past the unit's slots reads slot 0's record, and any chunk
+    // past the count is dropped after), so the row's loads are all in flight at once
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
       const int k = k0 + NR * i;
-      const bool v = k < nch;
-      const float* pk = base + (size_t)(v ? k : 0) * kStep;
-      mk[i] = v ? pk[0] : -__builtin_inff();
-      lk[i] = v ? pk[1] : 0.f;
-      ok[i] = v ? reinterpret_cast<const float4*>(pk + 4)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float* pk = base + (size_t)(k < slots ? k : 0) * kStep;
+      mk[i] = pk[0];
+      lk[i] = pk[1];
+      ok[i] = reinterpret_cast<const float4*>(pk + 4)[j];
     }
+#pragma unroll
+    for (int i = 0; i < UNR; ++i)
+      if (k0 + NR * i >= nch) mk[i] = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
       if (mk[i] != -__builtin_inff()) {

@@ -7,24 +7,32 @@
 // of the mass per value of a digit of the key decides several steps at once.  Only weights >= 2^-40
 // carry fixed-point mass, so the digits run over keys from that floor: 11 bits of (key - floor) >> 18,
 // then bits 17..9 and 8..0, which give the exact largest threshold T with mass{e >= T} >= p * Z, so
-// the kept set {e >= T} is the converged bisection's.  With fewer steps requested the threshold keeps only its top `iters`
-// bits, the point a shorter bisection stops at: a superset that still reaches p.
+// the kept set {e >= T} is the converged bisection's.  With fewer steps requested the threshold keeps
+// only its top `iters` bits, the point a shorter bisection stops at: a superset that still reaches p.
+// The first digit fixes key bits 30..18, so up to 13 steps the threshold is known once the first
+// level is resolved.
 //
 // Masses are 64-bit fixed point, floor(e * 2^40) (e <= 1, at most 2^22 candidates per head), so the
 // histograms can be summed across blocks with integer atomics in any order and still give the same
 // result on every run.  Truncation costs at most 2^-40 per weight, below 2.4e-7 of Z for 2^18
 // candidates.
 //
+// The weights are never stored: each pass forms e = exp(l - M) from the estimate's logits with the
+// same instructions, so both passes see the same values, and the logits are read twice in all.
+//
 // Kernels:
-//   k_wide_hist1    M from the estimate's per-block maxima; e written over the logits; histogram of
-//                   the first digit (four 4096-candidate chunks per block, the next chunk's loads in flight
-//                   while one is processed, one flush of integer atomics to the global histogram)
-//   k_wide_collect  resolve the first digit; the keys of the candidates inside its bin appended to a
-//                   per-head buffer (one atomic per block and chunk; their order does not matter)
-//   k_wide_finish   one block per head: bits 17..9 and 8..0 from LDS histograms over the collected keys
-//                   (the bisection steps left), the threshold
-//   k_wide_mask     per (unit, chunk): head masks, kept mass, union words and their count
-//   k_wide_emit     per (unit, chunk): compaction of the union (ascending ids and K/V rows), outputs
+//   k_wide_hist1   M from the estimate's per-block maxima (recorded for the later passes); histogram
+//                  of the first digit (four 4096-candidate chunks per block, the next chunk's loads in
+//                  flight while one is processed, one flush of integer atomics to the global histogram)
+//   k_wide_level1  one wave per head: the first digit resolved once (bin, remainder, and the key
+//                  bounds the mask pass sorts by)
+//   k_wide_mask    per (unit, chunk): weights above the chosen bin kept (head masks, kept mass, union
+//                  words and their count), those inside it recorded with their index in the chunk's
+//                  own record range
+//   k_wide_finish  one block per head: bits 17..9 and 8..0 from LDS histograms over the recorded keys
+//                  (the bisection steps left), the threshold, and the recorded candidates that reach it
+//                  set in the union words and head masks by atomic ORs
+//   k_wide_emit    per (unit, chunk): compaction of the union (ascending ids)
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -32,16 +40,19 @@ namespace twl {
 
 namespace {
 
-constexpr int NT = kWideThreads;
+constexpr int NT = kWideThreads;        // threads of the emit pass
 constexpr int NW = NT / 64;
-constexpr int EPT = kWideChunk / NT;  // candidates per thread
-constexpr int QPT = EPT / 4;            // of them as float4 (the histogram passes read 16 B per lane)
+constexpr int EPT = kWideChunk / NT;    // candidates per thread of a chunk there
+constexpr int HT = kWidePassThreads;    // threads of the histogram and mask passes
+constexpr int HW = HT / 64;
+constexpr int HEPT = kWideChunk / HT;   // candidates per thread of a chunk there
+constexpr int HQPT = HEPT / 4;          // of them as float4 (16 B per lane)
 
-// the thread's candidates of a chunk as float4: candidates 4 (j NT + t) .. + 3
-__device__ __forceinline__ void load_chunk4(const float* x, float (&v)[EPT]) {
+// the thread's candidates of a chunk as float4: candidates 4 (j HT + t) .. + 3
+__device__ __forceinline__ void load_chunk4(const float* x, float (&v)[HEPT]) {
 #pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const float4 q = reinterpret_cast<const float4*>(x)[j * NT + threadIdx.x];
+  for (int j = 0; j < HQPT; ++j) {
+    const float4 q = reinterpret_cast<const float4*>(x)[j * HT + threadIdx.x];
     v[4 * j] = q.x;
     v[4 * j + 1] = q.y;
     v[4 * j + 2] = q.z;
@@ -49,9 +60,9 @@ __device__ __forceinline__ void load_chunk4(const float* x, float (&v)[EPT]) {
   }
 }
 __device__ __forceinline__ void flush_hist(const uint64_t* h, int nbins, uint64_t* g_fine, uint64_t* g_coarse) {
-  for (int i = threadIdx.x; i < nbins; i += NT)
+  for (int i = threadIdx.x; i < nbins; i += HT)
     if (h[i]) atomicAdd((unsigned long long*)&g_fine[i], (unsigned long long)h[i]);
-  for (int cb = threadIdx.x; cb < nbins / 32; cb += NT) {
+  for (int cb = threadIdx.x; cb < nbins / 32; cb += HT) {
     uint64_t s = 0;
 #pragma unroll 8
     for (int i = 0; i < 32; ++i) s += h[32 * cb + i];
@@ -71,35 +82,46 @@ __device__ __forceinline__ uint32_t nibbles_to_word(uint32_t nib) {
 
 }  // namespace
 
-__global__ __launch_bounds__(kWideThreads) void k_wide_hist1(float* __restrict__ logits, int ncap,
+// The weight of a logit: exp(l - M), or -1 for a candidate that does not exist (l = -inf) and for a
+// head without candidates.  Every pass forms it with these same instructions.
+__device__ __forceinline__ float wide_weight(float l, float M) {
+  return (l == -__builtin_inff() || M == -__builtin_inff()) ? -1.f : exp_diff(l, M);
+}
+
+// Bisection steps decided by the first digit alone (it fixes key bits 30..18).
+constexpr int kWideKnownSteps = 13;
+
+// The threshold of a resolved first level when at most kWideKnownSteps steps are asked for: the
+// bin's lowest key with the bits below the top `iters` cleared (every key of the bin shares them).
+__device__ __forceinline__ uint32_t wide_known_threshold(uint32_t b1, int iters) {
+  return (kKeyFloor + (b1 << 18)) & ~((1u << (31 - iters)) - 1u);
+}
+
+__global__ __launch_bounds__(HT) void k_wide_hist1(const float* __restrict__ logits, int ncap,
                                                              const float* __restrict__ pmax, int npm,
                                                              uint64_t* __restrict__ state) {
   __shared__ uint64_t h[2048];
-  __shared__ float red[2 * NW * 4];
-  BlockReduce<NW> br{red};
+  __shared__ float red[2 * HW * 4];
+  BlockReduce<HW> br{red};
   const int nbk = ncap / kWideAlign;
   const int bh = blockIdx.x / nbk, bk = blockIdx.x - bh * nbk;
-  float* lg = logits + (size_t)bh * ncap + (size_t)bk * kWideAlign;
-  float v[2][EPT];
+  const float* lg = logits + (size_t)bh * ncap + (size_t)bk * kWideAlign;
+  uint64_t* st = state + (size_t)bh * kWideStateWords;
+  float v[2][HEPT];
   load_chunk4(lg, v[0]);  // in flight while M is formed
-  for (int i = threadIdx.x; i < 2048; i += NT) h[i] = 0ull;
+  for (int i = threadIdx.x; i < 2048; i += HT) h[i] = 0ull;
   float m = -__builtin_inff();
-  for (int i = threadIdx.x; i < npm; i += NT) m = fmaxf(m, pmax[(size_t)bh * npm + i]);
+  for (int i = threadIdx.x; i < npm; i += HT) m = fmaxf(m, pmax[(size_t)bh * npm + i]);
   const float M = br.max(m);  // (its barrier also orders the clearing of h)
+  if (bk == 0 && threadIdx.x == 0) st[kWideSM] = (uint64_t)__float_as_uint(M);
 #pragma unroll
   for (int c = 0; c < kWideBlockChunks; ++c) {
     // the next chunk's logits in flight while this one is weighted
     if (c + 1 < kWideBlockChunks) load_chunk4(lg + (size_t)(c + 1) * kWideChunk, v[(c + 1) & 1]);
-    float (&x)[EPT] = v[c & 1];
+    const float (&x)[HEPT] = v[c & 1];
 #pragma unroll
-    for (int j = 0; j < EPT; ++j)
-      x[j] = (x[j] == -__builtin_inff() || M == -__builtin_inff()) ? -1.f : exp_diff(x[j], M);
-    float4* out = reinterpret_cast<float4*>(lg + (size_t)c * kWideChunk);
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) out[j * NT + threadIdx.x] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const float e = x[j];
+    for (int j = 0; j < HEPT; ++j) {
+      const float e = wide_weight(x[j], M);
       if (e >= 0.f) {
         const uint64_t f = to_fix(e);
         if (f) atomicAdd((unsigned long long*)&h[key_d1(__float_as_uint(e))], (unsigned long long)f);
@@ -107,7 +129,6 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_hist1(float* __restrict__
     }
   }
   __syncthreads();
-  uint64_t* st = state + (size_t)bh * kWideStateWords;
   flush_hist(h, 2048, st + kWideH1, st + kWideC1);
 }
 
@@ -132,78 +153,285 @@ __device__ __forceinline__ void wide_level1(const uint64_t* st, float p, int& mo
   wide_find(st + kWideH1, st + kWideC1, 64, target, b1, rem1);
 }
 
-__global__ __launch_bounds__(kWideThreads) void k_wide_collect(const float* __restrict__ w, int ncap, float p,
-                                                               uint64_t* __restrict__ state,
-                                                               uint32_t* __restrict__ keys) {
-  __shared__ int s_mode, s_b1;
-  __shared__ int scan_sm[NW + 1];
-  __shared__ int s_base;
-  const int nbk = ncap / kWideAlign;
-  const int bh = blockIdx.x / nbk, bk = blockIdx.x - bh * nbk;
-  uint64_t* st = state + (size_t)bh * kWideStateWords;
-  const float* x0 = w + (size_t)bh * ncap + (size_t)bk * kWideAlign;
-  uint32_t* kout = keys + (size_t)bh * ncap;
-  float v[2][EPT];
-  load_chunk4(x0, v[0]);  // in flight during the resolution
-  if (threadIdx.x < 64) {
-    int mode, b1;
-    uint64_t Z, rem1;
-    wide_level1(st, p, mode, Z, b1, rem1);
-    if (threadIdx.x == 0) {
-      s_mode = mode;
-      s_b1 = b1;
-      if (bk == 0) {
-        st[kWideSZ] = Z;
-        st[kWideSMode] = (uint64_t)mode;
-        st[kWideSB1] = (uint64_t)b1;
-        st[kWideSR1] = rem1;
+// float32 bounds of a float64 value: the least float >= x and the greatest float <= x
+__device__ __forceinline__ float f32_at_least(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = nextafterf(f, __builtin_inff());
+  return f;
+}
+__device__ __forceinline__ float f32_at_most(double x) {
+  float f = (float)x;
+  if ((double)f > x) f = nextafterf(f, -__builtin_inff());
+  return f;
+}
+
+// One wave per head: the first level resolved once -- total mass, mode, bin and remainder -- and the
+// two keys the mask pass sorts by: a weight whose key reaches `keep` is kept for sure (every key above
+// the bin, or the whole threshold when the first level fixes it), one from `lo` up to `keep` lies
+// in the bin and is recorded for the finishing pass.  Mode 1 keeps every weight (keep = lo = 0).
+// The logit bounds A and B decide without the weight: a logit >= A has a weight >= keep and one
+// below B a weight below lo, for any weight within a relative 2^-16 of exp(l - M) (the weight's
+// own error is below 2e-7); only logits in [B, A) need it.  With keep = 0 every finite logit is kept.
+__global__ __launch_bounds__(64) void k_wide_level1(float p, int iters, uint64_t* __restrict__ state) {
+  uint64_t* st = state + (size_t)blockIdx.x * kWideStateWords;
+  int mode, b1;
+  uint64_t Z, rem1;
+  wide_level1(st, p, mode, Z, b1, rem1);
+  if (threadIdx.x == 0) {
+    uint32_t keep = 0u, lo = 0u;
+    if (mode == 0) {
+      if (iters <= kWideKnownSteps) {
+        keep = lo = wide_known_threshold((uint32_t)b1, iters);
+      } else {
+        lo = kKeyFloor + ((uint32_t)b1 << 18);
+        keep = lo + (1u << 18);
       }
     }
-  }
-  __syncthreads();
-  if (s_mode != 0) return;
-  const uint32_t b1 = (uint32_t)s_b1;
-#pragma unroll
-  for (int c = 0; c < kWideBlockChunks; ++c) {
-    if (c + 1 < kWideBlockChunks) load_chunk4(x0 + (size_t)(c + 1) * kWideChunk, v[(c + 1) & 1]);
-    const float (&x)[EPT] = v[c & 1];
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) cnt += (x[j] >= 0.f && key_d1(__float_as_uint(x[j])) == b1) ? 1 : 0;
-    int total;
-    const int off = block_excl_scan<NW>(cnt, scan_sm, &total);
-    if (total == 0) continue;  // uniform
-    if (threadIdx.x == 0)
-      s_base = (int)atomicAdd((unsigned long long*)&st[kWideNKeys], (unsigned long long)total);
-    __syncthreads();
-    int pos = s_base + off;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j)
-      if (x[j] >= 0.f && key_d1(__float_as_uint(x[j])) == b1) kout[pos++] = __float_as_uint(x[j]);
+    const float M = __uint_as_float((uint32_t)st[kWideSM]);
+    float A = -3.402823466e38f, B = -3.402823466e38f;
+    if (keep > 0u && M != -__builtin_inff()) {
+      constexpr double kMargin = 1.0 / 65536.0;
+      A = f32_at_least((double)M + log((double)__uint_as_float(keep)) + kMargin);
+      B = f32_at_most((double)M + log((double)__uint_as_float(lo)) - kMargin);
+    }
+    st[kWideSKeep] = keep;
+    st[kWideSLo] = lo;
+    st[kWideSA] = (uint64_t)__float_as_uint(A);
+    st[kWideSB] = (uint64_t)__float_as_uint(B);
+    st[kWideSZ] = Z;
+    st[kWideSMode] = (uint64_t)mode;
+    st[kWideSB1] = (uint64_t)b1;
+    st[kWideSR1] = rem1;
   }
 }
 
-// One block per head: the remaining 20 key bits from LDS histograms of the collected keys (all in the
-// first level's bin), then the threshold.
-__global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint64_t* __restrict__ state,
-                                                      const uint32_t* __restrict__ keys, float* threshold) {
-  constexpr int FT = 1024, FU = 8;
+// Per (unit, chunk): every candidate of the chunk and head is kept when its key reaches the head's
+// `keep` key, recorded (key, index) when it lies from `lo` up to there.  Writes the union words (and
+// with FULL the head masks, the chunk's kept mass per head and its union count) of what is sure; the
+// finishing pass adds the recorded candidates that reach the threshold.  Without FULL no kept mass is
+// needed, so the logit bounds decide most candidates and only those between them get their weight.
+// The per-head words are uniform loads, so they do not wait behind the chunk's logits.
+template <int G, bool FULL>
+__global__ __launch_bounds__(HT) void k_wide_mask(CacheView c, const float* __restrict__ logits, int ncap,
+                                                  const uint64_t* __restrict__ state, uint64_t* __restrict__ keys,
+                                                  int32_t* __restrict__ rec_cnt, uint32_t* __restrict__ head_mask,
+                                                  int mask_words, uint32_t* __restrict__ uwords,
+                                                  int32_t* __restrict__ chunk_cnt, uint64_t* __restrict__ chunk_mass) {
+  static_assert(HEPT == 4, "one float4 per thread and head");
+  constexpr int NS = 4 * G;  // slots of a thread: bit 4 hh + e is candidate 4 t + e of head hh
+  __shared__ int s_cnt[HW];
+  __shared__ int s_wrec[HW][G];  // records per wave and head
+  __shared__ uint64_t s_wmass[FULL ? HW : 1][G];
+  const int nch = ncap / kWideChunk;
+  const int u = blockIdx.x / nch, ch = blockIdx.x - u * nch;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const size_t bh0 = (size_t)b * c.Hq + (size_t)h * G;
+  float v[NS];  // logits, then the weights of the recorded slots
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const float4 q = reinterpret_cast<const float4*>(logits + (bh0 + hh) * ncap + (size_t)ch * kWideChunk)[threadIdx.x];
+    v[4 * hh] = q.x;
+    v[4 * hh + 1] = q.y;
+    v[4 * hh + 2] = q.z;
+    v[4 * hh + 3] = q.w;
+  }
+  float M[G], A[G], B[G];
+  uint32_t keep_key[G], lo_key[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint64_t* st = state + (bh0 + hh) * kWideStateWords;
+    M[hh] = __uint_as_float((uint32_t)st[kWideSM]);
+    keep_key[hh] = (uint32_t)st[kWideSKeep];
+    lo_key[hh] = (uint32_t)st[kWideSLo];
+    A[hh] = __uint_as_float((uint32_t)st[kWideSA]);
+    B[hh] = __uint_as_float((uint32_t)st[kWideSB]);
+  }
+  uint32_t keep = 0u, rec = 0u;
+  uint64_t kept[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) kept[hh] = 0ull;
+  if constexpr (FULL) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int hh = i >> 2;
+      const float w = wide_weight(v[i], M[hh]);
+      const uint32_t k = __float_as_uint(w);
+      const bool valid = w >= 0.f;
+      const bool kp = valid && k >= keep_key[hh];
+      const bool rc = valid && !kp && k >= lo_key[hh];
+      if (kp) kept[hh] += to_fix(w);
+      keep |= (kp ? 1u : 0u) << i;
+      rec |= (rc ? 1u : 0u) << i;
+      v[i] = w;
+    }
+  } else {
+    uint32_t unc = 0u;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int hh = i >> 2;
+      keep |= (v[i] >= A[hh] ? 1u : 0u) << i;
+      unc |= (v[i] < A[hh] && v[i] >= B[hh] ? 1u : 0u) << i;
+    }
+    // the exact weights between the bounds, one slot at a time per lane
+    while (unc) {
+      const int i = __builtin_ctz(unc);
+      unc &= unc - 1u;
+      float l = 0.f, m = 0.f;
+      uint32_t kk = 0u, lk = 0u;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) l = (s2 == i) ? v[s2] : l;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const bool mine = (i >> 2) == hh;
+        m = mine ? M[hh] : m;
+        kk = mine ? keep_key[hh] : kk;
+        lk = mine ? lo_key[hh] : lk;
+      }
+      const float w = wide_weight(l, m);
+      const uint32_t k = __float_as_uint(w);
+      if (w >= 0.f && k >= kk) {
+        keep |= 1u << i;
+      } else if (w >= 0.f && k >= lk) {
+        rec |= 1u << i;
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) v[s2] = (s2 == i) ? w : v[s2];
+      }
+    }
+  }
+  // union words (and head masks): lanes 8 q .. 8 q + 7 hold the 32 candidates of word q
+  const int MW = ncap / 32;
+  const int wd = ch * (kWideChunk / 32) + wv * 8 + (lane >> 3);
+  uint32_t unib = 0u;
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint32_t nib = (keep >> (4 * hh)) & 15u;
+    unib |= nib;
+    if (FULL && head_mask) {
+      const uint32_t word = nibbles_to_word(nib);
+      if ((lane & 7) == 0 && wd < mask_words) head_mask[(bh0 + hh) * mask_words + wd] = word;
+    }
+  }
+  const uint32_t uword = nibbles_to_word(unib);
+  if ((lane & 7) == 0) uwords[(size_t)u * MW + wd] = uword;
+  // the candidates inside the bins: (key << 32 | index) from slot ch * kWideChunk of the head's
+  // records, in thread order (a chunk records at most kWideChunk), and the chunk's count
+  int nrec[G], incl[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    nrec[hh] = __popc((rec >> (4 * hh)) & 15u);
+    incl[hh] = wave_incl_scan(nrec[hh]);
+    if (lane == 63) s_wrec[wv][hh] = incl[hh];
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < HW; ++w) t += s_wrec[w][threadIdx.x];
+    rec_cnt[(bh0 + threadIdx.x) * nch + ch] = t;
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    if (s_wrec[wv][hh] == 0) continue;  // wave-uniform
+    int pos = incl[hh] - nrec[hh];
+    for (int w = 0; w < wv; ++w) pos += s_wrec[w][hh];
+    uint64_t* kr = keys + (bh0 + hh) * ncap + (size_t)ch * kWideChunk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((rec >> (4 * hh + e)) & 1u) {
+        const uint32_t idx = (uint32_t)(ch * kWideChunk + 4 * threadIdx.x + e);
+        kr[pos++] = ((uint64_t)__float_as_uint(v[4 * hh + e]) << 32) | idx;
+      }
+    }
+  }
+  if (!FULL) return;
+  // the chunk's kept mass per head and its union count: wave sums, then one store each
+  const int cnt = wave_sum_int(__popc(unib));
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const uint64_t sm = wave_suffix_u64(kept[hh]);
+    if (lane == 0) s_wmass[wv][hh] = sm;
+  }
+  if (lane == 0) s_cnt[wv] = cnt;
+  __syncthreads();
+  if (threadIdx.x < G) {
+    uint64_t t = 0ull;
+#pragma unroll
+    for (int w = 0; w < HW; ++w) t += s_wmass[w][threadIdx.x];
+    chunk_mass[(bh0 + threadIdx.x) * nch + ch] = t;
+  }
+  if (threadIdx.x == 0) {
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < HW; ++i) t += s_cnt[i];
+    chunk_cnt[(size_t)u * nch + ch] = t;
+  }
+}
+
+// One block per head: the remaining 18 key bits from LDS histograms of the recorded keys (all in the
+// first level's bin), the threshold, and the recorded candidates that reach it added to the union
+// words (FULL: also to the head masks, kept mass and union counts).
+__global__ __launch_bounds__(1024) void k_wide_finish(int G, int ncap, int iters, bool full,
+                                                      uint64_t* __restrict__ state, const uint64_t* __restrict__ keys,
+                                                      const int32_t* __restrict__ rec_cnt,
+                                                      const uint64_t* __restrict__ chunk_mass, float* threshold,
+                                                      uint32_t* __restrict__ uwords, int32_t* __restrict__ chunk_cnt,
+                                                      uint32_t* __restrict__ head_mask, int mask_words) {
+  constexpr int FT = 1024, FU = 8, FW = FT / 64;
+  constexpr int kMaxChunks = kWideMaxCands / kWideChunk;
+  static_assert(kMaxChunks <= FT, "one chunk count per thread");
   __shared__ uint64_t h2[512], h3[512], cs[64];
+  __shared__ int s_off[kMaxChunks + 1];  // first record of each chunk in the head's record order
+  __shared__ int scan_sm[FW + 1];
   __shared__ int s_bin;
   __shared__ uint64_t s_rem;
+  __shared__ uint64_t s_mass[FW];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nch = ncap / kWideChunk;
+  // kept mass (FULL): the mask pass's chunk sums, plus the recorded candidates added below
+  uint64_t mass = 0ull;
+  if (full && tid < nch) mass = chunk_mass[(size_t)bh * nch + tid];
   uint64_t* st = state + (size_t)bh * kWideStateWords;
-  const uint32_t* kin = keys + (size_t)bh * ncap;
+  const uint64_t* kin = keys + (size_t)bh * ncap;
   const uint64_t mode = st[kWideSMode], Z = st[kWideSZ];
   const uint32_t b1 = (uint32_t)st[kWideSB1];
   const uint64_t rem1 = st[kWideSR1];
-  const int n = (int)min(st[kWideNKeys], (uint64_t)ncap);
   uint32_t T = 0u;
-  if (mode == 0ull) {
+  if (mode == 0ull && iters <= kWideKnownSteps) {
+    T = wide_known_threshold(b1, iters);  // nothing was recorded
+  } else if (mode == 0ull) {
     if (tid < 512) {
       h2[tid] = 0ull;
       h3[tid] = 0ull;
     }
+    int n;
+    {
+      const int cnt = tid < nch ? clampi(rec_cnt[(size_t)bh * nch + tid], 0, kWideChunk) : 0;
+      const int off = block_excl_scan<FW>(cnt, scan_sm, &n);
+      if (tid < nch) s_off[tid] = off;
+      if (tid == 0) s_off[nch] = n;
+    }
+    __syncthreads();
+    // record i of the head: chunk s = the last with s_off[s] <= i, then slot i - s_off[s] of it
+    auto record = [&](int i) -> uint64_t {
+      if (i >= n) return ~0ull;  // a weight key never has the sign bit set
+      int lo = 0, hi = nch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= i) lo = mid; else hi = mid;
+      }
+      return kin[(size_t)lo * kWideChunk + (i - s_off[lo])];
+    };
+    // up to FT * FU records stay in registers for all three passes (record e * FT + tid here)
+    const bool resident = n <= FT * FU;
+    uint64_t rr[FU];
+#pragma unroll
+    for (int e = 0; e < FU; ++e) rr[e] = record(e * FT + tid);
+    auto records = [&](int i0, uint64_t (&r)[FU]) {
+      if (resident) return;
+#pragma unroll
+      for (int e = 0; e < FU; ++e) r[e] = record(i0 + e * FT + tid);
+    };
     __syncthreads();
     auto coarse = [&](const uint64_t* h, int ncoarse) {
       if (tid < ncoarse * 16) {
@@ -212,19 +440,15 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
       }
       __syncthreads();
     };
-    // bits 17..9 of every collected key
+    // bits 17..9 of every recorded key
     for (int i0 = 0; i0 < n; i0 += FT * FU) {
-      uint32_t kk[FU];
+      records(i0, rr);
 #pragma unroll
       for (int e = 0; e < FU; ++e) {
-        const int i = i0 + e * FT + tid;
-        kk[e] = (i < n) ? kin[i] : 0xFFFFFFFFu;  // a weight key never has the sign bit set
-      }
-#pragma unroll
-      for (int e = 0; e < FU; ++e) {
-        if (kk[e] != 0xFFFFFFFFu) {
-          const uint64_t f = to_fix(__uint_as_float(kk[e]));
-          if (f) atomicAdd((unsigned long long*)&h2[key_d2(kk[e])], (unsigned long long)f);
+        const uint32_t kk = (uint32_t)(rr[e] >> 32);
+        if (rr[e] != ~0ull) {
+          const uint64_t f = to_fix(__uint_as_float(kk));
+          if (f) atomicAdd((unsigned long long*)&h2[key_d2(kk)], (unsigned long long)f);
         }
       }
     }
@@ -244,17 +468,13 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
     const uint64_t rem2 = s_rem;
     // bits 8..0 of the keys inside that bin
     for (int i0 = 0; i0 < n; i0 += FT * FU) {
-      uint32_t kk[FU];
+      records(i0, rr);
 #pragma unroll
       for (int e = 0; e < FU; ++e) {
-        const int i = i0 + e * FT + tid;
-        kk[e] = (i < n) ? kin[i] : 0xFFFFFFFFu;
-      }
-#pragma unroll
-      for (int e = 0; e < FU; ++e) {
-        if (kk[e] != 0xFFFFFFFFu && (kk[e] >> 9) == pre) {
-          const uint64_t f = to_fix(__uint_as_float(kk[e]));
-          if (f) atomicAdd((unsigned long long*)&h3[key_d3(kk[e])], (unsigned long long)f);
+        const uint32_t kk = (uint32_t)(rr[e] >> 32);
+        if (rr[e] != ~0ull && (kk >> 9) == pre) {
+          const uint64_t f = to_fix(__uint_as_float(kk));
+          if (f) atomicAdd((unsigned long long*)&h3[key_d3(kk)], (unsigned long long)f);
         }
       }
     }
@@ -269,86 +489,40 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int ncap, int iters, uint6
     __syncthreads();
     T = (pre << 9) | (uint32_t)s_bin;
     if (iters < 31) T &= ~((1u << (31 - iters)) - 1u);
-  }
-  if (tid == 0) {
-    st[kWideST] = (uint64_t)T;
-    if (threshold) threshold[bh] = Z ? __uint_as_float(T) / (float)((double)Z / 1099511627776.0) : 0.f;
-  }
-}
-
-// Per (unit, chunk): head masks under the finished thresholds, the kept mass per head, union words and count.
-// FULL = false: the union words only (no head masks, kept mass or counts are asked for).
-template <int G, bool FULL>
-__global__ __launch_bounds__(kWideThreads) void k_wide_mask(CacheView c, const float* __restrict__ w, int ncap,
-                                                            uint64_t* __restrict__ state,
-                                                            uint32_t* __restrict__ head_mask, int mask_words,
-                                                            uint32_t* __restrict__ uwords,
-                                                            int32_t* __restrict__ chunk_cnt) {
-  __shared__ float s_thr[G];
-  __shared__ int s_cnt[NW];
-  const int nch = ncap / kWideChunk;
-  const int u = blockIdx.x / nch, ch = blockIdx.x - u * nch;
-  const int b = u / c.Hkv, h = u - b * c.Hkv;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const size_t bh0 = (size_t)b * c.Hq + (size_t)h * G;
-  // every weight of the chunk in flight before the thresholds are resolved (thread t holds
-  // candidates 4 (j NT + t) .. + 3 of round j)
-  float4 x[QPT][G];
+    // the recorded candidates at or above the threshold
+    const int u = bh / G;
+    const int MW = ncap / 32;
+    for (int i0 = 0; i0 < n; i0 += FT * FU) {
+      records(i0, rr);
 #pragma unroll
-  for (int j = 0; j < QPT; ++j)
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-      x[j][hh] = reinterpret_cast<const float4*>(w + (bh0 + hh) * ncap + (size_t)ch * kWideChunk)[j * NT + threadIdx.x];
-  if (threadIdx.x < G) s_thr[threadIdx.x] = __uint_as_float((uint32_t)state[(bh0 + threadIdx.x) * kWideStateWords + kWideST]);
-  __syncthreads();
-  float thr[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) thr[hh] = s_thr[hh];
-  uint64_t kept[G];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) kept[hh] = 0ull;
-  int cnt = 0;
-  const int MW = ncap / 32;
-#pragma unroll
-  for (int j = 0; j < QPT; ++j) {
-    const int wbase = (ch * kWideChunk + 4 * (j * NT + wv * 64)) >> 5;  // first of the wave's 8 words
-    const int wd = wbase + (lane >> 3);
-    uint32_t unib = 0u;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float xs[4] = {x[j][hh].x, x[j][hh].y, x[j][hh].z, x[j][hh].w};
-      uint32_t nib = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool keep = xs[e] >= 0.f && xs[e] >= thr[hh];
-        if (FULL && keep) kept[hh] += to_fix(xs[e]);
-        nib |= (keep ? 1u : 0u) << e;
-      }
-      unib |= nib;
-      if (FULL && head_mask) {
-        const uint32_t word = nibbles_to_word(nib);
-        if ((lane & 7) == 0 && wd < mask_words) head_mask[(bh0 + hh) * mask_words + wd] = word;
+      for (int e = 0; e < FU; ++e) {
+        const uint32_t key = (uint32_t)(rr[e] >> 32), idx = (uint32_t)rr[e];
+        if (rr[e] != ~0ull && key >= T && idx < (uint32_t)ncap) {
+          const uint32_t bit = 1u << (idx & 31u), wd = idx >> 5;
+          const uint32_t old = atomicOr(&uwords[(size_t)u * MW + wd], bit);
+          if (full) {
+            if (!(old & bit)) atomicAdd(&chunk_cnt[(size_t)u * nch + idx / kWideChunk], 1);
+            if (head_mask && (int)wd < mask_words) atomicOr(&head_mask[(size_t)bh * mask_words + wd], bit);
+            mass += to_fix(__uint_as_float(key));
+          }
+        }
       }
     }
-    cnt += __popc(unib);
-    const uint32_t uword = nibbles_to_word(unib);
-    if ((lane & 7) == 0) uwords[(size_t)u * MW + wd] = uword;
   }
-  if (!FULL) return;
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    uint64_t s = wave_suffix_u64(kept[hh]);
-    if (lane == 0 && s) atomicAdd((unsigned long long*)&state[(bh0 + hh) * kWideStateWords + kWideMass],
-                                  (unsigned long long)s);
+  if (full) {
+    const uint64_t sm = wave_suffix_u64(mass);
+    if (lane == 0) s_mass[wv] = sm;
+    __syncthreads();
   }
-  cnt = wave_sum_int(cnt);
-  if (lane == 0) s_cnt[wv] = cnt;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int t = 0;
+  if (tid == 0) {
+    if (full) {
+      uint64_t t = 0ull;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) t += s_cnt[i];
-    chunk_cnt[(size_t)u * nch + ch] = t;
+      for (int w = 0; w < FW; ++w) t += s_mass[w];
+      st[kWideMass] = t;
+    }
+    st[kWideST] = (uint64_t)T;
+    if (threshold) threshold[bh] = Z ? __uint_as_float(T) / (float)((double)Z / 1099511627776.0) : 0.f;
   }
 }
 
@@ -406,26 +580,23 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_emit(CacheView c, int nca
   }
 }
 
-hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits, int ncap, float p, int iters,
+hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const float* logits, int ncap, float p, int iters,
                             float* threshold, uint32_t* head_mask, int mask_words, bool full, hipStream_t s) {
-  if (ncap % kWideChunk) return hipErrorInvalidValue;
+  if (ncap % kWideAlign || ncap > kWideMaxCands) return hipErrorInvalidValue;
   const int nch = ncap / kWideChunk;
-  if (ncap % kWideAlign) return hipErrorInvalidValue;
   const unsigned hgrid = (unsigned)(c.B * c.Hq * (ncap / kWideAlign)), ugrid = (unsigned)(c.B * c.Hkv * nch);
-  const dim3 blk(kWideThreads);
+  const dim3 blk(HT);
   const int npm = ncap / (64 * est_batches(ncap, (int64_t)c.B * c.Hkv));
   hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, npm, wd.state);
-  hipLaunchKernelGGL(k_wide_collect, dim3(hgrid), blk, 0, s, logits, ncap, p, wd.state, wd.keys);
-  hipLaunchKernelGGL(k_wide_finish, dim3((unsigned)(c.B * c.Hq)), dim3(1024), 0, s, ncap, iters, wd.state, wd.keys,
-                     threshold);
+  hipLaunchKernelGGL(k_wide_level1, dim3((unsigned)(c.B * c.Hq)), dim3(64), 0, s, p, iters, wd.state);
 #define TWL_WIDE_G(GG)                                                                                      \
   case GG:                                                                                                  \
     if (full)                                                                                               \
-      hipLaunchKernelGGL((k_wide_mask<GG, true>), dim3(ugrid), blk, 0, s, c, logits, ncap, wd.state,         \
-                         head_mask, mask_words, wd.uwords, wd.chunk_cnt);                                   \
+      hipLaunchKernelGGL((k_wide_mask<GG, true>), dim3(ugrid), blk, 0, s, c, logits, ncap, wd.state, wd.keys, \
+                         wd.rec_cnt, head_mask, mask_words, wd.uwords, wd.chunk_cnt, wd.chunk_mass);        \
     else                                                                                                    \
       hipLaunchKernelGGL((k_wide_mask<GG, false>), dim3(ugrid), blk, 0, s, c, logits, ncap, wd.state,        \
-                         nullptr, 0, wd.uwords, wd.chunk_cnt);                                              \
+                         wd.keys, wd.rec_cnt, nullptr, 0, wd.uwords, nullptr, nullptr);                     \
     break;
   switch (c.G) {
     TWL_WIDE_G(1)
@@ -435,6 +606,9 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits,
     default: return hipErrorInvalidValue;
   }
 #undef TWL_WIDE_G
+  hipLaunchKernelGGL(k_wide_finish, dim3((unsigned)(c.B * c.Hq)), dim3(1024), 0, s, c.G, ncap, iters, full, wd.state,
+                     wd.keys, wd.rec_cnt, wd.chunk_mass, threshold, wd.uwords, wd.chunk_cnt,
+                     full ? head_mask : nullptr, full ? mask_words : 0);
   return hipGetLastError();
 }
 

@@ -39,15 +39,20 @@ struct CandView {
 };
 
 // Wide top-p (more than 65536 candidates per head): per-head state in 64-bit words -- the first
-// histogram level (fine bins, then one coarse sum per 32 bins), the count of collected keys, the kept
-// mass, and the resolved search state.  Words [0, kWideZeroWords) must be zero before the first pass.
+// histogram level (fine bins, then one coarse sum per 32 bins; must be zero before the first pass),
+// the largest logit M, the resolved first level (the key from which a weight is surely kept, the key
+// from which it is recorded, the logit bounds that decide most candidates without their weight,
+// total mass, mode, bin, remainder), the kept mass and the threshold.
 constexpr int kWideChunk = 4096;  // candidates per chunk of the wide kernels
-constexpr int kWideThreads = 256;
-constexpr int kWideBlockChunks = 4;  // chunks per block of the first two passes (software-pipelined)
+constexpr int kWideThreads = 256;      // threads of the union emit pass
+constexpr int kWidePassThreads = 1024;  // threads of the histogram and mask passes
+constexpr int kWideBlockChunks = 4;  // chunks per block of the histogram pass (software-pipelined)
 constexpr int kWideAlign = kWideChunk * kWideBlockChunks;  // wide candidate capacities are multiples
-constexpr int kWideH1 = 0, kWideC1 = 2048, kWideNKeys = 2112, kWideMass = 2113, kWideZeroWords = 2114;
-constexpr int kWideSZ = 2114, kWideSMode = 2115, kWideSB1 = 2116, kWideSR1 = 2117, kWideST = 2118;
-constexpr int kWideStateWords = 2119;
+constexpr int kWideH1 = 0, kWideC1 = 2048, kWideZeroWords = 2112;
+// adjacent, read together per head by the mask pass
+constexpr int kWideSM = 2112, kWideSKeep = 2113, kWideSLo = 2114, kWideSA = 2115, kWideSB = 2116;
+constexpr int kWideSZ = 2117, kWideSMode = 2118, kWideSB1 = 2119, kWideSR1 = 2120, kWideMass = 2121, kWideST = 2122;
+constexpr int kWideStateWords = 2123;
 constexpr int kNarrowMaxCands = 65536;      // largest candidate count of the register-resident top-p
 constexpr int kWideMaxCands = 1 << 22;      // fixed-point mass bound
 struct WideWs {
@@ -55,7 +60,10 @@ struct WideWs {
   uint64_t* state;     // [B*Hq][kWideStateWords]
   int32_t* chunk_cnt;  // [B*Hkv][ncap / kWideChunk]
   uint32_t* uwords;    // [B*Hkv][ncap / 32] union bitmap
-  uint32_t* keys;      // [B*Hq][ncap] keys of the candidates in the first level's chosen bin
+  uint64_t* keys;      // [B*Hq][ncap] candidates of the first level's bin, key << 32 | candidate index,
+                       // those of chunk ch from slot ch * kWideChunk on
+  int32_t* rec_cnt;    // [B*Hq][ncap / kWideChunk] how many each chunk recorded
+  uint64_t* chunk_mass;  // [B*Hq][ncap / kWideChunk] kept mass of each chunk's sure candidates
 };
 constexpr int kEstCands = 256;  // candidate block of the range starts (chunk_first); divides the estimate's blocks
 
@@ -106,7 +114,7 @@ hipError_t launch_estimate(const CacheView& c, const QDigits& qd, float sm, cons
 // compacted union lists and the threshold/mass outputs
 // full: the mask pass also writes the head masks, the kept mass and the per-chunk union counts
 // (needed by head_mask, the mass output and the union lists); otherwise union words only
-hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, float* logits, int ncap, float p, int iters,
+hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const float* logits, int ncap, float p, int iters,
                             float* threshold, uint32_t* head_mask, int mask_words, bool full, hipStream_t s);
 hipError_t launch_wide_emit(const CacheView& c, const WideWs& wd, const int32_t* cand_tok, int ncap,
                             int32_t* union_tok, int32_t* union_cnt, float* mass, hipStream_t s);
