@@ -99,7 +99,7 @@ struct Layout {
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
          ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
-         wkeys = 0, wrcnt = 0, wmass = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
+         wkeys = 0, wrcnt = 0, wmass = 0, mpart = 0, mtick = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
 };
 
 // ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
@@ -143,6 +143,8 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->ctok = take((size_t)U * ncap * 4);
   L->crow = take((size_t)U * ncap * 4);
   L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
+  L->mpart = take((size_t)BH * kMergeSplits * kPartFloats * 4);  // second merge level
+  L->mtick = take((size_t)BH * 4);
   L->thr = take((size_t)BH * 4);
   L->apart = take((size_t)BH * kApproxSlices * kApproxStride * 4);  // unkept-cluster approximation
   L->qdig = take((size_t)BH * kGroups * kQDigits * 32);             // the estimate's query digits
@@ -187,6 +189,8 @@ twl_status hip_status(hipError_t e) { return e == hipSuccess ? TWL_OK : TWL_EHIP
     const hipError_t e_ = (expr);              \
     if (e_ != hipSuccess) return TWL_EHIP;     \
   } while (0)
+
+MergeWs merge_of(void* ws, const Layout& L) { return MergeWs{at<float>(ws, L.mpart), at<int32_t>(ws, L.mtick)}; }
 
 QDigits qdigits_of(void* ws, const Layout& L) { return QDigits{at<uint8_t>(ws, L.qdig), at<int32_t>(ws, L.qmeta)}; }
 
@@ -250,11 +254,14 @@ hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, const 
   mv.ncap = L.ncap;
   hipError_t e;
   if ((e = E.rec(8)) != hipSuccess) return e;
-  if ((e = launch_attn_masked(c, q, sm, mv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), headwise, s)) != hipSuccess)
+  if ((e = launch_attn_masked(c, q, sm, mv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), merge_of(ws, L),
+                              headwise, s)) != hipSuccess)
     return e;
   if ((e = E.rec(9)) != hipSuccess) return e;
   if ((e = E.rec(10)) != hipSuccess) return e;
-  if ((e = launch_merge(c, nullptr, L.chunk_tokens, L.slots, at<float>(ws, L.parts), out, lse, s)) != hipSuccess) return e;
+  if ((e = launch_merge(c, nullptr, L.chunk_tokens, L.slots, at<float>(ws, L.parts), merge_of(ws, L), out, lse,
+                        s)) != hipSuccess)
+    return e;
   return E.rec(11);
 }
 
@@ -551,8 +558,8 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
   TWL_TRY(launch_rows(c, sel_indptr, sel_tokens, at<int32_t>(ws, L.urow), U * ncap, s));
   ListView lv{sel_tokens, at<int32_t>(ws, L.urow), sel_indptr, nullptr, 0, U * ncap};
   TWL_TRY(launch_attn(c, static_cast<const uint16_t*>(q), sm_scale, lv, L.chunk_tokens, L.slots,
-                      at<float>(ws, L.parts), s));
-  TWL_TRY(launch_merge(c, &lv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), out, lse, s));
+                      at<float>(ws, L.parts), merge_of(ws, L), s));
+  TWL_TRY(launch_merge(c, &lv, L.chunk_tokens, L.slots, at<float>(ws, L.parts), merge_of(ws, L), out, lse, s));
   return TWL_OK;
 }
 

@@ -20,6 +20,8 @@
 //   * O += P V on the vector ALU in fp32: lane (g, n) owns dims 8n..8n+7 of tokens g, g+4, ...
 // The four waves' (max, sum, output) meet in LDS and the chunk's partial goes to the workspace; the
 // merge combines a unit's chunks in chunk order.
+#include <algorithm>
+
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -61,7 +63,8 @@ constexpr int kAttnSB = 16;  // tokens per sub-block
 template <int G, int NSB, bool MK, bool HW = false, bool BYPAGE = false>
 __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uint16_t* __restrict__ q,
                                                           float sm_log2, ListView L, MaskView MV, int slots,
-                                                          float* __restrict__ partials) {
+                                                          float* __restrict__ partials,
+                                                          int32_t* __restrict__ merge_ticket, int nticket) {
   constexpr int NWV = kAttnWaves, SB = kAttnSB, VS = SB / 4, CH = NWV * NSB * SB, QL = CH / NWV;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -73,6 +76,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
   __shared__ int cr[MK ? NWV : 1][MK ? QL : 1];
   __shared__ int crh[HW ? NWV : 1][HW ? QL : 1];
 
+  // the merge's split tickets start from zero
+  if (blockIdx.x == 0)
+    for (int i = tid; i < nticket; i += 64 * NWV) merge_ticket[i] = 0;
   // chunk slot k of unit u (the unit's chunks are its first ceil(count / CH) slots)
   const int u = blockIdx.x / slots, k = blockIdx.x - u * slots;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
@@ -359,52 +365,58 @@ __global__ __launch_bounds__(256) void k_rows(CacheView c, const int32_t* __rest
   }
 }
 
-// One block per (unit, head): the unit's chunk partials are merged by NR rows of 32 threads (8, 16 or
-// 32 rows as the slot count needs), row r taking chunks r, r + NR, ... in order with a running
-// maximum and thread j owning dims 4j..4j+3 (four chunks' loads in flight per thread); the NR row
-// results are then combined in row order.  With a token list the unit has ceil(count / CH) chunks;
-// without one every slot holds a partial.
-template <int G, int NR>
-__global__ __launch_bounds__(NR * 32) void k_merge(CacheView c, ListView L, bool use_list, int CH, int slots,
-                                                   const float* __restrict__ partials, float* out, float* lse) {
-  constexpr int UNR = 4;
-  const int u = blockIdx.x / G, hh = blockIdx.x - (blockIdx.x / G) * G;
+// Blocks per (unit, head): split sb of S merges the unit's chunk partials [sb per, (sb + 1) per) by
+// NR rows of 32 threads (8, 16 or 32 rows as the count needs), row r taking chunks r, r + NR, ... in
+// order with a running maximum and thread j owning dims 4j..4j+3 (UNR chunks' loads in flight per
+// thread); the NR row results are then combined in row order.  With a token list the unit has
+// ceil(count / CH) chunks; without one every slot holds a partial.  With S > 1 each split leaves its
+// (max, sum, row) record with agent-scope stores (seen by every die), takes a ticket, and the head's
+// last split combines the S records in split order, so the result does not depend on which finishes
+// last.
+template <int G, int NR, int UNR>
+__global__ __launch_bounds__(NR * 32) void k_merge(CacheView c, ListView L, bool use_list, int CH, int slots, int S,
+                                                   const float* __restrict__ partials, float* __restrict__ part2,
+                                                   int32_t* __restrict__ ticket, float* out, float* lse) {
+  const int hb = blockIdx.x / S, sb = blockIdx.x - hb * S;  // (unit, head) row and split
+  const int u = hb / G, hh = hb - u * G;
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int tid = threadIdx.x, r = tid >> 5, j = tid & 31;
   __shared__ float sM[NR], sL[NR];
   __shared__ float4 sO[NR][32];
+  __shared__ int s_last;
   const int nch = use_list ? min((max(0, list_count(L, u)) + CH - 1) / CH, slots) : slots;
-  const int c0 = u * slots;
-  const float* base = partials + ((size_t)c0 * G + hh) * kPartStride;
+  const int per = (slots + S - 1) / S;
+  const int k_lo = sb * per, k_hi = min(slots, k_lo + per), k_end = min(nch, k_hi);
+  const float* base = partials + ((size_t)u * slots * G + hh) * kPartStride;
   constexpr size_t kStep = (size_t)G * kPartStride;
   float M = -__builtin_inff(), Ls = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = r; k0 < slots; k0 += NR * UNR) {
+  for (int k0 = k_lo + r; k0 < k_hi; k0 += NR * UNR) {
     float mk[UNR], lk[UNR];
     float4 ok[UNR];
-    // every load unconditional (a chunk past the unit's slots reads slot 0's record, and any chunk
+    // every load unconditional (a chunk past the split reads the split's first record, and any chunk
     // past the count is dropped after), so the row's loads are all in flight at once
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
       const int k = k0 + NR * i;
-      const float* pk = base + (size_t)(k < slots ? k : 0) * kStep;
+      const float* pk = base + (size_t)(k < k_hi ? k : k_lo) * kStep;
       mk[i] = pk[0];
       lk[i] = pk[1];
       ok[i] = reinterpret_cast<const float4*>(pk + 4)[j];
     }
 #pragma unroll
     for (int i = 0; i < UNR; ++i)
-      if (k0 + NR * i >= nch) mk[i] = -__builtin_inff();
+      if (k0 + NR * i >= k_end) mk[i] = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < UNR; ++i) {
       if (mk[i] != -__builtin_inff()) {
         const float Mn = fmaxf(M, mk[i]);
-        const float sa = exp2f(M - Mn), sb = exp2f(mk[i] - Mn);
-        Ls = Ls * sa + lk[i] * sb;
-        o.x = o.x * sa + ok[i].x * sb;
-        o.y = o.y * sa + ok[i].y * sb;
-        o.z = o.z * sa + ok[i].z * sb;
-        o.w = o.w * sa + ok[i].w * sb;
+        const float sa = exp2f(M - Mn), sb2 = exp2f(mk[i] - Mn);
+        Ls = Ls * sa + lk[i] * sb2;
+        o.x = o.x * sa + ok[i].x * sb2;
+        o.y = o.y * sa + ok[i].y * sb2;
+        o.z = o.z * sa + ok[i].z * sb2;
+        o.w = o.w * sa + ok[i].w * sb2;
         M = Mn;
       }
     }
@@ -415,11 +427,10 @@ __global__ __launch_bounds__(NR * 32) void k_merge(CacheView c, ListView L, bool
   }
   sO[r][j] = o;
   __syncthreads();
+  float Mt = -__builtin_inff(), num = 0.f, den = 0.f;
   if (tid < kD) {
-    float Mt = -__builtin_inff();
 #pragma unroll 8
     for (int i = 0; i < NR; ++i) Mt = fmaxf(Mt, sM[i]);
-    float num = 0.f, den = 0.f;
     if (Mt != -__builtin_inff()) {
       const float* so = reinterpret_cast<const float*>(&sO[0][0]);
 #pragma unroll 8
@@ -431,6 +442,59 @@ __global__ __launch_bounds__(NR * 32) void k_merge(CacheView c, ListView L, bool
         }
       }
     }
+  }
+  if (S > 1) {
+    float* rec = part2 + ((size_t)hb * kMergeSplits + sb) * kPartStride;
+    if (tid < kD) {
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(rec) + 4 + tid, __float_as_uint(num), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(rec), __float_as_uint(Mt), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(rec) + 1, __float_as_uint(den), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // the record's stores performed before the ticket is taken
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&ticket[hb], 1) == S - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid < kD) {
+      // every split's (max, sum, dim tid) in flight at once
+      const float* r0 = part2 + (size_t)hb * kMergeSplits * kPartStride;
+      auto ld = [](const float* x) {
+        return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(x), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT));
+      };
+      float mi[kMergeSplits], li[kMergeSplits], oi[kMergeSplits];
+#pragma unroll
+      for (int i = 0; i < kMergeSplits; ++i) {
+        const float* ri = r0 + (size_t)(i < S ? i : 0) * kPartStride;
+        mi[i] = ld(ri);
+        li[i] = ld(ri + 1);
+        oi[i] = ld(ri + 4 + tid);
+      }
+      Mt = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < kMergeSplits; ++i)
+        if (i < S) Mt = fmaxf(Mt, mi[i]);
+      num = 0.f;
+      den = 0.f;
+      if (Mt != -__builtin_inff()) {
+#pragma unroll
+        for (int i = 0; i < kMergeSplits; ++i) {
+          if (i < S && mi[i] != -__builtin_inff()) {
+            const float s = exp2f(mi[i] - Mt);
+            num += oi[i] * s;
+            den += li[i] * s;
+          }
+        }
+      }
+    }
+  }
+  if (tid < kD) {
     const size_t oh = (size_t)b * c.Hq + (size_t)h * G + hh;
     out[oh * kD + tid] = (den > 0.f) ? num / den : 0.f;
     if (lse && tid == 0) lse[oh] = (den > 0.f) ? (Mt + log2f(den)) * 0.69314718055994530942f : -__builtin_inff();
@@ -450,14 +514,15 @@ int attn_chunk_tokens(int64_t total_upper, int group) {
 
 template <bool MK, bool HW = false, bool BYPAGE = false>
 static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float sm, const ListView& list,
-                                   const MaskView& mv, int chunk_tokens, int slots, float* partials, hipStream_t s) {
+                                   const MaskView& mv, int chunk_tokens, int slots, float* partials,
+                                   const MergeWs& mw, hipStream_t s) {
   if (slots < 1) return hipErrorInvalidValue;
   const float sm_log2 = sm * 1.44269504088896340736f;
   const dim3 grid((unsigned)((int64_t)c.B * c.Hkv * slots)), blk(64 * kAttnWaves);
 #define TWL_ATTN_G(GG, NS)                                                                                  \
   case GG:                                                                                                  \
     hipLaunchKernelGGL((k_attn<GG, NS, MK, HW, BYPAGE>), grid, blk, 0, s, c, q, sm_log2, list, mv, slots,   \
-                       partials);                                                                           \
+                       partials, mw.ticket, c.B * c.Hq);                                                   \
     break;
 #define TWL_ATTN_NSB(NS)                   \
   case NS * kAttnWaves * kAttnSB:          \
@@ -493,23 +558,24 @@ static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float 
 }
 
 hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
-                       int slots, float* partials, hipStream_t s) {
-  if (!list.rows) return hipErrorInvalidValue;
-  return launch_attn_impl<false>(c, q, sm, list, MaskView{}, chunk_tokens, slots, partials, s);
+                       int slots, float* partials, const MergeWs& mw, hipStream_t s) {
+  if (!list.rows || !mw.ticket) return hipErrorInvalidValue;
+  return launch_attn_impl<false>(c, q, sm, list, MaskView{}, chunk_tokens, slots, partials, mw, s);
 }
 
 hipError_t launch_attn_masked(const CacheView& c, const uint16_t* q, float sm, const MaskView& mv, int chunk_tokens,
-                              int slots, float* partials, bool headwise, hipStream_t s) {
-  if ((!mv.head_masks && !mv.union_words) || mv.ncap % chunk_tokens) return hipErrorInvalidValue;
+                              int slots, float* partials, const MergeWs& mw, bool headwise, hipStream_t s) {
+  if ((!mv.head_masks && !mv.union_words) || mv.ncap % chunk_tokens || !mw.ticket) return hipErrorInvalidValue;
   if ((mv.cand_mode == kCandRanges && !mv.cand_row) || (mv.cand_mode == kCandPages && !mv.page_phys))
     return hipErrorInvalidValue;
   const bool by_page = mv.cand_mode != kCandRanges;
   if (headwise) {
     if (!mv.head_masks || !by_page) return hipErrorInvalidValue;
-    return launch_attn_impl<true, true, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, s);
+    return launch_attn_impl<true, true, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
   }
-  if (by_page) return launch_attn_impl<true, false, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, s);
-  return launch_attn_impl<true, false, false>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, s);
+  if (by_page)
+    return launch_attn_impl<true, false, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
+  return launch_attn_impl<true, false, false>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
 }
 
 hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,
@@ -519,24 +585,33 @@ hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t*
 }
 
 hipError_t launch_merge(const CacheView& c, const ListView* list, int chunk_tokens, int slots, const float* partials,
-                        float* out, float* lse, hipStream_t s) {
-  dim3 grid((unsigned)(c.B * c.Hkv * c.G));
+                        const MergeWs& mw, float* out, float* lse, hipStream_t s) {
+  if (!mw.part || !mw.ticket || slots < 1) return hipErrorInvalidValue;
+  const int heads = c.B * c.Hq;
+  // splits per head, for long rows only (the split records and the ticket cost about one short
+  // row's merge): enough blocks to spread the records over the chip (about 512), at least 32 chunks
+  // per split, at most kMergeSplits
+  int S = 1;
+  if (slots > 128) S = std::max(1, std::min({kMergeSplits, 512 / std::max(heads, 1), slots / 32}));
+  const int per = (slots + S - 1) / S;
+  dim3 grid((unsigned)(heads * S));
   const ListView lv = list ? *list : ListView{};
   const bool use_list = list != nullptr;
   // rows of 32 threads: enough for about four chunks per row (one round of loads), at least 8 (the
-  // final combine uses 128 threads)
-  const int nr = slots <= 32 ? 8 : (slots <= 64 ? 16 : 32);
-#define TWL_MERGE_NR(GG, NR)                                                                                 \
+  // final combine uses 128 threads); past 128 chunks, 32 rows of 8 records each in flight
+  const int nr = per <= 32 ? 8 : (per <= 64 ? 16 : (per <= 128 ? 32 : 64));
+#define TWL_MERGE_NR(GG, NR, RR, UU)                                                                         \
   case NR:                                                                                                   \
-    hipLaunchKernelGGL((k_merge<GG, NR>), grid, dim3(NR * 32), 0, s, c, lv, use_list, chunk_tokens, slots,   \
-                       partials, out, lse);                                                                 \
+    hipLaunchKernelGGL((k_merge<GG, RR, UU>), grid, dim3(RR * 32), 0, s, c, lv, use_list, chunk_tokens,       \
+                       slots, S, partials, mw.part, mw.ticket, out, lse);                                   \
     break;
 #define TWL_MERGE_CASE(GG)     \
   case GG:                     \
     switch (nr) {              \
-      TWL_MERGE_NR(GG, 8)      \
-      TWL_MERGE_NR(GG, 16)     \
-      TWL_MERGE_NR(GG, 32)     \
+      TWL_MERGE_NR(GG, 8, 8, 4)      \
+      TWL_MERGE_NR(GG, 16, 16, 4)    \
+      TWL_MERGE_NR(GG, 32, 32, 4)    \
+      TWL_MERGE_NR(GG, 64, 32, 8)    \
     }                          \
     break;
   switch (c.G) {

@@ -23,9 +23,9 @@
 // Kernels:
 //   k_wide_hist1   M from the estimate's per-block maxima (recorded for the later passes); histogram
 //                  of the first digit (four 4096-candidate chunks per block, the next chunk's loads in
-//                  flight while one is processed, one flush of integer atomics to the global histogram)
-//   k_wide_level1  one wave per head: the first digit resolved once (bin, remainder, and the key
-//                  bounds the mask pass sorts by)
+//                  flight while one is processed, one flush of integer atomics to the global histogram);
+//                  the head's last block resolves the first digit (bin, remainder, and the key and
+//                  logit bounds the mask pass sorts by)
 //   k_wide_mask    per (unit, chunk): weights above the chosen bin kept (head masks, kept mass, union
 //                  words and their count), those inside it recorded with their index in the chunk's
 //                  own record range
@@ -97,9 +97,85 @@ __device__ __forceinline__ uint32_t wide_known_threshold(uint32_t b1, int iters)
   return (kKeyFloor + (b1 << 18)) & ~((1u << (31 - iters)) - 1u);
 }
 
+// Level-1 resolution of one head (whole wave): Z, the trivial cases, target, bin and remainder.
+template <bool COH>
+__device__ __forceinline__ void wide_level1(const uint64_t* st, float p, int& mode, uint64_t& Z, int& b1,
+                                            uint64_t& rem1) {
+  const int lane = threadIdx.x & 63;
+  uint64_t z = hist_load<COH>(st + kWideC1 + lane);
+  z = wave_suffix_u64(z);
+  Z = __shfl(z, 0);
+  b1 = 0;
+  rem1 = 0;
+  if (Z == 0ull || !(p < 1.0f)) {
+    mode = 1;  // keep every candidate (threshold 0)
+    return;
+  }
+  mode = 0;
+  double t = ceil((double)p * (double)Z);
+  uint64_t target = (uint64_t)t;
+  if (target < 1ull) target = 1ull;
+  if (target > Z) target = Z;
+  wide_find<COH>(st + kWideH1, st + kWideC1, 64, target, b1, rem1);
+}
+
+// float32 bounds of a float64 value: the least float >= x and the greatest float <= x
+__device__ __forceinline__ float f32_at_least(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = nextafterf(f, __builtin_inff());
+  return f;
+}
+__device__ __forceinline__ float f32_at_most(double x) {
+  float f = (float)x;
+  if ((double)f > x) f = nextafterf(f, -__builtin_inff());
+  return f;
+}
+
+// One wave: the first level of a head resolved once -- total mass, mode, bin and remainder -- and the
+// two keys the mask pass sorts by: a weight whose key reaches `keep` is kept for sure (every key above
+// the bin, or the whole threshold when the first level fixes it), one from `lo` up to `keep` lies
+// in the bin and is recorded for the finishing pass.  Mode 1 keeps every weight (keep = lo = 0).
+// The logit bounds A and B decide without the weight: a logit >= A has a weight >= keep and one
+// below B a weight below lo, for any weight within a relative 2^-16 of exp(l - M) (the weight's
+// own error is below 2e-7); only logits in [B, A) need it.  With keep = 0 every finite logit is kept.
+// The histogram is read with agent-scope loads (its last updates came from other blocks).
+__device__ __forceinline__ void wide_resolve_level1(uint64_t* st, float M, float p, int iters) {
+  int mode, b1;
+  uint64_t Z, rem1;
+  wide_level1<true>(st, p, mode, Z, b1, rem1);
+  if ((threadIdx.x & 63) == 0) {
+    uint32_t keep = 0u, lo = 0u;
+    if (mode == 0) {
+      if (iters <= kWideKnownSteps) {
+        keep = lo = wide_known_threshold((uint32_t)b1, iters);
+      } else {
+        lo = kKeyFloor + ((uint32_t)b1 << 18);
+        keep = lo + (1u << 18);
+      }
+    }
+    float A = -3.402823466e38f, B = -3.402823466e38f;
+    if (keep > 0u && M != -__builtin_inff()) {
+      constexpr double kMargin = 1.0 / 65536.0;
+      A = f32_at_least((double)M + log((double)__uint_as_float(keep)) + kMargin);
+      B = f32_at_most((double)M + log((double)__uint_as_float(lo)) - kMargin);
+    }
+    st[kWideSKeep] = keep;
+    st[kWideSLo] = lo;
+    st[kWideSA] = (uint64_t)__float_as_uint(A);
+    st[kWideSB] = (uint64_t)__float_as_uint(B);
+    st[kWideSZ] = Z;
+    st[kWideSMode] = (uint64_t)mode;
+    st[kWideSB1] = (uint64_t)b1;
+    st[kWideSR1] = rem1;
+  }
+}
+
+// Histogram blocks of a head: M, the first digit's mass histogram; the head's last block to finish
+// (a ticket counter) resolves the first level for the mask pass.
 __global__ __launch_bounds__(HT) void k_wide_hist1(const float* __restrict__ logits, int ncap,
-                                                             const float* __restrict__ pmax, int npm,
-                                                             uint64_t* __restrict__ state) {
+                                                   const float* __restrict__ pmax, int npm, float p, int iters,
+                                                   uint64_t* __restrict__ state) {
+  __shared__ int s_last;
   __shared__ uint64_t h[2048];
   __shared__ float red[2 * HW * 4];
   BlockReduce<HW> br{red};
@@ -130,80 +206,15 @@ __global__ __launch_bounds__(HT) void k_wide_hist1(const float* __restrict__ log
   }
   __syncthreads();
   flush_hist(h, 2048, st + kWideH1, st + kWideC1);
+  // this block's histogram atomics performed before its ticket is taken
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = atomicAdd((unsigned long long*)&st[kWideTicket], 1ull) == (unsigned long long)(nbk - 1);
+  __syncthreads();
+  if (s_last && threadIdx.x < 64) wide_resolve_level1(st, M, p, iters);
 }
 
-// Level-1 resolution of one head (whole wave): Z, the trivial cases, target, bin and remainder.
-__device__ __forceinline__ void wide_level1(const uint64_t* st, float p, int& mode, uint64_t& Z, int& b1,
-                                            uint64_t& rem1) {
-  const int lane = threadIdx.x & 63;
-  uint64_t z = st[kWideC1 + lane];
-  z = wave_suffix_u64(z);
-  Z = __shfl(z, 0);
-  b1 = 0;
-  rem1 = 0;
-  if (Z == 0ull || !(p < 1.0f)) {
-    mode = 1;  // keep every candidate (threshold 0)
-    return;
-  }
-  mode = 0;
-  double t = ceil((double)p * (double)Z);
-  uint64_t target = (uint64_t)t;
-  if (target < 1ull) target = 1ull;
-  if (target > Z) target = Z;
-  wide_find(st + kWideH1, st + kWideC1, 64, target, b1, rem1);
-}
-
-// float32 bounds of a float64 value: the least float >= x and the greatest float <= x
-__device__ __forceinline__ float f32_at_least(double x) {
-  float f = (float)x;
-  if ((double)f < x) f = nextafterf(f, __builtin_inff());
-  return f;
-}
-__device__ __forceinline__ float f32_at_most(double x) {
-  float f = (float)x;
-  if ((double)f > x) f = nextafterf(f, -__builtin_inff());
-  return f;
-}
-
-// One wave per head: the first level resolved once -- total mass, mode, bin and remainder -- and the
-// two keys the mask pass sorts by: a weight whose key reaches `keep` is kept for sure (every key above
-// the bin, or the whole threshold when the first level fixes it), one from `lo` up to `keep` lies
-// in the bin and is recorded for the finishing pass.  Mode 1 keeps every weight (keep = lo = 0).
-// The logit bounds A and B decide without the weight: a logit >= A has a weight >= keep and one
-// below B a weight below lo, for any weight within a relative 2^-16 of exp(l - M) (the weight's
-// own error is below 2e-7); only logits in [B, A) need it.  With keep = 0 every finite logit is kept.
-__global__ __launch_bounds__(64) void k_wide_level1(float p, int iters, uint64_t* __restrict__ state) {
-  uint64_t* st = state + (size_t)blockIdx.x * kWideStateWords;
-  int mode, b1;
-  uint64_t Z, rem1;
-  wide_level1(st, p, mode, Z, b1, rem1);
-  if (threadIdx.x == 0) {
-    uint32_t keep = 0u, lo = 0u;
-    if (mode == 0) {
-      if (iters <= kWideKnownSteps) {
-        keep = lo = wide_known_threshold((uint32_t)b1, iters);
-      } else {
-        lo = kKeyFloor + ((uint32_t)b1 << 18);
-        keep = lo + (1u << 18);
-      }
-    }
-    const float M = __uint_as_float((uint32_t)st[kWideSM]);
-    float A = -3.402823466e38f, B = -3.402823466e38f;
-    if (keep > 0u && M != -__builtin_inff()) {
-      constexpr double kMargin = 1.0 / 65536.0;
-      A = f32_at_least((double)M + log((double)__uint_as_float(keep)) + kMargin);
-      B = f32_at_most((double)M + log((double)__uint_as_float(lo)) - kMargin);
-    }
-    st[kWideSKeep] = keep;
-    st[kWideSLo] = lo;
-    st[kWideSA] = (uint64_t)__float_as_uint(A);
-    st[kWideSB] = (uint64_t)__float_as_uint(B);
-    st[kWideSZ] = Z;
-    st[kWideSMode] = (uint64_t)mode;
-    st[kWideSB1] = (uint64_t)b1;
-    st[kWideSR1] = rem1;
-  }
-}
 
 // Per (unit, chunk): every candidate of the chunk and head is kept when its key reaches the head's
 // `keep` key, recorded (key, index) when it lies from `lo` up to there.  Writes the union words (and
@@ -388,14 +399,19 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int G, int ncap, int iters
   __shared__ uint64_t s_mass[FW];
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nch = ncap / kWideChunk;
-  // kept mass (FULL): the mask pass's chunk sums, plus the recorded candidates added below
-  uint64_t mass = 0ull;
-  if (full && tid < nch) mass = chunk_mass[(size_t)bh * nch + tid];
   uint64_t* st = state + (size_t)bh * kWideStateWords;
   const uint64_t* kin = keys + (size_t)bh * ncap;
+  // every load that does not depend on another in flight together: the head's words, the chunks'
+  // record counts and (FULL) their kept mass, to which the recorded candidates are added below
   const uint64_t mode = st[kWideSMode], Z = st[kWideSZ];
   const uint32_t b1 = (uint32_t)st[kWideSB1];
   const uint64_t rem1 = st[kWideSR1];
+  // (loaded by every thread, so no branch makes them wait early)
+  const int ci = min(tid, nch - 1);
+  const int rc = rec_cnt[(size_t)bh * nch + ci];
+  const uint64_t cm = chunk_mass[(size_t)bh * nch + ci];
+  const int my_cnt = tid < nch ? clampi(rc, 0, kWideChunk) : 0;
+  uint64_t mass = (full && tid < nch) ? cm : 0ull;
   uint32_t T = 0u;
   if (mode == 0ull && iters <= kWideKnownSteps) {
     T = wide_known_threshold(b1, iters);  // nothing was recorded
@@ -406,8 +422,7 @@ __global__ __launch_bounds__(1024) void k_wide_finish(int G, int ncap, int iters
     }
     int n;
     {
-      const int cnt = tid < nch ? clampi(rec_cnt[(size_t)bh * nch + tid], 0, kWideChunk) : 0;
-      const int off = block_excl_scan<FW>(cnt, scan_sm, &n);
+      const int off = block_excl_scan<FW>(my_cnt, scan_sm, &n);
       if (tid < nch) s_off[tid] = off;
       if (tid == 0) s_off[nch] = n;
     }
@@ -587,8 +602,7 @@ hipError_t launch_topp_wide(const CacheView& c, const WideWs& wd, const float* l
   const unsigned hgrid = (unsigned)(c.B * c.Hq * (ncap / kWideAlign)), ugrid = (unsigned)(c.B * c.Hkv * nch);
   const dim3 blk(HT);
   const int npm = ncap / (64 * est_batches(ncap, (int64_t)c.B * c.Hkv));
-  hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, npm, wd.state);
-  hipLaunchKernelGGL(k_wide_level1, dim3((unsigned)(c.B * c.Hq)), dim3(64), 0, s, p, iters, wd.state);
+  hipLaunchKernelGGL(k_wide_hist1, dim3(hgrid), blk, 0, s, logits, ncap, wd.pmax, npm, p, iters, wd.state);
 #define TWL_WIDE_G(GG)                                                                                      \
   case GG:                                                                                                  \
     if (full)                                                                                               \

@@ -373,20 +373,29 @@ __device__ __forceinline__ uint64_t wave_suffix_u64(uint64_t x) {
   return readlane_u64(p, 63) - p + x;
 }
 
+// A histogram word: a plain load, or (COH) an agent-scope atomic load, which sees every device-scope
+// atomic already performed, also those of blocks on other dies, whose L2 this one does not share.
+template <bool COH>
+__device__ __forceinline__ uint64_t hist_load(const uint64_t* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
 // Largest bin of one histogram level whose suffix mass reaches `target` (>= 1), from its coarse
 // sums (one per 32 bins) and then the 32 bins of the chosen coarse block; `rem` is the mass still
 // needed inside the bin (target minus everything above it).  Called by a whole wave.
+template <bool COH = false>
 __device__ __forceinline__ void wide_find(const uint64_t* fine, const uint64_t* coarse, int ncoarse,
                                           uint64_t target, int& bin, uint64_t& rem) {
   const int lane = threadIdx.x & 63;
-  const uint64_t x = (lane < ncoarse) ? coarse[lane] : 0ull;
+  const uint64_t x = (lane < ncoarse) ? hist_load<COH>(coarse + lane) : 0ull;
   const uint64_t px = wave_incl_scan_u64(x);
   const uint64_t tx = readlane_u64(px, 63);
   unsigned long long bal = __ballot(lane < ncoarse && tx - px + x >= target);
   const int cb = bal ? 63 - __clzll(bal) : 0;
   const uint64_t above = tx - readlane_u64(px, cb);  // mass of the coarse blocks above cb
   const uint64_t r1 = target - above;
-  const uint64_t y = (lane < 32) ? fine[32 * cb + lane] : 0ull;
+  const uint64_t y = (lane < 32) ? hist_load<COH>(fine + 32 * cb + lane) : 0ull;
   const uint64_t py = wave_incl_scan_u64(y);
   const uint64_t ty = readlane_u64(py, 63);
   bal = __ballot(lane < 32 && ty - py + y >= r1);

@@ -39,7 +39,8 @@ struct CandView {
 };
 
 // Wide top-p (more than 65536 candidates per head): per-head state in 64-bit words -- the first
-// histogram level (fine bins, then one coarse sum per 32 bins; must be zero before the first pass),
+// histogram level (fine bins, then one coarse sum per 32 bins) and the count of histogram blocks
+// done (both zero before the first pass),
 // the largest logit M, the resolved first level (the key from which a weight is surely kept, the key
 // from which it is recorded, the logit bounds that decide most candidates without their weight,
 // total mass, mode, bin, remainder), the kept mass and the threshold.
@@ -48,11 +49,11 @@ constexpr int kWideThreads = 256;      // threads of the union emit pass
 constexpr int kWidePassThreads = 1024;  // threads of the histogram and mask passes
 constexpr int kWideBlockChunks = 4;  // chunks per block of the histogram pass (software-pipelined)
 constexpr int kWideAlign = kWideChunk * kWideBlockChunks;  // wide candidate capacities are multiples
-constexpr int kWideH1 = 0, kWideC1 = 2048, kWideZeroWords = 2112;
+constexpr int kWideH1 = 0, kWideC1 = 2048, kWideTicket = 2112, kWideZeroWords = 2113;
 // adjacent, read together per head by the mask pass
-constexpr int kWideSM = 2112, kWideSKeep = 2113, kWideSLo = 2114, kWideSA = 2115, kWideSB = 2116;
-constexpr int kWideSZ = 2117, kWideSMode = 2118, kWideSB1 = 2119, kWideSR1 = 2120, kWideMass = 2121, kWideST = 2122;
-constexpr int kWideStateWords = 2123;
+constexpr int kWideSM = 2113, kWideSKeep = 2114, kWideSLo = 2115, kWideSA = 2116, kWideSB = 2117;
+constexpr int kWideSZ = 2118, kWideSMode = 2119, kWideSB1 = 2120, kWideSR1 = 2121, kWideMass = 2122, kWideST = 2123;
+constexpr int kWideStateWords = 2124;
 constexpr int kNarrowMaxCands = 65536;      // largest candidate count of the register-resident top-p
 constexpr int kWideMaxCands = 1 << 22;      // fixed-point mass bound
 struct WideWs {
@@ -93,6 +94,15 @@ struct ListView {
   int64_t cap;            // CSR: entries the tokens/rows arrays hold (0 when padded)
 };
 
+constexpr int kPartFloats = 4 + kD;  // per (chunk, head): max, sum, 2 pad, output row (16-byte aligned)
+// Second level of the chunk merge: up to kMergeSplits blocks per (unit, head), each leaving one
+// record (same layout as a chunk partial), and a ticket per (unit, head) that the attention kernel
+// clears and the merge counts its finished splits with.
+constexpr int kMergeSplits = 16;
+struct MergeWs {
+  float* part;      // [B*Hq][kMergeSplits][kPartFloats]
+  int32_t* ticket;  // [B*Hq]
+};
 // ---- launchers (each returns the launch status) --------------------------------------------------
 hipError_t launch_quantize(const CacheView& c, const int32_t* tok_begin, const int32_t* tok_end,
                            int span_pages, hipStream_t s);
@@ -161,18 +171,17 @@ struct MaskView {
 };
 // one workgroup per chunk slot: slot k of unit u covers list entries [k*chunk_tokens, (k+1)*chunk_tokens)
 hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const ListView& list, int chunk_tokens,
-                       int slots, float* partials, hipStream_t s);
+                       int slots, float* partials, const MergeWs& mw, hipStream_t s);
 // one workgroup per chunk slot of the candidate space (every slot writes a partial); headwise: each
 // query head attends over its own bitmap's tokens (needs head_masks) instead of the group's union
 hipError_t launch_attn_masked(const CacheView& c, const uint16_t* q, float sm, const MaskView& mv, int chunk_tokens,
-                              int slots, float* partials, bool headwise, hipStream_t s);
+                              int slots, float* partials, const MergeWs& mw, bool headwise, hipStream_t s);
 // K/V rows of a CSR token list (into `rows`, same indexing), entries at or past `capacity` skipped
 hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,
                        int64_t capacity, hipStream_t s);
 // list: chunks per unit from the list counts; list == nullptr: every slot holds a partial
 hipError_t launch_merge(const CacheView& c, const ListView* list, int chunk_tokens, int slots, const float* partials,
-                        float* out, float* lse, hipStream_t s);
-constexpr int kPartFloats = 4 + kD;  // per (chunk, head): max, sum, 2 pad, output row (16-byte aligned)
+                        const MergeWs& mw, float* out, float* lse, hipStream_t s);
 // elements per thread of the top-p block for a candidate capacity (0 = unsupported)
 int topp_elems_per_thread(int64_t ncap);
 constexpr int kToppThreads = 1024;
