@@ -71,7 +71,7 @@ DESCR = {
 }
 HEADLINE = "C5"
 LINE = ["C2", "C3", "C4", "C5"]  # the metric's 32K-256K range, headline last
-STAGES_CLUSTER = ["cluster_scores_topp", "cluster_union", "estimate", "topp_union", "attention", "merge"]
+STAGES_CLUSTER = ["cluster_scores_topp", "cluster_pages", "estimate", "topp_union", "attention", "merge"]
 EVENT_NO_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
 

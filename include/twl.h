@@ -136,7 +136,7 @@ size_t twl_workspace_bytes(const twl_cache* cache, int64_t max_candidates_per_gr
 twl_status twl_quantize_k(const twl_cache* cache, const int32_t* tok_begin, const int32_t* tok_end,
                           int32_t max_span, void* stream);
 
-/* Base selector (Paper-Notes "整体框架": a conservative budget, e.g. 1/4; paperlayer §4.1 Fig. 5),
+/* Base selector (Paper-Notes "整体框架": a generous budget, e.g. 1/4; paperlayer §4.1 Fig. 5),
  * Quest-style: page score of query head h = sum_c max(q_c*kmin_c, q_c*kmax_c) as a float32
  * left-to-right fold over c from +0; group score = float32 fold over the G heads in order; keep
  * K_b = clamp(ceil(fp32(keep_frac)*fp32(P_b)), 1, P_b) pages (P_b = ceil(seq_lens[b]/16), 0 if
@@ -200,7 +200,7 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
                            void* ws, size_t ws_bytes, void* stream);
 
 /* The whole decode step for one layer, Twilight's select-then-prune path (Paper-Notes "整体框架";
- * paperlayer §4.1, Fig. 5: a base selector with a conservative budget, then top-p pruning of its
+ * paperlayer §4.1, Fig. 5: an existing selector with a generous budget, then top-p pruning of its
  * candidates, then sparse attention): twl_select_pages (skipped when keep_frac >= 1), then
  * twl_estimate_topp over the kept pages, then the sparse attention over the union.  Pages, top-p
  * sets and thresholds are bitwise those of the split calls; the attention reads the top-p bitmaps
@@ -280,13 +280,16 @@ twl_status twl_cluster_approx_unkept(const twl_cache* cache, const void* q, floa
                                      const float* vmean, float* out, float* lse, void* ws, size_t ws_bytes,
                                      void* stream);
 
-/* The whole Double-P decode step ("Double-P", 方法详解 and 关键设计): twl_select_clusters_topp with
- * p1, then twl_estimate_topp over the kept ranges with params->p (keep_frac is ignored), then the
- * sparse attention over the union -- the same kernels as the split calls.  Unkept clusters are
- * dropped.  Requires 2*num_clusters <= max_seq_len rounded up to the top-p capacity; the workspace
- * is twl_workspace_bytes(cache, max_seq_len).  `events` is NULL or holds 2*TWL_NUM_STAGES events as
- * for twl_decode_profiled, the stages being 0 cluster scores + cluster top-p, 1 cluster union (with
- * the kept ranges' prefix sums), 2 INT4 estimate, 3 token top-p + union, 4 attention, 5 merge. */
+/* The whole Double-P decode step ("Double-P", 方法详解 and 关键设计): the cluster stage of
+ * twl_select_clusters_topp with p1, then the token-level estimate and top-p with params->p
+ * (keep_frac is ignored) over the kept clusters' tokens, then the sparse attention over the union.
+ * The candidates are the same tokens as twl_estimate_topp over the kept ranges (so are the kept sets
+ * and token lists); here they are handed on as the pages the kept clusters touch, each with a mask
+ * of its kept slots.  Unkept clusters are dropped.  Requires 2*num_clusters <= max_seq_len rounded up
+ * to the top-p capacity; the workspace is twl_workspace_bytes(cache, max_seq_len).  `events` is NULL
+ * or holds 2*TWL_NUM_STAGES events as for twl_decode_profiled, the stages being 0 cluster scores +
+ * cluster top-p, 1 kept clusters as pages, 2 INT4 estimate, 3 token top-p + union, 4 attention,
+ * 5 merge. */
 twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_decode_params* params, float p1,
                                const void* centroids, const int32_t* csize, const int32_t* coff,
                                int32_t num_clusters, float* out, float* lse, float* threshold, int32_t* sel_indptr,
@@ -301,7 +304,7 @@ const char* twl_status_str(twl_status status);
 const char* twl_version(void);
 
 /* The base selector's page budget for a sequence of num_pages pages (Paper-Notes "整体框架": a
- * conservative budget such as 1/4 of the pages): clamp(ceil(fp32(keep_frac) * fp32(num_pages)), 1,
+ * generous budget such as 1/4 of the pages): clamp(ceil(fp32(keep_frac) * fp32(num_pages)), 1,
  * num_pages), 0 when num_pages <= 0; -1 when keep_frac is not finite and > 0.  Host-only, no HIP
  * call: callers size page lists (max_keep) and candidate capacities with it. */
 int32_t twl_keep_pages(int32_t num_pages, float keep_frac);

@@ -1,5 +1,5 @@
 """The whole select-then-prune decode step, composed from O1-O11 (Paper-Notes "整体框架";
-paperlayer §4.1, Fig. 5): base selector with a conservative budget -> INT4 weight estimate ->
+paperlayer §4.1, Fig. 5): existing selector with a generous budget -> INT4 weight estimate ->
 per-head top-p -> group union -> sparse attention over the survivors.
 
 ``decode_unit`` runs one (sequence b, kv-head h) unit; ``decode`` runs them all.  Inputs are plain

@@ -1,8 +1,8 @@
 """O3 Quest-style page scores and top-K page selection; O4 candidate token lists.
 
-The Twilight pages use a base token selector as a black box with a conservative budget (Paper-Notes
-"整体框架": e.g. 1/4 of the tokens; paperlayer §4.1, Fig. 5) and name Quest among the selectors, but
-do not define Quest's score.  Readings taken here:
+The Twilight pages take an existing token selector unchanged and give it a generous budget
+(Paper-Notes "整体框架": e.g. 1/4 of the tokens; paperlayer §4.1, Fig. 5); they name Quest among the
+selectors but do not define Quest's score.  Readings taken here:
 
 * page score of query head h:  sigma_h(page) = sum_c max(q_c * kmin_c, q_c * kmax_c), the tightest
   per-channel upper bound of q.k over keys inside the page's min/max box;

@@ -99,7 +99,7 @@ struct Layout {
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
          ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
-         wkeys = 0, wrcnt = 0, wmass = 0, mpart = 0, mtick = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
+         wkeys = 0, wrcnt = 0, wmass = 0, mpart = 0, mtick = 0, smask = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
 };
 
 // ncap_of(maxcand): up to 65536 candidates the top-p block holds 1024*E of them, E a power of two up
@@ -133,6 +133,7 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->pages = take((size_t)U * c->max_pages_per_seq * 4);
   L->pcnt = take((size_t)U * 4);
   L->pphys = take((size_t)U * c->max_pages_per_seq * 4);
+  L->smask = take((size_t)U * c->max_pages_per_seq * 4);  // the cluster stage's slot mask of every page
   L->rpre = take((size_t)U * (ncap + 1) * 4);
   L->cfirst = take((size_t)U * (ncap / kEstCands) * 4);
   L->logits = take((size_t)BH * ncap * 4);
@@ -383,25 +384,19 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   const Events E{events, s};
   const CacheView c = make_view(cache);
   const uint16_t* qb = static_cast<const uint16_t*>(q);
-  int32_t* ranges = at<int32_t>(ws, L.urow);
-  int32_t* rcount = at<int32_t>(ws, L.pcnt);
   TWL_TRY(E.rec(0));
   TWL_TRY(launch_cluster_scores_topp(c, qb, prm->sm_scale, p1, prm->iters, static_cast<const uint16_t*>(centroids),
                                      csize, num_clusters, (int)cpad, at<float>(ws, L.logits), at<float>(ws, L.thr),
                                      at<uint32_t>(ws, L.masks), qdigits_of(ws, L), s));
   TWL_TRY(E.rec(1));
   TWL_TRY(E.rec(2));
-  // the kept clusters' token ranges, with the prefix sums and block starts the estimate resolves by
-  TWL_TRY(launch_cluster_union(c, at<uint32_t>(ws, L.masks), (int)cpad, csize, coff, num_clusters, ranges, rcount,
-                               at<int32_t>(ws, L.rpre), at<int32_t>(ws, L.cfirst), (int)(ncap / kEstCands), s));
+  // the kept clusters' tokens as a slot mask of every page
+  TWL_TRY(launch_cluster_slots(c, at<uint32_t>(ws, L.masks), (int)cpad, csize, coff, num_clusters,
+                               at<uint32_t>(ws, L.smask), s));
   TWL_TRY(E.rec(3));
   CandView cand{};
-  cand.mode = kCandRanges;
-  cand.items = ranges;
-  cand.count = rcount;
-  cand.max_items = num_clusters;
-  cand.range_prefix = at<int32_t>(ws, L.rpre);
-  cand.chunk_first = at<int32_t>(ws, L.cfirst);
+  cand.mode = kCandAll;
+  cand.slot_mask = at<uint32_t>(ws, L.smask);
   float* thr = threshold ? threshold : at<float>(ws, L.thr);
   const bool csr = sel_tokens != nullptr;
   TWL_TRY(estimate_topp(c, prm->sm_scale, cand, ws, L, prm->p, prm->iters, thr, nullptr, nullptr, 0, csr, E, s));

@@ -231,16 +231,142 @@ hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int
   return hipGetLastError();
 }
 
+// Slots a .. b - 1 of a page (0 <= a < b <= 16).
+__device__ __forceinline__ uint32_t slot_bits(int a, int b) { return ((1u << b) - 1u) & ~((1u << a) - 1u); }
+
+// Per unit and segment of kSlotSeg pages, one block: the mask of kept token slots of every page of the
+// segment -- the token-level candidates as every page of the sequence with such a mask (page-indexed,
+// [U][maxP]; pages past the sequence get 0), so the estimate and the attention read K by page and
+// need no compacted list.  Every kept cluster (OR of the G head masks) is clipped to the segment's
+// tokens: its first and last pages get their slot bits by OR, the pages strictly between them a
+// +1 / -1 pair in a difference array whose prefix sums count the clusters covering each page whole.
+// Clusters may come in any order and overlap; tokens at or past the sequence length are not
+// candidates.  Each thread's clusters are read kSlotBatch at a time, their loads in flight together.
+constexpr int kSlotSeg = 1024, kSlotThreads = 256, kSlotBatch = 16;
+template <int G>
+__global__ __launch_bounds__(kSlotThreads) void k_cluster_slots(CacheView c, const uint32_t* __restrict__ mask_ws,
+                                                                int cpad, const int32_t* __restrict__ csize,
+                                                                const int32_t* __restrict__ coff, int C,
+                                                                int seg_blocks, uint32_t* __restrict__ smask) {
+  constexpr int NT = kSlotThreads, NW = NT / 64, PPT = kSlotSeg / NT;
+  static_assert(PPT == 4, "four pages per thread");
+  constexpr int kMaxWords = 65536 / 32;
+  __shared__ uint32_t uw[kMaxWords];
+  __shared__ __align__(16) uint32_t sp[kSlotSeg / 2];  // slot bits, two pages per word
+  __shared__ __align__(16) int sd[kSlotSeg + 4];       // difference counts
+  __shared__ int scan_sm[NW + 1];
+  const int u = blockIdx.x / seg_blocks, sg = blockIdx.x - u * seg_blocks;
+  const int b = u / c.Hkv, h = u - b * c.Hkv;
+  const int tid = threadIdx.x;
+  const int n = clampi(c.seq_lens[b], 0, min(c.maxTok, 16 * c.maxP));
+  const int s0 = sg * kSlotSeg;                           // the segment's first page
+  const int t0 = 16 * s0, t1 = min(16 * (s0 + kSlotSeg), n);  // its tokens inside the sequence
+  // kept clusters
+  const int MW = cpad / 32;
+  const uint32_t* m0 = mask_ws + ((size_t)b * c.Hq + (size_t)h * G) * MW;
+  for (int w = tid; w < MW; w += NT) {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) x |= m0[(size_t)hh * MW + w];
+    uw[w] = x;
+  }
+  for (int i = tid; i < kSlotSeg / 2; i += NT) sp[i] = 0u;
+  for (int i = tid; i < kSlotSeg + 4; i += NT) sd[i] = 0;
+  __syncthreads();
+  if (t0 < t1) {  // uniform
+    const int32_t* co = coff + (size_t)u * (C + 1);
+    const int32_t* cs = csize + (size_t)u * C;
+    for (int k0 = 0; k0 < C; k0 += NT * kSlotBatch) {
+      int begr[kSlotBatch], lenr[kSlotBatch];
+#pragma unroll
+      for (int i = 0; i < kSlotBatch; ++i) {
+        const int k = min(k0 + i * NT + tid, C - 1);
+        begr[i] = co[k];
+        lenr[i] = cs[k];
+      }
+#pragma unroll
+      for (int i = 0; i < kSlotBatch; ++i) {
+        const int k = k0 + i * NT + tid;
+        if (k >= C || !((uw[k >> 5] >> (k & 31)) & 1u)) continue;
+        const int lo = max(begr[i], t0);
+        const int hi = (int)min((int64_t)begr[i] + (int64_t)max(lenr[i], 0), (int64_t)t1);
+        if (hi <= lo) continue;
+        const int p0 = (lo >> 4) - s0, p1 = ((hi - 1) >> 4) - s0;
+        if (p0 == p1) {
+          atomicOr(&sp[p0 >> 1], slot_bits(lo & 15, hi - 16 * (s0 + p0)) << (16 * (p0 & 1)));
+        } else {
+          atomicOr(&sp[p0 >> 1], slot_bits(lo & 15, 16) << (16 * (p0 & 1)));
+          atomicOr(&sp[p1 >> 1], slot_bits(0, hi - 16 * (s0 + p1)) << (16 * (p1 & 1)));
+          if (p1 - p0 >= 2) {
+            atomicAdd(&sd[p0 + 1], 1);
+            atomicAdd(&sd[p1], -1);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // thread t: pages s0 + 4t .. + 3 (one 16-byte and one 8-byte LDS read)
+  const int4 d4 = reinterpret_cast<const int4*>(sd)[tid];
+  const uint2 sp2 = reinterpret_cast<const uint2*>(sp)[tid];
+  const int dv[PPT] = {d4.x, d4.y, d4.z, d4.w};
+  const uint32_t bits[PPT] = {sp2.x & 0xFFFFu, sp2.x >> 16, sp2.y & 0xFFFFu, sp2.y >> 16};
+  int tot;
+  int run = block_excl_scan<NW>(dv[0] + dv[1] + dv[2] + dv[3], scan_sm, &tot);
+  uint32_t* out = smask + (size_t)u * c.maxP;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int q = s0 + PPT * tid + i;
+    run += dv[i];
+    uint32_t m = 0u;
+    const int tq = 16 * q;
+    if (tq < n) {
+      m = bits[i] | (run > 0 ? 0xFFFFu : 0u);
+      if (tq + 16 > n) m &= slot_bits(0, n - tq);
+    }
+    if (q < c.maxP) out[q] = m;
+  }
+}
+
+hipError_t launch_cluster_slots(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
+                                const int32_t* coff, int C, uint32_t* smask, hipStream_t s) {
+  if (C < 1 || C > 65536 || cpad > 65536 || c.maxP < 1) return hipErrorInvalidValue;
+  const int seg_blocks = (c.maxP + kSlotSeg - 1) / kSlotSeg;
+  dim3 grid((unsigned)(c.B * c.Hkv * seg_blocks));
+#define TWL_CS_G(GG)                                                                                          \
+  case GG:                                                                                                    \
+    hipLaunchKernelGGL(k_cluster_slots<GG>, grid, dim3(kSlotThreads), 0, s, c, mask_ws, cpad, csize, coff, C,  \
+                       seg_blocks, smask);                                                                    \
+    break;
+  switch (c.G) {
+    TWL_CS_G(1)
+    TWL_CS_G(2)
+    TWL_CS_G(4)
+    TWL_CS_G(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef TWL_CS_G
+  return hipGetLastError();
+}
+
 hipError_t launch_cluster_scores_topp(const CacheView& c, const uint16_t* q, float sm, float p1, int iters,
                                       const uint16_t* centroids, const int32_t* csize, int C, int cpad, float* lam,
                                       float* thr, uint32_t* mask_ws, const QDigits& qd, hipStream_t s) {
   const int bpu = cpad / 64;
   dim3 grid((unsigned)(c.B * c.Hkv * bpu));
   switch (c.G) {
-    case 1: hipLaunchKernelGGL(k_cluster_score<1>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
-    case 2: hipLaunchKernelGGL(k_cluster_score<2>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
-    case 4: hipLaunchKernelGGL(k_cluster_score<4>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
-    case 8: hipLaunchKernelGGL(k_cluster_score<8>, grid, dim3(512), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd); break;
+    case 1:
+      hipLaunchKernelGGL(k_cluster_score<1>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_cluster_score<2>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd);
+      break;
+    case 4:
+      hipLaunchKernelGGL(k_cluster_score<4>, grid, dim3(256), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd);
+      break;
+    case 8:
+      hipLaunchKernelGGL(k_cluster_score<8>, grid, dim3(512), 0, s, c, q, centroids, csize, C, cpad, sm, lam, bpu, qd);
+      break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

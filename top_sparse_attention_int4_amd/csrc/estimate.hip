@@ -274,8 +274,9 @@ __device__ __forceinline__ void block_head_max(const EstWave<G, BITS>& ew, const
   }
 }
 
-// Candidates as pages (MODE kCandPages, physical pages listed by the selector) or as every token
-// (kCandAll): NB 16-candidate tiles (pages) per wave, 4 waves per block, 64 NB candidates per block.
+// Candidates as pages (MODE kCandPages, physical pages listed by the selector) or as every page of the
+// sequence (kCandAll), either optionally with a mask of each page's candidate slots (the cluster
+// stage's): NB 16-candidate tiles (pages) per wave, 4 waves per block, 64 NB candidates per block.
 template <int G, int NB, int BITS, int MODE>
 __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd, float sm, CandView cand, int ncap,
                                                         int chunks_per_unit, float* __restrict__ logits,
@@ -296,6 +297,7 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
   const int tp0 = ck * 4 * NB + wv * NB;
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   int page[NB], phys[NB];
+  uint32_t slots[NB];  // which of the page's 16 tokens are candidates
   if constexpr (MODE == kCandPages) {
     const int cnt = clampi(cand.count[u], 0, cand.max_items);
 #pragma unroll
@@ -306,12 +308,14 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
       // the selector lists the physical pages too; a caller's page list is looked up in the table
       phys[i] = cand.phys ? cand.phys[idx]
                           : c.page_table[(size_t)b * c.maxP + clampi(page[i], 0, c.maxP - 1)];
+      slots[i] = cand.slot_mask ? cand.slot_mask[idx] : 0xFFFFu;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       page[i] = tp0 + i;
       phys[i] = c.page_table[(size_t)b * c.maxP + min(tp0 + i, c.maxP - 1)];
+      slots[i] = cand.slot_mask ? cand.slot_mask[(size_t)u * c.maxP + min(tp0 + i, c.maxP - 1)] : 0xFFFFu;
     }
   }
   EW ew;
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
     for (int e = 0; e < 4; ++e) {
       const int slot = 4 * ew.rg + e;
       mw[i][e] = c.k4_meta[(size_t)(row0 + slot) * kGroups + (ew.gc & 3)];
-      tok_ok[i][e] = pg_ok && page[i] * kPage + slot < n;
+      tok_ok[i][e] = pg_ok && page[i] * kPage + slot < n && ((slots[i] >> slot) & 1u);
     }
   }
   if (cand_tok && ew.kb == 0) {
@@ -338,7 +342,8 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
     for (int i = 0; i < NB; ++i) {
       const bool pg_ok = page[i] >= 0 && page[i] * kPage < n && (unsigned)phys[i] < (unsigned)c.nphys;
       const int t = page[i] * kPage + ew.nn;
-      cand_tok[(size_t)u * ncap + (size_t)(tp0 + i) * kPage + ew.nn] = (pg_ok && t < n) ? t : -1;
+      const bool ok = pg_ok && t < n && ((slots[i] >> ew.nn) & 1u);
+      cand_tok[(size_t)u * ncap + (size_t)(tp0 + i) * kPage + ew.nn] = ok ? t : -1;
     }
   }
   float mx[NTL];

@@ -1,6 +1,6 @@
 // Base page selector: Quest-style page bound scores and exact top-K page selection.
 //
-// The Twilight pages run a base sparse-attention selector with a conservative budget before the
+// The Twilight pages run an existing sparse-attention selector with a generous budget before the
 // top-p pruner (Paper-Notes "整体框架"; paperlayer §4.1, Fig. 5) and name Quest among those
 // selectors.  The page score of query head h is sum_c max(q_c*kmin_c, q_c*kmax_c); it is evaluated
 // as a float32 left-to-right fold over the 128 channels, one lane per page, so the result equals the

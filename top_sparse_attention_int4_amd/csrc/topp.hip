@@ -18,8 +18,9 @@
 //
 // Masses are 64-bit fixed point, floor(e * 2^40), added with integer LDS atomics, so the decision does
 // not depend on the order of the additions; the cost is at most 2^-40 per weight (below 1e-7 of Z
-// for 65536 candidates).  Candidates that do not exist carry e = -1.  The reported threshold and kept
-// mass are float32 sums in a fixed order.
+// for 65536 candidates).  Candidates that do not exist carry e = -1.  The reported threshold is T over
+// the fixed-point mass total (the top-k search: over the float32 total); the kept mass is a float32
+// sum in a fixed order.
 //
 // The GQA union (paperlayer §B.2: the union over a group's query heads, read once) is a separate
 // small kernel over the head masks.
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   __shared__ float red[2 * NW * 4];
   __shared__ uint64_t h1[2048], h2[512], h3[512], cs[64];
   __shared__ uint64_t s_rem;
+  __shared__ uint64_t s_zfix;
   __shared__ int s_bin, s_mode;
   BlockReduce<NW> br{red};
 
@@ -81,7 +83,6 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
 #pragma unroll
     for (int j = 0; j < E; ++j) e[j] = -1.f;
   }
-  // (Z is reduced at the end with the kept mass: the search itself runs on the fixed-point sums)
 
   // ---- round 1: first digit (weights carrying mass are >= 2^-40) ---------------------------------------
 #pragma unroll
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
       s_mode = mode;
       s_bin = bin;
       s_rem = rem;
+      s_zfix = zf;  // the mass total (a count for the top-k search)
     }
   }
   __syncthreads();
@@ -169,13 +171,19 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     T = (pre << 9) | (uint32_t)s_bin;
     if (iters < 31) T &= ~((1u << (31 - iters)) - 1u);
   }
+  // the reported threshold relative to the fixed-point mass total (an exact sum: it does not depend
+  // on where the candidates sit, and the multi-block search reports the same; the top-k search,
+  // whose histograms count, over the float32 total); the kept mass as a float32 sum in a fixed order
   const float m = __uint_as_float(T);
   float f = 0.f;
 #pragma unroll
   for (int j = 0; j < E; ++j) f += (e[j] >= m) ? e[j] : 0.f;
   br.sum2(Z, f);
   if (tid == 0) {
-    threshold[bh] = (Z > 0.f) ? m / Z : 0.f;
+    if (topk > 0)
+      threshold[bh] = (Z > 0.f) ? m / Z : 0.f;
+    else
+      threshold[bh] = s_zfix ? m / (float)((double)s_zfix / 1099511627776.0) : 0.f;
     if (mass) mass[bh] = (Z > 0.f) ? f / Z : 0.f;
   }
 

@@ -36,6 +36,8 @@ struct CandView {
   const int32_t* chunk_first;   // [U][ncap/kEstCands] (ranges only): range holding each block's first candidate
   int max_items;
   const int32_t* phys;          // pages only, optional: physical page of each listed page id
+  const uint32_t* slot_mask;    // optional: which of a page's 16 slots are candidates -- per listed page
+                                // (pages) or per page of the sequence, [U][maxP] (all tokens)
 };
 
 // Wide top-p (more than 65536 candidates per head): per-head state in 64-bit words -- the first
@@ -149,6 +151,10 @@ constexpr int kApproxStride = 128 + 4;  // floats per slice partial: 128 sums, t
 hipError_t launch_cluster_union(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
                                 const int32_t* coff, int C, int32_t* ranges, int32_t* count, int32_t* prefix,
                                 int32_t* chunk_first, int nchunk, hipStream_t s);
+// union of a unit's head masks -> the mask of kept token slots of every page ([U][maxP], page-indexed;
+// 0 for pages past the sequence): the token-level candidates as every page with such a mask
+hipError_t launch_cluster_slots(const CacheView& c, const uint32_t* mask_ws, int cpad, const int32_t* csize,
+                                const int32_t* coff, int C, uint32_t* smask, hipStream_t s);
 // topk > 0: keep each head's topk largest weights (ties kept) instead of its top-p set
 hipError_t launch_topp(const CacheView& c, const float* logits, int ncap, float p, int iters, float* threshold,
                        float* mass, uint32_t* mask_ws, uint32_t* head_mask, int mask_words, int topk, hipStream_t s);
