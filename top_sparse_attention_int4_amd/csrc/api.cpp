@@ -98,7 +98,7 @@ struct Layout {
   int slots = 1;          // attention chunk slots per unit (ceil(ncap / chunk_tokens))
   int64_t max_chunks = 0;
   size_t scores = 0, pages = 0, pcnt = 0, rpre = 0, cfirst = 0, logits = 0, masks = 0, utok = 0, urow = 0,
-         ucnt = 0, ctok = 0, crow = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
+         ucnt = 0, ctok = 0, pphys = 0, parts = 0, thr = 0, pmax = 0, wstate = 0, wcnt = 0, uwords = 0,
          wkeys = 0, wrcnt = 0, wmass = 0, mpart = 0, mtick = 0, smask = 0, apart = 0, qdig = 0, qmeta = 0, total = 0;
 };
 
@@ -142,7 +142,6 @@ bool make_layout(const twl_cache* c, int64_t ncap, Layout* L) {
   L->urow = take((size_t)U * ncap * 4);
   L->ucnt = take((size_t)U * 4);
   L->ctok = take((size_t)U * ncap * 4);
-  L->crow = take((size_t)U * ncap * 4);
   L->parts = take((size_t)L->max_chunks * G * kPartFloats * 4);
   L->mpart = take((size_t)BH * kMergeSplits * kPartFloats * 4);  // second merge level
   L->mtick = take((size_t)BH * 4);
@@ -214,7 +213,7 @@ hipError_t estimate_topp(const CacheView& c, float sm, const CandView& cand, voi
   // token ids of the candidates are read only by the passes that emit the union lists
   const bool need_tok = with_union || (wide && mass);
   e = launch_estimate(c, qdigits_of(ws, L), sm, cand, ncap, at<float>(ws, L.logits),
-                      need_tok ? at<int32_t>(ws, L.ctok) : nullptr, at<int32_t>(ws, L.crow), wide ? &wd : nullptr, s);
+                      need_tok ? at<int32_t>(ws, L.ctok) : nullptr, wide ? &wd : nullptr, s);
   if (e != hipSuccess) return e;
   if ((e = E.rec(5)) != hipSuccess) return e;
   if ((e = E.rec(6)) != hipSuccess) return e;
@@ -236,8 +235,8 @@ hipError_t estimate_topp(const CacheView& c, float sm, const CandView& cand, voi
 }
 
 // Attention over the top-p bitmaps (no compacted list needed) and the merge; events 8..11.
-// `cand` names where the K/V row of each candidate comes from: the selector's physical page list,
-// the page table (every token a candidate), or the rows the estimate recorded (ranges).
+// `cand` names where the K/V row of each candidate comes from: the selector's physical page list, or
+// the page table (every page a candidate page).
 hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, const CandView& cand, void* ws,
                          const Layout& L, float* out, float* lse, const Events& E, hipStream_t s,
                          bool headwise = false) {
@@ -249,7 +248,6 @@ hipError_t attend_masked(const CacheView& c, const uint16_t* q, float sm, const 
     mv.head_masks = at<uint32_t>(ws, L.masks);
   }
   mv.cand_mode = cand.mode;
-  mv.cand_row = at<int32_t>(ws, L.crow);
   mv.page_phys = cand.phys;
   mv.page_stride = cand.max_items;
   mv.ncap = L.ncap;

@@ -58,9 +58,9 @@ constexpr int kAttnSB = 16;  // tokens per sub-block
 // wave compacts its kept candidates' rows in LDS first); otherwise it is a range of a token list.
 // HW (with MK): head-wise -- a row read for the group's union counts for head h only when h's own
 // bitmap keeps it (the row's head bits travel with it through the compaction).
-// BYPAGE (with MK): the candidates are the pages of a list (the selector's, or every page), so a
-// sub-block's K/V rows follow from its page; otherwise each candidate's row was recorded.
-template <int G, int NSB, bool MK, bool HW = false, bool BYPAGE = false>
+// With MK the candidates are pages (the selector's list, or every page of the sequence), so a
+// sub-block's K/V rows follow from its page.
+template <int G, int NSB, bool MK, bool HW = false>
 __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uint16_t* __restrict__ q,
                                                           float sm_log2, ListView L, MaskView MV, int slots,
                                                           float* __restrict__ partials,
@@ -103,7 +103,6 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     // one page of the candidate list (w_begin is a multiple of 16).  One vector load per wave brings
     // the quarter's mask words (lane hh * NWQ + j: word j of head hh, or of the union) and another its
     // pages' physical ids (lane i: sub-block i); each sub-block then takes them with readlanes.
-    const int64_t ub = (int64_t)u * MV.ncap;
     const int mw = (int)(MV.ncap >> 5);
     constexpr int NWQ = NSB / 2 + 1;  // words a quarter can touch
     const int w0 = w_begin >> 5;
@@ -116,14 +115,11 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     const uint32_t mword = mbase[min(w0 + j_l, mw - 1)];
     int crw[NSB];
     int ph_l = 0;
-    if constexpr (BYPAGE) {
+    {
       const bool sel = MV.cand_mode == kCandPages;
       const int32_t* pbase = sel ? MV.page_phys + (int64_t)u * MV.page_stride : c.page_table + (int64_t)b * c.maxP;
       const int plim = sel ? MV.page_stride : c.maxP;
       ph_l = pbase[min((w_begin >> 4) + min(lane, NSB - 1), plim - 1)];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NSB; ++i) crw[i] = MV.cand_row[ub + w_begin + i * SB + (lane & 15)];
     }
     uint32_t wd[NSB];
     int hb[NSB];
@@ -144,7 +140,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
         }
         wd[i] = x;
       }
-      if constexpr (BYPAGE) crw[i] = (__builtin_amdgcn_readlane(ph_l, i) * c.Hkv + h) * kPage + (lane & 15);
+      crw[i] = (__builtin_amdgcn_readlane(ph_l, i) * c.Hkv + h) * kPage + (lane & 15);
     }
     int kept = 0;
 #pragma unroll
@@ -512,7 +508,7 @@ int attn_chunk_tokens(int64_t total_upper, int group) {
   return 64 * s;
 }
 
-template <bool MK, bool HW = false, bool BYPAGE = false>
+template <bool MK, bool HW = false>
 static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float sm, const ListView& list,
                                    const MaskView& mv, int chunk_tokens, int slots, float* partials,
                                    const MergeWs& mw, hipStream_t s) {
@@ -521,8 +517,8 @@ static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float 
   const dim3 grid((unsigned)((int64_t)c.B * c.Hkv * slots)), blk(64 * kAttnWaves);
 #define TWL_ATTN_G(GG, NS)                                                                                  \
   case GG:                                                                                                  \
-    hipLaunchKernelGGL((k_attn<GG, NS, MK, HW, BYPAGE>), grid, blk, 0, s, c, q, sm_log2, list, mv, slots,   \
-                       partials, mw.ticket, c.B * c.Hq);                                                   \
+    hipLaunchKernelGGL((k_attn<GG, NS, MK, HW>), grid, blk, 0, s, c, q, sm_log2, list, mv, slots, partials,  \
+                       mw.ticket, c.B * c.Hq);                                                             \
     break;
 #define TWL_ATTN_NSB(NS)                   \
   case NS * kAttnWaves * kAttnSB:          \
@@ -566,16 +562,13 @@ hipError_t launch_attn(const CacheView& c, const uint16_t* q, float sm, const Li
 hipError_t launch_attn_masked(const CacheView& c, const uint16_t* q, float sm, const MaskView& mv, int chunk_tokens,
                               int slots, float* partials, const MergeWs& mw, bool headwise, hipStream_t s) {
   if ((!mv.head_masks && !mv.union_words) || mv.ncap % chunk_tokens || !mw.ticket) return hipErrorInvalidValue;
-  if ((mv.cand_mode == kCandRanges && !mv.cand_row) || (mv.cand_mode == kCandPages && !mv.page_phys))
+  if ((mv.cand_mode != kCandPages && mv.cand_mode != kCandAll) || (mv.cand_mode == kCandPages && !mv.page_phys))
     return hipErrorInvalidValue;
-  const bool by_page = mv.cand_mode != kCandRanges;
   if (headwise) {
-    if (!mv.head_masks || !by_page) return hipErrorInvalidValue;
-    return launch_attn_impl<true, true, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
+    if (!mv.head_masks) return hipErrorInvalidValue;
+    return launch_attn_impl<true, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
   }
-  if (by_page)
-    return launch_attn_impl<true, false, true>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
-  return launch_attn_impl<true, false, false>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
+  return launch_attn_impl<true, false>(c, q, sm, ListView{}, mv, chunk_tokens, slots, partials, mw, s);
 }
 
 hipError_t launch_rows(const CacheView& c, const int32_t* indptr, const int32_t* tokens, int32_t* rows,

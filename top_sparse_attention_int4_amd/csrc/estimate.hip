@@ -12,19 +12,20 @@
 //   logit = float32(sm * r)
 // -- the float64 definition of the estimate for the grid query q~, rounded once to float32.
 //
-// The sums are v_mfma_i32_16x16x32_i8 products: A = 16 candidates x 32 codes (lane (r, kb) reads the
-// code run of group kb of candidate r with one load -- 16 bytes of 4-bit codes; 8 or 32 bytes for the
-// 2- and 8-bit widths of the precision ablation, paperlayer §4.2, Fig. 6 -- and feeds 8 codes as bytes
-// to each of four MFMAs; 8-bit codes go in as code - 128 with the columns started at 128 x the digit
-// sums), B = the query digits, one column per (group, head) and zero outside the lane's group, so
-// each output column accumulates one group of one head.  A wave takes 16-candidate tiles; the four
-// groups of a (candidate, head) then meet by two DPP row rotations in the committed order.
+// The sums are v_mfma_i32_16x16x32_i8 products: A = the query digits, one row per (head, group) and
+// zero outside the row's group; B = 32 codes x 16 candidates (lane (kb, nn) reads the code run of
+// group kb of candidate nn with one load -- 16 bytes of 4-bit codes; 8 or 32 bytes for the 2- and
+// 8-bit widths of the precision ablation, paperlayer §4.2, Fig. 6 -- and feeds 8 codes as bytes to
+// each of four MFMAs; 8-bit codes go in as code - 128 with the rows started at 128 x the digit sums).
+// A wave takes 16-candidate tiles; each result lane holds the four group sums of one (candidate,
+// head), so the groups meet in-lane in the committed order.
 //
-// Candidates given as pages (the base selector's output) or as every token: a 16-candidate tile is
-// one page, so each wave finds its tiles' physical pages with scalar loads and works on its own (no
-// exchange, no barrier); the attention later derives the K/V rows from the same page lists.
-// Candidates given as token ranges (the cluster stage): the block resolves its candidates' rows
-// together (prefix sums of the range lengths, binary search) and records them for the attention.
+// Candidates given as pages (the base selector's output) or as every page of the sequence (the plain
+// decode, and the cluster stage's kept tokens as slot masks): a 16-candidate tile is one page, so
+// each wave finds its tiles' physical pages with scalar loads and works on its own (no exchange, no
+// barrier); the attention later derives the K/V rows from the same pages.  Candidates given as token
+// ranges (a caller's list): the block resolves its candidates' rows together (prefix sums of the
+// range lengths, binary search).
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -161,110 +162,113 @@ __device__ __forceinline__ long code_operand(const uint32_t (&w)[BITS], int j) {
   }
 }
 
-// One wave's share of the contraction: its lane (kb, nn) holds the B operands of column nn = (group
-// gc, head ct GT + hl) of each column tile ct, and turns the MFMA results of a 16-candidate tile into
-// the logits of candidates 4 rg .. 4 rg + 3 for that column (rg = lane / 16).
+// One wave's share of the contraction, as products (query digits) x (codes): the A operand row
+// i = 4 hh + g holds head hh's digits of group g (zero outside the k-slice of group g), the B operand
+// column is a candidate (lane (kb, nn) feeds the code run of group kb of candidate nn), so the
+// result lane (rg, nn) holds the four group sums of head rg (of the row tile) for candidate nn and
+// forms that candidate's logit itself: the groups meet in-lane in the committed order, and the lane
+// reads its candidate's four (scale, zero) words with one load.
 template <int G, int BITS>
 struct EstWave {
-  static constexpr int GT = G < 4 ? G : 4;  // heads per 16-column MFMA tile (4 groups x GT heads)
-  static constexpr int NTL = G / GT;        // column tiles
-  int lane, kb, nn, rg, gc, hl;
-  bool colok;
-  long Bop[NTL][kQDigits][4];
-  double cscale[NTL], bcol[NTL];  // 2^(E_g - 20) and b_g of the lane's column
-  int acc0[NTL][kQDigits];        // 8-bit codes: 128 x the digit sums (codes enter as code - 128)
+  static constexpr int GT = G < 4 ? G : 4;  // heads per 16-row MFMA tile (GT heads x 4 groups)
+  static constexpr int NTL = G / GT;        // row tiles
+  int lane, kb, nn, rg;
+  bool rowok;                     // head rg of a row tile exists (rg < GT)
+  long Aop[NTL][kQDigits][4];     // digits of row nn = (head nn / 4, group nn % 4), zero unless kb is the group
+  double cscale[NTL][kGroups], bcol[NTL][kGroups];  // 2^(E_g - 20) and b_g of head rg, group g
+  int acc0[NTL][kQDigits][kGroups];  // 8-bit codes: 128 x the digit sums (codes enter as code - 128)
   double smd;
 
-  // the B operands and column constants of query rows bh0 .. bh0 + G - 1 (the unit's heads)
+  // the A operands and row constants of query rows bh0 .. bh0 + G - 1 (the unit's heads)
   __device__ __forceinline__ void init(const QDigits& qd, size_t bh0, float sm) {
     lane = threadIdx.x & 63;
     kb = lane >> 4;
     nn = lane & 15;
     rg = lane >> 4;
-    gc = nn / GT;
-    hl = nn - gc * GT;
-    colok = nn < kGroups * GT;
+    rowok = rg < GT;
     smd = (double)sm;
+    const int ah = nn >> 2, ag = nn & 3;  // this lane's A row
 #pragma unroll
     for (int ct = 0; ct < NTL; ++ct) {
-      const size_t gi = (bh0 + ct * GT + hl) * kGroups + (gc & 3);
-      const bool mine = colok && kb == gc;
+      const bool mine = ah < GT && kb == ag;
+      const size_t gi = (bh0 + ct * GT + min(ah, GT - 1)) * kGroups + ag;
       const u32x4_t* dg = reinterpret_cast<const u32x4_t*>(qd.dig + gi * kQDigits * 32);
 #pragma unroll
       for (int d = 0; d < kQDigits; ++d) {
         const u32x4_t x0 = mine ? dg[2 * d] : u32x4_t{0u, 0u, 0u, 0u};
         const u32x4_t x1 = mine ? dg[2 * d + 1] : u32x4_t{0u, 0u, 0u, 0u};
-        Bop[ct][d][0] = (long)((uint64_t)x0.x | ((uint64_t)x0.y << 32));
-        Bop[ct][d][1] = (long)((uint64_t)x0.z | ((uint64_t)x0.w << 32));
-        Bop[ct][d][2] = (long)((uint64_t)x1.x | ((uint64_t)x1.y << 32));
-        Bop[ct][d][3] = (long)((uint64_t)x1.z | ((uint64_t)x1.w << 32));
+        Aop[ct][d][0] = (long)((uint64_t)x0.x | ((uint64_t)x0.y << 32));
+        Aop[ct][d][1] = (long)((uint64_t)x0.z | ((uint64_t)x0.w << 32));
+        Aop[ct][d][2] = (long)((uint64_t)x1.x | ((uint64_t)x1.y << 32));
+        Aop[ct][d][3] = (long)((uint64_t)x1.z | ((uint64_t)x1.w << 32));
       }
-      const int32_t* mt = qd.meta + gi * kQMeta;
-      const int E = colok ? mt[0] : 0;
-      cscale[ct] = colok ? ldexp(1.0, E - kQFracBits) : 0.0;
-      bcol[ct] = colok ? (double)mt[1] * cscale[ct] : 0.0;  // exact
 #pragma unroll
-      for (int d = 0; d < kQDigits; ++d) acc0[ct][d] = (BITS == 8 && colok) ? 128 * mt[2 + d] : 0;
+      for (int g = 0; g < kGroups; ++g) {
+        const int32_t* mt = qd.meta + ((bh0 + ct * GT + min(rg, GT - 1)) * kGroups + g) * kQMeta;
+        const int E = rowok ? mt[0] : 0;
+        cscale[ct][g] = rowok ? ldexp(1.0, E - kQFracBits) : 0.0;
+        bcol[ct][g] = rowok ? (double)mt[1] * cscale[ct][g] : 0.0;  // exact
+#pragma unroll
+        for (int d = 0; d < kQDigits; ++d) acc0[ct][d][g] = (BITS == 8 && rowok) ? 128 * mt[2 + d] : 0;
+      }
     }
   }
 
-  // One tile: cw = this lane's code run (candidate nn, group kb), mw[e] = scale | zero << 16 of
-  // candidate 4 rg + e in group gc, ok[e] = whether that candidate exists.  Logits of the lane's four
-  // candidates for column tile ct land in lg[ct][e] (-inf for candidates that do not exist).
-  __device__ __forceinline__ void tile(const uint32_t (&cw)[BITS], const uint32_t (&mw)[4], const bool (&ok)[4],
-                                       float (&lg)[NTL][4]) const {
+  // One tile: cw = this lane's code run (candidate nn, group kb), mw = scale | zero << 16 of candidate
+  // nn in groups 0..3, ok = whether candidate nn exists.  The logit of candidate nn for head rg of row
+  // tile ct lands in lg[ct] (-inf for a candidate that does not exist).
+  __device__ __forceinline__ void tile(const uint32_t (&cw)[BITS], const u32x4_t& mw, bool ok,
+                                       float (&lg)[NTL]) const {
     i32x4_t acc[NTL][kQDigits];
 #pragma unroll
     for (int ct = 0; ct < NTL; ++ct)
 #pragma unroll
-      for (int d = 0; d < kQDigits; ++d) acc[ct][d] = i32x4_t{acc0[ct][d], acc0[ct][d], acc0[ct][d], acc0[ct][d]};
+      for (int d = 0; d < kQDigits; ++d)
+        acc[ct][d] = i32x4_t{acc0[ct][d][0], acc0[ct][d][1], acc0[ct][d][2], acc0[ct][d][3]};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long a = code_operand<BITS>(cw, j);
+      const long bcode = code_operand<BITS>(cw, j);
 #pragma unroll
       for (int ct = 0; ct < NTL; ++ct)
 #pragma unroll
         for (int d = 0; d < kQDigits; ++d)
-          acc[ct][d] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a, Bop[ct][d][j], acc[ct][d], 0, 0, 0);
+          acc[ct][d] = __builtin_amdgcn_mfma_i32_16x16x32_i8(Aop[ct][d][j], bcode, acc[ct][d], 0, 0, 0);
     }
+    const uint32_t mwv[kGroups] = {mw.x, mw.y, mw.z, mw.w};
 #pragma unroll
     for (int ct = 0; ct < NTL; ++ct) {
+      double t[kGroups];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int g = 0; g < kGroups; ++g) {
         double S;
         if constexpr (BITS == 8) {
           // up to 2^34 in magnitude: combined in float64 (exact below 2^53)
-          S = (double)acc[ct][0][e] * 16384.0 + (double)acc[ct][1][e] * 128.0 + (double)acc[ct][2][e];
+          S = (double)acc[ct][0][g] * 16384.0 + (double)acc[ct][1][g] * 128.0 + (double)acc[ct][2][g];
         } else {
           // |S| <= 2^14 * 128 * 15 * 32 + (2^14 - 1) * 15 * 32 < 2^31: exact in int32
-          S = (double)(acc[ct][0][e] * 16384 + acc[ct][1][e] * 128 + acc[ct][2][e]);
+          S = (double)(acc[ct][0][g] * 16384 + acc[ct][1][g] * 128 + acc[ct][2][g]);
         }
-        const double s = (double)half_bits_to_float(mw[e] & 0xffffu);
-        const double z = (double)half_bits_to_float(mw[e] >> 16);
-        const double t = fma(s, S * cscale[ct], z * bcol[ct]);  // s a_g and z b_g are exact: one rounding
-        // groups meet along the row of 16 lanes (a rotation by 16 - N brings lane n + N to lane n):
-        // column gc GT + hl reads group gc + 1, then gc + 2
-        const double t01 = t + dpp_row_ror_f64<16 - GT>(t);          // (t0 + t1) in the lanes of group 0
-        const double r = t01 + dpp_row_ror_f64<16 - 2 * GT>(t01);    // (t0 + t1) + (t2 + t3)
-        lg[ct][e] = ok[e] ? (float)(smd * r) : -__builtin_inff();
+        const double s = (double)half_bits_to_float(mwv[g] & 0xffffu);
+        const double z = (double)half_bits_to_float(mwv[g] >> 16);
+        t[g] = fma(s, S * cscale[ct][g], z * bcol[ct][g]);  // s a_g and z b_g are exact: one rounding
       }
+      const double r = (t[0] + t[1]) + (t[2] + t[3]);
+      lg[ct] = (ok && rowok) ? (float)(smd * r) : -__builtin_inff();
     }
   }
 };
 
-// The block's largest logit per head over its waves' maxima (lanes of group 0 hold a head each).
+// The block's largest logit per head over its waves' maxima (lanes 16 rg .. 16 rg + 15 hold head rg).
 template <int G, int BITS>
 __device__ __forceinline__ void block_head_max(const EstWave<G, BITS>& ew, const float (&mx)[EstWave<G, BITS>::NTL],
                                                float (*s_max)[G], int wv, float* pmax_row, int stride) {
   constexpr int GT = EstWave<G, BITS>::GT, NTL = EstWave<G, BITS>::NTL;
 #pragma unroll
   for (int ct = 0; ct < NTL; ++ct) {
-    float v = (ew.colok && ew.gc == 0) ? mx[ct] : -__builtin_inff();
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
+    float v = ew.rowok ? mx[ct] : -__builtin_inff();
 #pragma unroll
-    for (int s = GT; s < 16; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
-    if (ew.lane < GT) s_max[wv][ct * GT + ew.lane] = v;
+    for (int s = 1; s < 16; s <<= 1) v = fmaxf(v, __shfl_xor(v, s));
+    if (ew.rowok && ew.nn == 0) s_max[wv][ct * GT + ew.rg] = v;
   }
   __syncthreads();
   if (threadIdx.x < G) {
@@ -320,47 +324,37 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
   }
   EW ew;
   ew.init(qd, (size_t)b * c.Hq + (size_t)h * G, sm);
-  // a tile exists when its page does; its candidate k exists when page * 16 + k is a token
-  bool tok_ok[NB][4];
+  // a tile exists when its page does; its candidate nn exists when page * 16 + nn is a token of the
+  // page's candidate slots
+  bool tok_ok[NB];
   uint32_t cw[NB][BITS];
-  uint32_t mw[NB][4];
+  u32x4_t mw[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const bool pg_ok = page[i] >= 0 && page[i] * kPage < n && (unsigned)phys[i] < (unsigned)c.nphys;
-    const int row0 = pg_ok ? (phys[i] * c.Hkv + h) * kPage : 0;
-    load_codes<BITS>(c.k4 + (size_t)(row0 + ew.nn) * (16 * BITS), ew.kb, cw[i]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int slot = 4 * ew.rg + e;
-      mw[i][e] = c.k4_meta[(size_t)(row0 + slot) * kGroups + (ew.gc & 3)];
-      tok_ok[i][e] = pg_ok && page[i] * kPage + slot < n && ((slots[i] >> slot) & 1u);
-    }
+    const int row = (pg_ok ? (phys[i] * c.Hkv + h) * kPage : 0) + ew.nn;
+    load_codes<BITS>(c.k4 + (size_t)row * (16 * BITS), ew.kb, cw[i]);
+    mw[i] = *reinterpret_cast<const u32x4_t*>(c.k4_meta + (size_t)row * kGroups);
+    tok_ok[i] = pg_ok && page[i] * kPage + ew.nn < n && ((slots[i] >> ew.nn) & 1u);
   }
   if (cand_tok && ew.kb == 0) {
     // token ids of the candidates, for the union lists (lane nn of each tile)
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const bool pg_ok = page[i] >= 0 && page[i] * kPage < n && (unsigned)phys[i] < (unsigned)c.nphys;
-      const int t = page[i] * kPage + ew.nn;
-      const bool ok = pg_ok && t < n && ((slots[i] >> ew.nn) & 1u);
-      cand_tok[(size_t)u * ncap + (size_t)(tp0 + i) * kPage + ew.nn] = ok ? t : -1;
-    }
+    for (int i = 0; i < NB; ++i)
+      cand_tok[(size_t)u * ncap + (size_t)(tp0 + i) * kPage + ew.nn] = tok_ok[i] ? page[i] * kPage + ew.nn : -1;
   }
   float mx[NTL];
 #pragma unroll
   for (int ct = 0; ct < NTL; ++ct) mx[ct] = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    float lg[NTL][4];
+    float lg[NTL];
     ew.tile(cw[i], mw[i], tok_ok[i], lg);
 #pragma unroll
     for (int ct = 0; ct < NTL; ++ct) {
-      mx[ct] = fmaxf(fmaxf(mx[ct], fmaxf(lg[ct][0], lg[ct][1])), fmaxf(lg[ct][2], lg[ct][3]));
-      if (ew.colok && ew.gc == 0) {
-        const int k = (tp0 + i) * kPage + 4 * ew.rg;
-        *reinterpret_cast<float4*>(logits + ((size_t)b * c.Hq + (size_t)h * G + ct * GT + ew.hl) * ncap + k) =
-            make_float4(lg[ct][0], lg[ct][1], lg[ct][2], lg[ct][3]);
-      }
+      mx[ct] = fmaxf(mx[ct], lg[ct]);
+      if (ew.rowok)
+        logits[((size_t)b * c.Hq + (size_t)h * G + ct * GT + ew.rg) * ncap + (size_t)(tp0 + i) * kPage + ew.nn] = lg[ct];
     }
   }
   if (pmax) {
@@ -376,8 +370,7 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
 template <int G, int NB, int BITS>
 __global__ __launch_bounds__(256) void k_estimate_ranges(CacheView c, QDigits qd, float sm, CandView cand, int ncap,
                                                          int chunks_per_unit, float* __restrict__ logits,
-                                                         int32_t* __restrict__ cand_tok,
-                                                         int32_t* __restrict__ cand_row, float* __restrict__ pmax,
+                                                         int32_t* __restrict__ cand_tok, float* __restrict__ pmax,
                                                          uint64_t* __restrict__ wstate, size_t wstate_words) {
   using EW = EstWave<G, BITS>;
   constexpr int NC = 64 * NB;
@@ -452,26 +445,21 @@ __global__ __launch_bounds__(256) void k_estimate_ranges(CacheView c, QDigits qd
       }
       s_row[bt][lane] = row;
       if (cand_tok) cand_tok[(size_t)u * ncap + k] = row >= 0 ? tok : -1;
-      cand_row[(size_t)u * ncap + k] = row;
     }
   }
   __syncthreads();  // rows in LDS
 
   // ---- this wave's tiles (wv, wv + 4, ...): code and scale/zero loads all in flight together
   uint32_t cw[NB][BITS];
-  uint32_t mw[NB][4];
-  bool ok[NB][4];
+  u32x4_t mw[NB];
+  bool ok[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int ti = wv + 4 * i;
     const int ra = (&s_row[0][0])[16 * ti + ew.nn];
     load_codes<BITS>(c.k4 + (size_t)max(ra, 0) * (16 * BITS), ew.kb, cw[i]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rwe = (&s_row[0][0])[16 * ti + 4 * ew.rg + e];
-      mw[i][e] = c.k4_meta[(size_t)max(rwe, 0) * kGroups + (ew.gc & 3)];
-      ok[i][e] = rwe >= 0;
-    }
+    mw[i] = *reinterpret_cast<const u32x4_t*>(c.k4_meta + (size_t)max(ra, 0) * kGroups);
+    ok[i] = ra >= 0;
   }
   float mx[NTL];
 #pragma unroll
@@ -479,16 +467,13 @@ __global__ __launch_bounds__(256) void k_estimate_ranges(CacheView c, QDigits qd
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int ti = wv + 4 * i;
-    float lg[NTL][4];
+    float lg[NTL];
     ew.tile(cw[i], mw[i], ok[i], lg);
 #pragma unroll
     for (int ct = 0; ct < NTL; ++ct) {
-      mx[ct] = fmaxf(fmaxf(mx[ct], fmaxf(lg[ct][0], lg[ct][1])), fmaxf(lg[ct][2], lg[ct][3]));
-      if (ew.colok && ew.gc == 0) {
-        const int k = k0 + 16 * ti + 4 * ew.rg;
-        *reinterpret_cast<float4*>(logits + ((size_t)b * c.Hq + (size_t)h * G + ct * GT + ew.hl) * ncap + k) =
-            make_float4(lg[ct][0], lg[ct][1], lg[ct][2], lg[ct][3]);
-      }
+      mx[ct] = fmaxf(mx[ct], lg[ct]);
+      if (ew.rowok)
+        logits[((size_t)b * c.Hq + (size_t)h * G + ct * GT + ew.rg) * ncap + k0 + 16 * ti + ew.nn] = lg[ct];
     }
   }
   if (pmax) {
@@ -524,10 +509,9 @@ int est_batches(int64_t ncap, int64_t units) {
 }
 
 hipError_t launch_estimate(const CacheView& c, const QDigits& qd, float sm, const CandView& cand, int ncap,
-                           float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s) {
+                           float* logits, int32_t* cand_tok, const WideWs* wide, hipStream_t s) {
   const int nb = est_batches(ncap, (int64_t)c.B * c.Hkv);
   if (ncap % (64 * nb) || ncap % kEstCands) return hipErrorInvalidValue;
-  if (cand.mode == kCandRanges && !cand_row) return hipErrorInvalidValue;
   const int cpu = ncap / (64 * nb);
   dim3 grid((unsigned)(c.B * c.Hkv * cpu));
   float* pmax = wide ? wide->pmax : nullptr;
@@ -537,7 +521,7 @@ hipError_t launch_estimate(const CacheView& c, const QDigits& qd, float sm, cons
   case GG:                                                                                                       \
     if (cand.mode == kCandRanges)                                                                                \
       hipLaunchKernelGGL((k_estimate_ranges<GG, NB, BB>), grid, dim3(256), 0, s, c, qd, sm, cand, ncap, cpu,     \
-                         logits, cand_tok, cand_row, pmax, wst, wwords);                                        \
+                         logits, cand_tok, pmax, wst, wwords);                                        \
     else if (cand.mode == kCandPages)                                                                            \
       hipLaunchKernelGGL((k_estimate_pages<GG, NB, BB, kCandPages>), grid, dim3(256), 0, s, c, qd, sm, cand,     \
                          ncap, cpu, logits, cand_tok, pmax, wst, wwords);                                        \

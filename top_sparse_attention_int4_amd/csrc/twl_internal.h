@@ -117,11 +117,9 @@ hipError_t launch_page_select(const CacheView& c, const float* scores, float kee
 hipError_t launch_range_prefix(const CacheView& c, const CandView& cand, int32_t* prefix, int32_t* chunk_first,
                                int nchunk, hipStream_t s);
 // wide: when non-null, the estimate also writes the per-block logit maxima and clears the wide state;
-// cand_tok may be null when no union list is emitted afterwards; cand_row (the K/V row of every
-// candidate) is written for the ranges form only -- for pages and all tokens the attention derives
-// rows from the page lists
+// cand_tok may be null when no union list is emitted afterwards
 hipError_t launch_estimate(const CacheView& c, const QDigits& qd, float sm, const CandView& cand, int ncap,
-                           float* logits, int32_t* cand_tok, int32_t* cand_row, const WideWs* wide, hipStream_t s);
+                           float* logits, int32_t* cand_tok, const WideWs* wide, hipStream_t s);
 // wide top-p: histogram passes and masks (union bitmap in wd.uwords); the emit kernel writes the
 // compacted union lists and the threshold/mass outputs
 // full: the mask pass also writes the head masks, the kept mass and the per-chunk union counts
@@ -169,8 +167,7 @@ int attn_chunk_tokens(int64_t total_upper, int group);
 struct MaskView {
   const uint32_t* head_masks;   // [B*Hq][ncap/32] per-head bitmaps (OR-ed over the group), or
   const uint32_t* union_words;  // [B*Hkv][ncap/32] union bitmaps (used when non-null)
-  int cand_mode;                // kCandPages / kCandAll: rows from the page lists; kCandRanges: cand_row
-  const int32_t* cand_row;      // [B*Hkv][ncap] K/V row of each candidate (ranges)
+  int cand_mode;                // kCandPages / kCandAll: rows from the page list / the page table
   const int32_t* page_phys;     // [B*Hkv][page_stride] physical page of each kept page (pages)
   int page_stride;
   int64_t ncap;
