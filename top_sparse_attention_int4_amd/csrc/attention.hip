@@ -80,7 +80,8 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
   if (blockIdx.x == 0)
     for (int i = tid; i < nticket; i += 64 * NWV) merge_ticket[i] = 0;
   // chunk slot k of unit u (the unit's chunks are its first ceil(count / CH) slots)
-  const int u = blockIdx.x / slots, k = blockIdx.x - u * slots;
+  int k;
+  const int u = head_fast_unit(blockIdx.x, c.Hkv, slots, k);
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int t_begin = k * CH;
   const int w_begin = t_begin + wv * QL;
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     }
   }
   __syncthreads();
-  float* part = partials + (size_t)blockIdx.x * G * kPartStride;
+  float* part = partials + ((size_t)u * slots + k) * G * kPartStride;
   for (int t = tid; t < G * 32; t += 64 * NWV) {
     const int hh = t >> 5, d4 = t & 31;
     float M = -__builtin_inff();

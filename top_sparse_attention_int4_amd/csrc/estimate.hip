@@ -288,8 +288,8 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
                                                         uint64_t* __restrict__ wstate, size_t wstate_words) {
   using EW = EstWave<G, BITS>;
   constexpr int GT = EW::GT, NTL = EW::NTL;
-  const int u = blockIdx.x / chunks_per_unit;
-  const int ck = blockIdx.x - u * chunks_per_unit;
+  int ck;
+  const int u = head_fast_unit(blockIdx.x, c.Hkv, chunks_per_unit, ck);
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   if (wstate) {

@@ -25,8 +25,8 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
                                                                      float* __restrict__ scores,
                                                                      int blocks_per_unit) {
   constexpr int NT = 64 * (G > 4 ? G : 4);
-  const int u = blockIdx.x / blocks_per_unit;
-  const int blk = blockIdx.x - u * blocks_per_unit;
+  int blk;
+  const int u = head_fast_unit(blockIdx.x, c.Hkv, blocks_per_unit, blk);
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   if (blk * 64 >= c.maxP) return;
   const int hh = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -139,8 +139,8 @@ template <int G>
 __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
                                                          float* __restrict__ scores, int blocks_per_unit) {
   constexpr int RS = 17;  // LDS row of a page: 16 x 16 B of one half (mn 64 ch, mx 64 ch) + 16 B pad
-  const int u = blockIdx.x / blocks_per_unit;
-  const int blk = blockIdx.x - u * blocks_per_unit;
+  int blk;
+  const int u = head_fast_unit(blockIdx.x, c.Hkv, blocks_per_unit, blk);
   const int b = u / c.Hkv, h = u - b * c.Hkv;
   const int lane = threadIdx.x;
 

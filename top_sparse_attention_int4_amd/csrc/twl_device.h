@@ -286,6 +286,17 @@ __device__ __forceinline__ float exp_diff(float a, float b) {
 // Clamp helpers
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// Block index of a grid over (sequence b, item k, kv-head h) with the kv-head fastest: the blocks that
+// take item k of a sequence for its kv-heads are dispatched side by side, so their reads of one page's
+// per-head slices, which are adjacent in the paged cache, reach HBM together.  Returns the unit
+// u = b * Hkv + h and writes the item.
+__device__ __forceinline__ int head_fast_unit(int bid, int Hkv, int items, int& k) {
+  const int h = bid % Hkv, r = bid / Hkv;
+  const int b = r / items;
+  k = r - b * items;
+  return b * Hkv + h;
+}
+
 // DPP row rotation of a 64-bit value: within each row of 16 lanes, rotated right by N (lane n receives
 // lane (n - N) mod 16).
 // (Every lane has a source inside its row, so no lane keeps an old value: a plain DPP move.)
