@@ -34,11 +34,15 @@
  * ------------------------------------------------------------------------------
  *   k, v      bf16 [num_phys_pages][Hkv][16][128]     token t of sequence b: physical page
  *                                                     page_table[b][t/16], slot t%16
- *   k4        u8   [num_phys_pages][Hkv][16][16*kb]   key codes of kb = key_bits bits, 8/kb per byte with the
- *                                                     lowest channel in the lowest bits (kb = 4: byte j =
- *                                                     code(2j) | code(2j+1)<<4)
- *   k4_meta   fp16 [num_phys_pages][Hkv][16][4][2]    per 32-channel group: (scale, zero)
- *   kbound    bf16 [num_phys_pages][Hkv][2][128]      per page: channel-wise key min row, max row
+ *   k4        u8   [B][max_pages_per_seq][Hkv][16][16*kb]   key codes of token t of sequence b at
+ *                                                     [b][t/16][.][t%16], kb = key_bits bits, 8/kb per byte
+ *                                                     with the lowest channel in the lowest bits (kb = 4:
+ *                                                     byte j = code(2j) | code(2j+1)<<4)
+ *   k4_meta   fp16 [B][max_pages_per_seq][Hkv][16][4][2]  per 32-channel group: (scale, zero)
+ *   kbound    bf16 [B][max_pages_per_seq][Hkv][2][128]    per logical page: channel-wise key min row, max row
+ *   The INT4 shadow is the library's own derived data: it is stored by (sequence, logical page), not
+ *   paged, so that the page selector and the weight estimate address it without a page-table lookup
+ *   (only the attention, which reads the paged K and V, translates pages).
  *   q         bf16 [B][Hq][128]; query head hq belongs to kv-head hq / G
  */
 #ifndef TWL_H

@@ -21,6 +21,17 @@ from tests import kernel_model
 SM = twl.DEFAULT_SM_SCALE
 
 
+def shadow_by_phys(w, arr):
+    """A shadow array of the library, stored [B][max_pages][...] by logical page, rearranged into the
+    physical page order [P][...] of the cache (pages no sequence maps stay zero)."""
+    arr = np.asarray(arr)
+    out = np.zeros((w.k_pages.shape[0],) + arr.shape[2:], arr.dtype)
+    for b, n in enumerate(w.seq_lens):
+        npg = -(-int(n) // 16)
+        out[w.page_table[b, :npg]] = arr[b, :npg]
+    return out
+
+
 def oracle_decode(w, **kw):
     """The oracle's decode with the ambiguity band of the estimate kernel's stated precision."""
     return pipeline.decode(w, band=kernel_model.band, **kw)

@@ -32,6 +32,8 @@ twl_status check_cache(const twl_cache* c, bool need_kv, bool need_quant) {
   if (c->max_seq_len < 0 || (int64_t)c->max_seq_len > 16 * (int64_t)c->max_pages_per_seq) return TWL_EINVAL;
   if ((int64_t)c->num_phys_pages * c->num_kv_heads * 16 >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
   if ((int64_t)c->batch * c->max_pages_per_seq >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
+  // rows of the codes (stored by sequence and logical page) are int32
+  if ((int64_t)c->batch * c->max_pages_per_seq * c->num_kv_heads * 16 >= ((int64_t)1 << 31)) return TWL_EUNSUPPORTED;
   if ((int64_t)c->batch * c->num_kv_heads > 65535) return TWL_EUNSUPPORTED;
   // int32 CSR offsets and candidate indices over all units (with headroom for padded capacities)
   if ((int64_t)c->batch * c->num_q_heads * c->max_seq_len > ((int64_t)1 << 31) / 4) return TWL_EUNSUPPORTED;

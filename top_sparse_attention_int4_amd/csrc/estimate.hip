@@ -21,11 +21,12 @@
 // head), so the groups meet in-lane in the committed order.
 //
 // Candidates given as pages (the base selector's output) or as every page of the sequence (the plain
-// decode, and the cluster stage's kept tokens as slot masks): a 16-candidate tile is one page, so
-// each wave finds its tiles' physical pages with scalar loads and works on its own (no exchange, no
-// barrier); the attention later derives the K/V rows from the same pages.  Candidates given as token
-// ranges (a caller's list): the block resolves its candidates' rows together (prefix sums of the
-// range lengths, binary search).
+// decode, and the cluster stage's kept tokens as slot masks): a 16-candidate tile is one page, and
+// the codes are stored by (sequence, logical page), so each wave addresses its tiles' codes from the
+// page ids alone and works on its own (no exchange, no barrier, no page-table lookup); the attention
+// later derives the K/V rows from the same pages.  Candidates given as token ranges (a caller's
+// list): the block resolves its candidates' rows together (prefix sums of the range lengths, binary
+// search).
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -278,7 +279,7 @@ __device__ __forceinline__ void block_head_max(const EstWave<G, BITS>& ew, const
   }
 }
 
-// Candidates as pages (MODE kCandPages, physical pages listed by the selector) or as every page of the
+// Candidates as pages (MODE kCandPages, logical pages listed by the selector) or as every page of the
 // sequence (kCandAll), either optionally with a mask of each page's candidate slots (the cluster
 // stage's): NB 16-candidate tiles (pages) per wave, 4 waves per block, 64 NB candidates per block.
 template <int G, int NB, int BITS, int MODE>
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
   // the wave's tiles: pages tp0 .. tp0 + NB - 1 of the unit's candidate list (wave-uniform values)
   const int tp0 = ck * 4 * NB + wv * NB;
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  int page[NB], phys[NB];
+  int page[NB];
   uint32_t slots[NB];  // which of the page's 16 tokens are candidates
   if constexpr (MODE == kCandPages) {
     const int cnt = clampi(cand.count[u], 0, cand.max_items);
@@ -309,16 +310,14 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
       const size_t idx = (size_t)u * cand.max_items + min(tp0 + i, cand.max_items - 1);
       page[i] = cand.items[idx];
       if (tp0 + i >= cnt) page[i] = -1;
-      // the selector lists the physical pages too; a caller's page list is looked up in the table
-      phys[i] = cand.phys ? cand.phys[idx]
-                          : c.page_table[(size_t)b * c.maxP + clampi(page[i], 0, c.maxP - 1)];
       slots[i] = cand.slot_mask ? cand.slot_mask[idx] : 0xFFFFu;
     }
   } else {
+    // every page of the sequence: the codes' addresses need no load (stored by logical page), so
+    // they are in flight together with the slot masks
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       page[i] = tp0 + i;
-      phys[i] = c.page_table[(size_t)b * c.maxP + min(tp0 + i, c.maxP - 1)];
       slots[i] = cand.slot_mask ? cand.slot_mask[(size_t)u * c.maxP + min(tp0 + i, c.maxP - 1)] : 0xFFFFu;
     }
   }
@@ -331,8 +330,8 @@ __global__ __launch_bounds__(256) void k_estimate_pages(CacheView c, QDigits qd,
   u32x4_t mw[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const bool pg_ok = page[i] >= 0 && page[i] * kPage < n && (unsigned)phys[i] < (unsigned)c.nphys;
-    const int row = (pg_ok ? (phys[i] * c.Hkv + h) * kPage : 0) + ew.nn;
+    const bool pg_ok = page[i] >= 0 && page[i] * kPage < n;
+    const int row = (pg_ok ? ((b * c.maxP + page[i]) * c.Hkv + h) * kPage : 0) + ew.nn;
     load_codes<BITS>(c.k4 + (size_t)row * (16 * BITS), ew.kb, cw[i]);
     mw[i] = *reinterpret_cast<const u32x4_t*>(c.k4_meta + (size_t)row * kGroups);
     tok_ok[i] = pg_ok && page[i] * kPage + ew.nn < n && ((slots[i] >> ew.nn) & 1u);
@@ -438,11 +437,7 @@ __global__ __launch_bounds__(256) void k_estimate_ranges(CacheView c, QDigits qd
         if (p0 <= k) t = beg + (k - p0);
       }
       const int tok = (t >= 0 && t < n) ? t : -1;
-      int row = -1;
-      if (tok >= 0) {
-        const int ph = c.page_table[(size_t)b * c.maxP + (tok >> 4)];
-        if ((unsigned)ph < (unsigned)c.nphys) row = (ph * c.Hkv + h) * kPage + (tok & 15);
-      }
+      const int row = tok >= 0 ? ((b * c.maxP + (tok >> 4)) * c.Hkv + h) * kPage + (tok & 15) : -1;
       s_row[bt][lane] = row;
       if (cand_tok) cand_tok[(size_t)u * ncap + k] = row >= 0 ? tok : -1;
     }

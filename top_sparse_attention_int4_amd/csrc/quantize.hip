@@ -3,6 +3,8 @@
 // Twilight keeps a 4-bit copy of K for weight estimation (Paper-Notes "关键设计 / 4-bit K缓存量化";
 // paperlayer §4.2 and §B.1: dynamic quantisation with fp16 scales and zero points, two values per
 // byte).  One workgroup handles one (page, kv-head): 64 lanes = 16 slots x 4 groups of 32 channels.
+// The codes, scale/zero and bounds are stored by (sequence, logical page), so the selector and the
+// estimate read them without a page-table lookup; only K itself comes from the physical page.
 // The page tile is read once (4 KB, coalesced) into LDS; each lane quantises its (slot, group) and
 // then recomputes two channels of the page's min/max bound (Quest-style key bounds used by the page
 // selector) over the slots that hold tokens below tok_end.
@@ -27,7 +29,8 @@ __global__ __launch_bounds__(64) void k_quantize(CacheView c, const int32_t* __r
   if (phys < 0 || phys >= c.nphys) return;
 
   __shared__ uint32_t tile[kPage * kD / 2];  // 16 slots x 128 bf16
-  const size_t row0 = ((size_t)phys * c.Hkv + h) * kPage;
+  const size_t row0 = ((size_t)phys * c.Hkv + h) * kPage;           // K: the physical page
+  const size_t lrow0 = (((size_t)b * c.maxP + page) * c.Hkv + h) * kPage;  // codes: the logical page
   const uint4* src = reinterpret_cast<const uint4*>(c.k + row0 * kD);
   const int tid = threadIdx.x;
 #pragma unroll
@@ -70,10 +73,10 @@ __global__ __launch_bounds__(64) void k_quantize(CacheView c, const int32_t* __r
         packed[i / PER] |= code << (BITS * (i % PER));
       }
     }
-    uint32_t* dst = reinterpret_cast<uint32_t*>(c.k4 + (row0 + slot) * (16 * BITS)) + g * BITS;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(c.k4 + (lrow0 + slot) * (16 * BITS)) + g * BITS;
 #pragma unroll
     for (int i = 0; i < BITS; ++i) dst[i] = packed[i];
-    c.k4_meta[(row0 + slot) * kGroups + g] = sbits | (zbits << 16);
+    c.k4_meta[(lrow0 + slot) * kGroups + g] = sbits | (zbits << 16);
   }
 
   // ---- page bound over slots holding tokens < tok_end: lane owns channels 2*tid, 2*tid+1 ----------
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(64) void k_quantize(CacheView c, const int32_t* __r
     mx0 = fmaxf(mx0, a);
     mx1 = fmaxf(mx1, bb);
   }
-  uint32_t* kb = reinterpret_cast<uint32_t*>(c.kbound + ((size_t)phys * c.Hkv + h) * 2 * kD);
+  uint32_t* kb = reinterpret_cast<uint32_t*>(c.kbound + (((size_t)b * c.maxP + page) * c.Hkv + h) * 2 * kD);
   kb[tid] = (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xffff0000u);
   kb[64 + tid] = (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xffff0000u);
 }

@@ -36,30 +36,20 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
   __shared__ float qpos[G][kD];
   __shared__ float qneg[G][kD];
   __shared__ float sig[G][64];
-  const int32_t* pt = c.page_table + (size_t)b * c.maxP;
   constexpr int R = 64 * 32 / NT;
-  int phys[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {  // page-table reads in flight with the sequence length
-    const int j = blk * 64 + ((int)threadIdx.x >> 5) + r * (NT / 32);
-    phys[r] = pt[min(j, c.maxP - 1)];
-  }
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
   if (blk * 64 >= P) return;
   {
-    // then all bound reads, so every load of the tile is in flight at once
+    // every bound read of the tile in flight at once (the bounds are stored by logical page)
     const int part = threadIdx.x & 31;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int j = blk * 64 + ((int)threadIdx.x >> 5) + r * (NT / 32);
-      if (j >= P) phys[r] = -1;
-    }
     uint4 v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const uint4* src = reinterpret_cast<const uint4*>(c.kbound + ((size_t)max(phys[r], 0) * c.Hkv + h) * 2 * kD);
-      v[r] = (phys[r] >= 0) ? src[part] : make_uint4(0u, 0u, 0u, 0u);
+      const int j = blk * 64 + ((int)threadIdx.x >> 5) + r * (NT / 32);
+      const uint4* src =
+          reinterpret_cast<const uint4*>(c.kbound + (((size_t)b * c.maxP + min(j, P - 1)) * c.Hkv + h) * 2 * kD);
+      v[r] = (j < P) ? src[part] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) tile[((int)threadIdx.x >> 5) + r * (NT / 32)][part] = v[r];
@@ -146,9 +136,8 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
 
   __shared__ uint4 tile[64 * RS];
   __shared__ float4 qp[G][kD / 4], qn[G][kD / 4];
-  // the page-table entry of this lane's page, in flight with the sequence length and q
+  // this lane's page (the bounds are stored by logical page: no page-table lookup)
   const int j = blk * 64 + lane;
-  int phys = c.page_table[(size_t)b * c.maxP + min(j, c.maxP - 1)];
   const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
   uint32_t qw[G * kD / 128];  // two bf16 channels per word, G * 64 words over 64 lanes
 #pragma unroll
@@ -156,7 +145,7 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
   if (blk * 64 >= P) return;  // uniform
-  if (j >= P) phys = -1;
+  const int lpg = min(j, P - 1);  // a lane past the sequence reads its last page and is dropped
   // q+ and q- of every (head, channel) into LDS: lane l holds channels 2l, 2l + 1 of head i
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -174,8 +163,8 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
   const uint4* rowp[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int pg = __shfl(phys, 4 * r + (lane >> 4));
-    rowp[r] = reinterpret_cast<const uint4*>(c.kbound + ((size_t)max(pg, 0) * c.Hkv + h) * 2 * kD) +
+    const int pg = __shfl(lpg, 4 * r + (lane >> 4));
+    rowp[r] = reinterpret_cast<const uint4*>(c.kbound + (((size_t)b * c.maxP + pg) * c.Hkv + h) * 2 * kD) +
               (seg < 8 ? 0 : 16) + (seg & 7);
   }
   // both halves in flight at once (32 x 16 B per lane); the tile then stages one half at a time
