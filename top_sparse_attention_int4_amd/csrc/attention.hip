@@ -231,6 +231,9 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2f(m_run - m_new);
+    // once the running maxima settle most sub-blocks leave every head's scale at exactly 1: the
+    // rescaling of the accumulators is then skipped (wave-uniform; multiplying by 1 changes nothing)
+    const bool rescale = __ballot(nn < G && alpha != 1.f) != 0ull;
     float ps = 0.f;
     float pv[4];
 #pragma unroll
@@ -250,11 +253,13 @@ __global__ __launch_bounds__(64 * kAttnWaves) void k_attn(CacheView c, const uin
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (rescale) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      const float a = Al[wv][hh];
+      for (int hh = 0; hh < G; ++hh) {
+        const float a = Al[wv][hh];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[hh][i] *= a;
+        for (int i = 0; i < 8; ++i) acc[hh][i] *= a;
+      }
     }
 #pragma unroll
     for (int s2 = 0; s2 < VS; ++s2) {
