@@ -61,6 +61,16 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
     e[j] = (k < ncap) ? lg[k] : -__builtin_inff();
     mloc = fmaxf(mloc, e[j]);
   }
+  // weighted mode: the multiplicities in flight together with the logits
+  int mk[W ? E : 1];
+  if constexpr (W) {
+    const int32_t* mu = mult + (size_t)(bh / c.G) * mult_stride;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int k = j * NT + tid;
+      mk[j] = (k < mult_stride) ? mu[k] : -1;
+    }
+  }
   for (int i = tid; i < 2048; i += NT) h1[i] = 0ull;
   if (tid < 512) {
     h2[tid] = 0ull;
@@ -69,13 +79,11 @@ __global__ __launch_bounds__(1024) void k_topp(CacheView c, const float* __restr
   const float M = br.max(mloc);  // its barrier also orders the clearing above
   float Z = 0.f;
   if (M != -__builtin_inff()) {
-    const int32_t* mu = W ? mult + (size_t)(bh / c.G) * mult_stride : nullptr;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       e[j] = (e[j] == -__builtin_inff()) ? -1.f : exp_diff(e[j], M);
-      if (W) {
-        const int k = j * NT + tid;
-        if (e[j] >= 0.f) e[j] = (k < mult_stride) ? (float)mu[k] * e[j] : -1.f;
+      if constexpr (W) {
+        if (e[j] >= 0.f) e[j] = (mk[j] >= 0) ? (float)mk[j] * e[j] : -1.f;
       }
       if (e[j] >= 0.f) Z += e[j];
     }
