@@ -37,26 +37,35 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
   __shared__ float qneg[G][kD];
   __shared__ float sig[G][64];
   constexpr int R = 64 * 32 / NT;
-  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int P = (n + kPage - 1) / kPage;
-  if (blk * 64 >= P) return;
+  constexpr int QR = (G * kD + NT - 1) / NT;  // query channels per thread
+  const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
+  uint16_t qr[QR];
+#pragma unroll
+  for (int i = 0; i < QR; ++i) qr[i] = qg[min((int)threadIdx.x + i * NT, G * kD - 1)];
+  int P;
   {
-    // every bound read of the tile in flight at once (the bounds are stored by logical page)
+    // every bound read of the tile in flight at once, with the sequence length (the bounds are stored
+    // by logical page; pages past the sequence are read from its allocated range and dropped)
     const int part = threadIdx.x & 31;
     uint4 v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int j = blk * 64 + ((int)threadIdx.x >> 5) + r * (NT / 32);
       const uint4* src =
-          reinterpret_cast<const uint4*>(c.kbound + (((size_t)b * c.maxP + min(j, P - 1)) * c.Hkv + h) * 2 * kD);
-      v[r] = (j < P) ? src[part] : make_uint4(0u, 0u, 0u, 0u);
+          reinterpret_cast<const uint4*>(c.kbound + (((size_t)b * c.maxP + min(j, c.maxP - 1)) * c.Hkv + h) * 2 * kD);
+      v[r] = src[part];
     }
+    const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+    P = (n + kPage - 1) / kPage;
+    if (blk * 64 >= P) return;  // uniform
 #pragma unroll
     for (int r = 0; r < R; ++r) tile[((int)threadIdx.x >> 5) + r * (NT / 32)][part] = v[r];
   }
-  const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
-  for (int i = threadIdx.x; i < G * kD; i += NT) {
-    const float x = __uint_as_float((uint32_t)qg[i] << 16);
+#pragma unroll
+  for (int k = 0; k < QR; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i >= G * kD) break;
+    const float x = __uint_as_float((uint32_t)qr[k] << 16);
     qpos[i / kD][i % kD] = x > 0.f ? x : 0.f;
     qneg[i / kD][i % kD] = x < 0.f ? x : 0.f;
   }
@@ -90,14 +99,14 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
   }
 }
 
-// Fold 64 channels (ch0 .. ch0 + 63) of one page into the G heads' scores: row = the page's staged
-// half (8 x 16 B of kmin, then 8 x 16 B of kmax), q+ / q- broadcast from LDS.
-template <int G>
+// Fold 8 NQ channels (ch0 .. ch0 + 8 NQ - 1) of one page into the G heads' scores: row = the page's
+// staged part (NQ x 16 B of kmin, then NQ x 16 B of kmax), q+ / q- broadcast from LDS.
+template <int G, int NQ>
 __device__ __forceinline__ void page_fold(const uint4* row, const float4 (*qp)[kD / 4], const float4 (*qn)[kD / 4],
                                           int ch0, float (&acc)[G]) {
 #pragma unroll 1
-  for (int c8 = 0; c8 < 8; ++c8) {
-    const uint4 mnv = row[c8], mxv = row[8 + c8];
+  for (int c8 = 0; c8 < NQ; ++c8) {
+    const uint4 mnv = row[c8], mxv = row[NQ + c8];
     const uint32_t wm[4] = {mnv.x, mnv.y, mnv.z, mnv.w};
     const uint32_t wx[4] = {mxv.x, mxv.y, mxv.z, mxv.w};
     float mn[8], mx[8];
@@ -128,7 +137,8 @@ __device__ __forceinline__ void page_fold(const uint4* row, const float4 (*qp)[k
 template <int G>
 __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
                                                          float* __restrict__ scores, int blocks_per_unit) {
-  constexpr int RS = 17;  // LDS row of a page: 16 x 16 B of one half (mn 64 ch, mx 64 ch) + 16 B pad
+  constexpr int NQ = 4;           // 16-byte words of one bound per staged quarter (32 channels)
+  constexpr int RS = 2 * NQ + 1;  // LDS row of a page: NQ words of kmin, NQ of kmax, 16 B pad
   int blk;
   const int u = head_fast_unit(blockIdx.x, c.Hkv, blocks_per_unit, blk);
   const int b = u / c.Hkv, h = u - b * c.Hkv;
@@ -142,10 +152,9 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
   uint32_t qw[G * kD / 128];  // two bf16 channels per word, G * 64 words over 64 lanes
 #pragma unroll
   for (int i = 0; i < G; ++i) qw[i] = reinterpret_cast<const uint32_t*>(qg)[i * 64 + lane];
-  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
-  const int P = (n + kPage - 1) / kPage;
-  if (blk * 64 >= P) return;  // uniform
-  const int lpg = min(j, P - 1);  // a lane past the sequence reads its last page and is dropped
+  // the bound reads do not wait for the sequence length: a lane past the sequence reads a page of
+  // the sequence's allocated range (stored, perhaps stale) and its score is dropped
+  const int lpg = min(j, c.maxP - 1);
   // q+ and q- of every (head, channel) into LDS: lane l holds channels 2l, 2l + 1 of head i
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -157,42 +166,45 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
     pn[2 * lane] = x0 < 0.f ? x0 : 0.f;
     pn[2 * lane + 1] = x1 < 0.f ? x1 : 0.f;
   }
-  // half hf of page p: mn channels 64 hf .. + 63 (128 B) and mx channels 64 hf .. + 63 (128 B);
-  // load r covers pages 4r .. 4r + 3, lane l taking 16 B (segment l & 15) of page 4r + (l >> 4)
-  const int seg = lane & 15;
-  const uint4* rowp[16];
+  // quarter qq of page p: kmin words 4 qq .. 4 qq + 3 and kmax words 16 + 4 qq ..; load r of a quarter
+  // covers pages 8 r .. 8 r + 7, lane l taking word l & 7 of the two runs of page 8 r + (l >> 3)
+  const int seg = lane & 7;
+  const uint4* rowp[8];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int pg = __shfl(lpg, 4 * r + (lane >> 4));
+  for (int r = 0; r < 8; ++r) {
+    const int pg = __shfl(lpg, 8 * r + (lane >> 3));
     rowp[r] = reinterpret_cast<const uint4*>(c.kbound + (((size_t)b * c.maxP + pg) * c.Hkv + h) * 2 * kD) +
-              (seg < 8 ? 0 : 16) + (seg & 7);
+              (seg < NQ ? seg : 16 + seg - NQ);
   }
-  // both halves in flight at once (32 x 16 B per lane); the tile then stages one half at a time
+  // all four quarters in flight at once (32 x 16 B per lane); the tile then stages one quarter at a
+  // time, so a block holds a quarter of the bounds in LDS and more blocks share a compute unit
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 va[16], vb[16];
+  u32x4 v[4][8];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) va[r] = reinterpret_cast<const u32x4*>(rowp[r])[0];
+  for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) vb[r] = reinterpret_cast<const u32x4*>(rowp[r])[8];
+    for (int r = 0; r < 8; ++r) v[qq][r] = reinterpret_cast<const u32x4*>(rowp[r])[NQ * qq];
+  const int n = clampi(c.seq_lens[b], 0, c.maxTok);
+  const int P = (n + kPage - 1) / kPage;
+  if (blk * 64 >= P) return;  // uniform
   float acc[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) acc[i] = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) reinterpret_cast<u32x4*>(tile)[(4 * r + (lane >> 4)) * RS + seg] = va[r];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  page_fold<G>(tile + lane * RS, qp, qn, 0, acc);
-  // the first half's reads are done before the second overwrites the tile
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int qq = 0; qq < 4; ++qq) {
+    if (qq > 0) {
+      // the previous quarter's reads are done before this one overwrites the tile
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 #pragma unroll
-  for (int r = 0; r < 16; ++r) reinterpret_cast<u32x4*>(tile)[(4 * r + (lane >> 4)) * RS + seg] = vb[r];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  page_fold<G>(tile + lane * RS, qp, qn, 64, acc);
+    for (int r = 0; r < 8; ++r) reinterpret_cast<u32x4*>(tile)[(8 * r + (lane >> 3)) * RS + seg] = v[qq][r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    page_fold<G, NQ>(tile + lane * RS, qp, qn, 32 * qq, acc);
+  }
   if (j < P) {
     float gs = 0.f;
 #pragma unroll
