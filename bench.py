@@ -207,12 +207,13 @@ def main():
                    "also_in_line": [n for n in names if n != head]},
         "hbm": r["hbm"],
         "step_us_with_events": r["step_us_with_events"],
+        "budgets": r["budgets"],
         "stages_us": r["stages_us"],
         "event_gap_us": r["event_gap_us"],
         "six_empty_kernels_us": floor_us,
         "roofline": r["roofline"],
         "workloads": {n: {k: recs[n][k] for k in ("config", "us_per_layer_step", "hbm", "stages_us", "event_gap_us",
-                                                  "roofline")}
+                                                  "roofline", "budgets")}
                       for n in names if n != head},
         "cpu_baseline": None,
     }
@@ -262,6 +263,65 @@ def plain_copy_gbps(dev) -> float:
     s = a.elapsed_time(b) / 5 * 1e-3
     del src, dst
     return 2 * (128 << 20) * 4 / s / 1e9
+
+
+def head_budgets(w, cache, t, dev):
+    """Every query head's top-p budget on one layer, read through the split entry points outside the
+    timed region: the candidates the base selector (or the cluster stage) hands the head and the tokens
+    its own top-p keeps.  The budget adapting per head and per step is the point of top-p over a fixed
+    budget (Paper-Notes 核心问题; paperlayer §3.2), and C3 is built to spread it."""
+    import torch
+    import top_sparse_attention_int4_amd as twl
+    B, Hq, Hkv, G = w.batch, w.num_q_heads, w.num_kv_heads, w.group
+    U = B * Hkv
+    sm = twl.DEFAULT_SM_SCALE
+    i32 = dict(dtype=torch.int32, device=dev)
+    if w.csize is not None:
+        C = w.num_clusters
+        maxcand = w.max_seq_len
+        ws = torch.empty(twl.workspace_bytes(cache, maxcand), dtype=torch.uint8, device=dev)
+        rg = torch.empty((U, C, 2), **i32)
+        ct = torch.empty((U,), **i32)
+        twl.select_clusters_topp(cache, t["q"], sm, w.p1, 32, t["centroids"], t["csize"], t["coff"], C, rg, ct, ws)
+        cand = dict(ranges=rg, count=ct, max_items=C)
+    elif w.keep_frac < 1.0:
+        mk = twl.keep_count(w.max_pages, w.keep_frac)
+        maxcand = 16 * mk
+        ws = torch.empty(twl.workspace_bytes(cache, maxcand), dtype=torch.uint8, device=dev)
+        ids = torch.full((U, mk), -1, **i32)
+        cnt = torch.zeros((U,), **i32)
+        twl.select_pages(cache, t["q"], w.keep_frac, mk, ids, cnt, ws)
+        cand = dict(page_ids=ids, count=cnt, max_items=mk)
+    else:
+        return None
+    mw = -(-maxcand // 32)
+    thr = torch.empty((B, Hq), device=dev)
+    hm = torch.zeros((B, Hq, mw), **i32)
+    indptr = torch.empty(U + 1, **i32)
+    toks = torch.empty(U * maxcand, **i32)
+    twl.estimate_topp(cache, t["q"], sm, w.p, 32, **cand, threshold=thr, head_mask=hm, mask_words=mw,
+                      sel_indptr=indptr, sel_tokens=toks, ws=ws)
+    torch.cuda.synchronize()
+    kept = np.unpackbits(hm.cpu().numpy().view(np.uint8), axis=-1).sum(axis=-1).reshape(B * Hq)
+    # candidates per unit: the valid slots of the listed pages, or the lengths of the kept ranges
+    ncand = np.zeros(U, np.int64)
+    if "ranges" in cand:
+        r, c_ = rg.cpu().numpy(), ct.cpu().numpy()
+        for u in range(U):
+            ncand[u] = int(np.maximum(r[u, :c_[u], 1], 0).sum())
+    else:
+        pg, c_ = ids.cpu().numpy(), cnt.cpu().numpy()
+        for u in range(U):
+            n = int(w.seq_lens[u // Hkv])
+            ncand[u] = int(np.clip(n - 16 * pg[u, :c_[u]].astype(np.int64), 0, 16).sum())
+    frac = kept / np.maximum(np.repeat(ncand, G), 1)
+    union = np.diff(indptr.cpu().numpy()) / np.maximum(ncand, 1)
+    pct = lambda x, qs: {f"p{q}": round(float(np.percentile(x, q)), 4) for q in qs}
+    return {"heads": int(B * Hq), "candidates_per_unit_median": int(np.median(ncand)),
+            "kept_tokens_per_head": {"min": int(kept.min()), **pct(kept, (10, 50, 90)), "max": int(kept.max())},
+            "kept_fraction_of_candidates": {"min": round(float(frac.min()), 4), **pct(frac, (10, 50, 90)),
+                                            "max": round(float(frac.max()), 4)},
+            "group_union_fraction_of_candidates_mean": round(float(union.mean()), 4)}
 
 
 def measure_workload(name, args, dev, copy_gbps):
@@ -364,6 +424,7 @@ def measure_workload(name, args, dev, copy_gbps):
         step(li, lists=True)
     torch.cuda.synchronize()
     kept = [indptrs[li].cpu().numpy() for li in range(L)]
+    budgets = head_budgets(w0, layers[0][1], layers[0][2], dev)
 
     # ---- per-step spread: a third pass with one event pair around each step -----------------------
     fp = FenceFreeEvents(2 * args.steps)
@@ -456,6 +517,7 @@ def measure_workload(name, args, dev, copy_gbps):
                 "append_gbps": round(append_gbps, 1),
                 "candidates_per_step": cand_units_total, "kept_tokens_per_step": sel_tokens_total},
         "step_us_with_events": step_spread,
+        "budgets": budgets,
         "stages_us": {n: round(float(x) * 1e3, 3)
                       for n, x in zip(STAGES_CLUSTER if clusters else twl.STAGE_NAMES, stage_ms)},
         "event_gap_us": round(gap_us, 3),
