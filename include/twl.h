@@ -122,7 +122,8 @@ typedef struct twl_decode_params {
 /* Workspace size, in bytes, sufficient for every entry point on `cache` when no unit has more than
  * `max_candidates_per_group` candidates (for twl_decode: 16 * ceil(keep_frac * max_pages_per_seq),
  * or 16 * max_pages_per_seq without a selector; for ranges: max_seq_len).  Returns 0 when `cache`
- * fails validation. */
+ * fails validation, or when max_candidates_per_group is negative or above the top-p capacity of 2^22
+ * candidates per unit (no entry point accepts such a unit). */
 size_t twl_workspace_bytes(const twl_cache* cache, int64_t max_candidates_per_group);
 
 /* INT4 K cache append (Twilight 4-bit K cache: Paper-Notes "关键设计 / 4-bit K缓存量化";

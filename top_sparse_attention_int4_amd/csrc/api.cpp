@@ -51,8 +51,9 @@ bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u)
 // Kept-page count bound for the longest sequence (matches the device computation).
 int keep_count(int P, float keep_frac) {
   if (P <= 0) return 0;
-  float kf = std::ceil(std::fmin(keep_frac * (float)P, (float)P));
-  int k = (int)kf;
+  const float kf = std::ceil(std::fmin(keep_frac * (float)P, (float)P));
+  if (!(kf < (float)P)) return P;  // (float)P may round above P: no out-of-range conversion
+  const int k = (int)kf;
   return k < 1 ? 1 : (k > P ? P : k);
 }
 
@@ -433,8 +434,8 @@ extern "C" {
 
 size_t twl_workspace_bytes(const twl_cache* cache, int64_t max_candidates_per_group) {
   if (check_cache(cache, false, false) != TWL_OK || max_candidates_per_group < 0) return 0;
-  int64_t ncap = ncap_of(max_candidates_per_group);
-  if (ncap == 0) ncap = ((max_candidates_per_group + 1023) / 1024) * 1024;
+  const int64_t ncap = ncap_of(max_candidates_per_group);
+  if (ncap == 0) return 0;  // beyond the top-p capacity: no entry point accepts such a unit
   Layout L;
   make_layout(cache, ncap, &L);
   return L.total;
