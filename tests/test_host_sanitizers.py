@@ -50,7 +50,12 @@ def test_abi_validation_under_asan_and_ubsan(tmp_path):
     subprocess.run([cxx, *san, drv_o, api_o, *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib",
                     "-o", exe], check=True, capture_output=True)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
-    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
-    assert r.returncode == 0, r.stdout + r.stderr
-    assert "host ABI checks passed" in r.stdout
-    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr
+    env.pop("TWL_TRACE", None)
+    # plain, and with the optional roctx ranges switched on (the tracer loads roctx at run time)
+    for trace in (None, "1"):
+        if trace:
+            env["TWL_TRACE"] = trace
+        r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+        assert r.returncode == 0, r.stdout + r.stderr
+        assert "host ABI checks passed" in r.stdout
+        assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr

@@ -3,10 +3,12 @@
 // Every entry point validates its arguments before its first HIP call, then checks that the
 // current device is gfx950, carves the caller's workspace and enqueues the kernels on the caller's
 // stream.  Nothing here allocates, frees or synchronises.
+#include <dlfcn.h>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 
 #include "twl.h"
@@ -176,11 +178,64 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// Event hook for profiled runs.
+// ---- optional tracing ----------------------------------------------------------------------------
+// With TWL_TRACE=1 in the environment when the library first traces, every entry point and every
+// stage of the fused decodes is bracketed by a roctx range (host-side ranges: what was enqueued
+// when, for rocprofv3 --marker-trace timelines).  The roctx library is looked up at run time, so the
+// library does not depend on it; without it, or without the variable, tracing costs one branch.
+struct Tracer {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Tracer& tracer() {
+  static const Tracer t = [] {
+    Tracer x;
+    const char* e = std::getenv("TWL_TRACE");
+    if (!e || std::strcmp(e, "1") != 0) return x;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return x;
+    auto push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    auto pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (push && pop) {
+      x.push = push;
+      x.pop = pop;
+    }
+    return x;
+  }();
+  return t;
+}
+
+// A roctx range for the lifetime of the object (a no-op unless tracing).
+struct TraceRange {
+  const bool on;
+  explicit TraceRange(const char* name) : on(tracer().push != nullptr) {
+    if (on) tracer().push(name);
+  }
+  ~TraceRange() {
+    if (on) tracer().pop();
+  }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
+
+const char* const kStageNames[TWL_NUM_STAGES] = {"page_score", "page_select", "estimate",
+                                                 "topp_union", "attention",   "merge"};
+const char* const kClusterStageNames[TWL_NUM_STAGES] = {"cluster_scores_topp", "cluster_pages", "estimate",
+                                                        "topp_union",          "attention",     "merge"};
+
+// Stage hook of the fused decodes: caller-owned events for profiled runs (event 2i before stage i,
+// 2i + 1 after it), and the stage's trace range.
 struct Events {
   void* const* ev = nullptr;
   hipStream_t s = nullptr;
+  const char* const* names = kStageNames;
   hipError_t rec(int i) const {
+    if (tracer().push) {
+      if (i % 2 == 0) tracer().push(names[i / 2]);
+      else tracer().pop();
+    }
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   }
 };
@@ -382,7 +437,7 @@ twl_status decode_clusters_impl(const twl_cache* cache, const void* q, const twl
   st = check_device();
   if (st != TWL_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  const Events E{events, s};
+  const Events E{events, s, kClusterStageNames};
   const CacheView c = make_view(cache);
   const uint16_t* qb = static_cast<const uint16_t*>(q);
   TWL_TRY(E.rec(0));
@@ -443,6 +498,7 @@ size_t twl_workspace_bytes(const twl_cache* cache, int64_t max_candidates_per_gr
 
 twl_status twl_quantize_k(const twl_cache* cache, const int32_t* tok_begin, const int32_t* tok_end,
                           int32_t max_span, void* stream) {
+  const TraceRange trace_("twl_quantize_k");
   twl_status st = check_cache(cache, true, true);
   if (st != TWL_OK) return st;
   if (!tok_begin || !tok_end) return TWL_EINVAL;
@@ -456,6 +512,7 @@ twl_status twl_quantize_k(const twl_cache* cache, const int32_t* tok_begin, cons
 
 twl_status twl_select_pages(const twl_cache* cache, const void* q, float keep_frac, int32_t max_keep,
                             int32_t* page_ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  const TraceRange trace_("twl_select_pages");
   twl_status st = check_cache(cache, false, true);
   if (st != TWL_OK) return st;
   if (!q || misaligned16(q) || !page_ids || !count) return TWL_EINVAL;
@@ -479,6 +536,7 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
                              const twl_candidates* cand, float* threshold, float* mass, uint32_t* head_mask,
                              int32_t mask_words, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
                              void* ws, size_t ws_bytes, void* stream) {
+  const TraceRange trace_("twl_estimate_topp");
   twl_status st = check_cache(cache, false, true);
   if (st != TWL_OK) return st;
   if (!q || misaligned16(q) || !cand || !threshold || !sel_indptr || !sel_tokens) return TWL_EINVAL;
@@ -535,6 +593,7 @@ twl_status twl_estimate_topp(const twl_cache* cache, const void* q, float sm_sca
 twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale, const int32_t* sel_indptr,
                            const int32_t* sel_tokens, int32_t max_selected_per_group, float* out, float* lse,
                            void* ws, size_t ws_bytes, void* stream) {
+  const TraceRange trace_("twl_sparse_attn");
   twl_status st = check_cache(cache, true, false);
   if (st != TWL_OK) return st;
   if (!q || misaligned16(q) || !sel_indptr || !sel_tokens || !out) return TWL_EINVAL;
@@ -562,6 +621,7 @@ twl_status twl_sparse_attn(const twl_cache* cache, const void* q, float sm_scale
 twl_status twl_decode(const twl_cache* cache, const void* q, const twl_decode_params* params, float* out,
                       float* lse, float* threshold, int32_t* sel_indptr, int32_t* sel_tokens, int64_t capacity,
                       void* ws, size_t ws_bytes, void* stream) {
+  const TraceRange trace_("twl_decode");
   return decode_impl(cache, q, params, out, lse, threshold, sel_indptr, sel_tokens, capacity, ws, ws_bytes,
                      stream, nullptr);
 }
@@ -570,6 +630,7 @@ twl_status twl_decode_profiled(const twl_cache* cache, const void* q, const twl_
                                float* out, float* lse, float* threshold, int32_t* sel_indptr,
                                int32_t* sel_tokens, int64_t capacity, void* ws, size_t ws_bytes,
                                void* stream, void* const* events) {
+  const TraceRange trace_("twl_decode_profiled");
   if (!events) return TWL_EINVAL;
   return decode_impl(cache, q, params, out, lse, threshold, sel_indptr, sel_tokens, capacity, ws, ws_bytes,
                      stream, events);
@@ -579,6 +640,7 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
                                     int32_t iters, const void* centroids, const int32_t* csize,
                                     const int32_t* coff, int32_t num_clusters, int32_t* ranges,
                                     int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  const TraceRange trace_("twl_select_clusters_topp");
   twl_status st = check_cache(cache, false, false);
   if (st != TWL_OK) return st;
   if (!q || misaligned16(q) || !centroids || !csize || !coff || !ranges || !count) return TWL_EINVAL;
@@ -604,6 +666,7 @@ twl_status twl_select_clusters_topp(const twl_cache* cache, const void* q, float
 
 twl_status twl_cluster_value_means(const twl_cache* cache, const int32_t* csize, const int32_t* coff,
                                    int32_t num_clusters, float* vmean, void* stream) {
+  const TraceRange trace_("twl_cluster_value_means");
   twl_status st = check_cache(cache, true, false);
   if (st != TWL_OK) return st;
   if (!csize || !coff || !vmean || num_clusters < 1 || num_clusters > kNarrowMaxCands) return TWL_EINVAL;
@@ -617,6 +680,7 @@ twl_status twl_cluster_approx_unkept(const twl_cache* cache, const void* q, floa
                                      const void* centroids, const int32_t* csize, int32_t num_clusters,
                                      const float* vmean, float* out, float* lse, void* ws, size_t ws_bytes,
                                      void* stream) {
+  const TraceRange trace_("twl_cluster_approx_unkept");
   twl_status st = check_cache(cache, false, false);
   if (st != TWL_OK) return st;
   if (!q || misaligned16(q) || !centroids || !csize || !vmean || !out || !lse) return TWL_EINVAL;
@@ -646,6 +710,7 @@ twl_status twl_decode_clusters(const twl_cache* cache, const void* q, const twl_
                                int32_t num_clusters, float* out, float* lse, float* threshold, int32_t* sel_indptr,
                                int32_t* sel_tokens, int64_t capacity, void* ws, size_t ws_bytes, void* stream,
                                void* const* events) {
+  const TraceRange trace_("twl_decode_clusters");
   return decode_clusters_impl(cache, q, params, p1, centroids, csize, coff, num_clusters, out, lse, threshold,
                               sel_indptr, sel_tokens, capacity, ws, ws_bytes, stream, events);
 }
