@@ -10,9 +10,10 @@
 // head reproduce the fold bit for bit without a compare.  Two layouts compute the same folds: for
 // small steps each wave of a 4-wave block folds one query head for 64 pages (latency bound: every
 // head in parallel); for large ones a block is one wave and 64 pages, one lane per page folding all G
-// query heads, so each bound is converted once (the bounds staged in LDS in two halves of 64
-// channels with coalesced loads, 17 KB of LDS so that several blocks share a compute unit and cover
-// each other's loads; q+ and q- broadcast from LDS).  The group score then folds the heads in order.
+// query heads, so each bound is converted once (every bound load of the block in flight at once,
+// then staged through LDS a quarter of the channels at a time: 13 KB of LDS, so that twelve blocks
+// share a compute unit and cover each other's loads; q+ and q- broadcast from LDS).  The group score
+// then folds the heads in order.
 #include "twl_device.h"
 #include "twl_internal.h"
 

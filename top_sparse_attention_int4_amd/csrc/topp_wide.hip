@@ -59,25 +59,30 @@ __device__ __forceinline__ void load_chunk4(const float* x, float (&v)[HEPT]) {
     v[4 * j + 3] = q.w;
   }
 }
-__device__ __forceinline__ void flush_hist(const uint64_t* h, int nbins, uint64_t* g_fine, uint64_t* g_coarse) {
-  for (int i = threadIdx.x; i < nbins; i += HT)
-    if (h[i]) atomicAdd((unsigned long long*)&g_fine[i], (unsigned long long)h[i]);
-  for (int cb = threadIdx.x; cb < nbins / 32; cb += HT) {
-    uint64_t s = 0;
-#pragma unroll 8
-    for (int i = 0; i < 32; ++i) s += h[32 * cb + i];
-    if (s) atomicAdd((unsigned long long*)&g_coarse[cb], (unsigned long long)s);
-  }
+// The block's first-digit histogram added to the head's: thread t takes bins 2t and 2t + 1, adds each
+// non-zero one with an integer atomic, and each row of 16 lanes sums its 32 bins (a DPP scan) for the
+// coarse histogram, one atomic per row.  Integer sums, so the order of the additions does not matter.
+__device__ __forceinline__ void flush_hist1(const uint64_t* h, uint64_t* g_fine, uint64_t* g_coarse) {
+  static_assert(2 * HT == 2048, "two bins per thread");
+  const int t = threadIdx.x;
+  const uint64_t a = h[2 * t], b = h[2 * t + 1];
+  if (a) atomicAdd((unsigned long long*)&g_fine[2 * t], (unsigned long long)a);
+  if (b) atomicAdd((unsigned long long*)&g_fine[2 * t + 1], (unsigned long long)b);
+  const uint64_t rs = row16_incl_scan_u64(a + b);  // lane 15 of the row: its 32 bins
+  if ((t & 15) == 15 && rs) atomicAdd((unsigned long long*)&g_coarse[t >> 4], (unsigned long long)rs);
 }
 
 // Lane l of each group of 8 lanes holds the keep bits of candidates 4l .. 4l + 3 of a 32-candidate
 // word (bit e for candidate 4l + e); every lane of the group gets the word (bit k <=> candidate k).
+// (DPP: the quads' ORs, then each quad takes its partner's, four lanes up or down within the row;
+// called by whole waves.)
 __device__ __forceinline__ uint32_t nibbles_to_word(uint32_t nib) {
-  uint32_t x = nib << (4 * (threadIdx.x & 7));
-  x |= (uint32_t)__shfl_xor((int)x, 1);
-  x |= (uint32_t)__shfl_xor((int)x, 2);
-  x |= (uint32_t)__shfl_xor((int)x, 4);
-  return x;
+  int x = (int)(nib << (4 * (threadIdx.x & 7)));
+  x |= dpp_i<kDppXor1>(x);
+  x |= dpp_i<kDppXor2>(x);
+  const int up = __builtin_amdgcn_update_dpp(0, x, kDppShl4, 0xf, 0xf, true);  // lane n + 4 (0 past the row)
+  const int dn = __builtin_amdgcn_update_dpp(0, x, kDppShr4, 0xf, 0xf, true);  // lane n - 4
+  return (uint32_t)(x | ((threadIdx.x & 4) ? dn : up));
 }
 
 }  // namespace
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(HT) void k_wide_hist1(const float* __restrict__ log
     }
   }
   __syncthreads();
-  flush_hist(h, 2048, st + kWideH1, st + kWideC1);
+  flush_hist1(h, st + kWideH1, st + kWideC1);
   // this block's histogram atomics performed before its ticket is taken
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();

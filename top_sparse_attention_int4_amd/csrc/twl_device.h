@@ -67,26 +67,8 @@ __device__ __forceinline__ float wave_min_dpp(float x) {
   const float r0 = readlane_f(x, 0), r1 = readlane_f(x, 16), r2 = readlane_f(x, 32), r3 = readlane_f(x, 48);
   return fminf(fminf(r0, r1), fminf(r2, r3));
 }
-__device__ __forceinline__ int wave_sum_int_dpp(int x) {
-  x += dpp_i<kDppXor1>(x);
-  x += dpp_i<kDppXor2>(x);
-  x += dpp_i<kDppRor4>(x);
-  x += dpp_i<kDppRor8>(x);
-  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
-         __builtin_amdgcn_readlane(x, 48);
-}
 
-// Butterfly all-reduce over the 64 lanes; every lane ends with the same bits (fp add/max commute).
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
+// Butterfly all-reduce of an integer over the 64 lanes; every lane ends with the total.
 __device__ __forceinline__ int wave_sum_int(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
@@ -99,6 +81,7 @@ __device__ __forceinline__ int dpp_scan_move(int x) {
   return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xf, true);
 }
 constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppShl4 = 0x104;  // row_shl:4 (lane n reads lane n + 4 of its row)
 constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
 
 // Inclusive prefix sum over the lanes of a wave (DPP: four in-row steps, two row broadcasts).
@@ -295,17 +278,6 @@ __device__ __forceinline__ int head_fast_unit(int bid, int Hkv, int items, int& 
   const int b = r / items;
   k = r - b * items;
   return b * Hkv + h;
-}
-
-// DPP row rotation of a 64-bit value: within each row of 16 lanes, rotated right by N (lane n receives
-// lane (n - N) mod 16).
-// (Every lane has a source inside its row, so no lane keeps an old value: a plain DPP move.)
-template <int N>
-__device__ __forceinline__ double dpp_row_ror_f64(double x) {
-  const uint64_t u = (uint64_t)__double_as_longlong(x);
-  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, 0x120 + N, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), 0x120 + N, 0xf, 0xf, false);
-  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
 // The estimate's fixed-point query for channel group g of query row bh, written by 32 lanes (one half
