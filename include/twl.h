@@ -39,7 +39,9 @@
  *                                                     with the lowest channel in the lowest bits (kb = 4:
  *                                                     byte j = code(2j) | code(2j+1)<<4)
  *   k4_meta   fp16 [B][max_pages_per_seq][Hkv][16][4][2]  per 32-channel group: (scale, zero)
- *   kbound    bf16 [B][max_pages_per_seq][Hkv][2][128]    per logical page: channel-wise key min row, max row
+ *   kbound    bf16 [B][max_pages_per_seq][Hkv][4][2][32] per logical page: channel-wise key min and max,
+ *                                                     by channel quarter (32 channels of min, then the
+ *                                                     same 32 of max: one 128-byte line per quarter)
  *   The INT4 shadow is the library's own derived data: it is stored by (sequence, logical page), not
  *   paged, so that the page selector and the weight estimate address it without a page-table lookup
  *   (only the attention, which reads the paged K and V, translates pages).

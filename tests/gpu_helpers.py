@@ -32,6 +32,14 @@ def shadow_by_phys(w, arr):
     return out
 
 
+def bounds_rows(arr):
+    """Page bounds as the library stores them, [..][4][2][32] (channel quarter, min/max, channel), as
+    [..][2][128] (min row, max row)."""
+    arr = np.asarray(arr)
+    lead = arr.shape[:-3]
+    return np.ascontiguousarray(np.swapaxes(arr, -3, -2)).reshape(lead + (2, 128))
+
+
 def oracle_decode(w, **kw):
     """The oracle's decode with the ambiguity band of the estimate kernel's stated precision."""
     return pipeline.decode(w, band=kernel_model.band, **kw)

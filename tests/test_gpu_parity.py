@@ -24,8 +24,8 @@ import top_sparse_attention_int4_amd as twl
 from gen import make_config, make_custom
 from oracle import numerics, quantize, select
 from oracle.topp import set_matches
-from tests.gpu_helpers import (SM, SetStats, attn_tolerance, check_bisect, check_union, device_cache, max_keep,
-                               oracle_decode, run_decode, shadow_by_phys, unit_tokens, workspace)
+from tests.gpu_helpers import (SM, SetStats, attn_tolerance, bounds_rows, check_bisect, check_union, device_cache,
+                               max_keep, oracle_decode, run_decode, shadow_by_phys, unit_tokens, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,7 @@ def test_quantize_bitexact(cfg):
     # the library stores the shadow by logical page; compare it in the oracle's physical order
     k4 = shadow_by_phys(w, cache.k4.cpu().numpy())
     meta = shadow_by_phys(w, cache.k4_meta.cpu().numpy().view(np.uint16))
-    kb = shadow_by_phys(w, cache.kbound.cpu().numpy().view(np.uint16))
+    kb = shadow_by_phys(w, bounds_rows(cache.kbound.cpu().numpy().view(np.uint16)))
     m3 = np.broadcast_to(exp["tok_mask"][:, None, :], k4.shape[:3])
     assert np.array_equal(k4[m3], exp["k4"][m3])
     assert np.array_equal(meta[m3], exp["k4_meta"][m3])

@@ -177,7 +177,8 @@ class PagedCache:
     ``page_table`` int32 [B][max_pages]; ``seq_lens`` int32 [B].  The key codes (``key_bits`` wide:
     4, or 2 / 8 for the estimator's precision ablation), fp16 scale/zero and page bounds are allocated
     here by (sequence, logical page) -- ``k4`` [B][max_pages][Hkv][16][16*key_bits], ``k4_meta``
-    [B][max_pages][Hkv][16][4][2], ``kbound`` [B][max_pages][Hkv][2][128] -- and filled by
+    [B][max_pages][Hkv][16][4][2], ``kbound`` [B][max_pages][Hkv][4][2][32] (channel quarter, min/max,
+    channel) -- and filled by
     :func:`quantize_k`.  ``k_pages``/``v_pages`` may instead be pinned host tensors
     (the offloading scenario): the kernels then read them over PCIe through the runtime's mapping of
     that memory, while the codes, bounds and everything else stay in device memory.
@@ -208,7 +209,7 @@ class PagedCache:
         B, MP = self.batch, self.max_pages
         self.k4 = torch.zeros((B, MP, Hkv, 16, 16 * key_bits), dtype=torch.uint8, device=dev)
         self.k4_meta = torch.zeros((B, MP, Hkv, 16, 4, 2), dtype=torch.int16, device=dev)
-        self.kbound = torch.zeros((B, MP, Hkv, 2, 128), dtype=torch.int16, device=dev)
+        self.kbound = torch.zeros((B, MP, Hkv, 4, 2, 32), dtype=torch.int16, device=dev)
         self._c = CacheC(self.batch, self.num_q_heads, self.num_kv_heads, 128, 16, 32, self.max_pages,
                          self.num_phys_pages, self.max_seq_len, _ptr(page_table), _ptr(seq_lens),
                          _ptr(k_pages, allow_host=True), _ptr(v_pages, allow_host=True), _ptr(self.k4),

@@ -91,9 +91,12 @@ __global__ __launch_bounds__(64) void k_quantize(CacheView c, const int32_t* __r
     mx0 = fmaxf(mx0, a);
     mx1 = fmaxf(mx1, bb);
   }
+  // quarter-major slice: quarter j = channels 32 j .. 32 j + 31 as 64 B of min then 64 B of max, so a
+  // quarter of a page is one 128-byte line (16 words of min, then 16 of max, per quarter)
   uint32_t* kb = reinterpret_cast<uint32_t*>(c.kbound + (((size_t)b * c.maxP + page) * c.Hkv + h) * 2 * kD);
-  kb[tid] = (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xffff0000u);
-  kb[64 + tid] = (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xffff0000u);
+  const int qw = (tid >> 4) * 32 + (tid & 15);
+  kb[qw] = (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xffff0000u);
+  kb[qw + 16] = (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xffff0000u);
 }
 
 hipError_t launch_quantize(const CacheView& c, const int32_t* tok_begin, const int32_t* tok_end,

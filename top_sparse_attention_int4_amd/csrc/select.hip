@@ -10,10 +10,11 @@
 // head reproduce the fold bit for bit without a compare.  Two layouts compute the same folds: for
 // small steps each wave of a 4-wave block folds one query head for 64 pages (latency bound: every
 // head in parallel); for large ones a block is one wave and 64 pages, one lane per page folding all G
-// query heads, so each bound is converted once (every bound load of the block in flight at once,
-// then staged through LDS a quarter of the channels at a time: 13 KB of LDS, so that twelve blocks
-// share a compute unit and cover each other's loads; q+ and q- broadcast from LDS).  The group score
-// then folds the heads in order.
+// query heads, so each bound is converted once (the bounds are stored quarter-major, so a quarter of
+// the channels of a page is one 128-byte line; two quarters of the block's loads are in flight and
+// each staged quarter requests the next, so the folds overlap the loads; 13 KB of LDS, so that twelve
+// blocks share a compute unit and cover each other's loads; q+ and q- broadcast from LDS).  The group
+// score then folds the heads in order.
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -59,8 +60,11 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
     const int n = clampi(c.seq_lens[b], 0, c.maxTok);
     P = (n + kPage - 1) / kPage;
     if (blk * 64 >= P) return;  // uniform
+    // stored quarter-major (8 words per quarter: 4 of min, then 4 of max); the tile row is all 16
+    // words of min, then all 16 of max
+    const int col = (part & 4) * 4 + (part >> 3) * 4 + (part & 3);
 #pragma unroll
-    for (int r = 0; r < R; ++r) tile[((int)threadIdx.x >> 5) + r * (NT / 32)][part] = v[r];
+    for (int r = 0; r < R; ++r) tile[((int)threadIdx.x >> 5) + r * (NT / 32)][col] = v[r];
   }
 #pragma unroll
   for (int k = 0; k < QR; ++k) {
@@ -167,24 +171,25 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
     pn[2 * lane] = x0 < 0.f ? x0 : 0.f;
     pn[2 * lane + 1] = x1 < 0.f ? x1 : 0.f;
   }
-  // quarter qq of page p: kmin words 4 qq .. 4 qq + 3 and kmax words 16 + 4 qq ..; load r of a quarter
-  // covers pages 8 r .. 8 r + 7, lane l taking word l & 7 of the two runs of page 8 r + (l >> 3)
+  // quarter qq of page p is the 128-byte line 8 qq .. 8 qq + 7 of its slice (4 words of kmin, then 4 of
+  // kmax); load r of a quarter covers pages 8 r .. 8 r + 7, lane l taking word l & 7 of page 8 r + (l >> 3)
   const int seg = lane & 7;
   const uint4* rowp[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int pg = __shfl(lpg, 8 * r + (lane >> 3));
-    rowp[r] = reinterpret_cast<const uint4*>(c.kbound + (((size_t)b * c.maxP + pg) * c.Hkv + h) * 2 * kD) +
-              (seg < NQ ? seg : 16 + seg - NQ);
+    rowp[r] = reinterpret_cast<const uint4*>(c.kbound + (((size_t)b * c.maxP + pg) * c.Hkv + h) * 2 * kD) + seg;
   }
-  // all four quarters in flight at once (32 x 16 B per lane); the tile then stages one quarter at a
-  // time, so a block holds a quarter of the bounds in LDS and more blocks share a compute unit
+  // two quarters in flight (16 x 16 B per lane): quarter qq + 2 is requested once quarter qq is staged,
+  // so its loads overlap the fold and each wave's folds are spread over its loads instead of all
+  // running after the last one arrives; the tile stages one quarter at a time
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kAhead = 2;
   u32x4 v[4][8];
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq)
+  for (int qq = 0; qq < kAhead; ++qq)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[qq][r] = reinterpret_cast<const u32x4*>(rowp[r])[NQ * qq];
+    for (int r = 0; r < 8; ++r) v[qq][r] = reinterpret_cast<const u32x4*>(rowp[r])[2 * NQ * qq];
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
   if (blk * 64 >= P) return;  // uniform
@@ -204,6 +209,10 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (qq + kAhead < 4) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[qq + kAhead][r] = reinterpret_cast<const u32x4*>(rowp[r])[2 * NQ * (qq + kAhead)];
+    }
     page_fold<G, NQ>(tile + lane * RS, qp, qn, 32 * qq, acc);
   }
   if (j < P) {
