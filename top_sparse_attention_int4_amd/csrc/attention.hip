@@ -504,12 +504,14 @@ __global__ __launch_bounds__(NR * 32) void k_merge(CacheView c, ListView L, bool
 }
 
 int attn_chunk_tokens(int64_t total_upper, int group) {
-  // 128 tokens (two pipelined sub-blocks per wave) up to 1024 (512 for groups of 8, whose larger
+  // 256 tokens (four pipelined sub-blocks per wave) up to 1024 (512 for groups of 8, whose larger
   // accumulators would not fit), aiming at about 1024 chunks: every chunk writes a partial, and those
-  // writes slow the K/V stream far beyond their byte count
+  // writes slow the K/V stream far beyond their byte count.  Small steps keep 256-token chunks: at 65536
+  // candidates (a 32K-token layer at keep 1/4) 128-token chunks cost the merge more than they save the
+  // attention, and 512-token chunks leave too few blocks
   const int smax = group >= 8 ? 8 : 16;
   int64_t sb = total_upper / (64 * 1024);
-  int s = 2;
+  int s = 4;
   while (s * 2 <= sb && s < smax) s *= 2;
   return 64 * s;
 }
@@ -546,8 +548,6 @@ static hipError_t launch_attn_impl(const CacheView& c, const uint16_t* q, float 
     }                                      \
     break;
   switch (chunk_tokens) {
-    TWL_ATTN_NSB(1)
-    TWL_ATTN_NSB(2)
     TWL_ATTN_NSB(4)
     TWL_ATTN_NSB(8)
     TWL_ATTN_NSB_SMALL_G(16)
