@@ -576,6 +576,36 @@ def test_fused_equals_split_and_is_deterministic():
     assert np.array_equal(g["out"], a["out"]) and np.array_equal(g["lse"], a["lse"]) and np.array_equal(g["thr"], a["thr"])
 
 
+# Decodes without the base selector (every page a candidate): thresholds and kept lists bitwise those
+# of the split call over every page, and both match the oracle, for top-p and the top-k baseline.
+# Shapes: C1 (one head, 4096 tokens), groups of 2 and 4 at 4096 / 2048 candidates with ragged and
+# empty sequences, and one of 1024 candidates.
+NO_SELECTOR = [
+    dict(batch=2, num_q_heads=4, num_kv_heads=2, seq_lens=[3000, 1500], kind="outlier", seed=81),
+    dict(batch=3, num_q_heads=8, num_kv_heads=2, seq_lens=[2000, 0, 1111], kind="temperature", seed=82),
+    dict(batch=2, num_q_heads=4, num_kv_heads=1, seq_lens=[1000, 17], kind="planted", seed=83),
+]
+
+
+@pytest.mark.parametrize("cfg", [None] + NO_SELECTOR, ids=["C1", "g2_4096", "g4_2048", "g4_1024"])
+def test_decode_without_selector_equals_split(cfg):
+    w = make_config("C1") if cfg is None else make_custom(**cfg, keep_frac=1.0, p=0.9)
+    _print_case(w.name + " every page a candidate")
+    cache, t = device_cache(w)
+    a = run_decode(w, cache, t, keep_frac=1.0)
+    U = w.batch * w.num_kv_heads
+    pages = [np.arange(-(-int(w.seq_lens[u // w.num_kv_heads]) // 16)) for u in range(U)]
+    e = _estimate_on_pages(w, cache, t, pages, w.p)
+    assert np.array_equal(e["thr"], a["thr"])
+    assert np.array_equal(e["indptr"], a["indptr"])
+    n = int(a["indptr"][-1])
+    assert np.array_equal(e["tokens"][:n], a["tokens"][:n])
+    _check_decode(w, a, oracle_decode(w, keep_frac=1.0))
+    # the top-k baseline
+    k = run_decode(w, cache, t, keep_frac=1.0, topk=40)
+    _check_decode(w, k, oracle_decode(w, keep_frac=1.0, topk=40), topk=True)
+
+
 @pytest.mark.parametrize("G", [1, 2, 8])
 def test_group_sizes(G):
     w = make_custom(batch=2, num_q_heads=2 * G, num_kv_heads=2, seq_lens=[1200, 700], kind="outlier", seed=30 + G,
