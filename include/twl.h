@@ -233,7 +233,7 @@ twl_status twl_decode(const twl_cache* cache, const void* q, const twl_decode_pa
  * device array of TWL_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
  * process ends; its device address is looked up once per device, on the first call there.  Calls
  * whose twl_workspace_bytes() would exceed that size return TWL_EWORKSPACE before any HIP call (the
- * Llama-shaped layer, B = 1, 32/8 heads, 32K context with a 1/4 page budget, needs 3.8 MiB; B = 16 at
+ * Llama-shaped layer, B = 1, 32/8 heads, 32K context with a 1/4 page budget, needs 3.3 MiB; B = 16 at
  * 32K 47 MiB, B = 4 at 128K 41 MiB).  Everything else is as for twl_decode, with the same
  * kernels and bitwise the same outputs.  This function allocates nothing; calls that overlap on one
  * GPU share the array and race, so serialise them (one stream, or events). */
