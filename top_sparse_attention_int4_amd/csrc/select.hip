@@ -9,12 +9,13 @@
 // is then an exact zero and adding it changes nothing, so two fused multiply-adds per channel and
 // head reproduce the fold bit for bit without a compare.  Two layouts compute the same folds: for
 // small steps each wave of a 4-wave block folds one query head for 64 pages (latency bound: every
-// head in parallel); for large ones a block is one wave and 64 pages, one lane per page folding all G
-// query heads, so each bound is converted once (the bounds are stored quarter-major, so a quarter of
-// the channels of a page is one 128-byte line; two quarters of the block's loads are in flight and
-// each staged quarter requests the next, so the folds overlap the loads; 13 KB of LDS, so that twelve
-// blocks share a compute unit and cover each other's loads; q+ and q- broadcast from LDS).  The group
-// score then folds the heads in order.
+// head in parallel); for large ones each wave takes 64 pages, one lane per page folding all G query
+// heads, so each bound is converted once (the bounds are stored quarter-major, so a quarter of the
+// channels of a page is one 128-byte line; two quarters of a wave's loads are in flight and each
+// staged quarter requests the next, so the folds overlap the loads; a block is four such waves
+// sharing q+ and q- in LDS, 40 KB with the waves' quarter tiles, so that four blocks -- sixteen waves,
+// at most 128 VGPRs each -- share a compute unit and a 32K-token, 16-sequence layer's grid is resident
+// at once).  The group score then folds the heads in order.
 #include "twl_device.h"
 #include "twl_internal.h"
 
@@ -140,36 +141,35 @@ __device__ __forceinline__ void page_fold(const uint4* row, const float4 (*qp)[k
 }
 
 template <int G>
-__global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 4) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
                                                          float* __restrict__ scores, int blocks_per_unit) {
   constexpr int NQ = 4;           // 16-byte words of one bound per staged quarter (32 channels)
   constexpr int RS = 2 * NQ + 1;  // LDS row of a page: NQ words of kmin, NQ of kmax, 16 B pad
   int blk;
   const int u = head_fast_unit(blockIdx.x, c.Hkv, blocks_per_unit, blk);
   const int b = u / c.Hkv, h = u - b * c.Hkv;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
 
-  __shared__ uint4 tile[64 * RS];
+  __shared__ uint4 tiles[4][64 * RS];
   __shared__ float4 qp[G][kD / 4], qn[G][kD / 4];
+  uint4* tile = tiles[wq];
   // this lane's page (the bounds are stored by logical page: no page-table lookup)
-  const int j = blk * 64 + lane;
+  const int j = blk * 256 + wq * 64 + lane;
   const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
-  uint32_t qw[G * kD / 128];  // two bf16 channels per word, G * 64 words over 64 lanes
-#pragma unroll
-  for (int i = 0; i < G; ++i) qw[i] = reinterpret_cast<const uint32_t*>(qg)[i * 64 + lane];
   // the bound reads do not wait for the sequence length: a lane past the sequence reads a page of
   // the sequence's allocated range (stored, perhaps stale) and its score is dropped
   const int lpg = min(j, c.maxP - 1);
-  // q+ and q- of every (head, channel) into LDS: lane l holds channels 2l, 2l + 1 of head i
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    const float x0 = bf16_lo(qw[i]), x1 = bf16_hi(qw[i]);
-    float* pp = reinterpret_cast<float*>(&qp[i][0]);
-    float* pn = reinterpret_cast<float*>(&qn[i][0]);
-    pp[2 * lane] = x0 > 0.f ? x0 : 0.f;
-    pp[2 * lane + 1] = x1 > 0.f ? x1 : 0.f;
-    pn[2 * lane] = x0 < 0.f ? x0 : 0.f;
-    pn[2 * lane + 1] = x1 < 0.f ? x1 : 0.f;
+  // q+ and q- of every (head, channel) into LDS, shared by the block's four waves
+  for (int t = threadIdx.x; t < G * 64; t += 256) {
+    const uint32_t qw = reinterpret_cast<const uint32_t*>(qg)[t];
+    const float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
+    float* pp = reinterpret_cast<float*>(&qp[t >> 6][0]);
+    float* pn = reinterpret_cast<float*>(&qn[t >> 6][0]);
+    const int ch = 2 * (t & 63);
+    pp[ch] = x0 > 0.f ? x0 : 0.f;
+    pp[ch + 1] = x1 > 0.f ? x1 : 0.f;
+    pn[ch] = x0 < 0.f ? x0 : 0.f;
+    pn[ch + 1] = x1 < 0.f ? x1 : 0.f;
   }
   // quarter qq of page p is the 128-byte line 8 qq .. 8 qq + 7 of its slice (4 words of kmin, then 4 of
   // kmax); load r of a quarter covers pages 8 r .. 8 r + 7, lane l taking word l & 7 of page 8 r + (l >> 3)
@@ -192,7 +192,8 @@ __global__ __launch_bounds__(64) void k_page_score_pages(CacheView c, const uint
     for (int r = 0; r < 8; ++r) v[qq][r] = reinterpret_cast<const u32x4*>(rowp[r])[2 * NQ * qq];
   const int n = clampi(c.seq_lens[b], 0, c.maxTok);
   const int P = (n + kPage - 1) / kPage;
-  if (blk * 64 >= P) return;  // uniform
+  __syncthreads();  // the query halves are staged
+  if (blk * 256 + wq * 64 >= P) return;  // uniform per wave (no block barrier follows)
   float acc[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) acc[i] = 0.f;
@@ -477,12 +478,14 @@ __global__ __launch_bounds__(1024) void k_page_select(CacheView c, const float* 
 hipError_t launch_page_score(const CacheView& c, const uint16_t* q, float* scores, hipStream_t s) {
   const int bpu = (c.maxP + 63) / 64;
   dim3 grid((unsigned)(c.B * c.Hkv * bpu));
+  const int bpu4 = (c.maxP + 255) / 256;
+  dim3 grid4((unsigned)(c.B * c.Hkv * bpu4));
   // up to two blocks per compute unit the step is latency bound: one wave per head; beyond, one lane
   // per page folds every head so that each bound is converted once
   const bool pages = grid.x > 512u;
 #define TWL_PS_G(GG)                                                                                        \
   case GG:                                                                                                  \
-    if (pages) hipLaunchKernelGGL(k_page_score_pages<GG>, grid, dim3(64), 0, s, c, q, scores, bpu);         \
+    if (pages) hipLaunchKernelGGL(k_page_score_pages<GG>, grid4, dim3(256), 0, s, c, q, scores, bpu4);      \
     else hipLaunchKernelGGL(k_page_score_heads<GG>, grid, dim3(64 * (GG > 4 ? GG : 4)), 0, s, c, q, scores, bpu); \
     break;
   switch (c.G) {
