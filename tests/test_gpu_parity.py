@@ -173,6 +173,22 @@ def _check_select_against_oracle(w, ids, cnt):
             assert np.array_equal(ids[u, :cnt[u]], want), (b, h)
 
 
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_select_pages_large_grid_ragged(G):
+    # more than 512 64-page blocks, so the page scores run as 4-wave blocks of 256 pages; 1400 pages
+    # per sequence is not a multiple of 256 (the last block of each unit reaches past the allocated
+    # pages) and the sequences end mid-page, mid-block and after one token
+    kv = 8 if G < 8 else 4
+    w = make_custom(batch=3 if G < 8 else 6, num_q_heads=G * kv, num_kv_heads=kv,
+                    seq_lens=([22400, 17001, 1] if G < 8 else [22400, 17001, 1, 300, 16 * 1400 - 7, 4100]),
+                    kind="outlier", seed=90 + G, keep_frac=0.25, p=0.85, name=f"select_large_grid_g{G}")
+    assert w.batch * kv * -(-w.max_seq_len // 16 // 64) > 512
+    _print_case(w.name)
+    cache, t = device_cache(w)
+    ids, cnt = _select_pages_gpu(w, cache, t, w.keep_frac)
+    _check_select_against_oracle(w, ids, cnt)
+
+
 def test_select_pages_tied_scores():
     # every sequence repeats 5 page contents, so each score value is shared by many pages and the
     # K-th key falls inside a run of ties, which go to the lowest page ids
