@@ -141,7 +141,7 @@ __device__ __forceinline__ void page_fold(const uint4* row, const float4 (*qp)[k
 }
 
 template <int G>
-__global__ __launch_bounds__(256, 4) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, G > 4 ? 3 : 4) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
                                                          float* __restrict__ scores, int blocks_per_unit) {
   constexpr int NQ = 4;           // 16-byte words of one bound per staged quarter (32 channels)
   constexpr int RS = 2 * NQ + 1;  // LDS row of a page: NQ words of kmin, NQ of kmax, 16 B pad
