@@ -8,8 +8,13 @@ selectors but do not define Quest's score.  Readings taken here:
   per-channel upper bound of q.k over keys inside the page's min/max box;
 * it is evaluated as a float32 left-to-right fold over c = 0..127 starting from +0 (the products of
   two bf16 values are exact in float32, so only the additions round);
-* a GQA group shares one candidate set per (sequence, kv-head), ranked by the group score, the
-  float32 fold over the group's query heads in order starting from +0;
+* a GQA group shares one candidate set per (sequence, kv-head), ranked by the group score, the sum
+  over the group's query heads of sigma_h.  Since kmin_c <= kmax_c, max(q_c kmin_c, q_c kmax_c) =
+  q+_c kmax_c + q-_c kmin_c (q+ = max(q, 0), q- = min(q, 0)), so the group score is
+  sum_c (P_c kmax_c + N_c kmin_c) with P_c, N_c the sums of the group's q+_c and q-_c: it is evaluated
+  that way, P_c and N_c as float32 sums over the heads in order from +0, then one float32 fold over
+  c = 0..127 from +0 that adds P_c kmax_c and then N_c kmin_c, each with one rounding (a fused
+  multiply-add: P_c kmax_c need not be exact in float32 once several heads are summed);
 * the kept count is K = ceil(fp32(keep_frac) * fp32(P)) clamped to [1, P] (0 for an empty sequence);
   ties in score go to the lower page id; the kept pages are listed in ascending order.
 
@@ -21,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import F32, bf16_to_f32
+from .numerics import F32, bf16_to_f32, f32_fma
 
 PAGE = 16
 
@@ -38,12 +43,26 @@ def page_scores_head(qbits: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> n
     return acc
 
 
+def group_query_parts(qbits_group: np.ndarray):
+    """P_c and N_c: float32 sums over the group's heads, in order from +0, of q+_c and q-_c."""
+    q = bf16_to_f32(qbits_group)
+    P = np.zeros(q.shape[1], F32)
+    N = np.zeros(q.shape[1], F32)
+    for h in range(q.shape[0]):
+        P = (P + np.where(q[h] > 0, q[h], F32(0.0))).astype(F32)
+        N = (N + np.where(q[h] < 0, q[h], F32(0.0))).astype(F32)
+    return P, N
+
+
 def group_scores(qbits_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
-    """Group score: float32 fold over the group's query heads (``qbits_group`` uint16 [G][128])."""
-    gs = np.zeros(kmin.shape[0], F32)
-    for h in range(qbits_group.shape[0]):
-        gs = (gs + page_scores_head(qbits_group[h], kmin, kmax)).astype(F32)
-    return gs
+    """Group score of every page (``qbits_group`` uint16 [G][128]; ``kmin``/``kmax`` float32 [P][128]):
+    the fold over channels of P_c kmax_c then N_c kmin_c, each added with one float32 rounding."""
+    P, N = group_query_parts(qbits_group)
+    acc = np.zeros(kmin.shape[0], F32)
+    for c in range(128):
+        acc = f32_fma(P[c], kmax[:, c], acc)
+        acc = f32_fma(N[c], kmin[:, c], acc)
+    return acc
 
 
 def keep_count(num_pages: int, keep_frac: float) -> int:

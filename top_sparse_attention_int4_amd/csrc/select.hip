@@ -2,27 +2,28 @@
 //
 // The Twilight pages run an existing sparse-attention selector with a generous budget before the
 // top-p pruner (Paper-Notes "整体框架"; paperlayer §4.1, Fig. 5) and name Quest among those
-// selectors.  The page score of query head h is sum_c max(q_c*kmin_c, q_c*kmax_c); it is evaluated
-// as a float32 left-to-right fold over the 128 channels, one lane per page, so the result equals the
-// documented operation sequence on every run.  Because q_c*bound is exact in float32 (bf16 x bf16),
-// max(q*kmin, q*kmax) = q+ * kmax + q- * kmin with q+ = max(q,0), q- = min(q,0): the second product
-// is then an exact zero and adding it changes nothing, so two fused multiply-adds per channel and
-// head reproduce the fold bit for bit without a compare.  Two layouts compute the same folds: for
-// small steps each wave of a 4-wave block folds one query head for 64 pages (latency bound: every
-// head in parallel); for large ones each wave takes 64 pages, one lane per page folding all G query
-// heads, so each bound is converted once (the bounds are stored quarter-major, so a quarter of the
-// channels of a page is one 128-byte line; two quarters of a wave's loads are in flight and each
-// staged quarter requests the next, so the folds overlap the loads; a block is four such waves
-// sharing q+ and q- in LDS, 40 KB with the waves' quarter tiles, so that four blocks -- sixteen waves,
-// at most 128 VGPRs each -- share a compute unit and a 32K-token, 16-sequence layer's grid is resident
-// at once).  The group score then folds the heads in order.
+// selectors.  The page score of query head h is sum_c max(q_c*kmin_c, q_c*kmax_c), and a GQA group
+// ranks its pages by the sum over its heads.  Since kmin_c <= kmax_c, max(q*kmin, q*kmax) =
+// q+ * kmax + q- * kmin with q+ = max(q,0), q- = min(q,0), so the group score is
+// sum_c (P_c * kmax_c + N_c * kmin_c) with P_c, N_c the group's q+ and q- summed over its heads: two
+// fused multiply-adds per channel for the whole group instead of two per channel and head.  P_c and
+// N_c are float32 sums over the heads in order, then one float32 left-to-right fold over the 128
+// channels adds P_c*kmax_c and then N_c*kmin_c with one rounding each (one lane per page), so the
+// result equals the documented operation sequence on every run.  Two layouts compute the same folds:
+// for small steps a 4-wave block stages 64 pages' bounds and P/N, and its first wave folds (latency
+// bound: the bounds of the block arrive together); for large ones each wave takes 64 pages, one lane
+// per page (the bounds are stored quarter-major, so a quarter of the channels of a page is one
+// 128-byte line; two quarters of a wave's loads are in flight and each staged quarter requests the
+// next, so the folds overlap the loads; a block is four such waves sharing P and N in LDS, 37 KB with
+// the waves' quarter tiles, so that four blocks -- sixteen waves, at most 128 VGPRs each -- share a
+// compute unit and a 32K-token, 16-sequence layer's grid is resident at once).
 #include "twl_device.h"
 #include "twl_internal.h"
 
 namespace twl {
 
-// Small steps (few blocks, latency bound): each wave of a block folds one query head for the block's
-// 64 pages, read from an LDS copy of the bounds that the whole block loads at once.
+// Small steps (few blocks, latency bound): the block loads its 64 pages' bounds at once into LDS with
+// the group's P and N, and its first wave folds them (one lane per page).
 template <int G>
 __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(CacheView c, const uint16_t* __restrict__ q,
                                                                      float* __restrict__ scores,
@@ -36,15 +37,14 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
 
   // the block's 64 pages of bounds, staged with coalesced loads (row = 32 x 16 B, padded by 16 B)
   __shared__ uint4 tile[64][33];
-  __shared__ float qpos[G][kD];
-  __shared__ float qneg[G][kD];
-  __shared__ float sig[G][64];
+  __shared__ float qpos[kD];  // P_c: the group's q+ summed over its heads
+  __shared__ float qneg[kD];  // N_c: the group's q- summed over its heads
   constexpr int R = 64 * 32 / NT;
-  constexpr int QR = (G * kD + NT - 1) / NT;  // query channels per thread
   const uint16_t* qg = q + ((size_t)b * c.Hq + (size_t)h * G) * kD;
-  uint16_t qr[QR];
+  // thread ch < 128 holds channel ch of every head of the group
+  uint16_t qr[G];
 #pragma unroll
-  for (int i = 0; i < QR; ++i) qr[i] = qg[min((int)threadIdx.x + i * NT, G * kD - 1)];
+  for (int i = 0; i < G; ++i) qr[i] = qg[i * kD + ((int)threadIdx.x & (kD - 1))];
   int P;
   {
     // every bound read of the tile in flight at once, with the sequence length (the bounds are stored
@@ -67,18 +67,22 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
 #pragma unroll
     for (int r = 0; r < R; ++r) tile[((int)threadIdx.x >> 5) + r * (NT / 32)][col] = v[r];
   }
+  if (threadIdx.x < kD) {
+    float sp = 0.f, sn = 0.f;
 #pragma unroll
-  for (int k = 0; k < QR; ++k) {
-    const int i = threadIdx.x + k * NT;
-    if (i >= G * kD) break;
-    const float x = __uint_as_float((uint32_t)qr[k] << 16);
-    qpos[i / kD][i % kD] = x > 0.f ? x : 0.f;
-    qneg[i / kD][i % kD] = x < 0.f ? x : 0.f;
+    for (int i = 0; i < G; ++i) {
+      const float x = __uint_as_float((uint32_t)qr[i] << 16);
+      sp = sp + (x > 0.f ? x : 0.f);
+      sn = sn + (x < 0.f ? x : 0.f);
+    }
+    qpos[threadIdx.x] = sp;
+    qneg[threadIdx.x] = sn;
   }
   __syncthreads();
 
+  // one fold per page (the group's): the first wave's lanes take the block's 64 pages
   const int j = blk * 64 + lane;
-  if (hh < G && j < P) {
+  if (hh == 0 && j < P) {
     float acc = 0.f;
 #pragma unroll
     for (int c8 = 0; c8 < 16; ++c8) {
@@ -90,26 +94,18 @@ __global__ __launch_bounds__(64 * (G > 4 ? G : 4)) void k_page_score_heads(Cache
         const int ch = c8 * 8 + e;
         const float mn = (e & 1) ? bf16_hi(wm[e >> 1]) : bf16_lo(wm[e >> 1]);
         const float mx = (e & 1) ? bf16_hi(wx[e >> 1]) : bf16_lo(wx[e >> 1]);
-        acc = fmaf(qpos[hh][ch], mx, acc);
-        acc = fmaf(qneg[hh][ch], mn, acc);
+        acc = fmaf(qpos[ch], mx, acc);
+        acc = fmaf(qneg[ch], mn, acc);
       }
     }
-    sig[hh][lane] = acc;
-  }
-  __syncthreads();
-  if (hh == 0 && j < P) {
-    float gs = 0.f;
-#pragma unroll
-    for (int k = 0; k < G; ++k) gs = gs + sig[k][lane];
-    scores[(size_t)u * c.maxP + j] = gs;
+    scores[(size_t)u * c.maxP + j] = acc;
   }
 }
 
-// Fold 8 NQ channels (ch0 .. ch0 + 8 NQ - 1) of one page into the G heads' scores: row = the page's
-// staged part (NQ x 16 B of kmin, then NQ x 16 B of kmax), q+ / q- broadcast from LDS.
-template <int G, int NQ>
-__device__ __forceinline__ void page_fold(const uint4* row, const float4 (*qp)[kD / 4], const float4 (*qn)[kD / 4],
-                                          int ch0, float (&acc)[G]) {
+// Fold 8 NQ channels (ch0 .. ch0 + 8 NQ - 1) of one page into the group score: row = the page's staged
+// part (NQ x 16 B of kmin, then NQ x 16 B of kmax), the group's P_c / N_c broadcast from LDS.
+template <int NQ>
+__device__ __forceinline__ void page_fold(const uint4* row, const float4* qp, const float4* qn, int ch0, float& acc) {
 #pragma unroll 1
   for (int c8 = 0; c8 < NQ; ++c8) {
     const uint4 mnv = row[c8], mxv = row[NQ + c8];
@@ -124,24 +120,21 @@ __device__ __forceinline__ void page_fold(const uint4* row, const float4 (*qp)[k
       mx[2 * e + 1] = bf16_hi(wx[e]);
     }
     const int ch4 = (ch0 + 8 * c8) / 4;
+    const float4 p0 = qp[ch4], p1 = qp[ch4 + 1], n0 = qn[ch4], n1 = qn[ch4 + 1];
+    const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const float nv[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+    float a = acc;
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float4 p0 = qp[i][ch4], p1 = qp[i][ch4 + 1], n0 = qn[i][ch4], n1 = qn[i][ch4 + 1];
-      const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      const float nv[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
-      float a = acc[i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        a = fmaf(pv[e], mx[e], a);
-        a = fmaf(nv[e], mn[e], a);
-      }
-      acc[i] = a;
+    for (int e = 0; e < 8; ++e) {
+      a = fmaf(pv[e], mx[e], a);
+      a = fmaf(nv[e], mn[e], a);
     }
+    acc = a;
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(256, G > 4 ? 3 : 4) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 4) void k_page_score_pages(CacheView c, const uint16_t* __restrict__ q,
                                                          float* __restrict__ scores, int blocks_per_unit) {
   constexpr int NQ = 4;           // 16-byte words of one bound per staged quarter (32 channels)
   constexpr int RS = 2 * NQ + 1;  // LDS row of a page: NQ words of kmin, NQ of kmax, 16 B pad
@@ -151,7 +144,7 @@ __global__ __launch_bounds__(256, G > 4 ? 3 : 4) void k_page_score_pages(CacheVi
   const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
 
   __shared__ uint4 tiles[4][64 * RS];
-  __shared__ float4 qp[G][kD / 4], qn[G][kD / 4];
+  __shared__ float4 qp[kD / 4], qn[kD / 4];  // the group's P_c and N_c
   uint4* tile = tiles[wq];
   // this lane's page (the bounds are stored by logical page: no page-table lookup)
   const int j = blk * 256 + wq * 64 + lane;
@@ -159,17 +152,18 @@ __global__ __launch_bounds__(256, G > 4 ? 3 : 4) void k_page_score_pages(CacheVi
   // the bound reads do not wait for the sequence length: a lane past the sequence reads a page of
   // the sequence's allocated range (stored, perhaps stale) and its score is dropped
   const int lpg = min(j, c.maxP - 1);
-  // q+ and q- of every (head, channel) into LDS, shared by the block's four waves
-  for (int t = threadIdx.x; t < G * 64; t += 256) {
-    const uint32_t qw = reinterpret_cast<const uint32_t*>(qg)[t];
-    const float x0 = bf16_lo(qw), x1 = bf16_hi(qw);
-    float* pp = reinterpret_cast<float*>(&qp[t >> 6][0]);
-    float* pn = reinterpret_cast<float*>(&qn[t >> 6][0]);
-    const int ch = 2 * (t & 63);
-    pp[ch] = x0 > 0.f ? x0 : 0.f;
-    pp[ch + 1] = x1 > 0.f ? x1 : 0.f;
-    pn[ch] = x0 < 0.f ? x0 : 0.f;
-    pn[ch + 1] = x1 < 0.f ? x1 : 0.f;
+  // P_c and N_c (the group's q+ and q- summed over its heads in order) into LDS, shared by the
+  // block's four waves: thread ch < 128 sums channel ch
+  if (threadIdx.x < kD) {
+    float sp = 0.f, sn = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float x = __uint_as_float((uint32_t)qg[i * kD + threadIdx.x] << 16);
+      sp = sp + (x > 0.f ? x : 0.f);
+      sn = sn + (x < 0.f ? x : 0.f);
+    }
+    reinterpret_cast<float*>(qp)[threadIdx.x] = sp;
+    reinterpret_cast<float*>(qn)[threadIdx.x] = sn;
   }
   // quarter qq of page p is the 128-byte line 8 qq .. 8 qq + 7 of its slice (4 words of kmin, then 4 of
   // kmax); load r of a quarter covers pages 8 r .. 8 r + 7, lane l taking word l & 7 of page 8 r + (l >> 3)
@@ -194,9 +188,7 @@ __global__ __launch_bounds__(256, G > 4 ? 3 : 4) void k_page_score_pages(CacheVi
   const int P = (n + kPage - 1) / kPage;
   __syncthreads();  // the query halves are staged
   if (blk * 256 + wq * 64 >= P) return;  // uniform per wave (no block barrier follows)
-  float acc[G];
-#pragma unroll
-  for (int i = 0; i < G; ++i) acc[i] = 0.f;
+  float acc = 0.f;
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     if (qq > 0) {
@@ -214,14 +206,9 @@ __global__ __launch_bounds__(256, G > 4 ? 3 : 4) void k_page_score_pages(CacheVi
 #pragma unroll
       for (int r = 0; r < 8; ++r) v[qq + kAhead][r] = reinterpret_cast<const u32x4*>(rowp[r])[2 * NQ * (qq + kAhead)];
     }
-    page_fold<G, NQ>(tile + lane * RS, qp, qn, 32 * qq, acc);
+    page_fold<NQ>(tile + lane * RS, qp, qn, 32 * qq, acc);
   }
-  if (j < P) {
-    float gs = 0.f;
-#pragma unroll
-    for (int i = 0; i < G; ++i) gs = gs + acc[i];
-    scores[(size_t)u * c.maxP + j] = gs;
-  }
+  if (j < P) scores[(size_t)u * c.maxP + j] = acc;
 }
 
 // Ascending key <=> descending score (float order mapped onto uint32).
