@@ -144,10 +144,13 @@ twl_status twl_quantize_k(const twl_cache* cache, const int32_t* tok_begin, cons
                           int32_t max_span, void* stream);
 
 /* Base selector (Paper-Notes "整体框架": a generous budget, e.g. 1/4; paperlayer §4.1 Fig. 5),
- * Quest-style: page score of query head h = sum_c max(q_c*kmin_c, q_c*kmax_c) as a float32
- * left-to-right fold over c from +0; group score = float32 fold over the G heads in order; keep
- * K_b = clamp(ceil(fp32(keep_frac)*fp32(P_b)), 1, P_b) pages (P_b = ceil(seq_lens[b]/16), 0 if
- * empty) with the largest group score, ties to the lower page id; list them ascending.
+ * Quest-style: page score of query head h = sum_c max(q_c*kmin_c, q_c*kmax_c); the group score,
+ * their sum over the G heads, equals sum_c (P_c*kmax_c + N_c*kmin_c) with P_c / N_c the heads'
+ * max(q_c, 0) / min(q_c, 0) summed in float32 in head order, and is evaluated so: one float32
+ * left-to-right fold over c from +0 adding P_c*kmax_c, then N_c*kmin_c, each rounded once (fused
+ * multiply-add); keep K_b = clamp(ceil(fp32(keep_frac)*fp32(P_b)), 1, P_b) pages
+ * (P_b = ceil(seq_lens[b]/16), 0 if empty) with the largest group score, ties to the lower page id;
+ * list them ascending.
  *   q          bf16 [B][Hq][128]
  *   keep_frac  > 0, finite
  *   max_keep   row stride of page_ids, >= clamp(ceil(keep_frac*max_pages_per_seq), 1, max_pages_per_seq)
